@@ -1,0 +1,265 @@
+"""Seeded synthetic inputs shaped like the pages' workloads.
+
+This module only draws random numbers and lays out page tables; it holds
+none of the method's arithmetic (no quantization, no attention), so both the
+HIP path and the CPU oracle can be fed from it.
+
+Every generator uses an explicit ``torch.Generator`` seeded by the caller.
+Large K/V tensors can be drawn on the GPU (``device="cuda"``); the oracle
+then receives host copies of exactly those tensors.
+
+Workloads (sizes follow the FP8 KV pages' serving shapes; distributions are
+the synthetic stand-ins stated in the design notes):
+  tiny      2 requests (64 and 100 tokens), Hq 4 / Hkv 2, D 64, bs 16,
+            one all-zero K/V row and one row with a single x50 element.
+  prefill   fused qkv bf16 [4096, (32+8+8)*128]; K ~ N(0,1); V ~ N(0,0.05)
+            with 1% of (token, head) rows x100 and 0.1% all zero; 4096
+            distinct slots from a 1,048,576-slot pool of 16-token blocks.
+  decode    64 requests, lengths uniform in [1024, 32768], Hq 32 / Hkv 8,
+            D 128, bs 16, K/V ~ N(0,1), q ~ N(0,1).
+  longctx   4 requests of 262,144 .. 1,048,576 tokens, 4 verify rows,
+            Hq 16 / Hkv 4, D 128, bs 64; 0.5% of K rows carry one x30
+            channel (one channel per KV head).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+
+def gen(seed: int, device="cpu") -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+@dataclass
+class PagedLayout:
+    """Where every cached token of every request lives.
+
+    block_tables[b, i] is the physical block holding tokens
+    [i*bs, (i+1)*bs) of request b; unused entries hold ``pad``.
+    token_slots is the slot of each cached token, request-major (request 0's
+    tokens first), i.e. the slot ids a quantize+scatter of the whole cache
+    uses.
+    """
+    context_lens: torch.Tensor      # int32 [B]
+    block_tables: torch.Tensor      # int32 [B, max_blocks]
+    token_slots: torch.Tensor       # int64 [sum(context_lens)]
+    block_size: int
+    num_blocks: int                 # physical blocks in the pool
+
+    @property
+    def num_slots(self) -> int:
+        return self.num_blocks * self.block_size
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.token_slots.numel())
+
+
+def paged_layout(context_lens, block_size: int, g: torch.Generator,
+                 extra_blocks: int = 0, pad: int = 0) -> PagedLayout:
+    """Random block permutation: the pool has exactly the blocks the requests
+    need (plus ``extra_blocks`` free ones), shuffled."""
+    lens = [int(x) for x in context_lens]
+    need = [(n + block_size - 1) // block_size for n in lens]
+    num_blocks = sum(need) + int(extra_blocks)
+    perm = torch.randperm(num_blocks, generator=g).to(torch.int32)
+    max_blocks = max(1, max(need) if need else 1)
+    bt = torch.full((len(lens), max_blocks), int(pad), dtype=torch.int32)
+    slots = []
+    pos = 0
+    for b, nb in enumerate(need):
+        blocks = perm[pos:pos + nb]
+        pos += nb
+        bt[b, :nb] = blocks
+        if lens[b]:
+            j = torch.arange(lens[b], dtype=torch.int64)
+            slots.append(blocks.to(torch.int64)[j // block_size] * block_size
+                         + j % block_size)
+    token_slots = (torch.cat(slots) if slots
+                   else torch.zeros(0, dtype=torch.int64))
+    return PagedLayout(torch.tensor(lens, dtype=torch.int32), bt,
+                       token_slots, block_size, num_blocks)
+
+
+def normal_bf16(shape, g: torch.Generator, std: float = 1.0, device="cpu"):
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(torch.bfloat16)
+
+
+@dataclass
+class DecodeCase:
+    """A decode workload: the K/V to store, where, and the queries."""
+    name: str
+    layout: PagedLayout
+    k: torch.Tensor                 # bf16 [T, Hkv, D] (T = total tokens)
+    v: torch.Tensor                 # bf16 [T, Hkv, D]
+    q: torch.Tensor                 # bf16 [B, R, Hq, D]
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    rows: int
+    softmax_scale: float
+    partition_tokens: int = 0
+    notes: dict = field(default_factory=dict)
+
+
+def tiny_case(seed: int = 0) -> DecodeCase:
+    """2 requests (64, 100 tokens), Hq 4, Hkv 2, D 64, bs 16; one all-zero
+    (token, head) row and one row with a single x50 element in K and V."""
+    g = gen(seed)
+    lens = [64, 100]
+    H, Hq, D, bs = 2, 4, 64, 16
+    layout = paged_layout(lens, bs, g)
+    T = layout.total_tokens
+    k = normal_bf16((T, H, D), g).float()
+    v = normal_bf16((T, H, D), g).float()
+    rows = torch.randperm(T * H, generator=g)[:2]
+    zt, zh = divmod(int(rows[0]), H)
+    ot, oh = divmod(int(rows[1]), H)
+    od = int(torch.randint(0, D, (1,), generator=g))
+    k[zt, zh] = 0.0
+    v[zt, zh] = 0.0
+    k[ot, oh, od] *= 50.0
+    v[ot, oh, od] *= 50.0
+    q = normal_bf16((2, 1, Hq, D), g)
+    return DecodeCase("tiny", layout, k.to(torch.bfloat16),
+                      v.to(torch.bfloat16), q, Hq, H, D, 1, 1.0 / 8.0,
+                      notes={"zero_row": (zt, zh), "x50": (ot, oh, od)})
+
+
+def decode_case(lens, num_q_heads, num_kv_heads, head_dim, block_size,
+                rows=1, seed=0, device="cpu", extra_blocks=0,
+                k_outlier_frac=0.0, k_outlier_mult=30.0,
+                name="decode") -> DecodeCase:
+    """Generic decode workload with N(0,1) bf16 K/V/q. With
+    ``k_outlier_frac`` > 0 that fraction of K (token, head) rows gets one
+    channel (fixed per KV head) multiplied by ``k_outlier_mult``."""
+    g = gen(seed)
+    layout = paged_layout(lens, block_size, g, extra_blocks=extra_blocks)
+    T = layout.total_tokens
+    B = len(lens)
+    gd = gen(seed + 1000, device) if device != "cpu" else g
+    k = normal_bf16((T, num_kv_heads, head_dim), gd, device=device)
+    v = normal_bf16((T, num_kv_heads, head_dim), gd, device=device)
+    if k_outlier_frac > 0:
+        chan = torch.randint(0, head_dim, (num_kv_heads,), generator=g)
+        n_out = int(round(k_outlier_frac * T * num_kv_heads))
+        pick = torch.randperm(T * num_kv_heads, generator=g)[:n_out]
+        t_idx = (pick // num_kv_heads).to(device)
+        h_idx = (pick % num_kv_heads).to(device)
+        c_idx = chan.to(device)[h_idx]
+        k[t_idx, h_idx, c_idx] = (k[t_idx, h_idx, c_idx].float()
+                                  * k_outlier_mult).to(torch.bfloat16)
+    q = normal_bf16((B, rows, num_q_heads, head_dim), g)
+    return DecodeCase(name, layout, k, v, q, num_q_heads, num_kv_heads,
+                      head_dim, rows, 1.0 / math.sqrt(head_dim))
+
+
+def decode_lens(batch: int, lo: int, hi: int, seed: int):
+    """Context lengths uniform on the integers [lo, hi]."""
+    g = gen(seed)
+    return torch.randint(lo, hi + 1, (batch,), generator=g).tolist()
+
+
+def decode_workload(seed: int = 2, device="cpu") -> DecodeCase:
+    """64 requests, lengths ~ U[1024, 32768], Hq 32 / Hkv 8, D 128, bs 16."""
+    lens = decode_lens(64, 1024, 32768, seed)
+    return decode_case(lens, 32, 8, 128, 16, rows=1, seed=seed,
+                       device=device, name="decode")
+
+
+def longctx_workload(seed: int = 3, device="cpu") -> DecodeCase:
+    """4 requests of 262,144 x {1,2,3,4} tokens, 4 causal verify rows,
+    Hq 16 / Hkv 4, D 128, bs 64, 0.5% x30 K outlier rows; split-K partitions
+    of 8192 tokens."""
+    lens = [262144 * i for i in (1, 2, 3, 4)]
+    c = decode_case(lens, 16, 4, 128, 64, rows=4, seed=seed, device=device,
+                    k_outlier_frac=0.005, k_outlier_mult=30.0,
+                    name="longctx")
+    c.partition_tokens = 8192
+    return c
+
+
+@dataclass
+class PrefillChunk:
+    """A fused qkv activation and the slots its K/V rows go to."""
+    qkv: torch.Tensor               # bf16 [T, (Hq + 2*Hkv) * D]
+    slot_ids: torch.Tensor          # int64 [T]
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    num_slots: int
+    block_size: int
+
+    def k_view(self):
+        T = self.qkv.shape[0]
+        o = self.num_q_heads * self.head_dim
+        n = self.num_kv_heads * self.head_dim
+        return self.qkv[:, o:o + n].view(T, self.num_kv_heads, self.head_dim)
+
+    def v_view(self):
+        T = self.qkv.shape[0]
+        o = (self.num_q_heads + self.num_kv_heads) * self.head_dim
+        n = self.num_kv_heads * self.head_dim
+        return self.qkv[:, o:o + n].view(T, self.num_kv_heads, self.head_dim)
+
+
+def prefill_chunk(seed: int = 1, tokens: int = 4096, num_q_heads: int = 32,
+                  num_kv_heads: int = 8, head_dim: int = 128,
+                  num_slots: int = 1 << 20, block_size: int = 16,
+                  device="cpu", contiguous_slots: bool = False
+                  ) -> PrefillChunk:
+    """Fused qkv [T, (Hq+2Hkv)*D] bf16: Q ~ N(0,1) (never read by the store),
+    K ~ N(0,1), V ~ N(0, 0.05) with 1% of V (token, head) rows x100 and 0.1%
+    all zero. Slots: ``tokens`` distinct ids drawn without replacement from
+    [0, num_slots) (or a contiguous run when ``contiguous_slots``)."""
+    g = gen(seed)
+    H, D, Hq = num_kv_heads, head_dim, num_q_heads
+    gd = gen(seed + 1000, device) if device != "cpu" else g
+    q = torch.randn((tokens, Hq * D), generator=gd, device=device)
+    k = torch.randn((tokens, H, D), generator=gd, device=device)
+    v = torch.randn((tokens, H, D), generator=gd, device=device) * 0.05
+    n_rows = tokens * H
+    pick = torch.randperm(n_rows, generator=g)
+    n_big = int(round(0.01 * n_rows))
+    n_zero = int(round(0.001 * n_rows))
+    big = pick[:n_big].to(device)
+    zero = pick[n_big:n_big + n_zero].to(device)
+    vf = v.view(n_rows, D)
+    vf[big] *= 100.0
+    vf[zero] = 0.0
+    qkv = torch.cat([q, k.reshape(tokens, H * D), v.reshape(tokens, H * D)],
+                    dim=1).to(torch.bfloat16)
+    if contiguous_slots:
+        start = int(torch.randint(0, num_slots - tokens + 1, (1,),
+                                  generator=g))
+        slots = torch.arange(start, start + tokens, dtype=torch.int64)
+    else:
+        slots = torch.randperm(num_slots, generator=g)[:tokens].to(
+            torch.int64)
+    return PrefillChunk(qkv, slots.to(device), Hq, H, D, num_slots,
+                        block_size)
+
+
+def strided_pitch_scenario(seed: int = 7, tokens: int = 8,
+                           num_kv_heads: int = 3, head_dim: int = 128,
+                           clamp: float = 448.0):
+    """The FreeToken V-pitch scenario: a fused qkv whose row is 3 * H * D
+    elements (pitch 1152 at H=3, D=128); K is a view of its K slice (pitch
+    1152) while V is materialized densely by a clamp (pitch H * D = 384).
+    Returns (k_view, v_dense) as bf16 [tokens, H, D] tensors."""
+    g = gen(seed)
+    H, D = num_kv_heads, head_dim
+    qkv = normal_bf16((tokens, 3 * H * D), g)
+    k = qkv[:, H * D:2 * H * D].view(tokens, H, D)
+    # small values on one side and large on the other, as in the report
+    v_rows = (qkv[:, 2 * H * D:].float() * 0.05).to(torch.bfloat16)
+    v = v_rows.view(tokens, H, D).clamp(-clamp, clamp)
+    return k, v

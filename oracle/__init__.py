@@ -1,0 +1,195 @@
+"""CPU oracle for the FP8 E4M3 paged KV cache -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The product path (the HIP library and
+its binding in ``fp8_e4m3_paged_kv_amd``) never touches it, and the two share
+no code.
+
+The arithmetic lives in plain C (``oracle/*.c``, built into
+``oracle/liboracle.so``); this module only marshals numpy arrays. Every
+function cites, in the C sources, the page passage it follows.
+
+Arrays: bf16 data is passed as ``numpy.uint16`` bit patterns; strided views
+are accepted as they are (their element strides are passed to C).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SOURCES = ["e4m3.c", "quant.c", "attn.c"]
+
+E4M3 = 0
+E5M2 = 1
+
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the oracle with gcc into oracle/liboracle.so (strict IEEE:
+    no contraction, no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", "-Wall", "-Wextra", "-o", LIB_PATH + ".tmp"]
+    cmd += [os.path.join(_HERE, s) for s in SOURCES] + ["-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I = ctypes.c_int
+    D = ctypes.c_double
+    lib.fo_decode.argtypes = [I, ctypes.c_uint]
+    lib.fo_decode.restype = D
+    lib.fo_encode.argtypes = [I, ctypes.c_float]
+    lib.fo_encode.restype = ctypes.c_uint
+    lib.fo_fmt_max.argtypes = [I]
+    lib.fo_fmt_max.restype = D
+    lib.fo_encode_array.argtypes = [I, P, I64, P]
+    lib.fo_decode_array.argtypes = [I, P, I64, P]
+    lib.fo_quantize_row.argtypes = [I, P, I64, P, P]
+    lib.fo_kv_quant_scatter_bf16.argtypes = [P, I64, I64, P, I64, I64,
+                                             I64, I64, I64, P, I64,
+                                             P, P, I64, I64, P, P, I64, I64]
+    lib.fo_attend_dense.argtypes = [P, P, P, I64, I64, D, P]
+    lib.fo_paged_decode_attn.argtypes = [I, P, I64, I64, I64, P, P, I64, I64,
+                                         P, P, I64, I64, P, I64, P,
+                                         I64, I64, I64, I64, I64, I64, D, I64,
+                                         P, I64, P]
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _estrides(a: np.ndarray):
+    return [s // a.itemsize for s in a.strides]
+
+
+def fmt_max(fmt: int = E4M3) -> float:
+    return _load().fo_fmt_max(fmt)
+
+
+def decode(codes, fmt: int = E4M3) -> np.ndarray:
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    out = np.empty(c.shape, dtype=np.float64)
+    _load().fo_decode_array(fmt, _ptr(c), c.size, _ptr(out))
+    return out
+
+
+def encode(values, fmt: int = E4M3) -> np.ndarray:
+    v = np.ascontiguousarray(np.asarray(values, dtype=np.float32))
+    out = np.empty(v.shape, dtype=np.uint8)
+    _load().fo_encode_array(fmt, _ptr(v), v.size, _ptr(out))
+    return out
+
+
+def bf16_to_f32(bits) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def quantize_rows(x, fmt: int = E4M3):
+    """Quantize each row of a float32 [N, D] array: (codes uint8 [N, D],
+    scales float32 [N])."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    n, d = x.shape
+    codes = np.empty((n, d), dtype=np.uint8)
+    scales = np.empty((n,), dtype=np.float32)
+    lib = _load()
+    for i in range(n):
+        lib.fo_quantize_row(fmt, _ptr(x[i]), d, _ptr(codes[i]),
+                            scales[i:].ctypes.data)
+    return codes, scales
+
+
+def kv_quant_scatter_bf16(k, v, slot_ids, k_cache, v_cache, k_scale, v_scale,
+                          num_slots=None):
+    """In-place quantize + scatter.
+
+    k, v       uint16 (bf16 bits) views [T, H, D], last stride 1, any other
+               strides (K and V each keep their own).
+    slot_ids   int64 [T]; <0 or >= num_slots writes nothing.
+    k_cache, v_cache  uint8 [S, H, D] views (same strides for both).
+    k_scale, v_scale  float32 [S, H] views (same strides for both).
+    """
+    assert k.dtype == np.uint16 and v.dtype == np.uint16
+    assert k.shape == v.shape and k.ndim == 3
+    T, H, D = k.shape
+    ks, vs = _estrides(k), _estrides(v)
+    assert ks[2] == 1 and vs[2] == 1
+    slots = np.ascontiguousarray(np.asarray(slot_ids, dtype=np.int64))
+    assert slots.shape == (T,)
+    cs, ss = _estrides(k_cache), _estrides(k_scale)
+    assert _estrides(v_cache) == cs and _estrides(v_scale) == ss and cs[2] == 1
+    if num_slots is None:
+        num_slots = k_cache.shape[0]
+    _load().fo_kv_quant_scatter_bf16(
+        _ptr(k), ks[0], ks[1], _ptr(v), vs[0], vs[1], T, H, D,
+        _ptr(slots), num_slots, _ptr(k_cache), _ptr(v_cache), cs[0], cs[1],
+        _ptr(k_scale), _ptr(v_scale), ss[0], ss[1])
+
+
+def attend_dense(q, keys, vals, scale):
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    keys = np.ascontiguousarray(keys, dtype=np.float64)
+    vals = np.ascontiguousarray(vals, dtype=np.float64)
+    n, d = keys.shape
+    out = np.empty((d,), dtype=np.float64)
+    _load().fo_attend_dense(_ptr(q), _ptr(keys), _ptr(vals), n, d, scale,
+                            _ptr(out))
+    return out
+
+
+def paged_decode_attn(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                      context_lens, num_kv_heads, block_size, softmax_scale,
+                      partition_tokens=0, rows=None, fmt: int = E4M3):
+    """Paged GQA decode attention in double.
+
+    q            uint16 (bf16 bits) [B, R, Hq, D] view, last stride 1.
+    k/v_cache    uint8 [S, Hkv, D] views; k/v_scale float32 [S, Hkv] views.
+    block_tables int32 [B, max_blocks] (row stride taken from the view).
+    context_lens int32 [B].
+    rows         optional list of flat row ids (b*R + r)*Hq + hq; output is
+                 then [len(rows), D], else [B, R, Hq, D].
+    """
+    assert q.dtype == np.uint16 and q.ndim == 4
+    B, R, Hq, D = q.shape
+    qs = _estrides(q)
+    assert qs[3] == 1
+    cs, ss = _estrides(k_cache), _estrides(k_scale)
+    assert _estrides(v_cache) == cs and _estrides(v_scale) == ss
+    bt = np.asarray(block_tables, dtype=np.int32)
+    assert bt.strides[1] == 4
+    cl = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    if rows is None:
+        sel, nsel = None, 0
+        out = np.empty((B, R, Hq, D), dtype=np.float64)
+    else:
+        sel = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nsel = sel.size
+        out = np.empty((nsel, D), dtype=np.float64)
+    _load().fo_paged_decode_attn(
+        fmt, _ptr(q), qs[0], qs[1], qs[2], _ptr(k_cache), _ptr(v_cache),
+        cs[0], cs[1], _ptr(k_scale), _ptr(v_scale), ss[0], ss[1],
+        _ptr(bt), bt.strides[0] // 4, _ptr(cl), B, R, Hq, num_kv_heads, D,
+        block_size, float(softmax_scale), int(partition_tokens),
+        None if sel is None else _ptr(sel), nsel, _ptr(out))
+    return out

@@ -1,0 +1,171 @@
+"""Pins of the oracle's per-row quantizer and paged scatter.
+
+Fixed outside the oracle:
+* the torch-side reference the FreeToken fix commit checks codes against:
+  scale = amax / 448 in fp32, codes = (x / scale).to(float8_e4m3fn);
+* "dynamic scales ... never saturate" (ATOM #2655, description): the row
+  maximum maps exactly onto the format maximum;
+* half-ulp reconstruction bounds of the format;
+* the byte accounting of the FreeToken description: codes halve the bytes
+  of a 16-bit row and the scale sidecar costs 4/head_dim (~3% at 128);
+* the V-pitch scenario of the FreeToken fix commit (K a view of the fused
+  qkv slice, pitch 1152; V materialized by a clamp, pitch 384): with each
+  tensor read at its own pitch, 0 codes differ; reading V at K's pitch
+  (the reported bug, planted here on the CPU) corrupts V and leaves K
+  byte-perfect.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_e4m3_paged_kv_amd import synth
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> numpy uint16 view with the same strides."""
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def torch_reference_rows(x: torch.Tensor):
+    """The reference quantizer as a framework expresses it (fp32)."""
+    x = x.float()
+    amax = x.abs().amax(dim=-1, keepdim=True)
+    s = amax / 448.0
+    q = torch.where(s == 0, x, x / torch.where(s == 0, torch.ones_like(s), s))
+    codes = q.to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.numpy(), s.squeeze(-1).numpy()
+
+
+def rows_mix(seed=0, n=2048, d=128):
+    g = synth.gen(seed)
+    x = torch.randn((n, d), generator=g)
+    x[::17] *= 100.0                      # large rows
+    x[1::19] *= 1e-3                      # small rows
+    x[2::23] *= 1e-30                     # rows whose scale is fp32-tiny
+    x[3::29, 5] *= 50.0                   # single outlier element
+    x[4] = 0.0                            # all-zero row
+    x[5] = -0.0
+    return x.to(torch.bfloat16).float()
+
+
+def test_codes_match_torch_reference_quantizer():
+    x = rows_mix()
+    codes, scales = oracle.quantize_rows(x.numpy())
+    rc, rs = torch_reference_rows(x)
+    assert np.array_equal(scales, rs)
+    bad = np.argwhere(codes != rc)
+    assert bad.size == 0, bad[:5]
+
+
+def test_row_max_maps_to_fp8_max():
+    """Never saturates, and uses the whole range: wherever the scale is a
+    normal fp32 number the row's largest element encodes to +-448."""
+    x = rows_mix(seed=1)
+    codes, scales = oracle.quantize_rows(x.numpy())
+    normal = scales >= np.finfo(np.float32).tiny
+    assert normal.sum() > 1000
+    mags = codes[normal] & 0x7F
+    assert np.all(mags.max(axis=1) == 0x7E)
+    assert not np.any((codes & 0x7F) == 0x7F)      # never a NaN code
+
+
+def test_reconstruction_within_half_ulp():
+    x = rows_mix(seed=2)
+    codes, scales = oracle.quantize_rows(x.numpy())
+    rec = oracle.decode(codes) * scales[:, None].astype(np.float64)
+    xd = x.double().numpy()
+    s = scales[:, None].astype(np.float64)
+    ok = s[:, 0] >= np.finfo(np.float32).tiny
+    err = np.abs(rec - xd)[ok]
+    # normal e4m3 range: half ulp = 2^-4 relative; subnormal range: 2^-10*s
+    bound = np.maximum(2.0 ** -4 * np.abs(xd[ok]), 2.0 ** -10 * s[ok])
+    # plus the fp32 rounding of the quotient x/s (one ulp of fp32)
+    bound = bound * (1 + 2.0 ** -22) + 1e-300
+    assert np.all(err <= bound)
+
+
+def test_zero_row():
+    x = np.zeros((2, 64), np.float32)
+    x[1] = -0.0
+    codes, scales = oracle.quantize_rows(x)
+    assert np.all(scales == 0.0)
+    assert np.all(codes[0] == 0x00) and np.all(codes[1] == 0x80)
+    rec = oracle.decode(codes) * scales[:, None]
+    assert not np.any(np.isnan(rec)) and np.all(rec == 0)
+
+
+def test_byte_accounting_matches_pages():
+    """Codes carry the 16-bit geometry with a 1-byte element; the sidecar is
+    one fp32 per row: 4/head_dim of the code bytes (~3% at 128)."""
+    S, H, D = 4096, 8, 128
+    code_bytes = S * H * D * np.dtype(np.uint8).itemsize
+    scale_bytes = S * H * np.dtype(np.float32).itemsize
+    bf16_bytes = S * H * D * 2
+    assert code_bytes * 2 == bf16_bytes
+    assert scale_bytes / code_bytes == pytest.approx(4 / D)
+    assert 0.025 < scale_bytes / code_bytes < 0.035          # "~3%"
+    # per cached token, fp8 + sidecar vs bf16: (D + 4) / (2 D)
+    assert (code_bytes + scale_bytes) / bf16_bytes == pytest.approx(
+        (D + 4) / (2 * D))
+
+
+def _scatter(k, v, slots, S):
+    T, H, D = k.shape
+    kc = np.full((S, H, D), 0xA5, np.uint8)
+    vc = np.full((S, H, D), 0xA5, np.uint8)
+    ks = np.full((S, H), -7.0, np.float32)
+    vs = np.full((S, H), -7.0, np.float32)
+    oracle.kv_quant_scatter_bf16(bf16_bits(k), bf16_bits(v), slots, kc, vc,
+                                 ks, vs)
+    return kc, vc, ks, vs
+
+
+def test_scatter_places_rows_and_leaves_the_rest():
+    g = synth.gen(3)
+    T, H, D, S = 40, 4, 64, 256
+    k = synth.normal_bf16((T, H, D), g)
+    v = synth.normal_bf16((T, H, D), g)
+    slots = torch.randperm(S, generator=g)[:T].numpy().astype(np.int64)
+    slots[7] = -1                 # padding token: skipped
+    slots[9] = S + 5              # out of range: skipped
+    kc, vc, ks, vs = _scatter(k, v, slots, S)
+    kcodes, kscales = torch_reference_rows(k.float().reshape(T * H, D))
+    vcodes, vscales = torch_reference_rows(v.float().reshape(T * H, D))
+    kcodes = kcodes.reshape(T, H, D)
+    vcodes = vcodes.reshape(T, H, D)
+    written = np.zeros(S, bool)
+    for t in range(T):
+        s = slots[t]
+        if s < 0 or s >= S:
+            continue
+        written[s] = True
+        assert np.array_equal(kc[s], kcodes[t]) and np.array_equal(vc[s], vcodes[t])
+        assert np.array_equal(ks[s], kscales.reshape(T, H)[t])
+        assert np.array_equal(vs[s], vscales.reshape(T, H)[t])
+    assert np.all(kc[~written] == 0xA5) and np.all(vc[~written] == 0xA5)
+    assert np.all(ks[~written] == -7.0) and np.all(vs[~written] == -7.0)
+
+
+def test_strided_pitch_scenario_and_planted_v_pitch_bug():
+    k, v = synth.strided_pitch_scenario()
+    assert k.stride(0) == 1152 and v.stride(0) == 384
+    T, H, D = k.shape
+    slots = np.arange(T, dtype=np.int64)
+    kc, vc, ks, vs = _scatter(k, v, slots, T)
+    kref, _ = torch_reference_rows(k.contiguous().float().reshape(T * H, D))
+    vref, _ = torch_reference_rows(v.contiguous().float().reshape(T * H, D))
+    assert (kc.reshape(T * H, D) != kref).sum() == 0
+    assert (vc.reshape(T * H, D) != vref).sum() == 0
+    # multiset check (separates placement from value errors)
+    assert np.array_equal(np.sort(vc.ravel()), np.sort(vref.ravel()))
+
+    # Plant the reported bug: V read with K's row pitch. Use a buffer large
+    # enough that the wrong reads stay in bounds of this host array.
+    big = torch.zeros((T * 3 * H * D,), dtype=torch.bfloat16)
+    big[:T * H * D] = v.contiguous().view(-1)
+    v_wrong = big.as_strided((T, H, D), (k.stride(0), D, 1))
+    kc2, vc2, _, _ = _scatter(k, v_wrong, slots, T)
+    assert (kc2.reshape(T * H, D) != kref).sum() == 0       # K byte-perfect
+    wrong = (vc2.reshape(T * H, D) != vref).sum()
+    assert wrong > T * H * D // 2                           # V is garbage
