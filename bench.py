@@ -1,0 +1,400 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 E4M3 paged KV hot path on one MI355X.
+
+One step = one serving decode step over the decode workload (64 requests,
+context lengths uniform in [1024, 32768], 32 query / 8 KV heads, head_dim
+128, 16-token blocks, bf16 ~ N(0,1) K/V/q):
+  1. kv_quant_scatter of the step's 64 new K/V rows (one per request, at the
+     slot of its last token), and
+  2. paged GQA decode attention of the 64 query rows over the whole E4M3
+     cache (partition phase, then log-sum-exp merge).
+`value` is the step's algorithmic HBM bytes / step time (GB/s). The
+dominant kernel (the decode partition kernel) is also timed alone with HIP
+events on the stream it runs on, for the roofline object.
+
+Also measured in the same run (reported under "also"): quantize+scatter
+tokens/s on the 4096-token prefill chunk (fused qkv, K/V strided slices,
+random slots in a 1,048,576-slot pool, 32 rotating input sets so reads come
+from HBM), the cache-build bandwidth, and the long-context verify decode
+(4 requests of 256K..1M tokens, 4 verify rows, 16/4 heads, 64-token
+blocks, 8192-token partitions).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partition_traffic.json")
+KERNEL_SOURCES = ["fp8_e4m3_paged_kv_amd/csrc/paged_decode.hip",
+                  "fp8_e4m3_paged_kv_amd/csrc/fp8kv_device.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--partition", type=int, default=0,
+                    help="decode partition tokens (0 = library choice)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the prefill-chunk and long-context extras")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def decode_bytes(lens, Hkv, D, B, R, Hq, bs):
+    """Algorithmic HBM bytes of one decode launch: K and V codes plus their
+    fp32 row scales for every (token, KV head), the page-table entries, q
+    and the bf16 output."""
+    kv = sum(lens) * Hkv * 2 * (D + 4)
+    tables = sum((n + bs - 1) // bs for n in lens) * 4
+    q_out = 2 * B * R * Hq * D * 2
+    return kv + tables + q_out, kv
+
+
+def quant_bytes(T, Hkv, D):
+    """Algorithmic bytes of quantize+scatter: bf16 K and V rows read, E4M3
+    codes and fp32 scales written, one int64 slot id per token."""
+    return T * Hkv * 2 * (2 * D + D + 4) + 8 * T
+
+
+def time_events(fn, n, stream):
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def traffic_entry(per_launch_alg_bytes):
+    """HBM traffic of the partition kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(case, dc, lens, max_threads=16, budget_s=20.0):
+    """The oracle (as it stands) on a bounded sample of the same workload:
+    every query row of the first few requests, one request per thread."""
+    import numpy as np
+    import torch
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    L = case.layout
+    bs = L.block_size
+    H, D = case.num_kv_heads, case.head_dim
+    NB = dc["k_cache"].shape[0] // bs
+    cores = max(1, min(max_threads, os.cpu_count() or 1))
+    nreq = min(len(lens), cores)
+
+    def host_request(b):
+        nb = (lens[b] + bs - 1) // bs
+        blk = L.block_tables[b, :nb].long().to(dc["k_cache"].device)
+        kc = dc["k_cache"].view(NB, bs, H, D)[blk].reshape(-1, H, D).cpu().numpy()
+        vc = dc["v_cache"].view(NB, bs, H, D)[blk].reshape(-1, H, D).cpu().numpy()
+        kp = dc["k_plane"].view(H, NB, bs)[:, blk].reshape(H, -1).cpu().numpy()
+        vp = dc["v_plane"].view(H, NB, bs)[:, blk].reshape(H, -1).cpu().numpy()
+        bt = np.arange(nb, dtype=np.int32)[None, :]
+        q = case.q[b:b + 1].contiguous().view(torch.int16).numpy().view(np.uint16)
+        return q, kc, vc, kp.T, vp.T, bt, np.array([lens[b]], np.int32)
+
+    inputs = [host_request(b) for b in range(nreq)]
+
+    def run(args):
+        q, kc, vc, ks, vs, bt, cl = args
+        return oracle.paged_decode_attn(q, kc, vc, ks, vs, bt, cl, H, bs,
+                                        case.softmax_scale)
+
+    # calibrate: one request alone, then as many in parallel as fit the
+    # budget (each thread runs one request)
+    t0 = time.perf_counter()
+    run(inputs[0])
+    one = time.perf_counter() - t0
+    n = max(1, min(nreq, int(budget_s / max(one, 1e-3))))
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=min(cores, n)) as ex:
+        list(ex.map(run, inputs[:n]))
+    wall = time.perf_counter() - t0
+    tokens = sum(lens[:n])
+    alg = tokens * H * 2 * (D + 4)
+    return {"value": round(alg / wall / 1e9, 4), "unit": "GB/s",
+            "cores": min(cores, n), "kind": "oracle",
+            "sample": f"all {case.num_q_heads} query rows of {n} decode requests "
+                      f"({tokens} cached tokens x {H} KV heads), one request per thread",
+            "seconds": round(wall, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; "
+                                   "run with --gpus 1"}))
+        sys.exit(2)
+    import torch
+    import fp8_e4m3_paged_kv_amd as fk
+    from fp8_e4m3_paged_kv_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---------------- decode workload (resident in HBM) ----------------
+    log("building the decode workload (64 requests)...")
+    case = synth.decode_workload(seed=2, device=dev)
+    L = case.layout
+    lens = L.context_lens.tolist()
+    B, R, Hq, Hkv, D, bs = 64, 1, 32, 8, 128, L.block_size
+    S = L.num_slots
+    k_cache = torch.empty((S, Hkv, D), dtype=torch.uint8, device=dev)
+    v_cache = torch.empty_like(k_cache)
+    k_plane = torch.empty((Hkv, S), dtype=torch.float32, device=dev)
+    v_plane = torch.empty_like(k_plane)
+    slots_all = L.token_slots.to(dev)
+    T = slots_all.numel()
+    # cache build: quantize+scatter of every cached token (chunks of 64K)
+    chunk = 1 << 16
+    torch.cuda.synchronize()
+    t_build = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(0, T, chunk):
+        fk.kv_quant_scatter(case.k[i:i + chunk], case.v[i:i + chunk],
+                            slots_all[i:i + chunk], k_cache, v_cache,
+                            k_plane.t(), v_plane.t())
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    build_ms = ev0.elapsed_time(ev1)
+    build_gbs = quant_bytes(T, Hkv, D) / (build_ms * 1e-3) / 1e9
+    log(f"cache build: {T} tokens in {build_ms:.2f} ms = {build_gbs:.1f} GB/s")
+
+    # the step's new K/V rows: the last token of each request
+    last = torch.tensor([sum(lens[:b + 1]) - 1 for b in range(B)], device=dev)
+    k_new = case.k[last].contiguous()
+    v_new = case.v[last].contiguous()
+    slots_new = slots_all[last].contiguous()
+    del case.k, case.v
+    torch.cuda.empty_cache()
+
+    q = case.q.to(dev)
+    bt = L.block_tables.to(dev)
+    cl = L.context_lens.to(dev)
+    maxc = 32768
+    part = fk.decode_partition_tokens(B, R, Hq, Hkv, D, bs, maxc, args.partition)
+    ws = torch.empty(fk.decode_workspace_bytes(B, R, Hq, Hkv, D, bs, maxc, part),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((B, R, Hq, D), dtype=torch.bfloat16, device=dev)
+    kw = dict(num_kv_heads=Hkv, block_size=bs, softmax_scale=case.softmax_scale,
+              max_context=maxc, partition_tokens=part)
+
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    rec = {"i": None}
+
+    def step():
+        fk.kv_quant_scatter(k_new, v_new, slots_new, k_cache, v_cache,
+                            k_plane.t(), v_plane.t())
+        i = rec["i"]
+        if i is not None:
+            ev_a[i].record(stream)
+        fk.paged_decode_partials(q, k_cache, v_cache, k_plane.t(), v_plane.t(),
+                                 bt, cl, workspace=ws, **kw)
+        if i is not None:
+            ev_b[i].record(stream)
+        fk.paged_decode_merge(ws, cl, out, rows=R, num_q_heads=Hq,
+                              num_kv_heads=Hkv, block_size=bs, max_context=maxc,
+                              partition_tokens=part)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        rec["i"] = i
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    rec["i"] = None
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    part_ms = sorted(a.elapsed_time(b) for a, b in zip(ev_a, ev_b))
+    part_avg_ms = sum(part_ms) / len(part_ms)
+
+    dec_bytes, dec_kv = decode_bytes(lens, Hkv, D, B, R, Hq, bs)
+    step_bytes = dec_bytes + quant_bytes(B, Hkv, D)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    part_bytes = dec_bytes - B * R * Hq * D * 2     # the merge writes out
+    achieved = part_bytes / (part_avg_ms * 1e-3) / 1e9
+    log(f"decode step: {ms_per_step * 1e3:.1f} us, partition kernel "
+        f"{part_avg_ms * 1e3:.1f} us = {achieved:.0f} GB/s")
+    traffic = traffic_entry(part_bytes)
+
+    result = {
+        "metric": "FP8 paged decode attn HBM GB/s (% peak) + quant-scatter tokens/s, 1 GPU",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 codes (u8) + fp32 scales; bf16/fp16 MFMA, fp32 accumulate",
+        "data": "synthetic (seeded N(0,1) bf16 K/V/q)",
+        "config": {"workload": "decode step: quant-scatter of 64 new tokens + paged GQA "
+                               "decode, 64 requests, lengths U[1024,32768]",
+                   "batch": B, "context_tokens": sum(lens), "num_q_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim": D, "block_size": bs,
+                   "partition_tokens": part, "scale_planes": "head-major [Hkv, slots]"},
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "decode_partition_kernel",
+                     "alg_bytes_per_launch": part_bytes,
+                     "avg_launch_us": round(part_avg_ms * 1e3, 2)},
+        "cpu_baseline": None,
+        "also": {"cache_build_GBps": round(build_gbs, 1)},
+    }
+
+    if not args.no_extras:
+        result["also"].update(prefill_quant_scatter(torch, fk, synth, dev, stream))
+        result["also"].update(longctx_decode(torch, fk, synth, dev, stream))
+
+    if not args.no_cpu_baseline:
+        log("timing the oracle on host cores...")
+        dc = {"k_cache": k_cache, "v_cache": v_cache, "k_plane": k_plane,
+              "v_plane": v_plane}
+        result["cpu_baseline"] = cpu_baseline(case, dc, lens)
+    print(json.dumps(result), flush=True)
+
+
+def prefill_quant_scatter(torch, fk, synth, dev, stream, sets=32, reps=4):
+    """Quantize+scatter of the 4096-token prefill chunk, rotating 32 input
+    sets (1.6 GB > the 256 MB MALL) and slot sets."""
+    log("prefill-chunk quantize+scatter...")
+    H, D, T, S = 8, 128, 4096, 1 << 20
+    chunks = [synth.prefill_chunk(seed=100 + i, device=dev) for i in range(sets)]
+    k_cache = torch.empty((S, H, D), dtype=torch.uint8, device=dev)
+    v_cache = torch.empty_like(k_cache)
+    k_plane = torch.empty((H, S), dtype=torch.float32, device=dev)
+    v_plane = torch.empty_like(k_plane)
+    it = {"i": 0}
+
+    def one():
+        c = chunks[it["i"] % sets]
+        it["i"] += 1
+        fk.kv_quant_scatter(c.k_view(), c.v_view(), c.slot_ids, k_cache,
+                            v_cache, k_plane.t(), v_plane.t())
+    for _ in range(sets):
+        one()
+    ms = time_events(one, sets * reps, stream)
+    avg = sum(ms) / len(ms)
+    tok_s = T / (avg * 1e-3)
+    gbs = quant_bytes(T, H, D) / (avg * 1e-3) / 1e9
+    del chunks
+    torch.cuda.empty_cache()
+    return {"quant_scatter_prefill_tokens_per_s": round(tok_s, 0),
+            "quant_scatter_prefill_us": round(avg * 1e3, 2),
+            "quant_scatter_prefill_GBps": round(gbs, 1)}
+
+
+def longctx_decode(torch, fk, synth, dev, stream, reps=20):
+    log("long-context verify decode (4 x 256K..1M tokens)...")
+    case = synth.longctx_workload(seed=3, device=dev)
+    L = case.layout
+    H, D, bs = 4, 128, L.block_size
+    S = L.num_slots
+    k_cache = torch.empty((S, H, D), dtype=torch.uint8, device=dev)
+    v_cache = torch.empty_like(k_cache)
+    k_plane = torch.empty((H, S), dtype=torch.float32, device=dev)
+    v_plane = torch.empty_like(k_plane)
+    slots = L.token_slots.to(dev)
+    T = slots.numel()
+    chunk = 1 << 18
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(0, T, chunk):
+        fk.kv_quant_scatter(case.k[i:i + chunk], case.v[i:i + chunk],
+                            slots[i:i + chunk], k_cache, v_cache, k_plane.t(),
+                            v_plane.t())
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    build_gbs = quant_bytes(T, H, D) / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del case.k, case.v
+    torch.cuda.empty_cache()
+    lens = L.context_lens.tolist()
+    maxc = max(lens)
+    part = case.partition_tokens
+    B, R, Hq = 4, 4, 16
+    q = case.q.to(dev)
+    bt = L.block_tables.to(dev)
+    cl = L.context_lens.to(dev)
+    ws = torch.empty(fk.decode_workspace_bytes(B, R, Hq, H, D, bs, maxc, part),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((B, R, Hq, D), dtype=torch.bfloat16, device=dev)
+    kw = dict(num_kv_heads=H, block_size=bs, softmax_scale=case.softmax_scale,
+              max_context=maxc, partition_tokens=part, workspace=ws)
+
+    def partials():
+        fk.paged_decode_partials(q, k_cache, v_cache, k_plane.t(), v_plane.t(),
+                                 bt, cl, **kw)
+
+    def full():
+        fk.paged_decode_attn_fp8(q, k_cache, v_cache, k_plane.t(), v_plane.t(),
+                                 bt, cl, out=out, **kw)
+    for _ in range(3):
+        full()
+    pm = time_events(partials, reps, stream)
+    fm = time_events(full, reps, stream)
+    dec, kvb = decode_bytes(lens, H, D, B, R, Hq, bs)
+    p_avg = sum(pm) / len(pm)
+    f_avg = sum(fm) / len(fm)
+    res = {"longctx_decode_us": round(f_avg * 1e3, 1),
+           "longctx_decode_GBps": round(dec / (f_avg * 1e-3) / 1e9, 1),
+           "longctx_partition_kernel_us": round(p_avg * 1e3, 1),
+           "longctx_partition_kernel_GBps": round((dec - B * R * Hq * D * 2) / (p_avg * 1e-3) / 1e9, 1),
+           "longctx_cache_build_GBps": round(build_gbs, 1)}
+    del k_cache, v_cache, k_plane, v_plane
+    torch.cuda.empty_cache()
+    return res
+
+
+if __name__ == "__main__":
+    main()

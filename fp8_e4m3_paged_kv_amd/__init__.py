@@ -1,0 +1,266 @@
+"""fp8_e4m3_paged_kv_amd -- FP8 E4M3 paged KV cache for MI355X (gfx950).
+
+A thin ctypes binding over ``libfp8kv.so`` (C ABI: ``include/fp8kv.h``).
+It only marshals arguments -- pointers, strides, the current HIP stream --
+and raises on a nonzero status; every step of the computation runs in the
+library's HIP kernels. There is no fallback: if the library is missing the
+import of any entry point raises.
+
+Cache layout used by the helpers here:
+  k_cache, v_cache   uint8  [num_slots, Hkv, D]  (or [num_blocks, bs, Hkv, D])
+  k_scale, v_scale   fp32   any 2-D view [num_slots, Hkv] -- including a
+                     transposed view of a head-major [Hkv, num_slots] plane
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfp8kv.so")
+
+DTYPE_BF16 = 1
+DTYPE_FP16 = 2
+DTYPE_FP32 = 3
+
+_TORCH_DTYPE = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_FP16,
+                torch.float32: DTYPE_FP32}
+
+_lib = None
+
+
+class Fp8KvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"fp8kv status {status}: {message}")
+        self.status = status
+
+
+def lib():
+    """Load libfp8kv.so (built in-tree by ``python -m
+    fp8_e4m3_paged_kv_amd.build``); raises if it is not there."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m fp8_e4m3_paged_kv_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    SZ = ctypes.c_size_t
+    L.fp8kv_abi_version.restype = ctypes.c_int
+    L.fp8kv_status_string.argtypes = [ctypes.c_int]
+    L.fp8kv_status_string.restype = ctypes.c_char_p
+    L.fp8kv_last_error.restype = ctypes.c_char_p
+    L.fp8kv_kv_quant_scatter.argtypes = [P, I64, I64, P, I64, I64, I32, I32,
+                                         I32, I32, P, P, P, I64, I64, P, P,
+                                         I64, I64, I64, P]
+    L.fp8kv_kv_quant_scatter.restype = ctypes.c_int
+    dec = [P, I64, I64, I64, I32, P, P, I64, I64, P, P, I64, I64, I64, P, I64,
+           P, I32, I32, I32, I32, I32, I32, F, I32, I32, P, SZ]
+    L.fp8kv_paged_decode_attn_fp8.argtypes = dec + [P, I64, I64, I64, I32, P]
+    L.fp8kv_paged_decode_attn_fp8.restype = ctypes.c_int
+    L.fp8kv_paged_decode_partials.argtypes = dec + [P]
+    L.fp8kv_paged_decode_partials.restype = ctypes.c_int
+    L.fp8kv_paged_decode_merge.argtypes = [P, I32, I32, I32, I32, I32, I32,
+                                           I32, I32, P, SZ, P, I64, I64, I64,
+                                           I32, P]
+    L.fp8kv_paged_decode_merge.restype = ctypes.c_int
+    shape = [I32] * 8
+    L.fp8kv_paged_decode_workspace_bytes.argtypes = shape
+    L.fp8kv_paged_decode_workspace_bytes.restype = I64
+    L.fp8kv_paged_decode_partition_tokens.argtypes = shape
+    L.fp8kv_paged_decode_partition_tokens.restype = I32
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        raise Fp8KvError(status, L.fp8kv_last_error().decode() or
+                         L.fp8kv_status_string(status).decode())
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("fp8kv: every tensor must live on the GPU")
+
+
+def _cache_strides(cache: torch.Tensor):
+    """(stride_slot, stride_head) of a [S, H, D] or [NB, bs, H, D] code
+    buffer, inner stride 1."""
+    if cache.dim() == 4:
+        nb, bs, H, D = cache.shape
+        if cache.stride(0) != bs * cache.stride(1):
+            raise ValueError("4-D cache: blocks must be evenly spaced slots")
+        return cache.stride(1), cache.stride(2), nb * bs, H, D
+    if cache.dim() == 3:
+        S, H, D = cache.shape
+        return cache.stride(0), cache.stride(1), S, H, D
+    raise ValueError("cache must be [S, H, D] or [NB, bs, H, D]")
+
+
+def _scale_strides(scale: torch.Tensor):
+    if scale.dim() == 3:          # [NB, bs, H]
+        return scale.stride(1), scale.stride(2)
+    if scale.dim() == 2:          # [S, H]
+        return scale.stride(0), scale.stride(1)
+    raise ValueError("scale plane must be [S, H] or [NB, bs, H]")
+
+
+def abi_version() -> int:
+    return lib().fp8kv_abi_version()
+
+
+def kv_quant_scatter(k: torch.Tensor, v: torch.Tensor, slot_ids: torch.Tensor,
+                     k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     k_scale: torch.Tensor, v_scale: torch.Tensor) -> None:
+    """Quantize K and V ([T, Hkv, D] bf16 views, each at its own strides) to
+    E4M3 + fp32 row scales and scatter them to ``slot_ids`` (int64 [T],
+    device) in one launch. Slot ids < 0 or >= num_slots are skipped."""
+    _dev(k, v, slot_ids, k_cache, v_cache, k_scale, v_scale)
+    if k.shape != v.shape or k.dim() != 3:
+        raise ValueError("k and v must both be [T, Hkv, D]")
+    if k.dtype != v.dtype or k.dtype not in _TORCH_DTYPE:
+        raise ValueError("k and v must share a float dtype")
+    if k.stride(2) != 1 or v.stride(2) != 1:
+        raise ValueError("head_dim must be the contiguous dimension")
+    if slot_ids.dtype != torch.int64 or slot_ids.shape != (k.shape[0],):
+        raise ValueError("slot_ids must be int64 [T]")
+    if not slot_ids.is_contiguous():
+        raise ValueError("slot_ids must be contiguous")
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("code buffers are uint8")
+    if k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32:
+        raise ValueError("scale planes are float32")
+    css, csh, S, H, D = _cache_strides(k_cache)
+    if _cache_strides(v_cache)[:2] != (css, csh):
+        raise ValueError("k_cache and v_cache must share strides")
+    sss, ssh = _scale_strides(k_scale)
+    if _scale_strides(v_scale) != (sss, ssh):
+        raise ValueError("k_scale and v_scale must share strides")
+    T, Hk, Dk = k.shape
+    if (Hk, Dk) != (H, D):
+        raise ValueError("K/V head count or head_dim differs from the cache")
+    _check(lib().fp8kv_kv_quant_scatter(
+        k.data_ptr(), k.stride(0), k.stride(1),
+        v.data_ptr(), v.stride(0), v.stride(1),
+        _TORCH_DTYPE[k.dtype], T, H, D, slot_ids.data_ptr(),
+        k_cache.data_ptr(), v_cache.data_ptr(), css, csh,
+        k_scale.data_ptr(), v_scale.data_ptr(), sss, ssh, S,
+        _stream(k.device)))
+
+
+def decode_workspace_bytes(batch, rows, num_q_heads, num_kv_heads, head_dim,
+                           block_size, max_context, partition_tokens=0) -> int:
+    n = lib().fp8kv_paged_decode_workspace_bytes(
+        batch, rows, num_q_heads, num_kv_heads, head_dim, block_size,
+        max_context, partition_tokens)
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def decode_partition_tokens(batch, rows, num_q_heads, num_kv_heads, head_dim,
+                            block_size, max_context, partition_tokens=0) -> int:
+    n = lib().fp8kv_paged_decode_partition_tokens(
+        batch, rows, num_q_heads, num_kv_heads, head_dim, block_size,
+        max_context, partition_tokens)
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def _decode_args(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                 context_lens, num_kv_heads, block_size, softmax_scale,
+                 max_context, partition_tokens, workspace):
+    _dev(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens)
+    if q.dim() != 4 or q.stride(3) != 1:
+        raise ValueError("q must be [B, R, Hq, D] with contiguous head_dim")
+    if q.dtype not in _TORCH_DTYPE:
+        raise ValueError("unsupported q dtype")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or \
+            block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be int32 [B, max_blocks], rows contiguous")
+    if context_lens.dtype != torch.int32 or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be contiguous int32 [B]")
+    B, R, Hq, D = q.shape
+    css, csh, S, H, Dc = _cache_strides(k_cache)
+    if _cache_strides(v_cache)[:2] != (css, csh) or H != num_kv_heads or Dc != D:
+        raise ValueError("cache geometry does not match q / num_kv_heads")
+    sss, ssh = _scale_strides(k_scale)
+    if _scale_strides(v_scale) != (sss, ssh):
+        raise ValueError("k_scale and v_scale must share strides")
+    ws_bytes = decode_workspace_bytes(B, R, Hq, num_kv_heads, D, block_size,
+                                      max_context, partition_tokens)
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8,
+                                device=q.device)
+    _dev(workspace)
+    args = [q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
+            _TORCH_DTYPE[q.dtype], k_cache.data_ptr(), v_cache.data_ptr(),
+            css, csh, k_scale.data_ptr(), v_scale.data_ptr(), sss, ssh, S,
+            block_tables.data_ptr(), block_tables.stride(0),
+            context_lens.data_ptr(), B, R, Hq, num_kv_heads, D, block_size,
+            float(softmax_scale), int(partition_tokens), int(max_context),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size()]
+    return args, workspace
+
+
+def paged_decode_attn_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                          context_lens, *, num_kv_heads, block_size,
+                          softmax_scale, max_context, partition_tokens=0,
+                          out=None, out_dtype=torch.bfloat16, workspace=None):
+    """Paged GQA decode attention over the E4M3 cache. q: [B, R, Hq, D]
+    bf16 (R verify rows, causal among themselves). Returns out [B, R, Hq, D]
+    (bf16 or fp32)."""
+    args, workspace = _decode_args(q, k_cache, v_cache, k_scale, v_scale,
+                                   block_tables, context_lens, num_kv_heads,
+                                   block_size, softmax_scale, max_context,
+                                   partition_tokens, workspace)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _dev(out)
+    if out.shape != q.shape or out.stride(3) != 1:
+        raise ValueError("out must be [B, R, Hq, D] with contiguous head_dim")
+    _check(lib().fp8kv_paged_decode_attn_fp8(
+        *args, out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
+        _TORCH_DTYPE[out.dtype], _stream(q.device)))
+    return out
+
+
+def paged_decode_partials(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                          context_lens, *, num_kv_heads, block_size,
+                          softmax_scale, max_context, partition_tokens=0,
+                          workspace=None):
+    """Partition phase only; returns the workspace holding the partials."""
+    args, workspace = _decode_args(q, k_cache, v_cache, k_scale, v_scale,
+                                   block_tables, context_lens, num_kv_heads,
+                                   block_size, softmax_scale, max_context,
+                                   partition_tokens, workspace)
+    _check(lib().fp8kv_paged_decode_partials(*args, _stream(q.device)))
+    return workspace
+
+
+def paged_decode_merge(workspace, context_lens, out, *, rows, num_q_heads,
+                       num_kv_heads, block_size, max_context,
+                       partition_tokens=0):
+    """Log-sum-exp merge of the partials in ``workspace`` into out
+    [B, R, Hq, D]."""
+    _dev(workspace, context_lens, out)
+    B, R, Hq, D = out.shape
+    _check(lib().fp8kv_paged_decode_merge(
+        context_lens.data_ptr(), B, rows, num_q_heads, num_kv_heads, D,
+        block_size, int(partition_tokens), int(max_context),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
+        _TORCH_DTYPE[out.dtype], _stream(out.device)))
+    return out

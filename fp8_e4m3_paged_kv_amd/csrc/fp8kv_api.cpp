@@ -1,0 +1,384 @@
+// fp8kv_api.cpp -- the C ABI of libfp8kv.so: host-side O(1) validation,
+// grid sizing and kernel launches. Nothing here touches device memory.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/fp8kv.h"
+#include "fp8kv_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return FP8KV_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) {
+    return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+constexpr int kTile = 32;          // tokens per decode tile
+constexpr int kMaxStackedRows = 16; // MFMA M dimension
+
+struct DecodeShape {
+    int32_t partition = 0;
+    int32_t num_partitions = 0;
+    int32_t group = 0;
+    int32_t m_rows = 0;
+    int64_t ws_o_floats = 0;
+    int64_t ws_lse_floats = 0;
+    int64_t ws_bytes = 0;
+    int64_t lse_offset_bytes = 0;
+};
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Shape rules shared by the workspace query and the calls.
+int decode_shape(int32_t batch, int32_t rows, int32_t num_q_heads,
+                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                 int32_t max_context, int32_t partition_tokens,
+                 DecodeShape* s) {
+    if (head_dim != 64 && head_dim != 128)
+        return fail(FP8KV_E_UNSUPPORTED, "head_dim %d: only 64 and 128 are supported", head_dim);
+    if (batch < 0 || max_context < 0)
+        return fail(FP8KV_E_SHAPE, "batch (%d) and max_context (%d) must be >= 0", batch, max_context);
+    if (rows < 1 || num_q_heads < 1 || num_kv_heads < 1)
+        return fail(FP8KV_E_SHAPE, "rows, num_q_heads and num_kv_heads must be >= 1");
+    if (num_q_heads % num_kv_heads != 0)
+        return fail(FP8KV_E_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                    num_q_heads, num_kv_heads);
+    const int32_t group = num_q_heads / num_kv_heads;
+    if ((int64_t)rows * group > kMaxStackedRows)
+        return fail(FP8KV_E_UNSUPPORTED,
+                    "rows * (num_q_heads / num_kv_heads) = %d exceeds the %d-row tile",
+                    rows * group, kMaxStackedRows);
+    if (block_size < 16 || block_size % 16 != 0)
+        return fail(FP8KV_E_UNSUPPORTED, "block_size %d: must be a positive multiple of 16", block_size);
+    if (partition_tokens < 0 || partition_tokens % kTile != 0)
+        return fail(FP8KV_E_SHAPE, "partition_tokens %d: must be 0 (auto) or a positive multiple of %d",
+                    partition_tokens, kTile);
+    int32_t part = partition_tokens;
+    if (part == 0) {
+        // Library choice: long contexts get long partitions (fewer partials
+        // to merge, more tiles per wave); short ones keep enough
+        // workgroups to fill 256 CUs.
+        if (max_context >= 131072) part = 8192;
+        else if (max_context > 1024) part = 1024;
+        else part = (int32_t)round_up(max_context > 0 ? max_context : 1, kTile);
+    }
+    s->partition = part;
+    s->group = group;
+    s->m_rows = rows * group;
+    s->num_partitions = max_context == 0 ? 0 : (int32_t)((max_context + part - 1) / part);
+    const int64_t units = (int64_t)batch * num_kv_heads * s->num_partitions * s->m_rows;
+    s->ws_o_floats = units * head_dim;
+    s->ws_lse_floats = units;
+    s->lse_offset_bytes = round_up(s->ws_o_floats * 4, 256);
+    s->ws_bytes = s->lse_offset_bytes + round_up(s->ws_lse_floats * 4, 256);
+    return FP8KV_OK;
+}
+
+int check_out_dtype(int32_t out_dtype) {
+    if (out_dtype != FP8KV_DTYPE_BF16 && out_dtype != FP8KV_DTYPE_FP32)
+        return fail(FP8KV_E_UNSUPPORTED, "out_dtype %d: only BF16 and FP32 outputs", out_dtype);
+    return FP8KV_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+    if (e != hipSuccess)
+        return fail(FP8KV_E_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8kv_abi_version(void) { return FP8KV_ABI_VERSION; }
+
+const char* fp8kv_status_string(int status) {
+    switch (status) {
+        case FP8KV_OK: return "ok";
+        case FP8KV_E_NULL: return "null pointer";
+        case FP8KV_E_SHAPE: return "bad shape";
+        case FP8KV_E_STRIDE: return "bad stride";
+        case FP8KV_E_ALIGN: return "misaligned pointer or stride";
+        case FP8KV_E_UNSUPPORTED: return "unsupported combination";
+        case FP8KV_E_WORKSPACE: return "workspace too small";
+        case FP8KV_E_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+const char* fp8kv_last_error(void) { return g_last_error; }
+
+int fp8kv_kv_quant_scatter(
+    const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+    const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+    int32_t in_dtype, int32_t num_tokens, int32_t num_kv_heads,
+    int32_t head_dim, const int64_t* slot_ids, uint8_t* k_cache,
+    uint8_t* v_cache, int64_t cache_stride_slot, int64_t cache_stride_head,
+    float* k_scale, float* v_scale, int64_t scale_stride_slot,
+    int64_t scale_stride_head, int64_t num_slots, void* stream) {
+    if (in_dtype != FP8KV_DTYPE_BF16)
+        return fail(FP8KV_E_UNSUPPORTED, "in_dtype %d: only BF16 K/V inputs", in_dtype);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(FP8KV_E_UNSUPPORTED, "head_dim %d: only 64 and 128 are supported", head_dim);
+    if (num_tokens < 0 || num_kv_heads < 1 || num_slots < 0)
+        return fail(FP8KV_E_SHAPE, "num_tokens %d, num_kv_heads %d, num_slots %lld",
+                    num_tokens, num_kv_heads, (long long)num_slots);
+    if (!k || !v || !slot_ids || !k_cache || !v_cache || !k_scale || !v_scale)
+        return fail(FP8KV_E_NULL, "kv_quant_scatter: a required pointer is NULL");
+    if (k_stride_tok < 0 || k_stride_head < 0 || v_stride_tok < 0 ||
+        v_stride_head < 0 || cache_stride_slot < 0 || cache_stride_head < 0 ||
+        scale_stride_slot < 0 || scale_stride_head < 0)
+        return fail(FP8KV_E_STRIDE, "kv_quant_scatter: negative stride");
+    // each lane moves head_dim/16 bf16 (8 or 16 bytes) and writes
+    // head_dim/16 codes; rows must start on those boundaries
+    const int64_t in_vec = head_dim / 16;
+    if (!aligned(k, in_vec * 2) || !aligned(v, in_vec * 2) ||
+        k_stride_tok % in_vec || k_stride_head % in_vec ||
+        v_stride_tok % in_vec || v_stride_head % in_vec)
+        return fail(FP8KV_E_ALIGN, "K/V rows must start on %lld-byte boundaries",
+                    (long long)(in_vec * 2));
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        cache_stride_slot % 16 || cache_stride_head % 16)
+        return fail(FP8KV_E_ALIGN, "cache rows must start on 16-byte boundaries");
+    if (!aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(slot_ids, 8))
+        return fail(FP8KV_E_ALIGN, "scale planes / slot ids misaligned");
+    if (num_tokens == 0) return ok();
+
+    fp8kv::QuantScatterParams p;
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.k_stride_tok = k_stride_tok;
+    p.k_stride_head = k_stride_head;
+    p.v_stride_tok = v_stride_tok;
+    p.v_stride_head = v_stride_head;
+    p.slot_ids = slot_ids;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.cache_stride_slot = cache_stride_slot;
+    p.cache_stride_head = cache_stride_head;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.scale_stride_slot = scale_stride_slot;
+    p.scale_stride_head = scale_stride_head;
+    p.num_slots = num_slots;
+    p.num_tokens = num_tokens;
+    p.num_kv_heads = num_kv_heads;
+    p.num_rows = (int64_t)num_tokens * num_kv_heads * 2;
+    return launched(fp8kv::launch_kv_quant_scatter(p, head_dim, (hipStream_t)stream),
+                    "kv_quant_scatter");
+}
+
+int64_t fp8kv_paged_decode_workspace_bytes(
+    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_context,
+    int32_t partition_tokens) {
+    DecodeShape s;
+    int st = decode_shape(batch, rows, num_q_heads, num_kv_heads, head_dim,
+                          block_size, max_context, partition_tokens, &s);
+    if (st != FP8KV_OK) return st;
+    return s.ws_bytes;
+}
+
+int32_t fp8kv_paged_decode_partition_tokens(
+    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_context,
+    int32_t partition_tokens) {
+    DecodeShape s;
+    int st = decode_shape(batch, rows, num_q_heads, num_kv_heads, head_dim,
+                          block_size, max_context, partition_tokens, &s);
+    if (st != FP8KV_OK) return st;
+    return s.partition;
+}
+
+int fp8kv_paged_decode_partials(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype, const uint8_t* k_cache,
+    const uint8_t* v_cache, int64_t cache_stride_slot,
+    int64_t cache_stride_head, const float* k_scale, const float* v_scale,
+    int64_t scale_stride_slot, int64_t scale_stride_head, int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, int32_t batch, int32_t rows,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float softmax_scale, int32_t partition_tokens,
+    int32_t max_context, void* workspace, size_t workspace_bytes,
+    void* stream) {
+    DecodeShape s;
+    int st = decode_shape(batch, rows, num_q_heads, num_kv_heads, head_dim,
+                          block_size, max_context, partition_tokens, &s);
+    if (st != FP8KV_OK) return st;
+    if (q_dtype != FP8KV_DTYPE_BF16)
+        return fail(FP8KV_E_UNSUPPORTED, "q_dtype %d: only BF16 queries", q_dtype);
+    if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables ||
+        !context_lens)
+        return fail(FP8KV_E_NULL, "paged_decode: a required pointer is NULL");
+    if (!workspace && s.ws_bytes > 0)
+        return fail(FP8KV_E_WORKSPACE, "paged_decode: workspace is NULL");
+    if ((int64_t)workspace_bytes < s.ws_bytes)
+        return fail(FP8KV_E_WORKSPACE, "workspace %zu bytes < required %lld",
+                    workspace_bytes, (long long)s.ws_bytes);
+    if (q_stride_b < 0 || q_stride_row < 0 || q_stride_head < 0 ||
+        cache_stride_slot < 0 || cache_stride_head < 0 ||
+        scale_stride_slot < 0 || scale_stride_head < 0 ||
+        block_table_stride < 0)
+        return fail(FP8KV_E_STRIDE, "paged_decode: negative stride");
+    if (!aligned(q, 16) || q_stride_b % 8 || q_stride_row % 8 || q_stride_head % 8)
+        return fail(FP8KV_E_ALIGN, "q rows must start on 16-byte boundaries");
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        cache_stride_slot % 16 || cache_stride_head % 16)
+        return fail(FP8KV_E_ALIGN, "cache rows must start on 16-byte boundaries");
+    if (!aligned(k_scale, 4) || !aligned(v_scale, 4) ||
+        !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
+        (workspace && !aligned(workspace, 256)))
+        return fail(FP8KV_E_ALIGN, "scale planes, tables or workspace misaligned");
+    const int64_t num_blocks = num_slots / block_size;
+    if (batch > 0 && max_context > 0 && num_blocks < 1)
+        return fail(FP8KV_E_SHAPE, "num_slots %lld holds no block of %d",
+                    (long long)num_slots, block_size);
+    if (num_blocks > INT32_MAX)
+        return fail(FP8KV_E_SHAPE, "num_slots / block_size exceeds int32 block ids");
+    if (batch == 0 || s.num_partitions == 0) return ok();
+
+    // float4 scale loads when one head's scales are contiguous per slot
+    const bool scale_contig = scale_stride_slot == 1 && aligned(k_scale, 16) &&
+                              aligned(v_scale, 16) && scale_stride_head % 4 == 0;
+    fp8kv::DecodeParams p;
+    p.q = static_cast<const uint16_t*>(q);
+    p.q_stride_b = q_stride_b;
+    p.q_stride_row = q_stride_row;
+    p.q_stride_head = q_stride_head;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.cache_stride_slot = cache_stride_slot;
+    p.cache_stride_head = cache_stride_head;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.scale_stride_slot = scale_stride_slot;
+    p.scale_stride_head = scale_stride_head;
+    p.block_tables = block_tables;
+    p.block_table_stride = block_table_stride;
+    p.context_lens = context_lens;
+    p.batch = batch;
+    p.rows = rows;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = s.group;
+    p.m_rows = s.m_rows;
+    p.block_size = block_size;
+    p.partition = s.partition;
+    p.num_partitions = s.num_partitions;
+    p.max_context = max_context;
+    p.num_blocks = (int32_t)num_blocks;
+    const int64_t pairs = (int64_t)batch * s.num_partitions;
+    p.pairs_padded = (int32_t)round_up(pairs, 8);
+    if ((int64_t)p.pairs_padded * num_kv_heads > INT32_MAX)
+        return fail(FP8KV_E_SHAPE, "too many (request, partition, head) units");
+    p.score_scale_log2 = softmax_scale * 1.4426950408889634f;
+    p.ws_o = static_cast<float*>(workspace);
+    p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + s.lse_offset_bytes);
+    return launched(fp8kv::launch_decode_partitions(p, head_dim, scale_contig,
+                                                    (hipStream_t)stream),
+                    "paged_decode_partials");
+}
+
+int fp8kv_paged_decode_merge(
+    const int32_t* context_lens, int32_t batch, int32_t rows,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t partition_tokens, int32_t max_context,
+    const void* workspace, size_t workspace_bytes, void* out,
+    int64_t out_stride_b, int64_t out_stride_row, int64_t out_stride_head,
+    int32_t out_dtype, void* stream) {
+    DecodeShape s;
+    int st = decode_shape(batch, rows, num_q_heads, num_kv_heads, head_dim,
+                          block_size, max_context, partition_tokens, &s);
+    if (st != FP8KV_OK) return st;
+    if ((st = check_out_dtype(out_dtype)) != FP8KV_OK) return st;
+    if (!context_lens || !out)
+        return fail(FP8KV_E_NULL, "paged_decode_merge: a required pointer is NULL");
+    if (!workspace && s.ws_bytes > 0)
+        return fail(FP8KV_E_WORKSPACE, "paged_decode_merge: workspace is NULL");
+    if ((int64_t)workspace_bytes < s.ws_bytes)
+        return fail(FP8KV_E_WORKSPACE, "workspace %zu bytes < required %lld",
+                    workspace_bytes, (long long)s.ws_bytes);
+    if (out_stride_b < 0 || out_stride_row < 0 || out_stride_head < 0)
+        return fail(FP8KV_E_STRIDE, "paged_decode_merge: negative stride");
+    const int esz = out_dtype == FP8KV_DTYPE_FP32 ? 4 : 2;
+    if (!aligned(out, esz) || !aligned(context_lens, 4) ||
+        (workspace && !aligned(workspace, 256)))
+        return fail(FP8KV_E_ALIGN, "out, context_lens or workspace misaligned");
+    if (batch == 0) return ok();
+    fp8kv::MergeParams p;
+    p.context_lens = context_lens;
+    p.ws_o = static_cast<const float*>(workspace);
+    p.ws_lse = workspace ? reinterpret_cast<const float*>(
+                               static_cast<const char*>(workspace) + s.lse_offset_bytes)
+                         : nullptr;
+    p.out = out;
+    p.out_stride_b = out_stride_b;
+    p.out_stride_row = out_stride_row;
+    p.out_stride_head = out_stride_head;
+    p.out_fp32 = out_dtype == FP8KV_DTYPE_FP32;
+    p.batch = batch;
+    p.num_kv_heads = num_kv_heads;
+    p.group = s.group;
+    p.m_rows = s.m_rows;
+    p.partition = s.partition;
+    p.num_partitions = s.num_partitions;
+    p.max_context = max_context;
+    p.total_rows = batch * num_kv_heads * s.m_rows;
+    return launched(fp8kv::launch_decode_merge(p, head_dim, (hipStream_t)stream),
+                    "paged_decode_merge");
+}
+
+int fp8kv_paged_decode_attn_fp8(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype, const uint8_t* k_cache,
+    const uint8_t* v_cache, int64_t cache_stride_slot,
+    int64_t cache_stride_head, const float* k_scale, const float* v_scale,
+    int64_t scale_stride_slot, int64_t scale_stride_head, int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, int32_t batch, int32_t rows,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float softmax_scale, int32_t partition_tokens,
+    int32_t max_context, void* workspace, size_t workspace_bytes, void* out,
+    int64_t out_stride_b, int64_t out_stride_row, int64_t out_stride_head,
+    int32_t out_dtype, void* stream) {
+    // validate everything before enqueueing anything
+    int st = check_out_dtype(out_dtype);
+    if (st != FP8KV_OK) return st;
+    if (!out) return fail(FP8KV_E_NULL, "paged_decode: out is NULL");
+    if (out_stride_b < 0 || out_stride_row < 0 || out_stride_head < 0)
+        return fail(FP8KV_E_STRIDE, "paged_decode: negative out stride");
+    if (!aligned(out, out_dtype == FP8KV_DTYPE_FP32 ? 4 : 2))
+        return fail(FP8KV_E_ALIGN, "out misaligned");
+    st = fp8kv_paged_decode_partials(
+        q, q_stride_b, q_stride_row, q_stride_head, q_dtype, k_cache, v_cache,
+        cache_stride_slot, cache_stride_head, k_scale, v_scale,
+        scale_stride_slot, scale_stride_head, num_slots, block_tables,
+        block_table_stride, context_lens, batch, rows, num_q_heads,
+        num_kv_heads, head_dim, block_size, softmax_scale, partition_tokens,
+        max_context, workspace, workspace_bytes, stream);
+    if (st != FP8KV_OK) return st;
+    return fp8kv_paged_decode_merge(
+        context_lens, batch, rows, num_q_heads, num_kv_heads, head_dim,
+        block_size, partition_tokens, max_context, workspace, workspace_bytes,
+        out, out_stride_b, out_stride_row, out_stride_head, out_dtype, stream);
+}
+
+}  // extern "C"

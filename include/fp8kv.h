@@ -1,0 +1,243 @@
+/*
+ * fp8kv.h -- C ABI of the MI355X (gfx950) FP8 E4M3 paged KV cache library
+ * (libfp8kv.so).
+ *
+ * The cache format ("feat(kvcache): store the KV cache as fp8 e4m3 codes",
+ * FreeToken #354, description; "fix(qwen4-exp): register the QSA FP8 scale
+ * planes for KV offload", ROCm/ATOM #2655, description, K/V bullet):
+ *   - every (token, KV head) row of K, and separately of V, is head_dim
+ *     OCP E4M3FN codes (max 448) kept in a plain uint8 buffer that has the
+ *     geometry of the 16-bit cache -- only the element type changes;
+ *   - plus ONE fp32 symmetric scale per row, scale = row amax / 448, held in
+ *     a separate fp32 "scale plane" per cache (k_scale, v_scale). Anything
+ *     that moves codes must move both planes with them.
+ *
+ * Conventions shared by every call:
+ *   - Pointers marked (device) are device memory owned by the caller. The
+ *     library never allocates, frees, synchronizes or reads device memory
+ *     from the host; every call only enqueues kernels on `stream` (a
+ *     hipStream_t passed as void*, NULL = the default stream), so every call
+ *     may be captured into a HIP graph.
+ *   - Strides are in ELEMENTS of the pointed-to type. The innermost
+ *     (head_dim) stride is always 1; every other stride is free, and K and V
+ *     inputs carry their OWN strides (the FreeToken V-pitch fix: a K view of
+ *     a fused qkv slice and a densely materialized V have different row
+ *     pitches and must each be read at their own).
+ *   - The compute dtype (what q, K/V inputs and outputs are) is an argument;
+ *     the store dtype is always E4M3 in uint8 (FreeToken #354, description:
+ *     pool.dtype vs pool.store_dtype).
+ *   - Unsupported combinations are refused with a status, never ignored
+ *     (FreeToken #354, description: fp8 is refused at startup where the row
+ *     scales cannot be applied). Functions return FP8KV_OK (0) or a negative
+ *     fp8kv_status and never abort or throw across the ABI. On failure
+ *     nothing has been enqueued, except for FP8KV_E_LAUNCH.
+ *   - Checks are host-side and O(1): sizes, strides, alignment, dtypes.
+ *     Device-resident ids (slot ids, block tables, context lengths) are not
+ *     read by the host; the kernels bound every id they use (see each call)
+ *     so a bad id never reads or writes outside the buffers described by the
+ *     arguments.
+ *   - fp8kv_last_error() returns a thread-local description of the most
+ *     recent failure on the calling thread.
+ */
+#ifndef FP8KV_H
+#define FP8KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8KV_ABI_VERSION 1
+
+typedef enum fp8kv_status {
+    FP8KV_OK = 0,
+    FP8KV_E_NULL = -1,         /* a required pointer is NULL                */
+    FP8KV_E_SHAPE = -2,        /* a size is out of range or inconsistent    */
+    FP8KV_E_STRIDE = -3,       /* an inner stride is not 1, or a stride is  */
+                               /* negative                                  */
+    FP8KV_E_ALIGN = -4,        /* a pointer or stride breaks the alignment  */
+                               /* the vector loads/stores need              */
+    FP8KV_E_UNSUPPORTED = -5,  /* dtype / head_dim / grouping not supported */
+    FP8KV_E_WORKSPACE = -6,    /* workspace NULL or smaller than required   */
+    FP8KV_E_LAUNCH = -7        /* the HIP runtime reported a launch error   */
+} fp8kv_status;
+
+typedef enum fp8kv_dtype {
+    FP8KV_DTYPE_BF16 = 1,
+    FP8KV_DTYPE_FP16 = 2,
+    FP8KV_DTYPE_FP32 = 3
+} fp8kv_dtype;
+
+int fp8kv_abi_version(void);
+const char* fp8kv_status_string(int status);
+const char* fp8kv_last_error(void);
+
+/*
+ * fp8kv_kv_quant_scatter -- quantize K and V rows to E4M3 + fp32 row scales
+ * and scatter them to cache slots, K and V in ONE launch (ATOM #2655,
+ * description, K/V bullet; FreeToken #354, description: one launch under
+ * graph capture with the slot ids arriving as a device tensor).
+ *
+ * For every token t < num_tokens, KV head h < num_kv_heads and each of K, V:
+ *   x[d]   = input[t * stride_tok + h * stride_head + d], d < head_dim
+ *   s      = fp32(max_d |x[d]| / 448)                (IEEE division)
+ *   c[d]   = E4M3(fp32(x[d] / s)) round-to-nearest-even, saturating;
+ *            when s == 0 (all-zero row) c[d] = E4M3(x[d]) = +-0
+ *   cache[slot * cache_stride_slot + h * cache_stride_head + d] = c[d]
+ *   scale[slot * scale_stride_slot + h * scale_stride_head]      = s
+ * with slot = slot_ids[t]. A slot id < 0 (padding) or >= num_slots writes
+ * nothing for that token. Two tokens with the same slot id race (undefined
+ * which row lands).
+ *
+ * k, v        (device) inputs of dtype in_dtype (FP8KV_DTYPE_BF16 only),
+ *             element (t, h, d) at t*stride_tok + h*stride_head + d. Each
+ *             row starts on a head_dim/8-byte boundary (16 bytes at 128, 8
+ *             at 64): pointer and strides multiples of head_dim/16 elements.
+ * slot_ids    (device) int64[num_tokens].
+ * k_cache, v_cache (device) uint8 code buffers sharing the cache strides;
+ *             pointers and cache strides multiples of 16 bytes.
+ * k_scale, v_scale (device) fp32 scale planes sharing the scale strides.
+ * head_dim    64 or 128. num_tokens may be 0 (nothing is launched).
+ * Errors: E_NULL, E_SHAPE, E_STRIDE, E_ALIGN, E_UNSUPPORTED, E_LAUNCH.
+ */
+int fp8kv_kv_quant_scatter(
+    const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+    const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+    int32_t in_dtype, int32_t num_tokens, int32_t num_kv_heads,
+    int32_t head_dim,
+    const int64_t* slot_ids,
+    uint8_t* k_cache, uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head,
+    float* k_scale, float* v_scale,
+    int64_t scale_stride_slot, int64_t scale_stride_head,
+    int64_t num_slots, void* stream);
+
+/*
+ * Paged GQA decode attention over the E4M3 cache (ATOM #2655, description,
+ * K/V bullet: the attend reads E4M3 tiles, multiplies the key scale into
+ * its score column and folds the value scale into the probability before
+ * PV; sglang-jax #1776, "Modifications": K/V tiles are widened to the query
+ * dtype before the score dot and the probabilities are never rounded to the
+ * cache dtype).
+ *
+ * Rows: request b < batch, verify row r < rows, query head hq < num_q_heads.
+ * G = num_q_heads / num_kv_heads; query head hq reads KV head hq / G. With
+ * L = min(context_lens[b], max_context), row r sees cache tokens
+ * 0 .. L - rows + r (the rows are causal among themselves; rows == 1 sees
+ * all L). Token j of request b lives in slot
+ *     block_tables[b * block_table_stride + j / block_size] * block_size
+ *     + j % block_size.
+ *   score_j = (q . dec(k_code_j)) * k_scale_j * softmax_scale
+ *   out     = sum_j softmax(score)_j * v_scale_j * dec(v_code_j)
+ * A row that sees no token gets out = 0.
+ *
+ * The keys are split into partitions of partition_tokens tokens (a
+ * positive multiple of 32; 0 lets the library choose); each (request, KV
+ * head, partition) is reduced to a partial (normalized output, log2
+ * log-sum-exp) in the workspace, and the partials are merged by
+ * log-sum-exp. The grid is sized from the host-known max_context, so the
+ * launch is graph-capturable with any context_lens <= max_context.
+ *
+ * q           (device) FP8KV_DTYPE_BF16, element (b, r, hq, d) at
+ *             b*q_stride_b + r*q_stride_row + hq*q_stride_head + d;
+ *             16-byte aligned rows.
+ * k_cache, v_cache, k_scale, v_scale  (device) as written by
+ *             fp8kv_kv_quant_scatter; num_slots bounds every slot used.
+ *             Pointers and cache strides multiples of 16 bytes.
+ * block_tables (device) int32; context_lens (device) int32[batch].
+ * Bounding: block ids are clamped into [0, num_slots / block_size) and
+ *             context lengths into [0, max_context] before use, so
+ *             invalid ids read wrong rows, never out-of-bounds memory.
+ * head_dim 64 or 128; block_size a multiple of 16; rows * G <= 16;
+ * num_q_heads % num_kv_heads == 0.
+ * out         (device) dtype out_dtype (BF16, round-to-nearest-even, or
+ *             FP32), element (b, r, hq, d) at b*out_stride_b +
+ *             r*out_stride_row + hq*out_stride_head + d.
+ * workspace   (device) at least fp8kv_paged_decode_workspace_bytes(...)
+ *             bytes, 256-byte aligned; no initialization needed.
+ * Errors: E_NULL, E_SHAPE, E_STRIDE, E_ALIGN, E_UNSUPPORTED, E_WORKSPACE,
+ *         E_LAUNCH.
+ */
+int fp8kv_paged_decode_attn_fp8(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype,
+    const uint8_t* k_cache, const uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head,
+    const float* k_scale, const float* v_scale,
+    int64_t scale_stride_slot, int64_t scale_stride_head,
+    int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens,
+    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, float softmax_scale,
+    int32_t partition_tokens, int32_t max_context,
+    void* workspace, size_t workspace_bytes,
+    void* out, int64_t out_stride_b, int64_t out_stride_row,
+    int64_t out_stride_head, int32_t out_dtype,
+    void* stream);
+
+/*
+ * Workspace bytes fp8kv_paged_decode_attn_fp8 / _partials / _merge need for
+ * these sizes (same partition_tokens rule: 0 = library choice). Returns a
+ * negative fp8kv_status for an unsupported combination.
+ *
+ * Layout (so that partials computed on several devices can be gathered and
+ * merged -- the context-parallel use): with NP = ceil(max_context /
+ * partition), M = rows * G, row m = r * G + (hq % G), the first
+ * batch*Hkv*NP*M*head_dim floats are the normalized partial outputs
+ * o[((b*Hkv + h)*NP + p)*M + m][d], followed by batch*Hkv*NP*M floats of
+ * log2-domain log-sum-exp lse[((b*Hkv + h)*NP + p)*M + m] (-inf when the
+ * partition holds no visible token of the row).
+ */
+int64_t fp8kv_paged_decode_workspace_bytes(
+    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_context,
+    int32_t partition_tokens);
+
+/* The partition used for these sizes (resolves partition_tokens == 0), or a
+ * negative fp8kv_status. */
+int32_t fp8kv_paged_decode_partition_tokens(
+    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_context,
+    int32_t partition_tokens);
+
+/*
+ * The two phases of fp8kv_paged_decode_attn_fp8, callable separately: the
+ * partition phase (page walk, KV streaming, scores, online softmax, PV,
+ * partials to the workspace) and the log-sum-exp merge of the partials into
+ * `out`. Same arguments and rules as the fused call; the merge reads only
+ * context_lens and the workspace. Running _partials then _merge on one
+ * stream equals one fp8kv_paged_decode_attn_fp8 call bit for bit.
+ */
+int fp8kv_paged_decode_partials(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype,
+    const uint8_t* k_cache, const uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head,
+    const float* k_scale, const float* v_scale,
+    int64_t scale_stride_slot, int64_t scale_stride_head,
+    int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens,
+    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, float softmax_scale,
+    int32_t partition_tokens, int32_t max_context,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+int fp8kv_paged_decode_merge(
+    const int32_t* context_lens,
+    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t partition_tokens,
+    int32_t max_context,
+    const void* workspace, size_t workspace_bytes,
+    void* out, int64_t out_stride_b, int64_t out_stride_row,
+    int64_t out_stride_head, int32_t out_dtype,
+    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8KV_H */

@@ -58,6 +58,14 @@ void fo_attend_dense(const double* q, const double* keys, const double* vals,
     free(s);
 }
 
+/* fo_decode of every code, tabulated once when the library loads. */
+static double g_value[2][256];
+
+__attribute__((constructor)) static void build_value_tables(void) {
+    for (int fmt = 0; fmt < 2; ++fmt)
+        for (unsigned c = 0; c < 256; ++c) g_value[fmt][c] = fo_decode(fmt, c);
+}
+
 /* One key or value row of the cache, dequantized into dst[0..D). */
 static void dequant_row(int fmt, const uint8_t* cache, const float* scales,
                         int64_t slot, int64_t h, int64_t cache_stride_slot,
@@ -66,7 +74,7 @@ static void dequant_row(int fmt, const uint8_t* cache, const float* scales,
     const uint8_t* c = cache + slot * cache_stride_slot + h * cache_stride_head;
     const double s =
         (double)scales[slot * scale_stride_slot + h * scale_stride_head];
-    for (int64_t d = 0; d < D; ++d) dst[d] = fo_decode(fmt, c[d]) * s;
+    for (int64_t d = 0; d < D; ++d) dst[d] = g_value[fmt][c[d]] * s;
 }
 
 /* Reduce keys [j0, j1) of a gathered row set to (max, sum, weighted sum). */

@@ -1,0 +1,172 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+* libfp8kv.so loads and exports every function include/fp8kv.h declares;
+* each refusal the header documents comes back as its status code, with a
+  message, before anything is enqueued (FreeToken #354: unsupported fp8
+  combinations are refused, not ignored; its review thread: bounds are
+  checked on the host where the host can check them);
+* the workspace size follows the documented layout.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8kv.h")
+
+OK, E_NULL, E_SHAPE, E_STRIDE, E_ALIGN, E_UNSUPPORTED, E_WORKSPACE, E_LAUNCH = \
+    0, -1, -2, -3, -4, -5, -6, -7
+BF16, FP16, FP32 = 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def L():
+    import fp8_e4m3_paged_kv_amd as pkg
+    if not os.path.exists(pkg.LIB_PATH):
+        from fp8_e4m3_paged_kv_amd import build
+        build.build()
+    return pkg.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8kv_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_strings(L):
+    text = open(HEADER).read()
+    ver = int(re.search(r"#define FP8KV_ABI_VERSION (\d+)", text).group(1))
+    assert L.fp8kv_abi_version() == ver
+    for st in (OK, E_NULL, E_SHAPE, E_STRIDE, E_ALIGN, E_UNSUPPORTED,
+               E_WORKSPACE, E_LAUNCH):
+        assert L.fp8kv_status_string(st).decode() != "unknown status"
+
+
+# A fake, well-aligned "device" address: validation never dereferences it.
+A = 1 << 40
+
+
+def qs(L, **kw):
+    a = dict(k=A, kst=6144, ksh=128, v=A + 8192, vst=6144, vsh=128,
+             dtype=BF16, T=16, H=8, D=128, slots=A, kc=A, vc=A, css=1024,
+             csh=128, ks=A, vs=A, sss=8, ssh=1, S=1 << 20)
+    a.update(kw)
+    return L.fp8kv_kv_quant_scatter(
+        a["k"], a["kst"], a["ksh"], a["v"], a["vst"], a["vsh"], a["dtype"],
+        a["T"], a["H"], a["D"], a["slots"], a["kc"], a["vc"], a["css"],
+        a["csh"], a["ks"], a["vs"], a["sss"], a["ssh"], a["S"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=FP16), E_UNSUPPORTED),
+    (dict(dtype=FP32), E_UNSUPPORTED),
+    (dict(D=96), E_UNSUPPORTED),
+    (dict(D=256), E_UNSUPPORTED),
+    (dict(T=-1), E_SHAPE),
+    (dict(H=0), E_SHAPE),
+    (dict(k=0), E_NULL),
+    (dict(slots=0), E_NULL),
+    (dict(vs=0), E_NULL),
+    (dict(vst=-384), E_STRIDE),
+    (dict(k=A + 2), E_ALIGN),
+    (dict(vst=6140), E_ALIGN),
+    (dict(kc=A + 8), E_ALIGN),
+    (dict(css=1000), E_ALIGN),
+    (dict(slots=A + 4), E_ALIGN),
+    (dict(T=0), OK),                     # nothing to do: nothing launched
+])
+def test_quant_scatter_refusals(L, kw, status):
+    assert qs(L, **kw) == status
+    if status != OK:
+        assert L.fp8kv_last_error().decode()
+
+
+def dec(L, fn="fp8kv_paged_decode_attn_fp8", **kw):
+    a = dict(q=A, qsb=4096, qsr=4096, qsh=128, qdt=BF16, kc=A, vc=A,
+             css=1024, csh=128, ks=A, vs=A, sss=1, ssh=1 << 20, S=1 << 20,
+             bt=A, bts=2048, cl=A, B=64, R=1, Hq=32, H=8, D=128, bs=16,
+             scale=0.088, P=0, maxc=32768, ws=A, wsb=1 << 34, out=A,
+             osb=4096, osr=4096, osh=128, odt=BF16)
+    a.update(kw)
+    common = [a["q"], a["qsb"], a["qsr"], a["qsh"], a["qdt"], a["kc"],
+              a["vc"], a["css"], a["csh"], a["ks"], a["vs"], a["sss"],
+              a["ssh"], a["S"], a["bt"], a["bts"], a["cl"], a["B"], a["R"],
+              a["Hq"], a["H"], a["D"], a["bs"], ctypes.c_float(a["scale"]),
+              a["P"], a["maxc"], a["ws"], a["wsb"]]
+    if fn == "fp8kv_paged_decode_partials":
+        return getattr(L, fn)(*common, None)
+    return getattr(L, fn)(*common, a["out"], a["osb"], a["osr"], a["osh"],
+                          a["odt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qdt=FP16), E_UNSUPPORTED),
+    (dict(odt=FP16), E_UNSUPPORTED),
+    (dict(D=96), E_UNSUPPORTED),
+    (dict(Hq=30), E_SHAPE),              # not a multiple of Hkv
+    (dict(R=5), E_UNSUPPORTED),          # 5 * 4 > 16 stacked rows
+    (dict(Hq=64, H=2), E_UNSUPPORTED),   # group 32 > 16
+    (dict(bs=8), E_UNSUPPORTED),
+    (dict(bs=24), E_UNSUPPORTED),
+    (dict(P=48), E_SHAPE),
+    (dict(P=-32), E_SHAPE),
+    (dict(B=-1), E_SHAPE),
+    (dict(q=0), E_NULL),
+    (dict(bt=0), E_NULL),
+    (dict(out=0), E_NULL),
+    (dict(ws=0), E_WORKSPACE),
+    (dict(wsb=1024), E_WORKSPACE),
+    (dict(css=-1024), E_STRIDE),
+    (dict(q=A + 8), E_ALIGN),
+    (dict(qsh=100), E_ALIGN),
+    (dict(css=1000), E_ALIGN),
+    (dict(ws=A + 64), E_ALIGN),
+    (dict(S=8), E_SHAPE),                # no whole block in the pool
+])
+def test_decode_refusals(L, kw, status):
+    assert dec(L, **kw) == status
+    assert L.fp8kv_last_error().decode()
+
+
+def test_partials_refusals(L):
+    assert dec(L, fn="fp8kv_paged_decode_partials", qdt=FP32) == E_UNSUPPORTED
+    assert dec(L, fn="fp8kv_paged_decode_partials", wsb=16) == E_WORKSPACE
+
+
+def test_workspace_layout(L):
+    B, R, Hq, H, D, bs, maxc, P = 64, 1, 32, 8, 128, 16, 32768, 1024
+    n = L.fp8kv_paged_decode_workspace_bytes(B, R, Hq, H, D, bs, maxc, P)
+    NP, M = maxc // P, R * Hq // H
+    units = B * H * NP * M
+    rnd = lambda x: (x + 255) // 256 * 256
+    assert n == rnd(units * D * 4) + rnd(units * 4)
+    assert L.fp8kv_paged_decode_workspace_bytes(B, R, Hq, H, 96, bs, maxc, P) == E_UNSUPPORTED
+
+
+def test_partition_choice(L):
+    f = L.fp8kv_paged_decode_partition_tokens
+    assert f(4, 4, 16, 4, 128, 64, 1 << 20, 8192) == 8192
+    assert f(4, 4, 16, 4, 128, 64, 1 << 20, 0) % 32 == 0
+    assert f(2, 1, 4, 2, 64, 16, 100, 0) % 32 == 0
+    assert f(2, 1, 4, 2, 64, 16, 100, 40) == E_SHAPE
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    import fp8_e4m3_paged_kv_amd as fk
+    k = torch.zeros((4, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fk.kv_quant_scatter(k, k, torch.zeros(4, dtype=torch.int64),
+                            torch.zeros((16, 2, 64), dtype=torch.uint8),
+                            torch.zeros((16, 2, 64), dtype=torch.uint8),
+                            torch.zeros((16, 2)), torch.zeros((16, 2)))

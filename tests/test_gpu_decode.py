@@ -1,0 +1,205 @@
+"""GPU parity of fp8kv_paged_decode_attn_fp8 against the oracle run on the
+same dequantized cache (the cache itself written by the GPU quantizer).
+
+Bar: fp32 output within max-abs 2e-3 and rel-L2 1e-3 of the oracle; bf16
+output equal, bit for bit, to the round-to-nearest-even of the same
+kernel's fp32 output (same partitioning)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_e4m3_paged_kv_amd as fk
+from fp8_e4m3_paged_kv_amd import synth
+
+from gpu_cases import (DevCache, assert_attn_close, attn_errors, bf16_rne,
+                       cache_case, compact_host_cache, log, oracle_decode,
+                       run_decode)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def check_case(case, partition=0, layout="head_major", also_bf16=True,
+               max_context=None):
+    log(f"decode {case.name}: lens={case.layout.context_lens.tolist()[:6]} "
+        f"R={case.rows} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
+        f"D={case.head_dim} bs={case.layout.block_size} P={partition} {layout}")
+    dc = cache_case(case, DEV, layout)
+    out = run_decode(case, dc, partition=partition, max_context=max_context)
+    torch.cuda.synchronize()
+    ref = oracle_decode(case, dc.host())
+    assert_attn_close(out.cpu().numpy(), ref, case.name)
+    if also_bf16:
+        ob = run_decode(case, dc, partition=partition, out_dtype=torch.bfloat16,
+                        max_context=max_context)
+        torch.cuda.synchronize()
+        assert torch.equal(ob, bf16_rne(out)), "bf16 output is not RNE of fp32"
+    return dc, out, ref
+
+
+def test_tiny_case():
+    case = synth.tiny_case(0)
+    check_case(case)
+
+
+@pytest.mark.parametrize("partition", [0, 32, 64, 256])
+def test_ragged_lengths_many_partitions(partition):
+    case = synth.decode_case([1, 31, 33, 1000, 5000, 77], 8, 2, 128, 16,
+                             rows=1, seed=3)
+    check_case(case, partition=partition)
+
+
+@pytest.mark.parametrize("layout", ["head_major", "slot_major"])
+@pytest.mark.parametrize("bs", [16, 32, 64, 128])
+def test_block_sizes_and_scale_layouts(bs, layout):
+    case = synth.decode_case([300, 1290, 64], 8, 4, 128, bs, rows=1, seed=bs)
+    check_case(case, partition=256, layout=layout)
+
+
+def test_head_dim_64():
+    case = synth.decode_case([700, 129, 2], 16, 4, 64, 16, rows=2, seed=6)
+    check_case(case, partition=128)
+
+
+@pytest.mark.parametrize("partition", [1024, 8192])
+def test_verify_rows_causal(partition):
+    """4 verify rows x 4 query heads stacked into the 16-row tile; request
+    lengths include one shorter than the row count (row 0 sees nothing)."""
+    case = synth.decode_case([3, 4, 2000, 9000], 16, 4, 128, 64, rows=4,
+                             seed=12, k_outlier_frac=0.005)
+    _, out, _ = check_case(case, partition=partition)
+    assert torch.all(out[0, 0] == 0)
+
+
+def test_outliers_and_zero_rows():
+    case = synth.decode_case([500, 2048], 8, 2, 128, 16, rows=1, seed=21)
+    k = case.k.float()
+    v = case.v.float()
+    k[5] = 0.0
+    v[6] = 0.0
+    k[100, 1, 7] = 3000.0
+    v[101, 0, 9] = -5000.0
+    v[200:260] *= 1e-3
+    case.k, case.v = k.to(torch.bfloat16), v.to(torch.bfloat16)
+    check_case(case, partition=512)
+
+
+def test_empty_contexts_and_zero_max_context():
+    case = synth.decode_case([0, 40, 0], 8, 2, 128, 16, rows=1, seed=2)
+    dc, out, _ = check_case(case, partition=64)
+    assert torch.all(out[0] == 0) and torch.all(out[2] == 0)
+    out0 = run_decode(case, dc, max_context=0)
+    torch.cuda.synchronize()
+    assert torch.all(out0 == 0)
+
+
+def test_context_lens_above_max_context_are_clamped():
+    case = synth.decode_case([900, 600], 8, 2, 128, 16, rows=1, seed=4)
+    dc = cache_case(case, DEV)
+    out = run_decode(case, dc, max_context=512, partition=128)
+    torch.cuda.synchronize()
+    clamped = torch.tensor([512, 512], dtype=torch.int32)
+    ref = oracle_decode(case, dc.host(), context_lens=clamped.numpy())
+    assert_attn_close(out.cpu().numpy(), ref, "clamped")
+
+
+def test_partials_then_merge_equal_fused():
+    case = synth.decode_case([3000, 100, 7777], 16, 4, 128, 16, rows=2, seed=9)
+    dc = cache_case(case, DEV)
+    L = case.layout
+    kw = dict(num_kv_heads=4, block_size=16, softmax_scale=case.softmax_scale,
+              max_context=8000, partition_tokens=512)
+    fused = fk.paged_decode_attn_fp8(case.q.to(DEV), dc.k_cache, dc.v_cache,
+                                     dc.k_scale, dc.v_scale,
+                                     L.block_tables.to(DEV),
+                                     L.context_lens.to(DEV),
+                                     out_dtype=torch.float32, **kw)
+    ws = fk.paged_decode_partials(case.q.to(DEV), dc.k_cache, dc.v_cache,
+                                  dc.k_scale, dc.v_scale,
+                                  L.block_tables.to(DEV),
+                                  L.context_lens.to(DEV), **kw)
+    out = torch.empty_like(fused)
+    fk.paged_decode_merge(ws, L.context_lens.to(DEV), out, rows=2,
+                          num_q_heads=16, num_kv_heads=4, block_size=16,
+                          max_context=8000, partition_tokens=512)
+    torch.cuda.synchronize()
+    assert torch.equal(out, fused)
+
+
+def test_graph_capture_replays_with_new_lengths():
+    case = synth.decode_case([4000, 2500, 333], 8, 2, 128, 16, rows=1, seed=30)
+    dc = cache_case(case, DEV)
+    L = case.layout
+    q = case.q.to(DEV).clone()
+    cl = L.context_lens.to(DEV).clone()
+    bt = L.block_tables.to(DEV)
+    maxc = 4096
+    ws = torch.empty(fk.decode_workspace_bytes(3, 1, 8, 2, 128, 16, maxc, 256),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    kw = dict(num_kv_heads=2, block_size=16, softmax_scale=case.softmax_scale,
+              max_context=maxc, partition_tokens=256, out=out, workspace=ws)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fk.paged_decode_attn_fp8(q, dc.k_cache, dc.v_cache, dc.k_scale,
+                                 dc.v_scale, bt, cl, **kw)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fk.paged_decode_attn_fp8(q, dc.k_cache, dc.v_cache, dc.k_scale,
+                                 dc.v_scale, bt, cl, **kw)
+    host = dc.host()
+    g = synth.gen(31)
+    for rep, lens in enumerate([[4000, 2500, 333], [17, 2400, 333], [3999, 1, 0]]):
+        cl.copy_(torch.tensor(lens, dtype=torch.int32))
+        q.copy_(synth.normal_bf16(q.shape, g))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = oracle_decode(case, host, context_lens=np.array(lens, np.int32),
+                            q=q.cpu())
+        assert_attn_close(out.cpu().numpy(), ref, f"replay {rep}")
+
+
+def test_decode_workload_full_size_sampled():
+    """64 requests, lengths U[1024, 32768], Hq 32 / Hkv 8, D 128, bs 16 --
+    the benchmark's decode launch (library-chosen partition); the oracle
+    recomputes every row of 4 sampled requests."""
+    case = synth.decode_workload(seed=2, device=DEV)
+    dc = cache_case(case, DEV)
+    out = run_decode(case, dc)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(out))
+    sel = [0, 17, 40, 63]
+    host, bt, cl = compact_host_cache(case, dc, sel)
+    sub = synth.DecodeCase("decode-sub", case.layout, None, None,
+                           case.q[sel], 32, 8, 128, 1, case.softmax_scale)
+    ref = oracle_decode(sub, host, block_tables=bt, context_lens=cl,
+                        q=case.q[sel])
+    assert_attn_close(out[sel].cpu().numpy(), ref, "decode sampled")
+
+
+def test_longctx_full_size_sampled():
+    """4 requests of 256K..1M tokens, 4 causal verify rows, Hq 16 / Hkv 4,
+    bs 64, 8192-token partitions: the oracle recomputes sampled rows of the
+    shortest and the longest request."""
+    case = synth.longctx_workload(seed=3, device=DEV)
+    dc = cache_case(case, DEV)
+    out = run_decode(case, dc, partition=case.partition_tokens)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(out))
+    for b, heads in ((0, [0, 5, 15]), (3, [2, 11])):
+        host, bt, cl = compact_host_cache(case, dc, [b])
+        sub = synth.DecodeCase("longctx-sub", case.layout, None, None,
+                               case.q[b:b + 1], 16, 4, 128, 4, case.softmax_scale)
+        rows = [r * 16 + hq for r in range(4) for hq in heads]
+        log(f"  oracle on request {b} ({int(cl[0])} tokens), {len(rows)} rows")
+        ref = oracle_decode(sub, host, rows=rows, block_tables=bt,
+                            context_lens=cl, q=case.q[b:b + 1])
+        got = out[b].reshape(-1, 128)[rows].cpu().numpy()
+        assert_attn_close(got, ref, f"longctx request {b}")
