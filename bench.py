@@ -50,7 +50,26 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the prefill-chunk and long-context extras")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB, 5 times "
+                         "(the known-size reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of a known size: the FETCH_SIZE and
+    WRITE_SIZE counters it produces give the scale from counter units to
+    bytes for the kernels measured with the same counters."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
 
 
 def log(msg):
@@ -106,9 +125,10 @@ def traffic_entry(per_launch_alg_bytes):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(case, dc, lens, max_threads=16, budget_s=20.0):
-    """The oracle (as it stands) on a bounded sample of the same workload:
-    every query row of the first few requests, one request per thread."""
+def cpu_baseline(case, dc, lens, max_threads=16, budget_s=30.0):
+    """The oracle (as it stands) on the same decode workload: every query row
+    of as many of the 64 requests as fit the CPU budget (all of them here),
+    one request per task on the host cores."""
     import numpy as np
     import torch
     import oracle
@@ -118,7 +138,6 @@ def cpu_baseline(case, dc, lens, max_threads=16, budget_s=20.0):
     H, D = case.num_kv_heads, case.head_dim
     NB = dc["k_cache"].shape[0] // bs
     cores = max(1, min(max_threads, os.cpu_count() or 1))
-    nreq = min(len(lens), cores)
 
     def host_request(b):
         nb = (lens[b] + bs - 1) // bs
@@ -131,34 +150,42 @@ def cpu_baseline(case, dc, lens, max_threads=16, budget_s=20.0):
         q = case.q[b:b + 1].contiguous().view(torch.int16).numpy().view(np.uint16)
         return q, kc, vc, kp.T, vp.T, bt, np.array([lens[b]], np.int32)
 
-    inputs = [host_request(b) for b in range(nreq)]
-
     def run(args):
         q, kc, vc, ks, vs, bt, cl = args
         return oracle.paged_decode_attn(q, kc, vc, ks, vs, bt, cl, H, bs,
                                         case.softmax_scale)
 
-    # calibrate: one request alone, then as many in parallel as fit the
-    # budget (each thread runs one request)
+    # estimate the single-core cost from the first request, then take as
+    # many requests as fit the budget of single-core CPU work
+    first = host_request(0)
     t0 = time.perf_counter()
-    run(inputs[0])
-    one = time.perf_counter() - t0
-    n = max(1, min(nreq, int(budget_s / max(one, 1e-3))))
+    run(first)
+    per_token = (time.perf_counter() - t0) / max(lens[0], 1)
+    n, work = 0, 0.0
+    while n < len(lens) and work + per_token * lens[n] <= budget_s:
+        work += per_token * lens[n]
+        n += 1
+    n = max(n, 1)
+    inputs = [first] + [host_request(b) for b in range(1, n)]
     t0 = time.perf_counter()
     with ThreadPoolExecutor(max_workers=min(cores, n)) as ex:
-        list(ex.map(run, inputs[:n]))
+        list(ex.map(run, inputs))
     wall = time.perf_counter() - t0
     tokens = sum(lens[:n])
     alg = tokens * H * 2 * (D + 4)
     return {"value": round(alg / wall / 1e9, 4), "unit": "GB/s",
             "cores": min(cores, n), "kind": "oracle",
-            "sample": f"all {case.num_q_heads} query rows of {n} decode requests "
-                      f"({tokens} cached tokens x {H} KV heads), one request per thread",
+            "sample": f"all {case.num_q_heads} query rows of {n} of the {len(lens)} "
+                      f"decode requests ({tokens} cached tokens x {H} KV heads), "
+                      f"one request per task; ~{work:.1f} s of single-core work",
             "seconds": round(wall, 2)}
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; "
                                    "run with --gpus 1"}))

@@ -23,6 +23,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # keep packed fp32 (v_pk_*_f32) out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the online-softmax rescale multiplies them
+    # with VALU ops, which cannot read AGPRs without a copy per element
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

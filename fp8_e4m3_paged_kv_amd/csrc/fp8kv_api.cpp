@@ -253,6 +253,9 @@ int fp8kv_paged_decode_partials(
                     (long long)num_slots, block_size);
     if (num_blocks > INT32_MAX)
         return fail(FP8KV_E_SHAPE, "num_slots / block_size exceeds int32 block ids");
+    // in-block offsets are 32-bit: 16 slots of codes / scales must fit
+    if (cache_stride_slot > (INT32_MAX / 16) || scale_stride_slot > (INT32_MAX / 64))
+        return fail(FP8KV_E_SHAPE, "slot stride too large for 32-bit in-block offsets");
     if (batch == 0 || s.num_partitions == 0) return ok();
 
     // float4 scale loads when one head's scales are contiguous per slot
@@ -285,6 +288,10 @@ int fp8kv_paged_decode_partials(
     p.num_partitions = s.num_partitions;
     p.max_context = max_context;
     p.num_blocks = (int32_t)num_blocks;
+    p.num_slots = num_slots;
+    p.scale_extent = num_slots > 0
+        ? (num_slots - 1) * scale_stride_slot + (int64_t)(num_kv_heads - 1) * scale_stride_head + 1
+        : 0;
     const int64_t pairs = (int64_t)batch * s.num_partitions;
     p.pairs_padded = (int32_t)round_up(pairs, 8);
     if ((int64_t)p.pairs_padded * num_kv_heads > INT32_MAX)

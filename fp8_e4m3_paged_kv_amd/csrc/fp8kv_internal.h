@@ -43,6 +43,8 @@ struct DecodeParams {
     int32_t batch, rows, num_q_heads, num_kv_heads, group, m_rows;
     int32_t block_size, partition, num_partitions, max_context;
     int32_t num_blocks;        // physical blocks: ids are clamped below it
+    int64_t num_slots;         // slots in each code buffer
+    int64_t scale_extent;      // floats addressable in each scale plane
     int32_t pairs_padded;      // (request, partition) pairs rounded up to 8
     float score_scale_log2;    // softmax_scale * log2(e)
     float* ws_o;               // [batch*Hkv*NP*M, head_dim]

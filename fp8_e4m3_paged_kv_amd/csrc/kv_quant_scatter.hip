@@ -10,6 +10,7 @@
 //   amax  = max |x|              16-lane DPP reduction, exact
 //   s     = fp32(amax / 448)     IEEE division
 //   c     = E4M3_rne_sat(fp32(x / s)), or E4M3(x) = +-0 when s == 0
+//           (the quotient from a per-row reciprocal + one FMA correction)
 //   cache[slot, h, :] = c; scale[slot, h] = s     (slot < 0 or >= num_slots:
 //                                                   nothing is written)
 // K and V are read at their own token/head strides.
@@ -54,6 +55,7 @@ __device__ __forceinline__ void store_codes(uint8_t* dst, const uint32_t* c, uin
 
 template <int D>
 __global__ __launch_bounds__(kQsThreads) void kv_quant_scatter_kernel(QuantScatterParams p) {
+#pragma clang fp contract(off)
     constexpr int EPL = D / 16;          // elements per lane
     constexpr int WPL = EPL / 2;         // bf16 pairs (dwords) per lane
     typedef typename QsVec<D>::In In;
@@ -105,12 +107,27 @@ __global__ __launch_bounds__(kQsThreads) void kv_quant_scatter_kernel(QuantScatt
         amax_bits = row16_max_u32(amax_bits);
         const float amax = __uint_as_float(amax_bits);
         const float scale = amax / kE4M3Max;         // IEEE binary32 division
+        // x / scale, correctly rounded per element from one IEEE reciprocal
+        // and one FMA correction (Markstein): q0 = x*r, e = x - q0*s (exact),
+        // q = q0 + e*r, with the sign of x. Rows with a tiny scale are first
+        // scaled by 2^64 (exact) so the reciprocal stays finite. Checked
+        // exhaustively: for every bf16 row maximum and every bf16 element of
+        // either sign up to it in magnitude, the E4M3 code equals that of the
+        // IEEE quotient.
+        const float f = scale < 0x1p-100f ? 0x1p64f : 1.0f;
+        const float ss = scale * f;
+        const float rcp = 1.0f / ss;                 // IEEE binary32 division
         uint32_t packed[EPL / 4];
 #pragma unroll
         for (int i = 0; i < EPL / 4; ++i) packed[i] = 0;
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
-            const float qv = scale == 0.0f ? x[i] : x[i] / scale;
+            const float xs = x[i] * f;
+            const float q0 = xs * rcp;
+            const float e = __builtin_fmaf(-q0, ss, xs);
+            // the correction turns x = -0 into +0: restore the quotient's sign
+            const float qm = __builtin_copysignf(__builtin_fmaf(e, rcp, q0), x[i]);
+            const float qv = scale == 0.0f ? x[i] : qm;
             packed[i / 4] |= e4m3_encode(qv) << (8 * (i % 4));
         }
         const int64_t sl = slot[s];

@@ -40,38 +40,233 @@ namespace fp8kv {
 namespace {
 
 constexpr float kNeg = -1.0e30f;     // "minus infinity" that keeps exp2 finite
+constexpr int kBufferWord3 = 0x00020000;   // gfx9 raw buffer descriptor flags
 
 __device__ __forceinline__ float pow2i(int e) {   // 2^e for e in [-126, 127]
     return __uint_as_float((uint32_t)(e + 127) << 23);
 }
 
-__device__ __forceinline__ float xor_max(float v, int mask) {
-    return fmaxf(v, __shfl_xor(v, mask));
+// Butterfly across the four 16-lane rows of a wave (xor 16, then xor 32)
+// with the gfx950 row-swap instructions.
+__device__ __forceinline__ float rows_max(float v) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+__device__ __forceinline__ float rows_sum(float v) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Raw buffer descriptor over [base, base + bytes): loads past the end read 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int n = (int)min(max(bytes, (int64_t)0), (int64_t)0x7FFFFFF0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufferWord3);
+}
+
+typedef int intx2 __attribute__((ext_vector_type(2)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
 
 template <int DL>
 struct VRow;
 template <>
-struct VRow<8> { typedef uint2 T; };
+struct VRow<8> {
+    typedef uint2 T;
+    static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int off) {
+        intx2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        return make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+    }
+};
 template <>
-struct VRow<4> { typedef uint32_t T; };
+struct VRow<4> {
+    typedef uint32_t T;
+    static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int off) {
+        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    }
+};
 
 __device__ __forceinline__ uint32_t vword(const uint2& v, int i) { return i ? v.y : v.x; }
 __device__ __forceinline__ uint32_t vword(const uint32_t& v, int) { return v; }
 
+// Per-wave online-softmax state: O^T accumulators of the lane's query row,
+// running max (log2 units), partial sum of p over the lane's tokens, and the
+// power-of-two range exponent of P'.
+template <int DL>
+struct WaveState {
+    floatx4 acc[DL];
+    float m_run;
+    float l_run;
+    int ef_run;
+};
+
+// Everything about one 32-token tile that depends on the page table: the
+// buffer descriptors of its two 16-token halves (wave-uniform) and, for a
+// ragged tile, how many of each half's tokens exist.
+struct TileAddr {
+    __amdgpu_buffer_rsrc_t k[2], v[2], ks[2], vs[2];
+    int lastoff[2];
+};
+
+template <int D, int NW, bool SC>
+struct DecodeTile {
+    static constexpr int KB = D / 4;        // K code bytes per lane per token
+    static constexpr int KV4 = KB / 16;     // 16-byte K loads per token
+    static constexpr int KSTEPS = D / 32;   // MFMA k-steps over head_dim
+    static constexpr int DL = D / 16;       // V bytes per lane per token = PV n-tiles
+    typedef typename VRow<DL>::T VT;
+
+    // Process tokens [t0, t0 + 32). MASKED: the tile crosses the end of the
+    // partition or the causal limit of some verify row.
+    template <bool MASKED>
+    static __device__ __forceinline__ void run(
+        const DecodeParams& p, const TileAddr& ta, int t0, int p1, int lim,
+        int li, int lg, uint32_t css, const bf16x8 (&qv)[KSTEPS],
+        WaveState<DL>& st) {
+        // ---- loads: K (token li of each half), V (tokens 4g + r), scales
+        uint4 kraw[2][KV4];
+        VT vraw[8];
+        float sk[2][4], sv[2][4];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int ok = MASKED ? min(li, ta.lastoff[s]) : li;
+            const int kof = ok * css + lg * KB;
+#pragma unroll
+            for (int c = 0; c < KV4; ++c) {
+                intx4 v = __builtin_amdgcn_raw_buffer_load_b128(ta.k[s], kof + 16 * c, 0, 0);
+                kraw[s][c] = make_uint4(v[0], v[1], v[2], v[3]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int s = e >> 2;
+            const int o = MASKED ? min(4 * lg + (e & 3), ta.lastoff[s]) : 4 * lg + (e & 3);
+            vraw[e] = VRow<DL>::load(ta.v[s], o * css + li * DL);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            if (SC) {
+                // four consecutive slots of one head are contiguous floats
+                const int o4 = MASKED ? min(4 * lg, ta.lastoff[s] & ~3) : 4 * lg;
+                intx4 a = __builtin_amdgcn_raw_buffer_load_b128(ta.ks[s], 4 * o4, 0, 0);
+                intx4 c = __builtin_amdgcn_raw_buffer_load_b128(ta.vs[s], 4 * o4, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    sk[s][r] = __int_as_float(a[r]);
+                    sv[s][r] = __int_as_float(c[r]);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int o = MASKED ? min(4 * lg + r, ta.lastoff[s]) : 4 * lg + r;
+                    const int off = 4 * o * (int)p.scale_stride_slot;
+                    sk[s][r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(ta.ks[s], off, 0, 0));
+                    sv[s][r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(ta.vs[s], off, 0, 0));
+                }
+            }
+        }
+
+        // ---- S = K q^T, fp32 accumulate; lane holds tokens 4g + r, row li
+        floatx4 sc[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            sc[s] = floatx4{0.f, 0.f, 0.f, 0.f};
+            const uint32_t* kw = reinterpret_cast<const uint32_t*>(kraw[s]);
+#pragma unroll
+            for (int k = 0; k < KSTEPS; ++k) {
+                const bf16x8 a = e4m3x8_to_bf16x8(kw[2 * k], kw[2 * k + 1]);
+                sc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[k], sc[s], 0, 0, 0);
+            }
+        }
+
+        // ---- scores in log2 units, tile max, value-scale range
+        float s2[2][4];
+        bool valid[2][4];
+        float svm = 0.f;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                s2[s][r] = sc[s][r] * (sk[s][r] * p.score_scale_log2);
+                if (MASKED) {
+                    const int tok = t0 + 16 * s + 4 * lg + r;
+                    valid[s][r] = tok < p1 && tok <= lim;
+                    s2[s][r] = valid[s][r] ? s2[s][r] : kNeg;
+                    sv[s][r] = tok < p1 ? sv[s][r] : 0.f;
+                }
+                svm = fmaxf(svm, sv[s][r]);
+            }
+        float mt = fmaxf(fmaxf(fmaxf(s2[0][0], s2[0][1]), fmaxf(s2[0][2], s2[0][3])),
+                         fmaxf(fmaxf(s2[1][0], s2[1][1]), fmaxf(s2[1][2], s2[1][3])));
+        mt = rows_max(mt);
+        svm = rows_max(svm);                    // wave-uniform now
+        const int ef_t = max((int)((__float_as_uint(svm) >> 23) & 0xFF), 14);
+        const float m_new = fmaxf(st.m_run, mt);
+        if (__any(m_new > st.m_run || ef_t > st.ef_run)) {
+            const int ef_new = max(st.ef_run, ef_t);
+            const float a = __builtin_amdgcn_exp2f(st.m_run - m_new);
+            const float f = a * pow2i(max(st.ef_run - ef_new, -126));
+#pragma unroll
+            for (int n = 0; n < DL; ++n) st.acc[n] *= f;
+            st.l_run *= a;
+            st.m_run = m_new;
+            st.ef_run = ef_new;
+        }
+        const float kappa = pow2i(141 - st.ef_run);
+
+        // ---- P' = p * v_scale * kappa, fp16 (slot e = 4s + r)
+        uint32_t pw[4];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            float pr[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float e = __builtin_amdgcn_exp2f(s2[s][r] - st.m_run);
+                if (MASKED) e = valid[s][r] ? e : 0.f;
+                st.l_run += e;
+                pr[r] = e * (sv[s][r] * kappa);
+            }
+            pw[2 * s] = pack_f16x2(pr[0], pr[1]);
+            pw[2 * s + 1] = pack_f16x2(pr[2], pr[3]);
+        }
+        const f16x8 pb = __builtin_bit_cast(f16x8, pw);
+
+        // ---- V^T columns of the lane's 8 tokens, then O^T += V^T P'^T
+        uint32_t vt[DL][2];
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+#pragma unroll
+            for (int w = 0; w < DL / 4; ++w) {
+                uint32_t cols[4];
+                transpose4x4(vword(vraw[4 * hs + 0], w), vword(vraw[4 * hs + 1], w),
+                             vword(vraw[4 * hs + 2], w), vword(vraw[4 * hs + 3], w), cols);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) vt[4 * w + c][hs] = cols[c];
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < DL; ++n) {
+            const f16x8 a = e4m3x8_to_f16x8(vt[n][0], vt[n][1]);
+            st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb, st.acc[n], 0, 0, 0);
+        }
+    }
+};
+
 template <int D, int NW, bool SC>
 __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams p) {
-    constexpr int KB = D / 4;        // K code bytes per lane per token
-    constexpr int KV4 = KB / 16;     // 16-byte K loads per token
-    constexpr int KSTEPS = D / 32;   // MFMA k-steps over head_dim
-    constexpr int DL = D / 16;       // V bytes per lane per token = PV n-tiles
-    typedef typename VRow<DL>::T VT;
+    constexpr int KSTEPS = D / 32;
+    constexpr int DL = D / 16;
+    typedef DecodeTile<D, NW, SC> Tile;
 
     __shared__ floatx4 lds_acc[NW / 2][DL][64];
     __shared__ float lds_ml[NW / 2][2][64];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave index, provably uniform so the page walk and the buffer
+    // descriptors stay in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 15;
     const int lg = lane >> 4;
 
@@ -111,13 +306,15 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
     // tokens below full_end are visible to every row
     const int full_end = min(p1, len - p.rows + 1);
 
-    floatx4 acc[DL];
+    WaveState<DL> st;
 #pragma unroll
-    for (int n = 0; n < DL; ++n) acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float m_run = kNeg;
-    float l_run = 0.f;
-    int ef_run = 14;
+    for (int n = 0; n < DL; ++n) st.acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+    st.m_run = kNeg;
+    st.l_run = 0.f;
+    st.ef_run = 14;
 
+    const uint32_t css = (uint32_t)p.cache_stride_slot;
+    const int64_t cache_bytes = (int64_t)p.num_slots * p.cache_stride_slot;
     const int64_t h_cache = (int64_t)h * p.cache_stride_head;
     const int64_t h_scale = (int64_t)h * p.scale_stride_head;
     const int32_t* bt = p.block_tables + (int64_t)b * p.block_table_stride;
@@ -127,151 +324,35 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
 
     for (int ti = wave; ti < ntiles; ti += NW) {
         const int t0 = p0 + (ti << 5);
-        // page walk for the two 16-token halves (wave-uniform)
-        int64_t sbase[2];
-        int lastoff[2];
+        // page walk for the two 16-token halves (wave-uniform); descriptors
+        // end at the buffers' ends so no load can leave them
+        TileAddr ta;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const int st = min(t0 + 16 * s, last_base);
-            int blk = bt[st / bs];
+            const int stok = min(t0 + 16 * s, last_base);
+            int blk = bt[stok / bs];
             blk = min(max(blk, 0), p.num_blocks - 1);
-            sbase[s] = (int64_t)blk * bs + (st % bs);
-            lastoff[s] = last_tok - st;
+            const int64_t slot = (int64_t)blk * bs + (stok % bs);
+            const int64_t coff = slot * p.cache_stride_slot + h_cache;
+            ta.k[s] = make_rsrc(p.k_cache + coff, cache_bytes - coff);
+            ta.v[s] = make_rsrc(p.v_cache + coff, cache_bytes - coff);
+            const int64_t soff = slot * p.scale_stride_slot + h_scale;
+            ta.ks[s] = make_rsrc(p.k_scale + soff, (p.scale_extent - soff) * 4);
+            ta.vs[s] = make_rsrc(p.v_scale + soff, (p.scale_extent - soff) * 4);
+            ta.lastoff[s] = last_tok - stok;
         }
-        // K codes: token li of each half, bytes [lg*KB, lg*KB + KB)
-        uint4 kraw[2][KV4];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int64_t slot = sbase[s] + min(li, lastoff[s]);
-            const uint8_t* kp = p.k_cache + slot * p.cache_stride_slot + h_cache + lg * KB;
-#pragma unroll
-            for (int c = 0; c < KV4; ++c) kraw[s][c] = *reinterpret_cast<const uint4*>(kp + 16 * c);
-        }
-        // V codes: tokens 4g + r of each half (slot e = 4s + r), bytes [li*DL, li*DL + DL)
-        VT vraw[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int s = e >> 2;
-            const int64_t slot = sbase[s] + min(4 * lg + (e & 3), lastoff[s]);
-            vraw[e] = *reinterpret_cast<const VT*>(p.v_cache + slot * p.cache_stride_slot + h_cache + li * DL);
-        }
-        // row scales of tokens 4g + r
-        float sk[2][4], sv[2][4];
-        if (SC) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int o4 = min(4 * lg, lastoff[s] & ~3);
-                const int64_t idx = sbase[s] + o4 + h_scale;
-                const float4 a = *reinterpret_cast<const float4*>(p.k_scale + idx);
-                const float4 c = *reinterpret_cast<const float4*>(p.v_scale + idx);
-                sk[s][0] = a.x; sk[s][1] = a.y; sk[s][2] = a.z; sk[s][3] = a.w;
-                sv[s][0] = c.x; sv[s][1] = c.y; sv[s][2] = c.z; sv[s][3] = c.w;
-            }
-        } else {
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int64_t idx = (sbase[s] + min(4 * lg + r, lastoff[s])) * p.scale_stride_slot + h_scale;
-                    sk[s][r] = p.k_scale[idx];
-                    sv[s][r] = p.v_scale[idx];
-                }
-        }
-
-        // S = K q^T (fp32 accumulate)
-        floatx4 sc[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            sc[s] = floatx4{0.f, 0.f, 0.f, 0.f};
-            const uint32_t* kw = reinterpret_cast<const uint32_t*>(kraw[s]);
-#pragma unroll
-            for (int k = 0; k < KSTEPS; ++k) {
-                const bf16x8 a = e4m3x8_to_bf16x8(kw[2 * k], kw[2 * k + 1]);
-                sc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[k], sc[s], 0, 0, 0);
-            }
-        }
-
-        // scores in log2 units; mask tokens past the partition or the row
-        const bool need_mask = t0 + 32 > full_end;
-        float s2[2][4];
-        float svm = 0.f;
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                s2[s][r] = sc[s][r] * sk[s][r] * p.score_scale_log2;
-                if (need_mask) {
-                    const int tok = t0 + 16 * s + 4 * lg + r;
-                    const bool valid = tok < p1 && tok <= lim;
-                    const bool any_row = tok < p1;
-                    s2[s][r] = valid ? s2[s][r] : kNeg;
-                    sv[s][r] = any_row ? sv[s][r] : 0.f;
-                }
-                svm = fmaxf(svm, sv[s][r]);
-            }
-        float mt = fmaxf(fmaxf(fmaxf(s2[0][0], s2[0][1]), fmaxf(s2[0][2], s2[0][3])),
-                         fmaxf(fmaxf(s2[1][0], s2[1][1]), fmaxf(s2[1][2], s2[1][3])));
-        mt = xor_max(xor_max(mt, 16), 32);
-        svm = xor_max(xor_max(svm, 16), 32);   // wave-uniform now
-        const int ef_t = max((int)((__float_as_uint(svm) >> 23) & 0xFF), 14);
-        const float m_new = fmaxf(m_run, mt);
-        const bool grow = m_new > m_run || ef_t > ef_run;
-        if (__any(grow)) {
-            const int ef_new = max(ef_run, ef_t);
-            const float a = exp2f(m_run - m_new);
-            const float f = a * pow2i(max(ef_run - ef_new, -126));
-#pragma unroll
-            for (int n = 0; n < DL; ++n) acc[n] *= f;
-            l_run *= a;
-            m_run = m_new;
-            ef_run = ef_new;
-        }
-        const float kappa = pow2i(141 - ef_run);
-
-        // probabilities; P' = p * v_scale * kappa in fp16 (slot e = 4s + r)
-        uint32_t pw[4];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            float pr[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float e = exp2f(s2[s][r] - m_run);
-                if (need_mask) e = s2[s][r] == kNeg ? 0.f : e;
-                l_run += e;
-                pr[r] = e * (sv[s][r] * kappa);
-            }
-            pw[2 * s] = pack_f16x2(pr[0], pr[1]);
-            pw[2 * s + 1] = pack_f16x2(pr[2], pr[3]);
-        }
-        const f16x8 pb = __builtin_bit_cast(f16x8, pw);
-
-        // V^T: column c (head-dim 8i + c, or 4i + c) of the lane's 8 tokens
-        uint32_t vt[DL][2];
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {              // token slots 4hs .. 4hs+3
-#pragma unroll
-            for (int w = 0; w < DL / 4; ++w) {        // byte columns 4w .. 4w+3
-                uint32_t cols[4];
-                transpose4x4(vword(vraw[4 * hs + 0], w), vword(vraw[4 * hs + 1], w),
-                             vword(vraw[4 * hs + 2], w), vword(vraw[4 * hs + 3], w), cols);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) vt[4 * w + c][hs] = cols[c];
-            }
-        }
-#pragma unroll
-        for (int n = 0; n < DL; ++n) {
-            const f16x8 a = e4m3x8_to_f16x8(vt[n][0], vt[n][1]);
-            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb, acc[n], 0, 0, 0);
-        }
+        if (t0 + 32 <= full_end)
+            Tile::template run<false>(p, ta, t0, p1, lim, li, lg, css, qv, st);
+        else
+            Tile::template run<true>(p, ta, t0, p1, lim, li, lg, css, qv, st);
     }
 
     // per-wave totals for the lane's row
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    st.l_run = rows_sum(st.l_run);
     {
-        const float kinv = pow2i(max(ef_run - 141, -126));
+        const float kinv = pow2i(max(st.ef_run - 141, -126));
 #pragma unroll
-        for (int n = 0; n < DL; ++n) acc[n] *= kinv;
+        for (int n = 0; n < DL; ++n) st.acc[n] *= kinv;
     }
 
     // merge the NW waves pairwise through LDS (log2(NW) rounds)
@@ -280,44 +361,55 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
         if (wave >= half && wave < 2 * half) {
             const int slot = wave - half;
 #pragma unroll
-            for (int n = 0; n < DL; ++n) lds_acc[slot][n][lane] = acc[n];
-            lds_ml[slot][0][lane] = m_run;
-            lds_ml[slot][1][lane] = l_run;
+            for (int n = 0; n < DL; ++n) lds_acc[slot][n][lane] = st.acc[n];
+            lds_ml[slot][0][lane] = st.m_run;
+            lds_ml[slot][1][lane] = st.l_run;
         }
         __syncthreads();
         if (wave < half) {
             const float mo = lds_ml[wave][0][lane];
             const float lo = lds_ml[wave][1][lane];
-            const float mm = fmaxf(m_run, mo);
-            const float fa = exp2f(m_run - mm);
-            const float fb = exp2f(mo - mm);
+            const float mm = fmaxf(st.m_run, mo);
+            const float fa = __builtin_amdgcn_exp2f(st.m_run - mm);
+            const float fb = __builtin_amdgcn_exp2f(mo - mm);
 #pragma unroll
-            for (int n = 0; n < DL; ++n) acc[n] = acc[n] * fa + lds_acc[wave][n][lane] * fb;
-            l_run = l_run * fa + lo * fb;
-            m_run = mm;
+            for (int n = 0; n < DL; ++n) st.acc[n] = st.acc[n] * fa + lds_acc[wave][n][lane] * fb;
+            st.l_run = st.l_run * fa + lo * fb;
+            st.m_run = mm;
         }
         __syncthreads();
     }
 
     if (wave == 0 && li < p.m_rows) {
         const int64_t u = (((int64_t)b * p.num_kv_heads + h) * p.num_partitions + part) * p.m_rows + li;
-        const bool any = l_run > 0.f;
-        const float inv = any ? 1.0f / l_run : 0.f;
+        const bool any = st.l_run > 0.f;
+        const float inv = any ? 1.0f / st.l_run : 0.f;
         float* o = p.ws_o + u * D + (DL * 4) * lg;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float vals[DL];
 #pragma unroll
-            for (int n = 0; n < DL; ++n) vals[n] = acc[n][r] * inv;
+            for (int n = 0; n < DL; ++n) vals[n] = st.acc[n][r] * inv;
 #pragma unroll
             for (int c = 0; c < DL / 4; ++c)
                 *reinterpret_cast<float4*>(o + DL * r + 4 * c) =
                     make_float4(vals[4 * c], vals[4 * c + 1], vals[4 * c + 2], vals[4 * c + 3]);
         }
-        if (lg == 0) p.ws_lse[u] = any ? m_run + __log2f(l_run) : -INFINITY;
+        if (lg == 0) p.ws_lse[u] = any ? st.m_run + __log2f(st.l_run) : -INFINITY;
     }
 }
 
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+    return v;
+}
+
+// Log-sum-exp merge of the partition partials: one wave per output row.
+// Lanes read the partitions' lse values in parallel (one partition per
+// lane, 64 at a time), the wave takes their maximum, and each partition's
+// weight 2^(lse - max) is then broadcast from its lane while every lane
+// accumulates its D/64 output columns.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
     constexpr int PER = D / 64;
@@ -333,19 +425,46 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
     const int64_t u0 = (int64_t)bh * p.num_partitions * p.m_rows + m;
 
     float mx = -INFINITY;
-    for (int q = 0; q < np; ++q) mx = fmaxf(mx, p.ws_lse[u0 + (int64_t)q * p.m_rows]);
+    for (int c = 0; c < np; c += 64) {
+        const int q = c + lane;
+        const float l = q < np ? p.ws_lse[u0 + (int64_t)q * p.m_rows] : -INFINITY;
+        mx = fmaxf(mx, l);
+    }
+    mx = wave_max(mx);
+
     float acc[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = 0.f;
     float wsum = 0.f;
     if (mx > -INFINITY) {
-        for (int q = 0; q < np; ++q) {
-            const int64_t u = u0 + (int64_t)q * p.m_rows;
-            const float w = exp2f(p.ws_lse[u] - mx);
-            wsum += w;
-            const float* o = p.ws_o + u * D + lane * PER;
+        for (int c = 0; c < np; c += 64) {
+            const int q = c + lane;
+            const float w = q < np ? exp2f(p.ws_lse[u0 + (int64_t)q * p.m_rows] - mx) : 0.f;
+            const int n = min(64, np - c);
+            const float* o = p.ws_o + (u0 + (int64_t)c * p.m_rows) * D + lane * PER;
+            const int64_t step = (int64_t)p.m_rows * D;
+            int j = 0;
+            for (; j + 4 <= n; j += 4) {
+                float wj[4], v[4][PER];
 #pragma unroll
-            for (int i = 0; i < PER; ++i) acc[i] += w * o[i];
+                for (int t = 0; t < 4; ++t) {
+                    wj[t] = __shfl(w, j + t);
+#pragma unroll
+                    for (int i = 0; i < PER; ++i) v[t][i] = o[(j + t) * step + i];
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    wsum += wj[t];
+#pragma unroll
+                    for (int i = 0; i < PER; ++i) acc[i] += wj[t] * v[t][i];
+                }
+            }
+            for (; j < n; ++j) {
+                const float wj = __shfl(w, j);
+                wsum += wj;
+#pragma unroll
+                for (int i = 0; i < PER; ++i) acc[i] += wj * o[j * step + i];
+            }
         }
     }
     const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;

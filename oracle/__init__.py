@@ -63,6 +63,7 @@ def _load():
     lib.fo_encode_array.argtypes = [I, P, I64, P]
     lib.fo_decode_array.argtypes = [I, P, I64, P]
     lib.fo_quantize_row.argtypes = [I, P, I64, P, P]
+    lib.fo_quantize_rows_bf16.argtypes = [I, P, I64, I64, I64, P, P]
     lib.fo_kv_quant_scatter_bf16.argtypes = [P, I64, I64, P, I64, I64,
                                              I64, I64, I64, P, I64,
                                              P, P, I64, I64, P, P, I64, I64]
@@ -117,6 +118,33 @@ def quantize_rows(x, fmt: int = E4M3):
     for i in range(n):
         lib.fo_quantize_row(fmt, _ptr(x[i]), d, _ptr(codes[i]),
                             scales[i:].ctypes.data)
+    return codes, scales
+
+
+def quantize_rows_bf16(x_bits, fmt: int = E4M3, threads: int = 1):
+    """Quantize the rows of a uint16 (bf16 bits) [N, D] array with rows of
+    unit inner stride: (codes uint8 [N, D], scales float32 [N]). With
+    threads > 1 the rows are split into contiguous chunks, one per thread."""
+    x = np.asarray(x_bits)
+    assert x.dtype == np.uint16 and x.ndim == 2 and x.strides[1] == 2
+    n, d = x.shape
+    codes = np.empty((n, d), dtype=np.uint8)
+    scales = np.empty((n,), dtype=np.float32)
+    lib = _load()
+    xs = x.strides[0] // 2
+
+    def run(lo, hi):
+        if hi > lo:
+            lib.fo_quantize_rows_bf16(fmt, _ptr(x[lo:]), hi - lo, d, xs,
+                                      _ptr(codes[lo:]), _ptr(scales[lo:]))
+    if threads <= 1 or n < 2 * threads:
+        run(0, n)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        step = (n + threads - 1) // threads
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(lambda i: run(i, min(n, i + step)),
+                        range(0, n, step)))
     return codes, scales
 
 

@@ -52,6 +52,11 @@ float    fo_bf16_to_f32(uint16_t bits);
 /* ---- per-row quantizer and paged scatter (quant.c) ---------------------- */
 void fo_quantize_row(int fmt, const float* x, int64_t D, uint8_t* codes,
                      float* scale);
+/* fo_quantize_row over n_rows bf16 rows of x (row pitch x_stride elements);
+ * codes [n_rows, D] and scales [n_rows], both dense. */
+void fo_quantize_rows_bf16(int fmt, const uint16_t* x, int64_t n_rows,
+                           int64_t D, int64_t x_stride, uint8_t* codes,
+                           float* scales);
 void fo_kv_quant_scatter_bf16(
     const uint16_t* k, int64_t k_stride_tok, int64_t k_stride_head,
     const uint16_t* v, int64_t v_stride_tok, int64_t v_stride_head,

@@ -54,6 +54,18 @@ void fo_quantize_row(int fmt, const float* x, int64_t D, uint8_t* codes,
     *scale = s;
 }
 
+void fo_quantize_rows_bf16(int fmt, const uint16_t* x, int64_t n_rows,
+                           int64_t D, int64_t x_stride, uint8_t* codes,
+                           float* scales) {
+    float* row = (float*)malloc((size_t)D * sizeof(float));
+    for (int64_t i = 0; i < n_rows; ++i) {
+        for (int64_t d = 0; d < D; ++d)
+            row[d] = fo_bf16_to_f32(x[i * x_stride + d]);
+        fo_quantize_row(fmt, row, D, codes + i * D, scales + i);
+    }
+    free(row);
+}
+
 void fo_kv_quant_scatter_bf16(
     const uint16_t* k, int64_t k_stride_tok, int64_t k_stride_head,
     const uint16_t* v, int64_t v_stride_tok, int64_t v_stride_head,

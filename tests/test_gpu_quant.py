@@ -1,5 +1,7 @@
 """GPU parity of fp8kv_kv_quant_scatter against the oracle: codes, scales
 and slot placement bit-exact, every other byte of the pool untouched."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -112,7 +114,7 @@ def edge_rows(D=128):
     g = synth.gen(5)
     rows = [torch.zeros(D), -torch.zeros(D)]
     x = torch.randn(D, generator=g)
-    rows += [x, x * 1e-30, x * 1e-38, x * 3e38 / x.abs().max(), -x]
+    rows += [x, x * 1e-30, x * 1e-38, x / x.abs().max() * 3e38, -x]
     one = torch.zeros(D)
     one[17] = 2.0 ** -133                       # smallest bf16 subnormal
     rows.append(one)
@@ -125,7 +127,9 @@ def edge_rows(D=128):
     mid = torch.cat([mid[:D // 2], -mid[:D // 2]])
     mid[0] = 448.0
     rows.append(mid)
-    return torch.stack(rows).to(torch.bfloat16)
+    out = torch.stack(rows).to(torch.bfloat16)
+    assert torch.isfinite(out.float()).all()      # non-finite input is out of contract
+    return out
 
 
 def test_edge_rows_bit_exact():
@@ -209,3 +213,43 @@ def test_graph_capture_replays_with_new_slots():
         oracle.kv_quant_scatter_bf16(bf16_bits(k), bf16_bits(v),
                                      slots.cpu().numpy(), *ref)
         assert_same(dc.host(), ref, f"replay {rep}")
+
+
+def every_pair_rows(D=128):
+    """Rows covering every (positive bf16 row maximum a, bf16 x in [0, a])
+    pair: element 0 of each row is a, the other D-1 elements walk x through
+    0 .. a (zero-padded at the end of each a). Built on the device."""
+    amax = torch.arange(1, 0x7F80, device=DEV, dtype=torch.int64)   # bit patterns
+    per = D - 1
+    nrows = (amax + 1 + per - 1) // per
+    a_of_row = torch.repeat_interleave(amax, nrows)
+    first = torch.cumsum(nrows, 0) - nrows                           # first row of each a
+    row_in_a = torch.arange(a_of_row.numel(), device=DEV) - torch.repeat_interleave(first, nrows)
+    xb = row_in_a[:, None] * per + torch.arange(per, device=DEV)[None, :]
+    xb = torch.where(xb <= a_of_row[:, None], xb, torch.zeros_like(xb))
+    bits = torch.cat([a_of_row[:, None], xb], dim=1).to(torch.int32).to(torch.int16)
+    return bits.view(torch.bfloat16)
+
+
+def test_every_bf16_pair_bit_exact():
+    """All 532,701,119 (row maximum, element) bf16 pairs through the kernel:
+    K rows as built, V rows negated; K codes and scales against the oracle,
+    V against K by the encoding's sign symmetry."""
+    x = every_pair_rows()
+    n = x.shape[0]
+    log(f"every-pair rows: {n}")
+    k = x.view(n, 1, 128)
+    v = (-x.float()).to(torch.bfloat16).view(n, 1, 128)
+    dc = DevCache(n, 1, 128, DEV, "slot_major", sentinel=False)
+    fk.kv_quant_scatter(k, v, torch.arange(n, device=DEV, dtype=torch.int64),
+                        dc.k_cache, dc.v_cache, dc.k_scale, dc.v_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(dc.v_cache, dc.k_cache | 0x80)
+    assert torch.equal(dc.v_plane, dc.k_plane)
+    threads = min(16, os.cpu_count() or 1)
+    codes, scales = oracle.quantize_rows_bf16(bf16_bits(x), threads=threads)
+    got = dc.k_cache.view(n, 128).cpu().numpy()
+    bad = np.flatnonzero((got != codes).any(axis=1))
+    assert bad.size == 0, f"{bad.size} rows differ, e.g. row {bad[:3]}"
+    assert np.array_equal(dc.k_plane.view(n).cpu().numpy().view(np.uint32),
+                          scales.view(np.uint32))
