@@ -284,6 +284,7 @@ int fp8kv_paged_decode_partials(
     p.group = s.group;
     p.m_rows = s.m_rows;
     p.block_size = block_size;
+    p.block_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
     p.partition = s.partition;
     p.num_partitions = s.num_partitions;
     p.max_context = max_context;

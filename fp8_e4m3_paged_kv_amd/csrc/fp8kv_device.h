@@ -52,6 +52,19 @@ __device__ __forceinline__ uint32_t e4m3_encode(float q) {
     return sign | (a >= 0x1p-6f ? normal : sub);
 }
 
+// Four fp32 values -> four E4M3 codes (bytes 0..3), round to nearest even,
+// magnitudes above 448 saturating to +-448: the gfx950 OCP converter after
+// a clamp (the quantizer's quotients never exceed 448 * (1 + 2^-23)).
+__device__ __forceinline__ uint32_t e4m3x4_encode(float a, float b, float c, float d) {
+    a = __builtin_amdgcn_fmed3f(a, -kE4M3Max, kE4M3Max);
+    b = __builtin_amdgcn_fmed3f(b, -kE4M3Max, kE4M3Max);
+    c = __builtin_amdgcn_fmed3f(c, -kE4M3Max, kE4M3Max);
+    d = __builtin_amdgcn_fmed3f(d, -kE4M3Max, kE4M3Max);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
 // Two E4M3 codes (16-bit half HI of w) -> two bf16, exact.
 template <bool HI>
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {

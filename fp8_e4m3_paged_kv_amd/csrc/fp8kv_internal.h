@@ -42,6 +42,7 @@ struct DecodeParams {
     const int32_t* context_lens;
     int32_t batch, rows, num_q_heads, num_kv_heads, group, m_rows;
     int32_t block_size, partition, num_partitions, max_context;
+    int32_t block_shift;       // log2(block_size) when a power of two, else -1
     int32_t num_blocks;        // physical blocks: ids are clamped below it
     int64_t num_slots;         // slots in each code buffer
     int64_t scale_extent;      // floats addressable in each scale plane

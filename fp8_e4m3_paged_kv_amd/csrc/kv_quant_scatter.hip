@@ -2,10 +2,11 @@
 // (one launch for both; ATOM #2655 description, K/V bullet; FreeToken #354
 // description and its V-pitch fix).
 //
-// Work unit: one (token, KV head, K-or-V) row of head_dim elements, handled
-// by one 16-lane DPP row of a wave64 (head_dim/16 bf16 per lane, one 8- or
-// 16-byte load). A wave covers 4 rows per step and 4 steps; all loads of a
-// wave are issued before any arithmetic so 64 B per lane are in flight.
+// Work unit: one (token, KV head) row of head_dim elements of K or of V
+// (grid y), handled by one 16-lane DPP row of a wave64 (head_dim/16 bf16 per
+// lane, one 8- or 16-byte load). A wave covers 4 rows per step and 4 steps;
+// all loads of a wave are issued before any arithmetic so 64 B per lane are
+// in flight.
 //
 //   amax  = max |x|              16-lane DPP reduction, exact
 //   s     = fp32(amax / 448)     IEEE division
@@ -53,7 +54,20 @@ __device__ __forceinline__ void store_codes(uint8_t* dst, const uint32_t* c, uin
     *reinterpret_cast<uint32_t*>(dst) = c[0];
 }
 
-template <int D>
+// Row r of K (or of V) is (token r / H, head r % H). HSHIFT = log2(H) when
+// H is a power of two (shifts), else -1 (32-bit division).
+template <int HSHIFT>
+__device__ __forceinline__ void split_row(uint32_t pair, uint32_t H, uint32_t& t, uint32_t& h) {
+    if (HSHIFT >= 0) {
+        t = pair >> HSHIFT;
+        h = pair & ((1u << HSHIFT) - 1u);
+    } else {
+        t = pair / H;
+        h = pair - t * H;
+    }
+}
+
+template <int D, int HSHIFT>
 __global__ __launch_bounds__(kQsThreads) void kv_quant_scatter_kernel(QuantScatterParams p) {
 #pragma clang fp contract(off)
     constexpr int EPL = D / 16;          // elements per lane
@@ -61,34 +75,41 @@ __global__ __launch_bounds__(kQsThreads) void kv_quant_scatter_kernel(QuantScatt
     typedef typename QsVec<D>::In In;
     typedef typename QsVec<D>::Out Out;
 
+    // blockIdx.y selects K (0) or V (1): every pointer and stride below is
+    // uniform over the workgroup
+    const bool is_v = blockIdx.y != 0;
+    const uint16_t* src = is_v ? p.v : p.k;
+    const int64_t st_tok = is_v ? p.v_stride_tok : p.k_stride_tok;
+    const int64_t st_head = is_v ? p.v_stride_head : p.k_stride_head;
+    uint8_t* cache = is_v ? p.v_cache : p.k_cache;
+    float* planes = is_v ? p.v_scale : p.k_scale;
+
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane >> 4;           // row within a 4-row group
     const int li = lane & 15;            // lane within the row
-    const int64_t wave_row0 = (int64_t)blockIdx.x * kQsRowsPerBlock + wave * kQsRowsPerWave;
-    const int H = p.num_kv_heads;
+    const uint32_t wave_row0 = blockIdx.x * kQsRowsPerBlock + wave * kQsRowsPerWave;
+    const uint32_t H = (uint32_t)p.num_kv_heads;
+    const uint32_t nrows = (uint32_t)(p.num_rows >> 1);   // (token, head) rows of K (or V)
 
     uint32_t w[kQsSteps][WPL];
     int64_t slot[kQsSteps];
-    int head[kQsSteps];
-    int is_v[kQsSteps];
+    uint32_t head[kQsSteps];
 
     // issue every load first
 #pragma unroll
     for (int s = 0; s < kQsSteps; ++s) {
-        const int64_t r = wave_row0 + 4 * s + sub;
-        const bool in_range = r < p.num_rows;
-        const int64_t pair = r >> 1;                 // (token, head)
-        const int64_t t = in_range ? pair / H : 0;
-        const int h = in_range ? (int)(pair - t * H) : 0;
-        is_v[s] = (int)(r & 1);
+        const uint32_t r = wave_row0 + 4 * s + sub;
+        const bool in_range = r < nrows;
+        uint32_t t, h;
+        split_row<HSHIFT>(in_range ? r : 0, H, t, h);
         head[s] = h;
         slot[s] = in_range ? p.slot_ids[t] : -1;
-        const uint16_t* src = is_v[s]
-            ? p.v + t * p.v_stride_tok + h * p.v_stride_head
-            : p.k + t * p.k_stride_tok + h * p.k_stride_head;
-        In v = {};
-        if (in_range) v = *reinterpret_cast<const In*>(src + li * EPL);
+        In v;
+        if (in_range)
+            v = *reinterpret_cast<const In*>(src + (int64_t)t * st_tok + (int64_t)h * st_head + li * EPL);
+        else
+            v = In{};
         unpack_words(v, w[s]);
     }
 
@@ -109,31 +130,41 @@ __global__ __launch_bounds__(kQsThreads) void kv_quant_scatter_kernel(QuantScatt
         const float scale = amax / kE4M3Max;         // IEEE binary32 division
         // x / scale, correctly rounded per element from one IEEE reciprocal
         // and one FMA correction (Markstein): q0 = x*r, e = x - q0*s (exact),
-        // q = q0 + e*r, with the sign of x. Rows with a tiny scale are first
-        // scaled by 2^64 (exact) so the reciprocal stays finite. Checked
-        // exhaustively: for every bf16 row maximum and every bf16 element of
-        // either sign up to it in magnitude, the E4M3 code equals that of the
-        // IEEE quotient.
-        const float f = scale < 0x1p-100f ? 0x1p64f : 1.0f;
-        const float ss = scale * f;
-        const float rcp = 1.0f / ss;                 // IEEE binary32 division
+        // q = q0 + e*r, with the sign of x (the correction turns -0 into +0).
+        // An all-zero row divides by 1 (its codes are the signed zeros of x).
+        // Checked exhaustively: for every bf16 row maximum and every bf16
+        // element of either sign up to it in magnitude, the E4M3 code equals
+        // that of the IEEE quotient.
+        float qv[EPL];
+        if (__builtin_expect(__any(scale < 0x1p-100f && scale != 0.0f), 0)) {
+            // rows this small are first scaled by 2^64 (exact) so the
+            // reciprocal stays finite
+            const float f = scale < 0x1p-100f ? 0x1p64f : 1.0f;
+            const float ss = scale == 0.0f ? 1.0f : scale * f;
+            const float rcp = 1.0f / ss;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const float xs = scale == 0.0f ? x[i] : x[i] * f;
+                const float q0 = xs * rcp;
+                const float e = __builtin_fmaf(-q0, ss, xs);
+                qv[i] = __builtin_copysignf(__builtin_fmaf(e, rcp, q0), x[i]);
+            }
+        } else {
+            const float ss = scale == 0.0f ? 1.0f : scale;
+            const float rcp = 1.0f / ss;                 // IEEE binary32 division
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const float q0 = x[i] * rcp;
+                const float e = __builtin_fmaf(-q0, ss, x[i]);
+                qv[i] = __builtin_copysignf(__builtin_fmaf(e, rcp, q0), x[i]);
+            }
+        }
         uint32_t packed[EPL / 4];
 #pragma unroll
-        for (int i = 0; i < EPL / 4; ++i) packed[i] = 0;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const float xs = x[i] * f;
-            const float q0 = xs * rcp;
-            const float e = __builtin_fmaf(-q0, ss, xs);
-            // the correction turns x = -0 into +0: restore the quotient's sign
-            const float qm = __builtin_copysignf(__builtin_fmaf(e, rcp, q0), x[i]);
-            const float qv = scale == 0.0f ? x[i] : qm;
-            packed[i / 4] |= e4m3_encode(qv) << (8 * (i % 4));
-        }
+        for (int i = 0; i < EPL / 4; ++i)
+            packed[i] = e4m3x4_encode(qv[4 * i], qv[4 * i + 1], qv[4 * i + 2], qv[4 * i + 3]);
         const int64_t sl = slot[s];
         if (sl >= 0 && sl < p.num_slots) {
-            uint8_t* cache = is_v[s] ? p.v_cache : p.k_cache;
-            float* planes = is_v[s] ? p.v_scale : p.k_scale;
             uint8_t* dst = cache + sl * p.cache_stride_slot +
                            (int64_t)head[s] * p.cache_stride_head + li * EPL;
             store_codes(dst, packed, (Out*)nullptr);
@@ -147,13 +178,31 @@ __global__ __launch_bounds__(kQsThreads) void kv_quant_scatter_kernel(QuantScatt
 
 hipError_t launch_kv_quant_scatter(const QuantScatterParams& p, int head_dim,
                                    hipStream_t stream) {
-    const int64_t blocks = (p.num_rows + kQsRowsPerBlock - 1) / kQsRowsPerBlock;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    dim3 grid((unsigned)blocks), block(kQsThreads);
-    if (head_dim == 128)
-        hipLaunchKernelGGL(kv_quant_scatter_kernel<128>, grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL(kv_quant_scatter_kernel<64>, grid, block, 0, stream, p);
+    // rows are numbered in 32 bits; K rows on grid y = 0, V rows on y = 1
+    const int64_t kv_rows = p.num_rows / 2;
+    if (kv_rows > 0x7FFFFFFF - kQsRowsPerBlock) return hipErrorInvalidValue;
+    const int64_t blocks = (kv_rows + kQsRowsPerBlock - 1) / kQsRowsPerBlock;
+    dim3 grid((unsigned)blocks, 2), block(kQsThreads);
+    const int H = p.num_kv_heads;
+    const int hs = (H & (H - 1)) == 0 ? __builtin_ctz((unsigned)H) : -1;
+#define FP8KV_QS_LAUNCH(DIM, HS) \
+    hipLaunchKernelGGL((kv_quant_scatter_kernel<DIM, HS>), grid, block, 0, stream, p)
+#define FP8KV_QS_DISPATCH(DIM)                                   \
+    switch (hs) {                                                \
+        case 0: FP8KV_QS_LAUNCH(DIM, 0); break;                  \
+        case 1: FP8KV_QS_LAUNCH(DIM, 1); break;                  \
+        case 2: FP8KV_QS_LAUNCH(DIM, 2); break;                  \
+        case 3: FP8KV_QS_LAUNCH(DIM, 3); break;                  \
+        case 4: FP8KV_QS_LAUNCH(DIM, 4); break;                  \
+        default: FP8KV_QS_LAUNCH(DIM, -1); break;                \
+    }
+    if (head_dim == 128) {
+        FP8KV_QS_DISPATCH(128)
+    } else {
+        FP8KV_QS_DISPATCH(64)
+    }
+#undef FP8KV_QS_DISPATCH
+#undef FP8KV_QS_LAUNCH
     return hipGetLastError();
 }
 

@@ -62,9 +62,8 @@ __device__ __forceinline__ float rows_sum(float v) {
 }
 
 // Raw buffer descriptor over [base, base + bytes): loads past the end read 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-    const int n = (int)min(max(bytes, (int64_t)0), (int64_t)0x7FFFFFF0);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufferWord3);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferWord3);
 }
 
 typedef int intx2 __attribute__((ext_vector_type(2)));
@@ -103,11 +102,34 @@ struct WaveState {
 };
 
 // Everything about one 32-token tile that depends on the page table: the
-// buffer descriptors of its two 16-token halves (wave-uniform) and, for a
-// ragged tile, how many of each half's tokens exist.
+// buffer descriptors of its two 16-token halves (wave-uniform) and whether
+// the tile needs masking. Each descriptor ends after the last token of its
+// half that lies inside the partition (and never past the buffer), so loads
+// for tokens beyond it return 0 without touching memory; a tile past the
+// wave's last one gets empty descriptors.
 struct TileAddr {
     __amdgpu_buffer_rsrc_t k[2], v[2], ks[2], vs[2];
-    int lastoff[2];
+    int t0;
+    bool masked;
+};
+
+// Loop-invariant byte offsets of the lane's loads inside a 16-token half.
+// They stay entirely in the VGPR offset: the buffer range check covers the
+// VGPR and immediate offsets but not the SGPR one.
+struct LaneOffsets {
+    int k;                // token li, head-dim bytes [lg*KB, lg*KB + KB)
+    int v[4];             // token 4g + r, head-dim bytes [li*DL, li*DL + DL)
+    int s[4];             // scale of token 4g + r (s[0]: the 4 scales, when contiguous)
+};
+
+template <int D, bool SC>
+struct TileRegs {
+    static constexpr int KV4 = D / 64;      // 16-byte K loads per token
+    static constexpr int DL = D / 16;
+    typedef typename VRow<DL>::T VT;
+    uint4 kraw[2][KV4];
+    VT vraw[8];
+    float sk[2][4], sv[2][4];
 };
 
 template <int D, int NW, bool SC>
@@ -117,87 +139,131 @@ struct DecodeTile {
     static constexpr int KSTEPS = D / 32;   // MFMA k-steps over head_dim
     static constexpr int DL = D / 16;       // V bytes per lane per token = PV n-tiles
     typedef typename VRow<DL>::T VT;
+    typedef TileRegs<D, SC> Regs;
 
-    // Process tokens [t0, t0 + 32). MASKED: the tile crosses the end of the
-    // partition or the causal limit of some verify row.
-    template <bool MASKED>
-    static __device__ __forceinline__ void run(
-        const DecodeParams& p, const TileAddr& ta, int t0, int p1, int lim,
-        int li, int lg, uint32_t css, const bf16x8 (&qv)[KSTEPS],
-        WaveState<DL>& st) {
-        // ---- loads: K (token li of each half), V (tokens 4g + r), scales
-        uint4 kraw[2][KV4];
-        VT vraw[8];
-        float sk[2][4], sv[2][4];
+    // Per-workgroup constants of the page walk.
+    struct WalkConsts {
+        const uint8_t* kbase;     // k_cache + h * cache_stride_head
+        const uint8_t* vbase;
+        const float* ksbase;      // k_scale + h * scale_stride_head
+        const float* vsbase;
+        const int32_t* bt;        // this request's block-table row
+        int p0, p1, ntiles, full_end, last_base;
+        int nr_codes_full;        // num_records of a full half: 15*css + D
+        int nr_scales_full;       // ... of its scales
+    };
+
+    // Page walk of tile ti (wave-uniform). Full halves use constant bounds;
+    // a ragged tile's halves end after their last token inside the
+    // partition, and a tile past the wave's last one gets empty ones.
+    template <bool BSP2>
+    static __device__ __forceinline__ void address(const DecodeParams& p, const WalkConsts& w,
+                                                   int ti, TileAddr& ta) {
+        const int t0 = w.p0 + (ti << 5);
+        const bool live = ti < w.ntiles;
+        const bool ragged = !live || t0 + 32 > w.p1;
+        const int bs = p.block_size;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const int ok = MASKED ? min(li, ta.lastoff[s]) : li;
-            const int kof = ok * css + lg * KB;
+            const int stok = t0 + 16 * s;
+            const int tab = min(stok, w.last_base);     // table entry stays valid
+            const int bi = BSP2 ? (tab >> p.block_shift) : tab / bs;
+            const int bo = BSP2 ? (tab & (bs - 1)) : tab - bi * bs;
+            int blk = w.bt[bi];
+            blk = min(max(blk, 0), p.num_blocks - 1);
+            const int64_t slot = (int64_t)blk * bs + bo;
+            const int64_t coff = slot * p.cache_stride_slot;
+            const int64_t soff = slot * p.scale_stride_slot;
+            int nrc = w.nr_codes_full, nrs = w.nr_scales_full;
+            if (ragged) {
+                // tokens of this half inside the partition (<= 0: none)
+                const int nvalid = live ? min(16, w.p1 - stok) : 0;
+                nrc = nvalid > 0 ? (nvalid - 1) * (int)p.cache_stride_slot + D : 0;
+                nrs = nvalid <= 0 ? 0
+                    : SC ? 16 * ((nvalid + 3) >> 2)          // whole 4-token groups
+                         : 4 * ((nvalid - 1) * (int)p.scale_stride_slot + 1);
+            }
+            ta.k[s] = make_rsrc(w.kbase + coff, nrc);
+            ta.v[s] = make_rsrc(w.vbase + coff, nrc);
+            ta.ks[s] = make_rsrc(w.ksbase + soff, nrs);
+            ta.vs[s] = make_rsrc(w.vsbase + soff, nrs);
+        }
+        ta.t0 = t0;
+        ta.masked = t0 + 32 > w.full_end;
+    }
+
+    static __device__ __forceinline__ void issue(const TileAddr& ta, const LaneOffsets& o, Regs& R) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int c = 0; c < KV4; ++c) {
-                intx4 v = __builtin_amdgcn_raw_buffer_load_b128(ta.k[s], kof + 16 * c, 0, 0);
-                kraw[s][c] = make_uint4(v[0], v[1], v[2], v[3]);
+                intx4 v = __builtin_amdgcn_raw_buffer_load_b128(ta.k[s], o.k + 16 * c, 0, 0);
+                R.kraw[s][c] = make_uint4(v[0], v[1], v[2], v[3]);
             }
-        }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int s = e >> 2;
-            const int o = MASKED ? min(4 * lg + (e & 3), ta.lastoff[s]) : 4 * lg + (e & 3);
-            vraw[e] = VRow<DL>::load(ta.v[s], o * css + li * DL);
-        }
+        for (int e = 0; e < 8; ++e) R.vraw[e] = VRow<DL>::load(ta.v[e >> 2], o.v[e & 3]);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             if (SC) {
-                // four consecutive slots of one head are contiguous floats
-                const int o4 = MASKED ? min(4 * lg, ta.lastoff[s] & ~3) : 4 * lg;
-                intx4 a = __builtin_amdgcn_raw_buffer_load_b128(ta.ks[s], 4 * o4, 0, 0);
-                intx4 c = __builtin_amdgcn_raw_buffer_load_b128(ta.vs[s], 4 * o4, 0, 0);
+                intx4 a = __builtin_amdgcn_raw_buffer_load_b128(ta.ks[s], o.s[0], 0, 0);
+                intx4 c = __builtin_amdgcn_raw_buffer_load_b128(ta.vs[s], o.s[0], 0, 0);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    sk[s][r] = __int_as_float(a[r]);
-                    sv[s][r] = __int_as_float(c[r]);
+                    R.sk[s][r] = __int_as_float(a[r]);
+                    R.sv[s][r] = __int_as_float(c[r]);
                 }
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int o = MASKED ? min(4 * lg + r, ta.lastoff[s]) : 4 * lg + r;
-                    const int off = 4 * o * (int)p.scale_stride_slot;
-                    sk[s][r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(ta.ks[s], off, 0, 0));
-                    sv[s][r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(ta.vs[s], off, 0, 0));
+                    R.sk[s][r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(ta.ks[s], o.s[r], 0, 0));
+                    R.sv[s][r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(ta.vs[s], o.s[r], 0, 0));
                 }
             }
         }
+    }
 
-        // ---- S = K q^T, fp32 accumulate; lane holds tokens 4g + r, row li
-        floatx4 sc[2];
+    // S = K q^T, fp32 accumulate; lane holds tokens 4g + r of each half, row li.
+    static __device__ __forceinline__ void qk(const Regs& R, const bf16x8 (&qv)[KSTEPS],
+                                              floatx4 (&sc)[2]) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             sc[s] = floatx4{0.f, 0.f, 0.f, 0.f};
-            const uint32_t* kw = reinterpret_cast<const uint32_t*>(kraw[s]);
+            const uint32_t* kw = reinterpret_cast<const uint32_t*>(R.kraw[s]);
 #pragma unroll
             for (int k = 0; k < KSTEPS; ++k) {
                 const bf16x8 a = e4m3x8_to_bf16x8(kw[2 * k], kw[2 * k + 1]);
                 sc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[k], sc[s], 0, 0, 0);
             }
         }
+    }
+
+    // Online-softmax update and PV with the tile's scores and V registers.
+    static __device__ __forceinline__ void rest(
+        const DecodeParams& p, const TileAddr& ta, const Regs& R, const floatx4 (&sc)[2],
+        int p1, int lim, int lg, WaveState<DL>& st) {
 
         // ---- scores in log2 units, tile max, value-scale range
         float s2[2][4];
-        bool valid[2][4];
-        float svm = 0.f;
+        float sv[2][4];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                s2[s][r] = sc[s][r] * (sk[s][r] * p.score_scale_log2);
-                if (MASKED) {
-                    const int tok = t0 + 16 * s + 4 * lg + r;
-                    valid[s][r] = tok < p1 && tok <= lim;
-                    s2[s][r] = valid[s][r] ? s2[s][r] : kNeg;
+                s2[s][r] = sc[s][r] * (R.sk[s][r] * p.score_scale_log2);
+                sv[s][r] = R.sv[s][r];
+            }
+        if (ta.masked) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tok = ta.t0 + 16 * s + 4 * lg + r;
+                    s2[s][r] = (tok < p1 && tok <= lim) ? s2[s][r] : kNeg;
                     sv[s][r] = tok < p1 ? sv[s][r] : 0.f;
                 }
-                svm = fmaxf(svm, sv[s][r]);
-            }
+        }
+        float svm = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                          fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
         float mt = fmaxf(fmaxf(fmaxf(s2[0][0], s2[0][1]), fmaxf(s2[0][2], s2[0][3])),
                          fmaxf(fmaxf(s2[1][0], s2[1][1]), fmaxf(s2[1][2], s2[1][3])));
         mt = rows_max(mt);
@@ -224,7 +290,7 @@ struct DecodeTile {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float e = __builtin_amdgcn_exp2f(s2[s][r] - st.m_run);
-                if (MASKED) e = valid[s][r] ? e : 0.f;
+                if (ta.masked) e = s2[s][r] == kNeg ? 0.f : e;
                 st.l_run += e;
                 pr[r] = e * (sv[s][r] * kappa);
             }
@@ -233,32 +299,40 @@ struct DecodeTile {
         }
         const f16x8 pb = __builtin_bit_cast(f16x8, pw);
 
-        // ---- V^T columns of the lane's 8 tokens, then O^T += V^T P'^T
-        uint32_t vt[DL][2];
+        // ---- V^T columns of the lane's 8 tokens, then O^T += V^T P'^T.
+        // Pairing two tokens' dwords byte-wise gives, in each 16-bit half, the
+        // two tokens' codes of one head-dim column: the fp16 convert then
+        // picks the half, so one v_perm level is enough.
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
+        for (int w = 0; w < DL / 4; ++w) {
+            uint32_t pr_lo[4], pr_hi[4];       // token pairs (0,1) (2,3) (4,5) (6,7)
 #pragma unroll
-            for (int w = 0; w < DL / 4; ++w) {
-                uint32_t cols[4];
-                transpose4x4(vword(vraw[4 * hs + 0], w), vword(vraw[4 * hs + 1], w),
-                             vword(vraw[4 * hs + 2], w), vword(vraw[4 * hs + 3], w), cols);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) vt[4 * w + c][hs] = cols[c];
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t a = vword(R.vraw[2 * t], w), b = vword(R.vraw[2 * t + 1], w);
+                pr_lo[t] = perm(b, a, 0x05010400u);   // a0 b0 a1 b1
+                pr_hi[t] = perm(b, a, 0x07030602u);   // a2 b2 a3 b3
             }
-        }
 #pragma unroll
-        for (int n = 0; n < DL; ++n) {
-            const f16x8 a = e4m3x8_to_f16x8(vt[n][0], vt[n][1]);
-            st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb, st.acc[n], 0, 0, 0);
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t* src = c < 2 ? pr_lo : pr_hi;
+                uint32_t h[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    h[t] = (c & 1) ? e4m3x2_to_f16x2<true>(src[t]) : e4m3x2_to_f16x2<false>(src[t]);
+                const f16x8 a = __builtin_bit_cast(f16x8, h);
+                st.acc[4 * w + c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb, st.acc[4 * w + c], 0, 0, 0);
+            }
         }
     }
 };
 
-template <int D, int NW, bool SC>
+template <int D, int NW, bool SC, bool BSP2>
 __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams p) {
     constexpr int KSTEPS = D / 32;
     constexpr int DL = D / 16;
+    constexpr int KB = D / 4;
     typedef DecodeTile<D, NW, SC> Tile;
+    typedef typename Tile::Regs Regs;
 
     __shared__ floatx4 lds_acc[NW / 2][DL][64];
     __shared__ float lds_ml[NW / 2][2][64];
@@ -313,38 +387,54 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
     st.l_run = 0.f;
     st.ef_run = 14;
 
-    const uint32_t css = (uint32_t)p.cache_stride_slot;
-    const int64_t cache_bytes = (int64_t)p.num_slots * p.cache_stride_slot;
-    const int64_t h_cache = (int64_t)h * p.cache_stride_head;
-    const int64_t h_scale = (int64_t)h * p.scale_stride_head;
-    const int32_t* bt = p.block_tables + (int64_t)b * p.block_table_stride;
-    const int last_tok = p1 - 1;
-    const int last_base = last_tok & ~15;
-    const int bs = p.block_size;
+    typename Tile::WalkConsts w;
+    w.kbase = p.k_cache + (int64_t)h * p.cache_stride_head;
+    w.vbase = p.v_cache + (int64_t)h * p.cache_stride_head;
+    w.ksbase = p.k_scale + (int64_t)h * p.scale_stride_head;
+    w.vsbase = p.v_scale + (int64_t)h * p.scale_stride_head;
+    w.bt = p.block_tables + (int64_t)b * p.block_table_stride;
+    w.p0 = p0;
+    w.p1 = p1;
+    w.ntiles = ntiles;
+    w.full_end = full_end;
+    w.last_base = (p1 - 1) & ~15;
+    w.nr_codes_full = 15 * (int)p.cache_stride_slot + D;
+    w.nr_scales_full = SC ? 64 : 4 * (15 * (int)p.scale_stride_slot + 1);
 
-    for (int ti = wave; ti < ntiles; ti += NW) {
-        const int t0 = p0 + (ti << 5);
-        // page walk for the two 16-token halves (wave-uniform); descriptors
-        // end at the buffers' ends so no load can leave them
-        TileAddr ta;
+    // loop-invariant load offsets
+    LaneOffsets lo;
+    {
+        const int css = (int)p.cache_stride_slot;
+        const int sss = (int)p.scale_stride_slot;
+        lo.k = li * css + lg * KB;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int stok = min(t0 + 16 * s, last_base);
-            int blk = bt[stok / bs];
-            blk = min(max(blk, 0), p.num_blocks - 1);
-            const int64_t slot = (int64_t)blk * bs + (stok % bs);
-            const int64_t coff = slot * p.cache_stride_slot + h_cache;
-            ta.k[s] = make_rsrc(p.k_cache + coff, cache_bytes - coff);
-            ta.v[s] = make_rsrc(p.v_cache + coff, cache_bytes - coff);
-            const int64_t soff = slot * p.scale_stride_slot + h_scale;
-            ta.ks[s] = make_rsrc(p.k_scale + soff, (p.scale_extent - soff) * 4);
-            ta.vs[s] = make_rsrc(p.v_scale + soff, (p.scale_extent - soff) * 4);
-            ta.lastoff[s] = last_tok - stok;
+        for (int r = 0; r < 4; ++r) {
+            lo.v[r] = (4 * lg + r) * css + li * DL;
+            lo.s[r] = SC ? 16 * lg : 4 * (4 * lg + r) * sss;
         }
-        if (t0 + 32 <= full_end)
-            Tile::template run<false>(p, ta, t0, p1, lim, li, lg, css, qv, st);
-        else
-            Tile::template run<true>(p, ta, t0, p1, lim, li, lg, css, qv, st);
+    }
+
+    // Two tiles in flight per wave: after a tile's QK^T has consumed its K
+    // registers, the loads of the wave's next tile are issued, then the
+    // tile's softmax and PV run while they are in flight (A/B ping-pong).
+    TileAddr ta_a, ta_b;
+    Regs ra, rb;
+    floatx4 sc[2];
+    int ti = wave;
+    Tile::template address<BSP2>(p, w, ti, ta_a);
+    Tile::issue(ta_a, lo, ra);
+    while (ti < ntiles) {
+        Tile::qk(ra, qv, sc);
+        Tile::template address<BSP2>(p, w, ti + NW, ta_b);
+        Tile::issue(ta_b, lo, rb);
+        Tile::rest(p, ta_a, ra, sc, p1, lim, lg, st);
+        ti += NW;
+        if (ti >= ntiles) break;
+        Tile::qk(rb, qv, sc);
+        Tile::template address<BSP2>(p, w, ti + NW, ta_a);
+        Tile::issue(ta_a, lo, ra);
+        Tile::rest(p, ta_b, rb, sc, p1, lim, lg, st);
+        ti += NW;
     }
 
     // per-wave totals for the lane's row
@@ -485,22 +575,22 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
     }
 }
 
-template <int D, int NW>
-hipError_t launch_partitions_nw(const DecodeParams& p, bool sc, hipStream_t stream) {
+template <int D, int NW, bool SC>
+hipError_t launch_partitions_sc(const DecodeParams& p, hipStream_t stream) {
     dim3 grid((unsigned)((int64_t)p.pairs_padded * p.num_kv_heads)), block(NW * 64);
-    if (sc)
-        hipLaunchKernelGGL((decode_partition_kernel<D, NW, true>), grid, block, 0, stream, p);
+    if (p.block_shift >= 0)
+        hipLaunchKernelGGL((decode_partition_kernel<D, NW, SC, true>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((decode_partition_kernel<D, NW, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((decode_partition_kernel<D, NW, SC, false>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_partitions_d(const DecodeParams& p, bool sc, hipStream_t stream) {
-    // waves per workgroup: about 8+ tiles of 32 tokens per wave
-    if (p.partition >= 4096) return launch_partitions_nw<D, 16>(p, sc, stream);
-    if (p.partition >= 2048) return launch_partitions_nw<D, 8>(p, sc, stream);
-    return launch_partitions_nw<D, 4>(p, sc, stream);
+    // Four waves per workgroup: with two tiles of registers per wave a SIMD
+    // holds three waves, so three workgroups share a CU.
+    return sc ? launch_partitions_sc<D, 4, true>(p, stream)
+              : launch_partitions_sc<D, 4, false>(p, stream);
 }
 
 }  // namespace
