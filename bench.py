@@ -125,6 +125,25 @@ def traffic_entry(per_launch_alg_bytes):
     return t.get("bytes_per_launch")
 
 
+def cache_build(torch, fk, k, v, slots, k_cache, v_cache, k_plane, v_plane,
+                stream, chunk=1 << 18):
+    """Quantize+scatter every cached token in chunks of 256K tokens; returns
+    the milliseconds of the whole build. One small call first loads the
+    kernels, so the timed region holds only the build."""
+    fk.kv_quant_scatter(k[:64], v[:64], slots[:64], k_cache, v_cache,
+                        k_plane.t(), v_plane.t())
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(0, slots.numel(), chunk):
+        fk.kv_quant_scatter(k[i:i + chunk], v[i:i + chunk], slots[i:i + chunk],
+                            k_cache, v_cache, k_plane.t(), v_plane.t())
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1)
+
+
 def cpu_baseline(case, dc, lens, max_threads=16, budget_s=30.0):
     """The oracle (as it stands) on the same decode workload: every query row
     of as many of the 64 requests as fit the CPU budget (all of them here),
@@ -211,19 +230,9 @@ def main():
     v_plane = torch.empty_like(k_plane)
     slots_all = L.token_slots.to(dev)
     T = slots_all.numel()
-    # cache build: quantize+scatter of every cached token (chunks of 64K)
-    chunk = 1 << 16
-    torch.cuda.synchronize()
-    t_build = time.perf_counter()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(0, T, chunk):
-        fk.kv_quant_scatter(case.k[i:i + chunk], case.v[i:i + chunk],
-                            slots_all[i:i + chunk], k_cache, v_cache,
-                            k_plane.t(), v_plane.t())
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    build_ms = ev0.elapsed_time(ev1)
+    # cache build: quantize+scatter of every cached token
+    build_ms = cache_build(torch, fk, case.k, case.v, slots_all, k_cache,
+                           v_cache, k_plane, v_plane, stream)
     build_gbs = quant_bytes(T, Hkv, D) / (build_ms * 1e-3) / 1e9
     log(f"cache build: {T} tokens in {build_ms:.2f} ms = {build_gbs:.1f} GB/s")
 
@@ -374,16 +383,9 @@ def longctx_decode(torch, fk, synth, dev, stream, reps=20):
     v_plane = torch.empty_like(k_plane)
     slots = L.token_slots.to(dev)
     T = slots.numel()
-    chunk = 1 << 18
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(0, T, chunk):
-        fk.kv_quant_scatter(case.k[i:i + chunk], case.v[i:i + chunk],
-                            slots[i:i + chunk], k_cache, v_cache, k_plane.t(),
-                            v_plane.t())
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    build_gbs = quant_bytes(T, H, D) / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    build_ms = cache_build(torch, fk, case.k, case.v, slots, k_cache, v_cache,
+                           k_plane, v_plane, stream)
+    build_gbs = quant_bytes(T, H, D) / (build_ms * 1e-3) / 1e9
     del case.k, case.v
     torch.cuda.empty_cache()
     lens = L.context_lens.tolist()

@@ -258,9 +258,6 @@ int fp8kv_paged_decode_partials(
         return fail(FP8KV_E_SHAPE, "slot stride too large for 32-bit in-block offsets");
     if (batch == 0 || s.num_partitions == 0) return ok();
 
-    // float4 scale loads when one head's scales are contiguous per slot
-    const bool scale_contig = scale_stride_slot == 1 && aligned(k_scale, 16) &&
-                              aligned(v_scale, 16) && scale_stride_head % 4 == 0;
     fp8kv::DecodeParams p;
     p.q = static_cast<const uint16_t*>(q);
     p.q_stride_b = q_stride_b;
@@ -289,10 +286,6 @@ int fp8kv_paged_decode_partials(
     p.num_partitions = s.num_partitions;
     p.max_context = max_context;
     p.num_blocks = (int32_t)num_blocks;
-    p.num_slots = num_slots;
-    p.scale_extent = num_slots > 0
-        ? (num_slots - 1) * scale_stride_slot + (int64_t)(num_kv_heads - 1) * scale_stride_head + 1
-        : 0;
     const int64_t pairs = (int64_t)batch * s.num_partitions;
     p.pairs_padded = (int32_t)round_up(pairs, 8);
     if ((int64_t)p.pairs_padded * num_kv_heads > INT32_MAX)
@@ -300,8 +293,7 @@ int fp8kv_paged_decode_partials(
     p.score_scale_log2 = softmax_scale * 1.4426950408889634f;
     p.ws_o = static_cast<float*>(workspace);
     p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + s.lse_offset_bytes);
-    return launched(fp8kv::launch_decode_partitions(p, head_dim, scale_contig,
-                                                    (hipStream_t)stream),
+    return launched(fp8kv::launch_decode_partitions(p, head_dim, (hipStream_t)stream),
                     "paged_decode_partials");
 }
 

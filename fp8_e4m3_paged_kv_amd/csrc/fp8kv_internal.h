@@ -44,8 +44,6 @@ struct DecodeParams {
     int32_t block_size, partition, num_partitions, max_context;
     int32_t block_shift;       // log2(block_size) when a power of two, else -1
     int32_t num_blocks;        // physical blocks: ids are clamped below it
-    int64_t num_slots;         // slots in each code buffer
-    int64_t scale_extent;      // floats addressable in each scale plane
     int32_t pairs_padded;      // (request, partition) pairs rounded up to 8
     float score_scale_log2;    // softmax_scale * log2(e)
     float* ws_o;               // [batch*Hkv*NP*M, head_dim]
@@ -64,8 +62,7 @@ struct MergeParams {
     int32_t total_rows;        // batch * num_kv_heads * m_rows
 };
 
-hipError_t launch_decode_partitions(const DecodeParams& p, int head_dim,
-                                    bool scale_contiguous, hipStream_t stream);
+hipError_t launch_decode_partitions(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_merge(const MergeParams& p, int head_dim,
                                hipStream_t stream);
 

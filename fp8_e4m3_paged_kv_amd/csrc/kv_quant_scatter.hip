@@ -95,21 +95,20 @@ __global__ __launch_bounds__(kQsThreads) void kv_quant_scatter_kernel(QuantScatt
     uint32_t w[kQsSteps][WPL];
     int64_t slot[kQsSteps];
     uint32_t head[kQsSteps];
+    bool valid[kQsSteps];
 
-    // issue every load first
+    // issue every load first, without branches: rows past the end re-read
+    // the last row (nrows >= 1) and are dropped at the store
 #pragma unroll
     for (int s = 0; s < kQsSteps; ++s) {
         const uint32_t r = wave_row0 + 4 * s + sub;
-        const bool in_range = r < nrows;
+        valid[s] = r < nrows;
         uint32_t t, h;
-        split_row<HSHIFT>(in_range ? r : 0, H, t, h);
+        split_row<HSHIFT>(min(r, nrows - 1), H, t, h);
         head[s] = h;
-        slot[s] = in_range ? p.slot_ids[t] : -1;
-        In v;
-        if (in_range)
-            v = *reinterpret_cast<const In*>(src + (int64_t)t * st_tok + (int64_t)h * st_head + li * EPL);
-        else
-            v = In{};
+        slot[s] = p.slot_ids[t];
+        const In v = *reinterpret_cast<const In*>(src + (int64_t)t * st_tok +
+                                                  (int64_t)h * st_head + li * EPL);
         unpack_words(v, w[s]);
     }
 
@@ -164,7 +163,7 @@ __global__ __launch_bounds__(kQsThreads) void kv_quant_scatter_kernel(QuantScatt
         for (int i = 0; i < EPL / 4; ++i)
             packed[i] = e4m3x4_encode(qv[4 * i], qv[4 * i + 1], qv[4 * i + 2], qv[4 * i + 3]);
         const int64_t sl = slot[s];
-        if (sl >= 0 && sl < p.num_slots) {
+        if (valid[s] && sl >= 0 && sl < p.num_slots) {
             uint8_t* dst = cache + sl * p.cache_stride_slot +
                            (int64_t)head[s] * p.cache_stride_head + li * EPL;
             store_codes(dst, packed, (Out*)nullptr);

@@ -119,27 +119,36 @@ struct TileAddr {
 struct LaneOffsets {
     int k;                // token li, head-dim bytes [lg*KB, lg*KB + KB)
     int v[4];             // token 4g + r, head-dim bytes [li*DL, li*DL + DL)
-    int s[4];             // scale of token 4g + r (s[0]: the 4 scales, when contiguous)
+    int s;                // scale of token (4g + li) mod 16
 };
 
-template <int D, bool SC>
+// One tile's loads. The scales arrive one per lane, rotated so that lane
+// r of every 16-lane row g holds token 4g + r: a row broadcast of lane r
+// then gives each lane the scales of the tokens of its score registers.
+template <int D>
 struct TileRegs {
     static constexpr int KV4 = D / 64;      // 16-byte K loads per token
     static constexpr int DL = D / 16;
     typedef typename VRow<DL>::T VT;
     uint4 kraw[2][KV4];
     VT vraw[8];
-    float sk[2][4], sv[2][4];
+    uint32_t ks[2], vs[2];
 };
 
-template <int D, int NW, bool SC>
+// row_newbcast:r -- every lane of a 16-lane row reads lane r of that row
+template <int R>
+__device__ __forceinline__ float row_bcast(uint32_t v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + R, 0xF, 0xF, false));
+}
+
+template <int D, int NW>
 struct DecodeTile {
     static constexpr int KB = D / 4;        // K code bytes per lane per token
     static constexpr int KV4 = KB / 16;     // 16-byte K loads per token
     static constexpr int KSTEPS = D / 32;   // MFMA k-steps over head_dim
     static constexpr int DL = D / 16;       // V bytes per lane per token = PV n-tiles
     typedef typename VRow<DL>::T VT;
-    typedef TileRegs<D, SC> Regs;
+    typedef TileRegs<D> Regs;
 
     // Per-workgroup constants of the page walk.
     struct WalkConsts {
@@ -150,15 +159,29 @@ struct DecodeTile {
         const int32_t* bt;        // this request's block-table row
         int p0, p1, ntiles, full_end, last_base;
         int nr_codes_full;        // num_records of a full half: 15*css + D
-        int nr_scales_full;       // ... of its scales
+        int nr_scales_full;       // ... of its scales: 4*(15*sss + 1)
     };
 
-    // Page walk of tile ti (wave-uniform). Full halves use constant bounds;
-    // a ragged tile's halves end after their last token inside the
-    // partition, and a tile past the wave's last one gets empty ones.
+    // Block-table entries of the wave's tiles k0 .. k0+31 (tile k of the wave
+    // is partition tile wave + NW*k): lane j holds the entry of tile
+    // k0 + j/2, half j%2. Indices are clamped to the partition's last
+    // half, so every lane reads an entry the request owns.
+    template <bool BSP2>
+    static __device__ __forceinline__ int table_window(const DecodeParams& p, const WalkConsts& w,
+                                                       int wave, int k0, int lane) {
+        const int k = k0 + (lane >> 1);
+        const int stok = min(w.p0 + 32 * (wave + NW * k) + 16 * (lane & 1), w.last_base);
+        const int bi = BSP2 ? (stok >> p.block_shift) : stok / p.block_size;
+        return w.bt[bi];
+    }
+
+    // Page walk of tile ti (wave-uniform) from its two table entries. Full
+    // halves use constant bounds; a ragged tile's halves end after their last
+    // token inside the partition, and a tile past the wave's last one gets
+    // empty ones.
     template <bool BSP2>
     static __device__ __forceinline__ void address(const DecodeParams& p, const WalkConsts& w,
-                                                   int ti, TileAddr& ta) {
+                                                   int ti, const int (&blk_in)[2], TileAddr& ta) {
         const int t0 = w.p0 + (ti << 5);
         const bool live = ti < w.ntiles;
         const bool ragged = !live || t0 + 32 > w.p1;
@@ -166,11 +189,9 @@ struct DecodeTile {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int stok = t0 + 16 * s;
-            const int tab = min(stok, w.last_base);     // table entry stays valid
-            const int bi = BSP2 ? (tab >> p.block_shift) : tab / bs;
-            const int bo = BSP2 ? (tab & (bs - 1)) : tab - bi * bs;
-            int blk = w.bt[bi];
-            blk = min(max(blk, 0), p.num_blocks - 1);
+            const int tab = min(stok, w.last_base);
+            const int bo = BSP2 ? (tab & (bs - 1)) : tab % bs;
+            const int blk = min(max(blk_in[s], 0), p.num_blocks - 1);
             const int64_t slot = (int64_t)blk * bs + bo;
             const int64_t coff = slot * p.cache_stride_slot;
             const int64_t soff = slot * p.scale_stride_slot;
@@ -179,9 +200,7 @@ struct DecodeTile {
                 // tokens of this half inside the partition (<= 0: none)
                 const int nvalid = live ? min(16, w.p1 - stok) : 0;
                 nrc = nvalid > 0 ? (nvalid - 1) * (int)p.cache_stride_slot + D : 0;
-                nrs = nvalid <= 0 ? 0
-                    : SC ? 16 * ((nvalid + 3) >> 2)          // whole 4-token groups
-                         : 4 * ((nvalid - 1) * (int)p.scale_stride_slot + 1);
+                nrs = nvalid > 0 ? 4 * ((nvalid - 1) * (int)p.scale_stride_slot + 1) : 0;
             }
             ta.k[s] = make_rsrc(w.kbase + coff, nrc);
             ta.v[s] = make_rsrc(w.vbase + coff, nrc);
@@ -204,21 +223,8 @@ struct DecodeTile {
         for (int e = 0; e < 8; ++e) R.vraw[e] = VRow<DL>::load(ta.v[e >> 2], o.v[e & 3]);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            if (SC) {
-                intx4 a = __builtin_amdgcn_raw_buffer_load_b128(ta.ks[s], o.s[0], 0, 0);
-                intx4 c = __builtin_amdgcn_raw_buffer_load_b128(ta.vs[s], o.s[0], 0, 0);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    R.sk[s][r] = __int_as_float(a[r]);
-                    R.sv[s][r] = __int_as_float(c[r]);
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    R.sk[s][r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(ta.ks[s], o.s[r], 0, 0));
-                    R.sv[s][r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(ta.vs[s], o.s[r], 0, 0));
-                }
-            }
+            R.ks[s] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ta.ks[s], o.s, 0, 0);
+            R.vs[s] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ta.vs[s], o.s, 0, 0);
         }
     }
 
@@ -246,12 +252,16 @@ struct DecodeTile {
         float s2[2][4];
         float sv[2][4];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < 2; ++s) {
+            const float sk[4] = {row_bcast<0>(R.ks[s]), row_bcast<1>(R.ks[s]),
+                                 row_bcast<2>(R.ks[s]), row_bcast<3>(R.ks[s])};
+            sv[s][0] = row_bcast<0>(R.vs[s]);
+            sv[s][1] = row_bcast<1>(R.vs[s]);
+            sv[s][2] = row_bcast<2>(R.vs[s]);
+            sv[s][3] = row_bcast<3>(R.vs[s]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                s2[s][r] = sc[s][r] * (R.sk[s][r] * p.score_scale_log2);
-                sv[s][r] = R.sv[s][r];
-            }
+            for (int r = 0; r < 4; ++r) s2[s][r] = sc[s][r] * (sk[r] * p.score_scale_log2);
+        }
         if (ta.masked) {
 #pragma unroll
             for (int s = 0; s < 2; ++s)
@@ -326,12 +336,12 @@ struct DecodeTile {
     }
 };
 
-template <int D, int NW, bool SC, bool BSP2>
+template <int D, int NW, bool BSP2>
 __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams p) {
     constexpr int KSTEPS = D / 32;
     constexpr int DL = D / 16;
     constexpr int KB = D / 4;
-    typedef DecodeTile<D, NW, SC> Tile;
+    typedef DecodeTile<D, NW> Tile;
     typedef typename Tile::Regs Regs;
 
     __shared__ floatx4 lds_acc[NW / 2][DL][64];
@@ -360,6 +370,27 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
     const int p1 = min(p0 + p.partition, len);
     const int ntiles = (p1 - p0 + 31) >> 5;
 
+    typename Tile::WalkConsts w;
+    w.kbase = p.k_cache + (int64_t)h * p.cache_stride_head;
+    w.vbase = p.v_cache + (int64_t)h * p.cache_stride_head;
+    w.ksbase = p.k_scale + (int64_t)h * p.scale_stride_head;
+    w.vsbase = p.v_scale + (int64_t)h * p.scale_stride_head;
+    w.bt = p.block_tables + (int64_t)b * p.block_table_stride;
+    w.p0 = p0;
+    w.p1 = p1;
+    w.ntiles = ntiles;
+    // tokens below full_end are visible to every row
+    w.full_end = min(p1, len - p.rows + 1);
+    w.last_base = (p1 - 1) & ~15;
+    w.nr_codes_full = 15 * (int)p.cache_stride_slot + D;
+    w.nr_scales_full = 4 * (15 * (int)p.scale_stride_slot + 1);
+
+    // the wave's block-table window (its tiles 0..31), then the next one
+    const int wave_tiles = wave < ntiles ? (ntiles - wave + NW - 1) / NW : 0;
+    int kw = 0;
+    int btw = Tile::template table_window<BSP2>(p, w, wave, 0, lane);
+    int btn = wave_tiles > 32 ? Tile::template table_window<BSP2>(p, w, wave, 32, lane) : 0;
+
     // q operand: row li of the stacked (verify row, query head) block
     bf16x8 qv[KSTEPS];
     int lim;                                   // last token row li sees
@@ -377,8 +408,6 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
         for (int k = 0; k < KSTEPS; ++k) qv[k] = bf16x8{};
         lim = len - 1;
     }
-    // tokens below full_end are visible to every row
-    const int full_end = min(p1, len - p.rows + 1);
 
     WaveState<DL> st;
 #pragma unroll
@@ -387,20 +416,6 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
     st.l_run = 0.f;
     st.ef_run = 14;
 
-    typename Tile::WalkConsts w;
-    w.kbase = p.k_cache + (int64_t)h * p.cache_stride_head;
-    w.vbase = p.v_cache + (int64_t)h * p.cache_stride_head;
-    w.ksbase = p.k_scale + (int64_t)h * p.scale_stride_head;
-    w.vsbase = p.v_scale + (int64_t)h * p.scale_stride_head;
-    w.bt = p.block_tables + (int64_t)b * p.block_table_stride;
-    w.p0 = p0;
-    w.p1 = p1;
-    w.ntiles = ntiles;
-    w.full_end = full_end;
-    w.last_base = (p1 - 1) & ~15;
-    w.nr_codes_full = 15 * (int)p.cache_stride_slot + D;
-    w.nr_scales_full = SC ? 64 : 4 * (15 * (int)p.scale_stride_slot + 1);
-
     // loop-invariant load offsets
     LaneOffsets lo;
     {
@@ -408,11 +423,22 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
         const int sss = (int)p.scale_stride_slot;
         lo.k = li * css + lg * KB;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            lo.v[r] = (4 * lg + r) * css + li * DL;
-            lo.s[r] = SC ? 16 * lg : 4 * (4 * lg + r) * sss;
-        }
+        for (int r = 0; r < 4; ++r) lo.v[r] = (4 * lg + r) * css + li * DL;
+        lo.s = ((4 * lg + li) & 15) * sss * 4;
     }
+
+    // table entries of the wave's tile k (wave-uniform k); windows move
+    // forward 32 tiles at a time, the next one already loaded
+    auto entries = [&](int k, int (&blk)[2]) {
+        if (k - kw >= 32) {
+            kw += 32;
+            btw = btn;
+            if (wave_tiles > kw + 32) btn = Tile::template table_window<BSP2>(p, w, wave, kw + 32, lane);
+        }
+        const int j = 2 * (k - kw);
+        blk[0] = __builtin_amdgcn_readlane(btw, j);
+        blk[1] = __builtin_amdgcn_readlane(btw, j + 1);
+    };
 
     // Two tiles in flight per wave: after a tile's QK^T has consumed its K
     // registers, the loads of the wave's next tile are issued, then the
@@ -420,21 +446,28 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
     TileAddr ta_a, ta_b;
     Regs ra, rb;
     floatx4 sc[2];
+    int blk[2];
+    int k = 0;
     int ti = wave;
-    Tile::template address<BSP2>(p, w, ti, ta_a);
+    entries(0, blk);
+    Tile::template address<BSP2>(p, w, ti, blk, ta_a);
     Tile::issue(ta_a, lo, ra);
     while (ti < ntiles) {
         Tile::qk(ra, qv, sc);
-        Tile::template address<BSP2>(p, w, ti + NW, ta_b);
+        entries(k + 1, blk);
+        Tile::template address<BSP2>(p, w, ti + NW, blk, ta_b);
         Tile::issue(ta_b, lo, rb);
         Tile::rest(p, ta_a, ra, sc, p1, lim, lg, st);
         ti += NW;
+        ++k;
         if (ti >= ntiles) break;
         Tile::qk(rb, qv, sc);
-        Tile::template address<BSP2>(p, w, ti + NW, ta_a);
+        entries(k + 1, blk);
+        Tile::template address<BSP2>(p, w, ti + NW, blk, ta_a);
         Tile::issue(ta_a, lo, ra);
         Tile::rest(p, ta_b, rb, sc, p1, lim, lg, st);
         ti += NW;
+        ++k;
     }
 
     // per-wave totals for the lane's row
@@ -458,13 +491,13 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
         __syncthreads();
         if (wave < half) {
             const float mo = lds_ml[wave][0][lane];
-            const float lo = lds_ml[wave][1][lane];
+            const float lo_ = lds_ml[wave][1][lane];
             const float mm = fmaxf(st.m_run, mo);
             const float fa = __builtin_amdgcn_exp2f(st.m_run - mm);
             const float fb = __builtin_amdgcn_exp2f(mo - mm);
 #pragma unroll
             for (int n = 0; n < DL; ++n) st.acc[n] = st.acc[n] * fa + lds_acc[wave][n][lane] * fb;
-            st.l_run = st.l_run * fa + lo * fb;
+            st.l_run = st.l_run * fa + lo_ * fb;
             st.m_run = mm;
         }
         __syncthreads();
@@ -575,30 +608,24 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
     }
 }
 
-template <int D, int NW, bool SC>
-hipError_t launch_partitions_sc(const DecodeParams& p, hipStream_t stream) {
-    dim3 grid((unsigned)((int64_t)p.pairs_padded * p.num_kv_heads)), block(NW * 64);
-    if (p.block_shift >= 0)
-        hipLaunchKernelGGL((decode_partition_kernel<D, NW, SC, true>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((decode_partition_kernel<D, NW, SC, false>), grid, block, 0, stream, p);
-    return hipGetLastError();
-}
-
 template <int D>
-hipError_t launch_partitions_d(const DecodeParams& p, bool sc, hipStream_t stream) {
+hipError_t launch_partitions_d(const DecodeParams& p, hipStream_t stream) {
     // Four waves per workgroup: with two tiles of registers per wave a SIMD
     // holds three waves, so three workgroups share a CU.
-    return sc ? launch_partitions_sc<D, 4, true>(p, stream)
-              : launch_partitions_sc<D, 4, false>(p, stream);
+    constexpr int NW = 4;
+    dim3 grid((unsigned)((int64_t)p.pairs_padded * p.num_kv_heads)), block(NW * 64);
+    if (p.block_shift >= 0)
+        hipLaunchKernelGGL((decode_partition_kernel<D, NW, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_partition_kernel<D, NW, false>), grid, block, 0, stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_partitions(const DecodeParams& p, int head_dim,
-                                    bool scale_contiguous, hipStream_t stream) {
-    if (head_dim == 128) return launch_partitions_d<128>(p, scale_contiguous, stream);
-    return launch_partitions_d<64>(p, scale_contiguous, stream);
+hipError_t launch_decode_partitions(const DecodeParams& p, int head_dim, hipStream_t stream) {
+    if (head_dim == 128) return launch_partitions_d<128>(p, stream);
+    return launch_partitions_d<64>(p, stream);
 }
 
 hipError_t launch_decode_merge(const MergeParams& p, int head_dim, hipStream_t stream) {
