@@ -7,9 +7,10 @@ context lengths uniform in [1024, 32768], 32 query / 8 KV heads, head_dim
   1. kv_quant_scatter of the step's 64 new K/V rows (one per request, at the
      slot of its last token), and
   2. paged GQA decode attention of the 64 query rows over the whole E4M3
-     cache (partition phase, then log-sum-exp merge).
+     cache (split phase: every KV head's tile sequence cut into equal
+     ranges, one wave each; then the log-sum-exp merge).
 `value` is the step's algorithmic HBM bytes / step time (GB/s). The
-dominant kernel (the decode partition kernel) is also timed alone with HIP
+dominant kernel (the decode split kernel) is also timed alone with HIP
 events on the stream it runs on, for the roofline object.
 
 Also measured in the same run (reported under "also"): quantize+scatter
@@ -17,7 +18,7 @@ tokens/s on the 4096-token prefill chunk (fused qkv, K/V strided slices,
 random slots in a 1,048,576-slot pool, 32 rotating input sets so reads come
 from HBM), the cache-build bandwidth, and the long-context verify decode
 (4 requests of 256K..1M tokens, 4 verify rows, 16/4 heads, 64-token
-blocks, 8192-token partitions).
+blocks).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -35,7 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partition_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_traffic.json")
 KERNEL_SOURCES = ["fp8_e4m3_paged_kv_amd/csrc/paged_decode.hip",
                   "fp8_e4m3_paged_kv_amd/csrc/fp8kv_device.h"]
 
@@ -45,8 +46,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--partition", type=int, default=0,
-                    help="decode partition tokens (0 = library choice)")
+    ap.add_argument("--ranges", type=int, default=0,
+                    help="decode split: ranges per KV head (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the prefill-chunk and long-context extras")
@@ -113,7 +114,7 @@ def time_events(fn, n, stream):
 
 
 def traffic_entry(per_launch_alg_bytes):
-    """HBM traffic of the partition kernel from the committed rocprofv3
+    """HBM traffic of the split kernel from the committed rocprofv3
     counter summary, if it was taken on the current kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
@@ -248,12 +249,12 @@ def main():
     bt = L.block_tables.to(dev)
     cl = L.context_lens.to(dev)
     maxc = 32768
-    part = fk.decode_partition_tokens(B, R, Hq, Hkv, D, bs, maxc, args.partition)
-    ws = torch.empty(fk.decode_workspace_bytes(B, R, Hq, Hkv, D, bs, maxc, part),
+    nr = fk.decode_num_ranges(Hkv, args.ranges)
+    ws = torch.empty(fk.decode_workspace_bytes(B, R, Hq, Hkv, D, nr),
                      dtype=torch.uint8, device=dev)
     out = torch.empty((B, R, Hq, D), dtype=torch.bfloat16, device=dev)
     kw = dict(num_kv_heads=Hkv, block_size=bs, softmax_scale=case.softmax_scale,
-              max_context=maxc, partition_tokens=part)
+              max_context=maxc, num_ranges=nr)
 
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -269,9 +270,8 @@ def main():
                                  bt, cl, workspace=ws, **kw)
         if i is not None:
             ev_b[i].record(stream)
-        fk.paged_decode_merge(ws, cl, out, rows=R, num_q_heads=Hq,
-                              num_kv_heads=Hkv, block_size=bs, max_context=maxc,
-                              partition_tokens=part)
+        fk.paged_decode_merge(ws, out, rows=R, num_q_heads=Hq,
+                              num_kv_heads=Hkv, num_ranges=nr)
 
     for _ in range(args.warmup):
         step()
@@ -295,7 +295,7 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     part_bytes = dec_bytes - B * R * Hq * D * 2     # the merge writes out
     achieved = part_bytes / (part_avg_ms * 1e-3) / 1e9
-    log(f"decode step: {ms_per_step * 1e3:.1f} us, partition kernel "
+    log(f"decode step: {ms_per_step * 1e3:.1f} us, split kernel "
         f"{part_avg_ms * 1e3:.1f} us = {achieved:.0f} GB/s")
     traffic = traffic_entry(part_bytes)
 
@@ -316,13 +316,14 @@ def main():
                                "decode, 64 requests, lengths U[1024,32768]",
                    "batch": B, "context_tokens": sum(lens), "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "block_size": bs,
-                   "partition_tokens": part, "scale_planes": "head-major [Hkv, slots]"},
+                   "decode_ranges_per_kv_head": nr,
+                   "scale_planes": "head-major [Hkv, slots]"},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "decode_partition_kernel",
+                     "kernel": "decode_split_kernel",
                      "alg_bytes_per_launch": part_bytes,
                      "avg_launch_us": round(part_avg_ms * 1e3, 2)},
         "cpu_baseline": None,
@@ -390,16 +391,16 @@ def longctx_decode(torch, fk, synth, dev, stream, reps=20):
     torch.cuda.empty_cache()
     lens = L.context_lens.tolist()
     maxc = max(lens)
-    part = case.partition_tokens
     B, R, Hq = 4, 4, 16
     q = case.q.to(dev)
     bt = L.block_tables.to(dev)
     cl = L.context_lens.to(dev)
-    ws = torch.empty(fk.decode_workspace_bytes(B, R, Hq, H, D, bs, maxc, part),
+    nr = fk.decode_num_ranges(H)
+    ws = torch.empty(fk.decode_workspace_bytes(B, R, Hq, H, D, nr),
                      dtype=torch.uint8, device=dev)
     out = torch.empty((B, R, Hq, D), dtype=torch.bfloat16, device=dev)
     kw = dict(num_kv_heads=H, block_size=bs, softmax_scale=case.softmax_scale,
-              max_context=maxc, partition_tokens=part, workspace=ws)
+              max_context=maxc, num_ranges=nr, workspace=ws)
 
     def partials():
         fk.paged_decode_partials(q, k_cache, v_cache, k_plane.t(), v_plane.t(),
@@ -417,8 +418,8 @@ def longctx_decode(torch, fk, synth, dev, stream, reps=20):
     f_avg = sum(fm) / len(fm)
     res = {"longctx_decode_us": round(f_avg * 1e3, 1),
            "longctx_decode_GBps": round(dec / (f_avg * 1e-3) / 1e9, 1),
-           "longctx_partition_kernel_us": round(p_avg * 1e3, 1),
-           "longctx_partition_kernel_GBps": round((dec - B * R * Hq * D * 2) / (p_avg * 1e-3) / 1e9, 1),
+           "longctx_split_kernel_us": round(p_avg * 1e3, 1),
+           "longctx_split_kernel_GBps": round((dec - B * R * Hq * D * 2) / (p_avg * 1e-3) / 1e9, 1),
            "longctx_cache_build_GBps": round(build_gbs, 1)}
     del k_cache, v_cache, k_plane, v_plane
     torch.cuda.empty_cache()

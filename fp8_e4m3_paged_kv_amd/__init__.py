@@ -64,15 +64,13 @@ def lib():
     L.fp8kv_paged_decode_attn_fp8.restype = ctypes.c_int
     L.fp8kv_paged_decode_partials.argtypes = dec + [P]
     L.fp8kv_paged_decode_partials.restype = ctypes.c_int
-    L.fp8kv_paged_decode_merge.argtypes = [P, I32, I32, I32, I32, I32, I32,
-                                           I32, I32, P, SZ, P, I64, I64, I64,
-                                           I32, P]
+    L.fp8kv_paged_decode_merge.argtypes = [I32, I32, I32, I32, I32, I32, P,
+                                           SZ, P, I64, I64, I64, I32, P]
     L.fp8kv_paged_decode_merge.restype = ctypes.c_int
-    shape = [I32] * 8
-    L.fp8kv_paged_decode_workspace_bytes.argtypes = shape
+    L.fp8kv_paged_decode_workspace_bytes.argtypes = [I32] * 6
     L.fp8kv_paged_decode_workspace_bytes.restype = I64
-    L.fp8kv_paged_decode_partition_tokens.argtypes = shape
-    L.fp8kv_paged_decode_partition_tokens.restype = I32
+    L.fp8kv_paged_decode_num_ranges.argtypes = [I32, I32]
+    L.fp8kv_paged_decode_num_ranges.restype = I32
     _lib = L
     return L
 
@@ -160,20 +158,19 @@ def kv_quant_scatter(k: torch.Tensor, v: torch.Tensor, slot_ids: torch.Tensor,
 
 
 def decode_workspace_bytes(batch, rows, num_q_heads, num_kv_heads, head_dim,
-                           block_size, max_context, partition_tokens=0) -> int:
+                           num_ranges=0) -> int:
+    """Workspace bytes of a decode call (num_ranges 0 = library choice)."""
     n = lib().fp8kv_paged_decode_workspace_bytes(
-        batch, rows, num_q_heads, num_kv_heads, head_dim, block_size,
-        max_context, partition_tokens)
+        batch, rows, num_q_heads, num_kv_heads, head_dim, int(num_ranges))
     if n < 0:
         _check(int(n))
     return int(n)
 
 
-def decode_partition_tokens(batch, rows, num_q_heads, num_kv_heads, head_dim,
-                            block_size, max_context, partition_tokens=0) -> int:
-    n = lib().fp8kv_paged_decode_partition_tokens(
-        batch, rows, num_q_heads, num_kv_heads, head_dim, block_size,
-        max_context, partition_tokens)
+def decode_num_ranges(num_kv_heads, num_ranges=0) -> int:
+    """The number of ranges each KV head's tile sequence is split into
+    (resolves 0 on the current device)."""
+    n = lib().fp8kv_paged_decode_num_ranges(num_kv_heads, int(num_ranges))
     if n < 0:
         _check(int(n))
     return int(n)
@@ -181,7 +178,7 @@ def decode_partition_tokens(batch, rows, num_q_heads, num_kv_heads, head_dim,
 
 def _decode_args(q, k_cache, v_cache, k_scale, v_scale, block_tables,
                  context_lens, num_kv_heads, block_size, softmax_scale,
-                 max_context, partition_tokens, workspace):
+                 max_context, num_ranges, workspace):
     _dev(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens)
     if q.dim() != 4 or q.stride(3) != 1:
         raise ValueError("q must be [B, R, Hq, D] with contiguous head_dim")
@@ -199,8 +196,7 @@ def _decode_args(q, k_cache, v_cache, k_scale, v_scale, block_tables,
     sss, ssh = _scale_strides(k_scale)
     if _scale_strides(v_scale) != (sss, ssh):
         raise ValueError("k_scale and v_scale must share strides")
-    ws_bytes = decode_workspace_bytes(B, R, Hq, num_kv_heads, D, block_size,
-                                      max_context, partition_tokens)
+    ws_bytes = decode_workspace_bytes(B, R, Hq, num_kv_heads, D, num_ranges)
     if workspace is None:
         workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8,
                                 device=q.device)
@@ -210,14 +206,14 @@ def _decode_args(q, k_cache, v_cache, k_scale, v_scale, block_tables,
             css, csh, k_scale.data_ptr(), v_scale.data_ptr(), sss, ssh, S,
             block_tables.data_ptr(), block_tables.stride(0),
             context_lens.data_ptr(), B, R, Hq, num_kv_heads, D, block_size,
-            float(softmax_scale), int(partition_tokens), int(max_context),
+            float(softmax_scale), int(num_ranges), int(max_context),
             workspace.data_ptr(), workspace.numel() * workspace.element_size()]
     return args, workspace
 
 
 def paged_decode_attn_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables,
                           context_lens, *, num_kv_heads, block_size,
-                          softmax_scale, max_context, partition_tokens=0,
+                          softmax_scale, max_context, num_ranges=0,
                           out=None, out_dtype=torch.bfloat16, workspace=None):
     """Paged GQA decode attention over the E4M3 cache. q: [B, R, Hq, D]
     bf16 (R verify rows, causal among themselves). Returns out [B, R, Hq, D]
@@ -225,7 +221,7 @@ def paged_decode_attn_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables,
     args, workspace = _decode_args(q, k_cache, v_cache, k_scale, v_scale,
                                    block_tables, context_lens, num_kv_heads,
                                    block_size, softmax_scale, max_context,
-                                   partition_tokens, workspace)
+                                   num_ranges, workspace)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     _dev(out)
@@ -239,27 +235,25 @@ def paged_decode_attn_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables,
 
 def paged_decode_partials(q, k_cache, v_cache, k_scale, v_scale, block_tables,
                           context_lens, *, num_kv_heads, block_size,
-                          softmax_scale, max_context, partition_tokens=0,
+                          softmax_scale, max_context, num_ranges=0,
                           workspace=None):
-    """Partition phase only; returns the workspace holding the partials."""
+    """Split phase only; returns the workspace holding the partials."""
     args, workspace = _decode_args(q, k_cache, v_cache, k_scale, v_scale,
                                    block_tables, context_lens, num_kv_heads,
                                    block_size, softmax_scale, max_context,
-                                   partition_tokens, workspace)
+                                   num_ranges, workspace)
     _check(lib().fp8kv_paged_decode_partials(*args, _stream(q.device)))
     return workspace
 
 
-def paged_decode_merge(workspace, context_lens, out, *, rows, num_q_heads,
-                       num_kv_heads, block_size, max_context,
-                       partition_tokens=0):
-    """Log-sum-exp merge of the partials in ``workspace`` into out
-    [B, R, Hq, D]."""
-    _dev(workspace, context_lens, out)
+def paged_decode_merge(workspace, out, *, rows, num_q_heads, num_kv_heads,
+                       num_ranges=0):
+    """Log-sum-exp merge of the partials in ``workspace`` (written by
+    paged_decode_partials with the same num_ranges) into out [B, R, Hq, D]."""
+    _dev(workspace, out)
     B, R, Hq, D = out.shape
     _check(lib().fp8kv_paged_decode_merge(
-        context_lens.data_ptr(), B, rows, num_q_heads, num_kv_heads, D,
-        block_size, int(partition_tokens), int(max_context),
+        B, rows, num_q_heads, num_kv_heads, D, int(num_ranges),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
         _TORCH_DTYPE[out.dtype], _stream(out.device)))

@@ -30,31 +30,42 @@ bool aligned(const void* p, uintptr_t a) {
     return (reinterpret_cast<uintptr_t>(p) % a) == 0;
 }
 
-constexpr int kTile = 32;          // tokens per decode tile
 constexpr int kMaxStackedRows = 16; // MFMA M dimension
+constexpr int kMaxRanges = 1 << 20;  // bound of the decode split
 
 struct DecodeShape {
-    int32_t partition = 0;
-    int32_t num_partitions = 0;
+    int32_t num_ranges = 0;
     int32_t group = 0;
     int32_t m_rows = 0;
-    int64_t ws_o_floats = 0;
-    int64_t ws_lse_floats = 0;
-    int64_t ws_bytes = 0;
+    int64_t pieces = 0;             // batch + num_ranges - 1
     int64_t lse_offset_bytes = 0;
+    int64_t prefix_offset_bytes = 0;
+    int64_t ws_bytes = 0;
 };
 
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
+// Ranges the library picks for num_ranges == 0: one wave per (range, KV
+// head) and one wave per SIMD of the current device.
+int auto_ranges(int32_t num_kv_heads, int32_t* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return fail(FP8KV_E_LAUNCH, "no HIP device to size the decode split for");
+    const int waves = fp8kv::decode_wave_slots(dev);
+    if (waves <= 0)
+        return fail(FP8KV_E_LAUNCH, "cannot query the CU count of device %d", dev);
+    *out = waves / num_kv_heads > 1 ? waves / num_kv_heads : 1;
+    return FP8KV_OK;
+}
+
 // Shape rules shared by the workspace query and the calls.
 int decode_shape(int32_t batch, int32_t rows, int32_t num_q_heads,
-                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                 int32_t max_context, int32_t partition_tokens,
+                 int32_t num_kv_heads, int32_t head_dim, int32_t num_ranges,
                  DecodeShape* s) {
     if (head_dim != 64 && head_dim != 128)
         return fail(FP8KV_E_UNSUPPORTED, "head_dim %d: only 64 and 128 are supported", head_dim);
-    if (batch < 0 || max_context < 0)
-        return fail(FP8KV_E_SHAPE, "batch (%d) and max_context (%d) must be >= 0", batch, max_context);
+    if (batch < 0)
+        return fail(FP8KV_E_SHAPE, "batch (%d) must be >= 0", batch);
     if (rows < 1 || num_q_heads < 1 || num_kv_heads < 1)
         return fail(FP8KV_E_SHAPE, "rows, num_q_heads and num_kv_heads must be >= 1");
     if (num_q_heads % num_kv_heads != 0)
@@ -65,29 +76,24 @@ int decode_shape(int32_t batch, int32_t rows, int32_t num_q_heads,
         return fail(FP8KV_E_UNSUPPORTED,
                     "rows * (num_q_heads / num_kv_heads) = %d exceeds the %d-row tile",
                     rows * group, kMaxStackedRows);
-    if (block_size < 16 || block_size % 16 != 0)
-        return fail(FP8KV_E_UNSUPPORTED, "block_size %d: must be a positive multiple of 16", block_size);
-    if (partition_tokens < 0 || partition_tokens % kTile != 0)
-        return fail(FP8KV_E_SHAPE, "partition_tokens %d: must be 0 (auto) or a positive multiple of %d",
-                    partition_tokens, kTile);
-    int32_t part = partition_tokens;
-    if (part == 0) {
-        // Library choice: long contexts get long partitions (fewer partials
-        // to merge, more tiles per wave); short ones keep enough
-        // workgroups to fill 256 CUs.
-        if (max_context >= 131072) part = 8192;
-        else if (max_context > 1024) part = 1024;
-        else part = (int32_t)round_up(max_context > 0 ? max_context : 1, kTile);
+    if (num_ranges < 0 || num_ranges > kMaxRanges)
+        return fail(FP8KV_E_SHAPE, "num_ranges %d: must be 0 (auto) or 1..%d", num_ranges, kMaxRanges);
+    int32_t R = num_ranges;
+    if (R == 0) {
+        const int st = auto_ranges(num_kv_heads, &R);
+        if (st != FP8KV_OK) return st;
     }
-    s->partition = part;
+    s->num_ranges = R;
     s->group = group;
     s->m_rows = rows * group;
-    s->num_partitions = max_context == 0 ? 0 : (int32_t)((max_context + part - 1) / part);
-    const int64_t units = (int64_t)batch * num_kv_heads * s->num_partitions * s->m_rows;
-    s->ws_o_floats = units * head_dim;
-    s->ws_lse_floats = units;
-    s->lse_offset_bytes = round_up(s->ws_o_floats * 4, 256);
-    s->ws_bytes = s->lse_offset_bytes + round_up(s->ws_lse_floats * 4, 256);
+    s->pieces = (int64_t)batch + R - 1;
+    const int64_t units = s->pieces * num_kv_heads * s->m_rows;
+    if (units * head_dim > INT64_C(1) << 40)
+        return fail(FP8KV_E_SHAPE, "decode workspace of %lld partial rows is too large",
+                    (long long)units);
+    s->lse_offset_bytes = round_up(units * head_dim * 4, 256);
+    s->prefix_offset_bytes = s->lse_offset_bytes + round_up(units * 4, 256);
+    s->ws_bytes = s->prefix_offset_bytes + round_up(((int64_t)batch + 1) * 4, 256);
     return FP8KV_OK;
 }
 
@@ -187,24 +193,19 @@ int fp8kv_kv_quant_scatter(
 
 int64_t fp8kv_paged_decode_workspace_bytes(
     int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
-    int32_t head_dim, int32_t block_size, int32_t max_context,
-    int32_t partition_tokens) {
+    int32_t head_dim, int32_t num_ranges) {
     DecodeShape s;
-    int st = decode_shape(batch, rows, num_q_heads, num_kv_heads, head_dim,
-                          block_size, max_context, partition_tokens, &s);
+    int st = decode_shape(batch, rows, num_q_heads, num_kv_heads, head_dim, num_ranges, &s);
     if (st != FP8KV_OK) return st;
     return s.ws_bytes;
 }
 
-int32_t fp8kv_paged_decode_partition_tokens(
-    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
-    int32_t head_dim, int32_t block_size, int32_t max_context,
-    int32_t partition_tokens) {
+int32_t fp8kv_paged_decode_num_ranges(int32_t num_kv_heads, int32_t num_ranges) {
+    if (num_kv_heads < 1) return fail(FP8KV_E_SHAPE, "num_kv_heads must be >= 1");
     DecodeShape s;
-    int st = decode_shape(batch, rows, num_q_heads, num_kv_heads, head_dim,
-                          block_size, max_context, partition_tokens, &s);
+    int st = decode_shape(0, 1, num_kv_heads, num_kv_heads, 128, num_ranges, &s);
     if (st != FP8KV_OK) return st;
-    return s.partition;
+    return s.num_ranges;
 }
 
 int fp8kv_paged_decode_partials(
@@ -216,19 +217,24 @@ int fp8kv_paged_decode_partials(
     const int32_t* block_tables, int64_t block_table_stride,
     const int32_t* context_lens, int32_t batch, int32_t rows,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-    int32_t block_size, float softmax_scale, int32_t partition_tokens,
+    int32_t block_size, float softmax_scale, int32_t num_ranges,
     int32_t max_context, void* workspace, size_t workspace_bytes,
     void* stream) {
     DecodeShape s;
-    int st = decode_shape(batch, rows, num_q_heads, num_kv_heads, head_dim,
-                          block_size, max_context, partition_tokens, &s);
+    int st = decode_shape(batch, rows, num_q_heads, num_kv_heads, head_dim, num_ranges, &s);
     if (st != FP8KV_OK) return st;
     if (q_dtype != FP8KV_DTYPE_BF16)
         return fail(FP8KV_E_UNSUPPORTED, "q_dtype %d: only BF16 queries", q_dtype);
+    if (block_size < 16 || block_size % 16 != 0)
+        return fail(FP8KV_E_UNSUPPORTED, "block_size %d: must be a positive multiple of 16", block_size);
+    if (max_context < 0)
+        return fail(FP8KV_E_SHAPE, "max_context (%d) must be >= 0", max_context);
+    if ((int64_t)batch * ((max_context + 31) / 32) > INT32_MAX)
+        return fail(FP8KV_E_SHAPE, "batch * max_context too large for 32-bit tile counts");
     if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables ||
         !context_lens)
         return fail(FP8KV_E_NULL, "paged_decode: a required pointer is NULL");
-    if (!workspace && s.ws_bytes > 0)
+    if (!workspace)
         return fail(FP8KV_E_WORKSPACE, "paged_decode: workspace is NULL");
     if ((int64_t)workspace_bytes < s.ws_bytes)
         return fail(FP8KV_E_WORKSPACE, "workspace %zu bytes < required %lld",
@@ -245,7 +251,7 @@ int fp8kv_paged_decode_partials(
         return fail(FP8KV_E_ALIGN, "cache rows must start on 16-byte boundaries");
     if (!aligned(k_scale, 4) || !aligned(v_scale, 4) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
-        (workspace && !aligned(workspace, 256)))
+        !aligned(workspace, 256))
         return fail(FP8KV_E_ALIGN, "scale planes, tables or workspace misaligned");
     const int64_t num_blocks = num_slots / block_size;
     if (batch > 0 && max_context > 0 && num_blocks < 1)
@@ -256,7 +262,7 @@ int fp8kv_paged_decode_partials(
     // in-block offsets are 32-bit: 16 slots of codes / scales must fit
     if (cache_stride_slot > (INT32_MAX / 16) || scale_stride_slot > (INT32_MAX / 64))
         return fail(FP8KV_E_SHAPE, "slot stride too large for 32-bit in-block offsets");
-    if (batch == 0 || s.num_partitions == 0) return ok();
+    if (batch == 0) return ok();
 
     fp8kv::DecodeParams p;
     p.q = static_cast<const uint16_t*>(q);
@@ -282,36 +288,31 @@ int fp8kv_paged_decode_partials(
     p.m_rows = s.m_rows;
     p.block_size = block_size;
     p.block_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
-    p.partition = s.partition;
-    p.num_partitions = s.num_partitions;
     p.max_context = max_context;
-    p.num_blocks = (int32_t)num_blocks;
-    const int64_t pairs = (int64_t)batch * s.num_partitions;
-    p.pairs_padded = (int32_t)round_up(pairs, 8);
-    if ((int64_t)p.pairs_padded * num_kv_heads > INT32_MAX)
-        return fail(FP8KV_E_SHAPE, "too many (request, partition, head) units");
+    p.num_blocks = (int32_t)(num_blocks > 0 ? num_blocks : 1);
+    p.num_ranges = s.num_ranges;
+    p.wgs_per_range = (num_kv_heads % 4 == 0 && num_kv_heads > 4) ? num_kv_heads / 4 : 1;
     p.score_scale_log2 = softmax_scale * 1.4426950408889634f;
-    p.ws_o = static_cast<float*>(workspace);
-    p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + s.lse_offset_bytes);
+    char* ws = static_cast<char*>(workspace);
+    p.ws_o = reinterpret_cast<float*>(ws);
+    p.ws_lse = reinterpret_cast<float*>(ws + s.lse_offset_bytes);
+    p.ws_prefix = reinterpret_cast<int32_t*>(ws + s.prefix_offset_bytes);
     return launched(fp8kv::launch_decode_partitions(p, head_dim, (hipStream_t)stream),
                     "paged_decode_partials");
 }
 
 int fp8kv_paged_decode_merge(
-    const int32_t* context_lens, int32_t batch, int32_t rows,
-    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-    int32_t block_size, int32_t partition_tokens, int32_t max_context,
-    const void* workspace, size_t workspace_bytes, void* out,
-    int64_t out_stride_b, int64_t out_stride_row, int64_t out_stride_head,
-    int32_t out_dtype, void* stream) {
+    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t num_ranges, const void* workspace,
+    size_t workspace_bytes, void* out, int64_t out_stride_b,
+    int64_t out_stride_row, int64_t out_stride_head, int32_t out_dtype,
+    void* stream) {
     DecodeShape s;
-    int st = decode_shape(batch, rows, num_q_heads, num_kv_heads, head_dim,
-                          block_size, max_context, partition_tokens, &s);
+    int st = decode_shape(batch, rows, num_q_heads, num_kv_heads, head_dim, num_ranges, &s);
     if (st != FP8KV_OK) return st;
     if ((st = check_out_dtype(out_dtype)) != FP8KV_OK) return st;
-    if (!context_lens || !out)
-        return fail(FP8KV_E_NULL, "paged_decode_merge: a required pointer is NULL");
-    if (!workspace && s.ws_bytes > 0)
+    if (!out) return fail(FP8KV_E_NULL, "paged_decode_merge: out is NULL");
+    if (!workspace)
         return fail(FP8KV_E_WORKSPACE, "paged_decode_merge: workspace is NULL");
     if ((int64_t)workspace_bytes < s.ws_bytes)
         return fail(FP8KV_E_WORKSPACE, "workspace %zu bytes < required %lld",
@@ -319,16 +320,14 @@ int fp8kv_paged_decode_merge(
     if (out_stride_b < 0 || out_stride_row < 0 || out_stride_head < 0)
         return fail(FP8KV_E_STRIDE, "paged_decode_merge: negative stride");
     const int esz = out_dtype == FP8KV_DTYPE_FP32 ? 4 : 2;
-    if (!aligned(out, esz) || !aligned(context_lens, 4) ||
-        (workspace && !aligned(workspace, 256)))
-        return fail(FP8KV_E_ALIGN, "out, context_lens or workspace misaligned");
+    if (!aligned(out, esz) || !aligned(workspace, 256))
+        return fail(FP8KV_E_ALIGN, "out or workspace misaligned");
     if (batch == 0) return ok();
     fp8kv::MergeParams p;
-    p.context_lens = context_lens;
-    p.ws_o = static_cast<const float*>(workspace);
-    p.ws_lse = workspace ? reinterpret_cast<const float*>(
-                               static_cast<const char*>(workspace) + s.lse_offset_bytes)
-                         : nullptr;
+    const char* ws = static_cast<const char*>(workspace);
+    p.ws_o = reinterpret_cast<const float*>(ws);
+    p.ws_lse = reinterpret_cast<const float*>(ws + s.lse_offset_bytes);
+    p.ws_prefix = reinterpret_cast<const int32_t*>(ws + s.prefix_offset_bytes);
     p.out = out;
     p.out_stride_b = out_stride_b;
     p.out_stride_row = out_stride_row;
@@ -338,9 +337,7 @@ int fp8kv_paged_decode_merge(
     p.num_kv_heads = num_kv_heads;
     p.group = s.group;
     p.m_rows = s.m_rows;
-    p.partition = s.partition;
-    p.num_partitions = s.num_partitions;
-    p.max_context = max_context;
+    p.num_ranges = s.num_ranges;
     p.total_rows = batch * num_kv_heads * s.m_rows;
     return launched(fp8kv::launch_decode_merge(p, head_dim, (hipStream_t)stream),
                     "paged_decode_merge");
@@ -355,7 +352,7 @@ int fp8kv_paged_decode_attn_fp8(
     const int32_t* block_tables, int64_t block_table_stride,
     const int32_t* context_lens, int32_t batch, int32_t rows,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-    int32_t block_size, float softmax_scale, int32_t partition_tokens,
+    int32_t block_size, float softmax_scale, int32_t num_ranges,
     int32_t max_context, void* workspace, size_t workspace_bytes, void* out,
     int64_t out_stride_b, int64_t out_stride_row, int64_t out_stride_head,
     int32_t out_dtype, void* stream) {
@@ -372,13 +369,13 @@ int fp8kv_paged_decode_attn_fp8(
         cache_stride_slot, cache_stride_head, k_scale, v_scale,
         scale_stride_slot, scale_stride_head, num_slots, block_tables,
         block_table_stride, context_lens, batch, rows, num_q_heads,
-        num_kv_heads, head_dim, block_size, softmax_scale, partition_tokens,
+        num_kv_heads, head_dim, block_size, softmax_scale, num_ranges,
         max_context, workspace, workspace_bytes, stream);
     if (st != FP8KV_OK) return st;
     return fp8kv_paged_decode_merge(
-        context_lens, batch, rows, num_q_heads, num_kv_heads, head_dim,
-        block_size, partition_tokens, max_context, workspace, workspace_bytes,
-        out, out_stride_b, out_stride_row, out_stride_head, out_dtype, stream);
+        batch, rows, num_q_heads, num_kv_heads, head_dim, num_ranges,
+        workspace, workspace_bytes, out, out_stride_b, out_stride_row,
+        out_stride_head, out_dtype, stream);
 }
 
 }  // extern "C"

@@ -41,26 +41,31 @@ struct DecodeParams {
     int64_t block_table_stride;
     const int32_t* context_lens;
     int32_t batch, rows, num_q_heads, num_kv_heads, group, m_rows;
-    int32_t block_size, partition, num_partitions, max_context;
+    int32_t block_size, max_context;
     int32_t block_shift;       // log2(block_size) when a power of two, else -1
     int32_t num_blocks;        // physical blocks: ids are clamped below it
-    int32_t pairs_padded;      // (request, partition) pairs rounded up to 8
+    int32_t num_ranges;        // R: equal ranges of each KV head's tile sequence
+    int32_t wgs_per_range;     // Hkv / 4 when that is a whole number > 1, else 1
     float score_scale_log2;    // softmax_scale * log2(e)
-    float* ws_o;               // [batch*Hkv*NP*M, head_dim]
-    float* ws_lse;             // [batch*Hkv*NP*M]
+    float* ws_o;               // [(batch + R - 1) * Hkv * M, head_dim]
+    float* ws_lse;             // [(batch + R - 1) * Hkv * M]
+    int32_t* ws_prefix;        // [batch + 1]: tiles before each request, then U
 };
 
 struct MergeParams {
-    const int32_t* context_lens;
     const float* ws_o;
     const float* ws_lse;
+    const int32_t* ws_prefix;
     void* out;
     int64_t out_stride_b, out_stride_row, out_stride_head;
     int32_t out_fp32;          // 1: fp32 output, 0: bf16
-    int32_t batch, num_kv_heads, group, m_rows, partition, num_partitions;
-    int32_t max_context;
+    int32_t batch, num_kv_heads, group, m_rows, num_ranges;
     int32_t total_rows;        // batch * num_kv_heads * m_rows
 };
+
+// Wave slots the decode split fills by default: one per SIMD (4 per CU),
+// 0 if the device query fails.
+int decode_wave_slots(int device);
 
 hipError_t launch_decode_partitions(const DecodeParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_merge(const MergeParams& p, int head_dim,

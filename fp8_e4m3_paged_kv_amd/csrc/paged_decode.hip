@@ -7,12 +7,24 @@
 // probabilities are never rounded to the cache format (they are carried in
 // fp16, see below).
 //
-// Decomposition. One workgroup per (request b, KV head h, partition of
-// `partition` tokens); its NW waves take interleaved 32-token tiles and are
-// merged through LDS at the end; a second kernel merges the partitions by
-// log-sum-exp. The M = rows * G query rows that share KV head h (GQA group
-// times MTP verify rows) are stacked into the 16-row dimension of the MFMA
-// tiles, so each K/V byte is read from HBM once per step.
+// Decomposition (persistent, evenly split). Per KV head the keys form one
+// sequence of 32-token tiles: request 0's tiles, then request 1's, ...
+// (U tiles in all). That sequence is cut into R equal ranges (+-1 tile) and
+// one wave owns each (range, KV head) pair. By default there is one wave
+// per SIMD: every wave streams the same number of tiles from start to end,
+// whatever the mix of context lengths, and each SIMD holds exactly one
+// stream (measured on MI355X: one stream per SIMD reads HBM faster than two
+// or three, and an uneven number of waves per CU leaves a tail). A wave
+// reduces each request piece of its range to a partial (normalized output,
+// log-sum-exp) in the workspace; piece (request b, range r) has id b + r,
+// unique because ids grow along the sequence, and a request's pieces have
+// consecutive ids. A second kernel merges each request's pieces by
+// log-sum-exp. The four waves of a workgroup are four KV heads of one
+// range, and the workgroups of a range sit on one XCD, so a tile's K/V
+// rows for all heads are read through one L2 at about the same time.
+// The M = rows * G query rows that share KV head h (GQA group times MTP
+// verify rows) are stacked into the 16-row dimension of the MFMA tiles, so
+// each K/V byte is read from HBM once per step.
 //
 // Per 32-token tile (two 16-token halves s = 0, 1), lane l = 16*g + i:
 //   QK^T  v_mfma_f32_16x16x32_bf16, A = K codes (token i, 8 head-dim slots
@@ -24,13 +36,14 @@
 //         O[row i][d] for d = (D/16)(4g + r) + n: its own row, so the online
 //         softmax rescale needs no cross-lane traffic.
 //   P' = p * v_scale * 2^(141 - e) in fp16, where e is the running maximum
-//   biased exponent of the value scales seen by the wave (floored at 14):
-//   P' <= 2^15 stays inside fp16's normal range and rescaling on a new
-//   exponent is exact (a power of two).
+//   biased exponent of the value scales seen by the wave (floored at 15):
+//   P' < 2^15 stays inside fp16's normal range, rescaling on a new exponent
+//   is exact (a power of two), and the final 2^(e - 141) >= 2^-126 is a
+//   normal float.
 // Memory: each lane reads K as two/one 16-byte loads per token and V as 8
 // (or 4) contiguous bytes per token: every 128-byte (64-byte) code row is
-// read whole by 4 or 16 lanes. Tokens past the partition end are clamped
-// to its last token (never beyond the caller's data) and masked.
+// read whole by 4 or 16 lanes. Tokens past a piece's end read zero through
+// the buffer range check and are masked.
 #include <hip/hip_runtime.h>
 
 #include "fp8kv_device.h"
@@ -141,7 +154,7 @@ __device__ __forceinline__ float row_bcast(uint32_t v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + R, 0xF, 0xF, false));
 }
 
-template <int D, int NW>
+template <int D>
 struct DecodeTile {
     static constexpr int KB = D / 4;        // K code bytes per lane per token
     static constexpr int KV4 = KB / 16;     // 16-byte K loads per token
@@ -150,7 +163,7 @@ struct DecodeTile {
     typedef typename VRow<DL>::T VT;
     typedef TileRegs<D> Regs;
 
-    // Per-workgroup constants of the page walk.
+    // Constants of one piece's page walk (wave-uniform).
     struct WalkConsts {
         const uint8_t* kbase;     // k_cache + h * cache_stride_head
         const uint8_t* vbase;
@@ -162,23 +175,21 @@ struct DecodeTile {
         int nr_scales_full;       // ... of its scales: 4*(15*sss + 1)
     };
 
-    // Block-table entries of the wave's tiles k0 .. k0+31 (tile k of the wave
-    // is partition tile wave + NW*k): lane j holds the entry of tile
-    // k0 + j/2, half j%2. Indices are clamped to the partition's last
-    // half, so every lane reads an entry the request owns.
+    // Block-table entries of the piece's tiles k0 .. k0+31: lane j holds the
+    // entry of tile k0 + j/2, half j%2. Indices are clamped to the piece's
+    // last half, so every lane reads an entry the request owns.
     template <bool BSP2>
     static __device__ __forceinline__ int table_window(const DecodeParams& p, const WalkConsts& w,
-                                                       int wave, int k0, int lane) {
-        const int k = k0 + (lane >> 1);
-        const int stok = min(w.p0 + 32 * (wave + NW * k) + 16 * (lane & 1), w.last_base);
+                                                       int k0, int lane) {
+        const int stok = min(w.p0 + 32 * (k0 + (lane >> 1)) + 16 * (lane & 1), w.last_base);
         const int bi = BSP2 ? (stok >> p.block_shift) : stok / p.block_size;
         return w.bt[bi];
     }
 
-    // Page walk of tile ti (wave-uniform) from its two table entries. Full
-    // halves use constant bounds; a ragged tile's halves end after their last
-    // token inside the partition, and a tile past the wave's last one gets
-    // empty ones.
+    // Page walk of tile ti of the piece (wave-uniform) from its two table
+    // entries. Full halves use constant bounds; a ragged tile's halves end
+    // after their last token inside the piece, and a tile past the piece's
+    // last one gets empty ones.
     template <bool BSP2>
     static __device__ __forceinline__ void address(const DecodeParams& p, const WalkConsts& w,
                                                    int ti, const int (&blk_in)[2], TileAddr& ta) {
@@ -197,7 +208,7 @@ struct DecodeTile {
             const int64_t soff = slot * p.scale_stride_slot;
             int nrc = w.nr_codes_full, nrs = w.nr_scales_full;
             if (ragged) {
-                // tokens of this half inside the partition (<= 0: none)
+                // tokens of this half inside the piece (<= 0: none)
                 const int nvalid = live ? min(16, w.p1 - stok) : 0;
                 nrc = nvalid > 0 ? (nvalid - 1) * (int)p.cache_stride_slot + D : 0;
                 nrs = nvalid > 0 ? 4 * ((nvalid - 1) * (int)p.scale_stride_slot + 1) : 0;
@@ -278,7 +289,7 @@ struct DecodeTile {
                          fmaxf(fmaxf(s2[1][0], s2[1][1]), fmaxf(s2[1][2], s2[1][3])));
         mt = rows_max(mt);
         svm = rows_max(svm);                    // wave-uniform now
-        const int ef_t = max((int)((__float_as_uint(svm) >> 23) & 0xFF), 14);
+        const int ef_t = max((int)((__float_as_uint(svm) >> 23) & 0xFF), 15);
         const float m_new = fmaxf(st.m_run, mt);
         if (__any(m_new > st.m_run || ef_t > st.ef_run)) {
             const int ef_new = max(st.ef_run, ef_t);
@@ -336,39 +347,39 @@ struct DecodeTile {
     }
 };
 
-template <int D, int NW, bool BSP2>
-__global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams p) {
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_scan(int v, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(v, d);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+// Tiles of a request of `len` cached tokens (after clamping).
+__device__ __forceinline__ int request_tiles(const DecodeParams& p, int b) {
+    const int len = min(max(p.context_lens[b], 0), p.max_context);
+    return (len + 31) >> 5;
+}
+
+// One piece: tiles [ja, jb) of request b for KV head h, reduced to a partial
+// (normalized output and log2 log-sum-exp of each of the M rows) at piece
+// id `pid`.
+template <int D, bool BSP2>
+__device__ __forceinline__ void decode_piece(const DecodeParams& p, int b, int len, int ja, int jb,
+                                             int h, int pid, int lane) {
     constexpr int KSTEPS = D / 32;
     constexpr int DL = D / 16;
     constexpr int KB = D / 4;
-    typedef DecodeTile<D, NW> Tile;
+    typedef DecodeTile<D> Tile;
     typedef typename Tile::Regs Regs;
-
-    __shared__ floatx4 lds_acc[NW / 2][DL][64];
-    __shared__ float lds_ml[NW / 2][2][64];
-
-    const int lane = threadIdx.x & 63;
-    // wave index, provably uniform so the page walk and the buffer
-    // descriptors stay in scalar registers
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 15;
     const int lg = lane >> 4;
 
-    // Unit of this workgroup. Consecutive (request, partition) pairs go to
-    // consecutive XCDs (dispatch is round-robin over the 8 XCDs) and the
-    // KV heads of one pair stay on one XCD, sharing its L2.
-    const int xcd = blockIdx.x & 7;
-    const int kx = blockIdx.x >> 3;
-    const int pair = (kx / p.num_kv_heads) * 8 + xcd;
-    const int h = kx % p.num_kv_heads;
-    if (pair >= p.batch * p.num_partitions) return;
-    const int b = pair / p.num_partitions;
-    const int part = pair - b * p.num_partitions;
-    const int len = min(max(p.context_lens[b], 0), p.max_context);
-    const int p0 = part * p.partition;
-    if (p0 >= len) return;
-    const int p1 = min(p0 + p.partition, len);
-    const int ntiles = (p1 - p0 + 31) >> 5;
+    const int p0 = ja << 5;
+    const int p1 = min(jb << 5, len);
+    const int ntiles = jb - ja;
 
     typename Tile::WalkConsts w;
     w.kbase = p.k_cache + (int64_t)h * p.cache_stride_head;
@@ -385,11 +396,10 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
     w.nr_codes_full = 15 * (int)p.cache_stride_slot + D;
     w.nr_scales_full = 4 * (15 * (int)p.scale_stride_slot + 1);
 
-    // the wave's block-table window (its tiles 0..31), then the next one
-    const int wave_tiles = wave < ntiles ? (ntiles - wave + NW - 1) / NW : 0;
+    // block-table window of tiles 0..31, and the next one when the piece is longer
     int kw = 0;
-    int btw = Tile::template table_window<BSP2>(p, w, wave, 0, lane);
-    int btn = wave_tiles > 32 ? Tile::template table_window<BSP2>(p, w, wave, 32, lane) : 0;
+    int btw = Tile::template table_window<BSP2>(p, w, 0, lane);
+    int btn = ntiles > 32 ? Tile::template table_window<BSP2>(p, w, 32, lane) : 0;
 
     // q operand: row li of the stacked (verify row, query head) block
     bf16x8 qv[KSTEPS];
@@ -414,7 +424,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
     for (int n = 0; n < DL; ++n) st.acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
     st.m_run = kNeg;
     st.l_run = 0.f;
-    st.ef_run = 14;
+    st.ef_run = 15;
 
     // loop-invariant load offsets
     LaneOffsets lo;
@@ -427,86 +437,52 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
         lo.s = ((4 * lg + li) & 15) * sss * 4;
     }
 
-    // table entries of the wave's tile k (wave-uniform k); windows move
-    // forward 32 tiles at a time, the next one already loaded
+    // table entries of tile k (wave-uniform k); windows move forward 32
+    // tiles at a time, the next one already loaded
     auto entries = [&](int k, int (&blk)[2]) {
         if (k - kw >= 32) {
             kw += 32;
             btw = btn;
-            if (wave_tiles > kw + 32) btn = Tile::template table_window<BSP2>(p, w, wave, kw + 32, lane);
+            if (ntiles > kw + 32) btn = Tile::template table_window<BSP2>(p, w, kw + 32, lane);
         }
         const int j = 2 * (k - kw);
         blk[0] = __builtin_amdgcn_readlane(btw, j);
         blk[1] = __builtin_amdgcn_readlane(btw, j + 1);
     };
 
-    // Two tiles in flight per wave: after a tile's QK^T has consumed its K
-    // registers, the loads of the wave's next tile are issued, then the
-    // tile's softmax and PV run while they are in flight (A/B ping-pong).
+    // Two tiles in flight: after a tile's QK^T has consumed its K registers,
+    // the loads of the next tile are issued, then the tile's softmax and PV
+    // run while they are in flight (A/B ping-pong).
     TileAddr ta_a, ta_b;
     Regs ra, rb;
     floatx4 sc[2];
     int blk[2];
-    int k = 0;
-    int ti = wave;
+    int ti = 0;
     entries(0, blk);
-    Tile::template address<BSP2>(p, w, ti, blk, ta_a);
+    Tile::template address<BSP2>(p, w, 0, blk, ta_a);
     Tile::issue(ta_a, lo, ra);
     while (ti < ntiles) {
         Tile::qk(ra, qv, sc);
-        entries(k + 1, blk);
-        Tile::template address<BSP2>(p, w, ti + NW, blk, ta_b);
+        entries(ti + 1, blk);
+        Tile::template address<BSP2>(p, w, ti + 1, blk, ta_b);
         Tile::issue(ta_b, lo, rb);
         Tile::rest(p, ta_a, ra, sc, p1, lim, lg, st);
-        ti += NW;
-        ++k;
-        if (ti >= ntiles) break;
+        if (++ti >= ntiles) break;
         Tile::qk(rb, qv, sc);
-        entries(k + 1, blk);
-        Tile::template address<BSP2>(p, w, ti + NW, blk, ta_a);
+        entries(ti + 1, blk);
+        Tile::template address<BSP2>(p, w, ti + 1, blk, ta_a);
         Tile::issue(ta_a, lo, ra);
         Tile::rest(p, ta_b, rb, sc, p1, lim, lg, st);
-        ti += NW;
-        ++k;
+        ++ti;
     }
 
-    // per-wave totals for the lane's row
+    // the piece's partial for the lane's row
     st.l_run = rows_sum(st.l_run);
-    {
-        const float kinv = pow2i(max(st.ef_run - 141, -126));
-#pragma unroll
-        for (int n = 0; n < DL; ++n) st.acc[n] *= kinv;
-    }
-
-    // merge the NW waves pairwise through LDS (log2(NW) rounds)
-#pragma unroll
-    for (int half = NW / 2; half >= 1; half >>= 1) {
-        if (wave >= half && wave < 2 * half) {
-            const int slot = wave - half;
-#pragma unroll
-            for (int n = 0; n < DL; ++n) lds_acc[slot][n][lane] = st.acc[n];
-            lds_ml[slot][0][lane] = st.m_run;
-            lds_ml[slot][1][lane] = st.l_run;
-        }
-        __syncthreads();
-        if (wave < half) {
-            const float mo = lds_ml[wave][0][lane];
-            const float lo_ = lds_ml[wave][1][lane];
-            const float mm = fmaxf(st.m_run, mo);
-            const float fa = __builtin_amdgcn_exp2f(st.m_run - mm);
-            const float fb = __builtin_amdgcn_exp2f(mo - mm);
-#pragma unroll
-            for (int n = 0; n < DL; ++n) st.acc[n] = st.acc[n] * fa + lds_acc[wave][n][lane] * fb;
-            st.l_run = st.l_run * fa + lo_ * fb;
-            st.m_run = mm;
-        }
-        __syncthreads();
-    }
-
-    if (wave == 0 && li < p.m_rows) {
-        const int64_t u = (((int64_t)b * p.num_kv_heads + h) * p.num_partitions + part) * p.m_rows + li;
+    if (li < p.m_rows) {
+        const int64_t u = ((int64_t)pid * p.num_kv_heads + h) * p.m_rows + li;
         const bool any = st.l_run > 0.f;
-        const float inv = any ? 1.0f / st.l_run : 0.f;
+        // undo the P' range factor 2^(141 - e) with the normalization
+        const float inv = any ? pow2i(max(st.ef_run - 141, -126)) / st.l_run : 0.f;
         float* o = p.ws_o + u * D + (DL * 4) * lg;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -522,114 +498,221 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
     }
 }
 
+// Workgroup = 4 waves = 4 workers; worker = (range r, KV head h). When the
+// KV heads fill whole workgroups (m = Hkv / 4 of them per range), the m
+// workgroups of a range are placed on one XCD: dispatch deals consecutive
+// workgroup ids round-robin to the 8 XCDs.
+__device__ __forceinline__ int logical_workgroup(int bid, int wgs_per_range) {
+    const int m = wgs_per_range;
+    if (m <= 1) return bid;
+    const int xcd = bid & 7, k = bid >> 3;
+    return (k / m) * 8 * m + xcd * m + (k % m);
+}
+
+template <int D, bool BSP2>
+__global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
+    const int lane = threadIdx.x & 63;
+    // wave index, provably uniform so the page walk and the buffer
+    // descriptors stay in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int worker = logical_workgroup(blockIdx.x, p.wgs_per_range) * 4 + wave;
+    const int r = worker / p.num_kv_heads;
+    const int h = worker - r * p.num_kv_heads;
+    if (r >= p.num_ranges) return;
+    const int R = p.num_ranges;
+
+    // total tiles U (per KV head); worker 0 also records the exclusive
+    // prefix of tiles per request and U for the merge
+    int U = 0;
+    for (int c = 0; c < p.batch; c += 64) {
+        const int n = c + lane < p.batch ? request_tiles(p, c + lane) : 0;
+        const int incl = wave_scan(n, lane);
+        if (worker == 0 && c + lane < p.batch) p.ws_prefix[c + lane] = U + incl - n;
+        U += __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (worker == 0 && lane == 0) p.ws_prefix[p.batch] = U;
+
+    // this range: tiles [u0, u1) of the sequence
+    const int u0 = (int)(((int64_t)r * U) / R);
+    const int u1 = (int)(((int64_t)(r + 1) * U) / R);
+    if (u0 >= u1) return;
+
+    // the request holding tile u0 and the tiles before it
+    int b = 0, pre = 0;
+    for (int c = 0, carry = 0; c < p.batch; c += 64) {
+        const int n = c + lane < p.batch ? request_tiles(p, c + lane) : 0;
+        const int incl = wave_scan(n, lane) + carry;
+        const uint64_t hit = __ballot(incl > u0);
+        if (hit) {
+            const int j = __builtin_ctzll(hit);
+            b = c + j;
+            pre = __builtin_amdgcn_readlane(incl - n, j);
+            break;
+        }
+        carry = __builtin_amdgcn_readlane(incl, 63);
+    }
+
+    // walk the pieces of the range
+    int u = u0;
+    while (u < u1) {
+        const int len = min(max(p.context_lens[b], 0), p.max_context);
+        const int n = (len + 31) >> 5;
+        if (n > 0) {
+            const int ja = u - pre;
+            const int jb = min(n, u1 - pre);
+            decode_piece<D, BSP2>(p, b, len, ja, jb, h, b + r, lane);
+            u = pre + jb;
+        }
+        pre += n;
+        ++b;
+    }
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
     return v;
 }
 
-// Log-sum-exp merge of the partition partials: one wave per output row.
-// Lanes read the partitions' lse values in parallel (one partition per
-// lane, 64 at a time), the wave takes their maximum, and each partition's
-// weight 2^(lse - max) is then broadcast from its lane while every lane
-// accumulates its D/64 output columns.
+// Log-sum-exp merge of each request's pieces: one workgroup per output
+// row (request b, KV head h, stacked row m). Request b's tiles are
+// [pre(b), pre(b) + n(b)) of the per-head sequence; they lie in ranges
+// r_first .. r_last, whose pieces have ids b + r. The workgroup first takes
+// the maximum lse of those pieces, then its threads stream the pieces' rows:
+// D/4 threads read one piece row (4 floats each), 256/(D/4) pieces per
+// step, several steps in flight; the per-slot sums meet in LDS.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
-    constexpr int PER = D / 64;
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    constexpr int TPP = D / 4;               // threads per piece row
+    constexpr int PPS = 256 / TPP;           // pieces per step
+    constexpr int UNROLL = 8;
+    __shared__ float lds_max[4];
+    __shared__ float lds_acc[PPS][D];
+    __shared__ float lds_w[PPS];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int row = blockIdx.x;
     if (row >= p.total_rows) return;
     const int m = row % p.m_rows;
     const int bh = row / p.m_rows;
     const int h = bh % p.num_kv_heads;
     const int b = bh / p.num_kv_heads;
-    const int len = min(max(p.context_lens[b], 0), p.max_context);
-    const int np = (len + p.partition - 1) / p.partition;
-    const int64_t u0 = (int64_t)bh * p.num_partitions * p.m_rows + m;
+    const int U = p.ws_prefix[p.batch];
+    const int pre = p.ws_prefix[b];
+    const int n = p.ws_prefix[b + 1] - pre;
 
-    float mx = -INFINITY;
-    for (int c = 0; c < np; c += 64) {
-        const int q = c + lane;
-        const float l = q < np ? p.ws_lse[u0 + (int64_t)q * p.m_rows] : -INFINITY;
-        mx = fmaxf(mx, l);
-    }
-    mx = wave_max(mx);
-
-    float acc[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+    const int slot = t / TPP;
+    const int col = (t % TPP) * 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float wsum = 0.f;
-    if (mx > -INFINITY) {
-        for (int c = 0; c < np; c += 64) {
-            const int q = c + lane;
-            const float w = q < np ? exp2f(p.ws_lse[u0 + (int64_t)q * p.m_rows] - mx) : 0.f;
-            const int n = min(64, np - c);
-            const float* o = p.ws_o + (u0 + (int64_t)c * p.m_rows) * D + lane * PER;
-            const int64_t step = (int64_t)p.m_rows * D;
-            int j = 0;
-            for (; j + 4 <= n; j += 4) {
-                float wj[4], v[4][PER];
+    if (n > 0) {
+        // range holding tile u: the r with floor(rU/R) <= u < floor((r+1)U/R)
+        const int64_t R = p.num_ranges;
+        const int r0 = (int)((((int64_t)pre + 1) * R - 1) / U);
+        const int r1 = (int)((((int64_t)pre + n) * R - 1) / U);
+        const int np = r1 - r0 + 1;
+        const int64_t u0 = ((int64_t)(b + r0) * p.num_kv_heads + h) * p.m_rows + m;
+        const int64_t step = (int64_t)p.num_kv_heads * p.m_rows;
+        // a range with no tile (more ranges than tiles) has no piece
+        auto piece_lse = [&](int q) -> float {
+            const int64_t rq = r0 + q;
+            if (q >= np || (rq * U) / R == ((rq + 1) * U) / R) return -INFINITY;
+            return p.ws_lse[u0 + q * step];
+        };
+
+        float mx = -INFINITY;
+        for (int q = t; q < np; q += 256) mx = fmaxf(mx, piece_lse(q));
+        mx = wave_max(mx);
+        if (lane == 0) lds_max[t >> 6] = mx;
+        __syncthreads();
+        mx = fmaxf(fmaxf(lds_max[0], lds_max[1]), fmaxf(lds_max[2], lds_max[3]));
+
+        if (mx > -INFINITY) {
+            const float* o = p.ws_o + u0 * D + col;
+            for (int q0 = slot; q0 < np; q0 += PPS * UNROLL) {
+                float w[UNROLL];
+                float4 v[UNROLL];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    wj[t] = __shfl(w, j + t);
-#pragma unroll
-                    for (int i = 0; i < PER; ++i) v[t][i] = o[(j + t) * step + i];
+                for (int j = 0; j < UNROLL; ++j) {
+                    const int q = q0 + j * PPS;
+                    const float lq = piece_lse(q);
+                    w[j] = lq > -INFINITY ? exp2f(lq - mx) : 0.f;
+                    v[j] = w[j] > 0.f ? *reinterpret_cast<const float4*>(o + q * step * D)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
                 }
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    wsum += wj[t];
-#pragma unroll
-                    for (int i = 0; i < PER; ++i) acc[i] += wj[t] * v[t][i];
+                for (int j = 0; j < UNROLL; ++j) {
+                    wsum += w[j];
+                    acc.x += w[j] * v[j].x;
+                    acc.y += w[j] * v[j].y;
+                    acc.z += w[j] * v[j].z;
+                    acc.w += w[j] * v[j].w;
                 }
-            }
-            for (; j < n; ++j) {
-                const float wj = __shfl(w, j);
-                wsum += wj;
-#pragma unroll
-                for (int i = 0; i < PER; ++i) acc[i] += wj * o[j * step + i];
             }
         }
     }
-    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-    const int r = m / p.group;
-    const int hq = h * p.group + (m - r * p.group);
-    const int64_t off = (int64_t)b * p.out_stride_b + (int64_t)r * p.out_stride_row +
-                        (int64_t)hq * p.out_stride_head + lane * PER;
+    // sum the PPS slots
+    *reinterpret_cast<float4*>(&lds_acc[slot][col]) = acc;
+    if (col == 0) lds_w[slot] = wsum;
+    __syncthreads();
+    if (t < TPP) {
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        float ws = 0.f;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const float v = acc[i] * inv;
-        if (p.out_fp32) {
-            static_cast<float*>(p.out)[off + i] = v;
-        } else {
-            uint32_t bits = __float_as_uint(v);
-            bits += 0x7FFFu + ((bits >> 16) & 1u);      // round to nearest even
-            static_cast<uint16_t*>(p.out)[off + i] = (uint16_t)(bits >> 16);
+        for (int k = 0; k < PPS; ++k) {
+            const float4 a = *reinterpret_cast<const float4*>(&lds_acc[k][col]);
+            s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
+            ws += lds_w[k];
+        }
+        const float inv = ws > 0.f ? 1.0f / ws : 0.f;
+        const float vals[4] = {s.x * inv, s.y * inv, s.z * inv, s.w * inv};
+        const int r = m / p.group;
+        const int hq = h * p.group + (m - r * p.group);
+        const int64_t off = (int64_t)b * p.out_stride_b + (int64_t)r * p.out_stride_row +
+                            (int64_t)hq * p.out_stride_head + col;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (p.out_fp32) {
+                static_cast<float*>(p.out)[off + i] = vals[i];
+            } else {
+                uint32_t bits = __float_as_uint(vals[i]);
+                bits += 0x7FFFu + ((bits >> 16) & 1u);      // round to nearest even
+                static_cast<uint16_t*>(p.out)[off + i] = (uint16_t)(bits >> 16);
+            }
         }
     }
 }
 
-template <int D>
-hipError_t launch_partitions_d(const DecodeParams& p, hipStream_t stream) {
-    // Four waves per workgroup: with two tiles of registers per wave a SIMD
-    // holds three waves, so three workgroups share a CU.
-    constexpr int NW = 4;
-    dim3 grid((unsigned)((int64_t)p.pairs_padded * p.num_kv_heads)), block(NW * 64);
-    if (p.block_shift >= 0)
-        hipLaunchKernelGGL((decode_partition_kernel<D, NW, true>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((decode_partition_kernel<D, NW, false>), grid, block, 0, stream, p);
+template <int D, bool BSP2>
+hipError_t launch_split(const DecodeParams& p, hipStream_t stream) {
+    const int64_t workers = (int64_t)p.num_ranges * p.num_kv_heads;
+    const int64_t quantum = p.wgs_per_range > 1 ? 8 * p.wgs_per_range : 1;
+    int64_t wgs = (workers + 3) / 4;
+    wgs = (wgs + quantum - 1) / quantum * quantum;
+    if (wgs > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_split_kernel<D, BSP2>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
+int decode_wave_slots(int device) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+        return 0;
+    return cus * 4;                            // one wave per SIMD
+}
+
 hipError_t launch_decode_partitions(const DecodeParams& p, int head_dim, hipStream_t stream) {
-    if (head_dim == 128) return launch_partitions_d<128>(p, stream);
-    return launch_partitions_d<64>(p, stream);
+    const bool pow2 = p.block_shift >= 0;
+    if (head_dim == 128)
+        return pow2 ? launch_split<128, true>(p, stream) : launch_split<128, false>(p, stream);
+    return pow2 ? launch_split<64, true>(p, stream) : launch_split<64, false>(p, stream);
 }
 
 hipError_t launch_decode_merge(const MergeParams& p, int head_dim, hipStream_t stream) {
-    dim3 grid((unsigned)((p.total_rows + 3) / 4)), block(256);
+    dim3 grid((unsigned)p.total_rows), block(256);
     if (head_dim == 128)
         hipLaunchKernelGGL(decode_merge_kernel<128>, grid, block, 0, stream, p);
     else

@@ -106,7 +106,6 @@ class DecodeCase:
     head_dim: int
     rows: int
     softmax_scale: float
-    partition_tokens: int = 0
     notes: dict = field(default_factory=dict)
 
 
@@ -177,14 +176,11 @@ def decode_workload(seed: int = 2, device="cpu") -> DecodeCase:
 
 def longctx_workload(seed: int = 3, device="cpu") -> DecodeCase:
     """4 requests of 262,144 x {1,2,3,4} tokens, 4 causal verify rows,
-    Hq 16 / Hkv 4, D 128, bs 64, 0.5% x30 K outlier rows; split-K partitions
-    of 8192 tokens."""
+    Hq 16 / Hkv 4, D 128, bs 64, 0.5% x30 K outlier rows."""
     lens = [262144 * i for i in (1, 2, 3, 4)]
-    c = decode_case(lens, 16, 4, 128, 64, rows=4, seed=seed, device=device,
-                    k_outlier_frac=0.005, k_outlier_mult=30.0,
-                    name="longctx")
-    c.partition_tokens = 8192
-    return c
+    return decode_case(lens, 16, 4, 128, 64, rows=4, seed=seed, device=device,
+                       k_outlier_frac=0.005, k_outlier_mult=30.0,
+                       name="longctx")
 
 
 @dataclass

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FP8KV_ABI_VERSION 1
+#define FP8KV_ABI_VERSION 2
 
 typedef enum fp8kv_status {
     FP8KV_OK = 0,
@@ -133,12 +133,18 @@ int fp8kv_kv_quant_scatter(
  *   out     = sum_j softmax(score)_j * v_scale_j * dec(v_code_j)
  * A row that sees no token gets out = 0.
  *
- * The keys are split into partitions of partition_tokens tokens (a
- * positive multiple of 32; 0 lets the library choose); each (request, KV
- * head, partition) is reduced to a partial (normalized output, log2
- * log-sum-exp) in the workspace, and the partials are merged by
- * log-sum-exp. The grid is sized from the host-known max_context, so the
- * launch is graph-capturable with any context_lens <= max_context.
+ * Split. Per KV head the visible keys of all requests form one sequence
+ * of 32-token tiles (request 0's ceil(L/32) tiles, then request 1's, ...;
+ * U tiles in all). It is cut into num_ranges equal ranges (range r holds
+ * tiles [floor(r*U/R), floor((r+1)*U/R))), each reduced by one wave per KV
+ * head, so the work per wave does not depend on how the lengths are mixed.
+ * Each piece (request b, range r) of a range becomes a partial (normalized
+ * output, log2 log-sum-exp) in the workspace, and a merge kernel combines
+ * each request's pieces by log-sum-exp. num_ranges = 0 lets the library
+ * choose (4 * the current device's CU count / num_kv_heads: one wave per
+ * SIMD). The
+ * grid depends only on host values, so the launch is graph-capturable with
+ * any context_lens; max_context is the bound the lengths are clamped to.
  *
  * q           (device) FP8KV_DTYPE_BF16, element (b, r, hq, d) at
  *             b*q_stride_b + r*q_stride_row + hq*q_stride_head + d;
@@ -156,7 +162,8 @@ int fp8kv_kv_quant_scatter(
  *             FP32), element (b, r, hq, d) at b*out_stride_b +
  *             r*out_stride_row + hq*out_stride_head + d.
  * workspace   (device) at least fp8kv_paged_decode_workspace_bytes(...)
- *             bytes, 256-byte aligned; no initialization needed.
+ *             bytes, 256-byte aligned; no initialization needed. Calls
+ *             that share a workspace must be ordered on one stream.
  * Errors: E_NULL, E_SHAPE, E_STRIDE, E_ALIGN, E_UNSUPPORTED, E_WORKSPACE,
  *         E_LAUNCH.
  */
@@ -172,7 +179,7 @@ int fp8kv_paged_decode_attn_fp8(
     const int32_t* context_lens,
     int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
     int32_t head_dim, int32_t block_size, float softmax_scale,
-    int32_t partition_tokens, int32_t max_context,
+    int32_t num_ranges, int32_t max_context,
     void* workspace, size_t workspace_bytes,
     void* out, int64_t out_stride_b, int64_t out_stride_row,
     int64_t out_stride_head, int32_t out_dtype,
@@ -180,36 +187,34 @@ int fp8kv_paged_decode_attn_fp8(
 
 /*
  * Workspace bytes fp8kv_paged_decode_attn_fp8 / _partials / _merge need for
- * these sizes (same partition_tokens rule: 0 = library choice). Returns a
+ * these sizes (same num_ranges rule: 0 = library choice). Returns a
  * negative fp8kv_status for an unsupported combination.
  *
- * Layout (so that partials computed on several devices can be gathered and
- * merged -- the context-parallel use): with NP = ceil(max_context /
- * partition), M = rows * G, row m = r * G + (hq % G), the first
- * batch*Hkv*NP*M*head_dim floats are the normalized partial outputs
- * o[((b*Hkv + h)*NP + p)*M + m][d], followed by batch*Hkv*NP*M floats of
- * log2-domain log-sum-exp lse[((b*Hkv + h)*NP + p)*M + m] (-inf when the
- * partition holds no visible token of the row).
+ * Layout, with R the resolved num_ranges, P = batch + R - 1 piece ids,
+ * M = rows * G and row m = r * G + (hq % G): P*Hkv*M*head_dim floats of
+ * normalized partial outputs o[(id*Hkv + h)*M + m][d], then (256-byte
+ * aligned) P*Hkv*M floats of log2-domain log-sum-exp
+ * lse[(id*Hkv + h)*M + m] (-inf when the piece holds no token the row
+ * sees), then (256-byte aligned) batch + 1 int32: the tiles before each
+ * request and, last, U. Piece (b, r) has id b + r; request b's pieces are
+ * those of the non-empty ranges r holding its tiles.
  */
 int64_t fp8kv_paged_decode_workspace_bytes(
     int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
-    int32_t head_dim, int32_t block_size, int32_t max_context,
-    int32_t partition_tokens);
+    int32_t head_dim, int32_t num_ranges);
 
-/* The partition used for these sizes (resolves partition_tokens == 0), or a
- * negative fp8kv_status. */
-int32_t fp8kv_paged_decode_partition_tokens(
-    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
-    int32_t head_dim, int32_t block_size, int32_t max_context,
-    int32_t partition_tokens);
+/* The number of ranges used for num_kv_heads (resolves num_ranges == 0 on
+ * the current device), or a negative fp8kv_status. */
+int32_t fp8kv_paged_decode_num_ranges(int32_t num_kv_heads, int32_t num_ranges);
 
 /*
  * The two phases of fp8kv_paged_decode_attn_fp8, callable separately: the
- * partition phase (page walk, KV streaming, scores, online softmax, PV,
+ * split phase (page walk, KV streaming, scores, online softmax, PV,
  * partials to the workspace) and the log-sum-exp merge of the partials into
  * `out`. Same arguments and rules as the fused call; the merge reads only
- * context_lens and the workspace. Running _partials then _merge on one
- * stream equals one fp8kv_paged_decode_attn_fp8 call bit for bit.
+ * the workspace (and must use the num_ranges of the partials). Running
+ * _partials then _merge on one stream equals one
+ * fp8kv_paged_decode_attn_fp8 call bit for bit.
  */
 int fp8kv_paged_decode_partials(
     const void* q, int64_t q_stride_b, int64_t q_stride_row,
@@ -223,14 +228,12 @@ int fp8kv_paged_decode_partials(
     const int32_t* context_lens,
     int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
     int32_t head_dim, int32_t block_size, float softmax_scale,
-    int32_t partition_tokens, int32_t max_context,
+    int32_t num_ranges, int32_t max_context,
     void* workspace, size_t workspace_bytes, void* stream);
 
 int fp8kv_paged_decode_merge(
-    const int32_t* context_lens,
     int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
-    int32_t head_dim, int32_t block_size, int32_t partition_tokens,
-    int32_t max_context,
+    int32_t head_dim, int32_t num_ranges,
     const void* workspace, size_t workspace_bytes,
     void* out, int64_t out_stride_b, int64_t out_stride_row,
     int64_t out_stride_head, int32_t out_dtype,

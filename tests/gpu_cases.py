@@ -127,7 +127,7 @@ def compact_host_cache(case, dc: DevCache, requests):
     return (kc, vc, ks, vs), bt, cl
 
 
-def run_decode(case, dc: DevCache, *, out_dtype=torch.float32, partition=0,
+def run_decode(case, dc: DevCache, *, out_dtype=torch.float32, ranges=0,
                max_context=None, context_lens=None, q=None, workspace=None):
     L = case.layout
     dev = dc.k_cache.device
@@ -139,7 +139,7 @@ def run_decode(case, dc: DevCache, *, out_dtype=torch.float32, partition=0,
         q, dc.k_cache, dc.v_cache, dc.k_scale, dc.v_scale,
         L.block_tables.to(dev), cl, num_kv_heads=case.num_kv_heads,
         block_size=L.block_size, softmax_scale=case.softmax_scale,
-        max_context=max_context, partition_tokens=partition,
+        max_context=max_context, num_ranges=ranges,
         out_dtype=out_dtype, workspace=workspace)
 
 

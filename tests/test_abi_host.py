@@ -95,7 +95,7 @@ def dec(L, fn="fp8kv_paged_decode_attn_fp8", **kw):
     a = dict(q=A, qsb=4096, qsr=4096, qsh=128, qdt=BF16, kc=A, vc=A,
              css=1024, csh=128, ks=A, vs=A, sss=1, ssh=1 << 20, S=1 << 20,
              bt=A, bts=2048, cl=A, B=64, R=1, Hq=32, H=8, D=128, bs=16,
-             scale=0.088, P=0, maxc=32768, ws=A, wsb=1 << 34, out=A,
+             scale=0.088, P=384, maxc=32768, ws=A, wsb=1 << 34, out=A,
              osb=4096, osr=4096, osh=128, odt=BF16)
     a.update(kw)
     common = [a["q"], a["qsb"], a["qsr"], a["qsh"], a["qdt"], a["kc"],
@@ -118,8 +118,9 @@ def dec(L, fn="fp8kv_paged_decode_attn_fp8", **kw):
     (dict(Hq=64, H=2), E_UNSUPPORTED),   # group 32 > 16
     (dict(bs=8), E_UNSUPPORTED),
     (dict(bs=24), E_UNSUPPORTED),
-    (dict(P=48), E_SHAPE),
-    (dict(P=-32), E_SHAPE),
+    (dict(P=-1), E_SHAPE),               # num_ranges
+    (dict(P=1 << 21), E_SHAPE),
+    (dict(maxc=-1), E_SHAPE),
     (dict(B=-1), E_SHAPE),
     (dict(q=0), E_NULL),
     (dict(bt=0), E_NULL),
@@ -144,21 +145,22 @@ def test_partials_refusals(L):
 
 
 def test_workspace_layout(L):
-    B, R, Hq, H, D, bs, maxc, P = 64, 1, 32, 8, 128, 16, 32768, 1024
-    n = L.fp8kv_paged_decode_workspace_bytes(B, R, Hq, H, D, bs, maxc, P)
-    NP, M = maxc // P, R * Hq // H
-    units = B * H * NP * M
+    B, R, Hq, H, D, NR = 64, 1, 32, 8, 128, 384
+    n = L.fp8kv_paged_decode_workspace_bytes(B, R, Hq, H, D, NR)
+    M = R * Hq // H
+    units = (B + NR - 1) * H * M          # piece ids b + r < B + NR - 1
     rnd = lambda x: (x + 255) // 256 * 256
-    assert n == rnd(units * D * 4) + rnd(units * 4)
-    assert L.fp8kv_paged_decode_workspace_bytes(B, R, Hq, H, 96, bs, maxc, P) == E_UNSUPPORTED
+    assert n == rnd(units * D * 4) + rnd(units * 4) + rnd((B + 1) * 4)
+    assert L.fp8kv_paged_decode_workspace_bytes(B, R, Hq, H, 96, NR) == E_UNSUPPORTED
+    assert L.fp8kv_paged_decode_workspace_bytes(B, R, Hq, H, D, -3) == E_SHAPE
 
 
-def test_partition_choice(L):
-    f = L.fp8kv_paged_decode_partition_tokens
-    assert f(4, 4, 16, 4, 128, 64, 1 << 20, 8192) == 8192
-    assert f(4, 4, 16, 4, 128, 64, 1 << 20, 0) % 32 == 0
-    assert f(2, 1, 4, 2, 64, 16, 100, 0) % 32 == 0
-    assert f(2, 1, 4, 2, 64, 16, 100, 40) == E_SHAPE
+def test_num_ranges(L):
+    f = L.fp8kv_paged_decode_num_ranges
+    assert f(8, 384) == 384
+    assert f(4, 1) == 1
+    assert f(8, -1) == E_SHAPE
+    assert f(0, 16) == E_SHAPE
 
 
 def test_binding_refuses_host_tensors():

@@ -3,7 +3,11 @@ same dequantized cache (the cache itself written by the GPU quantizer).
 
 Bar: fp32 output within max-abs 2e-3 and rel-L2 1e-3 of the oracle; bf16
 output equal, bit for bit, to the round-to-nearest-even of the same
-kernel's fp32 output (same partitioning)."""
+kernel's fp32 output (same split).
+
+The split into ranges is exercised from one range per KV head (one wave
+walks every request) to many more ranges than tiles (most ranges empty, so
+the merge must skip them)."""
 import math
 
 import numpy as np
@@ -22,18 +26,18 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def check_case(case, partition=0, layout="head_major", also_bf16=True,
+def check_case(case, ranges=0, layout="head_major", also_bf16=True,
                max_context=None):
     log(f"decode {case.name}: lens={case.layout.context_lens.tolist()[:6]} "
         f"R={case.rows} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
-        f"D={case.head_dim} bs={case.layout.block_size} P={partition} {layout}")
+        f"D={case.head_dim} bs={case.layout.block_size} ranges={ranges} {layout}")
     dc = cache_case(case, DEV, layout)
-    out = run_decode(case, dc, partition=partition, max_context=max_context)
+    out = run_decode(case, dc, ranges=ranges, max_context=max_context)
     torch.cuda.synchronize()
     ref = oracle_decode(case, dc.host())
     assert_attn_close(out.cpu().numpy(), ref, case.name)
     if also_bf16:
-        ob = run_decode(case, dc, partition=partition, out_dtype=torch.bfloat16,
+        ob = run_decode(case, dc, ranges=ranges, out_dtype=torch.bfloat16,
                         max_context=max_context)
         torch.cuda.synchronize()
         assert torch.equal(ob, bf16_rne(out)), "bf16 output is not RNE of fp32"
@@ -45,32 +49,34 @@ def test_tiny_case():
     check_case(case)
 
 
-@pytest.mark.parametrize("partition", [0, 32, 64, 256])
-def test_ragged_lengths_many_partitions(partition):
+@pytest.mark.parametrize("ranges", [0, 1, 3, 7, 64, 5000])
+def test_ragged_lengths_across_ranges(ranges):
+    """198 tiles per KV head: one range, ranges spanning several requests,
+    ranges inside one request, and 5000 ranges (most of them empty)."""
     case = synth.decode_case([1, 31, 33, 1000, 5000, 77], 8, 2, 128, 16,
                              rows=1, seed=3)
-    check_case(case, partition=partition)
+    check_case(case, ranges=ranges)
 
 
 @pytest.mark.parametrize("layout", ["head_major", "slot_major"])
 @pytest.mark.parametrize("bs", [16, 32, 64, 128])
 def test_block_sizes_and_scale_layouts(bs, layout):
     case = synth.decode_case([300, 1290, 64], 8, 4, 128, bs, rows=1, seed=bs)
-    check_case(case, partition=256, layout=layout)
+    check_case(case, ranges=11, layout=layout)
 
 
 def test_head_dim_64():
     case = synth.decode_case([700, 129, 2], 16, 4, 64, 16, rows=2, seed=6)
-    check_case(case, partition=128)
+    check_case(case, ranges=5)
 
 
-@pytest.mark.parametrize("partition", [1024, 8192])
-def test_verify_rows_causal(partition):
+@pytest.mark.parametrize("ranges", [0, 2, 33])
+def test_verify_rows_causal(ranges):
     """4 verify rows x 4 query heads stacked into the 16-row tile; request
     lengths include one shorter than the row count (row 0 sees nothing)."""
     case = synth.decode_case([3, 4, 2000, 9000], 16, 4, 128, 64, rows=4,
                              seed=12, k_outlier_frac=0.005)
-    _, out, _ = check_case(case, partition=partition)
+    _, out, _ = check_case(case, ranges=ranges)
     assert torch.all(out[0, 0] == 0)
 
 
@@ -84,12 +90,31 @@ def test_outliers_and_zero_rows():
     v[101, 0, 9] = -5000.0
     v[200:260] *= 1e-3
     case.k, case.v = k.to(torch.bfloat16), v.to(torch.bfloat16)
-    check_case(case, partition=512)
+    check_case(case, ranges=9)
+
+
+def test_tiny_value_scales():
+    """V rows of ~1e-33 (value scales below 2^-112): the fp16 range factor
+    of P' sits at its floor and must be undone exactly."""
+    case = synth.decode_case([300, 77], 8, 2, 128, 16, rows=1, seed=23)
+    v = case.v.float() * 1e-33
+    v[10:20] *= 1e30                      # a few ordinary rows as well
+    case.v = v.to(torch.bfloat16)
+    dc, out, ref = check_case(case, ranges=0)
+    tiny = synth.decode_case([300, 77], 8, 2, 128, 16, rows=1, seed=23)
+    tiny.v = (tiny.v.float() * 1e-33).to(torch.bfloat16)
+    dc2 = cache_case(tiny, DEV)
+    out2 = run_decode(tiny, dc2)
+    torch.cuda.synchronize()
+    ref2 = oracle_decode(tiny, dc2.host())
+    scale = float(np.abs(ref2).max())
+    assert scale > 0
+    assert_attn_close(out2.cpu().numpy() / scale, ref2 / scale, "all-tiny V (scaled)")
 
 
 def test_empty_contexts_and_zero_max_context():
     case = synth.decode_case([0, 40, 0], 8, 2, 128, 16, rows=1, seed=2)
-    dc, out, _ = check_case(case, partition=64)
+    dc, out, _ = check_case(case, ranges=3)
     assert torch.all(out[0] == 0) and torch.all(out[2] == 0)
     out0 = run_decode(case, dc, max_context=0)
     torch.cuda.synchronize()
@@ -99,7 +124,7 @@ def test_empty_contexts_and_zero_max_context():
 def test_context_lens_above_max_context_are_clamped():
     case = synth.decode_case([900, 600], 8, 2, 128, 16, rows=1, seed=4)
     dc = cache_case(case, DEV)
-    out = run_decode(case, dc, max_context=512, partition=128)
+    out = run_decode(case, dc, max_context=512, ranges=6)
     torch.cuda.synchronize()
     clamped = torch.tensor([512, 512], dtype=torch.int32)
     ref = oracle_decode(case, dc.host(), context_lens=clamped.numpy())
@@ -111,7 +136,7 @@ def test_partials_then_merge_equal_fused():
     dc = cache_case(case, DEV)
     L = case.layout
     kw = dict(num_kv_heads=4, block_size=16, softmax_scale=case.softmax_scale,
-              max_context=8000, partition_tokens=512)
+              max_context=8000, num_ranges=37)
     fused = fk.paged_decode_attn_fp8(case.q.to(DEV), dc.k_cache, dc.v_cache,
                                      dc.k_scale, dc.v_scale,
                                      L.block_tables.to(DEV),
@@ -122,9 +147,8 @@ def test_partials_then_merge_equal_fused():
                                   L.block_tables.to(DEV),
                                   L.context_lens.to(DEV), **kw)
     out = torch.empty_like(fused)
-    fk.paged_decode_merge(ws, L.context_lens.to(DEV), out, rows=2,
-                          num_q_heads=16, num_kv_heads=4, block_size=16,
-                          max_context=8000, partition_tokens=512)
+    fk.paged_decode_merge(ws, out, rows=2, num_q_heads=16, num_kv_heads=4,
+                          num_ranges=37)
     torch.cuda.synchronize()
     assert torch.equal(out, fused)
 
@@ -137,11 +161,11 @@ def test_graph_capture_replays_with_new_lengths():
     cl = L.context_lens.to(DEV).clone()
     bt = L.block_tables.to(DEV)
     maxc = 4096
-    ws = torch.empty(fk.decode_workspace_bytes(3, 1, 8, 2, 128, 16, maxc, 256),
+    ws = torch.empty(fk.decode_workspace_bytes(3, 1, 8, 2, 128, 13),
                      dtype=torch.uint8, device=DEV)
     out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
     kw = dict(num_kv_heads=2, block_size=16, softmax_scale=case.softmax_scale,
-              max_context=maxc, partition_tokens=256, out=out, workspace=ws)
+              max_context=maxc, num_ranges=13, out=out, workspace=ws)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -168,7 +192,7 @@ def test_graph_capture_replays_with_new_lengths():
 
 def test_decode_workload_full_size_sampled():
     """64 requests, lengths U[1024, 32768], Hq 32 / Hkv 8, D 128, bs 16 --
-    the benchmark's decode launch (library-chosen partition); the oracle
+    the benchmark's decode launch (library-chosen split); the oracle
     recomputes every row of 4 sampled requests."""
     case = synth.decode_workload(seed=2, device=DEV)
     dc = cache_case(case, DEV)
@@ -186,11 +210,11 @@ def test_decode_workload_full_size_sampled():
 
 def test_longctx_full_size_sampled():
     """4 requests of 256K..1M tokens, 4 causal verify rows, Hq 16 / Hkv 4,
-    bs 64, 8192-token partitions: the oracle recomputes sampled rows of the
+    bs 64, library-chosen split: the oracle recomputes sampled rows of the
     shortest and the longest request."""
     case = synth.longctx_workload(seed=3, device=DEV)
     dc = cache_case(case, DEV)
-    out = run_decode(case, dc, partition=case.partition_tokens)
+    out = run_decode(case, dc)
     torch.cuda.synchronize()
     assert torch.all(torch.isfinite(out))
     for b, heads in ((0, [0, 5, 15]), (3, [2, 11])):
