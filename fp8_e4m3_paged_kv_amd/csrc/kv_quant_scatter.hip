@@ -4,9 +4,12 @@
 //
 // Work unit: one (token, KV head) row of head_dim elements of K or of V
 // (grid y), handled by one 16-lane DPP row of a wave64 (head_dim/16 bf16 per
-// lane, one 8- or 16-byte load). A wave covers 4 rows per step and 4 steps;
-// all loads of a wave are issued before any arithmetic so 64 B per lane are
-// in flight.
+// lane, one 8- or 16-byte load). A wave covers 4 rows per step and 2 steps;
+// all loads of a wave are issued before any arithmetic. The bf16 rows are
+// read and the code rows written with the non-temporal hint (each byte is
+// touched once, so they should not displace anything in L2); the 4-byte
+// scale stores stay ordinary so L2 can merge neighbouring rows' scales
+// into whole lines before they reach HBM.
 //
 //   amax  = max |x|              16-lane DPP reduction, exact
 //   s     = fp32(amax / 448)     IEEE division
@@ -24,7 +27,7 @@ namespace fp8kv {
 namespace {
 
 constexpr int kQsThreads = 256;
-constexpr int kQsSteps = 4;                       // row groups per wave
+constexpr int kQsSteps = 2;                       // row groups per wave
 constexpr int kQsRowsPerWave = 4 * kQsSteps;      // 16 lanes per row
 constexpr int kQsRowsPerBlock = kQsRowsPerWave * (kQsThreads / 64);
 
@@ -47,11 +50,24 @@ __device__ __forceinline__ void unpack_words(const uint4& v, uint32_t w[4]) {
 __device__ __forceinline__ void unpack_words(const uint2& v, uint32_t w[2]) {
     w[0] = v.x; w[1] = v.y;
 }
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ void store_codes(uint8_t* dst, const uint32_t* c, uint2*) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(c[0], c[1]);
+    __builtin_nontemporal_store(u32x2{c[0], c[1]}, reinterpret_cast<u32x2*>(dst));
 }
 __device__ __forceinline__ void store_codes(uint8_t* dst, const uint32_t* c, uint32_t*) {
-    *reinterpret_cast<uint32_t*>(dst) = c[0];
+    __builtin_nontemporal_store(c[0], reinterpret_cast<uint32_t*>(dst));
+}
+
+// One lane's bf16 elements of a row, non-temporal.
+__device__ __forceinline__ uint4 load_row(const uint16_t* p, uint4*) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint2 load_row(const uint16_t* p, uint2*) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    return make_uint2(v[0], v[1]);
 }
 
 // Row r of K (or of V) is (token r / H, head r % H). HSHIFT = log2(H) when
@@ -107,8 +123,8 @@ __global__ __launch_bounds__(kQsThreads) void kv_quant_scatter_kernel(QuantScatt
         split_row<HSHIFT>(min(r, nrows - 1), H, t, h);
         head[s] = h;
         slot[s] = p.slot_ids[t];
-        const In v = *reinterpret_cast<const In*>(src + (int64_t)t * st_tok +
-                                                  (int64_t)h * st_head + li * EPL);
+        const In v = load_row(src + (int64_t)t * st_tok + (int64_t)h * st_head + li * EPL,
+                              (In*)nullptr);
         unpack_words(v, w[s]);
     }
 
