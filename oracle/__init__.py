@@ -22,10 +22,12 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
-SOURCES = ["e4m3.c", "quant.c", "attn.c"]
+SOURCES = ["e4m3.c", "quant.c", "attn.c", "index.c"]
 
 E4M3 = 0
 E5M2 = 1
+KEYS_MXFP4 = 0
+KEYS_E4M3 = 1
 
 _lib = None
 
@@ -72,6 +74,15 @@ def _load():
                                          P, P, I64, I64, P, I64, P,
                                          I64, I64, I64, I64, I64, I64, D, I64,
                                          P, I64, P]
+    lib.fo_e2m1_value.argtypes = [ctypes.c_uint]
+    lib.fo_e2m1_value.restype = D
+    lib.fo_e8m0_value.argtypes = [ctypes.c_uint]
+    lib.fo_e8m0_value.restype = D
+    lib.fo_mxfp4_encode_group.argtypes = [P, P, P]
+    lib.fo_index_keys_mxfp4.argtypes = [P, I64, I64, I64, P, I64, P, I64]
+    lib.fo_index_score.argtypes = [I, P, I64, I64, I64, P, I64, I64, I64,
+                                   P, I64, I64, P, I64, I64,
+                                   I64, I64, I64, I64, I64, P]
     _lib = lib
     return lib
 
@@ -220,4 +231,76 @@ def paged_decode_attn(q, k_cache, v_cache, k_scale, v_scale, block_tables,
         _ptr(bt), bt.strides[0] // 4, _ptr(cl), B, R, Hq, num_kv_heads, D,
         block_size, float(softmax_scale), int(partition_tokens),
         None if sel is None else _ptr(sel), nsel, _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------- index keys
+def e2m1_value(code: int) -> float:
+    return _load().fo_e2m1_value(code)
+
+
+def e8m0_value(code: int) -> float:
+    return _load().fo_e8m0_value(code)
+
+
+def mxfp4_encode_group(x):
+    """One group of 32 float32 values -> (exponent code, 16 packed bytes)."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    assert x.shape == (32,)
+    packed = np.zeros(16, np.uint8)
+    e = np.zeros(1, np.uint8)
+    _load().fo_mxfp4_encode_group(_ptr(x), _ptr(packed), _ptr(e))
+    return int(e[0]), packed
+
+
+def index_keys_mxfp4(keys_bits):
+    """bf16 bits [N, D] (rows of unit inner stride) -> (packed uint8
+    [N, D/2], exponent codes uint8 [N, D/32])."""
+    k = np.asarray(keys_bits)
+    assert k.dtype == np.uint16 and k.ndim == 2 and k.strides[1] == 2
+    n, d = k.shape
+    assert d % 32 == 0
+    packed = np.zeros((n, d // 2), np.uint8)
+    exps = np.zeros((n, d // 32), np.uint8)
+    _load().fo_index_keys_mxfp4(_ptr(k), n, d, k.strides[0] // 2, _ptr(packed),
+                                d // 2, _ptr(exps), d // 32)
+    return packed, exps
+
+
+def index_keys_e4m3(keys_bits, threads: int = 1):
+    """bf16 bits [N, D] -> (E4M3 codes uint8 [N, D], fp32 scales [N]): the
+    per-row quantizer of the KV cache applied to the keys."""
+    return quantize_rows_bf16(keys_bits, E4M3, threads)
+
+
+def index_score(q_bits, w, key_format, codes, scales):
+    """score [B, R, N] (float64) = sum_h w[b,r,h] * relu(q[b,r,h,:] . k^[b,n,:]).
+
+    q_bits  uint16 (bf16 bits) [B, R, H, D] view, last stride 1.
+    w       float32 [B, R, H] view.
+    codes   uint8 [B, N, D] (E4M3) or [B, N, D/2] (MXFP4), last stride 1.
+    scales  float32 [B, N] (E4M3) or uint8 [B, N, D/32] (MXFP4 exponents).
+    """
+    q = np.asarray(q_bits)
+    assert q.dtype == np.uint16 and q.ndim == 4 and q.strides[3] == 2
+    B, R, H, D = q.shape
+    w = np.asarray(w, dtype=np.float32)
+    assert w.shape == (B, R, H)
+    qs, ws = _estrides(q), _estrides(w)
+    codes = np.asarray(codes, dtype=np.uint8)
+    assert codes.ndim == 3 and codes.strides[2] == 1
+    N = codes.shape[1]
+    if key_format == KEYS_MXFP4:
+        scales = np.asarray(scales, dtype=np.uint8)
+        assert scales.shape == (B, N, D // 32) and scales.strides[2] == 1
+        sb, ss = scales.strides[0], scales.strides[1]
+    else:
+        scales = np.asarray(scales, dtype=np.float32)
+        assert scales.shape == (B, N)
+        sb, ss = scales.strides[0] // 4, scales.strides[1] // 4
+    out = np.empty((B, R, N), np.float64)
+    _load().fo_index_score(int(key_format), _ptr(q), qs[0], qs[1], qs[2],
+                           _ptr(w), ws[0], ws[1], ws[2],
+                           _ptr(codes), codes.strides[0], codes.strides[1],
+                           _ptr(scales), sb, ss, B, R, H, D, N, _ptr(out))
     return out

@@ -23,6 +23,8 @@
  *           cache" (sglang-jax #1776), description and "Three design
  *           points": e4m3 range 448, 0.0156 subnormal floor, ~6% vs ~12.5%
  *           worst-case relative error for e4m3 vs e5m2.
+ *   [OCPMX] OCP Microscaling Formats (MX) Specification v1.0: E2M1 (FP4,
+ *           bias 1, max 6, no inf/NaN) and the E8M0 shared scale 2^(c-127).
  *   [OFP8]  OCP 8-bit Floating Point Specification (OFP8) rev. 1.0: the bit
  *           layouts of E4M3 (bias 7, no infinities, S.1111.111 = NaN, max
  *           448) and E5M2 (bias 15, IEEE-style inf/NaN, max 57344).
@@ -95,6 +97,24 @@ void fo_paged_decode_attn(
     int64_t B, int64_t R, int64_t Hq, int64_t Hkv, int64_t D,
     int64_t block_size, double softmax_scale, int64_t partition_tokens,
     const int64_t* rows_sel, int64_t n_rows_sel, double* out);
+
+/* ---- compressed index keys and the index scorer (index.c) --------------
+ * [ATOM] description, compressed-index bullet and the stacked-scorer
+ * paragraph. Parity: the codec is pinned by closed forms, the OCP tables
+ * and brute force; the nibble order and the zero-group code are
+ * conventions (parity unpinned beyond self-consistency); the scorer is
+ * pinned by closed forms and an independent float64 evaluation. */
+enum { FO_KEYS_MXFP4 = 0, FO_KEYS_E4M3 = 1 };
+double fo_e2m1_value(unsigned code);                 /* 4-bit code -> value   */
+double fo_e8m0_value(unsigned code);                 /* 2^(code - 127)        */
+void   fo_mxfp4_encode_group(const float* x, uint8_t* packed, uint8_t* exp_code);
+void   fo_index_keys_mxfp4(const uint16_t* keys, int64_t n, int64_t d, int64_t ks,
+                           uint8_t* packed, int64_t ps, uint8_t* exps, int64_t es);
+void   fo_index_score(int key_format, const uint16_t* q, int64_t qb, int64_t qr, int64_t qh,
+                      const float* w, int64_t wb, int64_t wr, int64_t wh,
+                      const void* codes, int64_t cb, int64_t cs,
+                      const void* scales, int64_t sb, int64_t ss,
+                      int64_t B, int64_t R, int64_t H, int64_t D, int64_t N, double* out);
 
 #ifdef __cplusplus
 }
