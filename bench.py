@@ -16,9 +16,10 @@ events on the stream it runs on, for the roofline object.
 Also measured in the same run (reported under "also"): quantize+scatter
 tokens/s on the 4096-token prefill chunk (fused qkv, K/V strided slices,
 random slots in a 1,048,576-slot pool, 32 rotating input sets so reads come
-from HBM), the cache-build bandwidth, and the long-context verify decode
+from HBM), the cache-build bandwidth, the long-context verify decode
 (4 requests of 256K..1M tokens, 4 verify rows, 16/4 heads, 64-token
-blocks).
+blocks), and the compressed-index scorer (8 x 256 rows x 16 heads x 65,536
+keys, MXFP4 and E4M3 keys) with its key encoders.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -50,7 +51,7 @@ def parse():
                     help="decode split: ranges per KV head (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the prefill-chunk and long-context extras")
+                    help="skip the prefill-chunk, long-context and index extras")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times "
                          "(the known-size reference for HBM byte counters)")
@@ -336,6 +337,7 @@ def main():
     if not args.no_extras:
         result["also"].update(prefill_quant_scatter(torch, fk, synth, dev, stream))
         result["also"].update(longctx_decode(torch, fk, synth, dev, stream))
+        result["also"].update(index_scorer(torch, fk, synth, dev, stream))
 
     if not args.no_cpu_baseline:
         log("timing the oracle on host cores...")
@@ -425,6 +427,43 @@ def longctx_decode(torch, fk, synth, dev, stream, reps=20):
            "longctx_split_kernel_GBps": round((dec - B * R * Hq * D * 2) / (p_avg * 1e-3) / 1e9, 1),
            "longctx_cache_build_GBps": round(build_gbs, 1)}
     del k_cache, v_cache, k_plane, v_plane
+    torch.cuda.empty_cache()
+    return res
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def index_scorer(torch, fk, synth, dev, stream, reps=20):
+    """The compressed-index workload: 8 requests x 256 query rows x 16 index
+    heads x 65,536 keys (dim 128), keys stored as MXFP4 and as E4M3; the
+    scorer's useful work is 2 * B * R * H * N * 128 flops (bf16 MFMA)."""
+    log("index scorer (8 x 256 rows x 16 heads x 65,536 keys)...")
+    case = synth.index_workload(seed=4, device=dev)
+    B, R, H, _ = case.q.shape
+    N = case.keys.shape[1]
+    flops = 2.0 * B * R * H * N * 128
+    out = torch.empty((B, R, N), dtype=torch.float32, device=dev)
+    res = {}
+    for name, fmt, kbytes in (("mxfp4", fk.KEYS_MXFP4, 64 + 4),
+                              ("e4m3", fk.KEYS_E4M3, 128 + 4)):
+        codes, scales = fk.index_keys_quantize(case.keys, fmt)
+        enc = time_events(lambda: fk.index_keys_quantize(case.keys, fmt, codes, scales),
+                          reps, stream)
+        for _ in range(3):
+            fk.index_score_mxfp4(case.q, case.w, fmt, codes, scales, out=out)
+        ms = time_events(lambda: fk.index_score_mxfp4(case.q, case.w, fmt, codes,
+                                                      scales, out=out), reps, stream)
+        avg = sum(ms) / len(ms)
+        e_avg = sum(enc) / len(enc)
+        tf = flops / (avg * 1e-3) / 1e12
+        res[f"index_score_{name}_us"] = round(avg * 1e3, 1)
+        res[f"index_score_{name}_TFLOPs"] = round(tf, 1)
+        res[f"index_score_{name}_mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+        res[f"index_keys_{name}_GBps"] = round(
+            B * N * (256 + kbytes) / (e_avg * 1e-3) / 1e9, 1)
+        del codes, scales
+    del case, out
     torch.cuda.empty_cache()
     return res
 

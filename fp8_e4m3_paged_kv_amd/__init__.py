@@ -25,6 +25,9 @@ DTYPE_BF16 = 1
 DTYPE_FP16 = 2
 DTYPE_FP32 = 3
 
+KEYS_MXFP4 = 0
+KEYS_E4M3 = 1
+
 _TORCH_DTYPE = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_FP16,
                 torch.float32: DTYPE_FP32}
 
@@ -71,6 +74,14 @@ def lib():
     L.fp8kv_paged_decode_workspace_bytes.restype = I64
     L.fp8kv_paged_decode_num_ranges.argtypes = [I32, I32]
     L.fp8kv_paged_decode_num_ranges.restype = I32
+    L.fp8kv_index_keys_quantize.argtypes = [P, I64, I64, I32, I32, P, I64, P,
+                                            I64, P]
+    L.fp8kv_index_keys_quantize.restype = ctypes.c_int
+    L.fp8kv_index_score_mxfp4.argtypes = [P, I64, I64, I64, I32, P, I64, I64,
+                                          I64, I32, P, I64, I64, P, I64, I64,
+                                          I32, I32, I32, I32, I32, I32, P,
+                                          I64, I64, P]
+    L.fp8kv_index_score_mxfp4.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -257,4 +268,79 @@ def paged_decode_merge(workspace, out, *, rows, num_q_heads, num_kv_heads,
         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
         _TORCH_DTYPE[out.dtype], _stream(out.device)))
+    return out
+
+
+def index_keys_quantize(keys: torch.Tensor, key_format: int, codes=None,
+                        scales=None):
+    """Encode bf16 index keys [..., N, 128] (rows of unit inner stride).
+    KEYS_MXFP4: returns (packed uint8 [..., N, 64], E8M0 codes uint8
+    [..., N, 4]); KEYS_E4M3: (codes uint8 [..., N, 128], fp32 scales
+    [..., N])."""
+    _dev(keys)
+    if keys.dtype != torch.bfloat16 or keys.shape[-1] != 128:
+        raise ValueError("keys must be bf16 [..., 128]")
+    lead = keys.shape[:-1]
+    flat = keys.reshape(-1, 128)
+    if flat.stride(1) != 1:
+        raise ValueError("keys need a contiguous last dimension")
+    n = flat.shape[0]
+    mx = key_format == KEYS_MXFP4
+    if codes is None:
+        codes = torch.empty(lead + ((64,) if mx else (128,)), dtype=torch.uint8,
+                            device=keys.device)
+    if scales is None:
+        scales = torch.empty(lead + ((4,) if mx else ()),
+                             dtype=torch.uint8 if mx else torch.float32,
+                             device=keys.device)
+    _dev(codes, scales)
+    cf = codes.view(-1, codes.shape[-1])
+    sf = scales.view(-1, 4) if mx else scales.view(-1)
+    if cf.shape[0] != n or sf.shape[0] != n:
+        raise ValueError("codes / scales do not match the number of keys")
+    _check(lib().fp8kv_index_keys_quantize(
+        flat.data_ptr(), flat.stride(0), n, 128, int(key_format),
+        cf.data_ptr(), cf.stride(0), sf.data_ptr(), sf.stride(0),
+        _stream(keys.device)))
+    return codes, scales
+
+
+def index_score_mxfp4(q: torch.Tensor, w: torch.Tensor, key_format: int,
+                      codes: torch.Tensor, scales: torch.Tensor, *,
+                      key_chunk: int = 0, out=None):
+    """score[b, r, n] = sum_h w[b, r, h] * relu(q[b, r, h, :] . k^[b, n, :]).
+
+    q       bf16 [B, R, H, 128] (H <= 16), w fp32 [B, R, H];
+    codes   uint8 [B, N, 64] (MXFP4) or [B, N, 128] (E4M3);
+    scales  uint8 [B, N, 4] (MXFP4 exponents) or fp32 [B, N] (E4M3).
+    Returns out fp32 [B, R, N]."""
+    _dev(q, w, codes, scales)
+    if q.dim() != 4 or q.dtype != torch.bfloat16 or q.stride(3) != 1:
+        raise ValueError("q must be bf16 [B, R, H, D], contiguous D")
+    B, R, H, D = q.shape
+    if w.shape != (B, R, H) or w.dtype != torch.float32:
+        raise ValueError("w must be fp32 [B, R, H]")
+    mx = key_format == KEYS_MXFP4
+    if codes.dim() != 3 or codes.dtype != torch.uint8 or codes.stride(2) != 1:
+        raise ValueError("codes must be uint8 [B, N, bytes], contiguous bytes")
+    N = codes.shape[1]
+    if mx:
+        if scales.shape != (B, N, 4) or scales.dtype != torch.uint8 or \
+                scales.stride(2) != 1:
+            raise ValueError("MXFP4 exponents must be uint8 [B, N, 4]")
+    elif scales.shape != (B, N) or scales.dtype != torch.float32:
+        raise ValueError("E4M3 key scales must be fp32 [B, N]")
+    if out is None:
+        out = torch.empty((B, R, N), dtype=torch.float32, device=q.device)
+    _dev(out)
+    if out.shape != (B, R, N) or out.dtype != torch.float32 or \
+            (N > 1 and out.stride(2) != 1):
+        raise ValueError("out must be fp32 [B, R, N], contiguous N")
+    _check(lib().fp8kv_index_score_mxfp4(
+        q.data_ptr(), q.stride(0), q.stride(1), q.stride(2), DTYPE_BF16,
+        w.data_ptr(), w.stride(0), w.stride(1), w.stride(2), int(key_format),
+        codes.data_ptr(), codes.stride(0), codes.stride(1),
+        scales.data_ptr(), scales.stride(0), scales.stride(1),
+        B, R, H, D, N, int(key_chunk), out.data_ptr(), out.stride(0),
+        out.stride(1), _stream(q.device)))
     return out

@@ -378,4 +378,122 @@ int fp8kv_paged_decode_attn_fp8(
         out_stride_head, out_dtype, stream);
 }
 
+int fp8kv_index_keys_quantize(
+    const void* keys, int64_t key_stride, int64_t num_keys, int32_t head_dim,
+    int32_t key_format, uint8_t* codes, int64_t code_stride,
+    void* scales, int64_t scale_stride, void* stream) {
+    if (head_dim != fp8kv::kIndexDim)
+        return fail(FP8KV_E_UNSUPPORTED, "index keys: head_dim %d, only 128", head_dim);
+    if (key_format != FP8KV_KEYS_MXFP4 && key_format != FP8KV_KEYS_E4M3)
+        return fail(FP8KV_E_UNSUPPORTED, "key_format %d", key_format);
+    if (num_keys < 0 || num_keys > (INT64_C(1) << 36))
+        return fail(FP8KV_E_SHAPE, "num_keys %lld", (long long)num_keys);
+    if (!keys || !codes || !scales)
+        return fail(FP8KV_E_NULL, "index_keys_quantize: a required pointer is NULL");
+    if (key_stride < 0 || code_stride < 0 || scale_stride < 0)
+        return fail(FP8KV_E_STRIDE, "index_keys_quantize: negative stride");
+    if (!aligned(keys, 16) || key_stride % 8)
+        return fail(FP8KV_E_ALIGN, "key rows must start on 16-byte boundaries");
+    const bool e4m3 = key_format == FP8KV_KEYS_E4M3;
+    if (!aligned(codes, e4m3 ? 8 : 4) || code_stride % (e4m3 ? 8 : 4))
+        return fail(FP8KV_E_ALIGN, "code rows must start on %d-byte boundaries", e4m3 ? 8 : 4);
+    if (e4m3 && !aligned(scales, 4))
+        return fail(FP8KV_E_ALIGN, "fp32 key scales misaligned");
+    if (num_keys == 0) return ok();
+    fp8kv::IndexKeysParams p;
+    p.keys = static_cast<const uint16_t*>(keys);
+    p.key_stride = key_stride;
+    p.codes = codes;
+    p.code_stride = code_stride;
+    p.scales = scales;
+    p.scale_stride = scale_stride;
+    p.num_keys = num_keys;
+    return launched(fp8kv::launch_index_keys(p, key_format, (hipStream_t)stream),
+                    "index_keys_quantize");
+}
+
+int fp8kv_index_score_mxfp4(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype,
+    const float* w, int64_t w_stride_b, int64_t w_stride_row, int64_t w_stride_head,
+    int32_t key_format, const uint8_t* codes, int64_t codes_stride_b,
+    int64_t codes_stride_key, const void* scales, int64_t scales_stride_b,
+    int64_t scales_stride_key, int32_t batch, int32_t rows, int32_t num_heads,
+    int32_t head_dim, int32_t num_keys, int32_t key_chunk,
+    float* out, int64_t out_stride_b, int64_t out_stride_row, void* stream) {
+    if (head_dim != fp8kv::kIndexDim)
+        return fail(FP8KV_E_UNSUPPORTED, "index scorer: head_dim %d, only 128", head_dim);
+    if (q_dtype != FP8KV_DTYPE_BF16)
+        return fail(FP8KV_E_UNSUPPORTED, "q_dtype %d: only BF16 queries", q_dtype);
+    if (key_format != FP8KV_KEYS_MXFP4 && key_format != FP8KV_KEYS_E4M3)
+        return fail(FP8KV_E_UNSUPPORTED, "key_format %d", key_format);
+    if (num_heads < 1 || num_heads > fp8kv::kIndexMaxHeads)
+        return fail(FP8KV_E_UNSUPPORTED, "num_heads %d: 1..%d index heads", num_heads,
+                    fp8kv::kIndexMaxHeads);
+    if (batch < 0 || rows < 1 || num_keys < 0)
+        return fail(FP8KV_E_SHAPE, "batch %d, rows %d, num_keys %d", batch, rows, num_keys);
+    if (key_chunk < 0 || key_chunk % 16)
+        return fail(FP8KV_E_SHAPE, "key_chunk %d: 0 (auto) or a positive multiple of 16", key_chunk);
+    if (!q || !w || !codes || !scales || !out)
+        return fail(FP8KV_E_NULL, "index_score: a required pointer is NULL");
+    if (q_stride_b < 0 || q_stride_row < 0 || q_stride_head < 0 || w_stride_b < 0 ||
+        w_stride_row < 0 || w_stride_head < 0 || codes_stride_b < 0 || codes_stride_key < 0 ||
+        scales_stride_b < 0 || scales_stride_key < 0 || out_stride_b < 0 || out_stride_row < 0)
+        return fail(FP8KV_E_STRIDE, "index_score: negative stride");
+    if (!aligned(q, 16) || q_stride_b % 8 || q_stride_row % 8 || q_stride_head % 8)
+        return fail(FP8KV_E_ALIGN, "q rows must start on 16-byte boundaries");
+    if (!aligned(codes, 16) || codes_stride_b % 16 || codes_stride_key % 16)
+        return fail(FP8KV_E_ALIGN, "key code rows must start on 16-byte boundaries");
+    const bool e4m3 = key_format == FP8KV_KEYS_E4M3;
+    if (!aligned(w, 4) || !aligned(out, 4) || (e4m3 && !aligned(scales, 4)))
+        return fail(FP8KV_E_ALIGN, "w, out or key scales misaligned");
+    if (batch == 0 || num_keys == 0) return ok();
+
+    const int32_t row_groups = (rows + fp8kv::kIndexRowsPerBlock - 1) / fp8kv::kIndexRowsPerBlock;
+    int32_t chunk = key_chunk;
+    if (chunk == 0) {
+        // two waves per SIMD, every workgroup a (request, row group, chunk)
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess)
+            return fail(FP8KV_E_LAUNCH, "no HIP device to size the index scorer for");
+        const int slots = fp8kv::decode_wave_slots(dev);
+        if (slots <= 0) return fail(FP8KV_E_LAUNCH, "cannot query the CU count of device %d", dev);
+        const int64_t wgs_wanted = 2 * (int64_t)slots / 4;
+        const int64_t per_chunk = (int64_t)batch * row_groups;
+        const int64_t chunks = (wgs_wanted + per_chunk - 1) / per_chunk;
+        chunk = (int32_t)round_up((num_keys + chunks - 1) / chunks, 16);
+    }
+    const int64_t chunks = ((int64_t)num_keys + chunk - 1) / chunk;
+    if ((int64_t)batch * chunks * row_groups > INT32_MAX / 2)
+        return fail(FP8KV_E_SHAPE, "index scorer grid too large");
+
+    fp8kv::IndexScoreParams p;
+    p.q = static_cast<const uint16_t*>(q);
+    p.q_stride_b = q_stride_b;
+    p.q_stride_row = q_stride_row;
+    p.q_stride_head = q_stride_head;
+    p.w = w;
+    p.w_stride_b = w_stride_b;
+    p.w_stride_row = w_stride_row;
+    p.w_stride_head = w_stride_head;
+    p.codes = codes;
+    p.codes_stride_b = codes_stride_b;
+    p.codes_stride_key = codes_stride_key;
+    p.scales = static_cast<const uint8_t*>(scales);
+    p.scales_stride_b = e4m3 ? scales_stride_b * 4 : scales_stride_b;
+    p.scales_stride_key = e4m3 ? scales_stride_key * 4 : scales_stride_key;
+    p.out = out;
+    p.out_stride_b = out_stride_b;
+    p.out_stride_row = out_stride_row;
+    p.batch = batch;
+    p.rows = rows;
+    p.heads = num_heads;
+    p.num_keys = num_keys;
+    p.key_chunk = chunk;
+    p.chunks = (int32_t)chunks;
+    p.row_groups = row_groups;
+    return launched(fp8kv::launch_index_score(p, key_format, (hipStream_t)stream),
+                    "index_score");
+}
+
 }  // extern "C"

@@ -37,21 +37,6 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
     return v;
 }
 
-// E4M3 (OCP E4M3FN) code of a finite fp32 value: round to nearest, ties to
-// the even code, magnitudes above 448 saturate to 448. Both rounding ranges
-// are computed and selected, so the wave never diverges.
-__device__ __forceinline__ uint32_t e4m3_encode(float q) {
-    const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
-    const float a = fminf(fabsf(q), kE4M3Max);
-    // normal range (a >= 2^-6): round the fp32 mantissa to 3 bits
-    uint32_t b = __float_as_uint(a);
-    b += 0x7FFFFu + ((b >> 20) & 1u);
-    const uint32_t normal = (b >> 20) - (120u << 3);   // rebias 127 -> 7
-    // subnormal range (a < 2^-6): integer multiple of 2^-9, nearest even
-    const uint32_t sub = (uint32_t)__builtin_rintf(a * 512.0f);
-    return sign | (a >= 0x1p-6f ? normal : sub);
-}
-
 // Four fp32 values -> four E4M3 codes (bytes 0..3), round to nearest even,
 // magnitudes above 448 saturating to +-448: the gfx950 OCP converter after
 // a clamp (the quantizer's quotients never exceed 448 * (1 + 2^-23)).
@@ -63,6 +48,42 @@ __device__ __forceinline__ uint32_t e4m3x4_encode(float a, float b, float c, flo
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
+}
+
+// q[i] = x[i] / scale for every element of a row, each the correctly rounded
+// quotient: one IEEE reciprocal of the scale and one FMA correction per
+// element (Markstein): q0 = x*r, e = x - q0*s (exact), q = q0 + e*r, with
+// the sign of x restored (the correction turns -0 into +0). A zero scale
+// divides by 1 (the row's codes are then the signed zeros of x). Scales
+// below 2^-100 are first multiplied by 2^64, as are their elements (exact),
+// so the reciprocal stays finite; that path is taken by the whole wave.
+// Checked exhaustively: for every bf16 row maximum and every bf16 element of
+// either sign up to it in magnitude, the E4M3 code of q equals that of the
+// IEEE quotient.
+template <int N>
+__device__ __forceinline__ void row_quotients(const float (&x)[N], float scale, float (&q)[N]) {
+#pragma clang fp contract(off)
+    if (__builtin_expect(__any(scale < 0x1p-100f && scale != 0.0f), 0)) {
+        const float f = scale < 0x1p-100f ? 0x1p64f : 1.0f;
+        const float ss = scale == 0.0f ? 1.0f : scale * f;
+        const float rcp = 1.0f / ss;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const float xs = scale == 0.0f ? x[i] : x[i] * f;
+            const float q0 = xs * rcp;
+            const float e = __builtin_fmaf(-q0, ss, xs);
+            q[i] = __builtin_copysignf(__builtin_fmaf(e, rcp, q0), x[i]);
+        }
+    } else {
+        const float ss = scale == 0.0f ? 1.0f : scale;
+        const float rcp = 1.0f / ss;                 // IEEE binary32 division
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const float q0 = x[i] * rcp;
+            const float e = __builtin_fmaf(-q0, ss, x[i]);
+            q[i] = __builtin_copysignf(__builtin_fmaf(e, rcp, q0), x[i]);
+        }
+    }
 }
 
 // Two E4M3 codes (16-bit half HI of w) -> two bf16, exact.
@@ -98,20 +119,6 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
     return __builtin_amdgcn_perm(hi, lo, sel);
-}
-
-// Transpose a 4 x 4 byte block: rows a..d (one dword each) -> columns.
-// c[i] holds byte i of a, b, c, d in bytes 0..3.
-__device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c,
-                                             uint32_t d, uint32_t out[4]) {
-    const uint32_t ab_lo = perm(b, a, 0x05010400u);   // a0 b0 a1 b1
-    const uint32_t ab_hi = perm(b, a, 0x07030602u);   // a2 b2 a3 b3
-    const uint32_t cd_lo = perm(d, c, 0x05010400u);   // c0 d0 c1 d1
-    const uint32_t cd_hi = perm(d, c, 0x07030602u);   // c2 d2 c3 d3
-    out[0] = perm(cd_lo, ab_lo, 0x05040100u);         // a0 b0 c0 d0
-    out[1] = perm(cd_lo, ab_lo, 0x07060302u);         // a1 b1 c1 d1
-    out[2] = perm(cd_hi, ab_hi, 0x05040100u);         // a2 b2 c2 d2
-    out[3] = perm(cd_hi, ab_hi, 0x07060302u);         // a3 b3 c3 d3
 }
 
 }  // namespace fp8kv

@@ -71,4 +71,42 @@ hipError_t launch_decode_partitions(const DecodeParams& p, int head_dim, hipStre
 hipError_t launch_decode_merge(const MergeParams& p, int head_dim,
                                hipStream_t stream);
 
+// Compressed index keys (head_dim 128).
+constexpr int kKeysMXFP4 = 0;
+constexpr int kKeysE4M3 = 1;
+constexpr int kIndexDim = 128;
+constexpr int kIndexMaxHeads = 16;     // MFMA M dimension
+constexpr int kIndexRowsPerWave = 8;
+constexpr int kIndexRowsPerBlock = 4 * kIndexRowsPerWave;
+
+struct IndexKeysParams {
+    const uint16_t* keys;      // bf16 bits [num_keys, 128], row stride key_stride elements
+    int64_t key_stride;
+    uint8_t* codes;            // E4M3 [., 128] / packed E2M1 [., 64]; row stride in bytes
+    int64_t code_stride;
+    void* scales;              // E4M3: fp32 [.], MXFP4: E8M0 bytes [., 4]; row stride in elements
+    int64_t scale_stride;
+    int64_t num_keys;
+};
+
+struct IndexScoreParams {
+    const uint16_t* q;         // bf16 bits [B, rows, heads, 128]
+    int64_t q_stride_b, q_stride_row, q_stride_head;
+    const float* w;            // [B, rows, heads]
+    int64_t w_stride_b, w_stride_row, w_stride_head;
+    const uint8_t* codes;      // per request, keys at codes_stride_key bytes
+    int64_t codes_stride_b, codes_stride_key;
+    const uint8_t* scales;     // per request; strides in bytes
+    int64_t scales_stride_b, scales_stride_key;
+    float* out;                // [B, rows, num_keys], key stride 1
+    int64_t out_stride_b, out_stride_row;
+    int32_t batch, rows, heads, num_keys;
+    int32_t key_chunk;         // keys per workgroup, a multiple of 16
+    int32_t chunks;            // ceil(num_keys / key_chunk)
+    int32_t row_groups;        // ceil(rows / kIndexRowsPerBlock)
+};
+
+hipError_t launch_index_keys(const IndexKeysParams& p, int key_format, hipStream_t stream);
+hipError_t launch_index_score(const IndexScoreParams& p, int key_format, hipStream_t stream);
+
 }  // namespace fp8kv

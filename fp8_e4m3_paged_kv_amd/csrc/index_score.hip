@@ -1,0 +1,301 @@
+// index_score.hip -- compressed-index keys and the decode-sized index scorer
+// ("fix(qwen4-exp): register the QSA FP8 scale planes for KV offload",
+// ROCm/ATOM #2655, description: the compressed-index bullet and the stacked
+// decode scorer paragraph).
+//
+// Keys. A compressed index key (head_dim 128) is stored either as E4M3
+// codes with one fp32 scale (the KV cache's row quantizer), or as MXFP4:
+// 64 bytes of E2M1 pairs (element 2j in the low nibble of byte j) and one
+// E8M0 exponent per 32 dims, the exponent the smallest e with
+// amax <= 6 * 2^e so that no group clips; each element is x / 2^e rounded
+// to the nearest E2M1 value, ties to the even code, sign kept.
+//
+// Scorer. For request b, query row r and key n:
+//     score[b, r, n] = sum_h w[b, r, h] * max(0, q[b, r, h, :] . k^[b, n, :])
+// One v_mfma_f32_16x16x32_bf16 chain (4 k-steps over 128 dims) multiplies
+// the 16 index heads of one query row (M) by 16 keys (N, widened exactly to
+// bf16 once per tile and shared by every row of the wave): the heads fill
+// the MFMA rows, as rows x heads do in the page's stacked scorer. Lane
+// (g, i) then holds the dots of heads 4g .. 4g+3 with key i; the ReLU and
+// the head weights are applied in the lane, and four rows at a time are
+// summed over the four lane groups by two cross-lane swaps
+// (v_permlane32_swap, v_permlane16_swap), which leave row 4c + g of the
+// quad in lane group g. E4M3 key scales are >= 0, so they multiply the
+// summed score; MXFP4 exponents vary along the dims and are folded into the
+// widened keys (E2M1 * 2^e is exact in bf16).
+#include <hip/hip_runtime.h>
+
+#include "fp8kv_device.h"
+#include "fp8kv_internal.h"
+
+namespace fp8kv {
+namespace {
+
+constexpr int kScoreWaves = 4;
+
+// E2M1 code of |v| (v = x / 2^e, so |v| <= 6): nearest of
+// {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even code. The thresholds are the
+// midpoints; a midpoint rounds up exactly when the upper neighbour's code is
+// even.
+__device__ __forceinline__ uint32_t e2m1_code(float a) {
+    return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+           (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+           (uint32_t)(a > 5.0f);
+}
+
+// ---------------------------------------------------------------- keys
+// One 16-lane DPP row per key (8 bf16 per lane), 4 keys per wave step, two
+// steps, four waves: 32 keys per workgroup.
+template <int FMT>
+__global__ __launch_bounds__(256) void index_keys_kernel(IndexKeysParams p) {
+#pragma clang fp contract(off)
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int sub = lane >> 4;
+    const int li = lane & 15;
+    const int64_t key0 = (int64_t)blockIdx.x * 32 + wave * 8;
+    uint4 raw[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int64_t key = min(key0 + 4 * s + sub, p.num_keys - 1);
+        raw[s] = *reinterpret_cast<const uint4*>(p.keys + key * p.key_stride + li * 8);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int64_t key = key0 + 4 * s + sub;
+        const uint32_t wds[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = bf16_lo(wds[i]);
+            x[2 * i + 1] = bf16_hi(wds[i]);
+        }
+        uint32_t amax_bits = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax_bits = max(amax_bits, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+        if (FMT == kKeysE4M3) {
+            const float amax = __uint_as_float(row16_max_u32(amax_bits));
+            const float scale = amax / kE4M3Max;         // IEEE binary32 division
+            float qv[8];
+            row_quotients(x, scale, qv);
+            const uint32_t lo = e4m3x4_encode(qv[0], qv[1], qv[2], qv[3]);
+            const uint32_t hi = e4m3x4_encode(qv[4], qv[5], qv[6], qv[7]);
+            if (key < p.num_keys) {
+                *reinterpret_cast<uint2*>(p.codes + key * p.code_stride + li * 8) = make_uint2(lo, hi);
+                if (li == 0) static_cast<float*>(p.scales)[key * p.scale_stride] = scale;
+            }
+        } else {
+            // a group of 32 dims is one quad of lanes
+            amax_bits = max(amax_bits, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax_bits, 0xB1, 0xF, 0xF, false));
+            amax_bits = max(amax_bits, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax_bits, 0x4E, 0xF, 0xF, false));
+            const float amax = __uint_as_float(amax_bits);
+            int e = 0;
+            if (amax > 0.0f) {
+                int ex;
+                const float mant = frexpf(amax, &ex);       // amax = mant * 2^ex, mant in [.5, 1)
+                e = mant <= 0.75f ? ex - 3 : ex - 2;         // smallest e with amax <= 6 * 2^e
+                e = max(e, -127);
+            }
+            uint32_t packed = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float v = ldexpf(x[i], -e);             // exact wherever a code boundary lies
+                const uint32_t c = e2m1_code(fabsf(v)) | ((__float_as_uint(x[i]) >> 28) & 8u);
+                packed |= c << (4 * i);
+            }
+            if (key < p.num_keys) {
+                *reinterpret_cast<uint32_t*>(p.codes + key * p.code_stride + li * 4) = packed;
+                if ((li & 3) == 0)
+                    static_cast<uint8_t*>(p.scales)[key * p.scale_stride + (li >> 2)] = (uint8_t)(e + 127);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- scorer
+// A 16-key tile, widened to the bf16 B operand of four k-steps. Lane
+// (g, i): key i of the tile, dims [32g, 32g + 32); k-step k takes dims
+// 32g + 8k .. +7, and q is read with the same permutation of the dims.
+template <int FMT>
+struct KeyTile {
+    uint4 raw[2];        // E4M3: the lane's 32 code bytes; MXFP4: 16 packed bytes in raw[0]
+    uint32_t exp;        // MXFP4: E8M0 code of group g of key i
+    float kscale;        // E4M3: scale of key i
+
+    __device__ __forceinline__ void load(const IndexScoreParams& p, const uint8_t* codes,
+                                         const uint8_t* scales, int t, int lane) {
+        const int li = lane & 15, lg = lane >> 4;
+        const int key = min(t + li, p.num_keys - 1);
+        const uint8_t* row = codes + (int64_t)key * p.codes_stride_key;
+        if (FMT == kKeysE4M3) {
+            raw[0] = *reinterpret_cast<const uint4*>(row + 32 * lg);
+            raw[1] = *reinterpret_cast<const uint4*>(row + 32 * lg + 16);
+            kscale = *reinterpret_cast<const float*>(scales + (int64_t)key * p.scales_stride_key);
+        } else {
+            raw[0] = *reinterpret_cast<const uint4*>(row + 16 * lg);
+            exp = scales[(int64_t)key * p.scales_stride_key + lg];
+        }
+    }
+
+    __device__ __forceinline__ void widen(bf16x8 (&kb)[4]) const {
+        if (FMT == kKeysE4M3) {
+            kb[0] = e4m3x8_to_bf16x8(raw[0].x, raw[0].y);
+            kb[1] = e4m3x8_to_bf16x8(raw[0].z, raw[0].w);
+            kb[2] = e4m3x8_to_bf16x8(raw[1].x, raw[1].y);
+            kb[3] = e4m3x8_to_bf16x8(raw[1].z, raw[1].w);
+        } else {
+            // 2^(exp - 127) as an fp32 scale (code 0 is the subnormal 2^-127)
+            const float s = exp == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(exp << 23);
+            const uint32_t w[4] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                // one dword = 8 E2M1 codes = dims 32g + 8k .. +7, element 2j in the low nibble
+                uint32_t h[4];
+                h[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[k], s, 0));
+                h[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[k], s, 1));
+                h[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[k], s, 2));
+                h[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[k], s, 3));
+                kb[k] = __builtin_bit_cast(bf16x8, h);
+            }
+        }
+    }
+};
+
+// a and b exchanged between the lower and upper 32 lanes, then summed: the
+// lower half holds a(l) + a(l + 32), the upper half b(l - 32) + b(l).
+__device__ __forceinline__ float swap32_sum(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// The same between 16-lane rows 2c and 2c + 1: row 2c holds a(l) + a(l + 16),
+// row 2c + 1 holds b(l - 16) + b(l).
+__device__ __forceinline__ float swap16_sum(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Workgroup = 4 waves x RW query rows of one request and one chunk of its
+// keys; each wave scores its rows against every 16-key tile of the chunk.
+// The row groups of one (request, chunk) are placed on one XCD, so their key
+// reads meet in that XCD's L2.
+template <int FMT, int RW>
+__global__ __launch_bounds__(256) void index_score_kernel(IndexScoreParams p) {
+    static_assert(RW % 4 == 0, "rows are reduced four at a time");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int li = lane & 15, lg = lane >> 4;
+
+    int bid = blockIdx.x;
+    const int m = p.row_groups;
+    if (m > 1) {
+        const int xcd = bid & 7, k = bid >> 3;
+        bid = (k / m) * 8 * m + xcd * m + (k % m);
+    }
+    const int rg = bid % m;
+    const int bc = bid / m;
+    const int ck = bc % p.chunks;
+    const int b = bc / p.chunks;
+    if (b >= p.batch) return;
+    const int row0 = (rg * kScoreWaves + wave) * RW;
+    const int n_begin = ck * p.key_chunk;
+    const int n_end = min(n_begin + p.key_chunk, p.num_keys);
+    if (row0 >= p.rows || n_begin >= n_end) return;
+
+    // q (A operand) and w of the wave's rows: lane (g, i) holds head i,
+    // dims [32g, 32g + 32), and the weights of heads 4g .. 4g+3
+    bf16x8 qa[RW][4];
+    float wv[RW][4];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        const int row = row0 + r;
+        const bool rv = row < p.rows;
+        if (rv && li < p.heads) {
+            const uint16_t* qp = p.q + (int64_t)b * p.q_stride_b + (int64_t)row * p.q_stride_row +
+                                 (int64_t)li * p.q_stride_head + 32 * lg;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                qa[r][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 8 * k));
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) qa[r][k] = bf16x8{};
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int h = 4 * lg + j;
+            wv[r][j] = rv && h < p.heads
+                           ? p.w[(int64_t)b * p.w_stride_b + (int64_t)row * p.w_stride_row +
+                                 (int64_t)h * p.w_stride_head]
+                           : 0.0f;
+        }
+    }
+
+    const uint8_t* codes = p.codes + (int64_t)b * p.codes_stride_b;
+    const uint8_t* scales = p.scales + (int64_t)b * p.scales_stride_b;
+    float* out = p.out + (int64_t)b * p.out_stride_b;
+    const int quads = min(RW, p.rows - row0 + 3) / 4;    // quads holding a valid row
+
+    KeyTile<FMT> cur, nxt;
+    cur.load(p, codes, scales, n_begin, lane);
+    for (int t = n_begin; t < n_end; t += 16) {
+        bf16x8 kb[4];
+        cur.widen(kb);
+        const float ks = FMT == kKeysE4M3 ? cur.kscale : 1.0f;
+        if (t + 16 < n_end) nxt.load(p, codes, scales, t + 16, lane);
+        const bool key_ok = t + li < n_end;
+#pragma unroll
+        for (int c = 0; c < RW / 4; ++c) {
+            if (c >= quads) break;
+            float s[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[4 * c + r][k], kb[k], acc, 0, 0, 0);
+                // acc[j] = q(head 4g + j) . key i
+                const float* wr = wv[4 * c + r];
+                float v = fmaxf(acc[0], 0.f) * wr[0];
+                v = __builtin_fmaf(fmaxf(acc[1], 0.f), wr[1], v);
+                v = __builtin_fmaf(fmaxf(acc[2], 0.f), wr[2], v);
+                s[r] = __builtin_fmaf(fmaxf(acc[3], 0.f), wr[3], v);
+            }
+            // lane group g ends with row 4c + g summed over all 16 heads
+            const float sc = swap16_sum(swap32_sum(s[0], s[2]), swap32_sum(s[1], s[3])) * ks;
+            const int row = row0 + 4 * c + lg;
+            if (key_ok && row < p.rows)
+                __builtin_nontemporal_store(sc, out + (int64_t)row * p.out_stride_row + t + li);
+        }
+        cur = nxt;
+    }
+}
+
+template <int FMT>
+hipError_t launch_score(const IndexScoreParams& p, hipStream_t stream) {
+    const int64_t m = p.row_groups;
+    int64_t wgs = (int64_t)p.batch * p.chunks * m;
+    if (m > 1) wgs = (wgs + 8 * m - 1) / (8 * m) * (8 * m);
+    if (wgs > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((index_score_kernel<FMT, kIndexRowsPerWave>), dim3((unsigned)wgs),
+                       dim3(64 * kScoreWaves), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_index_keys(const IndexKeysParams& p, int key_format, hipStream_t stream) {
+    const int64_t blocks = (p.num_keys + 31) / 32;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    dim3 grid((unsigned)blocks), block(256);
+    if (key_format == kKeysE4M3)
+        hipLaunchKernelGGL((index_keys_kernel<kKeysE4M3>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((index_keys_kernel<kKeysMXFP4>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_index_score(const IndexScoreParams& p, int key_format, hipStream_t stream) {
+    return key_format == kKeysE4M3 ? launch_score<kKeysE4M3>(p, stream)
+                                   : launch_score<kKeysMXFP4>(p, stream);
+}
+
+}  // namespace fp8kv

@@ -143,37 +143,8 @@ __global__ __launch_bounds__(kQsThreads) void kv_quant_scatter_kernel(QuantScatt
         amax_bits = row16_max_u32(amax_bits);
         const float amax = __uint_as_float(amax_bits);
         const float scale = amax / kE4M3Max;         // IEEE binary32 division
-        // x / scale, correctly rounded per element from one IEEE reciprocal
-        // and one FMA correction (Markstein): q0 = x*r, e = x - q0*s (exact),
-        // q = q0 + e*r, with the sign of x (the correction turns -0 into +0).
-        // An all-zero row divides by 1 (its codes are the signed zeros of x).
-        // Checked exhaustively: for every bf16 row maximum and every bf16
-        // element of either sign up to it in magnitude, the E4M3 code equals
-        // that of the IEEE quotient.
         float qv[EPL];
-        if (__builtin_expect(__any(scale < 0x1p-100f && scale != 0.0f), 0)) {
-            // rows this small are first scaled by 2^64 (exact) so the
-            // reciprocal stays finite
-            const float f = scale < 0x1p-100f ? 0x1p64f : 1.0f;
-            const float ss = scale == 0.0f ? 1.0f : scale * f;
-            const float rcp = 1.0f / ss;
-#pragma unroll
-            for (int i = 0; i < EPL; ++i) {
-                const float xs = scale == 0.0f ? x[i] : x[i] * f;
-                const float q0 = xs * rcp;
-                const float e = __builtin_fmaf(-q0, ss, xs);
-                qv[i] = __builtin_copysignf(__builtin_fmaf(e, rcp, q0), x[i]);
-            }
-        } else {
-            const float ss = scale == 0.0f ? 1.0f : scale;
-            const float rcp = 1.0f / ss;                 // IEEE binary32 division
-#pragma unroll
-            for (int i = 0; i < EPL; ++i) {
-                const float q0 = x[i] * rcp;
-                const float e = __builtin_fmaf(-q0, ss, x[i]);
-                qv[i] = __builtin_copysignf(__builtin_fmaf(e, rcp, q0), x[i]);
-            }
-        }
+        row_quotients(x, scale, qv);
         uint32_t packed[EPL / 4];
 #pragma unroll
         for (int i = 0; i < EPL / 4; ++i)

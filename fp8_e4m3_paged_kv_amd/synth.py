@@ -259,3 +259,31 @@ def strided_pitch_scenario(seed: int = 7, tokens: int = 8,
     v_rows = (qkv[:, 2 * H * D:].float() * 0.05).to(torch.bfloat16)
     v = v_rows.view(tokens, H, D).clamp(-clamp, clamp)
     return k, v
+
+
+@dataclass
+class IndexCase:
+    """A compressed-index scoring workload."""
+    q: torch.Tensor                 # bf16 [B, R, H, 128]
+    w: torch.Tensor                 # fp32 [B, R, H]
+    keys: torch.Tensor              # bf16 [B, N, 128]
+
+
+def index_case(batch: int, rows: int, heads: int, num_keys: int, seed: int,
+               device="cpu", pool: int = 4, dim: int = 128) -> IndexCase:
+    """q ~ N(0,1) bf16, w ~ U(0,1) fp32 per (row, head); each compressed key
+    is the mean of ``pool`` raw bf16 N(0,1) keys, L2-normalised, rounded to
+    bf16 (the input recipe of the index workload; the pooling is input
+    preparation, not part of the scorer)."""
+    g = gen(seed, device)
+    q = normal_bf16((batch, rows, heads, dim), g, device=device)
+    w = torch.rand((batch, rows, heads), generator=g, device=device)
+    raw = normal_bf16((batch, num_keys, pool, dim), g, device=device)
+    k = raw.float().mean(dim=2)
+    k = k / k.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+    return IndexCase(q, w, k.to(torch.bfloat16))
+
+
+def index_workload(seed: int = 4, device="cpu") -> IndexCase:
+    """8 requests x 256 query rows, 16 index heads, 65,536 keys each."""
+    return index_case(8, 256, 16, 65536, seed, device=device)

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FP8KV_ABI_VERSION 2
+#define FP8KV_ABI_VERSION 3
 
 typedef enum fp8kv_status {
     FP8KV_OK = 0,
@@ -238,6 +238,78 @@ int fp8kv_paged_decode_merge(
     void* out, int64_t out_stride_b, int64_t out_stride_row,
     int64_t out_stride_head, int32_t out_dtype,
     void* stream);
+
+/*
+ * Compressed index keys and the index scorer ("fix(qwen4-exp): register
+ * the QSA FP8 scale planes for KV offload", ROCm/ATOM #2655, description:
+ * the compressed-index bullet and the stacked decode scorer paragraph).
+ * Keys have head_dim 128 and are stored in one of two formats.
+ */
+typedef enum fp8kv_key_format {
+    FP8KV_KEYS_MXFP4 = 0,   /* packed E2M1 pairs + one E8M0 exponent per 32 dims */
+    FP8KV_KEYS_E4M3 = 1     /* E4M3 codes + one fp32 scale per key              */
+} fp8kv_key_format;
+
+/*
+ * fp8kv_index_keys_quantize -- encode num_keys bf16 keys.
+ *
+ * keys        (device) bf16, element (n, d) at n * key_stride + d, d < 128;
+ *             pointer 16-byte aligned, key_stride a multiple of 8.
+ * FP8KV_KEYS_E4M3: the KV row quantizer (codes and scale exactly those of
+ *   fp8kv_kv_quant_scatter): codes (device) uint8, code (n, d) at
+ *   n * code_stride + d; scales (device) fp32, scale n at n * scale_stride.
+ *   Code rows start on 8-byte boundaries.
+ * FP8KV_KEYS_MXFP4: for each group g < 4 of 32 dims, e is the smallest
+ *   integer with max |x| <= 6 * 2^e (exact comparison, clamped to
+ *   [-127, 127]; an all-zero group has e = 0), scales (device) uint8 at
+ *   n * scale_stride + g holds the E8M0 code e + 127, and every element is
+ *   the E2M1 value nearest to x / 2^e (ties to the even code, sign of x
+ *   kept). codes (device) uint8 at n * code_stride + j, j < 64: element 2j
+ *   in the low nibble, 2j + 1 in the high nibble. Code rows start on 4-byte
+ *   boundaries.
+ * num_keys may be 0 (nothing is launched).
+ * Errors: E_NULL, E_SHAPE, E_STRIDE, E_ALIGN, E_UNSUPPORTED, E_LAUNCH.
+ */
+int fp8kv_index_keys_quantize(
+    const void* keys, int64_t key_stride, int64_t num_keys, int32_t head_dim,
+    int32_t key_format, uint8_t* codes, int64_t code_stride,
+    void* scales, int64_t scale_stride, void* stream);
+
+/*
+ * fp8kv_index_score_mxfp4 -- the decode-sized index scorer, over MXFP4 or
+ * E4M3 keys:
+ *   out[b, r, n] = sum_{h < num_heads} w[b, r, h] * max(0, q[b, r, h, :] . k^[b, n, :])
+ * for b < batch, r < rows, n < num_keys, with k^ the dequantized key
+ * (MXFP4: E2M1 value * 2^e of its group; E4M3: code value * key scale),
+ * accumulated in fp32 (the products of bf16 q and the exactly widened key
+ * elements are exact; the sums are fp32 MFMA and lane sums).
+ *
+ * q           (device) FP8KV_DTYPE_BF16, element (b, r, h, d) at
+ *             b*q_stride_b + r*q_stride_row + h*q_stride_head + d; pointer
+ *             16-byte aligned, strides multiples of 8.
+ * w           (device) fp32, (b, r, h) at b*w_stride_b + r*w_stride_row +
+ *             h*w_stride_head (any stride may be 0: broadcast).
+ * codes       (device) key n of request b at b*codes_stride_b +
+ *             n*codes_stride_key (bytes), laid out as written by
+ *             fp8kv_index_keys_quantize; pointer and strides multiples of 16.
+ * scales      (device) MXFP4: uint8 exponent (b, n, g) at b*scales_stride_b
+ *             + n*scales_stride_key + g; E4M3: fp32 scale (b, n) at
+ *             b*scales_stride_b + n*scales_stride_key (elements).
+ * num_heads   1..16; head_dim 128; rows >= 1; batch, num_keys >= 0.
+ * key_chunk   keys per workgroup: 0 = chosen for the current device, else
+ *             a positive multiple of 16.
+ * out         (device) fp32, (b, r, n) at b*out_stride_b + r*out_stride_row + n.
+ * Errors: E_NULL, E_SHAPE, E_STRIDE, E_ALIGN, E_UNSUPPORTED, E_LAUNCH.
+ */
+int fp8kv_index_score_mxfp4(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype,
+    const float* w, int64_t w_stride_b, int64_t w_stride_row, int64_t w_stride_head,
+    int32_t key_format, const uint8_t* codes, int64_t codes_stride_b,
+    int64_t codes_stride_key, const void* scales, int64_t scales_stride_b,
+    int64_t scales_stride_key, int32_t batch, int32_t rows, int32_t num_heads,
+    int32_t head_dim, int32_t num_keys, int32_t key_chunk,
+    float* out, int64_t out_stride_b, int64_t out_stride_row, void* stream);
 
 #ifdef __cplusplus
 }

@@ -172,3 +172,79 @@ def test_binding_refuses_host_tensors():
                             torch.zeros((16, 2, 64), dtype=torch.uint8),
                             torch.zeros((16, 2, 64), dtype=torch.uint8),
                             torch.zeros((16, 2)), torch.zeros((16, 2)))
+
+
+MXFP4, E4M3 = 0, 1
+
+
+def ikq(L, **kw):
+    a = dict(keys=A, ks=128, n=1024, D=128, fmt=MXFP4, codes=A, cs=64,
+             scales=A, ss=4)
+    a.update(kw)
+    return L.fp8kv_index_keys_quantize(a["keys"], a["ks"], a["n"], a["D"],
+                                       a["fmt"], a["codes"], a["cs"],
+                                       a["scales"], a["ss"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=64), E_UNSUPPORTED),
+    (dict(fmt=2), E_UNSUPPORTED),
+    (dict(n=-1), E_SHAPE),
+    (dict(keys=0), E_NULL),
+    (dict(scales=0), E_NULL),
+    (dict(ks=-128), E_STRIDE),
+    (dict(keys=A + 8), E_ALIGN),
+    (dict(ks=132), E_ALIGN),
+    (dict(codes=A + 2), E_ALIGN),
+    (dict(fmt=E4M3, cs=132), E_ALIGN),   # E4M3 code rows are 8-byte aligned
+    (dict(fmt=E4M3, cs=128, scales=A + 2), E_ALIGN),
+    (dict(n=0), OK),
+])
+def test_index_keys_refusals(L, kw, status):
+    assert ikq(L, **kw) == status
+    if status != OK:
+        assert L.fp8kv_last_error().decode()
+
+
+def isc(L, **kw):
+    a = dict(q=A, qsb=1 << 19, qsr=2048, qsh=128, qdt=BF16, w=A, wsb=4096,
+             wsr=16, wsh=1, fmt=MXFP4, codes=A, csb=1 << 22, csk=64, scales=A,
+             ssb=1 << 18, ssk=4, B=8, R=256, H=16, D=128, N=65536, chunk=4096,
+             out=A, osb=1 << 24, osr=65536)
+    a.update(kw)
+    return L.fp8kv_index_score_mxfp4(
+        a["q"], a["qsb"], a["qsr"], a["qsh"], a["qdt"], a["w"], a["wsb"],
+        a["wsr"], a["wsh"], a["fmt"], a["codes"], a["csb"], a["csk"],
+        a["scales"], a["ssb"], a["ssk"], a["B"], a["R"], a["H"], a["D"],
+        a["N"], a["chunk"], a["out"], a["osb"], a["osr"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=64), E_UNSUPPORTED),
+    (dict(qdt=FP16), E_UNSUPPORTED),
+    (dict(fmt=3), E_UNSUPPORTED),
+    (dict(H=17), E_UNSUPPORTED),
+    (dict(H=0), E_UNSUPPORTED),
+    (dict(R=0), E_SHAPE),
+    (dict(B=-1), E_SHAPE),
+    (dict(N=-5), E_SHAPE),
+    (dict(chunk=24), E_SHAPE),
+    (dict(chunk=-16), E_SHAPE),
+    (dict(q=0), E_NULL),
+    (dict(w=0), E_NULL),
+    (dict(out=0), E_NULL),
+    (dict(wsh=-1), E_STRIDE),
+    (dict(osr=-1), E_STRIDE),
+    (dict(q=A + 4), E_ALIGN),
+    (dict(qsh=100), E_ALIGN),
+    (dict(csk=72), E_ALIGN),
+    (dict(codes=A + 8), E_ALIGN),
+    (dict(fmt=E4M3, csk=128, scales=A + 1), E_ALIGN),
+    (dict(out=A + 2), E_ALIGN),
+    (dict(B=0), OK),
+    (dict(N=0), OK),
+])
+def test_index_score_refusals(L, kw, status):
+    assert isc(L, **kw) == status
+    if status != OK:
+        assert L.fp8kv_last_error().decode()

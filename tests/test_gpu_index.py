@@ -1,0 +1,280 @@
+"""GPU parity of the compressed-index key encoders and the index scorer
+against the oracle ("fix(qwen4-exp): register the QSA FP8 scale planes for
+KV offload", ROCm/ATOM #2655, description: compressed-index bullet and the
+stacked decode scorer paragraph).
+
+Bars:
+* key codes (E4M3 codes + fp32 scales; MXFP4 nibbles + E8M0 codes) equal
+  the oracle's bit for bit;
+* the widened keys are exact: a one-hot query reads back every E2M1 code at
+  every exponent as exactly E2M1 * 2^e;
+* scores: |got - ref| <= 2^-16 * sum_h |w_h| * sum_d |q_hd * k^_nd| per
+  element, the forward error bound of any-order fp32 summation of the
+  <= 145 terms each score adds (products of bf16 q and the exactly widened
+  keys are exact in fp32), with ref the oracle's float64 score.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_e4m3_paged_kv_amd as fk
+from fp8_e4m3_paged_kv_amd import synth
+
+from gpu_cases import bf16_bits, log
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+MX, E4 = fk.KEYS_MXFP4, fk.KEYS_E4M3
+TOL = 2.0 ** -16
+
+E2M1 = np.array([oracle.e2m1_value(c) for c in range(16)])
+
+
+def dequant_keys(fmt, codes, scales):
+    """k^ [B, N, 128] float64 from host codes/scales, by the oracle's
+    code tables."""
+    codes = np.asarray(codes)
+    if fmt == MX:
+        nib = np.stack([codes & 15, codes >> 4], axis=-1).reshape(
+            codes.shape[:-1] + (128,))
+        exps = np.asarray(scales).astype(np.int64)
+        sc = np.ldexp(1.0, exps - 127)                      # [.., 4]
+        return E2M1[nib] * np.repeat(sc, 32, axis=-1)
+    table = oracle.decode(np.arange(256, dtype=np.uint8))
+    return table[codes] * np.asarray(scales, np.float64)[..., None]
+
+
+def score_bound(q_bits, w, kh):
+    q = oracle.bf16_to_f32(q_bits).astype(np.float64)      # [B, R, H, D]
+    B, R, H, D = q.shape
+    aq = np.abs(q).reshape(B, R * H, D)
+    ak = np.abs(kh)                                        # [B, N, D]
+    s = np.matmul(aq, ak.transpose(0, 2, 1)).reshape(B, R, H, -1)
+    return (np.abs(np.asarray(w, np.float64))[..., None] * s).sum(axis=2)
+
+
+def check_scores(got, q, w, fmt, codes, scales, what):
+    qb = bf16_bits(q)
+    wh = w.cpu().numpy()
+    ch, sh = codes.cpu().numpy(), scales.cpu().numpy()
+    ref = oracle.index_score(qb, wh, fmt, ch, sh)
+    kh = dequant_keys(fmt, ch, sh)
+    bound = TOL * score_bound(qb, wh, kh) + 1e-37
+    err = np.abs(got.cpu().numpy().astype(np.float64) - ref)
+    worst = float((err / bound).max()) if err.size else 0.0
+    log(f"  {what}: max |err| {err.max() if err.size else 0:.3e}, "
+        f"worst err/bound {worst:.3f}")
+    assert np.all(err <= bound), what
+
+
+def encode(keys, fmt):
+    codes, scales = fk.index_keys_quantize(keys, fmt)
+    torch.cuda.synchronize()
+    return codes, scales
+
+
+def oracle_keys(keys, fmt):
+    kb = bf16_bits(keys.reshape(-1, 128))
+    if fmt == MX:
+        return oracle.index_keys_mxfp4(kb)
+    return oracle.index_keys_e4m3(kb)
+
+
+def edge_keys():
+    """Rows exercising ties, group boundaries, zeros, signed zeros, bf16
+    subnormals and the largest bf16 values."""
+    rows = []
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], np.float32)
+    g = np.concatenate([ties, -ties, ties * 0.5, -ties * 0.5])   # amax 6 -> e = 0
+    rows.append(np.concatenate([g, g * 2.0 ** -20, g * 2.0 ** 90, -g * 2.0 ** -120]))
+    rows.append(np.zeros(128, np.float32))                     # all-zero groups
+    r = np.zeros(128, np.float32)
+    r[3], r[40], r[77], r[100] = 4.0, -6.0, 3.0 * 2.0 ** -130, 1.0e-40
+    rows.append(r)                                             # lone values / subnormals
+    r = np.full(128, -0.0, np.float32)
+    r[::7] = 0.0
+    rows.append(r)                                             # signed zeros
+    big = float(torch.finfo(torch.bfloat16).max)
+    rows.append(np.where(np.arange(128) % 2 == 0, big, -big / 3).astype(np.float32))
+    r = np.linspace(-1.0, 1.0, 128, dtype=np.float32)
+    r[0:32] *= 6.0 * 2.0 ** -3 / np.abs(r[0:32]).max()        # amax exactly 6 * 2^e
+    r[32:64] *= (6.0 * 2.0 ** 5) * (1 + 2 ** -7) / np.abs(r[32:64]).max()  # just above
+    rows.append(r)
+    sub = np.array([2.0 ** -133, -2.0 ** -130, 2.0 ** -127, 3 * 2.0 ** -128], np.float32)
+    rows.append(np.tile(sub, 32))                              # all-subnormal row
+    x = torch.tensor(np.stack(rows)).to(torch.bfloat16)
+    return x
+
+
+@pytest.mark.parametrize("fmt", [MX, E4])
+def test_key_codes_bit_exact(fmt):
+    case = synth.index_case(2, 1, 1, 333, seed=41)
+    keys = torch.cat([case.keys.reshape(-1, 128), edge_keys(),
+                      synth.normal_bf16((64, 128), synth.gen(5), std=300.0)])
+    log(f"index keys fmt={fmt}: {keys.shape[0]} keys")
+    codes, scales = encode(keys.to(DEV), fmt)
+    rc, rs = oracle_keys(keys, fmt)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    if fmt == MX:
+        assert np.array_equal(scales.cpu().numpy(), rs)
+    else:
+        assert np.array_equal(scales.cpu().numpy().view(np.uint32),
+                              np.asarray(rs, np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", [MX, E4])
+def test_key_codes_strided_rows(fmt):
+    """Keys read from every other row of a wider tensor; codes written into
+    padded rows (the padding must stay untouched)."""
+    base = synth.normal_bf16((50, 256), synth.gen(8)).to(DEV)
+    keys = base[:, 64:192]
+    nbytes = 64 if fmt == MX else 128
+    codes_buf = torch.full((50, nbytes + 32), 0x5A, dtype=torch.uint8, device=DEV)
+    codes = codes_buf[:, :nbytes]
+    if fmt == MX:
+        sbuf = torch.full((50, 8), 0x5A, dtype=torch.uint8, device=DEV)
+        scales = sbuf[:, 2:6]
+    else:
+        sbuf = torch.full((50, 2), -3.0, device=DEV)
+        scales = sbuf[:, 1]
+    lib = fk.lib()
+    fk._check(lib.fp8kv_index_keys_quantize(
+        keys.data_ptr(), keys.stride(0), 50, 128, fmt, codes.data_ptr(),
+        codes.stride(0), scales.data_ptr(), scales.stride(0),
+        torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    rc, rs = oracle_keys(keys.cpu(), fmt)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert torch.all(codes_buf[:, nbytes:] == 0x5A)
+    if fmt == MX:
+        assert np.array_equal(scales.cpu().numpy(), rs)
+        assert torch.all(sbuf[:, :2] == 0x5A) and torch.all(sbuf[:, 6:] == 0x5A)
+    else:
+        assert np.array_equal(scales.cpu().numpy(), np.asarray(rs, np.float32))
+        assert torch.all(sbuf[:, 0] == -3.0)
+
+
+def widen_case(exps):
+    """Keys n with exponent code exps[n] in all 4 groups and nibbles cycling
+    through all 16 codes at every position; 256 one-hot query rows (head 0,
+    dim d, sign +-), so row (d, sign) reads back max(0, +-k^[n, d])."""
+    N = exps.size
+    j = np.arange(64)
+    n = np.arange(N)[:, None]
+    lo = (j[None, :] + n) % 16
+    hi = (j[None, :] * 3 + n + 7) % 16
+    packed = (lo | (hi << 4)).astype(np.uint8)[None]           # [1, N, 64]
+    ex = np.repeat(exps[:, None], 4, axis=1)[None]            # [1, N, 4]
+    q = torch.zeros((1, 256, 1, 128), dtype=torch.float32)
+    for d in range(128):
+        q[0, 2 * d, 0, d] = 1.0
+        q[0, 2 * d + 1, 0, d] = -1.0
+    q = q.to(torch.bfloat16).to(DEV)
+    w = torch.ones((1, 256, 1), device=DEV)
+    out = fk.index_score_mxfp4(q, w, MX, torch.tensor(packed).to(DEV),
+                               torch.tensor(ex).to(DEV))
+    torch.cuda.synchronize()
+    kh = dequant_keys(MX, packed, ex)[0]                      # [N, 128]
+    want = np.empty((256, N))
+    want[0::2] = np.maximum(kh.T, 0.0)
+    want[1::2] = np.maximum(-kh.T, 0.0)
+    return out[0].cpu().numpy().astype(np.float64), want
+
+
+def test_mxfp4_widening_exact_for_every_code_and_exponent():
+    """Exponent codes 2..252: every E2M1 * 2^e is a finite normal bf16."""
+    got, want = widen_case(np.arange(2, 253, dtype=np.uint8))
+    assert np.array_equal(got, want)
+
+
+def test_mxfp4_widening_subnormal_exponents():
+    """Exponent codes 0 and 1, where E2M1 * 2^e falls to bf16 subnormals."""
+    got, want = widen_case(np.array([0, 1, 0, 1], dtype=np.uint8))
+    bad = got != want
+    if bad.any():
+        log(f"  subnormal widening: {int(bad.sum())} mismatches, e.g. "
+            f"got {got[bad][:4]} want {want[bad][:4]}")
+    assert not bad.any()
+
+
+@pytest.mark.parametrize("fmt", [MX, E4])
+@pytest.mark.parametrize("B,R,H,N,chunk", [
+    (2, 37, 16, 333, 0),        # ragged rows and keys, library chunking
+    (3, 5, 16, 200, 48),        # several chunks with a tail
+    (1, 1, 4, 17, 16),          # one row, 4 heads, a 1-key tail tile
+    (2, 70, 1, 64, 32),         # one head, rows across 3 workgroups
+    (1, 256, 16, 1000, 0),      # the verify-sized row count
+])
+def test_scores_match_oracle(fmt, B, R, H, N, chunk):
+    case = synth.index_case(B, R, H, N, seed=B * 1000 + R + N)
+    log(f"index score fmt={fmt} B={B} R={R} H={H} N={N} chunk={chunk}")
+    codes, scales = encode(case.keys.to(DEV), fmt)
+    q, w = case.q.to(DEV), case.w.to(DEV)
+    out = fk.index_score_mxfp4(q, w, fmt, codes, scales, key_chunk=chunk)
+    torch.cuda.synchronize()
+    check_scores(out, q, w, fmt, codes, scales, f"B{B} R{R} H{H} N{N}")
+
+
+@pytest.mark.parametrize("fmt", [MX, E4])
+def test_scores_strided_views_and_signed_weights(fmt):
+    """q and w as non-contiguous views, negative weights, keys with padded
+    rows, out with a padded row stride: only the addressed bytes matter."""
+    B, R, H, N = 2, 9, 16, 130
+    case = synth.index_case(B, R, H, N, seed=77)
+    qbig = torch.zeros((B, R, H + 3, 136), dtype=torch.bfloat16)
+    qbig[:, :, 1:H + 1, :128] = case.q
+    q = qbig.to(DEV)[:, :, 1:H + 1, :128]
+    wbig = torch.zeros((B, R, 2 * H))
+    wbig[:, :, ::2] = case.w - 0.5
+    w = wbig.to(DEV)[:, :, ::2]
+    codes, scales = encode(case.keys.to(DEV), fmt)
+    cpad = torch.zeros((B, N, codes.shape[2] + 16), dtype=torch.uint8, device=DEV)
+    cpad[:, :, :codes.shape[2]] = codes
+    cview = cpad[:, :, :codes.shape[2]]
+    obuf = torch.full((B, R, N + 20), 7.0, device=DEV)
+    out = obuf[:, :, :N]
+    fk.index_score_mxfp4(q, w, fmt, cview, scales, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(obuf[:, :, N:] == 7.0)
+    check_scores(out, q.contiguous(), w.contiguous(), fmt, codes, scales, "strided")
+
+
+def test_negative_dots_contribute_nothing():
+    """Keys = -q direction for every head: every dot is negative and every
+    score is exactly 0 (ReLU per head before the head sum)."""
+    B, R, H, N = 1, 8, 16, 48
+    g = synth.gen(3)
+    q = torch.rand((B, R, H, 128), generator=g).to(torch.bfloat16)
+    keys = -torch.rand((B, N, 128), generator=g).to(torch.bfloat16)
+    w = torch.rand((B, R, H), generator=g)
+    for fmt in (MX, E4):
+        codes, scales = encode(keys.to(DEV), fmt)
+        out = fk.index_score_mxfp4(q.to(DEV), w.to(DEV), fmt, codes, scales)
+        torch.cuda.synchronize()
+        assert torch.all(out == 0)
+
+
+@pytest.mark.parametrize("fmt", [MX, E4])
+def test_index_workload_full_size_sampled(fmt):
+    """8 requests x 256 rows x 16 heads x 65,536 keys, the benchmark's
+    launch (library-chosen chunks); key codes of two requests are checked
+    bit for bit, and the oracle rescores 8 rows x 2048 keys of two
+    requests."""
+    case = synth.index_workload(seed=4, device=DEV)
+    codes, scales = encode(case.keys, fmt)
+    out = fk.index_score_mxfp4(case.q, case.w, fmt, codes, scales)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(out))
+    for b in (0, 7):
+        rc, rs = oracle_keys(case.keys[b].cpu(), fmt)
+        assert np.array_equal(codes[b].cpu().numpy(), rc)
+    rows = torch.tensor([0, 3, 64, 100, 127, 128, 200, 255])
+    keys = torch.arange(0, 65536, 32)
+    for b in (1, 6):
+        sub_q = case.q[b:b + 1, rows]
+        sub_w = case.w[b:b + 1, rows]
+        sub_c = codes[b:b + 1, keys.to(DEV)]
+        sub_s = scales[b:b + 1, keys.to(DEV)]
+        got = out[b:b + 1][:, rows.to(DEV)][:, :, keys.to(DEV)]
+        check_scores(got, sub_q, sub_w, fmt, sub_c, sub_s, f"full-size request {b}")
