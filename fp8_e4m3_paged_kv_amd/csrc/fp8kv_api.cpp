@@ -466,6 +466,16 @@ int fp8kv_index_score_mxfp4(
     const int64_t chunks = ((int64_t)num_keys + chunk - 1) / chunk;
     if ((int64_t)batch * chunks * row_groups > INT32_MAX / 2)
         return fail(FP8KV_E_SHAPE, "index scorer grid too large");
+    // each request's keys, scales and scores are addressed with 32-bit
+    // byte offsets below 2^30
+    const int64_t scale_key_bytes = e4m3 ? scales_stride_key * 4 : scales_stride_key;
+    const int64_t key_bytes = (int64_t)(num_keys - 1) * codes_stride_key + (e4m3 ? 128 : 64);
+    const int64_t scale_bytes = (int64_t)(num_keys - 1) * scale_key_bytes + 4;
+    const int64_t out_bytes = ((int64_t)(rows - 1) * out_stride_row + num_keys) * 4;
+    if (key_bytes >= (INT64_C(1) << 30) || scale_bytes >= (INT64_C(1) << 30) ||
+        out_bytes >= (INT64_C(1) << 30))
+        return fail(FP8KV_E_SHAPE, "index scorer: one request's keys, scales or scores "
+                                   "span 2^30 bytes or more");
 
     fp8kv::IndexScoreParams p;
     p.q = static_cast<const uint16_t*>(q);
@@ -492,6 +502,9 @@ int fp8kv_index_score_mxfp4(
     p.key_chunk = chunk;
     p.chunks = (int32_t)chunks;
     p.row_groups = row_groups;
+    p.key_bytes = (int32_t)key_bytes;
+    p.scale_bytes = (int32_t)scale_bytes;
+    p.out_bytes = (int32_t)out_bytes;
     return launched(fp8kv::launch_index_score(p, key_format, (hipStream_t)stream),
                     "index_score");
 }

@@ -19,6 +19,14 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kE4M3Max = 448.0f;
+constexpr int kBufferWord3 = 0x00020000;   // gfx9 raw buffer descriptor flags (32-bit data format)
+
+// Raw buffer descriptor over [base, base + bytes): loads past the end read
+// 0, stores past the end are dropped (the range check covers the VGPR
+// offset; keep the SGPR offset 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferWord3);
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) {
     return __uint_as_float(w << 16);

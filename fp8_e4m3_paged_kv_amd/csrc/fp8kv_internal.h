@@ -104,6 +104,9 @@ struct IndexScoreParams {
     int32_t key_chunk;         // keys per workgroup, a multiple of 16
     int32_t chunks;            // ceil(num_keys / key_chunk)
     int32_t row_groups;        // ceil(rows / kIndexRowsPerBlock)
+    int32_t key_bytes;         // per request: extent of the key codes in bytes
+    int32_t scale_bytes;       // per request: extent of the key scales in bytes
+    int32_t out_bytes;         // per request: (rows - 1) * out_stride_row * 4 + num_keys * 4
 };
 
 hipError_t launch_index_keys(const IndexKeysParams& p, int key_format, hipStream_t stream);

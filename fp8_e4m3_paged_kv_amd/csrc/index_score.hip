@@ -22,7 +22,10 @@
 // (v_permlane32_swap, v_permlane16_swap), which leave row 4c + g of the
 // quad in lane group g. E4M3 key scales are >= 0, so they multiply the
 // summed score; MXFP4 exponents vary along the dims and are folded into the
-// widened keys (E2M1 * 2^e is exact in bf16).
+// widened keys (E2M1 * 2^e is exact in bf16). The ReLU and head weights cost
+// two VALU ops per (row, head, key), which bounds the kernel together with
+// the MFMAs: on gfx950 the vector ALU and the matrix core overlap only in
+// part.
 #include <hip/hip_runtime.h>
 
 #include "fp8kv_device.h"
@@ -32,6 +35,7 @@ namespace fp8kv {
 namespace {
 
 constexpr int kScoreWaves = 4;
+constexpr int kStoreNT = 2;         // cache policy of the score stores: non-temporal
 
 // E2M1 code of |v| (v = x / 2^e, so |v| <= 6): nearest of
 // {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even code. The thresholds are the
@@ -116,24 +120,25 @@ __global__ __launch_bounds__(256) void index_keys_kernel(IndexKeysParams p) {
 // A 16-key tile, widened to the bf16 B operand of four k-steps. Lane
 // (g, i): key i of the tile, dims [32g, 32g + 32); k-step k takes dims
 // 32g + 8k .. +7, and q is read with the same permutation of the dims.
+// Loads go through buffer descriptors bounded by the request's keys: keys
+// past the end read as 0 and are never stored.
 template <int FMT>
 struct KeyTile {
     uint4 raw[2];        // E4M3: the lane's 32 code bytes; MXFP4: 16 packed bytes in raw[0]
     uint32_t exp;        // MXFP4: E8M0 code of group g of key i
     float kscale;        // E4M3: scale of key i
 
-    __device__ __forceinline__ void load(const IndexScoreParams& p, const uint8_t* codes,
-                                         const uint8_t* scales, int t, int lane) {
-        const int li = lane & 15, lg = lane >> 4;
-        const int key = min(t + li, p.num_keys - 1);
-        const uint8_t* row = codes + (int64_t)key * p.codes_stride_key;
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t srs,
+                                         uint32_t koff, uint32_t soff) {
+        typedef int intx4 __attribute__((ext_vector_type(4)));
+        const intx4 a = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)koff, 0, 0);
+        raw[0] = make_uint4(a[0], a[1], a[2], a[3]);
         if (FMT == kKeysE4M3) {
-            raw[0] = *reinterpret_cast<const uint4*>(row + 32 * lg);
-            raw[1] = *reinterpret_cast<const uint4*>(row + 32 * lg + 16);
-            kscale = *reinterpret_cast<const float*>(scales + (int64_t)key * p.scales_stride_key);
+            const intx4 c = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)koff + 16, 0, 0);
+            raw[1] = make_uint4(c[0], c[1], c[2], c[3]);
+            kscale = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(srs, (int)soff, 0, 0));
         } else {
-            raw[0] = *reinterpret_cast<const uint4*>(row + 16 * lg);
-            exp = scales[(int64_t)key * p.scales_stride_key + lg];
+            exp = __builtin_amdgcn_raw_buffer_load_b8(srs, (int)soff, 0, 0);
         }
     }
 
@@ -174,13 +179,27 @@ __device__ __forceinline__ float swap16_sum(float a, float b) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// max(x, 0) on the bit pattern: negative floats are negative integers. One
+// integer max, where a float max needs its operand canonicalized first.
+__device__ __forceinline__ float relu(float x) {
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// Byte offset that every store range check rejects (request spans are
+// below 2^30 bytes, so the sum of two such offsets is rejected too).
+constexpr uint32_t kDropped = 0x40000000u;
+
 // Workgroup = 4 waves x RW query rows of one request and one chunk of its
 // keys; each wave scores its rows against every 16-key tile of the chunk.
 // The row groups of one (request, chunk) are placed on one XCD, so their key
-// reads meet in that XCD's L2.
+// reads meet in that XCD's L2. The tile loop has no branch: loads past the
+// chunk read in-bounds keys or zeros, stores of rows and keys outside the
+// output carry an offset the range check drops. Key loads run two tiles
+// ahead (three register buffers), and the MFMAs of each quad of rows are
+// issued next to the previous quad's epilogue, which does not depend on
+// them, so the matrix core and the vector ALU work side by side.
 template <int FMT, int RW>
 __global__ __launch_bounds__(256) void index_score_kernel(IndexScoreParams p) {
-    static_assert(RW % 4 == 0, "rows are reduced four at a time");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 15, lg = lane >> 4;
@@ -229,43 +248,91 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexScoreParams p) {
         }
     }
 
-    const uint8_t* codes = p.codes + (int64_t)b * p.codes_stride_b;
-    const uint8_t* scales = p.scales + (int64_t)b * p.scales_stride_b;
-    float* out = p.out + (int64_t)b * p.out_stride_b;
-    const int quads = min(RW, p.rows - row0 + 3) / 4;    // quads holding a valid row
+    const __amdgpu_buffer_rsrc_t krs =
+        make_rsrc(p.codes + (int64_t)b * p.codes_stride_b, p.key_bytes);
+    const __amdgpu_buffer_rsrc_t srs =
+        make_rsrc(p.scales + (int64_t)b * p.scales_stride_b, p.scale_bytes);
+    const __amdgpu_buffer_rsrc_t ors =
+        make_rsrc(p.out + (int64_t)b * p.out_stride_b, p.out_bytes);
+    const uint32_t kstep = 16u * (uint32_t)p.codes_stride_key;
+    const uint32_t sstep = 16u * (uint32_t)p.scales_stride_key;
+    uint32_t koff = (uint32_t)(n_begin + li) * (uint32_t)p.codes_stride_key +
+                    (FMT == kKeysE4M3 ? 32u : 16u) * lg;
+    uint32_t soff = (uint32_t)(n_begin + li) * (uint32_t)p.scales_stride_key +
+                    (FMT == kKeysE4M3 ? 0u : (uint32_t)lg);
+    uint32_t orow[RW / 4];
+#pragma unroll
+    for (int c = 0; c < RW / 4; ++c) {
+        const int row = row0 + 4 * c + lg;
+        orow[c] = row < p.rows ? (uint32_t)row * (uint32_t)p.out_stride_row * 4u : kDropped;
+    }
 
-    KeyTile<FMT> cur, nxt;
-    cur.load(p, codes, scales, n_begin, lane);
-    for (int t = n_begin; t < n_end; t += 16) {
-        bf16x8 kb[4];
-        cur.widen(kb);
-        const float ks = FMT == kKeysE4M3 ? cur.kscale : 1.0f;
-        if (t + 16 < n_end) nxt.load(p, codes, scales, t + 16, lane);
-        const bool key_ok = t + li < n_end;
+    static_assert(RW == 8, "two quads of rows per wave");
+    floatx4 acc0[4], acc1[4];
+    auto mfma_quad = [&](const bf16x8 (&kb)[4], int c, floatx4 (&acc)[4]) {
 #pragma unroll
-        for (int c = 0; c < RW / 4; ++c) {
-            if (c >= quads) break;
-            float s[4];
+        for (int r = 0; r < 4; ++r) {
+            acc[r] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[4 * c + r][k], kb[k], acc, 0, 0, 0);
-                // acc[j] = q(head 4g + j) . key i
-                const float* wr = wv[4 * c + r];
-                float v = fmaxf(acc[0], 0.f) * wr[0];
-                v = __builtin_fmaf(fmaxf(acc[1], 0.f), wr[1], v);
-                v = __builtin_fmaf(fmaxf(acc[2], 0.f), wr[2], v);
-                s[r] = __builtin_fmaf(fmaxf(acc[3], 0.f), wr[3], v);
-            }
-            // lane group g ends with row 4c + g summed over all 16 heads
-            const float sc = swap16_sum(swap32_sum(s[0], s[2]), swap32_sum(s[1], s[3])) * ks;
-            const int row = row0 + 4 * c + lg;
-            if (key_ok && row < p.rows)
-                __builtin_nontemporal_store(sc, out + (int64_t)row * p.out_stride_row + t + li);
+            for (int k = 0; k < 4; ++k)
+                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[4 * c + r][k], kb[k], acc[r], 0, 0, 0);
         }
-        cur = nxt;
+    };
+    auto epilogue = [&](const floatx4 (&acc)[4], int c, float ks, uint32_t ocol) {
+        float s[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float* wr = wv[4 * c + r];
+            float v = relu(acc[r][0]) * wr[0];
+            v = __builtin_fmaf(relu(acc[r][1]), wr[1], v);
+            v = __builtin_fmaf(relu(acc[r][2]), wr[2], v);
+            s[r] = __builtin_fmaf(relu(acc[r][3]), wr[3], v);
+        }
+        const float sc = swap16_sum(swap32_sum(s[0], s[2]), swap32_sum(s[1], s[3])) * ks;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(sc), ors, (int)(orow[c] + ocol), 0,
+                                              kStoreNT);
+    };
+    auto col = [&](int t) { return t + li < n_end ? (uint32_t)(t + li) * 4u : kDropped; };
+
+    // one step: tile t's quad 0 MFMAs overlap the previous tile's quad 1
+    // epilogue, tile t's quad 1 MFMAs overlap its own quad 0 epilogue
+    float ks_prev = 0.f;
+    uint32_t ocol_prev = kDropped;
+    auto step = [&](const KeyTile<FMT>& kt, int t) {
+        bf16x8 kb[4];
+        kt.widen(kb);
+        const float ks = FMT == kKeysE4M3 ? kt.kscale : 1.0f;
+        const uint32_t ocol = col(t);
+        mfma_quad(kb, 0, acc0);
+        epilogue(acc1, 1, ks_prev, ocol_prev);
+        mfma_quad(kb, 1, acc1);
+        epilogue(acc0, 0, ks, ocol);
+        ks_prev = ks;
+        ocol_prev = ocol;
+    };
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc1[r] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // tiles n_begin, n_begin + 16, ... and one more (its stores all dropped)
+    // to drain the pipeline; loads run two tiles ahead in three buffers
+    KeyTile<FMT> ta, tb, tc;
+    ta.load(krs, srs, koff, soff);
+    koff += kstep;
+    soff += sstep;
+    tb.load(krs, srs, koff, soff);
+    for (int t = n_begin; t < n_end + 16; t += 48) {
+        koff += kstep;
+        soff += sstep;
+        tc.load(krs, srs, koff, soff);
+        step(ta, t);
+        koff += kstep;
+        soff += sstep;
+        ta.load(krs, srs, koff, soff);
+        step(tb, t + 16);
+        koff += kstep;
+        soff += sstep;
+        tb.load(krs, srs, koff, soff);
+        step(tc, t + 32);
     }
 }
 

@@ -53,7 +53,6 @@ namespace fp8kv {
 namespace {
 
 constexpr float kNeg = -1.0e30f;     // "minus infinity" that keeps exp2 finite
-constexpr int kBufferWord3 = 0x00020000;   // gfx9 raw buffer descriptor flags
 
 __device__ __forceinline__ float pow2i(int e) {   // 2^e for e in [-126, 127]
     return __uint_as_float((uint32_t)(e + 127) << 23);
@@ -74,10 +73,6 @@ __device__ __forceinline__ float rows_sum(float v) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Raw buffer descriptor over [base, base + bytes): loads past the end read 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferWord3);
-}
 
 typedef int intx2 __attribute__((ext_vector_type(2)));
 typedef int intx4 __attribute__((ext_vector_type(4)));

@@ -241,6 +241,7 @@ def isc(L, **kw):
     (dict(codes=A + 8), E_ALIGN),
     (dict(fmt=E4M3, csk=128, scales=A + 1), E_ALIGN),
     (dict(out=A + 2), E_ALIGN),
+    (dict(osr=1 << 22), E_SHAPE),        # one request's scores span >= 2^30 bytes
     (dict(B=0), OK),
     (dict(N=0), OK),
 ])
