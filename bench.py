@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the prefill-chunk, long-context and index extras")
+    ap.add_argument("--extras", default="prefill,longctx,index",
+                    help="comma list of the extras to run (prefill, longctx, index)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times "
                          "(the known-size reference for HBM byte counters)")
@@ -102,8 +104,27 @@ def quant_bytes(T, Hkv, D):
     return T * Hkv * 2 * (2 * D + D + 4) + 8 * T
 
 
+SETTLE_S = 0.3
+
+
+def settle(fn, seconds=SETTLE_S):
+    """Run fn back to back for about `seconds` of wall time (untimed). After
+    a phase of other work the GPU needs some tens of launches before its
+    clocks and memory subsystem reach the steady state every later launch
+    sees (the first ~25 decode launches after the cache build run ~8%
+    slower); this brings each measured workload there before its warmup."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
 def time_events(fn, n, stream):
     import torch
+    settle(fn)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n)]
     for a, b in evs:
@@ -128,18 +149,18 @@ def traffic_entry(per_launch_alg_bytes):
 
 
 def cache_build(torch, fk, k, v, slots, k_cache, v_cache, k_plane, v_plane,
-                stream, chunk=1 << 18):
-    """Quantize+scatter every cached token in chunks of 256K tokens; returns
-    the milliseconds of one whole build. The build runs once untimed (it
-    loads the kernels and touches the freshly allocated cache pages once),
-    then again timed: quantize+scatter is idempotent, so the second build
-    writes the same bytes and measures the kernel in steady state."""
+                stream, chunk=1 << 20):
+    """Quantize+scatter every cached token in launches of up to 1M tokens; returns
+    the milliseconds of one whole build. The build first runs untimed for
+    a settle period (it loads the kernels and touches the freshly allocated
+    cache pages), then once more timed: quantize+scatter is idempotent, so
+    the timed build writes the same bytes and measures the kernel in steady
+    state."""
     def build():
         for i in range(0, slots.numel(), chunk):
             fk.kv_quant_scatter(k[i:i + chunk], v[i:i + chunk], slots[i:i + chunk],
                                 k_cache, v_cache, k_plane.t(), v_plane.t())
-    build()
-    torch.cuda.synchronize()
+    settle(build)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
@@ -277,6 +298,7 @@ def main():
         fk.paged_decode_merge(ws, out, rows=R, num_q_heads=Hq,
                               num_kv_heads=Hkv, num_ranges=nr)
 
+    settle(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -334,9 +356,12 @@ def main():
         "also": {"cache_build_GBps": round(build_gbs, 1)},
     }
 
-    if not args.no_extras:
+    extras = set() if args.no_extras else set(args.extras.split(","))
+    if "prefill" in extras:
         result["also"].update(prefill_quant_scatter(torch, fk, synth, dev, stream))
+    if "longctx" in extras:
         result["also"].update(longctx_decode(torch, fk, synth, dev, stream))
+    if "index" in extras:
         result["also"].update(index_scorer(torch, fk, synth, dev, stream))
 
     if not args.no_cpu_baseline:

@@ -104,7 +104,14 @@ __global__ __launch_bounds__(kQsThreads) void kv_quant_scatter_kernel(QuantScatt
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane >> 4;           // row within a 4-row group
     const int li = lane & 15;            // lane within the row
-    const uint32_t wave_row0 = blockIdx.x * kQsRowsPerBlock + wave * kQsRowsPerWave;
+    // Dispatch deals consecutive workgroups round-robin to the 8 XCDs, each
+    // with its own L2. Row blocks are renumbered so that every XCD takes a
+    // contiguous eighth of the rows: the 4-byte scales of neighbouring slots
+    // then meet in one L2 and leave it as whole lines (gridDim.x is a
+    // multiple of 8).
+    const uint32_t per_xcd = gridDim.x >> 3;
+    const uint32_t block = (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
+    const uint32_t wave_row0 = block * kQsRowsPerBlock + wave * kQsRowsPerWave;
     const uint32_t H = (uint32_t)p.num_kv_heads;
     const uint32_t nrows = (uint32_t)(p.num_rows >> 1);   // (token, head) rows of K (or V)
 
@@ -166,8 +173,10 @@ hipError_t launch_kv_quant_scatter(const QuantScatterParams& p, int head_dim,
                                    hipStream_t stream) {
     // rows are numbered in 32 bits; K rows on grid y = 0, V rows on y = 1
     const int64_t kv_rows = p.num_rows / 2;
-    if (kv_rows > 0x7FFFFFFF - kQsRowsPerBlock) return hipErrorInvalidValue;
-    const int64_t blocks = (kv_rows + kQsRowsPerBlock - 1) / kQsRowsPerBlock;
+    if (kv_rows > 0x7FFFFFFF - 8 * kQsRowsPerBlock) return hipErrorInvalidValue;
+    // whole multiples of 8 workgroups (the XCD renumbering); the extra ones
+    // find no rows
+    const int64_t blocks = (kv_rows + 8 * kQsRowsPerBlock - 1) / (8 * kQsRowsPerBlock) * 8;
     dim3 grid((unsigned)blocks, 2), block(kQsThreads);
     const int H = p.num_kv_heads;
     const int hs = (H & (H - 1)) == 0 ? __builtin_ctz((unsigned)H) : -1;
