@@ -287,3 +287,50 @@ def index_case(batch: int, rows: int, heads: int, num_keys: int, seed: int,
 def index_workload(seed: int = 4, device="cpu") -> IndexCase:
     """8 requests x 256 query rows, 16 index heads, 65,536 keys each."""
     return index_case(8, 256, 16, 65536, seed, device=device)
+
+
+@dataclass
+class SparseSelection:
+    """Selected blocks per request, as a page table of its own."""
+    block_tables: torch.Tensor      # int32 [B, max_sel]: selected blocks, position order
+    block_valid: torch.Tensor       # int32 [B, max_sel]: keys of each, from its start
+    context_lens: torch.Tensor      # int32 [B]: virtual positions (i * bs + offset)
+
+
+def sparse_selection(layout: PagedLayout, keep_frac: float, seed: int,
+                     partial_frac: float = 0.0, pad: int = 0) -> SparseSelection:
+    """A random top-k-like block selection of every request: a fraction
+    `keep_frac` of its blocks (at least one) drawn without replacement from
+    all but the last, plus the last block (which holds the newest tokens),
+    in position order. Valid counts are the block size, the last block's
+    filled count, and for a fraction `partial_frac` of the other selected
+    blocks a random count in [0, bs]."""
+    g = gen(seed)
+    bs = layout.block_size
+    lens = layout.context_lens.tolist()
+    tables, valids, vlens = [], [], []
+    for b, n in enumerate(lens):
+        nb = (n + bs - 1) // bs
+        if nb == 0:
+            tables.append([]); valids.append([]); vlens.append(0)
+            continue
+        k = max(1, int(round(keep_frac * (nb - 1)))) if nb > 1 else 0
+        pick = torch.randperm(nb - 1, generator=g)[:k].sort().values.tolist() if nb > 1 else []
+        idx = pick + [nb - 1]
+        blocks = [int(layout.block_tables[b, i]) for i in idx]
+        valid = [bs] * len(idx)
+        valid[-1] = n - (nb - 1) * bs
+        for i in range(len(idx) - 1):
+            if float(torch.rand((), generator=g)) < partial_frac:
+                valid[i] = int(torch.randint(0, bs + 1, (), generator=g))
+        tables.append(blocks)
+        valids.append(valid)
+        vlens.append((len(idx) - 1) * bs + valid[-1])
+    m = max(1, max(len(t) for t in tables))
+    bt = torch.full((len(lens), m), int(pad), dtype=torch.int32)
+    bv = torch.zeros((len(lens), m), dtype=torch.int32)
+    for b in range(len(lens)):
+        if tables[b]:
+            bt[b, :len(tables[b])] = torch.tensor(tables[b], dtype=torch.int32)
+            bv[b, :len(valids[b])] = torch.tensor(valids[b], dtype=torch.int32)
+    return SparseSelection(bt, bv, torch.tensor(vlens, dtype=torch.int32))

@@ -74,6 +74,10 @@ def _load():
                                          P, P, I64, I64, P, I64, P,
                                          I64, I64, I64, I64, I64, I64, D, I64,
                                          P, I64, P]
+    lib.fo_sparse_decode_attn.argtypes = [I, P, I64, I64, I64, P, P, I64, I64,
+                                          P, P, I64, I64, P, I64, P, I64, P,
+                                          I64, I64, I64, I64, I64, I64, D,
+                                          P, I64, P]
     lib.fo_e2m1_value.argtypes = [ctypes.c_uint]
     lib.fo_e2m1_value.restype = D
     lib.fo_e8m0_value.argtypes = [ctypes.c_uint]
@@ -230,6 +234,44 @@ def paged_decode_attn(q, k_cache, v_cache, k_scale, v_scale, block_tables,
         cs[0], cs[1], _ptr(k_scale), _ptr(v_scale), ss[0], ss[1],
         _ptr(bt), bt.strides[0] // 4, _ptr(cl), B, R, Hq, num_kv_heads, D,
         block_size, float(softmax_scale), int(partition_tokens),
+        None if sel is None else _ptr(sel), nsel, _ptr(out))
+    return out
+
+
+def sparse_decode_attn(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                       block_valid, context_lens, num_kv_heads, block_size,
+                       softmax_scale, rows=None, fmt: int = E4M3):
+    """Decode attention over selected blocks, in double.
+
+    block_tables int32 [B, max_sel]: the selected blocks in position order.
+    block_valid  int32 [B, max_sel]: keys of each selected block, from its
+                 start (0 .. block_size).
+    context_lens int32 [B]: virtual positions (i * block_size + offset) of
+                 the request; row r of R sees positions 0 .. len - R + r.
+    Other arguments as in paged_decode_attn.
+    """
+    assert q.dtype == np.uint16 and q.ndim == 4
+    B, R, Hq, D = q.shape
+    qs = _estrides(q)
+    assert qs[3] == 1
+    cs, ss = _estrides(k_cache), _estrides(k_scale)
+    assert _estrides(v_cache) == cs and _estrides(v_scale) == ss
+    bt = np.asarray(block_tables, dtype=np.int32)
+    bv = np.asarray(block_valid, dtype=np.int32)
+    assert bt.strides[1] == 4 and bv.strides[1] == 4 and bv.shape == bt.shape
+    cl = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    if rows is None:
+        sel, nsel = None, 0
+        out = np.empty((B, R, Hq, D), dtype=np.float64)
+    else:
+        sel = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nsel = sel.size
+        out = np.empty((nsel, D), dtype=np.float64)
+    _load().fo_sparse_decode_attn(
+        fmt, _ptr(q), qs[0], qs[1], qs[2], _ptr(k_cache), _ptr(v_cache),
+        cs[0], cs[1], _ptr(k_scale), _ptr(v_scale), ss[0], ss[1],
+        _ptr(bt), bt.strides[0] // 4, _ptr(bv), bv.strides[0] // 4, _ptr(cl),
+        B, R, Hq, num_kv_heads, D, block_size, float(softmax_scale),
         None if sel is None else _ptr(sel), nsel, _ptr(out))
     return out
 

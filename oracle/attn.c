@@ -28,6 +28,10 @@
  * Parity pins: torch float64 softmax(q K^T) V on the dequantized keys,
  * single-key and constant-score closed forms, MTP-row / prefix equivalence,
  * GQA == MHA with replicated KV, split == unsplit.
+ *
+ * fo_sparse_decode_attn is the same attention over selected blocks (see its
+ * comment); pins: torch on the explicitly gathered keys, full selection ==
+ * dense, single key, empty blocks and block order.
  */
 #include <math.h>
 #include <stdint.h>
@@ -106,26 +110,37 @@ static void attend_one_row(
     const uint8_t* v_cache, int64_t cache_stride_slot,
     int64_t cache_stride_head, const float* k_scale, const float* v_scale,
     int64_t scale_stride_slot, int64_t scale_stride_head,
-    const int32_t* bt_row, int64_t n, int64_t h, int64_t D,
-    int64_t block_size, double softmax_scale, int64_t partition_tokens,
-    double* out) {
+    const int32_t* bt_row, const int32_t* valid_row, int64_t n, int64_t h,
+    int64_t D, int64_t block_size, double softmax_scale,
+    int64_t partition_tokens, double* out) {
     for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
     if (n <= 0) return;
     double* q = (double*)malloc((size_t)D * sizeof(double));
     double* keys = (double*)malloc((size_t)(n * D) * sizeof(double));
     double* vals = (double*)malloc((size_t)(n * D) * sizeof(double));
     for (int64_t d = 0; d < D; ++d) q[d] = (double)fo_bf16_to_f32(q_row[d]);
-    /* page-table walk: token j lives in block bt_row[j / bs] at offset
-     * j % bs */
+    /* page-table walk: position j lives in block bt_row[j / bs] at offset
+     * j % bs; with a valid row, only offsets below the block's valid count
+     * are keys (the others are skipped, not zeroed) */
+    int64_t kept = 0;
     for (int64_t j = 0; j < n; ++j) {
-        const int64_t slot =
-            (int64_t)bt_row[j / block_size] * block_size + j % block_size;
+        const int64_t i = j / block_size, o = j % block_size;
+        if (valid_row && o >= (int64_t)valid_row[i]) continue;
+        const int64_t slot = (int64_t)bt_row[i] * block_size + o;
         dequant_row(fmt, k_cache, k_scale, slot, h, cache_stride_slot,
                     cache_stride_head, scale_stride_slot, scale_stride_head, D,
-                    keys + j * D);
+                    keys + kept * D);
         dequant_row(fmt, v_cache, v_scale, slot, h, cache_stride_slot,
                     cache_stride_head, scale_stride_slot, scale_stride_head, D,
-                    vals + j * D);
+                    vals + kept * D);
+        ++kept;
+    }
+    n = kept;
+    if (n == 0) {
+        free(vals);
+        free(keys);
+        free(q);
+        return;
     }
     if (partition_tokens <= 0) {
         fo_attend_dense(q, keys, vals, n, D, softmax_scale, out);
@@ -186,8 +201,51 @@ void fo_paged_decode_attn(
                        q + b * q_stride_b + r * q_stride_row + hq * q_stride_head,
                        k_cache, v_cache, cache_stride_slot, cache_stride_head,
                        k_scale, v_scale, scale_stride_slot, scale_stride_head,
-                       block_tables + b * block_table_stride, n, hq / G, D,
-                       block_size, softmax_scale, partition_tokens,
+                       block_tables + b * block_table_stride, NULL, n, hq / G,
+                       D, block_size, softmax_scale, partition_tokens,
                        out + i * D);
+    }
+}
+
+/*
+ * Decode attention over selected blocks ([ATOM] description, K/V bullet:
+ * the sparse GQA kernel reads E4M3 tiles with the same scale handling;
+ * FreeToken #354, description: only the selected K/V rows are read back
+ * as codes). The selected blocks of request b are its page table, in
+ * position order; block_valid[b][i] (0 .. bs) counts the tokens of the i-th
+ * selected block that are keys, from its start. Virtual position
+ * j = i * bs + o is a key iff o < block_valid[b][i]; row r of R sees the
+ * virtual positions 0 .. context_lens[b] - R + r (context_lens counts
+ * virtual positions). Everything else is fo_paged_decode_attn.
+ */
+void fo_sparse_decode_attn(
+    int fmt,
+    const uint16_t* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head,
+    const uint8_t* k_cache, const uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head,
+    const float* k_scale, const float* v_scale,
+    int64_t scale_stride_slot, int64_t scale_stride_head,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* block_valid, int64_t block_valid_stride,
+    const int32_t* context_lens,
+    int64_t B, int64_t R, int64_t Hq, int64_t Hkv, int64_t D,
+    int64_t block_size, double softmax_scale,
+    const int64_t* rows_sel, int64_t n_rows_sel, double* out) {
+    const int64_t G = Hq / Hkv;
+    const int64_t total = rows_sel ? n_rows_sel : B * R * Hq;
+    for (int64_t i = 0; i < total; ++i) {
+        const int64_t flat = rows_sel ? rows_sel[i] : i;
+        const int64_t hq = flat % Hq;
+        const int64_t r = (flat / Hq) % R;
+        const int64_t b = flat / (Hq * R);
+        const int64_t n = (int64_t)context_lens[b] - R + r + 1;
+        attend_one_row(fmt,
+                       q + b * q_stride_b + r * q_stride_row + hq * q_stride_head,
+                       k_cache, v_cache, cache_stride_slot, cache_stride_head,
+                       k_scale, v_scale, scale_stride_slot, scale_stride_head,
+                       block_tables + b * block_table_stride,
+                       block_valid + b * block_valid_stride, n, hq / G, D,
+                       block_size, softmax_scale, 0, out + i * D);
     }
 }

@@ -98,6 +98,21 @@ void fo_paged_decode_attn(
     int64_t block_size, double softmax_scale, int64_t partition_tokens,
     const int64_t* rows_sel, int64_t n_rows_sel, double* out);
 
+void fo_sparse_decode_attn(
+    int fmt,
+    const uint16_t* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head,
+    const uint8_t* k_cache, const uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head,
+    const float* k_scale, const float* v_scale,
+    int64_t scale_stride_slot, int64_t scale_stride_head,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* block_valid, int64_t block_valid_stride,
+    const int32_t* context_lens,
+    int64_t B, int64_t R, int64_t Hq, int64_t Hkv, int64_t D,
+    int64_t block_size, double softmax_scale,
+    const int64_t* rows_sel, int64_t n_rows_sel, double* out);
+
 /* ---- compressed index keys and the index scorer (index.c) --------------
  * [ATOM] description, compressed-index bullet and the stacked-scorer
  * paragraph. Parity: the codec is pinned by closed forms, the OCP tables
