@@ -52,8 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the prefill-chunk, long-context and index extras")
-    ap.add_argument("--extras", default="prefill,longctx,index",
-                    help="comma list of the extras to run (prefill, longctx, index)")
+    ap.add_argument("--extras", default="prefill,longctx,sparse,index",
+                    help="comma list of the extras to run (prefill, longctx, sparse, index)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times "
                          "(the known-size reference for HBM byte counters)")
@@ -361,6 +361,9 @@ def main():
         result["also"].update(prefill_quant_scatter(torch, fk, synth, dev, stream))
     if "longctx" in extras:
         result["also"].update(longctx_decode(torch, fk, synth, dev, stream))
+    if "sparse" in extras:
+        result["also"].update(sparse_decode(torch, fk, synth, dev, stream, case, q, bt,
+                                            k_cache, v_cache, k_plane, v_plane))
     if "index" in extras:
         result["also"].update(index_scorer(torch, fk, synth, dev, stream))
 
@@ -454,6 +457,47 @@ def longctx_decode(torch, fk, synth, dev, stream, reps=20):
     del k_cache, v_cache, k_plane, v_plane
     torch.cuda.empty_cache()
     return res
+
+
+def sparse_decode(torch, fk, synth, dev, stream, case, q, bt, k_cache, v_cache,
+                  k_plane, v_plane, reps=20):
+    """Decode over selected blocks on the decode workload's cache: every
+    request keeps 1/8 of its blocks (drawn at random) plus its last one.
+    Algorithmic bytes: the selected keys' codes and scales, the selected
+    table entries and valid counts, q."""
+    log("sparse decode (1/8 of the blocks of the decode workload)...")
+    sel = synth.sparse_selection(case.layout, 0.125, seed=52)
+    B, R, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    bs = case.layout.block_size
+    sbt = sel.block_tables.to(dev)
+    sbv = sel.block_valid.to(dev)
+    scl = sel.context_lens.to(dev)
+    nr = fk.decode_num_ranges(Hkv, 0)
+    ws = torch.empty(fk.decode_workspace_bytes(B, R, Hq, Hkv, D, nr),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((B, R, Hq, D), dtype=torch.bfloat16, device=dev)
+    kw = dict(num_kv_heads=Hkv, block_size=bs, softmax_scale=case.softmax_scale,
+              max_context=32768, num_ranges=nr, workspace=ws)
+
+    def partials():
+        fk.sparse_decode_partials(q, k_cache, v_cache, k_plane.t(), v_plane.t(),
+                                  sbt, sbv, scl, **kw)
+
+    def full():
+        fk.sparse_decode_attn_fp8(q, k_cache, v_cache, k_plane.t(), v_plane.t(),
+                                  sbt, sbv, scl, out=out, **kw)
+    keys = int(sel.block_valid.clamp(0, bs).sum())
+    nsel = int((sel.block_valid > 0).sum())
+    alg = keys * Hkv * (2 * D + 8) + nsel * 8 + B * R * Hq * D * 2
+    pm = time_events(partials, reps, stream)
+    fm = time_events(full, reps, stream)
+    p_avg = sum(pm) / len(pm)
+    f_avg = sum(fm) / len(fm)
+    return {"sparse_selected_tokens": keys,
+            "sparse_decode_us": round(f_avg * 1e3, 1),
+            "sparse_split_kernel_us": round(p_avg * 1e3, 1),
+            "sparse_split_kernel_GBps": round(alg / (p_avg * 1e-3) / 1e9, 1)}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA

@@ -67,6 +67,11 @@ def lib():
     L.fp8kv_paged_decode_attn_fp8.restype = ctypes.c_int
     L.fp8kv_paged_decode_partials.argtypes = dec + [P]
     L.fp8kv_paged_decode_partials.restype = ctypes.c_int
+    sdec = dec[:16] + [P, I64] + dec[16:]
+    L.fp8kv_sparse_decode_attn_fp8.argtypes = sdec + [P, I64, I64, I64, I32, P]
+    L.fp8kv_sparse_decode_attn_fp8.restype = ctypes.c_int
+    L.fp8kv_sparse_decode_partials.argtypes = sdec + [P]
+    L.fp8kv_sparse_decode_partials.restype = ctypes.c_int
     L.fp8kv_paged_decode_merge.argtypes = [I32, I32, I32, I32, I32, I32, P,
                                            SZ, P, I64, I64, I64, I32, P]
     L.fp8kv_paged_decode_merge.restype = ctypes.c_int
@@ -254,6 +259,58 @@ def paged_decode_partials(q, k_cache, v_cache, k_scale, v_scale, block_tables,
                                    block_size, softmax_scale, max_context,
                                    num_ranges, workspace)
     _check(lib().fp8kv_paged_decode_partials(*args, _stream(q.device)))
+    return workspace
+
+
+def _sparse_args(args, block_valid):
+    """Insert the selected blocks' valid counts after the block table."""
+    _dev(block_valid)
+    if block_valid.dtype != torch.int32 or block_valid.dim() != 2 or \
+            block_valid.stride(1) != 1:
+        raise ValueError("block_valid must be int32 [B, max_sel], rows contiguous")
+    return args[:16] + [block_valid.data_ptr(), block_valid.stride(0)] + args[16:]
+
+
+def sparse_decode_attn_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                           block_valid, context_lens, *, num_kv_heads,
+                           block_size, softmax_scale, max_context,
+                           num_ranges=0, out=None, out_dtype=torch.bfloat16,
+                           workspace=None):
+    """Decode attention over selected blocks: block_tables [B, max_sel]
+    lists each request's selected blocks in position order, block_valid
+    [B, max_sel] the keys of each from its start, context_lens the virtual
+    positions (verify rows are causal on them). Returns out [B, R, Hq, D]."""
+    if block_valid.shape != block_tables.shape:
+        raise ValueError("block_valid must have the shape of block_tables")
+    args, workspace = _decode_args(q, k_cache, v_cache, k_scale, v_scale,
+                                   block_tables, context_lens, num_kv_heads,
+                                   block_size, softmax_scale, max_context,
+                                   num_ranges, workspace)
+    args = _sparse_args(args, block_valid)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _dev(out)
+    if out.shape != q.shape or out.stride(3) != 1:
+        raise ValueError("out must be [B, R, Hq, D] with contiguous head_dim")
+    _check(lib().fp8kv_sparse_decode_attn_fp8(
+        *args, out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
+        _TORCH_DTYPE[out.dtype], _stream(q.device)))
+    return out
+
+
+def sparse_decode_partials(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                           block_valid, context_lens, *, num_kv_heads,
+                           block_size, softmax_scale, max_context,
+                           num_ranges=0, workspace=None):
+    """Split phase of sparse_decode_attn_fp8; merge with paged_decode_merge."""
+    if block_valid.shape != block_tables.shape:
+        raise ValueError("block_valid must have the shape of block_tables")
+    args, workspace = _decode_args(q, k_cache, v_cache, k_scale, v_scale,
+                                   block_tables, context_lens, num_kv_heads,
+                                   block_size, softmax_scale, max_context,
+                                   num_ranges, workspace)
+    _check(lib().fp8kv_sparse_decode_partials(*_sparse_args(args, block_valid),
+                                              _stream(q.device)))
     return workspace
 
 

@@ -109,6 +109,102 @@ int launched(hipError_t e, const char* what) {
     return ok();
 }
 
+static int decode_partials(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype, const uint8_t* k_cache,
+    const uint8_t* v_cache, int64_t cache_stride_slot,
+    int64_t cache_stride_head, const float* k_scale, const float* v_scale,
+    int64_t scale_stride_slot, int64_t scale_stride_head, int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* block_valid, int64_t block_valid_stride,
+    const int32_t* context_lens, int32_t batch, int32_t rows,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float softmax_scale, int32_t num_ranges,
+    int32_t max_context, void* workspace, size_t workspace_bytes,
+    void* stream) {
+    DecodeShape s;
+    int st = decode_shape(batch, rows, num_q_heads, num_kv_heads, head_dim, num_ranges, &s);
+    if (st != FP8KV_OK) return st;
+    if (q_dtype != FP8KV_DTYPE_BF16)
+        return fail(FP8KV_E_UNSUPPORTED, "q_dtype %d: only BF16 queries", q_dtype);
+    if (block_size < 16 || block_size % 16 != 0)
+        return fail(FP8KV_E_UNSUPPORTED, "block_size %d: must be a positive multiple of 16", block_size);
+    if (max_context < 0)
+        return fail(FP8KV_E_SHAPE, "max_context (%d) must be >= 0", max_context);
+    if ((int64_t)batch * ((max_context + 31) / 32) > INT32_MAX)
+        return fail(FP8KV_E_SHAPE, "batch * max_context too large for 32-bit tile counts");
+    if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables ||
+        !context_lens)
+        return fail(FP8KV_E_NULL, "paged_decode: a required pointer is NULL");
+    if (!workspace)
+        return fail(FP8KV_E_WORKSPACE, "paged_decode: workspace is NULL");
+    if ((int64_t)workspace_bytes < s.ws_bytes)
+        return fail(FP8KV_E_WORKSPACE, "workspace %zu bytes < required %lld",
+                    workspace_bytes, (long long)s.ws_bytes);
+    if (q_stride_b < 0 || q_stride_row < 0 || q_stride_head < 0 ||
+        cache_stride_slot < 0 || cache_stride_head < 0 ||
+        scale_stride_slot < 0 || scale_stride_head < 0 ||
+        block_table_stride < 0 || block_valid_stride < 0)
+        return fail(FP8KV_E_STRIDE, "paged_decode: negative stride");
+    if (!aligned(q, 16) || q_stride_b % 8 || q_stride_row % 8 || q_stride_head % 8)
+        return fail(FP8KV_E_ALIGN, "q rows must start on 16-byte boundaries");
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        cache_stride_slot % 16 || cache_stride_head % 16)
+        return fail(FP8KV_E_ALIGN, "cache rows must start on 16-byte boundaries");
+    if (!aligned(k_scale, 4) || !aligned(v_scale, 4) ||
+        !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
+        !aligned(block_valid, 4) || !aligned(workspace, 256))
+        return fail(FP8KV_E_ALIGN, "scale planes, tables or workspace misaligned");
+    const int64_t num_blocks = num_slots / block_size;
+    if (batch > 0 && max_context > 0 && num_blocks < 1)
+        return fail(FP8KV_E_SHAPE, "num_slots %lld holds no block of %d",
+                    (long long)num_slots, block_size);
+    if (num_blocks > INT32_MAX)
+        return fail(FP8KV_E_SHAPE, "num_slots / block_size exceeds int32 block ids");
+    // in-block offsets are 32-bit: 16 slots of codes / scales must fit
+    if (cache_stride_slot > (INT32_MAX / 16) || scale_stride_slot > (INT32_MAX / 64))
+        return fail(FP8KV_E_SHAPE, "slot stride too large for 32-bit in-block offsets");
+    if (batch == 0) return ok();
+
+    fp8kv::DecodeParams p;
+    p.q = static_cast<const uint16_t*>(q);
+    p.q_stride_b = q_stride_b;
+    p.q_stride_row = q_stride_row;
+    p.q_stride_head = q_stride_head;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.cache_stride_slot = cache_stride_slot;
+    p.cache_stride_head = cache_stride_head;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.scale_stride_slot = scale_stride_slot;
+    p.scale_stride_head = scale_stride_head;
+    p.block_tables = block_tables;
+    p.block_table_stride = block_table_stride;
+    p.block_valid = block_valid;
+    p.block_valid_stride = block_valid_stride;
+    p.context_lens = context_lens;
+    p.batch = batch;
+    p.rows = rows;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = s.group;
+    p.m_rows = s.m_rows;
+    p.block_size = block_size;
+    p.block_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
+    p.max_context = max_context;
+    p.num_blocks = (int32_t)(num_blocks > 0 ? num_blocks : 1);
+    p.num_ranges = s.num_ranges;
+    p.wgs_per_range = (num_kv_heads % 4 == 0 && num_kv_heads > 4) ? num_kv_heads / 4 : 1;
+    p.score_scale_log2 = softmax_scale * 1.4426950408889634f;
+    char* ws = static_cast<char*>(workspace);
+    p.ws_o = reinterpret_cast<float*>(ws);
+    p.ws_lse = reinterpret_cast<float*>(ws + s.lse_offset_bytes);
+    p.ws_prefix = reinterpret_cast<int32_t*>(ws + s.prefix_offset_bytes);
+    return launched(fp8kv::launch_decode_partitions(p, head_dim, (hipStream_t)stream),
+                    "paged_decode_partials");
+}
+
 }  // namespace
 
 extern "C" {
@@ -220,85 +316,36 @@ int fp8kv_paged_decode_partials(
     int32_t block_size, float softmax_scale, int32_t num_ranges,
     int32_t max_context, void* workspace, size_t workspace_bytes,
     void* stream) {
-    DecodeShape s;
-    int st = decode_shape(batch, rows, num_q_heads, num_kv_heads, head_dim, num_ranges, &s);
-    if (st != FP8KV_OK) return st;
-    if (q_dtype != FP8KV_DTYPE_BF16)
-        return fail(FP8KV_E_UNSUPPORTED, "q_dtype %d: only BF16 queries", q_dtype);
-    if (block_size < 16 || block_size % 16 != 0)
-        return fail(FP8KV_E_UNSUPPORTED, "block_size %d: must be a positive multiple of 16", block_size);
-    if (max_context < 0)
-        return fail(FP8KV_E_SHAPE, "max_context (%d) must be >= 0", max_context);
-    if ((int64_t)batch * ((max_context + 31) / 32) > INT32_MAX)
-        return fail(FP8KV_E_SHAPE, "batch * max_context too large for 32-bit tile counts");
-    if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables ||
-        !context_lens)
-        return fail(FP8KV_E_NULL, "paged_decode: a required pointer is NULL");
-    if (!workspace)
-        return fail(FP8KV_E_WORKSPACE, "paged_decode: workspace is NULL");
-    if ((int64_t)workspace_bytes < s.ws_bytes)
-        return fail(FP8KV_E_WORKSPACE, "workspace %zu bytes < required %lld",
-                    workspace_bytes, (long long)s.ws_bytes);
-    if (q_stride_b < 0 || q_stride_row < 0 || q_stride_head < 0 ||
-        cache_stride_slot < 0 || cache_stride_head < 0 ||
-        scale_stride_slot < 0 || scale_stride_head < 0 ||
-        block_table_stride < 0)
-        return fail(FP8KV_E_STRIDE, "paged_decode: negative stride");
-    if (!aligned(q, 16) || q_stride_b % 8 || q_stride_row % 8 || q_stride_head % 8)
-        return fail(FP8KV_E_ALIGN, "q rows must start on 16-byte boundaries");
-    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-        cache_stride_slot % 16 || cache_stride_head % 16)
-        return fail(FP8KV_E_ALIGN, "cache rows must start on 16-byte boundaries");
-    if (!aligned(k_scale, 4) || !aligned(v_scale, 4) ||
-        !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
-        !aligned(workspace, 256))
-        return fail(FP8KV_E_ALIGN, "scale planes, tables or workspace misaligned");
-    const int64_t num_blocks = num_slots / block_size;
-    if (batch > 0 && max_context > 0 && num_blocks < 1)
-        return fail(FP8KV_E_SHAPE, "num_slots %lld holds no block of %d",
-                    (long long)num_slots, block_size);
-    if (num_blocks > INT32_MAX)
-        return fail(FP8KV_E_SHAPE, "num_slots / block_size exceeds int32 block ids");
-    // in-block offsets are 32-bit: 16 slots of codes / scales must fit
-    if (cache_stride_slot > (INT32_MAX / 16) || scale_stride_slot > (INT32_MAX / 64))
-        return fail(FP8KV_E_SHAPE, "slot stride too large for 32-bit in-block offsets");
-    if (batch == 0) return ok();
+    return decode_partials(q, q_stride_b, q_stride_row, q_stride_head, q_dtype, k_cache,
+                           v_cache, cache_stride_slot, cache_stride_head, k_scale, v_scale,
+                           scale_stride_slot, scale_stride_head, num_slots, block_tables,
+                           block_table_stride, nullptr, 0, context_lens, batch, rows,
+                           num_q_heads, num_kv_heads, head_dim, block_size, softmax_scale,
+                           num_ranges, max_context, workspace, workspace_bytes, stream);
+}
 
-    fp8kv::DecodeParams p;
-    p.q = static_cast<const uint16_t*>(q);
-    p.q_stride_b = q_stride_b;
-    p.q_stride_row = q_stride_row;
-    p.q_stride_head = q_stride_head;
-    p.k_cache = k_cache;
-    p.v_cache = v_cache;
-    p.cache_stride_slot = cache_stride_slot;
-    p.cache_stride_head = cache_stride_head;
-    p.k_scale = k_scale;
-    p.v_scale = v_scale;
-    p.scale_stride_slot = scale_stride_slot;
-    p.scale_stride_head = scale_stride_head;
-    p.block_tables = block_tables;
-    p.block_table_stride = block_table_stride;
-    p.context_lens = context_lens;
-    p.batch = batch;
-    p.rows = rows;
-    p.num_q_heads = num_q_heads;
-    p.num_kv_heads = num_kv_heads;
-    p.group = s.group;
-    p.m_rows = s.m_rows;
-    p.block_size = block_size;
-    p.block_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
-    p.max_context = max_context;
-    p.num_blocks = (int32_t)(num_blocks > 0 ? num_blocks : 1);
-    p.num_ranges = s.num_ranges;
-    p.wgs_per_range = (num_kv_heads % 4 == 0 && num_kv_heads > 4) ? num_kv_heads / 4 : 1;
-    p.score_scale_log2 = softmax_scale * 1.4426950408889634f;
-    char* ws = static_cast<char*>(workspace);
-    p.ws_o = reinterpret_cast<float*>(ws);
-    p.ws_lse = reinterpret_cast<float*>(ws + s.lse_offset_bytes);
-    p.ws_prefix = reinterpret_cast<int32_t*>(ws + s.prefix_offset_bytes);
-    return launched(fp8kv::launch_decode_partitions(p, head_dim, (hipStream_t)stream),
-                    "paged_decode_partials");
+int fp8kv_sparse_decode_partials(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype, const uint8_t* k_cache,
+    const uint8_t* v_cache, int64_t cache_stride_slot,
+    int64_t cache_stride_head, const float* k_scale, const float* v_scale,
+    int64_t scale_stride_slot, int64_t scale_stride_head, int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* block_valid, int64_t block_valid_stride,
+    const int32_t* context_lens, int32_t batch, int32_t rows,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float softmax_scale, int32_t num_ranges,
+    int32_t max_context, void* workspace, size_t workspace_bytes,
+    void* stream) {
+    if (!block_valid)
+        return fail(FP8KV_E_NULL, "sparse_decode: block_valid is NULL");
+    return decode_partials(q, q_stride_b, q_stride_row, q_stride_head, q_dtype, k_cache,
+                           v_cache, cache_stride_slot, cache_stride_head, k_scale, v_scale,
+                           scale_stride_slot, scale_stride_head, num_slots, block_tables,
+                           block_table_stride, block_valid, block_valid_stride, context_lens,
+                           batch, rows, num_q_heads, num_kv_heads, head_dim, block_size,
+                           softmax_scale, num_ranges, max_context, workspace,
+                           workspace_bytes, stream);
 }
 
 int fp8kv_paged_decode_merge(
@@ -370,6 +417,42 @@ int fp8kv_paged_decode_attn_fp8(
         scale_stride_slot, scale_stride_head, num_slots, block_tables,
         block_table_stride, context_lens, batch, rows, num_q_heads,
         num_kv_heads, head_dim, block_size, softmax_scale, num_ranges,
+        max_context, workspace, workspace_bytes, stream);
+    if (st != FP8KV_OK) return st;
+    return fp8kv_paged_decode_merge(
+        batch, rows, num_q_heads, num_kv_heads, head_dim, num_ranges,
+        workspace, workspace_bytes, out, out_stride_b, out_stride_row,
+        out_stride_head, out_dtype, stream);
+}
+
+int fp8kv_sparse_decode_attn_fp8(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype, const uint8_t* k_cache,
+    const uint8_t* v_cache, int64_t cache_stride_slot,
+    int64_t cache_stride_head, const float* k_scale, const float* v_scale,
+    int64_t scale_stride_slot, int64_t scale_stride_head, int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* block_valid, int64_t block_valid_stride,
+    const int32_t* context_lens, int32_t batch, int32_t rows,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float softmax_scale, int32_t num_ranges,
+    int32_t max_context, void* workspace, size_t workspace_bytes, void* out,
+    int64_t out_stride_b, int64_t out_stride_row, int64_t out_stride_head,
+    int32_t out_dtype, void* stream) {
+    // validate everything before enqueueing anything
+    int st = check_out_dtype(out_dtype);
+    if (st != FP8KV_OK) return st;
+    if (!out) return fail(FP8KV_E_NULL, "sparse_decode: out is NULL");
+    if (out_stride_b < 0 || out_stride_row < 0 || out_stride_head < 0)
+        return fail(FP8KV_E_STRIDE, "sparse_decode: negative out stride");
+    if (!aligned(out, out_dtype == FP8KV_DTYPE_FP32 ? 4 : 2))
+        return fail(FP8KV_E_ALIGN, "out misaligned");
+    st = fp8kv_sparse_decode_partials(
+        q, q_stride_b, q_stride_row, q_stride_head, q_dtype, k_cache, v_cache,
+        cache_stride_slot, cache_stride_head, k_scale, v_scale,
+        scale_stride_slot, scale_stride_head, num_slots, block_tables,
+        block_table_stride, block_valid, block_valid_stride, context_lens, batch, rows,
+        num_q_heads, num_kv_heads, head_dim, block_size, softmax_scale, num_ranges,
         max_context, workspace, workspace_bytes, stream);
     if (st != FP8KV_OK) return st;
     return fp8kv_paged_decode_merge(

@@ -39,6 +39,8 @@ struct DecodeParams {
     int64_t scale_stride_slot, scale_stride_head;
     const int32_t* block_tables;
     int64_t block_table_stride;
+    const int32_t* block_valid;   // selected blocks: valid keys per entry, or null (dense)
+    int64_t block_valid_stride;
     const int32_t* context_lens;
     int32_t batch, rows, num_q_heads, num_kv_heads, group, m_rows;
     int32_t block_size, max_context;

@@ -123,6 +123,7 @@ struct TileAddr {
     __amdgpu_buffer_rsrc_t k[2], v[2], ks[2], vs[2];
     int t0;
     bool masked;
+    int nv[2];            // selected blocks: keys of each half, from its start
 };
 
 // Loop-invariant byte offsets of the lane's loads inside a 16-token half.
@@ -169,6 +170,7 @@ struct DecodeTile {
         const float* ksbase;      // k_scale + h * scale_stride_head
         const float* vsbase;
         const int32_t* bt;        // this request's block-table row
+        const int32_t* bv;        // ... and its valid-key counts (selected blocks)
         int p0, p1, ntiles, full_end, last_base;
         int nr_codes_full;        // num_records of a full half: 15*css + D
         int nr_scales_full;       // ... of its scales: 4*(15*sss + 1)
@@ -179,22 +181,25 @@ struct DecodeTile {
     // last half, so every lane reads an entry the request owns.
     template <bool BSP2>
     static __device__ __forceinline__ int table_window(const DecodeParams& p, const WalkConsts& w,
-                                                       int k0, int lane) {
+                                                       const int32_t* row, int k0, int lane) {
         const int stok = min(w.p0 + 32 * (k0 + (lane >> 1)) + 16 * (lane & 1), w.last_base);
         const int bi = BSP2 ? (stok >> p.block_shift) : stok / p.block_size;
-        return w.bt[bi];
+        return row[bi];
     }
 
     // Page walk of tile ti of the piece (wave-uniform) from its two table
     // entries. Full halves use constant bounds; a ragged tile's halves end
     // after their last token inside the piece, and a tile past the piece's
     // last one gets empty ones.
-    template <bool BSP2>
+    // With selected blocks (SP), every half is bounded by the keys its block
+    // holds from the half's start, and a tile with a partial half is masked.
+    template <bool BSP2, bool SP>
     static __device__ __forceinline__ void address(const DecodeParams& p, const WalkConsts& w,
-                                                   int ti, const int (&blk_in)[2], TileAddr& ta) {
+                                                   int ti, const int (&blk_in)[2],
+                                                   const int (&valid_in)[2], TileAddr& ta) {
         const int t0 = w.p0 + (ti << 5);
         const bool live = ti < w.ntiles;
-        const bool ragged = !live || t0 + 32 > w.p1;
+        const bool ragged = SP || !live || t0 + 32 > w.p1;
         const int bs = p.block_size;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -207,10 +212,13 @@ struct DecodeTile {
             const int64_t soff = slot * p.scale_stride_slot;
             int nrc = w.nr_codes_full, nrs = w.nr_scales_full;
             if (ragged) {
-                // tokens of this half inside the piece (<= 0: none)
-                const int nvalid = live ? min(16, w.p1 - stok) : 0;
+                // tokens of this half inside the piece (<= 0: none), and with
+                // selected blocks only the block's keys from the half's start
+                int nvalid = live ? min(16, w.p1 - stok) : 0;
+                if (SP) nvalid = min(nvalid, min(max(valid_in[s], 0), bs) - bo);
                 nrc = nvalid > 0 ? (nvalid - 1) * (int)p.cache_stride_slot + D : 0;
                 nrs = nvalid > 0 ? 4 * ((nvalid - 1) * (int)p.scale_stride_slot + 1) : 0;
+                ta.nv[s] = max(nvalid, 0);
             }
             ta.k[s] = make_rsrc(w.kbase + coff, nrc);
             ta.v[s] = make_rsrc(w.vbase + coff, nrc);
@@ -218,7 +226,7 @@ struct DecodeTile {
             ta.vs[s] = make_rsrc(w.vsbase + soff, nrs);
         }
         ta.t0 = t0;
-        ta.masked = t0 + 32 > w.full_end;
+        ta.masked = t0 + 32 > w.full_end || (SP && (ta.nv[0] < 16 || ta.nv[1] < 16));
     }
 
     static __device__ __forceinline__ void issue(const TileAddr& ta, const LaneOffsets& o, Regs& R) {
@@ -254,6 +262,7 @@ struct DecodeTile {
     }
 
     // Online-softmax update and PV with the tile's scores and V registers.
+    template <bool SP>
     static __device__ __forceinline__ void rest(
         const DecodeParams& p, const TileAddr& ta, const Regs& R, const floatx4 (&sc)[2],
         int p1, int lim, int lg, WaveState<DL>& st) {
@@ -278,8 +287,11 @@ struct DecodeTile {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int tok = ta.t0 + 16 * s + 4 * lg + r;
-                    s2[s][r] = (tok < p1 && tok <= lim) ? s2[s][r] : kNeg;
-                    sv[s][r] = tok < p1 ? sv[s][r] : 0.f;
+                    // a key: inside the piece (and, with selected blocks,
+                    // among its block's keys); visible: not after the row
+                    const bool key = SP ? (4 * lg + r < ta.nv[s]) : tok < p1;
+                    s2[s][r] = (key && tok <= lim) ? s2[s][r] : kNeg;
+                    sv[s][r] = key ? sv[s][r] : 0.f;
                 }
         }
         float svm = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
@@ -365,7 +377,7 @@ __device__ __forceinline__ int request_tiles(const DecodeParams& p, int b) {
 // One piece: tiles [ja, jb) of request b for KV head h, reduced to a partial
 // (normalized output and log2 log-sum-exp of each of the M rows) at piece
 // id `pid`.
-template <int D, bool BSP2>
+template <int D, bool BSP2, bool SP>
 __device__ __forceinline__ void decode_piece(const DecodeParams& p, int b, int len, int ja, int jb,
                                              int h, int pid, int lane) {
     constexpr int KSTEPS = D / 32;
@@ -386,6 +398,7 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int b, int l
     w.ksbase = p.k_scale + (int64_t)h * p.scale_stride_head;
     w.vsbase = p.v_scale + (int64_t)h * p.scale_stride_head;
     w.bt = p.block_tables + (int64_t)b * p.block_table_stride;
+    w.bv = SP ? p.block_valid + (int64_t)b * p.block_valid_stride : nullptr;
     w.p0 = p0;
     w.p1 = p1;
     w.ntiles = ntiles;
@@ -397,8 +410,10 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int b, int l
 
     // block-table window of tiles 0..31, and the next one when the piece is longer
     int kw = 0;
-    int btw = Tile::template table_window<BSP2>(p, w, 0, lane);
-    int btn = ntiles > 32 ? Tile::template table_window<BSP2>(p, w, 32, lane) : 0;
+    int btw = Tile::template table_window<BSP2>(p, w, w.bt, 0, lane);
+    int btn = ntiles > 32 ? Tile::template table_window<BSP2>(p, w, w.bt, 32, lane) : 0;
+    int bvw = SP ? Tile::template table_window<BSP2>(p, w, w.bv, 0, lane) : 0;
+    int bvn = SP && ntiles > 32 ? Tile::template table_window<BSP2>(p, w, w.bv, 32, lane) : 0;
 
     // q operand: row li of the stacked (verify row, query head) block
     bf16x8 qv[KSTEPS];
@@ -438,15 +453,21 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int b, int l
 
     // table entries of tile k (wave-uniform k); windows move forward 32
     // tiles at a time, the next one already loaded
-    auto entries = [&](int k, int (&blk)[2]) {
+    auto entries = [&](int k, int (&blk)[2], int (&valid)[2]) {
         if (k - kw >= 32) {
             kw += 32;
             btw = btn;
-            if (ntiles > kw + 32) btn = Tile::template table_window<BSP2>(p, w, kw + 32, lane);
+            if (ntiles > kw + 32) btn = Tile::template table_window<BSP2>(p, w, w.bt, kw + 32, lane);
+            if (SP) {
+                bvw = bvn;
+                if (ntiles > kw + 32) bvn = Tile::template table_window<BSP2>(p, w, w.bv, kw + 32, lane);
+            }
         }
         const int j = 2 * (k - kw);
         blk[0] = __builtin_amdgcn_readlane(btw, j);
         blk[1] = __builtin_amdgcn_readlane(btw, j + 1);
+        valid[0] = SP ? __builtin_amdgcn_readlane(bvw, j) : 0;
+        valid[1] = SP ? __builtin_amdgcn_readlane(bvw, j + 1) : 0;
     };
 
     // Two tiles in flight: after a tile's QK^T has consumed its K registers,
@@ -455,23 +476,23 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int b, int l
     TileAddr ta_a, ta_b;
     Regs ra, rb;
     floatx4 sc[2];
-    int blk[2];
+    int blk[2], valid[2];
     int ti = 0;
-    entries(0, blk);
-    Tile::template address<BSP2>(p, w, 0, blk, ta_a);
+    entries(0, blk, valid);
+    Tile::template address<BSP2, SP>(p, w, 0, blk, valid, ta_a);
     Tile::issue(ta_a, lo, ra);
     while (ti < ntiles) {
         Tile::qk(ra, qv, sc);
-        entries(ti + 1, blk);
-        Tile::template address<BSP2>(p, w, ti + 1, blk, ta_b);
+        entries(ti + 1, blk, valid);
+        Tile::template address<BSP2, SP>(p, w, ti + 1, blk, valid, ta_b);
         Tile::issue(ta_b, lo, rb);
-        Tile::rest(p, ta_a, ra, sc, p1, lim, lg, st);
+        Tile::template rest<SP>(p, ta_a, ra, sc, p1, lim, lg, st);
         if (++ti >= ntiles) break;
         Tile::qk(rb, qv, sc);
-        entries(ti + 1, blk);
-        Tile::template address<BSP2>(p, w, ti + 1, blk, ta_a);
+        entries(ti + 1, blk, valid);
+        Tile::template address<BSP2, SP>(p, w, ti + 1, blk, valid, ta_a);
         Tile::issue(ta_a, lo, ra);
-        Tile::rest(p, ta_b, rb, sc, p1, lim, lg, st);
+        Tile::template rest<SP>(p, ta_b, rb, sc, p1, lim, lg, st);
         ++ti;
     }
 
@@ -508,7 +529,7 @@ __device__ __forceinline__ int logical_workgroup(int bid, int wgs_per_range) {
     return (k / m) * 8 * m + xcd * m + (k % m);
 }
 
-template <int D, bool BSP2>
+template <int D, bool BSP2, bool SP>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     const int lane = threadIdx.x & 63;
     // wave index, provably uniform so the page walk and the buffer
@@ -559,7 +580,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         if (n > 0) {
             const int ja = u - pre;
             const int jb = min(n, u1 - pre);
-            decode_piece<D, BSP2>(p, b, len, ja, jb, h, b + r, lane);
+            decode_piece<D, BSP2, SP>(p, b, len, ja, jb, h, b + r, lane);
             u = pre + jb;
         }
         pre += n;
@@ -683,15 +704,21 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
     }
 }
 
-template <int D, bool BSP2>
+template <int D, bool BSP2, bool SP>
 hipError_t launch_split(const DecodeParams& p, hipStream_t stream) {
     const int64_t workers = (int64_t)p.num_ranges * p.num_kv_heads;
     const int64_t quantum = p.wgs_per_range > 1 ? 8 * p.wgs_per_range : 1;
     int64_t wgs = (workers + 3) / 4;
     wgs = (wgs + quantum - 1) / quantum * quantum;
     if (wgs > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_split_kernel<D, BSP2>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, BSP2, SP>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int D, bool SP>
+hipError_t launch_split_bs(const DecodeParams& p, hipStream_t stream) {
+    return p.block_shift >= 0 ? launch_split<D, true, SP>(p, stream)
+                              : launch_split<D, false, SP>(p, stream);
 }
 
 }  // namespace
@@ -704,10 +731,10 @@ int decode_wave_slots(int device) {
 }
 
 hipError_t launch_decode_partitions(const DecodeParams& p, int head_dim, hipStream_t stream) {
-    const bool pow2 = p.block_shift >= 0;
+    const bool sp = p.block_valid != nullptr;
     if (head_dim == 128)
-        return pow2 ? launch_split<128, true>(p, stream) : launch_split<128, false>(p, stream);
-    return pow2 ? launch_split<64, true>(p, stream) : launch_split<64, false>(p, stream);
+        return sp ? launch_split_bs<128, true>(p, stream) : launch_split_bs<128, false>(p, stream);
+    return sp ? launch_split_bs<64, true>(p, stream) : launch_split_bs<64, false>(p, stream);
 }
 
 hipError_t launch_decode_merge(const MergeParams& p, int head_dim, hipStream_t stream) {

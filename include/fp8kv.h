@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FP8KV_ABI_VERSION 3
+#define FP8KV_ABI_VERSION 4
 
 typedef enum fp8kv_status {
     FP8KV_OK = 0,
@@ -238,6 +238,71 @@ int fp8kv_paged_decode_merge(
     void* out, int64_t out_stride_b, int64_t out_stride_row,
     int64_t out_stride_head, int32_t out_dtype,
     void* stream);
+
+/*
+ * fp8kv_sparse_decode_attn_fp8 -- the decode attention over SELECTED blocks
+ * only ([ATOM] "fix(qwen4-exp): register the QSA FP8 scale planes for KV
+ * offload", ROCm/ATOM #2655, description, K/V bullet: the sparse GQA kernel
+ * reads E4M3 tiles, key scale on the score column, value scale folded into
+ * P; "feat(kvcache): store the KV cache as fp8 e4m3 codes", FreeToken #354,
+ * description: the block-selection keys stay 16-bit and only the selected
+ * K/V rows are read back as codes).
+ *
+ * Same arguments, rules and workspace as fp8kv_paged_decode_attn_fp8,
+ * except:
+ * block_tables  (device) int32: row b lists the blocks request b selected,
+ *               in position order (the selection is its page table).
+ * block_valid   (device) int32, entry (b, i) at b*block_valid_stride + i:
+ *               how many tokens of the i-th selected block, from its start,
+ *               are keys (clamped to [0, block_size]); the rest are neither
+ *               read nor attended. Must not be NULL.
+ * context_lens  (device) int32: virtual positions of request b, where
+ *               position j is offset j % block_size of selected block
+ *               j / block_size; verify row r of R attends the keys at
+ *               positions 0 .. context_lens[b] - R + r (causal on virtual
+ *               positions). Typically (n_selected - 1) * block_size +
+ *               block_valid of the last block, which holds the newest
+ *               tokens. Clamped to [0, max_context].
+ * A row with no key outputs 0. With every block selected and full counts
+ * this is fp8kv_paged_decode_attn_fp8.
+ * Errors: as fp8kv_paged_decode_attn_fp8; E_NULL for block_valid.
+ */
+int fp8kv_sparse_decode_attn_fp8(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype,
+    const uint8_t* k_cache, const uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head,
+    const float* k_scale, const float* v_scale,
+    int64_t scale_stride_slot, int64_t scale_stride_head,
+    int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* block_valid, int64_t block_valid_stride,
+    const int32_t* context_lens,
+    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, float softmax_scale,
+    int32_t num_ranges, int32_t max_context,
+    void* workspace, size_t workspace_bytes,
+    void* out, int64_t out_stride_b, int64_t out_stride_row,
+    int64_t out_stride_head, int32_t out_dtype,
+    void* stream);
+
+/* Split phase of fp8kv_sparse_decode_attn_fp8; merge with
+ * fp8kv_paged_decode_merge. */
+int fp8kv_sparse_decode_partials(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype,
+    const uint8_t* k_cache, const uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head,
+    const float* k_scale, const float* v_scale,
+    int64_t scale_stride_slot, int64_t scale_stride_head,
+    int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* block_valid, int64_t block_valid_stride,
+    const int32_t* context_lens,
+    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, float softmax_scale,
+    int32_t num_ranges, int32_t max_context,
+    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Compressed index keys and the index scorer ("fix(qwen4-exp): register

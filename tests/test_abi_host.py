@@ -249,3 +249,39 @@ def test_index_score_refusals(L, kw, status):
     assert isc(L, **kw) == status
     if status != OK:
         assert L.fp8kv_last_error().decode()
+
+
+def sdec(L, fn="fp8kv_sparse_decode_attn_fp8", bv=A, bvs=2048, **kw):
+    """The sparse calls take (block_valid, stride) after the block table."""
+    a = dict(q=A, qsb=4096, qsr=4096, qsh=128, qdt=BF16, kc=A, vc=A,
+             css=1024, csh=128, ks=A, vs=A, sss=1, ssh=1 << 20, S=1 << 20,
+             bt=A, bts=2048, cl=A, B=64, R=1, Hq=32, H=8, D=128, bs=16,
+             scale=0.088, P=384, maxc=32768, ws=A, wsb=1 << 34, out=A,
+             osb=4096, osr=4096, osh=128, odt=BF16)
+    a.update(kw)
+    common = [a["q"], a["qsb"], a["qsr"], a["qsh"], a["qdt"], a["kc"],
+              a["vc"], a["css"], a["csh"], a["ks"], a["vs"], a["sss"],
+              a["ssh"], a["S"], a["bt"], a["bts"], bv, bvs, a["cl"], a["B"],
+              a["R"], a["Hq"], a["H"], a["D"], a["bs"],
+              ctypes.c_float(a["scale"]), a["P"], a["maxc"], a["ws"], a["wsb"]]
+    if fn == "fp8kv_sparse_decode_partials":
+        return getattr(L, fn)(*common, None)
+    return getattr(L, fn)(*common, a["out"], a["osb"], a["osr"], a["osh"],
+                          a["odt"], None)
+
+
+@pytest.mark.parametrize("fn", ["fp8kv_sparse_decode_attn_fp8",
+                                "fp8kv_sparse_decode_partials"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(bv=0), E_NULL),
+    (dict(bv=A + 2), E_ALIGN),
+    (dict(bvs=-1), E_STRIDE),
+    (dict(qdt=FP16), E_UNSUPPORTED),
+    (dict(D=96), E_UNSUPPORTED),
+    (dict(bs=24), E_UNSUPPORTED),
+    (dict(wsb=1024), E_WORKSPACE),
+    (dict(bt=0), E_NULL),
+])
+def test_sparse_decode_refusals(L, fn, kw, status):
+    assert sdec(L, fn=fn, **kw) == status
+    assert L.fp8kv_last_error().decode()
