@@ -84,6 +84,7 @@ def _load():
     lib.fo_e8m0_value.restype = D
     lib.fo_mxfp4_encode_group.argtypes = [P, P, P]
     lib.fo_index_keys_mxfp4.argtypes = [P, I64, I64, I64, P, I64, P, I64]
+    lib.fo_index_keys_pool.argtypes = [P, I64, I64, I64, I64, P]
     lib.fo_index_score.argtypes = [I, P, I64, I64, I64, P, I64, I64, I64,
                                    P, I64, I64, P, I64, I64,
                                    I64, I64, I64, I64, I64, P]
@@ -313,6 +314,19 @@ def index_keys_e4m3(keys_bits, threads: int = 1):
     """bf16 bits [N, D] -> (E4M3 codes uint8 [N, D], fp32 scales [N]): the
     per-row quantizer of the KV cache applied to the keys."""
     return quantize_rows_bf16(keys_bits, E4M3, threads)
+
+
+def index_keys_pool(raw_bits, g0, g1):
+    """Compressed keys g0 .. g1-1 (float64 [g1 - g0, D]) of one request's
+    raw bf16 keys [L, D] (bits): the mean of each group of 4 consecutive
+    raw keys, L2-normalized (0 for an all-zero mean)."""
+    r = np.asarray(raw_bits)
+    assert r.dtype == np.uint16 and r.ndim == 2 and r.strides[1] == 2
+    L, D = r.shape
+    assert 0 <= g0 <= g1 and 4 * g1 <= L
+    out = np.empty((g1 - g0, D), np.float64)
+    _load().fo_index_keys_pool(_ptr(r), r.strides[0] // 2, D, g0, g1, _ptr(out))
+    return out
 
 
 def index_score(q_bits, w, key_format, codes, scales):

@@ -147,3 +147,28 @@ void fo_index_score(int key_format, const uint16_t* q, int64_t qb, int64_t qr, i
             }
     }
 }
+
+/* Index-key builder ([ATOM] description, compressed-index bullet: the raw
+ * index keys stay BF16 and are mean-pooled before normalization; a pooling
+ * group can straddle a prefill chunk). Compressed key g of a request is
+ *     m[d] = (r[4g][d] + r[4g+1][d] + r[4g+2][d] + r[4g+3][d]) / 4
+ *     k[d] = m[d] / ||m||_2            (k = 0 when m = 0)
+ * evaluated in double for groups g0 .. g1-1 of raw keys r (bf16 bits, row
+ * stride rs elements); out[(g - g0) * d + i] = k[i]. Which group a key
+ * belongs to depends only on its position, never on the chunk it arrived
+ * in. */
+void fo_index_keys_pool(const uint16_t* raw, int64_t rs, int64_t d, int64_t g0,
+                        int64_t g1, double* out) {
+    for (int64_t g = g0; g < g1; ++g) {
+        double* k = out + (g - g0) * d;
+        double ss = 0.0;
+        for (int64_t i = 0; i < d; ++i) {
+            double s = 0.0;
+            for (int t = 0; t < 4; ++t) s += bf16_value(raw[(4 * g + t) * rs + i]);
+            k[i] = s / 4.0;
+            ss += k[i] * k[i];
+        }
+        const double n = sqrt(ss);
+        for (int64_t i = 0; i < d; ++i) k[i] = n > 0.0 ? k[i] / n : 0.0;
+    }
+}

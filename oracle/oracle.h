@@ -98,6 +98,11 @@ void fo_paged_decode_attn(
     int64_t block_size, double softmax_scale, int64_t partition_tokens,
     const int64_t* rows_sel, int64_t n_rows_sel, double* out);
 
+/* The same attention over selected blocks: block_tables rows list each
+ * request's selected blocks in position order; block_valid[b][i] counts the
+ * keys of the i-th selected block from its start (0 .. block_size).
+ * Virtual position j = i * block_size + o is a key iff o < block_valid[b][i];
+ * row r sees virtual positions 0 .. context_lens[b] - R + r. */
 void fo_sparse_decode_attn(
     int fmt,
     const uint16_t* q, int64_t q_stride_b, int64_t q_stride_row,
@@ -125,6 +130,8 @@ double fo_e8m0_value(unsigned code);                 /* 2^(code - 127)        */
 void   fo_mxfp4_encode_group(const float* x, uint8_t* packed, uint8_t* exp_code);
 void   fo_index_keys_mxfp4(const uint16_t* keys, int64_t n, int64_t d, int64_t ks,
                            uint8_t* packed, int64_t ps, uint8_t* exps, int64_t es);
+void   fo_index_keys_pool(const uint16_t* raw, int64_t rs, int64_t d, int64_t g0,
+                          int64_t g1, double* out);
 void   fo_index_score(int key_format, const uint16_t* q, int64_t qb, int64_t qr, int64_t qh,
                       const float* w, int64_t wb, int64_t wr, int64_t wh,
                       const void* codes, int64_t cb, int64_t cs,

@@ -243,3 +243,54 @@ def test_scorer_relu_linearity_and_permutation():
     wc = w.clone()
     wc[:, :, 1] += 1.0
     assert np.all(oracle.index_score(bits(qn), wc.numpy(), fmt, cpos, spos) >= sa)
+
+
+# ---------------------------------------------------------------- key builder
+def pool_torch(raw_bits, g0, g1):
+    x = torch.from_numpy(raw_bits.astype(np.int32) << 16).view(torch.float32).double()
+    m = x[4 * g0:4 * g1].reshape(g1 - g0, 4, -1).mean(dim=1)
+    return torch.nn.functional.normalize(m, dim=1).numpy()
+
+
+def bf16_bits_of(x):
+    return torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_pooling_matches_torch_mean_and_normalize():
+    g = torch.Generator().manual_seed(3)
+    raw = bf16_bits_of(torch.randn((4 * 37, 128), generator=g).numpy())
+    got = oracle.index_keys_pool(raw, 0, 37)
+    assert np.abs(got - pool_torch(raw, 0, 37)).max() < 1e-15
+    assert np.allclose(np.linalg.norm(got, axis=1), 1.0, atol=1e-15)
+
+
+def test_pooling_closed_forms():
+    x = np.zeros((8, 128), np.float32)
+    x[0:4, 5] = 3.0
+    x[0:4, 9] = -4.0                     # four identical keys -> (0.6, -0.8)
+    x[4:8] = 0.0                         # an all-zero group -> 0
+    got = oracle.index_keys_pool(bf16_bits_of(x), 0, 2)
+    want = np.zeros((2, 128))
+    want[0, 5], want[0, 9] = 0.6, -0.8
+    assert np.abs(got - want).max() < 1e-15
+    # scaling every raw key by 2 changes nothing
+    g = torch.Generator().manual_seed(4)
+    r = torch.randn((16, 128), generator=g).numpy()
+    a = oracle.index_keys_pool(bf16_bits_of(r), 0, 4)
+    b = oracle.index_keys_pool(bf16_bits_of(2 * r), 0, 4)
+    assert np.array_equal(a, b)
+
+
+def test_groups_follow_positions_not_chunks():
+    """A group straddling two prefill chunks is the group of its positions:
+    building [0, 5) and [5, 9) equals building [0, 9)."""
+    g = torch.Generator().manual_seed(5)
+    raw = bf16_bits_of(torch.randn((36, 128), generator=g).numpy())
+    whole = oracle.index_keys_pool(raw, 0, 9)
+    parts = np.concatenate([oracle.index_keys_pool(raw, 0, 5), oracle.index_keys_pool(raw, 5, 9)])
+    assert np.array_equal(whole, parts)
+    # a group's value depends on its four rows only
+    raw2 = raw.copy()
+    raw2[20:24] = bf16_bits_of(np.full((4, 128), 7.0, np.float32))
+    diff = np.abs(oracle.index_keys_pool(raw2, 0, 9) - whole).max(axis=1)
+    assert np.all(diff[[0, 1, 2, 3, 4, 6, 7, 8]] == 0) and diff[5] > 0
