@@ -534,6 +534,23 @@ def index_scorer(torch, fk, synth, dev, stream, reps=20):
         del codes, scales
     del case, out
     torch.cuda.empty_cache()
+    # key builder: 4 raw bf16 keys -> one compressed key (mean, L2 norm, encode)
+    raw = synth.normal_bf16((B, 4 * N, 128), synth.gen(5, dev), device=dev)
+    for name, fmt, kbytes in (("mxfp4", fk.KEYS_MXFP4, 64 + 4),
+                              ("e4m3", fk.KEYS_E4M3, 128 + 4)):
+        codes = torch.empty((B, N, 64 if fmt == fk.KEYS_MXFP4 else 128),
+                            dtype=torch.uint8, device=dev)
+        scales = (torch.empty((B, N, 4), dtype=torch.uint8, device=dev)
+                  if fmt == fk.KEYS_MXFP4 else torch.empty((B, N), device=dev))
+        ms = time_events(lambda: fk.index_keys_build(raw, 0, N, fmt, codes, scales),
+                         reps, stream)
+        avg = sum(ms) / len(ms)
+        res[f"index_keys_build_{name}_us"] = round(avg * 1e3, 1)
+        res[f"index_keys_build_{name}_GBps"] = round(
+            B * N * (4 * 256 + kbytes) / (avg * 1e-3) / 1e9, 1)
+        del codes, scales
+    del raw
+    torch.cuda.empty_cache()
     return res
 
 

@@ -27,6 +27,7 @@ DTYPE_FP32 = 3
 
 KEYS_MXFP4 = 0
 KEYS_E4M3 = 1
+KEYS_BF16 = 2
 
 _TORCH_DTYPE = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_FP16,
                 torch.float32: DTYPE_FP32}
@@ -82,6 +83,9 @@ def lib():
     L.fp8kv_index_keys_quantize.argtypes = [P, I64, I64, I32, I32, P, I64, P,
                                             I64, P]
     L.fp8kv_index_keys_quantize.restype = ctypes.c_int
+    L.fp8kv_index_keys_build.argtypes = [P, I64, I64, I32, I64, I64, I32, I32,
+                                         P, I64, I64, P, I64, I64, P]
+    L.fp8kv_index_keys_build.restype = ctypes.c_int
     L.fp8kv_index_score_mxfp4.argtypes = [P, I64, I64, I64, I32, P, I64, I64,
                                           I64, I32, P, I64, I64, P, I64, I64,
                                           I32, I32, I32, I32, I32, I32, P,
@@ -360,6 +364,43 @@ def index_keys_quantize(keys: torch.Tensor, key_format: int, codes=None,
         cf.data_ptr(), cf.stride(0), sf.data_ptr(), sf.stride(0),
         _stream(keys.device)))
     return codes, scales
+
+
+def index_keys_build(raw: torch.Tensor, g0: int, g1: int, key_format: int,
+                     codes: torch.Tensor, scales=None) -> None:
+    """Compressed keys g0 .. g1-1 of every request from raw bf16 index keys
+    raw [B, L, 128] (4*g1 <= L): mean of 4, L2-normalized, rounded to bf16,
+    stored in key_format into codes [B, N, 64 | 128 | 256 bytes] (and
+    scales [B, N, 4] uint8 or [B, N] fp32) at rows g0 .. g1-1."""
+    _dev(raw, codes)
+    if raw.dim() != 3 or raw.dtype != torch.bfloat16 or raw.shape[2] != 128 or \
+            raw.stride(2) != 1:
+        raise ValueError("raw must be bf16 [B, L, 128], contiguous last dim")
+    B, L, _ = raw.shape
+    if not (0 <= g0 <= g1 and 4 * g1 <= L):
+        raise ValueError("need 0 <= g0 <= g1 and 4 * g1 <= L")
+    nbytes = {KEYS_MXFP4: 64, KEYS_E4M3: 128, KEYS_BF16: 256}[key_format]
+    if codes.dim() != 3 or codes.dtype != torch.uint8 or codes.shape[0] != B or \
+            codes.shape[1] < g1 or codes.shape[2] != nbytes or codes.stride(2) != 1:
+        raise ValueError(f"codes must be uint8 [B, >= g1, {nbytes}]")
+    if key_format == KEYS_BF16:
+        sp, s0, s1 = None, 0, 0
+    else:
+        if scales is None:
+            raise ValueError("scales are required for quantized keys")
+        _dev(scales)
+        if key_format == KEYS_MXFP4 and (scales.dtype != torch.uint8 or scales.dim() != 3
+                                         or scales.shape[2] != 4 or scales.stride(2) != 1):
+            raise ValueError("MXFP4 exponents must be uint8 [B, N, 4]")
+        if key_format == KEYS_E4M3 and (scales.dtype != torch.float32 or scales.dim() != 2):
+            raise ValueError("E4M3 key scales must be fp32 [B, N]")
+        if scales.shape[0] != B or scales.shape[1] < g1:
+            raise ValueError("scales do not cover the keys")
+        sp, s0, s1 = scales.data_ptr(), scales.stride(0), scales.stride(1)
+    _check(lib().fp8kv_index_keys_build(
+        raw.data_ptr(), raw.stride(0), raw.stride(1), B, int(g0), int(g1), 128,
+        int(key_format), codes.data_ptr(), codes.stride(0), codes.stride(1),
+        sp, s0, s1, _stream(raw.device)))
 
 
 def index_score_mxfp4(q: torch.Tensor, w: torch.Tensor, key_format: int,

@@ -495,6 +495,50 @@ int fp8kv_index_keys_quantize(
                     "index_keys_quantize");
 }
 
+int fp8kv_index_keys_build(
+    const void* raw, int64_t raw_stride_b, int64_t raw_stride_tok, int32_t batch,
+    int64_t g0, int64_t g1, int32_t head_dim, int32_t key_format, uint8_t* codes,
+    int64_t code_stride_b, int64_t code_stride_key, void* scales,
+    int64_t scale_stride_b, int64_t scale_stride_key, void* stream) {
+    if (head_dim != fp8kv::kIndexDim)
+        return fail(FP8KV_E_UNSUPPORTED, "index keys: head_dim %d, only 128", head_dim);
+    if (key_format != FP8KV_KEYS_MXFP4 && key_format != FP8KV_KEYS_E4M3 &&
+        key_format != FP8KV_KEYS_BF16)
+        return fail(FP8KV_E_UNSUPPORTED, "key_format %d", key_format);
+    if (batch < 0 || batch > 65535 || g0 < 0 || g1 < g0 || g1 - g0 > (INT64_C(1) << 36))
+        return fail(FP8KV_E_SHAPE, "batch %d, groups [%lld, %lld)", batch, (long long)g0,
+                    (long long)g1);
+    const bool bf16 = key_format == FP8KV_KEYS_BF16;
+    if (!raw || !codes || (!scales && !bf16))
+        return fail(FP8KV_E_NULL, "index_keys_build: a required pointer is NULL");
+    if (raw_stride_b < 0 || raw_stride_tok < 0 || code_stride_b < 0 || code_stride_key < 0 ||
+        scale_stride_b < 0 || scale_stride_key < 0)
+        return fail(FP8KV_E_STRIDE, "index_keys_build: negative stride");
+    if (!aligned(raw, 16) || raw_stride_b % 8 || raw_stride_tok % 8)
+        return fail(FP8KV_E_ALIGN, "raw key rows must start on 16-byte boundaries");
+    const int cal = bf16 ? 16 : key_format == FP8KV_KEYS_E4M3 ? 8 : 4;
+    if (!aligned(codes, cal) || code_stride_b % cal || code_stride_key % cal)
+        return fail(FP8KV_E_ALIGN, "code rows must start on %d-byte boundaries", cal);
+    if (key_format == FP8KV_KEYS_E4M3 && !aligned(scales, 4))
+        return fail(FP8KV_E_ALIGN, "fp32 key scales misaligned");
+    if (batch == 0 || g1 == g0) return ok();
+    fp8kv::IndexBuildParams p;
+    p.raw = static_cast<const uint16_t*>(raw);
+    p.raw_stride_b = raw_stride_b;
+    p.raw_stride_tok = raw_stride_tok;
+    p.g0 = g0;
+    p.g1 = g1;
+    p.codes = codes;
+    p.code_stride_b = code_stride_b;
+    p.code_stride_key = code_stride_key;
+    p.scales = scales;
+    p.scale_stride_b = scale_stride_b;
+    p.scale_stride_key = scale_stride_key;
+    p.batch = batch;
+    return launched(fp8kv::launch_index_keys_build(p, key_format, (hipStream_t)stream),
+                    "index_keys_build");
+}
+
 int fp8kv_index_score_mxfp4(
     const void* q, int64_t q_stride_b, int64_t q_stride_row,
     int64_t q_stride_head, int32_t q_dtype,

@@ -76,6 +76,7 @@ hipError_t launch_decode_merge(const MergeParams& p, int head_dim,
 // Compressed index keys (head_dim 128).
 constexpr int kKeysMXFP4 = 0;
 constexpr int kKeysE4M3 = 1;
+constexpr int kKeysBF16 = 2;           // the builder's unquantized output
 constexpr int kIndexDim = 128;
 constexpr int kIndexMaxHeads = 16;     // MFMA M dimension
 constexpr int kIndexRowsPerWave = 8;
@@ -111,7 +112,19 @@ struct IndexScoreParams {
     int32_t out_bytes;         // per request: (rows - 1) * out_stride_row * 4 + num_keys * 4
 };
 
+struct IndexBuildParams {
+    const uint16_t* raw;       // bf16 bits [B, L, 128]: raw index keys by position
+    int64_t raw_stride_b, raw_stride_tok;
+    int64_t g0, g1;            // compressed keys g0 .. g1-1 (raw keys 4*g0 .. 4*g1-1)
+    uint8_t* codes;            // [B, N, bytes]: strides in bytes
+    int64_t code_stride_b, code_stride_key;
+    void* scales;              // [B, N(, 4)]: strides in elements
+    int64_t scale_stride_b, scale_stride_key;
+    int32_t batch;
+};
+
 hipError_t launch_index_keys(const IndexKeysParams& p, int key_format, hipStream_t stream);
+hipError_t launch_index_keys_build(const IndexBuildParams& p, int key_format, hipStream_t stream);
 hipError_t launch_index_score(const IndexScoreParams& p, int key_format, hipStream_t stream);
 
 }  // namespace fp8kv

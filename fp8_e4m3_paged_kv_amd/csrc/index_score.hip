@@ -35,6 +35,7 @@ namespace fp8kv {
 namespace {
 
 constexpr int kScoreWaves = 4;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kStoreNT = 2;         // cache policy of the score stores: non-temporal
 
 // E2M1 code of |v| (v = x / 2^e, so |v| <= 6): nearest of
@@ -48,11 +49,68 @@ __device__ __forceinline__ uint32_t e2m1_code(float a) {
 }
 
 // ---------------------------------------------------------------- keys
+// Encode one key held by a 16-lane DPP row: lane li holds dims 8li .. 8li+7
+// as floats (each exactly a bf16 value). E4M3: the KV row quantizer (row
+// amax, IEEE amax/448, correctly rounded quotients, RNE + saturating
+// encode), codes at code_row + 8li, the scale by lane 0. MXFP4: a group of
+// 32 dims is one quad of lanes; 4 code bytes per lane at code_row + 4li,
+// the group's E8M0 code by the quad's first lane. BF16: the values
+// themselves, 16 bytes per lane. Nothing is stored when `store` is false.
+template <int FMT>
+__device__ __forceinline__ void encode_key(const float (&x)[8], int li, bool store,
+                                           uint8_t* code_row, void* scale_row) {
+#pragma clang fp contract(off)
+    if (FMT == kKeysBF16) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = (__float_as_uint(x[2 * i]) >> 16) | (__float_as_uint(x[2 * i + 1]) & 0xFFFF0000u);
+        if (store) *reinterpret_cast<uint4*>(code_row + li * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+        return;
+    }
+    uint32_t amax_bits = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax_bits = max(amax_bits, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+    if (FMT == kKeysE4M3) {
+        const float amax = __uint_as_float(row16_max_u32(amax_bits));
+        const float scale = amax / kE4M3Max;         // IEEE binary32 division
+        float qv[8];
+        row_quotients(x, scale, qv);
+        const uint32_t lo = e4m3x4_encode(qv[0], qv[1], qv[2], qv[3]);
+        const uint32_t hi = e4m3x4_encode(qv[4], qv[5], qv[6], qv[7]);
+        if (store) {
+            *reinterpret_cast<uint2*>(code_row + li * 8) = make_uint2(lo, hi);
+            if (li == 0) *static_cast<float*>(scale_row) = scale;
+        }
+    } else {
+        amax_bits = max(amax_bits, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax_bits, 0xB1, 0xF, 0xF, false));
+        amax_bits = max(amax_bits, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax_bits, 0x4E, 0xF, 0xF, false));
+        const float amax = __uint_as_float(amax_bits);
+        int e = 0;
+        if (amax > 0.0f) {
+            int ex;
+            const float mant = frexpf(amax, &ex);       // amax = mant * 2^ex, mant in [.5, 1)
+            e = mant <= 0.75f ? ex - 3 : ex - 2;         // smallest e with amax <= 6 * 2^e
+            e = max(e, -127);
+        }
+        uint32_t packed = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float v = ldexpf(x[i], -e);             // exact wherever a code boundary lies
+            const uint32_t c = e2m1_code(fabsf(v)) | ((__float_as_uint(x[i]) >> 28) & 8u);
+            packed |= c << (4 * i);
+        }
+        if (store) {
+            *reinterpret_cast<uint32_t*>(code_row + li * 4) = packed;
+            if ((li & 3) == 0) static_cast<uint8_t*>(scale_row)[li >> 2] = (uint8_t)(e + 127);
+        }
+    }
+}
+
 // One 16-lane DPP row per key (8 bf16 per lane), 4 keys per wave step, two
 // steps, four waves: 32 keys per workgroup.
 template <int FMT>
 __global__ __launch_bounds__(256) void index_keys_kernel(IndexKeysParams p) {
-#pragma clang fp contract(off)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane >> 4;
@@ -74,45 +132,89 @@ __global__ __launch_bounds__(256) void index_keys_kernel(IndexKeysParams p) {
             x[2 * i] = bf16_lo(wds[i]);
             x[2 * i + 1] = bf16_hi(wds[i]);
         }
+        const int64_t k = min(key, p.num_keys - 1);
+        encode_key<FMT>(x, li, key < p.num_keys, p.codes + k * p.code_stride,
+                        FMT == kKeysE4M3
+                            ? (void*)(static_cast<float*>(p.scales) + k * p.scale_stride)
+                            : (void*)(static_cast<uint8_t*>(p.scales) + k * p.scale_stride));
+    }
+}
+
+// Sum over the 16 lanes of a DPP row.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+    return v;
+}
+
+// Index-key builder: compressed key g of request b is the mean of raw keys
+// 4g .. 4g+3, L2-normalized and rounded to bf16, then encoded as above.
+// One 16-lane row per compressed key (its lanes read 8 dims of each of the
+// 4 raw keys), 32 keys per workgroup; grid y = request.
+template <int FMT>
+__global__ __launch_bounds__(256) void index_keys_build_kernel(IndexBuildParams p) {
+#pragma clang fp contract(off)
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int sub = lane >> 4;
+    const int li = lane & 15;
+    const int b = blockIdx.y;
+    const int64_t gi0 = (int64_t)blockIdx.x * 32 + wave * 8;
+    const int64_t ng = p.g1 - p.g0;
+    const uint16_t* raw_b = p.raw + (int64_t)b * p.raw_stride_b;
+    uint4 raw[2][4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int64_t g = p.g0 + min(gi0 + 4 * s + sub, ng - 1);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                raw_b + (4 * g + t) * p.raw_stride_tok + li * 8));
+            raw[s][t] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int64_t gi = gi0 + 4 * s + sub;
+        float m[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w0 = (&raw[s][0].x)[i], w1 = (&raw[s][1].x)[i];
+            const uint32_t w2 = (&raw[s][2].x)[i], w3 = (&raw[s][3].x)[i];
+            m[2 * i] = ((bf16_lo(w0) + bf16_lo(w1)) + (bf16_lo(w2) + bf16_lo(w3))) * 0.25f;
+            m[2 * i + 1] = ((bf16_hi(w0) + bf16_hi(w1)) + (bf16_hi(w2) + bf16_hi(w3))) * 0.25f;
+        }
+        // scale the mean by a power of two that brings its largest element
+        // to [0.5, 1) (exact), so the sum of squares neither underflows nor
+        // overflows; the normalized key does not depend on the scale
         uint32_t amax_bits = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax_bits = max(amax_bits, __float_as_uint(x[i]) & 0x7FFFFFFFu);
-        if (FMT == kKeysE4M3) {
-            const float amax = __uint_as_float(row16_max_u32(amax_bits));
-            const float scale = amax / kE4M3Max;         // IEEE binary32 division
-            float qv[8];
-            row_quotients(x, scale, qv);
-            const uint32_t lo = e4m3x4_encode(qv[0], qv[1], qv[2], qv[3]);
-            const uint32_t hi = e4m3x4_encode(qv[4], qv[5], qv[6], qv[7]);
-            if (key < p.num_keys) {
-                *reinterpret_cast<uint2*>(p.codes + key * p.code_stride + li * 8) = make_uint2(lo, hi);
-                if (li == 0) static_cast<float*>(p.scales)[key * p.scale_stride] = scale;
-            }
-        } else {
-            // a group of 32 dims is one quad of lanes
-            amax_bits = max(amax_bits, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax_bits, 0xB1, 0xF, 0xF, false));
-            amax_bits = max(amax_bits, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax_bits, 0x4E, 0xF, 0xF, false));
-            const float amax = __uint_as_float(amax_bits);
-            int e = 0;
-            if (amax > 0.0f) {
-                int ex;
-                const float mant = frexpf(amax, &ex);       // amax = mant * 2^ex, mant in [.5, 1)
-                e = mant <= 0.75f ? ex - 3 : ex - 2;         // smallest e with amax <= 6 * 2^e
-                e = max(e, -127);
-            }
-            uint32_t packed = 0;
+        for (int i = 0; i < 8; ++i) amax_bits = max(amax_bits, __float_as_uint(m[i]) & 0x7FFFFFFFu);
+        int ex = 0;
+        frexpf(__uint_as_float(row16_max_u32(amax_bits)), &ex);
+        float ss = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float v = ldexpf(x[i], -e);             // exact wherever a code boundary lies
-                const uint32_t c = e2m1_code(fabsf(v)) | ((__float_as_uint(x[i]) >> 28) & 8u);
-                packed |= c << (4 * i);
-            }
-            if (key < p.num_keys) {
-                *reinterpret_cast<uint32_t*>(p.codes + key * p.code_stride + li * 4) = packed;
-                if ((li & 3) == 0)
-                    static_cast<uint8_t*>(p.scales)[key * p.scale_stride + (li >> 2)] = (uint8_t)(e + 127);
-            }
+        for (int i = 0; i < 8; ++i) {
+            m[i] = ldexpf(m[i], -ex);
+            ss = __builtin_fmaf(m[i], m[i], ss);
         }
+        const float n = __builtin_sqrtf(row16_sum(ss));
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float c = n > 0.f ? m[i] / n : 0.f;
+            x[i] = (float)(__bf16)c;                      // round to nearest even
+        }
+        const int64_t g = p.g0 + min(gi, ng - 1);
+        uint8_t* code_row = p.codes + (int64_t)b * p.code_stride_b + g * p.code_stride_key;
+        void* scale_row = FMT == kKeysE4M3
+                              ? (void*)(static_cast<float*>(p.scales) + (int64_t)b * p.scale_stride_b +
+                                        g * p.scale_stride_key)
+                              : (void*)(static_cast<uint8_t*>(p.scales) + (int64_t)b * p.scale_stride_b +
+                                        g * p.scale_stride_key);
+        encode_key<FMT>(x, li, gi < ng, code_row, scale_row);
     }
 }
 
@@ -357,6 +459,19 @@ hipError_t launch_index_keys(const IndexKeysParams& p, int key_format, hipStream
         hipLaunchKernelGGL((index_keys_kernel<kKeysE4M3>), grid, block, 0, stream, p);
     else
         hipLaunchKernelGGL((index_keys_kernel<kKeysMXFP4>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_index_keys_build(const IndexBuildParams& p, int key_format, hipStream_t stream) {
+    const int64_t blocks = (p.g1 - p.g0 + 31) / 32;
+    if (blocks > INT32_MAX || p.batch > 65535) return hipErrorInvalidValue;
+    dim3 grid((unsigned)blocks, (unsigned)p.batch), block(256);
+    if (key_format == kKeysE4M3)
+        hipLaunchKernelGGL((index_keys_build_kernel<kKeysE4M3>), grid, block, 0, stream, p);
+    else if (key_format == kKeysMXFP4)
+        hipLaunchKernelGGL((index_keys_build_kernel<kKeysMXFP4>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((index_keys_build_kernel<kKeysBF16>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FP8KV_ABI_VERSION 4
+#define FP8KV_ABI_VERSION 5
 
 typedef enum fp8kv_status {
     FP8KV_OK = 0,
@@ -312,7 +312,8 @@ int fp8kv_sparse_decode_partials(
  */
 typedef enum fp8kv_key_format {
     FP8KV_KEYS_MXFP4 = 0,   /* packed E2M1 pairs + one E8M0 exponent per 32 dims */
-    FP8KV_KEYS_E4M3 = 1     /* E4M3 codes + one fp32 scale per key              */
+    FP8KV_KEYS_E4M3 = 1,    /* E4M3 codes + one fp32 scale per key              */
+    FP8KV_KEYS_BF16 = 2     /* unquantized bf16 keys (fp8kv_index_keys_build)   */
 } fp8kv_key_format;
 
 /*
@@ -339,6 +340,37 @@ int fp8kv_index_keys_quantize(
     const void* keys, int64_t key_stride, int64_t num_keys, int32_t head_dim,
     int32_t key_format, uint8_t* codes, int64_t code_stride,
     void* scales, int64_t scale_stride, void* stream);
+
+/*
+ * fp8kv_index_keys_build -- build compressed index keys from raw bf16 index
+ * keys ([ATOM] description, compressed-index bullet: the raw index keys stay
+ * BF16, are mean-pooled before normalization, and a pooling group can
+ * straddle a prefill chunk). For every request b < batch and compressed key
+ * g in [g0, g1):
+ *   m[d] = (r[4g][d] + r[4g+1][d] + r[4g+2][d] + r[4g+3][d]) / 4      (fp32)
+ *   k[d] = bf16_rne(m[d] / ||m||_2)            (0 when m = 0)
+ * then k is stored in key_format exactly as fp8kv_index_keys_quantize would
+ * store the bf16 key k (FP8KV_KEYS_BF16: the 128 bf16 values themselves).
+ * Groups follow positions, not chunks: after a chunk ends at raw position
+ * L, call with g1 = L / 4, and build the straddling group in the next call
+ * once its fourth raw key exists.
+ * raw     (device) bf16, raw key t of request b at b*raw_stride_b +
+ *         t*raw_stride_tok (elements); 16-byte aligned rows.
+ * codes   (device) key g of request b at b*code_stride_b + g*code_stride_key
+ *         (bytes): 64 (MXFP4), 128 (E4M3) or 256 (BF16) bytes; rows aligned
+ *         to 4 / 8 / 16 bytes.
+ * scales  (device) E4M3: fp32 at b*scale_stride_b + g*scale_stride_key;
+ *         MXFP4: 4 E8M0 bytes from there; unused (may be NULL) for BF16.
+ * The fp32 mean and norm are accurate to a few fp32 ulps, so k is the
+ * correctly rounded bf16 of the exact normalized mean except within about
+ * 2^-16 (relative) of a rounding midpoint.
+ * Errors: E_NULL, E_SHAPE, E_STRIDE, E_ALIGN, E_UNSUPPORTED, E_LAUNCH.
+ */
+int fp8kv_index_keys_build(
+    const void* raw, int64_t raw_stride_b, int64_t raw_stride_tok, int32_t batch,
+    int64_t g0, int64_t g1, int32_t head_dim, int32_t key_format,
+    uint8_t* codes, int64_t code_stride_b, int64_t code_stride_key,
+    void* scales, int64_t scale_stride_b, int64_t scale_stride_key, void* stream);
 
 /*
  * fp8kv_index_score_mxfp4 -- the decode-sized index scorer, over MXFP4 or

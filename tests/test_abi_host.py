@@ -285,3 +285,34 @@ def sdec(L, fn="fp8kv_sparse_decode_attn_fp8", bv=A, bvs=2048, **kw):
 def test_sparse_decode_refusals(L, fn, kw, status):
     assert sdec(L, fn=fn, **kw) == status
     assert L.fp8kv_last_error().decode()
+
+
+def ikb(L, **kw):
+    a = dict(raw=A, rsb=1 << 25, rst=128, B=8, g0=0, g1=65536, D=128, fmt=MXFP4,
+             codes=A, csb=1 << 22, csk=64, scales=A, ssb=1 << 18, ssk=4)
+    a.update(kw)
+    return L.fp8kv_index_keys_build(a["raw"], a["rsb"], a["rst"], a["B"], a["g0"],
+                                    a["g1"], a["D"], a["fmt"], a["codes"], a["csb"],
+                                    a["csk"], a["scales"], a["ssb"], a["ssk"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=64), E_UNSUPPORTED),
+    (dict(fmt=3), E_UNSUPPORTED),
+    (dict(g1=-1), E_SHAPE),
+    (dict(g0=5, g1=4), E_SHAPE),
+    (dict(B=-1), E_SHAPE),
+    (dict(raw=0), E_NULL),
+    (dict(scales=0), E_NULL),
+    (dict(fmt=2, scales=0, csk=256, g0=3, g1=3), OK),   # BF16 keys need no scales
+    (dict(rst=-128), E_STRIDE),
+    (dict(raw=A + 8), E_ALIGN),
+    (dict(rst=132), E_ALIGN),
+    (dict(fmt=2, csk=264), E_ALIGN),        # BF16 rows are 16-byte aligned
+    (dict(fmt=1, csk=132), E_ALIGN),
+    (dict(g0=7, g1=7), OK),
+])
+def test_index_keys_build_refusals(L, kw, status):
+    assert ikb(L, **kw) == status
+    if status != OK:
+        assert L.fp8kv_last_error().decode()

@@ -278,3 +278,101 @@ def test_index_workload_full_size_sampled(fmt):
         sub_s = scales[b:b + 1, keys.to(DEV)]
         got = out[b:b + 1][:, rows.to(DEV)][:, :, keys.to(DEV)]
         check_scores(got, sub_q, sub_w, fmt, sub_c, sub_s, f"full-size request {b}")
+
+
+# ---------------------------------------------------------------- key builder
+def build_keys(raw, g0, g1, fmt, N=None):
+    B = raw.shape[0]
+    N = g1 if N is None else N
+    nbytes = {MX: 64, E4: 128, fk.KEYS_BF16: 256}[fmt]
+    codes = torch.full((B, N, nbytes), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = (torch.full((B, N, 4), 0x5A, dtype=torch.uint8, device=DEV) if fmt == MX
+              else torch.full((B, N), -3.0, device=DEV) if fmt == E4 else None)
+    fk.index_keys_build(raw, g0, g1, fmt, codes, scales)
+    torch.cuda.synchronize()
+    return codes, scales
+
+
+def bf16_keys_of(codes):
+    """BF16-format builder output [B, N, 256 bytes] -> bf16 bits [B, N, 128]."""
+    return codes.cpu().numpy().view(np.uint16)
+
+
+def check_pooled(bits, raw, g0, g1, what):
+    """Every pooled key is the correctly rounded bf16 of the exact normalized
+    mean, or its neighbour when the exact value lies within 2^-16 (relative)
+    of a rounding midpoint (the fp32 mean and norm are accurate to a few
+    ulps)."""
+    got = oracle.bf16_to_f32(bits).astype(np.float64)
+    want = oracle.index_keys_pool(bf16_bits(raw), g0, g1)
+    mag = np.abs(want)
+    ulp = np.where(mag > 0, 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-300))) - 7), 0)
+    err = np.abs(got - want)
+    assert np.all(err <= 0.5 * ulp + 2.0 ** -16 * mag), what
+    rne = oracle.bf16_to_f32(bf16_bits(torch.from_numpy(want).to(torch.bfloat16)))
+    off = int((got != rne).sum())
+    log(f"  {what}: {off} of {got.size} values off the correctly rounded bf16")
+    assert off <= max(4, got.size // 10000)
+
+
+def test_builder_pools_and_normalizes():
+    g = synth.gen(60)
+    raw = synth.normal_bf16((2, 4 * 300 + 3, 128), g)
+    raw[0, 40:44] = 0                                        # an all-zero group
+    raw[1, 8:12] = synth.normal_bf16((4, 128), g, std=1e-30)  # tiny magnitudes
+    raw = raw.to(DEV)
+    codes, _ = build_keys(raw, 0, 300, fk.KEYS_BF16)
+    bits = bf16_keys_of(codes)
+    for b in range(2):
+        check_pooled(bits[b], raw[b].cpu(), 0, 300, f"request {b}")
+    assert np.all(bits[0, 10] == 0)
+
+
+@pytest.mark.parametrize("fmt", [MX, E4])
+def test_builder_codes_equal_the_encoding_of_its_bf16_keys(fmt):
+    raw = synth.normal_bf16((3, 4 * 257, 128), synth.gen(61)).to(DEV)
+    kb, _ = build_keys(raw, 0, 257, fk.KEYS_BF16)
+    codes, scales = build_keys(raw, 0, 257, fmt)
+    for b in range(3):
+        rc, rs = oracle_keys(torch.from_numpy(bf16_keys_of(kb)[b].view(np.int16)).view(torch.bfloat16), fmt)
+        assert np.array_equal(codes[b].cpu().numpy(), rc)
+        if fmt == MX:
+            assert np.array_equal(scales[b].cpu().numpy(), rs)
+        else:
+            assert np.array_equal(scales[b].cpu().numpy().view(np.uint32),
+                                  np.asarray(rs, np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", [MX, E4, fk.KEYS_BF16])
+def test_builder_chunked_equals_whole(fmt):
+    """Two calls [0, 77) and [77, 200) -- a raw chunk boundary inside group
+    77 -- write exactly what one call [0, 200) writes, and nothing else."""
+    raw = synth.normal_bf16((2, 4 * 200 + 1, 128), synth.gen(62)).to(DEV)
+    whole = build_keys(raw, 0, 200, fmt, N=210)
+    B = 2
+    nbytes = whole[0].shape[2]
+    codes = torch.full((B, 210, nbytes), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = (torch.full((B, 210, 4), 0x5A, dtype=torch.uint8, device=DEV) if fmt == MX
+              else torch.full((B, 210), -3.0, device=DEV) if fmt == E4 else None)
+    fk.index_keys_build(raw, 0, 77, fmt, codes, scales)
+    fk.index_keys_build(raw, 77, 200, fmt, codes, scales)
+    torch.cuda.synchronize()
+    assert torch.equal(codes, whole[0])
+    assert torch.all(codes[:, 200:] == 0x5A)
+    if scales is not None:
+        assert torch.equal(scales, whole[1])
+
+
+def test_builder_index_workload_full_size_sampled():
+    """8 requests x 262,144 raw keys -> 65,536 compressed keys each (the
+    index workload's key recipe), MXFP4; sampled keys checked."""
+    raw = synth.normal_bf16((8, 4 * 65536, 128), synth.gen(63, DEV), device=DEV)
+    kb, _ = build_keys(raw, 0, 65536, fk.KEYS_BF16)
+    codes, scales = build_keys(raw, 0, 65536, MX)
+    pick = torch.arange(0, 65536, 97)
+    for b in (0, 5):
+        sub = raw[b].view(65536, 4, 128)[pick.to(DEV)].reshape(-1, 128).cpu()
+        check_pooled(bf16_keys_of(kb)[b][pick.numpy()], sub, 0, pick.numel(), f"request {b}")
+        rc, rs = oracle_keys(torch.from_numpy(bf16_keys_of(kb)[b][pick.numpy()].view(np.int16)).view(torch.bfloat16), MX)
+        assert np.array_equal(codes[b][pick.to(DEV)].cpu().numpy(), rc)
+        assert np.array_equal(scales[b][pick.to(DEV)].cpu().numpy(), rs)
