@@ -52,8 +52,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the prefill-chunk, long-context and index extras")
-    ap.add_argument("--extras", default="prefill,longctx,sparse,index",
-                    help="comma list of the extras to run (prefill, longctx, sparse, index)")
+    ap.add_argument("--extras", default="prefill,longctx,sparse,prefill_attn,index",
+                    help="comma list of the extras to run (prefill, longctx, sparse, "
+                         "prefill_attn, index)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times "
                          "(the known-size reference for HBM byte counters)")
@@ -364,6 +365,8 @@ def main():
     if "sparse" in extras:
         result["also"].update(sparse_decode(torch, fk, synth, dev, stream, case, q, bt,
                                             k_cache, v_cache, k_plane, v_plane))
+    if "prefill_attn" in extras:
+        result["also"].update(prefill_attention(torch, fk, synth, dev, stream))
     if "index" in extras:
         result["also"].update(index_scorer(torch, fk, synth, dev, stream))
 
@@ -501,6 +504,47 @@ def sparse_decode(torch, fk, synth, dev, stream, case, q, bt, k_cache, v_cache,
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def prefill_attention(torch, fk, synth, dev, stream, reps=10):
+    """Chunked-prefill attention: a 4096-token chunk at the end of a
+    32,768-token request, Hq 32 / Hkv 8, D 128, bs 16. Useful work: for
+    every chunk token i (position P + i) and query head, P + i + 1 keys
+    at 4 * D flops each (QK^T and PV)."""
+    log("prefill attention (4096-token chunk on a 32,768-token request)...")
+    case = synth.prefill_attn_workload(seed=71, device=dev)
+    L = case.layout
+    H, D = case.num_kv_heads, case.head_dim
+    S = L.num_slots
+    k_cache = torch.empty((S, H, D), dtype=torch.uint8, device=dev)
+    v_cache = torch.empty_like(k_cache)
+    k_plane = torch.empty((H, S), dtype=torch.float32, device=dev)
+    v_plane = torch.empty_like(k_plane)
+    slots = L.token_slots.to(dev)
+    cache_build(torch, fk, case.k, case.v, slots, k_cache, v_cache, k_plane, v_plane, stream)
+    del case.k, case.v
+    q = case.q.to(dev)
+    B, C, Hq, _ = q.shape
+    ctx = int(L.context_lens[0])
+    P = ctx - C
+    ql = torch.full((B,), C, dtype=torch.int32, device=dev)
+    bt = L.block_tables.to(dev)
+    cl = L.context_lens.to(dev)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+
+    def run():
+        fk.prefill_attn_fp8(q, k_cache, v_cache, k_plane.t(), v_plane.t(), bt, cl, ql,
+                            num_kv_heads=H, block_size=L.block_size,
+                            softmax_scale=case.softmax_scale, max_context=ctx, out=out)
+    ms = time_events(run, reps, stream)
+    avg = sum(ms) / len(ms)
+    flops = (P * C + C * (C + 1) // 2) * Hq * 4 * D
+    tf = flops / (avg * 1e-3) / 1e12
+    del k_cache, v_cache, k_plane, v_plane, out
+    torch.cuda.empty_cache()
+    return {"prefill_attn_us": round(avg * 1e3, 1),
+            "prefill_attn_TFLOPs": round(tf, 1),
+            "prefill_attn_mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
 def index_scorer(torch, fk, synth, dev, stream, reps=20):

@@ -73,6 +73,11 @@ def lib():
     L.fp8kv_sparse_decode_attn_fp8.restype = ctypes.c_int
     L.fp8kv_sparse_decode_partials.argtypes = sdec + [P]
     L.fp8kv_sparse_decode_partials.restype = ctypes.c_int
+    L.fp8kv_prefill_attn_fp8.argtypes = [P, I64, I64, I64, I32, P, P, I64, I64,
+                                         P, P, I64, I64, I64, P, I64, P, P,
+                                         I32, I32, I32, I32, I32, I32, F, I32,
+                                         P, I64, I64, I64, I32, P]
+    L.fp8kv_prefill_attn_fp8.restype = ctypes.c_int
     L.fp8kv_paged_decode_merge.argtypes = [I32, I32, I32, I32, I32, I32, P,
                                            SZ, P, I64, I64, I64, I32, P]
     L.fp8kv_paged_decode_merge.restype = ctypes.c_int
@@ -316,6 +321,46 @@ def sparse_decode_partials(q, k_cache, v_cache, k_scale, v_scale, block_tables,
     _check(lib().fp8kv_sparse_decode_partials(*_sparse_args(args, block_valid),
                                               _stream(q.device)))
     return workspace
+
+
+def prefill_attn_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                     context_lens, q_lens, *, num_kv_heads, block_size,
+                     softmax_scale, max_context, out=None,
+                     out_dtype=torch.bfloat16):
+    """Chunked-prefill attention: q [B, max_q, Hq, D] bf16 holds each
+    request's last q_lens[b] tokens (already in the cache); token i attends
+    to the cached tokens 0 .. context_lens[b] - q_lens[b] + i. Returns out
+    [B, max_q, Hq, D] (rows i >= q_lens[b] are left untouched)."""
+    _dev(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, q_lens)
+    if q.dim() != 4 or q.stride(3) != 1 or q.dtype not in _TORCH_DTYPE:
+        raise ValueError("q must be [B, max_q, Hq, D] with contiguous head_dim")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or \
+            block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be int32 [B, max_blocks], rows contiguous")
+    for t in (context_lens, q_lens):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("context_lens and q_lens must be contiguous int32 [B]")
+    B, Q, Hq, D = q.shape
+    css, csh, S, H, Dc = _cache_strides(k_cache)
+    if _cache_strides(v_cache)[:2] != (css, csh) or H != num_kv_heads or Dc != D:
+        raise ValueError("cache geometry does not match q / num_kv_heads")
+    sss, ssh = _scale_strides(k_scale)
+    if _scale_strides(v_scale) != (sss, ssh):
+        raise ValueError("k_scale and v_scale must share strides")
+    if out is None:
+        out = torch.zeros(q.shape, dtype=out_dtype, device=q.device)
+    _dev(out)
+    if out.shape != q.shape or out.stride(3) != 1:
+        raise ValueError("out must be [B, max_q, Hq, D] with contiguous head_dim")
+    _check(lib().fp8kv_prefill_attn_fp8(
+        q.data_ptr(), q.stride(0), q.stride(1), q.stride(2), _TORCH_DTYPE[q.dtype],
+        k_cache.data_ptr(), v_cache.data_ptr(), css, csh, k_scale.data_ptr(),
+        v_scale.data_ptr(), sss, ssh, S, block_tables.data_ptr(),
+        block_tables.stride(0), context_lens.data_ptr(), q_lens.data_ptr(), B, Q,
+        Hq, num_kv_heads, D, block_size, float(softmax_scale), int(max_context),
+        out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
+        _TORCH_DTYPE[out.dtype], _stream(q.device)))
+    return out
 
 
 def paged_decode_merge(workspace, out, *, rows, num_q_heads, num_kv_heads,

@@ -461,6 +461,97 @@ int fp8kv_sparse_decode_attn_fp8(
         out_stride_head, out_dtype, stream);
 }
 
+int fp8kv_prefill_attn_fp8(
+    const void* q, int64_t q_stride_b, int64_t q_stride_tok, int64_t q_stride_head,
+    int32_t q_dtype, const uint8_t* k_cache, const uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head, const float* k_scale,
+    const float* v_scale, int64_t scale_stride_slot, int64_t scale_stride_head,
+    int64_t num_slots, const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, const int32_t* q_lens, int32_t batch, int32_t max_q,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    float softmax_scale, int32_t max_context, void* out, int64_t out_stride_b,
+    int64_t out_stride_tok, int64_t out_stride_head, int32_t out_dtype, void* stream) {
+    if (head_dim != 64 && head_dim != 128)
+        return fail(FP8KV_E_UNSUPPORTED, "head_dim %d: only 64 and 128 are supported", head_dim);
+    if (q_dtype != FP8KV_DTYPE_BF16)
+        return fail(FP8KV_E_UNSUPPORTED, "q_dtype %d: only BF16 queries", q_dtype);
+    int st = check_out_dtype(out_dtype);
+    if (st != FP8KV_OK) return st;
+    if (batch < 0 || max_q < 0 || max_context < 0 || num_q_heads < 1 || num_kv_heads < 1)
+        return fail(FP8KV_E_SHAPE, "batch %d, max_q %d, max_context %d, heads %d/%d", batch,
+                    max_q, max_context, num_q_heads, num_kv_heads);
+    if (num_q_heads % num_kv_heads != 0)
+        return fail(FP8KV_E_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                    num_q_heads, num_kv_heads);
+    const int32_t group = num_q_heads / num_kv_heads;
+    if (group > kMaxStackedRows || kMaxStackedRows % group != 0)
+        return fail(FP8KV_E_UNSUPPORTED, "GQA group %d: must divide %d", group, kMaxStackedRows);
+    if (block_size < 16 || block_size % 16 != 0)
+        return fail(FP8KV_E_UNSUPPORTED, "block_size %d: must be a positive multiple of 16", block_size);
+    if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables || !context_lens ||
+        !q_lens || !out)
+        return fail(FP8KV_E_NULL, "prefill: a required pointer is NULL");
+    if (q_stride_b < 0 || q_stride_tok < 0 || q_stride_head < 0 || cache_stride_slot < 0 ||
+        cache_stride_head < 0 || scale_stride_slot < 0 || scale_stride_head < 0 ||
+        block_table_stride < 0 || out_stride_b < 0 || out_stride_tok < 0 || out_stride_head < 0)
+        return fail(FP8KV_E_STRIDE, "prefill: negative stride");
+    if (!aligned(q, 16) || q_stride_b % 8 || q_stride_tok % 8 || q_stride_head % 8)
+        return fail(FP8KV_E_ALIGN, "q rows must start on 16-byte boundaries");
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || cache_stride_slot % 16 ||
+        cache_stride_head % 16)
+        return fail(FP8KV_E_ALIGN, "cache rows must start on 16-byte boundaries");
+    const int oal = out_dtype == FP8KV_DTYPE_FP32 ? 16 : 8;     // vector row stores
+    const int oel = out_dtype == FP8KV_DTYPE_FP32 ? 4 : 2;
+    if (!aligned(out, oal) || (out_stride_b * oel) % oal || (out_stride_tok * oel) % oal ||
+        (out_stride_head * oel) % oal)
+        return fail(FP8KV_E_ALIGN, "out rows must start on %d-byte boundaries", oal);
+    if (!aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(block_tables, 4) ||
+        !aligned(context_lens, 4) || !aligned(q_lens, 4))
+        return fail(FP8KV_E_ALIGN, "scale planes or tables misaligned");
+    const int64_t num_blocks = num_slots / block_size;
+    if (batch > 0 && max_context > 0 && num_blocks < 1)
+        return fail(FP8KV_E_SHAPE, "num_slots %lld holds no block of %d", (long long)num_slots,
+                    block_size);
+    if (num_blocks > INT32_MAX)
+        return fail(FP8KV_E_SHAPE, "num_slots / block_size exceeds int32 block ids");
+    if (batch == 0 || max_q == 0) return ok();
+    fp8kv::PrefillParams p;
+    p.q = static_cast<const uint16_t*>(q);
+    p.q_stride_b = q_stride_b;
+    p.q_stride_tok = q_stride_tok;
+    p.q_stride_head = q_stride_head;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.cache_stride_slot = cache_stride_slot;
+    p.cache_stride_head = cache_stride_head;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.scale_stride_slot = scale_stride_slot;
+    p.scale_stride_head = scale_stride_head;
+    p.block_tables = block_tables;
+    p.block_table_stride = block_table_stride;
+    p.context_lens = context_lens;
+    p.q_lens = q_lens;
+    p.out = out;
+    p.out_stride_b = out_stride_b;
+    p.out_stride_tok = out_stride_tok;
+    p.out_stride_head = out_stride_head;
+    p.out_fp32 = out_dtype == FP8KV_DTYPE_FP32;
+    p.batch = batch;
+    p.max_q = max_q;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = group;
+    p.tokens_per_wave = kMaxStackedRows / group;
+    p.qblocks = (max_q + 4 * p.tokens_per_wave - 1) / (4 * p.tokens_per_wave);
+    p.block_size = block_size;
+    p.block_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
+    p.num_blocks = (int32_t)(num_blocks > 0 ? num_blocks : 1);
+    p.max_context = max_context;
+    p.score_scale_log2 = softmax_scale * 1.4426950408889634f;
+    return launched(fp8kv::launch_prefill(p, head_dim, (hipStream_t)stream), "prefill_attn");
+}
+
 int fp8kv_index_keys_quantize(
     const void* keys, int64_t key_stride, int64_t num_keys, int32_t head_dim,
     int32_t key_format, uint8_t* codes, int64_t code_stride,

@@ -65,6 +65,31 @@ struct MergeParams {
     int32_t total_rows;        // batch * num_kv_heads * m_rows
 };
 
+struct PrefillParams {
+    const uint16_t* q;         // bf16 bits [B, max_q, Hq, D]
+    int64_t q_stride_b, q_stride_tok, q_stride_head;
+    const uint8_t* k_cache;
+    const uint8_t* v_cache;
+    int64_t cache_stride_slot, cache_stride_head;
+    const float* k_scale;
+    const float* v_scale;
+    int64_t scale_stride_slot, scale_stride_head;
+    const int32_t* block_tables;
+    int64_t block_table_stride;
+    const int32_t* context_lens;   // cached tokens of request b, the chunk included
+    const int32_t* q_lens;         // query tokens of request b: its last q_lens[b] tokens
+    void* out;                     // [B, max_q, Hq, D]
+    int64_t out_stride_b, out_stride_tok, out_stride_head;
+    int32_t out_fp32;
+    int32_t batch, max_q, num_q_heads, num_kv_heads, group;
+    int32_t tokens_per_wave;       // 16 / group
+    int32_t qblocks;               // ceil(max_q / (4 * tokens_per_wave))
+    int32_t block_size, block_shift, num_blocks, max_context;
+    float score_scale_log2;
+};
+
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream);
+
 // Wave slots the decode split fills by default: one per SIMD (4 per CU),
 // 0 if the device query fails.
 int decode_wave_slots(int device);

@@ -721,6 +721,196 @@ hipError_t launch_split_bs(const DecodeParams& p, hipStream_t stream) {
                               : launch_split<D, false, SP>(p, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Chunked-prefill attention over the FP8 cache: every query token of a chunk
+// attends to the cached tokens up to its own position. Workgroup = (request,
+// KV head, block of 4 x 16/G query tokens); each of its 4 waves stacks
+// 16/G tokens x G query heads into the 16 MFMA rows, exactly as the decode
+// split kernel stacks verify rows, and runs the same tile math (QK^T MFMA,
+// online softmax, P' = p * v_scale in fp16, PV MFMA). The K/V codes and
+// scales of each 32-token tile are read from the cache once per workgroup
+// into LDS (double-buffered) and all 4 waves read their operands from there
+// in the decode kernel's register layout. Workgroups of one (request, KV
+// head) run on one XCD, the deepest query blocks first.
+template <int D, bool BSP2>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
+    constexpr int KSTEPS = D / 32;
+    constexpr int DL = D / 16;
+    constexpr int KB = D / 4;
+    constexpr int ROW = D + 16;               // padded LDS row: conflict-free row reads
+    constexpr int CPR = D / 16;               // 16-byte chunks per row
+    typedef DecodeTile<D> Tile;
+    typedef typename Tile::Regs Regs;
+    __shared__ __align__(16) uint8_t lds_k[2][32 * ROW];
+    __shared__ __align__(16) uint8_t lds_v[2][32 * ROW];
+    __shared__ float lds_s[2][2][32];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int li = lane & 15, lg = lane >> 4;
+
+    // XCD-contiguous numbering, deepest query block first within a group
+    const int nwg = gridDim.x;
+    const int L_id = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    const int grp = L_id / p.qblocks;
+    if (grp >= p.batch * p.num_kv_heads) return;
+    const int qb = p.qblocks - 1 - (L_id - grp * p.qblocks);
+    const int b = grp / p.num_kv_heads;
+    const int h = grp - b * p.num_kv_heads;
+    const int L = min(max(p.context_lens[b], 0), p.max_context);
+    const int qlen = min(min(max(p.q_lens[b], 0), p.max_q), L);
+    const int TPW = p.tokens_per_wave;
+    const int q0 = qb * 4 * TPW;
+    if (q0 >= qlen) return;
+    const int P = L - qlen;                               // cached tokens before the chunk
+    const int kv_end = P + min(q0 + 4 * TPW, qlen);       // no row of the block sees beyond
+    const int ntiles = (kv_end + 31) >> 5;
+
+    // q operand and causal limit of row li: token tq of the chunk, head hq
+    const int tq = q0 + wave * TPW + li / p.group;
+    const int hq = h * p.group + li % p.group;
+    const bool row_ok = li < 16 && tq < qlen;
+    bf16x8 qv[KSTEPS];
+    if (row_ok) {
+        const uint16_t* qp = p.q + (int64_t)b * p.q_stride_b + (int64_t)tq * p.q_stride_tok +
+                             (int64_t)hq * p.q_stride_head + lg * (D / 4);
+#pragma unroll
+        for (int k = 0; k < KSTEPS; ++k)
+            qv[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 8 * k));
+    } else {
+#pragma unroll
+        for (int k = 0; k < KSTEPS; ++k) qv[k] = bf16x8{};
+    }
+    const int lim = P + tq;
+    const int wave_lim = P + q0 + wave * TPW;             // smallest limit of the wave's rows
+
+    DecodeParams dp;
+    dp.score_scale_log2 = p.score_scale_log2;
+    WaveState<DL> st;
+#pragma unroll
+    for (int n = 0; n < DL; ++n) st.acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+    st.m_run = kNeg;
+    st.l_run = 0.f;
+    st.ef_run = 15;
+
+    // cooperative tile load: thread t moves 16 bytes of token t / CPR's K
+    // and V rows; threads 0..63 also the token's K or V scale
+    const int ld_tok = t / CPR, ld_chunk = t % CPR;
+    const bool ld_rows = ld_tok < 32;
+    const uint8_t* kbase = p.k_cache + (int64_t)h * p.cache_stride_head + 16 * ld_chunk;
+    const uint8_t* vbase = p.v_cache + (int64_t)h * p.cache_stride_head + 16 * ld_chunk;
+    const int32_t* bt = p.block_tables + (int64_t)b * p.block_table_stride;
+    uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
+    float sr = 0.f;
+    auto slot_of = [&](int tok) -> int64_t {
+        const int bi = BSP2 ? (tok >> p.block_shift) : tok / p.block_size;
+        const int bo = BSP2 ? (tok & (p.block_size - 1)) : tok - bi * p.block_size;
+        const int blk = min(max(bt[bi], 0), p.num_blocks - 1);
+        return (int64_t)blk * p.block_size + bo;
+    };
+    auto load_tile = [&](int ti) {
+        if (ld_rows) {
+            const int tok = (ti << 5) + ld_tok;
+            if (tok < kv_end) {
+                const int64_t slot = slot_of(tok);
+                kr = *reinterpret_cast<const uint4*>(kbase + slot * p.cache_stride_slot);
+                vr = *reinterpret_cast<const uint4*>(vbase + slot * p.cache_stride_slot);
+            } else {
+                kr = make_uint4(0, 0, 0, 0);
+                vr = make_uint4(0, 0, 0, 0);
+            }
+        }
+        if (t < 64) {
+            const int tok = (ti << 5) + (t & 31);
+            sr = 0.f;
+            if (tok < kv_end) {
+                const float* plane = t < 32 ? p.k_scale : p.v_scale;
+                sr = plane[slot_of(tok) * p.scale_stride_slot + (int64_t)h * p.scale_stride_head];
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        if (ld_rows) {
+            *reinterpret_cast<uint4*>(&lds_k[buf][ld_tok * ROW + 16 * ld_chunk]) = kr;
+            *reinterpret_cast<uint4*>(&lds_v[buf][ld_tok * ROW + 16 * ld_chunk]) = vr;
+        }
+        if (t < 64) lds_s[buf][t >> 5][t & 31] = sr;
+    };
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    for (int ti = 0; ti < ntiles; ++ti) {
+        const int buf = ti & 1;
+        if (ti + 1 < ntiles) load_tile(ti + 1);
+        // operands in the decode kernel's register layout
+        Regs R;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+            for (int c = 0; c < Tile::KV4; ++c)
+                R.kraw[s][c] = *reinterpret_cast<const uint4*>(
+                    &lds_k[buf][(16 * s + li) * ROW + lg * KB + 16 * c]);
+        }
+        floatx4 sc[2];
+        Tile::qk(R, qv, sc);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint8_t* src = &lds_v[buf][(16 * (e >> 2) + 4 * lg + (e & 3)) * ROW + li * DL];
+            if constexpr (DL == 8)
+                R.vraw[e] = *reinterpret_cast<const uint2*>(src);
+            else
+                R.vraw[e] = *reinterpret_cast<const uint32_t*>(src);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int tk = 16 * s + ((4 * lg + li) & 15);
+            R.ks[s] = __float_as_uint(lds_s[buf][0][tk]);
+            R.vs[s] = __float_as_uint(lds_s[buf][1][tk]);
+        }
+        TileAddr ta;
+        ta.t0 = ti << 5;
+        ta.masked = (ti << 5) + 31 > wave_lim;
+        Tile::template rest<false>(dp, ta, R, sc, L, lim, lg, st);
+        if (ti + 1 < ntiles) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // normalized output of row li: dims [32 lg, 32 lg + 32) (D = 128)
+    st.l_run = rows_sum(st.l_run);
+    if (row_ok) {
+        const float inv = st.l_run > 0.f ? pow2i(max(st.ef_run - 141, -126)) / st.l_run : 0.f;
+        const int64_t off = (int64_t)b * p.out_stride_b + (int64_t)tq * p.out_stride_tok +
+                            (int64_t)hq * p.out_stride_head + (DL * 4) * lg;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float vals[DL];
+#pragma unroll
+            for (int n = 0; n < DL; ++n) vals[n] = st.acc[n][r] * inv;
+            if (p.out_fp32) {
+                float* o = static_cast<float*>(p.out) + off + DL * r;
+#pragma unroll
+                for (int c = 0; c < DL / 4; ++c)
+                    *reinterpret_cast<float4*>(o + 4 * c) =
+                        make_float4(vals[4 * c], vals[4 * c + 1], vals[4 * c + 2], vals[4 * c + 3]);
+            } else {
+                uint16_t* o = static_cast<uint16_t*>(p.out) + off + DL * r;
+                uint32_t w[DL / 2];
+#pragma unroll
+                for (int n = 0; n < DL / 2; ++n) {
+                    const bf16x2 v2 = {(__bf16)vals[2 * n], (__bf16)vals[2 * n + 1]};
+                    w[n] = __builtin_bit_cast(uint32_t, v2);
+                }
+                if constexpr (DL == 8)
+                    *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+                else
+                    *reinterpret_cast<uint2*>(o) = make_uint2(w[0], w[1]);
+            }
+        }
+    }
+}
+
 }  // namespace
 
 int decode_wave_slots(int device) {
@@ -735,6 +925,21 @@ hipError_t launch_decode_partitions(const DecodeParams& p, int head_dim, hipStre
     if (head_dim == 128)
         return sp ? launch_split_bs<128, true>(p, stream) : launch_split_bs<128, false>(p, stream);
     return sp ? launch_split_bs<64, true>(p, stream) : launch_split_bs<64, false>(p, stream);
+}
+
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream) {
+    const int64_t wgs = ((int64_t)p.batch * p.num_kv_heads * p.qblocks + 7) / 8 * 8;
+    if (wgs > INT32_MAX) return hipErrorInvalidValue;
+    const bool pow2 = p.block_shift >= 0;
+    dim3 grid((unsigned)wgs), block(256);
+    if (head_dim == 128) {
+        if (pow2) hipLaunchKernelGGL((prefill_kernel<128, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((prefill_kernel<128, false>), grid, block, 0, stream, p);
+    } else {
+        if (pow2) hipLaunchKernelGGL((prefill_kernel<64, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((prefill_kernel<64, false>), grid, block, 0, stream, p);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_merge(const MergeParams& p, int head_dim, hipStream_t stream) {

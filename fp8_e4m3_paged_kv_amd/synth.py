@@ -334,3 +334,10 @@ def sparse_selection(layout: PagedLayout, keep_frac: float, seed: int,
             bt[b, :len(tables[b])] = torch.tensor(tables[b], dtype=torch.int32)
             bv[b, :len(valids[b])] = torch.tensor(valids[b], dtype=torch.int32)
     return SparseSelection(bt, bv, torch.tensor(vlens, dtype=torch.int32))
+
+
+def prefill_attn_workload(seed: int = 71, device="cpu") -> DecodeCase:
+    """One request of 32,768 cached tokens whose last 4096 are the prefill
+    chunk being attended (q [1, 4096, 32, 128]); Hkv 8, bs 16, N(0,1)."""
+    return decode_case([32768], 32, 8, 128, 16, rows=4096, seed=seed,
+                       device=device, name="prefill-attn")

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FP8KV_ABI_VERSION 5
+#define FP8KV_ABI_VERSION 6
 
 typedef enum fp8kv_status {
     FP8KV_OK = 0,
@@ -303,6 +303,43 @@ int fp8kv_sparse_decode_partials(
     int32_t head_dim, int32_t block_size, float softmax_scale,
     int32_t num_ranges, int32_t max_context,
     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp8kv_prefill_attn_fp8 -- chunked-prefill attention over the FP8 cache
+ * ("feat(dsa): implement fp8 KV cache (e4m3) with a bf16 indexer cache",
+ * sglang-jax #1776, "Modifications", qblock prefill bullet: the KV tile is
+ * upcast to the query dtype once before the score dot and P never goes to
+ * the cache dtype; ATOM #2655 description, K/V bullet: key scale on the
+ * score column, value scale folded into P).
+ *
+ * Request b has context_lens[b] cached tokens, the last q_lens[b] of which
+ * are its chunk (already written with fp8kv_kv_quant_scatter); its query
+ * token i < q_lens[b] (position P + i, P = context_lens[b] - q_lens[b])
+ * attends to the cached tokens 0 .. P + i:
+ *   out[b, i, hq, :] = softmax_j(softmax_scale * q . dec(kc_j) * ks_j)
+ *                      weighted sum of dec(vc_j) * vs_j
+ * with the cache, strides and GQA mapping of fp8kv_paged_decode_attn_fp8.
+ * q         (device) bf16 [B, max_q, Hq, D] at (b, i, hq) strides; 16-byte rows.
+ * q_lens    (device) int32 [B], clamped to [0, min(max_q, context_lens[b])].
+ * out       (device) bf16 or fp32, element (b, i, hq, d) at b*out_stride_b +
+ *           i*out_stride_tok + hq*out_stride_head + d; rows aligned to 8
+ *           (bf16) or 16 (fp32) bytes. Rows i >= q_lens[b] are not written.
+ * Constraints: head_dim 64 or 128; num_q_heads / num_kv_heads divides 16;
+ * block_size a multiple of 16. No workspace.
+ * Errors: E_NULL, E_SHAPE, E_STRIDE, E_ALIGN, E_UNSUPPORTED, E_LAUNCH.
+ */
+int fp8kv_prefill_attn_fp8(
+    const void* q, int64_t q_stride_b, int64_t q_stride_tok, int64_t q_stride_head,
+    int32_t q_dtype, const uint8_t* k_cache, const uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head,
+    const float* k_scale, const float* v_scale,
+    int64_t scale_stride_slot, int64_t scale_stride_head, int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, const int32_t* q_lens,
+    int32_t batch, int32_t max_q, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, float softmax_scale, int32_t max_context,
+    void* out, int64_t out_stride_b, int64_t out_stride_tok, int64_t out_stride_head,
+    int32_t out_dtype, void* stream);
 
 /*
  * Compressed index keys and the index scorer ("fix(qwen4-exp): register

@@ -316,3 +316,40 @@ def test_index_keys_build_refusals(L, kw, status):
     assert ikb(L, **kw) == status
     if status != OK:
         assert L.fp8kv_last_error().decode()
+
+
+def pf(L, **kw):
+    a = dict(q=A, qsb=1 << 20, qst=4096, qsh=128, qdt=BF16, kc=A, vc=A, css=1024,
+             csh=128, ks=A, vs=A, sss=1, ssh=1 << 20, S=1 << 20, bt=A, bts=2048,
+             cl=A, ql=A, B=1, Q=4096, Hq=32, H=8, D=128, bs=16, scale=0.088,
+             maxc=32768, out=A, osb=1 << 20, ost=4096, osh=128, odt=BF16)
+    a.update(kw)
+    return L.fp8kv_prefill_attn_fp8(
+        a["q"], a["qsb"], a["qst"], a["qsh"], a["qdt"], a["kc"], a["vc"], a["css"],
+        a["csh"], a["ks"], a["vs"], a["sss"], a["ssh"], a["S"], a["bt"], a["bts"],
+        a["cl"], a["ql"], a["B"], a["Q"], a["Hq"], a["H"], a["D"], a["bs"],
+        ctypes.c_float(a["scale"]), a["maxc"], a["out"], a["osb"], a["ost"], a["osh"],
+        a["odt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), E_UNSUPPORTED),
+    (dict(qdt=FP32), E_UNSUPPORTED),
+    (dict(odt=FP16), E_UNSUPPORTED),
+    (dict(Hq=24, H=8), E_UNSUPPORTED),   # group 3 does not divide 16
+    (dict(Hq=64, H=2), E_UNSUPPORTED),   # group 32
+    (dict(Hq=30), E_SHAPE),
+    (dict(bs=8), E_UNSUPPORTED),
+    (dict(B=-1), E_SHAPE),
+    (dict(ql=0), E_NULL),
+    (dict(out=0), E_NULL),
+    (dict(qst=-8), E_STRIDE),
+    (dict(q=A + 8), E_ALIGN),
+    (dict(out=A + 4), E_ALIGN),
+    (dict(osh=101), E_ALIGN),            # bf16 rows must start on 8 bytes
+    (dict(Q=0), OK),
+])
+def test_prefill_refusals(L, kw, status):
+    assert pf(L, **kw) == status
+    if status != OK:
+        assert L.fp8kv_last_error().decode()
