@@ -514,6 +514,8 @@ int fp8kv_prefill_attn_fp8(
                     block_size);
     if (num_blocks > INT32_MAX)
         return fail(FP8KV_E_SHAPE, "num_slots / block_size exceeds int32 block ids");
+    if (cache_stride_slot > (INT32_MAX / 16) || scale_stride_slot > (INT32_MAX / 64))
+        return fail(FP8KV_E_SHAPE, "slot stride too large for 32-bit in-block offsets");
     if (batch == 0 || max_q == 0) return ok();
     fp8kv::PrefillParams p;
     p.q = static_cast<const uint16_t*>(q);
@@ -543,7 +545,8 @@ int fp8kv_prefill_attn_fp8(
     p.num_kv_heads = num_kv_heads;
     p.group = group;
     p.tokens_per_wave = kMaxStackedRows / group;
-    p.qblocks = (max_q + 4 * p.tokens_per_wave - 1) / (4 * p.tokens_per_wave);
+    const int block_tokens = 4 * fp8kv::kPrefillRowTiles * p.tokens_per_wave;
+    p.qblocks = (max_q + block_tokens - 1) / block_tokens;
     p.block_size = block_size;
     p.block_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
     p.num_blocks = (int32_t)(num_blocks > 0 ? num_blocks : 1);

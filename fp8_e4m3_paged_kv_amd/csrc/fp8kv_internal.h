@@ -82,11 +82,14 @@ struct PrefillParams {
     int64_t out_stride_b, out_stride_tok, out_stride_head;
     int32_t out_fp32;
     int32_t batch, max_q, num_q_heads, num_kv_heads, group;
-    int32_t tokens_per_wave;       // 16 / group
-    int32_t qblocks;               // ceil(max_q / (4 * tokens_per_wave))
+    int32_t tokens_per_wave;       // per 16-row tile: 16 / group
+    int32_t qblocks;               // ceil(max_q / (4 * kPrefillRowTiles * tokens_per_wave))
     int32_t block_size, block_shift, num_blocks, max_context;
     float score_scale_log2;
 };
+
+// 16-row MFMA tiles of query rows per prefill wave.
+constexpr int kPrefillRowTiles = 2;
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream);
 

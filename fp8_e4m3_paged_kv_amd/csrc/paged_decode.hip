@@ -78,6 +78,31 @@ __device__ __forceinline__ float rows_sum(float v) {
 }
 
 
+// IEEE-754 maximum (gfx950 v_maximum3_f32): unlike fmaxf it needs no
+// NaN-quieting step on each operand; for the finite scores here the two
+// agree (up to the sign of a zero maximum, which exp2 does not see).
+__device__ __forceinline__ float fmax_fin(float a, float b) {
+    return __builtin_elementwise_maximum(a, b);
+}
+__device__ __forceinline__ float max8(const float (&v)[2][4]) {
+    return fmax_fin(fmax_fin(fmax_fin(v[0][0], v[0][1]), fmax_fin(v[0][2], v[0][3])),
+                    fmax_fin(fmax_fin(v[1][0], v[1][1]), fmax_fin(v[1][2], v[1][3])));
+}
+__device__ __forceinline__ float rows_max_fin(float v) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmax_fin(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmax_fin(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+// Maximum over the four 16-lane rows for values that order as unsigned
+// integers (non-negative floats).
+__device__ __forceinline__ uint32_t rows_max_u32(uint32_t v) {
+    auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = max((uint32_t)a[0], (uint32_t)a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max((uint32_t)b[0], (uint32_t)b[1]);
+}
+
 typedef int intx2 __attribute__((ext_vector_type(2)));
 typedef int intx4 __attribute__((ext_vector_type(4)));
 
@@ -261,23 +286,45 @@ struct DecodeTile {
         }
     }
 
-    // Online-softmax update and PV with the tile's scores and V registers.
+    // The same for NT 16-row tiles of queries: each K operand is widened
+    // once and feeds every tile's MFMA chain.
+    template <int NT>
+    static __device__ __forceinline__ void qk_tiles(const Regs& R, const bf16x8 (&qv)[NT][KSTEPS],
+                                                    floatx4 (&sc)[NT][2]) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) sc[j][s] = floatx4{0.f, 0.f, 0.f, 0.f};
+            const uint32_t* kw = reinterpret_cast<const uint32_t*>(R.kraw[s]);
+#pragma unroll
+            for (int k = 0; k < KSTEPS; ++k) {
+                const bf16x8 a = e4m3x8_to_bf16x8(kw[2 * k], kw[2 * k + 1]);
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    sc[j][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[j][k], sc[j][s], 0, 0, 0);
+            }
+        }
+    }
+
+    // Online-softmax update of the tile's scores; returns P' = p * v_scale *
+    // kappa of the lane's 8 tokens in fp16 (the B operand of PV).
     template <bool SP>
-    static __device__ __forceinline__ void rest(
-        const DecodeParams& p, const TileAddr& ta, const Regs& R, const floatx4 (&sc)[2],
-        int p1, int lim, int lg, WaveState<DL>& st) {
+    static __device__ __forceinline__ f16x8 softmax(
+        const DecodeParams& p, const TileAddr& ta, const uint32_t (&ks)[2],
+        const uint32_t (&vs)[2], const floatx4 (&sc)[2], int p1, int lim, int lg,
+        WaveState<DL>& st) {
 
         // ---- scores in log2 units, tile max, value-scale range
         float s2[2][4];
         float sv[2][4];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const float sk[4] = {row_bcast<0>(R.ks[s]), row_bcast<1>(R.ks[s]),
-                                 row_bcast<2>(R.ks[s]), row_bcast<3>(R.ks[s])};
-            sv[s][0] = row_bcast<0>(R.vs[s]);
-            sv[s][1] = row_bcast<1>(R.vs[s]);
-            sv[s][2] = row_bcast<2>(R.vs[s]);
-            sv[s][3] = row_bcast<3>(R.vs[s]);
+            const float sk[4] = {row_bcast<0>(ks[s]), row_bcast<1>(ks[s]),
+                                 row_bcast<2>(ks[s]), row_bcast<3>(ks[s])};
+            sv[s][0] = row_bcast<0>(vs[s]);
+            sv[s][1] = row_bcast<1>(vs[s]);
+            sv[s][2] = row_bcast<2>(vs[s]);
+            sv[s][3] = row_bcast<3>(vs[s]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) s2[s][r] = sc[s][r] * (sk[r] * p.score_scale_log2);
         }
@@ -329,8 +376,14 @@ struct DecodeTile {
             pw[2 * s] = pack_f16x2(pr[0], pr[1]);
             pw[2 * s + 1] = pack_f16x2(pr[2], pr[3]);
         }
-        const f16x8 pb = __builtin_bit_cast(f16x8, pw);
+        return __builtin_bit_cast(f16x8, pw);
+    }
 
+    // O^T += V^T P'^T for NT 16-row tiles from the tile's V code registers;
+    // each V operand is widened once and feeds every tile's MFMA.
+    template <int NT>
+    static __device__ __forceinline__ void pv_tiles(const Regs& R, const f16x8 (&pbs)[NT],
+                                                    WaveState<DL>* const (&sts)[NT]) {
         // ---- V^T columns of the lane's 8 tokens, then O^T += V^T P'^T.
         // Pairing two tokens' dwords byte-wise gives, in each 16-bit half, the
         // two tokens' codes of one head-dim column: the fp16 convert then
@@ -352,9 +405,22 @@ struct DecodeTile {
                 for (int t = 0; t < 4; ++t)
                     h[t] = (c & 1) ? e4m3x2_to_f16x2<true>(src[t]) : e4m3x2_to_f16x2<false>(src[t]);
                 const f16x8 a = __builtin_bit_cast(f16x8, h);
-                st.acc[4 * w + c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb, st.acc[4 * w + c], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    sts[j]->acc[4 * w + c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        a, pbs[j], sts[j]->acc[4 * w + c], 0, 0, 0);
             }
         }
+    }
+
+    // Online-softmax update and PV with the tile's scores and V registers.
+    template <bool SP>
+    static __device__ __forceinline__ void rest(
+        const DecodeParams& p, const TileAddr& ta, const Regs& R, const floatx4 (&sc)[2],
+        int p1, int lim, int lg, WaveState<DL>& st) {
+        const f16x8 pb[1] = {softmax<SP>(p, ta, R.ks, R.vs, sc, p1, lim, lg, st)};
+        WaveState<DL>* const sts[1] = {&st};
+        pv_tiles<1>(R, pb, sts);
     }
 };
 
@@ -724,26 +790,40 @@ hipError_t launch_split_bs(const DecodeParams& p, hipStream_t stream) {
 // ---------------------------------------------------------------------------
 // Chunked-prefill attention over the FP8 cache: every query token of a chunk
 // attends to the cached tokens up to its own position. Workgroup = (request,
-// KV head, block of 4 x 16/G query tokens); each of its 4 waves stacks
-// 16/G tokens x G query heads into the 16 MFMA rows, exactly as the decode
-// split kernel stacks verify rows, and runs the same tile math (QK^T MFMA,
-// online softmax, P' = p * v_scale in fp16, PV MFMA). The K/V codes and
-// scales of each 32-token tile are read from the cache once per workgroup
-// into LDS (double-buffered) and all 4 waves read their operands from there
-// in the decode kernel's register layout. Workgroups of one (request, KV
-// head) run on one XCD, the deepest query blocks first.
-template <int D, bool BSP2>
+// KV head, block of 4 x NT x 16/G query tokens); each of its 4 waves carries
+// NT row tiles, each stacking 16/G tokens x G query heads into the 16 MFMA
+// rows exactly as the decode split kernel stacks verify rows, and runs the
+// decode kernel's tile math (QK^T MFMA, online softmax, P' = p * v_scale in
+// fp16, PV MFMA) with the same rounding at every step. Each K and V operand
+// is widened from E4M3 once per wave and feeds all NT row tiles; the
+// value-scale range exponent of P' depends only on the tile, so it and
+// v_scale * kappa are shared by the row tiles too.
+//
+// The K/V codes and scales of each 32-token tile are read from the cache
+// once per workgroup into LDS (double-buffered): every loader wave moves the
+// rows of 8 (head_dim 128) or 16 (head_dim 64) tokens of one 16-token half,
+// whose page lookup is wave-uniform, through buffer descriptors that end
+// after the chunk's last visible key, so nothing past it is read. The key
+// scales go to LDS already multiplied by softmax_scale * log2(e). All 4
+// waves read their operands from LDS in the decode kernel's register layout,
+// the scales as four consecutive tokens per lane (no lane broadcast needed).
+// Workgroups of one (request, KV head) run on one XCD, the deepest query
+// blocks first.
+template <int D, bool BSP2, int NT>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     constexpr int KSTEPS = D / 32;
     constexpr int DL = D / 16;
     constexpr int KB = D / 4;
     constexpr int ROW = D + 16;               // padded LDS row: conflict-free row reads
-    constexpr int CPR = D / 16;               // 16-byte chunks per row
+    constexpr int CPR = D / 16;               // 16-byte chunks per code row
+    constexpr int TPL = 64 / CPR;             // tokens one loader wave moves
+    constexpr int LOAD_WAVES = 32 / TPL;
+    static_assert(TPL <= 16 && 16 % TPL == 0, "a loader wave stays inside one half");
     typedef DecodeTile<D> Tile;
     typedef typename Tile::Regs Regs;
     __shared__ __align__(16) uint8_t lds_k[2][32 * ROW];
     __shared__ __align__(16) uint8_t lds_v[2][32 * ROW];
-    __shared__ float lds_s[2][2][32];
+    __shared__ __align__(16) float lds_s[2][2][32];   // [buf][k_scale * score scale | v_scale][token]
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -761,89 +841,98 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     const int L = min(max(p.context_lens[b], 0), p.max_context);
     const int qlen = min(min(max(p.q_lens[b], 0), p.max_q), L);
     const int TPW = p.tokens_per_wave;
-    const int q0 = qb * 4 * TPW;
+    const int q0 = qb * 4 * NT * TPW;
     if (q0 >= qlen) return;
     const int P = L - qlen;                               // cached tokens before the chunk
-    const int kv_end = P + min(q0 + 4 * TPW, qlen);       // no row of the block sees beyond
+    const int kv_end = P + min(q0 + 4 * NT * TPW, qlen);  // no row of the block sees beyond
     const int ntiles = (kv_end + 31) >> 5;
 
-    // q operand and causal limit of row li: token tq of the chunk, head hq
-    const int tq = q0 + wave * TPW + li / p.group;
+    // q operand and causal limit of row li of tile j: token tq of the chunk,
+    // head hq
     const int hq = h * p.group + li % p.group;
-    const bool row_ok = li < 16 && tq < qlen;
-    bf16x8 qv[KSTEPS];
-    if (row_ok) {
-        const uint16_t* qp = p.q + (int64_t)b * p.q_stride_b + (int64_t)tq * p.q_stride_tok +
-                             (int64_t)hq * p.q_stride_head + lg * (D / 4);
+    int tq[NT], lim[NT];
+    bf16x8 qv[NT][KSTEPS];
 #pragma unroll
-        for (int k = 0; k < KSTEPS; ++k)
-            qv[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 8 * k));
-    } else {
+    for (int j = 0; j < NT; ++j) {
+        tq[j] = q0 + (wave * NT + j) * TPW + li / p.group;
+        lim[j] = P + tq[j];
+        if (tq[j] < qlen) {
+            const uint16_t* qp = p.q + (int64_t)b * p.q_stride_b + (int64_t)tq[j] * p.q_stride_tok +
+                                 (int64_t)hq * p.q_stride_head + lg * (D / 4);
 #pragma unroll
-        for (int k = 0; k < KSTEPS; ++k) qv[k] = bf16x8{};
+            for (int k = 0; k < KSTEPS; ++k)
+                qv[j][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 8 * k));
+        } else {
+#pragma unroll
+            for (int k = 0; k < KSTEPS; ++k) qv[j][k] = bf16x8{};
+        }
     }
-    const int lim = P + tq;
-    const int wave_lim = P + q0 + wave * TPW;             // smallest limit of the wave's rows
+    const int wave_lim = P + q0 + wave * NT * TPW;        // smallest limit of the wave's rows
 
-    DecodeParams dp;
-    dp.score_scale_log2 = p.score_scale_log2;
-    WaveState<DL> st;
+    // softmax state of each row tile; the P' range exponent is shared
+    WaveState<DL> st[NT];
 #pragma unroll
-    for (int n = 0; n < DL; ++n) st.acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
-    st.m_run = kNeg;
-    st.l_run = 0.f;
-    st.ef_run = 15;
+    for (int j = 0; j < NT; ++j) {
+#pragma unroll
+        for (int n = 0; n < DL; ++n) st[j].acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+        st[j].m_run = kNeg;
+        st[j].l_run = 0.f;
+    }
+    int ef_run = 15;
 
-    // cooperative tile load: thread t moves 16 bytes of token t / CPR's K
-    // and V rows; threads 0..63 also the token's K or V scale
+    // cooperative tile load: lane t of a loader wave moves 16 bytes of token
+    // t / CPR's K and V rows and reads the token's two scales; its chunk-0
+    // lanes store the key scale, its chunk-1 lanes the value scale
+    const bool loader = wave < LOAD_WAVES;
     const int ld_tok = t / CPR, ld_chunk = t % CPR;
-    const bool ld_rows = ld_tok < 32;
-    const uint8_t* kbase = p.k_cache + (int64_t)h * p.cache_stride_head + 16 * ld_chunk;
-    const uint8_t* vbase = p.v_cache + (int64_t)h * p.cache_stride_head + 16 * ld_chunk;
+    const int ld_half = (wave * TPL) >> 4;
+    const int ld_code = (ld_tok & 15) * (int)p.cache_stride_slot + 16 * ld_chunk;
+    const int ld_scale = (ld_tok & 15) * (int)p.scale_stride_slot * 4;
+    const int lds_code = ld_tok * ROW + 16 * ld_chunk;
+    const uint8_t* kbase = p.k_cache + (int64_t)h * p.cache_stride_head;
+    const uint8_t* vbase = p.v_cache + (int64_t)h * p.cache_stride_head;
+    const float* ksbase = p.k_scale + (int64_t)h * p.scale_stride_head;
+    const float* vsbase = p.v_scale + (int64_t)h * p.scale_stride_head;
     const int32_t* bt = p.block_tables + (int64_t)b * p.block_table_stride;
-    uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
+    intx4 kr = {0, 0, 0, 0}, vr = {0, 0, 0, 0};
     float sr = 0.f;
-    auto slot_of = [&](int tok) -> int64_t {
-        const int bi = BSP2 ? (tok >> p.block_shift) : tok / p.block_size;
-        const int bo = BSP2 ? (tok & (p.block_size - 1)) : tok - bi * p.block_size;
-        const int blk = min(max(bt[bi], 0), p.num_blocks - 1);
-        return (int64_t)blk * p.block_size + bo;
-    };
     auto load_tile = [&](int ti) {
-        if (ld_rows) {
-            const int tok = (ti << 5) + ld_tok;
-            if (tok < kv_end) {
-                const int64_t slot = slot_of(tok);
-                kr = *reinterpret_cast<const uint4*>(kbase + slot * p.cache_stride_slot);
-                vr = *reinterpret_cast<const uint4*>(vbase + slot * p.cache_stride_slot);
-            } else {
-                kr = make_uint4(0, 0, 0, 0);
-                vr = make_uint4(0, 0, 0, 0);
-            }
+        // the wave's half: keys stok .. stok + nvalid - 1, all in one block
+        const int stok = (ti << 5) + 16 * ld_half;
+        const int nvalid = min(16, kv_end - stok);
+        int64_t slot = 0;
+        if (nvalid > 0) {
+            const int bi = BSP2 ? (stok >> p.block_shift) : stok / p.block_size;
+            const int bo = BSP2 ? (stok & (p.block_size - 1)) : stok - bi * p.block_size;
+            const int blk = min(max(bt[bi], 0), p.num_blocks - 1);
+            slot = (int64_t)blk * p.block_size + bo;
         }
-        if (t < 64) {
-            const int tok = (ti << 5) + (t & 31);
-            sr = 0.f;
-            if (tok < kv_end) {
-                const float* plane = t < 32 ? p.k_scale : p.v_scale;
-                sr = plane[slot_of(tok) * p.scale_stride_slot + (int64_t)h * p.scale_stride_head];
-            }
-        }
+        const int nrc = nvalid > 0 ? (nvalid - 1) * (int)p.cache_stride_slot + D : 0;
+        const int nrs = nvalid > 0 ? 4 * ((nvalid - 1) * (int)p.scale_stride_slot + 1) : 0;
+        const int64_t coff = slot * p.cache_stride_slot;
+        const int64_t soff = slot * p.scale_stride_slot;
+        kr = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(kbase + coff, nrc), ld_code, 0, 0);
+        vr = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(vbase + coff, nrc), ld_code, 0, 0);
+        const float ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                       make_rsrc(ksbase + soff, nrs), ld_scale, 0, 0));
+        const float vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                       make_rsrc(vsbase + soff, nrs), ld_scale, 0, 0));
+        sr = ld_chunk == 0 ? ks * p.score_scale_log2 : vs;
     };
     auto store_tile = [&](int buf) {
-        if (ld_rows) {
-            *reinterpret_cast<uint4*>(&lds_k[buf][ld_tok * ROW + 16 * ld_chunk]) = kr;
-            *reinterpret_cast<uint4*>(&lds_v[buf][ld_tok * ROW + 16 * ld_chunk]) = vr;
-        }
-        if (t < 64) lds_s[buf][t >> 5][t & 31] = sr;
+        *reinterpret_cast<intx4*>(&lds_k[buf][lds_code]) = kr;
+        *reinterpret_cast<intx4*>(&lds_v[buf][lds_code]) = vr;
+        if (ld_chunk < 2) lds_s[buf][ld_chunk][ld_tok] = sr;
     };
 
-    load_tile(0);
-    store_tile(0);
+    if (loader) {
+        load_tile(0);
+        store_tile(0);
+    }
     __syncthreads();
     for (int ti = 0; ti < ntiles; ++ti) {
         const int buf = ti & 1;
-        if (ti + 1 < ntiles) load_tile(ti + 1);
+        if (loader && ti + 1 < ntiles) load_tile(ti + 1);
         // operands in the decode kernel's register layout
         Regs R;
 #pragma unroll
@@ -853,8 +942,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
                 R.kraw[s][c] = *reinterpret_cast<const uint4*>(
                     &lds_k[buf][(16 * s + li) * ROW + lg * KB + 16 * c]);
         }
-        floatx4 sc[2];
-        Tile::qk(R, qv, sc);
+        floatx4 sc[NT][2];
+        Tile::template qk_tiles<NT>(R, qv, sc);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const uint8_t* src = &lds_v[buf][(16 * (e >> 2) + 4 * lg + (e & 3)) * ROW + li * DL];
@@ -863,31 +952,102 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
             else
                 R.vraw[e] = *reinterpret_cast<const uint32_t*>(src);
         }
+        // scales of the lane's score tokens 16 s + 4 lg + r
+        float sk[2][4], sv[2][4];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const int tk = 16 * s + ((4 * lg + li) & 15);
-            R.ks[s] = __float_as_uint(lds_s[buf][0][tk]);
-            R.vs[s] = __float_as_uint(lds_s[buf][1][tk]);
+            const float4 a = *reinterpret_cast<const float4*>(&lds_s[buf][0][16 * s + 4 * lg]);
+            const float4 c = *reinterpret_cast<const float4*>(&lds_s[buf][1][16 * s + 4 * lg]);
+            sk[s][0] = a.x; sk[s][1] = a.y; sk[s][2] = a.z; sk[s][3] = a.w;
+            sv[s][0] = c.x; sv[s][1] = c.y; sv[s][2] = c.z; sv[s][3] = c.w;
         }
-        TileAddr ta;
-        ta.t0 = ti << 5;
-        ta.masked = (ti << 5) + 31 > wave_lim;
-        Tile::template rest<false>(dp, ta, R, sc, L, lim, lg, st);
-        if (ti + 1 < ntiles) store_tile(buf ^ 1);
+
+        // ---- P' range of the tile (keys past the chunk have v_scale 0);
+        // the scales are >= 0, so their bit patterns order as integers
+        uint32_t svm = 0;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) svm = max(svm, __float_as_uint(sv[s][r]));
+        svm = rows_max_u32(svm);
+        const int ef_t = max((int)(svm >> 23), 15);
+        const int ef_new = max(ef_run, ef_t);
+        const bool ef_up = ef_new > ef_run;
+        const float fe = pow2i(max(ef_run - ef_new, -126));
+        ef_run = ef_new;
+        const float kappa = pow2i(141 - ef_run);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sv[s][r] *= kappa;
+
+        // ---- online softmax of each row tile; P' = p * v_scale * kappa
+        const bool masked = (ti << 5) + 31 > wave_lim;
+        f16x8 pb[NT];
+        WaveState<DL>* sts[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            float s2[2][4];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s2[s][r] = sc[j][s][r] * sk[s][r];
+            if (masked) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int tok = (ti << 5) + 16 * s + 4 * lg + r;
+                        s2[s][r] = tok <= lim[j] ? s2[s][r] : kNeg;
+                    }
+            }
+            const float mt = rows_max_fin(max8(s2));
+            const float m_new = fmax_fin(st[j].m_run, mt);
+            if (__any(m_new > st[j].m_run) || ef_up) {
+                const float a = __builtin_amdgcn_exp2f(st[j].m_run - m_new);
+                const float f = a * fe;
+#pragma unroll
+                for (int n = 0; n < DL; ++n) st[j].acc[n] *= f;
+                st[j].l_run *= a;
+                st[j].m_run = m_new;
+            }
+            uint32_t pw[4];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                float pr[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // a masked score gives exp2(kNeg - m) = 0: every row sees
+                    // key 0 in the first tile, so m is a real score throughout
+                    const float e = __builtin_amdgcn_exp2f(s2[s][r] - st[j].m_run);
+                    st[j].l_run += e;
+                    pr[r] = e * sv[s][r];
+                }
+                pw[2 * s] = pack_f16x2(pr[0], pr[1]);
+                pw[2 * s + 1] = pack_f16x2(pr[2], pr[3]);
+            }
+            pb[j] = __builtin_bit_cast(f16x8, pw);
+            sts[j] = &st[j];
+        }
+        Tile::template pv_tiles<NT>(R, pb, sts);
+        if (loader && ti + 1 < ntiles) store_tile(buf ^ 1);
         __syncthreads();
     }
 
-    // normalized output of row li: dims [32 lg, 32 lg + 32) (D = 128)
-    st.l_run = rows_sum(st.l_run);
-    if (row_ok) {
-        const float inv = st.l_run > 0.f ? pow2i(max(st.ef_run - 141, -126)) / st.l_run : 0.f;
-        const int64_t off = (int64_t)b * p.out_stride_b + (int64_t)tq * p.out_stride_tok +
+    // normalized output of row li of each tile: dims [DL*4 lg, DL*4 lg + DL*4)
+    const float un = pow2i(max(ef_run - 141, -126));
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const float l_sum = rows_sum(st[j].l_run);
+        if (tq[j] >= qlen) continue;
+        const float inv = l_sum > 0.f ? un / l_sum : 0.f;
+        const int64_t off = (int64_t)b * p.out_stride_b + (int64_t)tq[j] * p.out_stride_tok +
                             (int64_t)hq * p.out_stride_head + (DL * 4) * lg;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float vals[DL];
 #pragma unroll
-            for (int n = 0; n < DL; ++n) vals[n] = st.acc[n][r] * inv;
+            for (int n = 0; n < DL; ++n) vals[n] = st[j].acc[n][r] * inv;
             if (p.out_fp32) {
                 float* o = static_cast<float*>(p.out) + off + DL * r;
 #pragma unroll
@@ -933,11 +1093,11 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stre
     const bool pow2 = p.block_shift >= 0;
     dim3 grid((unsigned)wgs), block(256);
     if (head_dim == 128) {
-        if (pow2) hipLaunchKernelGGL((prefill_kernel<128, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((prefill_kernel<128, false>), grid, block, 0, stream, p);
+        if (pow2) hipLaunchKernelGGL((prefill_kernel<128, true, kPrefillRowTiles>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((prefill_kernel<128, false, kPrefillRowTiles>), grid, block, 0, stream, p);
     } else {
-        if (pow2) hipLaunchKernelGGL((prefill_kernel<64, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((prefill_kernel<64, false>), grid, block, 0, stream, p);
+        if (pow2) hipLaunchKernelGGL((prefill_kernel<64, true, kPrefillRowTiles>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((prefill_kernel<64, false, kPrefillRowTiles>), grid, block, 0, stream, p);
     }
     return hipGetLastError();
 }
