@@ -993,13 +993,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) s2[s][r] = sc[j][s][r] * sk[s][r];
             if (masked) {
+                // key 16 s + 4 lg + r of the tile is visible iff
+                // 16 s + r <= lim - t0 - 4 lg
+                const int d = lim[j] - (ti << 5) - 4 * lg;
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int tok = (ti << 5) + 16 * s + 4 * lg + r;
-                        s2[s][r] = tok <= lim[j] ? s2[s][r] : kNeg;
-                    }
+                    for (int r = 0; r < 4; ++r) s2[s][r] = 16 * s + r <= d ? s2[s][r] : kNeg;
             }
             const float mt = rows_max_fin(max8(s2));
             const float m_new = fmax_fin(st[j].m_run, mt);
