@@ -59,8 +59,10 @@ def test_ragged_lengths_across_ranges(ranges):
 
 
 @pytest.mark.parametrize("layout", ["head_major", "slot_major"])
-@pytest.mark.parametrize("bs", [16, 32, 64, 128])
+@pytest.mark.parametrize("bs", [16, 32, 48, 64, 128])
 def test_block_sizes_and_scale_layouts(bs, layout):
+    """Power-of-two block sizes take the shift/mask page walk, 48 the
+    division path."""
     case = synth.decode_case([300, 1290, 64], 8, 4, 128, bs, rows=1, seed=bs)
     check_case(case, ranges=11, layout=layout)
 

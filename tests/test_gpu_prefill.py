@@ -47,6 +47,7 @@ def oracle_prefill(case, host, rows=None):
     ([900, 1300], 130, 8, 8, 128, 64),     # MHA (16 tokens per wave), bs 64
     ([600, 800], 45, 16, 2, 128, 32),      # GQA 8
     ([500, 777], 64, 16, 4, 64, 16),       # head_dim 64
+    ([700, 1000], 40, 16, 4, 128, 48),     # block size 48 (division page walk)
 ])
 def test_chunk_matches_oracle(lens, C, Hq, Hkv, D, bs):
     case = synth.decode_case(lens, Hq, Hkv, D, bs, rows=C, seed=C + bs)

@@ -57,7 +57,7 @@ def check(case, sel, ranges=0, layout="head_major", name=""):
     return dc, out
 
 
-@pytest.mark.parametrize("bs", [16, 64])
+@pytest.mark.parametrize("bs", [16, 48, 64])
 @pytest.mark.parametrize("keep,partial", [(0.3, 0.0), (0.3, 0.5), (0.05, 0.2), (1.0, 0.7)])
 def test_selected_blocks_match_oracle(bs, keep, partial):
     case = synth.decode_case([1, 31, 700, 3000, 77], 8, 2, 128, bs, rows=1,
