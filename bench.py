@@ -233,7 +233,7 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; "
+        print(json.dumps({"error": "the benchmark measures one GPU only; "
                                    "run with --gpus 1"}))
         sys.exit(2)
     import torch

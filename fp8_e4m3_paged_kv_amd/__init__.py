@@ -58,6 +58,8 @@ def lib():
     L.fp8kv_status_string.argtypes = [ctypes.c_int]
     L.fp8kv_status_string.restype = ctypes.c_char_p
     L.fp8kv_last_error.restype = ctypes.c_char_p
+    L.fp8kv_set_checked.argtypes = [ctypes.c_int]
+    L.fp8kv_set_checked.restype = ctypes.c_int
     L.fp8kv_kv_quant_scatter.argtypes = [P, I64, I64, P, I64, I64, I32, I32,
                                          I32, I32, P, P, P, I64, I64, P, P,
                                          I64, I64, I64, P]
@@ -141,6 +143,16 @@ def _scale_strides(scale: torch.Tensor):
 
 def abi_version() -> int:
     return lib().fp8kv_abi_version()
+
+
+def set_checked(enabled: bool) -> bool:
+    """Switch the library's checked mode (process-wide) and return the
+    previous setting. In checked mode every call also verifies that its
+    pointers are device memory of the current device and range-checks the
+    device-resident ids (slot ids, context lengths, page tables, valid
+    counts, chunk lengths) on the host, synchronizing the stream; it is
+    refused under graph capture."""
+    return bool(lib().fp8kv_set_checked(1 if enabled else 0))
 
 
 def kv_quant_scatter(k: torch.Tensor, v: torch.Tensor, slot_ids: torch.Tensor,

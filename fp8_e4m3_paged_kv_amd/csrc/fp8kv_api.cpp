@@ -2,9 +2,13 @@
 // grid sizing and kernel launches. Nothing here touches device memory.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
+#include <utility>
+#include <vector>
 
 #include "../../include/fp8kv.h"
 #include "fp8kv_internal.h"
@@ -109,6 +113,109 @@ int launched(hipError_t e, const char* what) {
     return ok();
 }
 
+// ---------------------------------------------------------------------------
+// Checked mode (fp8kv_set_checked): before a launch, every pointer argument
+// must be device memory of the current device, and the device-resident ids
+// are copied to the host and range-checked. It synchronizes the stream, so
+// it is refused under graph capture. Off by default.
+std::atomic<int> g_checked{0};
+
+bool checked() { return g_checked.load(std::memory_order_relaxed) != 0; }
+
+int checked_begin(void* stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(FP8KV_E_LAUNCH, "checked mode: cannot query the stream's capture state");
+    }
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(FP8KV_E_UNSUPPORTED,
+                    "checked mode synchronizes the stream and cannot run under graph capture");
+    return FP8KV_OK;
+}
+
+int check_device_ptr(const void* ptr, const char* name) {
+    if (!ptr) return FP8KV_OK;             // required pointers were refused as NULL before
+    hipPointerAttribute_t a;
+    const hipError_t e = hipPointerGetAttributes(&a, ptr);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(FP8KV_E_NOT_DEVICE, "%s (%p) is not memory the HIP runtime knows", name, ptr);
+    }
+    if (a.type == hipMemoryTypeManaged || a.isManaged) return FP8KV_OK;
+    if (a.type != hipMemoryTypeDevice)
+        return fail(FP8KV_E_NOT_DEVICE, "%s (%p) is host memory, not device memory", name, ptr);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(FP8KV_E_LAUNCH, "checked mode: no current HIP device");
+    }
+    if (a.device != dev)
+        return fail(FP8KV_E_NOT_DEVICE, "%s (%p) is on device %d, the current device is %d", name,
+                    ptr, a.device, dev);
+    return FP8KV_OK;
+}
+
+int check_device_ptrs(std::initializer_list<std::pair<const void*, const char*>> ptrs) {
+    for (const auto& x : ptrs) {
+        const int st = check_device_ptr(x.first, x.second);
+        if (st != FP8KV_OK) return st;
+    }
+    return FP8KV_OK;
+}
+
+// Host copy of n device elements once the stream's earlier work is done.
+template <class T>
+int fetch(std::vector<T>& h, const T* d, int64_t n, void* stream) {
+    h.resize(static_cast<size_t>(n));
+    if (n == 0) return FP8KV_OK;
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e == hipSuccess)
+        e = hipMemcpy(h.data(), d, static_cast<size_t>(n) * sizeof(T), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(FP8KV_E_LAUNCH, "checked mode: reading device ids failed: %s",
+                    hipGetErrorString(e));
+    }
+    return FP8KV_OK;
+}
+
+// Context lengths within [0, max_context] and, for every request, the
+// table entries of the blocks that hold its tokens within [0, num_blocks);
+// with selected blocks also each valid count within [0, block_size] (an
+// entry with no valid key is never read, so its id is not checked).
+int check_tables(const int32_t* context_lens, const int32_t* block_tables, int64_t bt_stride,
+                 const int32_t* block_valid, int64_t bv_stride, int32_t batch,
+                 int32_t block_size, int64_t num_blocks, int32_t max_context, void* stream,
+                 std::vector<int32_t>* lens_out) {
+    std::vector<int32_t> lens, ids, valid;
+    int st = fetch(lens, context_lens, batch, stream);
+    if (st != FP8KV_OK) return st;
+    for (int32_t b = 0; b < batch; ++b) {
+        if (lens[b] < 0 || lens[b] > max_context)
+            return fail(FP8KV_E_RANGE, "context_lens[%d] = %d is outside [0, max_context = %d]",
+                        b, lens[b], max_context);
+        const int64_t nb = ((int64_t)lens[b] + block_size - 1) / block_size;
+        if ((st = fetch(ids, block_tables + b * bt_stride, nb, stream)) != FP8KV_OK) return st;
+        if (block_valid &&
+            (st = fetch(valid, block_valid + b * bv_stride, nb, stream)) != FP8KV_OK)
+            return st;
+        for (int64_t i = 0; i < nb; ++i) {
+            if (block_valid) {
+                if (valid[i] < 0 || valid[i] > block_size)
+                    return fail(FP8KV_E_RANGE, "block_valid[%d][%lld] = %d is outside [0, %d]", b,
+                                (long long)i, valid[i], block_size);
+                if (valid[i] == 0) continue;
+            }
+            if (ids[i] < 0 || ids[i] >= num_blocks)
+                return fail(FP8KV_E_RANGE, "block_tables[%d][%lld] = %d is outside [0, %lld)", b,
+                            (long long)i, ids[i], (long long)num_blocks);
+        }
+    }
+    if (lens_out) *lens_out = std::move(lens);
+    return FP8KV_OK;
+}
+
 static int decode_partials(
     const void* q, int64_t q_stride_b, int64_t q_stride_row,
     int64_t q_stride_head, int32_t q_dtype, const uint8_t* k_cache,
@@ -165,6 +272,18 @@ static int decode_partials(
     if (cache_stride_slot > (INT32_MAX / 16) || scale_stride_slot > (INT32_MAX / 64))
         return fail(FP8KV_E_SHAPE, "slot stride too large for 32-bit in-block offsets");
     if (batch == 0) return ok();
+    if (checked()) {
+        if ((st = checked_begin(stream)) != FP8KV_OK) return st;
+        st = check_device_ptrs({{q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"},
+                                {k_scale, "k_scale"}, {v_scale, "v_scale"},
+                                {block_tables, "block_tables"}, {block_valid, "block_valid"},
+                                {context_lens, "context_lens"}, {workspace, "workspace"}});
+        if (st != FP8KV_OK) return st;
+        st = check_tables(context_lens, block_tables, block_table_stride, block_valid,
+                          block_valid_stride, batch, block_size, num_blocks, max_context, stream,
+                          nullptr);
+        if (st != FP8KV_OK) return st;
+    }
 
     fp8kv::DecodeParams p;
     p.q = static_cast<const uint16_t*>(q);
@@ -221,11 +340,17 @@ const char* fp8kv_status_string(int status) {
         case FP8KV_E_UNSUPPORTED: return "unsupported combination";
         case FP8KV_E_WORKSPACE: return "workspace too small";
         case FP8KV_E_LAUNCH: return "kernel launch failed";
+        case FP8KV_E_NOT_DEVICE: return "pointer is not device memory (checked mode)";
+        case FP8KV_E_RANGE: return "device id out of range (checked mode)";
         default: return "unknown status";
     }
 }
 
 const char* fp8kv_last_error(void) { return g_last_error; }
+
+int fp8kv_set_checked(int enabled) {
+    return g_checked.exchange(enabled ? 1 : 0);
+}
 
 int fp8kv_kv_quant_scatter(
     const void* k, int64_t k_stride_tok, int64_t k_stride_head,
@@ -262,6 +387,19 @@ int fp8kv_kv_quant_scatter(
     if (!aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(slot_ids, 8))
         return fail(FP8KV_E_ALIGN, "scale planes / slot ids misaligned");
     if (num_tokens == 0) return ok();
+    if (checked()) {
+        int st = checked_begin(stream);
+        if (st != FP8KV_OK) return st;
+        st = check_device_ptrs({{k, "k"}, {v, "v"}, {slot_ids, "slot_ids"}, {k_cache, "k_cache"},
+                                {v_cache, "v_cache"}, {k_scale, "k_scale"}, {v_scale, "v_scale"}});
+        if (st != FP8KV_OK) return st;
+        std::vector<int64_t> slots;
+        if ((st = fetch(slots, slot_ids, num_tokens, stream)) != FP8KV_OK) return st;
+        for (int32_t t = 0; t < num_tokens; ++t)
+            if (slots[t] >= num_slots)
+                return fail(FP8KV_E_RANGE, "slot_ids[%d] = %lld is not below num_slots = %lld", t,
+                            (long long)slots[t], (long long)num_slots);
+    }
 
     fp8kv::QuantScatterParams p;
     p.k = static_cast<const uint16_t*>(k);
@@ -370,6 +508,11 @@ int fp8kv_paged_decode_merge(
     if (!aligned(out, esz) || !aligned(workspace, 256))
         return fail(FP8KV_E_ALIGN, "out or workspace misaligned");
     if (batch == 0) return ok();
+    if (checked()) {
+        if ((st = checked_begin(stream)) != FP8KV_OK) return st;
+        if ((st = check_device_ptrs({{workspace, "workspace"}, {out, "out"}})) != FP8KV_OK)
+            return st;
+    }
     fp8kv::MergeParams p;
     const char* ws = static_cast<const char*>(workspace);
     p.ws_o = reinterpret_cast<const float*>(ws);
@@ -411,6 +554,7 @@ int fp8kv_paged_decode_attn_fp8(
         return fail(FP8KV_E_STRIDE, "paged_decode: negative out stride");
     if (!aligned(out, out_dtype == FP8KV_DTYPE_FP32 ? 4 : 2))
         return fail(FP8KV_E_ALIGN, "out misaligned");
+    if (checked() && batch > 0 && (st = check_device_ptr(out, "out")) != FP8KV_OK) return st;
     st = fp8kv_paged_decode_partials(
         q, q_stride_b, q_stride_row, q_stride_head, q_dtype, k_cache, v_cache,
         cache_stride_slot, cache_stride_head, k_scale, v_scale,
@@ -447,6 +591,7 @@ int fp8kv_sparse_decode_attn_fp8(
         return fail(FP8KV_E_STRIDE, "sparse_decode: negative out stride");
     if (!aligned(out, out_dtype == FP8KV_DTYPE_FP32 ? 4 : 2))
         return fail(FP8KV_E_ALIGN, "out misaligned");
+    if (checked() && batch > 0 && (st = check_device_ptr(out, "out")) != FP8KV_OK) return st;
     st = fp8kv_sparse_decode_partials(
         q, q_stride_b, q_stride_row, q_stride_head, q_dtype, k_cache, v_cache,
         cache_stride_slot, cache_stride_head, k_scale, v_scale,
@@ -517,6 +662,23 @@ int fp8kv_prefill_attn_fp8(
     if (cache_stride_slot > (INT32_MAX / 16) || scale_stride_slot > (INT32_MAX / 64))
         return fail(FP8KV_E_SHAPE, "slot stride too large for 32-bit in-block offsets");
     if (batch == 0 || max_q == 0) return ok();
+    if (checked()) {
+        if ((st = checked_begin(stream)) != FP8KV_OK) return st;
+        st = check_device_ptrs({{q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"},
+                                {k_scale, "k_scale"}, {v_scale, "v_scale"},
+                                {block_tables, "block_tables"}, {context_lens, "context_lens"},
+                                {q_lens, "q_lens"}, {out, "out"}});
+        if (st != FP8KV_OK) return st;
+        std::vector<int32_t> lens, qls;
+        st = check_tables(context_lens, block_tables, block_table_stride, nullptr, 0, batch,
+                          block_size, num_blocks, max_context, stream, &lens);
+        if (st != FP8KV_OK) return st;
+        if ((st = fetch(qls, q_lens, batch, stream)) != FP8KV_OK) return st;
+        for (int32_t b = 0; b < batch; ++b)
+            if (qls[b] < 0 || qls[b] > max_q || qls[b] > lens[b])
+                return fail(FP8KV_E_RANGE, "q_lens[%d] = %d is outside [0, min(max_q = %d, "
+                            "context_lens[%d] = %d)]", b, qls[b], max_q, b, lens[b]);
+    }
     fp8kv::PrefillParams p;
     p.q = static_cast<const uint16_t*>(q);
     p.q_stride_b = q_stride_b;
@@ -577,6 +739,12 @@ int fp8kv_index_keys_quantize(
     if (e4m3 && !aligned(scales, 4))
         return fail(FP8KV_E_ALIGN, "fp32 key scales misaligned");
     if (num_keys == 0) return ok();
+    if (checked()) {
+        int st = checked_begin(stream);
+        if (st != FP8KV_OK) return st;
+        st = check_device_ptrs({{keys, "keys"}, {codes, "codes"}, {scales, "scales"}});
+        if (st != FP8KV_OK) return st;
+    }
     fp8kv::IndexKeysParams p;
     p.keys = static_cast<const uint16_t*>(keys);
     p.key_stride = key_stride;
@@ -616,6 +784,12 @@ int fp8kv_index_keys_build(
     if (key_format == FP8KV_KEYS_E4M3 && !aligned(scales, 4))
         return fail(FP8KV_E_ALIGN, "fp32 key scales misaligned");
     if (batch == 0 || g1 == g0) return ok();
+    if (checked()) {
+        int st = checked_begin(stream);
+        if (st != FP8KV_OK) return st;
+        st = check_device_ptrs({{raw, "raw"}, {codes, "codes"}, {scales, "scales"}});
+        if (st != FP8KV_OK) return st;
+    }
     fp8kv::IndexBuildParams p;
     p.raw = static_cast<const uint16_t*>(raw);
     p.raw_stride_b = raw_stride_b;
@@ -669,6 +843,13 @@ int fp8kv_index_score_mxfp4(
     if (!aligned(w, 4) || !aligned(out, 4) || (e4m3 && !aligned(scales, 4)))
         return fail(FP8KV_E_ALIGN, "w, out or key scales misaligned");
     if (batch == 0 || num_keys == 0) return ok();
+    if (checked()) {
+        int st = checked_begin(stream);
+        if (st != FP8KV_OK) return st;
+        st = check_device_ptrs({{q, "q"}, {w, "w"}, {codes, "codes"}, {scales, "scales"},
+                                {out, "out"}});
+        if (st != FP8KV_OK) return st;
+    }
 
     const int32_t row_groups = (rows + fp8kv::kIndexRowsPerBlock - 1) / fp8kv::kIndexRowsPerBlock;
     int32_t chunk = key_chunk;

@@ -38,6 +38,8 @@
  *     arguments.
  *   - fp8kv_last_error() returns a thread-local description of the most
  *     recent failure on the calling thread.
+ *   - An optional checked mode (fp8kv_set_checked) adds pointer-kind and
+ *     id-range checks that synchronize; it is off by default.
  */
 #ifndef FP8KV_H
 #define FP8KV_H
@@ -49,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FP8KV_ABI_VERSION 6
+#define FP8KV_ABI_VERSION 7
 
 typedef enum fp8kv_status {
     FP8KV_OK = 0,
@@ -61,7 +63,11 @@ typedef enum fp8kv_status {
                                /* the vector loads/stores need              */
     FP8KV_E_UNSUPPORTED = -5,  /* dtype / head_dim / grouping not supported */
     FP8KV_E_WORKSPACE = -6,    /* workspace NULL or smaller than required   */
-    FP8KV_E_LAUNCH = -7        /* the HIP runtime reported a launch error   */
+    FP8KV_E_LAUNCH = -7,       /* the HIP runtime reported a launch error   */
+    FP8KV_E_NOT_DEVICE = -8,   /* checked mode: a pointer is not device     */
+                               /* memory of the current device              */
+    FP8KV_E_RANGE = -9         /* checked mode: a device-resident id or     */
+                               /* length is out of range                    */
 } fp8kv_status;
 
 typedef enum fp8kv_dtype {
@@ -73,6 +79,31 @@ typedef enum fp8kv_dtype {
 int fp8kv_abi_version(void);
 const char* fp8kv_status_string(int status);
 const char* fp8kv_last_error(void);
+
+/*
+ * fp8kv_set_checked -- switch the process-wide checked mode on (enabled !=
+ * 0) or off; returns the previous setting (0 or 1). Off by default.
+ *
+ * The pages report a CPU tensor reaching the kernel as a real failure, and
+ * out-of-range ids as undefined on the fast path ("feat(kvcache): store the
+ * KV cache as fp8 e4m3 codes", FreeToken #354, review thread). In checked
+ * mode every call, after its O(1) checks and before it enqueues anything:
+ *   - refuses, with FP8KV_E_NOT_DEVICE, a pointer argument that is not
+ *     device (or managed) memory of the current device
+ *     (hipPointerGetAttributes);
+ *   - synchronizes `stream`, copies the device-resident ids to the host and
+ *     refuses, with FP8KV_E_RANGE: a slot id >= num_slots (ids < 0 stay
+ *     padding); a context length outside [0, max_context]; a block-table
+ *     entry of a request's tokens outside [0, num_slots / block_size); a
+ *     selected block's valid count outside [0, block_size] (an entry with
+ *     count 0 is never read and its id is not checked); a prefill q_lens
+ *     entry outside [0, min(max_q, context length)].
+ * Because it synchronizes, checked mode refuses to run under graph capture
+ * (FP8KV_E_UNSUPPORTED), and it breaks the "never synchronizes or reads
+ * device memory" convention above by design; the fast path (the default)
+ * keeps it, bounding every id inside the kernels instead.
+ */
+int fp8kv_set_checked(int enabled);
 
 /*
  * fp8kv_kv_quant_scatter -- quantize K and V rows to E4M3 + fp32 row scales

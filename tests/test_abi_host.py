@@ -18,6 +18,7 @@ HEADER = os.path.join(ROOT, "include", "fp8kv.h")
 
 OK, E_NULL, E_SHAPE, E_STRIDE, E_ALIGN, E_UNSUPPORTED, E_WORKSPACE, E_LAUNCH = \
     0, -1, -2, -3, -4, -5, -6, -7
+E_NOT_DEVICE, E_RANGE = -8, -9
 BF16, FP16, FP32 = 1, 2, 3
 
 
@@ -48,8 +49,37 @@ def test_abi_version_and_strings(L):
     ver = int(re.search(r"#define FP8KV_ABI_VERSION (\d+)", text).group(1))
     assert L.fp8kv_abi_version() == ver
     for st in (OK, E_NULL, E_SHAPE, E_STRIDE, E_ALIGN, E_UNSUPPORTED,
-               E_WORKSPACE, E_LAUNCH):
+               E_WORKSPACE, E_LAUNCH, E_NOT_DEVICE, E_RANGE):
         assert L.fp8kv_status_string(st).decode() != "unknown status"
+    for name, st in (("E_NOT_DEVICE", E_NOT_DEVICE), ("E_RANGE", E_RANGE)):
+        assert re.search(rf"FP8KV_{name} = {st}\b", text), name
+
+
+def test_checked_mode_switch(L):
+    prev = L.fp8kv_set_checked(1)
+    try:
+        assert L.fp8kv_set_checked(1) == 1
+        assert L.fp8kv_set_checked(0) == 1
+        assert L.fp8kv_set_checked(0) == 0
+        assert L.fp8kv_set_checked(7) == 0       # any nonzero value switches it on
+        assert L.fp8kv_set_checked(0) == 1
+    finally:
+        L.fp8kv_set_checked(prev)
+
+
+def test_checked_mode_keeps_the_host_checks_first(L):
+    """In checked mode the O(1) refusals still come first, and a call whose
+    pointers the runtime does not know as device memory is refused (here:
+    fake addresses) -- nothing is launched either way."""
+    prev = L.fp8kv_set_checked(1)
+    try:
+        assert qs(L, k=0) == E_NULL
+        assert qs(L, D=96) == E_UNSUPPORTED
+        st = qs(L)
+        assert st in (E_NOT_DEVICE, E_LAUNCH), st    # E_LAUNCH: no HIP device here
+        assert L.fp8kv_last_error().decode()
+    finally:
+        L.fp8kv_set_checked(prev)
 
 
 # A fake, well-aligned "device" address: validation never dereferences it.
