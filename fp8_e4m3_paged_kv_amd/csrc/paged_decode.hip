@@ -809,6 +809,12 @@ hipError_t launch_split_bs(const DecodeParams& p, hipStream_t stream) {
 // the scales as four consecutive tokens per lane (no lane broadcast needed).
 // Workgroups of one (request, KV head) run on one XCD, the deepest query
 // blocks first.
+// The prefill kernel keeps a row's running maximum until a tile's scores
+// exceed it by more than kLazyMax (log2 units), so p = exp2(s - m) stays
+// below 2^kLazyMax; its P' range factor is 2^(141 - kLazyMax - e), which
+// keeps P' below 2^15 as in the decode kernel.
+constexpr int kLazyMax = 8;
+
 template <int D, bool BSP2, int NT>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     constexpr int KSTEPS = D / 32;
@@ -975,7 +981,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
         const bool ef_up = ef_new > ef_run;
         const float fe = pow2i(max(ef_run - ef_new, -126));
         ef_run = ef_new;
-        const float kappa = pow2i(141 - ef_run);
+        const float kappa = pow2i(141 - kLazyMax - ef_run);
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -1001,9 +1007,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) s2[s][r] = 16 * s + r <= d ? s2[s][r] : kNeg;
             }
+            // lazy maximum: the running maximum moves only when a score
+            // exceeds it by more than kLazyMax, so most tiles skip the rescale
             const float mt = rows_max_fin(max8(s2));
-            const float m_new = fmax_fin(st[j].m_run, mt);
-            if (__any(m_new > st[j].m_run) || ef_up) {
+            if (__any(mt > st[j].m_run + kLazyMax) || ef_up) {
+                const float m_new = fmax_fin(st[j].m_run, mt);
                 const float a = __builtin_amdgcn_exp2f(st[j].m_run - m_new);
                 const float f = a * fe;
 #pragma unroll
@@ -1035,7 +1043,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     }
 
     // normalized output of row li of each tile: dims [DL*4 lg, DL*4 lg + DL*4)
-    const float un = pow2i(max(ef_run - 141, -126));
+    const float un = pow2i(max(ef_run - 141 + kLazyMax, -126));
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         const float l_sum = rows_sum(st[j].l_run);

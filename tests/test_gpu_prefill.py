@@ -62,6 +62,33 @@ def test_chunk_matches_oracle(lens, C, Hq, Hkv, D, bs):
     assert torch.equal(ob, bf16_rne(out)), "bf16 output is not RNE of fp32"
 
 
+def test_value_ranges_and_growing_scores():
+    """Mixed V magnitudes (rows x1e-3, x100, zero, ~1e-33) with 1% K outlier
+    channels, and K rows whose size grows along the sequence, so a row's
+    running maximum moves many times, also by more than the kernel's lazy
+    maximum slack."""
+    case = synth.decode_case([900, 1500], 16, 4, 128, 16, rows=70, seed=98,
+                             k_outlier_frac=0.01)
+    T, H = case.k.shape[0], case.num_kv_heads
+    g = torch.Generator().manual_seed(99)
+    grow = torch.linspace(0.2, 6.0, T)[:, None, None]
+    case.k = (case.k.float() * grow).to(torch.bfloat16)
+    mult = torch.tensor([1.0, 1e-3, 100.0, 0.0])[torch.randint(0, 4, (T, H), generator=g)]
+    vf = case.v.float() * mult[..., None]
+    vf[torch.rand(T, H, generator=g) < 0.01] *= 1e-33
+    case.v = vf.to(torch.bfloat16)
+    log("prefill value ranges / growing scores")
+    dc = cache_case(case, DEV)
+    out = run_prefill(case, dc)
+    torch.cuda.synchronize()
+    ref = oracle_prefill(case, dc.host())
+    # V rows x100 put outputs in the hundreds: the bar applies to the
+    # output scaled to a unit maximum
+    scale = float(np.abs(ref).max())
+    assert scale > 0
+    assert_attn_close(out.cpu().numpy() / scale, ref / scale, "value ranges (scaled)")
+
+
 def test_per_request_chunk_lengths_and_untouched_rows():
     case = synth.decode_case([400, 350, 90], 32, 8, 128, 16, rows=48, seed=70)
     dc = cache_case(case, DEV)
