@@ -16,10 +16,14 @@ events on the stream it runs on, for the roofline object.
 Also measured in the same run (reported under "also"): quantize+scatter
 tokens/s on the 4096-token prefill chunk (fused qkv, K/V strided slices,
 random slots in a 1,048,576-slot pool, 32 rotating input sets so reads come
-from HBM), the cache-build bandwidth, the long-context verify decode
-(4 requests of 256K..1M tokens, 4 verify rows, 16/4 heads, 64-token
-blocks), and the compressed-index scorer (8 x 256 rows x 16 heads x 65,536
-keys, MXFP4 and E4M3 keys) with its key encoders.
+from HBM, replayed from a HIP graph), the cache-build bandwidth, the
+long-context verify decode (4 requests of 256K..1M tokens, 4 verify rows,
+16/4 heads, 64-token blocks), the decode over selected blocks (1/8 of the
+decode workload's blocks), chunked-prefill attention (a 4096-token chunk
+after 28,672 cached tokens), the compressed-index scorer (8 x 256 rows x 16
+heads x 65,536 keys, MXFP4 and E4M3 keys) with its key encoders and key
+builder, and the HBM ceilings of plain library copy and read kernels on the
+same GPU.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -52,9 +56,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the prefill-chunk, long-context and index extras")
-    ap.add_argument("--extras", default="prefill,longctx,sparse,prefill_attn,index",
+    ap.add_argument("--extras", default="prefill,longctx,sparse,prefill_attn,index,ceilings",
                     help="comma list of the extras to run (prefill, longctx, sparse, "
-                         "prefill_attn, index)")
+                         "prefill_attn, index, ceilings)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times "
                          "(the known-size reference for HBM byte counters)")
@@ -369,6 +373,8 @@ def main():
         result["also"].update(prefill_attention(torch, fk, synth, dev, stream))
     if "index" in extras:
         result["also"].update(index_scorer(torch, fk, synth, dev, stream))
+    if "ceilings" in extras:
+        result["also"].update(hbm_ceilings(torch, dev, stream))
 
     if not args.no_cpu_baseline:
         log("timing the oracle on host cores...")
@@ -526,6 +532,25 @@ def sparse_decode(torch, fk, synth, dev, stream, case, q, bt, k_cache, v_cache,
             "sparse_decode_us": round(f_avg * 1e3, 1),
             "sparse_split_kernel_us": round(p_avg * 1e3, 1),
             "sparse_split_kernel_GBps": round(alg / (p_avg * 1e-3) / 1e9, 1)}
+
+
+def hbm_ceilings(torch, dev, stream, gib=2, reps=10):
+    """What plain library kernels reach on this GPU: a device copy of 2 GiB
+    (read + write bytes) and an int64 sum over 2 GiB (read bytes)."""
+    log("HBM ceilings (library copy and read kernels)...")
+    n = gib << 30
+    src = torch.ones(n // 8, dtype=torch.int64, device=dev)
+    dst = torch.empty_like(src)
+    res = {}
+    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * n),
+                            ("read", lambda: src.sum(), n)):
+        for _ in range(3):
+            fn()
+        ms = sorted(time_events(fn, reps, stream))
+        res[f"hbm_{name}_ceiling_GBps"] = round(moved / (ms[len(ms) // 2] * 1e-3) / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return res
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
