@@ -69,6 +69,9 @@ def _load():
     lib.fo_kv_quant_scatter_bf16.argtypes = [P, I64, I64, P, I64, I64,
                                              I64, I64, I64, P, I64,
                                              P, P, I64, I64, P, P, I64, I64]
+    lib.fo_kv_scatter_unscaled_bf16.argtypes = [I, P, I64, I64, P, I64, I64,
+                                                I64, I64, I64, P, I64,
+                                                P, P, I64, I64]
     lib.fo_attend_dense.argtypes = [P, P, P, I64, I64, D, P]
     lib.fo_paged_decode_attn.argtypes = [I, P, I64, I64, I64, P, P, I64, I64,
                                          P, P, I64, I64, P, I64, P,
@@ -189,6 +192,26 @@ def kv_quant_scatter_bf16(k, v, slot_ids, k_cache, v_cache, k_scale, v_scale,
         _ptr(k), ks[0], ks[1], _ptr(v), vs[0], vs[1], T, H, D,
         _ptr(slots), num_slots, _ptr(k_cache), _ptr(v_cache), cs[0], cs[1],
         _ptr(k_scale), _ptr(v_scale), ss[0], ss[1])
+
+
+def kv_scatter_unscaled_bf16(fmt, k, v, slot_ids, k_cache, v_cache, num_slots=None):
+    """In-place unscaled encode + scatter (no scale planes): every element is
+    encoded by itself in fmt (E4M3 or E5M2), saturating. Views as in
+    kv_quant_scatter_bf16."""
+    assert k.dtype == np.uint16 and v.dtype == np.uint16
+    assert k.shape == v.shape and k.ndim == 3
+    T, H, D = k.shape
+    ks, vs = _estrides(k), _estrides(v)
+    assert ks[2] == 1 and vs[2] == 1
+    slots = np.ascontiguousarray(np.asarray(slot_ids, dtype=np.int64))
+    assert slots.shape == (T,)
+    cs = _estrides(k_cache)
+    assert _estrides(v_cache) == cs and cs[2] == 1
+    if num_slots is None:
+        num_slots = k_cache.shape[0]
+    _load().fo_kv_scatter_unscaled_bf16(
+        int(fmt), _ptr(k), ks[0], ks[1], _ptr(v), vs[0], vs[1], T, H, D,
+        _ptr(slots), num_slots, _ptr(k_cache), _ptr(v_cache), cs[0], cs[1])
 
 
 def attend_dense(q, keys, vals, scale):

@@ -69,6 +69,18 @@ void fo_kv_quant_scatter_bf16(
     float* k_scale, float* v_scale,
     int64_t scale_stride_slot, int64_t scale_stride_head);
 
+/* The unscaled cache: every element encoded by itself in fmt (saturating),
+ * placed like the scaled codes, no scale planes. Parity: pinned by the
+ * codec pins, torch casts of in-range values and a sentinel pool. */
+void fo_kv_scatter_unscaled_bf16(
+    int fmt,
+    const uint16_t* k, int64_t k_stride_tok, int64_t k_stride_head,
+    const uint16_t* v, int64_t v_stride_tok, int64_t v_stride_head,
+    int64_t num_tokens, int64_t num_kv_heads, int64_t head_dim,
+    const int64_t* slot_ids, int64_t num_slots,
+    uint8_t* k_cache, uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head);
+
 /* ---- attention (attn.c) ------------------------------------------------- */
 /* Dense softmax attention of one query row over n already-dequantized keys:
  * out[d] = sum_j softmax_j(scale * q.k_j) * v_j[d], all in double. n == 0

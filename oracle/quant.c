@@ -101,3 +101,34 @@ void fo_kv_quant_scatter_bf16(
     free(codes);
     free(row);
 }
+
+/* The unscaled cache ("feat(dsa): implement fp8 KV cache (e4m3) with a bf16
+ * indexer cache", sglang-jax #1776, description and "Three design points":
+ * new K/V are cast to the cache dtype with no scale). Each element is
+ * encoded by itself in fmt (nearest, ties to even, saturating to the
+ * format's largest finite value) and placed like the scaled codes; there
+ * are no scale planes. */
+void fo_kv_scatter_unscaled_bf16(
+    int fmt,
+    const uint16_t* k, int64_t k_stride_tok, int64_t k_stride_head,
+    const uint16_t* v, int64_t v_stride_tok, int64_t v_stride_head,
+    int64_t num_tokens, int64_t num_kv_heads, int64_t head_dim,
+    const int64_t* slot_ids, int64_t num_slots,
+    uint8_t* k_cache, uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head) {
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        const int64_t slot = slot_ids[t];
+        if (slot < 0 || slot >= num_slots) continue;
+        for (int64_t h = 0; h < num_kv_heads; ++h) {
+            for (int kv = 0; kv < 2; ++kv) {
+                const uint16_t* src = kv == 0
+                    ? k + t * k_stride_tok + h * k_stride_head
+                    : v + t * v_stride_tok + h * v_stride_head;
+                uint8_t* dst = (kv == 0 ? k_cache : v_cache) +
+                               slot * cache_stride_slot + h * cache_stride_head;
+                for (int64_t d = 0; d < head_dim; ++d)
+                    dst[d] = (uint8_t)fo_encode(fmt, fo_bf16_to_f32(src[d]));
+            }
+        }
+    }
+}
