@@ -70,6 +70,14 @@ def lib():
     L.fp8kv_paged_decode_attn_fp8.restype = ctypes.c_int
     L.fp8kv_paged_decode_partials.argtypes = dec + [P]
     L.fp8kv_paged_decode_partials.restype = ctypes.c_int
+    L.fp8kv_kv_quant_scatter_unscaled.argtypes = [P, I64, I64, P, I64, I64, I32, I32,
+                                                  I32, I32, P, P, P, I64, I64, I64, I32, P]
+    L.fp8kv_kv_quant_scatter_unscaled.restype = ctypes.c_int
+    udec = dec[:9] + dec[13:]                 # no scale planes
+    L.fp8kv_paged_decode_attn_unscaled.argtypes = udec + [P, I64, I64, I64, I32, I32, P]
+    L.fp8kv_paged_decode_attn_unscaled.restype = ctypes.c_int
+    L.fp8kv_paged_decode_partials_unscaled.argtypes = udec + [I32, P]
+    L.fp8kv_paged_decode_partials_unscaled.restype = ctypes.c_int
     sdec = dec[:16] + [P, I64] + dec[16:]
     L.fp8kv_sparse_decode_attn_fp8.argtypes = sdec + [P, I64, I64, I64, I32, P]
     L.fp8kv_sparse_decode_attn_fp8.restype = ctypes.c_int
@@ -194,6 +202,39 @@ def kv_quant_scatter(k: torch.Tensor, v: torch.Tensor, slot_ids: torch.Tensor,
         _stream(k.device)))
 
 
+CODES_E4M3 = 0   # unscaled cache code formats
+CODES_E5M2 = 1
+
+
+def kv_quant_scatter_unscaled(k: torch.Tensor, v: torch.Tensor, slot_ids: torch.Tensor,
+                              k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              code_format: int = CODES_E4M3) -> None:
+    """Store K and V ([T, Hkv, D] bf16 views) as unscaled E4M3 or E5M2 codes
+    (round to nearest even, saturating) at ``slot_ids``; no scale planes."""
+    _dev(k, v, slot_ids, k_cache, v_cache)
+    if k.dim() != 3 or v.shape != k.shape or k.dtype not in _TORCH_DTYPE or v.dtype != k.dtype:
+        raise ValueError("k and v must be [T, Hkv, D] views of one float dtype")
+    if k.stride(2) != 1 or v.stride(2) != 1:
+        raise ValueError("head_dim must be the contiguous dimension")
+    if slot_ids.dtype != torch.int64 or slot_ids.shape != (k.shape[0],) or \
+            not slot_ids.is_contiguous():
+        raise ValueError("slot_ids must be contiguous int64 [T]")
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("code buffers are uint8")
+    css, csh, S, H, D = _cache_strides(k_cache)
+    if _cache_strides(v_cache)[:2] != (css, csh):
+        raise ValueError("k_cache and v_cache must share strides")
+    T, Hk, Dk = k.shape
+    if (Hk, Dk) != (H, D):
+        raise ValueError("K/V head count or head_dim differs from the cache")
+    _check(lib().fp8kv_kv_quant_scatter_unscaled(
+        k.data_ptr(), k.stride(0), k.stride(1),
+        v.data_ptr(), v.stride(0), v.stride(1),
+        _TORCH_DTYPE[k.dtype], T, H, D, slot_ids.data_ptr(),
+        k_cache.data_ptr(), v_cache.data_ptr(), css, csh, S,
+        int(code_format), _stream(k.device)))
+
+
 def decode_workspace_bytes(batch, rows, num_q_heads, num_kv_heads, head_dim,
                            num_ranges=0) -> int:
     """Workspace bytes of a decode call (num_ranges 0 = library choice)."""
@@ -216,7 +257,12 @@ def decode_num_ranges(num_kv_heads, num_ranges=0) -> int:
 def _decode_args(q, k_cache, v_cache, k_scale, v_scale, block_tables,
                  context_lens, num_kv_heads, block_size, softmax_scale,
                  max_context, num_ranges, workspace):
-    _dev(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens)
+    """Argument list of the scaled decode calls; with k_scale = v_scale =
+    None that of the unscaled ones (no scale planes)."""
+    unscaled = k_scale is None and v_scale is None
+    _dev(q, k_cache, v_cache, block_tables, context_lens)
+    if not unscaled:
+        _dev(k_scale, v_scale)
     if q.dim() != 4 or q.stride(3) != 1:
         raise ValueError("q must be [B, R, Hq, D] with contiguous head_dim")
     if q.dtype not in _TORCH_DTYPE:
@@ -230,17 +276,19 @@ def _decode_args(q, k_cache, v_cache, k_scale, v_scale, block_tables,
     css, csh, S, H, Dc = _cache_strides(k_cache)
     if _cache_strides(v_cache)[:2] != (css, csh) or H != num_kv_heads or Dc != D:
         raise ValueError("cache geometry does not match q / num_kv_heads")
-    sss, ssh = _scale_strides(k_scale)
-    if _scale_strides(v_scale) != (sss, ssh):
-        raise ValueError("k_scale and v_scale must share strides")
+    if not unscaled:
+        sss, ssh = _scale_strides(k_scale)
+        if _scale_strides(v_scale) != (sss, ssh):
+            raise ValueError("k_scale and v_scale must share strides")
     ws_bytes = decode_workspace_bytes(B, R, Hq, num_kv_heads, D, num_ranges)
     if workspace is None:
         workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8,
                                 device=q.device)
     _dev(workspace)
+    scales = [] if unscaled else [k_scale.data_ptr(), v_scale.data_ptr(), sss, ssh]
     args = [q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
             _TORCH_DTYPE[q.dtype], k_cache.data_ptr(), v_cache.data_ptr(),
-            css, csh, k_scale.data_ptr(), v_scale.data_ptr(), sss, ssh, S,
+            css, csh] + scales + [S,
             block_tables.data_ptr(), block_tables.stride(0),
             context_lens.data_ptr(), B, R, Hq, num_kv_heads, D, block_size,
             float(softmax_scale), int(num_ranges), int(max_context),
@@ -280,6 +328,38 @@ def paged_decode_partials(q, k_cache, v_cache, k_scale, v_scale, block_tables,
                                    block_size, softmax_scale, max_context,
                                    num_ranges, workspace)
     _check(lib().fp8kv_paged_decode_partials(*args, _stream(q.device)))
+    return workspace
+
+
+def paged_decode_attn_unscaled(q, k_cache, v_cache, block_tables, context_lens, *,
+                               num_kv_heads, block_size, softmax_scale, max_context,
+                               code_format=CODES_E4M3, num_ranges=0, out=None,
+                               out_dtype=torch.bfloat16, workspace=None):
+    """Paged GQA decode attention over an unscaled E4M3 or E5M2 cache
+    (scale 1); otherwise as paged_decode_attn_fp8."""
+    args, workspace = _decode_args(q, k_cache, v_cache, None, None, block_tables,
+                                   context_lens, num_kv_heads, block_size,
+                                   softmax_scale, max_context, num_ranges, workspace)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _dev(out)
+    if out.shape != q.shape or out.stride(3) != 1:
+        raise ValueError("out must be [B, R, Hq, D] with contiguous head_dim")
+    _check(lib().fp8kv_paged_decode_attn_unscaled(
+        *args, out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
+        _TORCH_DTYPE[out.dtype], int(code_format), _stream(q.device)))
+    return out
+
+
+def paged_decode_partials_unscaled(q, k_cache, v_cache, block_tables, context_lens, *,
+                                   num_kv_heads, block_size, softmax_scale, max_context,
+                                   code_format=CODES_E4M3, num_ranges=0, workspace=None):
+    """Split phase only over an unscaled cache; returns the workspace."""
+    args, workspace = _decode_args(q, k_cache, v_cache, None, None, block_tables,
+                                   context_lens, num_kv_heads, block_size,
+                                   softmax_scale, max_context, num_ranges, workspace)
+    _check(lib().fp8kv_paged_decode_partials_unscaled(*args, int(code_format),
+                                                      _stream(q.device)))
     return workspace
 
 

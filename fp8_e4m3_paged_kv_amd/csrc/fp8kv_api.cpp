@@ -228,10 +228,11 @@ static int decode_partials(
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
     int32_t block_size, float softmax_scale, int32_t num_ranges,
     int32_t max_context, void* workspace, size_t workspace_bytes,
-    void* stream) {
+    int32_t codes, void* stream) {
     DecodeShape s;
     int st = decode_shape(batch, rows, num_q_heads, num_kv_heads, head_dim, num_ranges, &s);
     if (st != FP8KV_OK) return st;
+    const bool scaled = codes == fp8kv::kCodesE4M3Scaled;
     if (q_dtype != FP8KV_DTYPE_BF16)
         return fail(FP8KV_E_UNSUPPORTED, "q_dtype %d: only BF16 queries", q_dtype);
     if (block_size < 16 || block_size % 16 != 0)
@@ -240,7 +241,7 @@ static int decode_partials(
         return fail(FP8KV_E_SHAPE, "max_context (%d) must be >= 0", max_context);
     if ((int64_t)batch * ((max_context + 31) / 32) > INT32_MAX)
         return fail(FP8KV_E_SHAPE, "batch * max_context too large for 32-bit tile counts");
-    if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables ||
+    if (!q || !k_cache || !v_cache || (scaled && (!k_scale || !v_scale)) || !block_tables ||
         !context_lens)
         return fail(FP8KV_E_NULL, "paged_decode: a required pointer is NULL");
     if (!workspace)
@@ -258,7 +259,7 @@ static int decode_partials(
     if (!aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         cache_stride_slot % 16 || cache_stride_head % 16)
         return fail(FP8KV_E_ALIGN, "cache rows must start on 16-byte boundaries");
-    if (!aligned(k_scale, 4) || !aligned(v_scale, 4) ||
+    if ((scaled && (!aligned(k_scale, 4) || !aligned(v_scale, 4))) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
         !aligned(block_valid, 4) || !aligned(workspace, 256))
         return fail(FP8KV_E_ALIGN, "scale planes, tables or workspace misaligned");
@@ -316,6 +317,7 @@ static int decode_partials(
     p.num_ranges = s.num_ranges;
     p.wgs_per_range = (num_kv_heads % 4 == 0 && num_kv_heads > 4) ? num_kv_heads / 4 : 1;
     p.score_scale_log2 = softmax_scale * 1.4426950408889634f;
+    p.codes = codes;
     char* ws = static_cast<char*>(workspace);
     p.ws_o = reinterpret_cast<float*>(ws);
     p.ws_lse = reinterpret_cast<float*>(ws + s.lse_offset_bytes);
@@ -352,14 +354,15 @@ int fp8kv_set_checked(int enabled) {
     return g_checked.exchange(enabled ? 1 : 0);
 }
 
-int fp8kv_kv_quant_scatter(
+static int quant_scatter(
     const void* k, int64_t k_stride_tok, int64_t k_stride_head,
     const void* v, int64_t v_stride_tok, int64_t v_stride_head,
     int32_t in_dtype, int32_t num_tokens, int32_t num_kv_heads,
     int32_t head_dim, const int64_t* slot_ids, uint8_t* k_cache,
     uint8_t* v_cache, int64_t cache_stride_slot, int64_t cache_stride_head,
     float* k_scale, float* v_scale, int64_t scale_stride_slot,
-    int64_t scale_stride_head, int64_t num_slots, void* stream) {
+    int64_t scale_stride_head, int64_t num_slots, int32_t codes, void* stream) {
+    const bool scaled = codes == fp8kv::kCodesE4M3Scaled;
     if (in_dtype != FP8KV_DTYPE_BF16)
         return fail(FP8KV_E_UNSUPPORTED, "in_dtype %d: only BF16 K/V inputs", in_dtype);
     if (head_dim != 64 && head_dim != 128)
@@ -367,7 +370,7 @@ int fp8kv_kv_quant_scatter(
     if (num_tokens < 0 || num_kv_heads < 1 || num_slots < 0)
         return fail(FP8KV_E_SHAPE, "num_tokens %d, num_kv_heads %d, num_slots %lld",
                     num_tokens, num_kv_heads, (long long)num_slots);
-    if (!k || !v || !slot_ids || !k_cache || !v_cache || !k_scale || !v_scale)
+    if (!k || !v || !slot_ids || !k_cache || !v_cache || (scaled && (!k_scale || !v_scale)))
         return fail(FP8KV_E_NULL, "kv_quant_scatter: a required pointer is NULL");
     if (k_stride_tok < 0 || k_stride_head < 0 || v_stride_tok < 0 ||
         v_stride_head < 0 || cache_stride_slot < 0 || cache_stride_head < 0 ||
@@ -384,7 +387,7 @@ int fp8kv_kv_quant_scatter(
     if (!aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         cache_stride_slot % 16 || cache_stride_head % 16)
         return fail(FP8KV_E_ALIGN, "cache rows must start on 16-byte boundaries");
-    if (!aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(slot_ids, 8))
+    if ((scaled && (!aligned(k_scale, 4) || !aligned(v_scale, 4))) || !aligned(slot_ids, 8))
         return fail(FP8KV_E_ALIGN, "scale planes / slot ids misaligned");
     if (num_tokens == 0) return ok();
     if (checked()) {
@@ -421,8 +424,48 @@ int fp8kv_kv_quant_scatter(
     p.num_tokens = num_tokens;
     p.num_kv_heads = num_kv_heads;
     p.num_rows = (int64_t)num_tokens * num_kv_heads * 2;
+    p.codes = codes;
     return launched(fp8kv::launch_kv_quant_scatter(p, head_dim, (hipStream_t)stream),
                     "kv_quant_scatter");
+}
+
+int fp8kv_kv_quant_scatter(
+    const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+    const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+    int32_t in_dtype, int32_t num_tokens, int32_t num_kv_heads,
+    int32_t head_dim, const int64_t* slot_ids, uint8_t* k_cache,
+    uint8_t* v_cache, int64_t cache_stride_slot, int64_t cache_stride_head,
+    float* k_scale, float* v_scale, int64_t scale_stride_slot,
+    int64_t scale_stride_head, int64_t num_slots, void* stream) {
+    return quant_scatter(k, k_stride_tok, k_stride_head, v, v_stride_tok, v_stride_head,
+                         in_dtype, num_tokens, num_kv_heads, head_dim, slot_ids, k_cache,
+                         v_cache, cache_stride_slot, cache_stride_head, k_scale, v_scale,
+                         scale_stride_slot, scale_stride_head, num_slots,
+                         fp8kv::kCodesE4M3Scaled, stream);
+}
+
+// FP8KV_CODES_* of the public header -> the kernels' unscaled formats
+static int unscaled_codes(int32_t code_format, int32_t* codes) {
+    if (code_format == FP8KV_CODES_E4M3) *codes = fp8kv::kCodesE4M3;
+    else if (code_format == FP8KV_CODES_E5M2) *codes = fp8kv::kCodesE5M2;
+    else return fail(FP8KV_E_UNSUPPORTED, "code_format %d: E4M3 (0) or E5M2 (1)", code_format);
+    return FP8KV_OK;
+}
+
+int fp8kv_kv_quant_scatter_unscaled(
+    const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+    const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+    int32_t in_dtype, int32_t num_tokens, int32_t num_kv_heads,
+    int32_t head_dim, const int64_t* slot_ids, uint8_t* k_cache,
+    uint8_t* v_cache, int64_t cache_stride_slot, int64_t cache_stride_head,
+    int64_t num_slots, int32_t code_format, void* stream) {
+    int32_t codes = 0;
+    const int st = unscaled_codes(code_format, &codes);
+    if (st != FP8KV_OK) return st;
+    return quant_scatter(k, k_stride_tok, k_stride_head, v, v_stride_tok, v_stride_head,
+                         in_dtype, num_tokens, num_kv_heads, head_dim, slot_ids, k_cache,
+                         v_cache, cache_stride_slot, cache_stride_head, nullptr, nullptr, 0, 0,
+                         num_slots, codes, stream);
 }
 
 int64_t fp8kv_paged_decode_workspace_bytes(
@@ -459,7 +502,8 @@ int fp8kv_paged_decode_partials(
                            scale_stride_slot, scale_stride_head, num_slots, block_tables,
                            block_table_stride, nullptr, 0, context_lens, batch, rows,
                            num_q_heads, num_kv_heads, head_dim, block_size, softmax_scale,
-                           num_ranges, max_context, workspace, workspace_bytes, stream);
+                           num_ranges, max_context, workspace, workspace_bytes,
+                           fp8kv::kCodesE4M3Scaled, stream);
 }
 
 int fp8kv_sparse_decode_partials(
@@ -483,7 +527,29 @@ int fp8kv_sparse_decode_partials(
                            block_table_stride, block_valid, block_valid_stride, context_lens,
                            batch, rows, num_q_heads, num_kv_heads, head_dim, block_size,
                            softmax_scale, num_ranges, max_context, workspace,
-                           workspace_bytes, stream);
+                           workspace_bytes, fp8kv::kCodesE4M3Scaled, stream);
+}
+
+int fp8kv_paged_decode_partials_unscaled(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype, const uint8_t* k_cache,
+    const uint8_t* v_cache, int64_t cache_stride_slot,
+    int64_t cache_stride_head, int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, int32_t batch, int32_t rows,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float softmax_scale, int32_t num_ranges,
+    int32_t max_context, void* workspace, size_t workspace_bytes,
+    int32_t code_format, void* stream) {
+    int32_t codes = 0;
+    const int st = unscaled_codes(code_format, &codes);
+    if (st != FP8KV_OK) return st;
+    return decode_partials(q, q_stride_b, q_stride_row, q_stride_head, q_dtype, k_cache,
+                           v_cache, cache_stride_slot, cache_stride_head, nullptr, nullptr, 0, 0,
+                           num_slots, block_tables, block_table_stride, nullptr, 0, context_lens,
+                           batch, rows, num_q_heads, num_kv_heads, head_dim, block_size,
+                           softmax_scale, num_ranges, max_context, workspace, workspace_bytes,
+                           codes, stream);
 }
 
 int fp8kv_paged_decode_merge(
@@ -599,6 +665,39 @@ int fp8kv_sparse_decode_attn_fp8(
         block_table_stride, block_valid, block_valid_stride, context_lens, batch, rows,
         num_q_heads, num_kv_heads, head_dim, block_size, softmax_scale, num_ranges,
         max_context, workspace, workspace_bytes, stream);
+    if (st != FP8KV_OK) return st;
+    return fp8kv_paged_decode_merge(
+        batch, rows, num_q_heads, num_kv_heads, head_dim, num_ranges,
+        workspace, workspace_bytes, out, out_stride_b, out_stride_row,
+        out_stride_head, out_dtype, stream);
+}
+
+int fp8kv_paged_decode_attn_unscaled(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype, const uint8_t* k_cache,
+    const uint8_t* v_cache, int64_t cache_stride_slot,
+    int64_t cache_stride_head, int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, int32_t batch, int32_t rows,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float softmax_scale, int32_t num_ranges,
+    int32_t max_context, void* workspace, size_t workspace_bytes, void* out,
+    int64_t out_stride_b, int64_t out_stride_row, int64_t out_stride_head,
+    int32_t out_dtype, int32_t code_format, void* stream) {
+    // validate everything before enqueueing anything
+    int st = check_out_dtype(out_dtype);
+    if (st != FP8KV_OK) return st;
+    if (!out) return fail(FP8KV_E_NULL, "paged_decode: out is NULL");
+    if (out_stride_b < 0 || out_stride_row < 0 || out_stride_head < 0)
+        return fail(FP8KV_E_STRIDE, "paged_decode: negative out stride");
+    if (!aligned(out, out_dtype == FP8KV_DTYPE_FP32 ? 4 : 2))
+        return fail(FP8KV_E_ALIGN, "out misaligned");
+    if (checked() && batch > 0 && (st = check_device_ptr(out, "out")) != FP8KV_OK) return st;
+    st = fp8kv_paged_decode_partials_unscaled(
+        q, q_stride_b, q_stride_row, q_stride_head, q_dtype, k_cache, v_cache,
+        cache_stride_slot, cache_stride_head, num_slots, block_tables, block_table_stride,
+        context_lens, batch, rows, num_q_heads, num_kv_heads, head_dim, block_size,
+        softmax_scale, num_ranges, max_context, workspace, workspace_bytes, code_format, stream);
     if (st != FP8KV_OK) return st;
     return fp8kv_paged_decode_merge(
         batch, rows, num_q_heads, num_kv_heads, head_dim, num_ranges,

@@ -58,6 +58,19 @@ __device__ __forceinline__ uint32_t e4m3x4_encode(float a, float b, float c, flo
     return (uint32_t)w;
 }
 
+// Four fp32 values -> four E5M2 codes, round to nearest even, magnitudes
+// above 57344 saturating to +-57344 (the gfx950 OCP converter after a clamp).
+constexpr float kE5M2Max = 57344.0f;
+__device__ __forceinline__ uint32_t e5m2x4_encode(float a, float b, float c, float d) {
+    a = __builtin_amdgcn_fmed3f(a, -kE5M2Max, kE5M2Max);
+    b = __builtin_amdgcn_fmed3f(b, -kE5M2Max, kE5M2Max);
+    c = __builtin_amdgcn_fmed3f(c, -kE5M2Max, kE5M2Max);
+    d = __builtin_amdgcn_fmed3f(d, -kE5M2Max, kE5M2Max);
+    int w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
 // q[i] = x[i] / scale for every element of a row, each the correctly rounded
 // quotient: one IEEE reciprocal of the scale and one FMA correction per
 // element (Markstein): q0 = x*r, e = x - q0*s (exact), q = q0 + e*r, with
@@ -118,6 +131,24 @@ __device__ __forceinline__ f16x8 e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
     uint32_t r[4] = {e4m3x2_to_f16x2<false>(lo), e4m3x2_to_f16x2<true>(lo),
                      e4m3x2_to_f16x2<false>(hi), e4m3x2_to_f16x2<true>(hi)};
     return __builtin_bit_cast(f16x8, r);
+}
+
+// The same for E5M2 codes (OCP E5M2: every finite value is exact in bf16
+// and in fp16, of which it is the top byte).
+template <bool HI>
+__device__ __forceinline__ uint32_t e5m2x2_to_bf16x2(uint32_t w) {
+    bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, r);
+}
+template <bool HI>
+__device__ __forceinline__ uint32_t e5m2x2_to_f16x2(uint32_t w) {
+    f16x2 r = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ bf16x8 e5m2x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+    uint32_t r[4] = {e5m2x2_to_bf16x2<false>(lo), e5m2x2_to_bf16x2<true>(lo),
+                     e5m2x2_to_bf16x2<false>(hi), e5m2x2_to_bf16x2<true>(hi)};
+    return __builtin_bit_cast(bf16x8, r);
 }
 
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {

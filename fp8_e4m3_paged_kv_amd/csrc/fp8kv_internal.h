@@ -8,6 +8,13 @@
 
 namespace fp8kv {
 
+// Cache code formats: E4M3 codes with one fp32 scale per (token, KV head)
+// row (the default), or codes without scales (the value itself, scale 1)
+// in E4M3 or E5M2.
+constexpr int kCodesE4M3Scaled = 0;
+constexpr int kCodesE4M3 = 1;
+constexpr int kCodesE5M2 = 2;
+
 struct QuantScatterParams {
     const uint16_t* k;         // bf16 bits
     const uint16_t* v;
@@ -23,6 +30,7 @@ struct QuantScatterParams {
     int64_t num_slots;
     int32_t num_tokens, num_kv_heads;
     int64_t num_rows;          // num_tokens * num_kv_heads * 2
+    int32_t codes;             // kCodes*: unscaled formats write no scales
 };
 
 hipError_t launch_kv_quant_scatter(const QuantScatterParams& p, int head_dim,
@@ -49,6 +57,7 @@ struct DecodeParams {
     int32_t num_ranges;        // R: equal ranges of each KV head's tile sequence
     int32_t wgs_per_range;     // Hkv / 4 when that is a whole number > 1, else 1
     float score_scale_log2;    // softmax_scale * log2(e)
+    int32_t codes;             // kCodes*: unscaled formats read no scales
     float* ws_o;               // [(batch + R - 1) * Hkv * M, head_dim]
     float* ws_lse;             // [(batch + R - 1) * Hkv * M]
     int32_t* ws_prefix;        // [batch + 1]: tiles before each request, then U

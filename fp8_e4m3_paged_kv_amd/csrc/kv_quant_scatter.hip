@@ -18,6 +18,10 @@
 //   cache[slot, h, :] = c; scale[slot, h] = s     (slot < 0 or >= num_slots:
 //                                                   nothing is written)
 // K and V are read at their own token/head strides.
+//
+// The unscaled variants store the values themselves, with no scale:
+//   c = E4M3_rne_sat(x) or E5M2_rne_sat(x) (magnitudes above the format's
+//   largest finite value saturate to it).
 #include <hip/hip_runtime.h>
 
 #include "fp8kv_device.h"
@@ -83,7 +87,7 @@ __device__ __forceinline__ void split_row(uint32_t pair, uint32_t H, uint32_t& t
     }
 }
 
-template <int D, int HSHIFT>
+template <int D, int HSHIFT, int CODES>
 __global__ __launch_bounds__(kQsThreads) void kv_quant_scatter_kernel(QuantScatterParams p) {
 #pragma clang fp contract(off)
     constexpr int EPL = D / 16;          // elements per lane
@@ -143,25 +147,34 @@ __global__ __launch_bounds__(kQsThreads) void kv_quant_scatter_kernel(QuantScatt
             x[2 * i] = bf16_lo(w[s][i]);
             x[2 * i + 1] = bf16_hi(w[s][i]);
         }
-        uint32_t amax_bits = 0;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            amax_bits = max(amax_bits, __float_as_uint(x[i]) & 0x7FFFFFFFu);
-        amax_bits = row16_max_u32(amax_bits);
-        const float amax = __uint_as_float(amax_bits);
-        const float scale = amax / kE4M3Max;         // IEEE binary32 division
-        float qv[EPL];
-        row_quotients(x, scale, qv);
         uint32_t packed[EPL / 4];
+        float scale = 1.0f;
+        if constexpr (CODES == kCodesE4M3Scaled) {
+            uint32_t amax_bits = 0;
 #pragma unroll
-        for (int i = 0; i < EPL / 4; ++i)
-            packed[i] = e4m3x4_encode(qv[4 * i], qv[4 * i + 1], qv[4 * i + 2], qv[4 * i + 3]);
+            for (int i = 0; i < EPL; ++i)
+                amax_bits = max(amax_bits, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+            amax_bits = row16_max_u32(amax_bits);
+            const float amax = __uint_as_float(amax_bits);
+            scale = amax / kE4M3Max;                  // IEEE binary32 division
+            float qv[EPL];
+            row_quotients(x, scale, qv);
+#pragma unroll
+            for (int i = 0; i < EPL / 4; ++i)
+                packed[i] = e4m3x4_encode(qv[4 * i], qv[4 * i + 1], qv[4 * i + 2], qv[4 * i + 3]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < EPL / 4; ++i)
+                packed[i] = CODES == kCodesE5M2
+                                ? e5m2x4_encode(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3])
+                                : e4m3x4_encode(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+        }
         const int64_t sl = slot[s];
         if (valid[s] && sl >= 0 && sl < p.num_slots) {
             uint8_t* dst = cache + sl * p.cache_stride_slot +
                            (int64_t)head[s] * p.cache_stride_head + li * EPL;
             store_codes(dst, packed, (Out*)nullptr);
-            if (li == 0)
+            if (CODES == kCodesE4M3Scaled && li == 0)
                 planes[sl * p.scale_stride_slot + (int64_t)head[s] * p.scale_stride_head] = scale;
         }
     }
@@ -181,7 +194,7 @@ hipError_t launch_kv_quant_scatter(const QuantScatterParams& p, int head_dim,
     const int H = p.num_kv_heads;
     const int hs = (H & (H - 1)) == 0 ? __builtin_ctz((unsigned)H) : -1;
 #define FP8KV_QS_LAUNCH(DIM, HS) \
-    hipLaunchKernelGGL((kv_quant_scatter_kernel<DIM, HS>), grid, block, 0, stream, p)
+    hipLaunchKernelGGL((kv_quant_scatter_kernel<DIM, HS, kCodesE4M3Scaled>), grid, block, 0, stream, p)
 #define FP8KV_QS_DISPATCH(DIM)                                   \
     switch (hs) {                                                \
         case 0: FP8KV_QS_LAUNCH(DIM, 0); break;                  \
@@ -191,7 +204,17 @@ hipError_t launch_kv_quant_scatter(const QuantScatterParams& p, int head_dim,
         case 4: FP8KV_QS_LAUNCH(DIM, 4); break;                  \
         default: FP8KV_QS_LAUNCH(DIM, -1); break;                \
     }
-    if (head_dim == 128) {
+    if (p.codes != kCodesE4M3Scaled) {
+        // unscaled codes: the generic row split only
+        const bool e5 = p.codes == kCodesE5M2;
+        if (head_dim == 128) {
+            if (e5) hipLaunchKernelGGL((kv_quant_scatter_kernel<128, -1, kCodesE5M2>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((kv_quant_scatter_kernel<128, -1, kCodesE4M3>), grid, block, 0, stream, p);
+        } else {
+            if (e5) hipLaunchKernelGGL((kv_quant_scatter_kernel<64, -1, kCodesE5M2>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((kv_quant_scatter_kernel<64, -1, kCodesE4M3>), grid, block, 0, stream, p);
+        }
+    } else if (head_dim == 128) {
         FP8KV_QS_DISPATCH(128)
     } else {
         FP8KV_QS_DISPATCH(64)

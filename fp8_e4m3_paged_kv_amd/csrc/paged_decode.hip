@@ -179,8 +179,11 @@ __device__ __forceinline__ float row_bcast(uint32_t v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + R, 0xF, 0xF, false));
 }
 
-template <int D>
+// CODES: kCodesE4M3Scaled (E4M3 codes, one fp32 scale per row), or the
+// unscaled kCodesE4M3 / kCodesE5M2 (no scales are read: scale 1).
+template <int D, int CODES = kCodesE4M3Scaled>
 struct DecodeTile {
+    static constexpr bool kScaled = CODES == kCodesE4M3Scaled;
     static constexpr int KB = D / 4;        // K code bytes per lane per token
     static constexpr int KV4 = KB / 16;     // 16-byte K loads per token
     static constexpr int KSTEPS = D / 32;   // MFMA k-steps over head_dim
@@ -254,6 +257,17 @@ struct DecodeTile {
         ta.masked = t0 + 32 > w.full_end || (SP && (ta.nv[0] < 16 || ta.nv[1] < 16));
     }
 
+    // exact widening of 8 K codes to bf16 and of 2 V codes to fp16
+    static __device__ __forceinline__ bf16x8 widen_k(uint32_t lo, uint32_t hi) {
+        if constexpr (CODES == kCodesE5M2) return e5m2x8_to_bf16x8(lo, hi);
+        else return e4m3x8_to_bf16x8(lo, hi);
+    }
+    template <bool HI>
+    static __device__ __forceinline__ uint32_t widen_v(uint32_t w) {
+        if constexpr (CODES == kCodesE5M2) return e5m2x2_to_f16x2<HI>(w);
+        else return e4m3x2_to_f16x2<HI>(w);
+    }
+
     static __device__ __forceinline__ void issue(const TileAddr& ta, const LaneOffsets& o, Regs& R) {
 #pragma unroll
         for (int s = 0; s < 2; ++s)
@@ -266,8 +280,12 @@ struct DecodeTile {
         for (int e = 0; e < 8; ++e) R.vraw[e] = VRow<DL>::load(ta.v[e >> 2], o.v[e & 3]);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            R.ks[s] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ta.ks[s], o.s, 0, 0);
-            R.vs[s] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ta.vs[s], o.s, 0, 0);
+            if constexpr (kScaled) {
+                R.ks[s] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ta.ks[s], o.s, 0, 0);
+                R.vs[s] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ta.vs[s], o.s, 0, 0);
+            } else {
+                R.ks[s] = R.vs[s] = 0x3F800000u;      // 1.0f
+            }
         }
     }
 
@@ -280,7 +298,7 @@ struct DecodeTile {
             const uint32_t* kw = reinterpret_cast<const uint32_t*>(R.kraw[s]);
 #pragma unroll
             for (int k = 0; k < KSTEPS; ++k) {
-                const bf16x8 a = e4m3x8_to_bf16x8(kw[2 * k], kw[2 * k + 1]);
+                const bf16x8 a = widen_k(kw[2 * k], kw[2 * k + 1]);
                 sc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[k], sc[s], 0, 0, 0);
             }
         }
@@ -298,7 +316,7 @@ struct DecodeTile {
             const uint32_t* kw = reinterpret_cast<const uint32_t*>(R.kraw[s]);
 #pragma unroll
             for (int k = 0; k < KSTEPS; ++k) {
-                const bf16x8 a = e4m3x8_to_bf16x8(kw[2 * k], kw[2 * k + 1]);
+                const bf16x8 a = widen_k(kw[2 * k], kw[2 * k + 1]);
 #pragma unroll
                 for (int j = 0; j < NT; ++j)
                     sc[j][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[j][k], sc[j][s], 0, 0, 0);
@@ -319,12 +337,18 @@ struct DecodeTile {
         float sv[2][4];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const float sk[4] = {row_bcast<0>(ks[s]), row_bcast<1>(ks[s]),
-                                 row_bcast<2>(ks[s]), row_bcast<3>(ks[s])};
-            sv[s][0] = row_bcast<0>(vs[s]);
-            sv[s][1] = row_bcast<1>(vs[s]);
-            sv[s][2] = row_bcast<2>(vs[s]);
-            sv[s][3] = row_bcast<3>(vs[s]);
+            float sk[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+            sv[s][0] = sv[s][1] = sv[s][2] = sv[s][3] = 1.0f;
+            if constexpr (kScaled) {
+                sk[0] = row_bcast<0>(ks[s]);
+                sk[1] = row_bcast<1>(ks[s]);
+                sk[2] = row_bcast<2>(ks[s]);
+                sk[3] = row_bcast<3>(ks[s]);
+                sv[s][0] = row_bcast<0>(vs[s]);
+                sv[s][1] = row_bcast<1>(vs[s]);
+                sv[s][2] = row_bcast<2>(vs[s]);
+                sv[s][3] = row_bcast<3>(vs[s]);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) s2[s][r] = sc[s][r] * (sk[r] * p.score_scale_log2);
         }
@@ -403,7 +427,7 @@ struct DecodeTile {
                 uint32_t h[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    h[t] = (c & 1) ? e4m3x2_to_f16x2<true>(src[t]) : e4m3x2_to_f16x2<false>(src[t]);
+                    h[t] = (c & 1) ? widen_v<true>(src[t]) : widen_v<false>(src[t]);
                 const f16x8 a = __builtin_bit_cast(f16x8, h);
 #pragma unroll
                 for (int j = 0; j < NT; ++j)
@@ -443,13 +467,13 @@ __device__ __forceinline__ int request_tiles(const DecodeParams& p, int b) {
 // One piece: tiles [ja, jb) of request b for KV head h, reduced to a partial
 // (normalized output and log2 log-sum-exp of each of the M rows) at piece
 // id `pid`.
-template <int D, bool BSP2, bool SP>
+template <int D, bool BSP2, bool SP, int CODES>
 __device__ __forceinline__ void decode_piece(const DecodeParams& p, int b, int len, int ja, int jb,
                                              int h, int pid, int lane) {
     constexpr int KSTEPS = D / 32;
     constexpr int DL = D / 16;
     constexpr int KB = D / 4;
-    typedef DecodeTile<D> Tile;
+    typedef DecodeTile<D, CODES> Tile;
     typedef typename Tile::Regs Regs;
     const int li = lane & 15;
     const int lg = lane >> 4;
@@ -595,7 +619,7 @@ __device__ __forceinline__ int logical_workgroup(int bid, int wgs_per_range) {
     return (k / m) * 8 * m + xcd * m + (k % m);
 }
 
-template <int D, bool BSP2, bool SP>
+template <int D, bool BSP2, bool SP, int CODES>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     const int lane = threadIdx.x & 63;
     // wave index, provably uniform so the page walk and the buffer
@@ -646,7 +670,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         if (n > 0) {
             const int ja = u - pre;
             const int jb = min(n, u1 - pre);
-            decode_piece<D, BSP2, SP>(p, b, len, ja, jb, h, b + r, lane);
+            decode_piece<D, BSP2, SP, CODES>(p, b, len, ja, jb, h, b + r, lane);
             u = pre + jb;
         }
         pre += n;
@@ -770,21 +794,21 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
     }
 }
 
-template <int D, bool BSP2, bool SP>
+template <int D, bool BSP2, bool SP, int CODES>
 hipError_t launch_split(const DecodeParams& p, hipStream_t stream) {
     const int64_t workers = (int64_t)p.num_ranges * p.num_kv_heads;
     const int64_t quantum = p.wgs_per_range > 1 ? 8 * p.wgs_per_range : 1;
     int64_t wgs = (workers + 3) / 4;
     wgs = (wgs + quantum - 1) / quantum * quantum;
     if (wgs > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_split_kernel<D, BSP2, SP>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, BSP2, SP, CODES>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int D, bool SP>
+template <int D, bool SP, int CODES = kCodesE4M3Scaled>
 hipError_t launch_split_bs(const DecodeParams& p, hipStream_t stream) {
-    return p.block_shift >= 0 ? launch_split<D, true, SP>(p, stream)
-                              : launch_split<D, false, SP>(p, stream);
+    return p.block_shift >= 0 ? launch_split<D, true, SP, CODES>(p, stream)
+                              : launch_split<D, false, SP, CODES>(p, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -1090,6 +1114,16 @@ int decode_wave_slots(int device) {
 
 hipError_t launch_decode_partitions(const DecodeParams& p, int head_dim, hipStream_t stream) {
     const bool sp = p.block_valid != nullptr;
+    if (p.codes != kCodesE4M3Scaled) {
+        // unscaled caches: the dense walk only
+        if (sp) return hipErrorInvalidValue;
+        const bool e5 = p.codes == kCodesE5M2;
+        if (head_dim == 128)
+            return e5 ? launch_split_bs<128, false, kCodesE5M2>(p, stream)
+                      : launch_split_bs<128, false, kCodesE4M3>(p, stream);
+        return e5 ? launch_split_bs<64, false, kCodesE5M2>(p, stream)
+                  : launch_split_bs<64, false, kCodesE4M3>(p, stream);
+    }
     if (head_dim == 128)
         return sp ? launch_split_bs<128, true>(p, stream) : launch_split_bs<128, false>(p, stream);
     return sp ? launch_split_bs<64, true>(p, stream) : launch_split_bs<64, false>(p, stream);

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FP8KV_ABI_VERSION 7
+#define FP8KV_ABI_VERSION 8
 
 typedef enum fp8kv_status {
     FP8KV_OK = 0,
@@ -334,6 +334,69 @@ int fp8kv_sparse_decode_partials(
     int32_t head_dim, int32_t block_size, float softmax_scale,
     int32_t num_ranges, int32_t max_context,
     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Unscaled FP8 caches ("feat(dsa): implement fp8 KV cache (e4m3) with a
+ * bf16 indexer cache", sglang-jax #1776, description and "Three design
+ * points": new K/V are cast to the cache dtype with no scale, since fp8
+ * precision is relative and the cached values are O(1); e4m3 is preferred
+ * over e5m2 for its extra mantissa bit, at about half the error).
+ *
+ * The cache holds the values themselves as codes, with the same geometry as
+ * the scaled cache and no scale planes:
+ *   c[d] = E4M3 or E5M2 of x[d], round to nearest even; magnitudes above the
+ *          format's largest finite value (448 / 57344) saturate to it
+ * and attention reads them with scale 1. The calls mirror
+ * fp8kv_kv_quant_scatter and fp8kv_paged_decode_attn_fp8 /
+ * fp8kv_paged_decode_partials (same arguments, conventions, constraints and
+ * errors) without the scale planes; the split phase merges with
+ * fp8kv_paged_decode_merge.
+ * code_format  FP8KV_CODES_E4M3 or FP8KV_CODES_E5M2 (else E_UNSUPPORTED).
+ */
+typedef enum fp8kv_code_format {
+    FP8KV_CODES_E4M3 = 0,   /* OCP E4M3FN, max 448                        */
+    FP8KV_CODES_E5M2 = 1    /* OCP E5M2, max 57344                        */
+} fp8kv_code_format;
+
+int fp8kv_kv_quant_scatter_unscaled(
+    const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+    const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+    int32_t in_dtype, int32_t num_tokens, int32_t num_kv_heads,
+    int32_t head_dim,
+    const int64_t* slot_ids,
+    uint8_t* k_cache, uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head,
+    int64_t num_slots, int32_t code_format, void* stream);
+
+int fp8kv_paged_decode_attn_unscaled(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype,
+    const uint8_t* k_cache, const uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head,
+    int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens,
+    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, float softmax_scale,
+    int32_t num_ranges, int32_t max_context,
+    void* workspace, size_t workspace_bytes,
+    void* out, int64_t out_stride_b, int64_t out_stride_row,
+    int64_t out_stride_head, int32_t out_dtype,
+    int32_t code_format, void* stream);
+
+int fp8kv_paged_decode_partials_unscaled(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype,
+    const uint8_t* k_cache, const uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head,
+    int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens,
+    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, float softmax_scale,
+    int32_t num_ranges, int32_t max_context,
+    void* workspace, size_t workspace_bytes,
+    int32_t code_format, void* stream);
 
 /*
  * fp8kv_prefill_attn_fp8 -- chunked-prefill attention over the FP8 cache

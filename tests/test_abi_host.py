@@ -383,3 +383,47 @@ def test_prefill_refusals(L, kw, status):
     assert pf(L, **kw) == status
     if status != OK:
         assert L.fp8kv_last_error().decode()
+
+
+def qsu(L, **kw):
+    a = dict(k=A, kst=6144, ksh=128, v=A + 8192, vst=6144, vsh=128,
+             dtype=BF16, T=16, H=8, D=128, slots=A, kc=A, vc=A, css=1024,
+             csh=128, S=1 << 20, fmt=0)
+    a.update(kw)
+    return L.fp8kv_kv_quant_scatter_unscaled(
+        a["k"], a["kst"], a["ksh"], a["v"], a["vst"], a["vsh"], a["dtype"],
+        a["T"], a["H"], a["D"], a["slots"], a["kc"], a["vc"], a["css"],
+        a["csh"], a["S"], a["fmt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fmt=2), E_UNSUPPORTED),
+    (dict(fmt=-1), E_UNSUPPORTED),
+    (dict(D=96), E_UNSUPPORTED),
+    (dict(kc=0), E_NULL),
+    (dict(slots=0), E_NULL),
+    (dict(kst=-1), E_STRIDE),
+    (dict(kc=A + 8), E_ALIGN),
+    (dict(T=0), OK),                      # nothing to do, nothing launched
+])
+def test_unscaled_quant_scatter_refusals(L, kw, status):
+    assert qsu(L, **kw) == status
+    if status != OK:
+        assert L.fp8kv_last_error().decode()
+
+
+def test_unscaled_decode_refusals(L):
+    def call(**kw):
+        a = dict(q=A, kc=A, vc=A, css=1024, csh=128, S=1 << 20, bt=A, bts=64, cl=A,
+                 B=4, R=1, Hq=32, Hkv=8, D=128, bs=16, scale=0.088, nr=16, maxc=1024,
+                 ws=A, wsb=1 << 30, fmt=1)
+        a.update(kw)
+        return L.fp8kv_paged_decode_partials_unscaled(
+            a["q"], 8 * 32 * 128, 32 * 128, 128, BF16, a["kc"], a["vc"], a["css"], a["csh"],
+            a["S"], a["bt"], a["bts"], a["cl"], a["B"], a["R"], a["Hq"], a["Hkv"], a["D"],
+            a["bs"], a["scale"], a["nr"], a["maxc"], a["ws"], a["wsb"], a["fmt"], None)
+    assert call(fmt=2) == E_UNSUPPORTED
+    assert call(kc=0) == E_NULL
+    assert call(D=96) == E_UNSUPPORTED
+    assert call(wsb=16) == E_WORKSPACE
+    assert call(B=0) == OK
