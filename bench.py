@@ -22,7 +22,8 @@ long-context verify decode (4 requests of 256K..1M tokens, 4 verify rows,
 decode workload's blocks), chunked-prefill attention (a 4096-token chunk
 after 28,672 cached tokens), the compressed-index scorer (8 x 256 rows x 16
 heads x 65,536 keys, MXFP4 and E4M3 keys) with its key encoders and key
-builder, and the HBM ceilings of plain library copy and read kernels on the
+builder, the decode workload over unscaled E4M3 / E5M2 caches, and the HBM
+ceilings of plain library copy and read kernels on the
 same GPU.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -56,9 +57,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the prefill-chunk, long-context and index extras")
-    ap.add_argument("--extras", default="prefill,longctx,sparse,prefill_attn,index,ceilings",
+    ap.add_argument("--extras",
+                    default="prefill,longctx,sparse,prefill_attn,index,unscaled,ceilings",
                     help="comma list of the extras to run (prefill, longctx, sparse, "
-                         "prefill_attn, index, ceilings)")
+                         "prefill_attn, index, unscaled, ceilings)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times "
                          "(the known-size reference for HBM byte counters)")
@@ -373,6 +375,8 @@ def main():
         result["also"].update(prefill_attention(torch, fk, synth, dev, stream))
     if "index" in extras:
         result["also"].update(index_scorer(torch, fk, synth, dev, stream))
+    if "unscaled" in extras:
+        result["also"].update(unscaled_decode(torch, fk, synth, dev, stream, case, q, bt, cl))
     if "ceilings" in extras:
         result["also"].update(hbm_ceilings(torch, dev, stream))
 
@@ -532,6 +536,58 @@ def sparse_decode(torch, fk, synth, dev, stream, case, q, bt, k_cache, v_cache,
             "sparse_decode_us": round(f_avg * 1e3, 1),
             "sparse_split_kernel_us": round(p_avg * 1e3, 1),
             "sparse_split_kernel_GBps": round(alg / (p_avg * 1e-3) / 1e9, 1)}
+
+
+def unscaled_decode(torch, fk, synth, dev, stream, case, q, bt, cl, reps=20):
+    """The decode workload over unscaled caches (E4M3 and E5M2 codes, no
+    scale planes): cache build and split kernel. Algorithmic bytes: 2 x D
+    code bytes per (token, KV head) for the split kernel, 2 x (2D + D) + 8
+    per token for the build."""
+    log("unscaled E4M3 / E5M2 caches on the decode workload...")
+    L = case.layout
+    B, R, Hq, D = q.shape
+    Hkv = 8
+    S = L.num_slots
+    lens = L.context_lens.tolist()
+    g = synth.gen(2 + 1000, dev)
+    T = int(sum(lens))
+    kc = torch.empty((S, Hkv, D), dtype=torch.uint8, device=dev)
+    vc = torch.empty_like(kc)
+    slots = L.token_slots.to(dev)
+    nr = fk.decode_num_ranges(Hkv, 0)
+    ws = torch.empty(fk.decode_workspace_bytes(B, R, Hq, Hkv, D, nr), dtype=torch.uint8,
+                     device=dev)
+    res = {}
+    for name, cf in (("e4m3", fk.CODES_E4M3), ("e5m2", fk.CODES_E5M2)):
+        # the same K/V distribution as the scaled cache, drawn in chunks
+        c = 1 << 20
+        build_ms = 0.0
+        for i in range(0, T, c):
+            n = min(c, T - i)
+            k = synth.normal_bf16((n, Hkv, D), g, device=dev)
+            v = synth.normal_bf16((n, Hkv, D), g, device=dev)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fk.kv_quant_scatter_unscaled(k, v, slots[i:i + n], kc, vc, cf)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            build_ms += e0.elapsed_time(e1)
+            del k, v
+        kw = dict(num_kv_heads=Hkv, block_size=L.block_size, softmax_scale=case.softmax_scale,
+                  max_context=32768, code_format=cf, num_ranges=nr, workspace=ws)
+        run = lambda: fk.paged_decode_partials_unscaled(q, kc, vc, bt, cl, **kw)
+        ms = sorted(time_events(run, reps, stream))
+        med = ms[len(ms) // 2]
+        alg = T * Hkv * 2 * D + sum((n + L.block_size - 1) // L.block_size for n in lens) * 4 \
+            + B * R * Hq * D * 2
+        res[f"unscaled_{name}_split_kernel_us"] = round(med * 1e3, 1)
+        res[f"unscaled_{name}_split_kernel_GBps"] = round(alg / (med * 1e-3) / 1e9, 1)
+        res[f"unscaled_{name}_cache_build_GBps"] = round(
+            T * Hkv * 2 * 3 * D / (build_ms * 1e-3) / 1e9, 1)
+    del kc, vc, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def hbm_ceilings(torch, dev, stream, gib=2, reps=10):
