@@ -124,3 +124,50 @@ def test_index_build_and_score_replay(fmt):
         step(o2, c2, s2)
         torch.cuda.synchronize()
         assert torch.equal(codes, c2) and torch.equal(scales, s2) and torch.equal(out, o2), rep
+
+
+def test_unscaled_store_and_decode_replay():
+    """One graph holding the unscaled E5M2 store of new tokens and the decode
+    over the cache; replayed with new K/V, slots, queries and lengths."""
+    case = synth.decode_case([800, 1200], 16, 4, 128, 16, rows=1, seed=86)
+    L = case.layout
+    S = L.num_slots
+    kc = torch.zeros((S, 4, 128), dtype=torch.uint8, device=DEV)
+    vc = torch.zeros_like(kc)
+    fk.kv_quant_scatter_unscaled(case.k.to(DEV), case.v.to(DEV), L.token_slots.to(DEV),
+                                 kc, vc, fk.CODES_E5M2)
+    gen = synth.gen(87)
+    k_new = synth.normal_bf16((2, 4, 128), gen).to(DEV)
+    v_new = synth.normal_bf16((2, 4, 128), gen).to(DEV)
+    slots = torch.zeros(2, dtype=torch.int64, device=DEV)
+    q = case.q.to(DEV).clone()
+    bt, cl = L.block_tables.to(DEV), L.context_lens.to(DEV).clone()
+    ws = torch.empty(fk.decode_workspace_bytes(2, 1, 16, 4, 128, 13), dtype=torch.uint8,
+                     device=DEV)
+    out = torch.empty(q.shape, device=DEV)
+    kw = dict(num_kv_heads=4, block_size=16, softmax_scale=case.softmax_scale,
+              max_context=1200, code_format=fk.CODES_E5M2, num_ranges=13, workspace=ws)
+
+    def step(o):
+        fk.kv_quant_scatter_unscaled(k_new, v_new, slots, kc, vc, fk.CODES_E5M2)
+        fk.paged_decode_attn_unscaled(q, kc, vc, bt, cl, out=o, **kw)
+    slots.copy_(L.token_slots[torch.tensor([799, 1999])])
+    g = capture(lambda: step(out))
+    lens = L.context_lens.tolist()
+    for rep in range(3):
+        n = [lens[0] - 50 * rep, lens[1] - 70 * rep]
+        cl.copy_(torch.tensor(n, dtype=torch.int32))
+        slots.copy_(L.token_slots[torch.tensor([n[0] - 1, lens[0] + n[1] - 1])])
+        k_new.copy_(synth.normal_bf16(k_new.shape, gen))
+        v_new.copy_(synth.normal_bf16(v_new.shape, gen))
+        q.copy_(synth.normal_bf16(q.shape, gen))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_k, got_v = kc.clone(), vc.clone()
+        eager = torch.empty_like(out)
+        step(eager)
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+        assert torch.equal(got_k, kc) and torch.equal(got_v, vc), rep
