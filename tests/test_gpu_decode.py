@@ -67,6 +67,20 @@ def test_block_sizes_and_scale_layouts(bs, layout):
     check_case(case, ranges=11, layout=layout)
 
 
+@pytest.mark.parametrize("Hq,Hkv,rows", [
+    (8, 8, 1),        # MHA
+    (32, 2, 1),       # G = 16: the whole 16-row tile
+    (24, 8, 1),       # G = 3
+    (30, 6, 2),       # G = 5, 2 verify rows (10 rows), Hkv not a multiple of 4
+    (36, 12, 1),      # Hkv 12: 3 workgroups per range on one XCD
+    (7, 1, 2),        # one KV head, G = 7, 2 verify rows (14 rows)
+])
+def test_group_and_row_stacking(Hq, Hkv, rows):
+    case = synth.decode_case([1, 50, 1300, 777], Hq, Hkv, 128, 16, rows=rows,
+                             seed=100 + Hq + Hkv)
+    check_case(case, ranges=0)
+
+
 def test_head_dim_64():
     case = synth.decode_case([700, 129, 2], 16, 4, 64, 16, rows=2, seed=6)
     check_case(case, ranges=5)

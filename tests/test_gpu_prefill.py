@@ -48,6 +48,8 @@ def oracle_prefill(case, host, rows=None):
     ([600, 800], 45, 16, 2, 128, 32),      # GQA 8
     ([500, 777], 64, 16, 4, 64, 16),       # head_dim 64
     ([700, 1000], 40, 16, 4, 128, 48),     # block size 48 (division page walk)
+    ([300, 420], 33, 32, 2, 128, 16),      # GQA 16 (one token per 16-row tile)
+    ([300, 420], 21, 16, 8, 64, 16),       # GQA 2, head_dim 64
 ])
 def test_chunk_matches_oracle(lens, C, Hq, Hkv, D, bs):
     case = synth.decode_case(lens, Hq, Hkv, D, bs, rows=C, seed=C + bs)
