@@ -794,6 +794,90 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
     }
 }
 
+// The same merge with one wave per output row, for requests of few pieces:
+// the prefix, then every piece's lse (scalar loads) and row (D/64 floats
+// per lane) in one round trip per 8 pieces, with an online maximum across
+// batches of 8.
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge_rows_kernel(MergeParams p) {
+    constexpr int EPL = D / 64;              // floats per lane
+    constexpr int BATCH = 8;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row = blockIdx.x * 4 + wave;
+    if (row >= p.total_rows) return;
+    const int m = row % p.m_rows;
+    const int bh = row / p.m_rows;
+    const int h = bh % p.num_kv_heads;
+    const int b = bh / p.num_kv_heads;
+    const int U = p.ws_prefix[p.batch];
+    const int pre = p.ws_prefix[b];
+    const int n = p.ws_prefix[b + 1] - pre;
+
+    float acc[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
+    float wsum = 0.f;
+    if (n > 0) {
+        const int64_t R = p.num_ranges;
+        const int r0 = (int)((((int64_t)pre + 1) * R - 1) / U);
+        const int r1 = (int)((((int64_t)pre + n) * R - 1) / U);
+        const int np = r1 - r0 + 1;
+        const int64_t u0 = ((int64_t)(b + r0) * p.num_kv_heads + h) * p.m_rows + m;
+        const int64_t step = (int64_t)p.num_kv_heads * p.m_rows;
+        const float* o = p.ws_o + u0 * D + lane * EPL;
+        float mx = -INFINITY;
+        for (int q0 = 0; q0 < np; q0 += BATCH) {
+            float lq[BATCH];
+            float v[BATCH][EPL];
+#pragma unroll
+            for (int j = 0; j < BATCH; ++j) {
+                const int q = q0 + j;
+                const int64_t rq = r0 + q;
+                // a range with no tile (more ranges than tiles) has no piece
+                const bool live = q < np && (rq * U) / R != ((rq + 1) * U) / R;
+                lq[j] = live ? p.ws_lse[u0 + q * step] : -INFINITY;
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) v[j][i] = live ? o[q * step * D + i] : 0.f;
+            }
+            float cm = mx;
+#pragma unroll
+            for (int j = 0; j < BATCH; ++j) cm = fmaxf(cm, lq[j]);
+            if (cm == -INFINITY) continue;
+            if (cm > mx) {
+                const float a = mx == -INFINITY ? 0.f : exp2f(mx - cm);
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) acc[i] *= a;
+                wsum *= a;
+                mx = cm;
+            }
+#pragma unroll
+            for (int j = 0; j < BATCH; ++j) {
+                const float w = lq[j] > -INFINITY ? exp2f(lq[j] - mx) : 0.f;
+                wsum += w;
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) acc[i] += w * v[j][i];
+            }
+        }
+    }
+    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+    const int r = m / p.group;
+    const int hq = h * p.group + (m - r * p.group);
+    const int64_t off = (int64_t)b * p.out_stride_b + (int64_t)r * p.out_stride_row +
+                        (int64_t)hq * p.out_stride_head + lane * EPL;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const float val = acc[i] * inv;
+        if (p.out_fp32) {
+            static_cast<float*>(p.out)[off + i] = val;
+        } else {
+            uint32_t bits = __float_as_uint(val);
+            bits += 0x7FFFu + ((bits >> 16) & 1u);      // round to nearest even
+            static_cast<uint16_t*>(p.out)[off + i] = (uint16_t)(bits >> 16);
+        }
+    }
+}
+
 template <int D, bool BSP2, bool SP, int CODES>
 hipError_t launch_split(const DecodeParams& p, hipStream_t stream) {
     const int64_t workers = (int64_t)p.num_ranges * p.num_kv_heads;
@@ -1145,6 +1229,16 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stre
 }
 
 hipError_t launch_decode_merge(const MergeParams& p, int head_dim, hipStream_t stream) {
+    // few pieces per request on average (ranges per KV head up to 4 per
+    // request): one wave per output row; else one workgroup per row
+    if ((int64_t)p.num_ranges <= 4 * (int64_t)p.batch) {
+        dim3 grid((unsigned)((p.total_rows + 3) / 4)), block(256);
+        if (head_dim == 128)
+            hipLaunchKernelGGL(decode_merge_rows_kernel<128>, grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL(decode_merge_rows_kernel<64>, grid, block, 0, stream, p);
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)p.total_rows), block(256);
     if (head_dim == 128)
         hipLaunchKernelGGL(decode_merge_kernel<128>, grid, block, 0, stream, p);
