@@ -1116,10 +1116,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
                     for (int r = 0; r < 4; ++r) s2[s][r] = 16 * s + r <= d ? s2[s][r] : kNeg;
             }
             // lazy maximum: the running maximum moves only when a score
-            // exceeds it by more than kLazyMax, so most tiles skip the rescale
-            const float mt = rows_max_fin(max8(s2));
-            if (__any(mt > st[j].m_run + kLazyMax) || ef_up) {
-                const float m_new = fmax_fin(st[j].m_run, mt);
+            // exceeds it by more than kLazyMax, so most tiles skip the rescale.
+            // m_run is the same in the four lanes of a row, so "some lane's
+            // scores exceed it" is "some row's scores exceed it": the row
+            // maximum across lanes is only needed when the branch is taken
+            const float ml = max8(s2);
+            if (__any(ml > st[j].m_run + kLazyMax) || ef_up) {
+                const float m_new = fmax_fin(st[j].m_run, rows_max_fin(ml));
                 const float a = __builtin_amdgcn_exp2f(st[j].m_run - m_new);
                 const float f = a * fe;
 #pragma unroll
