@@ -44,6 +44,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_traffic.json")
 KERNEL_SOURCES = ["fp8_e4m3_paged_kv_amd/csrc/paged_decode.hip",
+                  "fp8_e4m3_paged_kv_amd/csrc/attn_tile.h",
                   "fp8_e4m3_paged_kv_amd/csrc/fp8kv_device.h"]
 
 

@@ -1,0 +1,327 @@
+// prefill_attn.hip -- chunked-prefill attention over the E4M3 cache
+// (sglang-jax #1776, "Modifications": each KV tile is widened to the query
+// dtype before the score dot, and P never takes the cache dtype; ATOM #2655
+// description: prefill sparse GQA over the E4M3 cache). The tile math it
+// shares with the decode split kernel is in attn_tile.h.
+//
+// Every query token of a chunk attends to the cached tokens up to its own
+// position (the chunk was scattered into the cache first). Workgroup = (request,
+// KV head, block of 4 x NT x 16/G query tokens); each of its 4 waves carries
+// NT row tiles, each stacking 16/G tokens x G query heads into the 16 MFMA
+// rows exactly as the decode split kernel stacks verify rows, and runs the
+// decode kernel's tile math (QK^T MFMA, online softmax, P' = p * v_scale in
+// fp16, PV MFMA) with the same rounding at every step. Each K and V operand
+// is widened from E4M3 once per wave and feeds all NT row tiles; the
+// value-scale range exponent of P' depends only on the tile, so it and
+// v_scale * kappa are shared by the row tiles too.
+//
+// The K/V codes and scales of each 32-token tile are read from the cache
+// once per workgroup into LDS (double-buffered): every loader wave moves the
+// rows of 8 (head_dim 128) or 16 (head_dim 64) tokens of one 16-token half,
+// whose page lookup is wave-uniform, through buffer descriptors that end
+// after the chunk's last visible key, so nothing past it is read. The key
+// scales go to LDS already multiplied by softmax_scale * log2(e). All 4
+// waves read their operands from LDS in the decode kernel's register layout,
+// the scales as four consecutive tokens per lane (no lane broadcast needed).
+// Workgroups of one (request, KV head) run on one XCD, the deepest query
+// blocks first.
+// The prefill kernel keeps a row's running maximum until a tile's scores
+// exceed it by more than kLazyMax (log2 units), so p = exp2(s - m) stays
+// below 2^kLazyMax; its P' range factor is 2^(141 - kLazyMax - e), which
+// keeps P' below 2^15 as in the decode kernel.
+#include <hip/hip_runtime.h>
+
+#include "attn_tile.h"
+#include "fp8kv_device.h"
+#include "fp8kv_internal.h"
+
+namespace fp8kv {
+namespace {
+
+constexpr int kLazyMax = 8;
+
+template <int D, bool BSP2, int NT>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
+    constexpr int KSTEPS = D / 32;
+    constexpr int DL = D / 16;
+    constexpr int KB = D / 4;
+    constexpr int ROW = D + 16;               // padded LDS row: conflict-free row reads
+    constexpr int CPR = D / 16;               // 16-byte chunks per code row
+    constexpr int TPL = 64 / CPR;             // tokens one loader wave moves
+    constexpr int LOAD_WAVES = 32 / TPL;
+    static_assert(TPL <= 16 && 16 % TPL == 0, "a loader wave stays inside one half");
+    typedef DecodeTile<D> Tile;
+    typedef typename Tile::Regs Regs;
+    __shared__ __align__(16) uint8_t lds_k[2][32 * ROW];
+    __shared__ __align__(16) uint8_t lds_v[2][32 * ROW];
+    __shared__ __align__(16) float lds_s[2][2][32];   // [buf][k_scale * score scale | v_scale][token]
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int li = lane & 15, lg = lane >> 4;
+
+    // XCD-contiguous numbering, deepest query block first within a group
+    const int nwg = gridDim.x;
+    const int L_id = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    const int grp = L_id / p.qblocks;
+    if (grp >= p.batch * p.num_kv_heads) return;
+    const int qb = p.qblocks - 1 - (L_id - grp * p.qblocks);
+    const int b = grp / p.num_kv_heads;
+    const int h = grp - b * p.num_kv_heads;
+    const int L = min(max(p.context_lens[b], 0), p.max_context);
+    const int qlen = min(min(max(p.q_lens[b], 0), p.max_q), L);
+    const int TPW = p.tokens_per_wave;
+    const int q0 = qb * 4 * NT * TPW;
+    if (q0 >= qlen) return;
+    const int P = L - qlen;                               // cached tokens before the chunk
+    const int kv_end = P + min(q0 + 4 * NT * TPW, qlen);  // no row of the block sees beyond
+    const int ntiles = (kv_end + 31) >> 5;
+
+    // q operand and causal limit of row li of tile j: token tq of the chunk,
+    // head hq
+    const int hq = h * p.group + li % p.group;
+    int tq[NT], lim[NT];
+    bf16x8 qv[NT][KSTEPS];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        tq[j] = q0 + (wave * NT + j) * TPW + li / p.group;
+        lim[j] = P + tq[j];
+        if (tq[j] < qlen) {
+            const uint16_t* qp = p.q + (int64_t)b * p.q_stride_b + (int64_t)tq[j] * p.q_stride_tok +
+                                 (int64_t)hq * p.q_stride_head + lg * (D / 4);
+#pragma unroll
+            for (int k = 0; k < KSTEPS; ++k)
+                qv[j][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 8 * k));
+        } else {
+#pragma unroll
+            for (int k = 0; k < KSTEPS; ++k) qv[j][k] = bf16x8{};
+        }
+    }
+    const int wave_lim = P + q0 + wave * NT * TPW;        // smallest limit of the wave's rows
+
+    // softmax state of each row tile; the P' range exponent is shared
+    WaveState<DL> st[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+#pragma unroll
+        for (int n = 0; n < DL; ++n) st[j].acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+        st[j].m_run = kNeg;
+        st[j].l_run = 0.f;
+    }
+    int ef_run = 15;
+
+    // cooperative tile load: lane t of a loader wave moves 16 bytes of token
+    // t / CPR's K and V rows and reads the token's two scales; its chunk-0
+    // lanes store the key scale, its chunk-1 lanes the value scale
+    const bool loader = wave < LOAD_WAVES;
+    const int ld_tok = t / CPR, ld_chunk = t % CPR;
+    const int ld_half = (wave * TPL) >> 4;
+    const int ld_code = (ld_tok & 15) * (int)p.cache_stride_slot + 16 * ld_chunk;
+    const int ld_scale = (ld_tok & 15) * (int)p.scale_stride_slot * 4;
+    const int lds_code = ld_tok * ROW + 16 * ld_chunk;
+    const uint8_t* kbase = p.k_cache + (int64_t)h * p.cache_stride_head;
+    const uint8_t* vbase = p.v_cache + (int64_t)h * p.cache_stride_head;
+    const float* ksbase = p.k_scale + (int64_t)h * p.scale_stride_head;
+    const float* vsbase = p.v_scale + (int64_t)h * p.scale_stride_head;
+    const int32_t* bt = p.block_tables + (int64_t)b * p.block_table_stride;
+    intx4 kr = {0, 0, 0, 0}, vr = {0, 0, 0, 0};
+    float sr = 0.f;
+    auto load_tile = [&](int ti) {
+        // the wave's half: keys stok .. stok + nvalid - 1, all in one block
+        const int stok = (ti << 5) + 16 * ld_half;
+        const int nvalid = min(16, kv_end - stok);
+        int64_t slot = 0;
+        if (nvalid > 0) {
+            const int bi = BSP2 ? (stok >> p.block_shift) : stok / p.block_size;
+            const int bo = BSP2 ? (stok & (p.block_size - 1)) : stok - bi * p.block_size;
+            const int blk = min(max(bt[bi], 0), p.num_blocks - 1);
+            slot = (int64_t)blk * p.block_size + bo;
+        }
+        const int nrc = nvalid > 0 ? (nvalid - 1) * (int)p.cache_stride_slot + D : 0;
+        const int nrs = nvalid > 0 ? 4 * ((nvalid - 1) * (int)p.scale_stride_slot + 1) : 0;
+        const int64_t coff = slot * p.cache_stride_slot;
+        const int64_t soff = slot * p.scale_stride_slot;
+        kr = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(kbase + coff, nrc), ld_code, 0, 0);
+        vr = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(vbase + coff, nrc), ld_code, 0, 0);
+        const float ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                       make_rsrc(ksbase + soff, nrs), ld_scale, 0, 0));
+        const float vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                       make_rsrc(vsbase + soff, nrs), ld_scale, 0, 0));
+        sr = ld_chunk == 0 ? ks * p.score_scale_log2 : vs;
+    };
+    auto store_tile = [&](int buf) {
+        *reinterpret_cast<intx4*>(&lds_k[buf][lds_code]) = kr;
+        *reinterpret_cast<intx4*>(&lds_v[buf][lds_code]) = vr;
+        if (ld_chunk < 2) lds_s[buf][ld_chunk][ld_tok] = sr;
+    };
+
+    if (loader) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+    for (int ti = 0; ti < ntiles; ++ti) {
+        const int buf = ti & 1;
+        if (loader && ti + 1 < ntiles) load_tile(ti + 1);
+        // operands in the decode kernel's register layout
+        Regs R;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+            for (int c = 0; c < Tile::KV4; ++c)
+                R.kraw[s][c] = *reinterpret_cast<const uint4*>(
+                    &lds_k[buf][(16 * s + li) * ROW + lg * KB + 16 * c]);
+        }
+        floatx4 sc[NT][2];
+        Tile::template qk_tiles<NT>(R, qv, sc);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint8_t* src = &lds_v[buf][(16 * (e >> 2) + 4 * lg + (e & 3)) * ROW + li * DL];
+            if constexpr (DL == 8)
+                R.vraw[e] = *reinterpret_cast<const uint2*>(src);
+            else
+                R.vraw[e] = *reinterpret_cast<const uint32_t*>(src);
+        }
+        // scales of the lane's score tokens 16 s + 4 lg + r
+        float sk[2][4], sv[2][4];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const float4 a = *reinterpret_cast<const float4*>(&lds_s[buf][0][16 * s + 4 * lg]);
+            const float4 c = *reinterpret_cast<const float4*>(&lds_s[buf][1][16 * s + 4 * lg]);
+            sk[s][0] = a.x; sk[s][1] = a.y; sk[s][2] = a.z; sk[s][3] = a.w;
+            sv[s][0] = c.x; sv[s][1] = c.y; sv[s][2] = c.z; sv[s][3] = c.w;
+        }
+
+        // ---- P' range of the tile (keys past the chunk have v_scale 0);
+        // the scales are >= 0, so their bit patterns order as integers
+        uint32_t svm = 0;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) svm = max(svm, __float_as_uint(sv[s][r]));
+        svm = rows_max_u32(svm);
+        const int ef_t = max((int)(svm >> 23), 15);
+        const int ef_new = max(ef_run, ef_t);
+        const bool ef_up = ef_new > ef_run;
+        const float fe = pow2i(max(ef_run - ef_new, -126));
+        ef_run = ef_new;
+        const float kappa = pow2i(141 - kLazyMax - ef_run);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sv[s][r] *= kappa;
+
+        // ---- online softmax of each row tile; P' = p * v_scale * kappa
+        const bool masked = (ti << 5) + 31 > wave_lim;
+        f16x8 pb[NT];
+        WaveState<DL>* sts[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            float s2[2][4];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s2[s][r] = sc[j][s][r] * sk[s][r];
+            if (masked) {
+                // key 16 s + 4 lg + r of the tile is visible iff
+                // 16 s + r <= lim - t0 - 4 lg
+                const int d = lim[j] - (ti << 5) - 4 * lg;
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) s2[s][r] = 16 * s + r <= d ? s2[s][r] : kNeg;
+            }
+            // lazy maximum: the running maximum moves only when a score
+            // exceeds it by more than kLazyMax, so most tiles skip the rescale.
+            // m_run is the same in the four lanes of a row, so "some lane's
+            // scores exceed it" is "some row's scores exceed it": the row
+            // maximum across lanes is only needed when the branch is taken
+            const float ml = max8(s2);
+            if (__any(ml > st[j].m_run + kLazyMax) || ef_up) {
+                const float m_new = fmax_fin(st[j].m_run, rows_max_fin(ml));
+                const float a = __builtin_amdgcn_exp2f(st[j].m_run - m_new);
+                const float f = a * fe;
+#pragma unroll
+                for (int n = 0; n < DL; ++n) st[j].acc[n] *= f;
+                st[j].l_run *= a;
+                st[j].m_run = m_new;
+            }
+            uint32_t pw[4];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                float pr[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // a masked score gives exp2(kNeg - m) = 0: every row sees
+                    // key 0 in the first tile, so m is a real score throughout
+                    const float e = __builtin_amdgcn_exp2f(s2[s][r] - st[j].m_run);
+                    st[j].l_run += e;
+                    pr[r] = e * sv[s][r];
+                }
+                pw[2 * s] = pack_f16x2(pr[0], pr[1]);
+                pw[2 * s + 1] = pack_f16x2(pr[2], pr[3]);
+            }
+            pb[j] = __builtin_bit_cast(f16x8, pw);
+            sts[j] = &st[j];
+        }
+        Tile::template pv_tiles<NT>(R, pb, sts);
+        if (loader && ti + 1 < ntiles) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // normalized output of row li of each tile: dims [DL*4 lg, DL*4 lg + DL*4)
+    const float un = pow2i(max(ef_run - 141 + kLazyMax, -126));
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const float l_sum = rows_sum(st[j].l_run);
+        if (tq[j] >= qlen) continue;
+        const float inv = l_sum > 0.f ? un / l_sum : 0.f;
+        const int64_t off = (int64_t)b * p.out_stride_b + (int64_t)tq[j] * p.out_stride_tok +
+                            (int64_t)hq * p.out_stride_head + (DL * 4) * lg;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float vals[DL];
+#pragma unroll
+            for (int n = 0; n < DL; ++n) vals[n] = st[j].acc[n][r] * inv;
+            if (p.out_fp32) {
+                float* o = static_cast<float*>(p.out) + off + DL * r;
+#pragma unroll
+                for (int c = 0; c < DL / 4; ++c)
+                    *reinterpret_cast<float4*>(o + 4 * c) =
+                        make_float4(vals[4 * c], vals[4 * c + 1], vals[4 * c + 2], vals[4 * c + 3]);
+            } else {
+                uint16_t* o = static_cast<uint16_t*>(p.out) + off + DL * r;
+                uint32_t w[DL / 2];
+#pragma unroll
+                for (int n = 0; n < DL / 2; ++n) {
+                    const bf16x2 v2 = {(__bf16)vals[2 * n], (__bf16)vals[2 * n + 1]};
+                    w[n] = __builtin_bit_cast(uint32_t, v2);
+                }
+                if constexpr (DL == 8)
+                    *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+                else
+                    *reinterpret_cast<uint2*>(o) = make_uint2(w[0], w[1]);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream) {
+    const int64_t wgs = ((int64_t)p.batch * p.num_kv_heads * p.qblocks + 7) / 8 * 8;
+    if (wgs > INT32_MAX) return hipErrorInvalidValue;
+    const bool pow2 = p.block_shift >= 0;
+    dim3 grid((unsigned)wgs), block(256);
+    if (head_dim == 128) {
+        if (pow2) hipLaunchKernelGGL((prefill_kernel<128, true, kPrefillRowTiles>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((prefill_kernel<128, false, kPrefillRowTiles>), grid, block, 0, stream, p);
+    } else {
+        if (pow2) hipLaunchKernelGGL((prefill_kernel<64, true, kPrefillRowTiles>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((prefill_kernel<64, false, kPrefillRowTiles>), grid, block, 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fp8kv
