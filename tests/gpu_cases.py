@@ -28,6 +28,8 @@ class DevCache:
 
     scale_layout "head_major": planes stored [H, S] and passed as the
     transposed [S, H] view (one head's scales contiguous per slot);
+    "interleaved": one [H, S, 2] array holding each row's K and V scales
+    side by side, passed as two [S, H] views with slot stride 2;
     "slot_major": planes stored [S, H]."""
 
     def __init__(self, num_slots, H, D, device="cuda",
@@ -44,6 +46,12 @@ class DevCache:
             self.v_plane = torch.full_like(self.k_plane, sfill)
             self.k_scale = self.k_plane.t()
             self.v_scale = self.v_plane.t()
+        elif scale_layout == "interleaved":
+            self.kv_planes = torch.full((H, num_slots, 2), sfill, device=device)
+            self.k_plane = self.kv_planes[:, :, 0]
+            self.v_plane = self.kv_planes[:, :, 1]
+            self.k_scale = self.k_plane.t()
+            self.v_scale = self.v_plane.t()
         else:
             self.k_plane = torch.full((num_slots, H), sfill, device=device)
             self.v_plane = torch.full_like(self.k_plane, sfill)
@@ -56,7 +64,7 @@ class DevCache:
         vc = self.v_cache.cpu().numpy()
         kp = self.k_plane.cpu().numpy()
         vp = self.v_plane.cpu().numpy()
-        if self.layout == "head_major":
+        if self.layout != "slot_major":
             return kc, vc, kp.T, vp.T
         return kc, vc, kp, vp
 
@@ -70,7 +78,7 @@ class DevCache:
 def host_empty_like(dc: DevCache):
     kc = np.full((dc.S, dc.H, dc.D), SENTINEL, np.uint8)
     vc = np.full_like(kc, SENTINEL)
-    if dc.layout == "head_major":
+    if dc.layout != "slot_major":
         kp = np.full((dc.H, dc.S), SCALE_SENTINEL, np.float32)
         vp = np.full_like(kp, SCALE_SENTINEL)
         return kc, vc, kp.T, vp.T
@@ -116,7 +124,7 @@ def compact_host_cache(case, dc: DevCache, requests):
     NB = dc.S // bs
     kc = dc.k_cache.view(NB, bs, dc.H, dc.D)[dev_idx].reshape(-1, dc.H, dc.D).cpu().numpy()
     vc = dc.v_cache.view(NB, bs, dc.H, dc.D)[dev_idx].reshape(-1, dc.H, dc.D).cpu().numpy()
-    if dc.layout == "head_major":
+    if dc.layout != "slot_major":
         kp = dc.k_plane.view(dc.H, NB, bs)[:, dev_idx].reshape(dc.H, -1).cpu().numpy()
         vp = dc.v_plane.view(dc.H, NB, bs)[:, dev_idx].reshape(dc.H, -1).cpu().numpy()
         ks, vs = kp.T, vp.T

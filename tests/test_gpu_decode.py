@@ -58,7 +58,7 @@ def test_ragged_lengths_across_ranges(ranges):
     check_case(case, ranges=ranges)
 
 
-@pytest.mark.parametrize("layout", ["head_major", "slot_major"])
+@pytest.mark.parametrize("layout", ["head_major", "interleaved", "slot_major"])
 @pytest.mark.parametrize("bs", [16, 32, 48, 64, 128])
 def test_block_sizes_and_scale_layouts(bs, layout):
     """Power-of-two block sizes take the shift/mask page walk, 48 the

@@ -43,7 +43,7 @@ def assert_same(got, ref, what):
         assert bad.size == 0, f"{what}: {n} differs at {bad.size} places, e.g. {bad[:4]}"
 
 
-@pytest.mark.parametrize("layout", ["head_major", "slot_major"])
+@pytest.mark.parametrize("layout", ["head_major", "interleaved", "slot_major"])
 def test_tiny_case_bit_exact(layout):
     case = synth.tiny_case(0)
     log(f"tiny quant-scatter layout={layout}")
