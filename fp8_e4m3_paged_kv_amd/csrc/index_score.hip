@@ -38,16 +38,6 @@ constexpr int kScoreWaves = 4;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kStoreNT = 2;         // cache policy of the score stores: non-temporal
 
-// E2M1 code of |v| (v = x / 2^e, so |v| <= 6): nearest of
-// {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even code. The thresholds are the
-// midpoints; a midpoint rounds up exactly when the upper neighbour's code is
-// even.
-__device__ __forceinline__ uint32_t e2m1_code(float a) {
-    return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-           (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-           (uint32_t)(a > 5.0f);
-}
-
 // ---------------------------------------------------------------- keys
 // Encode one key held by a 16-lane DPP row: lane li holds dims 8li .. 8li+7
 // as floats (each exactly a bf16 value). E4M3: the KV row quantizer (row
@@ -93,13 +83,17 @@ __device__ __forceinline__ void encode_key(const float (&x)[8], int li, bool sto
             e = mant <= 0.75f ? ex - 3 : ex - 2;         // smallest e with amax <= 6 * 2^e
             e = max(e, -127);
         }
-        uint32_t packed = 0;
+        // v = x / 2^e (exact wherever a code boundary lies), then the
+        // hardware E2M1 converter with unit scale: round to nearest even,
+        // sign kept; element 2j in the low nibble of byte j
+        float v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float v = ldexpf(x[i], -e);             // exact wherever a code boundary lies
-            const uint32_t c = e2m1_code(fabsf(v)) | ((__float_as_uint(x[i]) >> 28) & 8u);
-            packed |= c << (4 * i);
-        }
+        for (int i = 0; i < 8; ++i) v[i] = ldexpf(x[i], -e);
+        uint32_t packed = 0;
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[0], v[1], 1.0f, 0);
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[2], v[3], 1.0f, 1);
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[4], v[5], 1.0f, 2);
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[6], v[7], 1.0f, 3);
         if (store) {
             *reinterpret_cast<uint32_t*>(code_row + li * 4) = packed;
             if ((li & 3) == 0) static_cast<uint8_t*>(scale_row)[li >> 2] = (uint8_t)(e + 127);

@@ -123,6 +123,30 @@ def test_key_codes_bit_exact(fmt):
                               np.asarray(rs, np.float32).view(np.uint32))
 
 
+def test_mxfp4_codes_every_bf16_value_at_unit_exponent():
+    """Every finite bf16 value in [-6, 6], both zeros and the subnormals
+    included, encoded with its group's exponent at 0 (each group of 32
+    opens with 6) and compared with the oracle: the E2M1 rounding
+    (midpoints to the even code, sign kept) checked exhaustively."""
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    vals = bits.view(torch.bfloat16).float()
+    vals = vals[torch.isfinite(vals) & (vals.abs() <= 6.0)]
+    per_group = 31
+    n_groups = -(-vals.numel() // per_group)
+    n_groups += (-n_groups) % 4                      # whole keys of 4 groups
+    body = torch.zeros(n_groups * per_group)
+    body[:vals.numel()] = vals
+    groups = torch.cat([torch.full((n_groups, 1), 6.0), body.view(n_groups, per_group)], 1)
+    keys = groups.reshape(-1, 128).to(torch.bfloat16)
+    log(f"mxfp4 exhaustive: {vals.numel()} values in {keys.shape[0]} keys")
+    codes, scales = encode(keys.to(DEV), MX)
+    rc, rs = oracle_keys(keys, MX)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.all(rs == 127)
+    bad = np.flatnonzero(codes.cpu().numpy() != rc)
+    assert bad.size == 0, f"{bad.size} code bytes differ, e.g. at {bad[:4]}"
+
+
 @pytest.mark.parametrize("fmt", [MX, E4])
 def test_key_codes_strided_rows(fmt):
     """Keys read from every other row of a wider tensor; codes written into
