@@ -18,7 +18,8 @@ for the roofline object.
 Also measured in the same run (reported under "also"): quantize+scatter
 tokens/s on the 4096-token prefill chunk (fused qkv, K/V strided slices,
 random slots in a 1,048,576-slot pool, 32 rotating input sets so reads come
-from HBM, replayed from a HIP graph), the cache-build bandwidth, the
+from HBM, replayed from a HIP graph; and the same chunks stored into
+consecutive slots, as a prefill filling fresh blocks), the cache-build bandwidth, the
 long-context verify decode (4 requests of 256K..1M tokens, 4 verify rows,
 16/4 heads, 64-token blocks), the decode over selected blocks (1/8 of the
 decode workload's blocks), chunked-prefill attention (a 4096-token chunk
@@ -448,6 +449,26 @@ def prefill_quant_scatter(torch, fk, synth, dev, stream, sets=32, reps=4):
     torch.cuda.synchronize()
     g_avg = t0.elapsed_time(t1) / (reps * sets)
     del graph
+    # the same chunks stored into consecutive slots (a prefill filling
+    # freshly allocated blocks): input set i takes slots [i*T, (i+1)*T)
+    contig = [torch.arange(i * T, (i + 1) * T, device=dev) for i in range(sets)]
+    graph = torch.cuda.CUDAGraph()
+    side.wait_stream(stream)
+    with torch.cuda.graph(graph, stream=side):
+        for i, c in enumerate(chunks):
+            fk.kv_quant_scatter(c.k_view(), c.v_view(), contig[i], k_cache,
+                                v_cache, k_plane.t(), v_plane.t())
+    stream.wait_stream(side)
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    c_avg = t0.elapsed_time(t1) / (reps * sets)
+    del graph
     tok_s = T / (g_avg * 1e-3)
     gbs = quant_bytes(T, H, D) / (g_avg * 1e-3) / 1e9
     del chunks
@@ -455,7 +476,9 @@ def prefill_quant_scatter(torch, fk, synth, dev, stream, sets=32, reps=4):
     return {"quant_scatter_prefill_tokens_per_s": round(tok_s, 0),
             "quant_scatter_prefill_us": round(g_avg * 1e3, 2),
             "quant_scatter_prefill_GBps": round(gbs, 1),
-            "quant_scatter_prefill_eager_us": round(avg * 1e3, 2)}
+            "quant_scatter_prefill_eager_us": round(avg * 1e3, 2),
+            "quant_scatter_prefill_contiguous_slots_us": round(c_avg * 1e3, 2),
+            "quant_scatter_prefill_contiguous_slots_tokens_per_s": round(T / (c_avg * 1e-3), 0)}
 
 
 def longctx_decode(torch, fk, synth, dev, stream, reps=20):
