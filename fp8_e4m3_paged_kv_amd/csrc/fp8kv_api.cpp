@@ -241,6 +241,8 @@ static int decode_partials(
         return fail(FP8KV_E_SHAPE, "max_context (%d) must be >= 0", max_context);
     if ((int64_t)batch * ((max_context + 31) / 32) > INT32_MAX)
         return fail(FP8KV_E_SHAPE, "batch * max_context too large for 32-bit tile counts");
+    // no request: nothing is read or written, any pointer may be NULL
+    if (batch == 0) return ok();
     if (!q || !k_cache || !v_cache || (scaled && (!k_scale || !v_scale)) || !block_tables ||
         !context_lens)
         return fail(FP8KV_E_NULL, "paged_decode: a required pointer is NULL");
@@ -272,7 +274,6 @@ static int decode_partials(
     // in-block offsets are 32-bit: 16 slots of codes / scales must fit
     if (cache_stride_slot > (INT32_MAX / 16) || scale_stride_slot > (INT32_MAX / 64))
         return fail(FP8KV_E_SHAPE, "slot stride too large for 32-bit in-block offsets");
-    if (batch == 0) return ok();
     if (checked()) {
         if ((st = checked_begin(stream)) != FP8KV_OK) return st;
         st = check_device_ptrs({{q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"},
@@ -370,6 +371,8 @@ static int quant_scatter(
     if (num_tokens < 0 || num_kv_heads < 1 || num_slots < 0)
         return fail(FP8KV_E_SHAPE, "num_tokens %d, num_kv_heads %d, num_slots %lld",
                     num_tokens, num_kv_heads, (long long)num_slots);
+    // nothing to store: nothing is read or written, any pointer may be NULL
+    if (num_tokens == 0) return ok();
     if (!k || !v || !slot_ids || !k_cache || !v_cache || (scaled && (!k_scale || !v_scale)))
         return fail(FP8KV_E_NULL, "kv_quant_scatter: a required pointer is NULL");
     if (k_stride_tok < 0 || k_stride_head < 0 || v_stride_tok < 0 ||
@@ -389,7 +392,6 @@ static int quant_scatter(
         return fail(FP8KV_E_ALIGN, "cache rows must start on 16-byte boundaries");
     if ((scaled && (!aligned(k_scale, 4) || !aligned(v_scale, 4))) || !aligned(slot_ids, 8))
         return fail(FP8KV_E_ALIGN, "scale planes / slot ids misaligned");
-    if (num_tokens == 0) return ok();
     if (checked()) {
         int st = checked_begin(stream);
         if (st != FP8KV_OK) return st;
@@ -519,7 +521,7 @@ int fp8kv_sparse_decode_partials(
     int32_t block_size, float softmax_scale, int32_t num_ranges,
     int32_t max_context, void* workspace, size_t workspace_bytes,
     void* stream) {
-    if (!block_valid)
+    if (!block_valid && batch > 0)
         return fail(FP8KV_E_NULL, "sparse_decode: block_valid is NULL");
     return decode_partials(q, q_stride_b, q_stride_row, q_stride_head, q_dtype, k_cache,
                            v_cache, cache_stride_slot, cache_stride_head, k_scale, v_scale,
@@ -562,6 +564,8 @@ int fp8kv_paged_decode_merge(
     int st = decode_shape(batch, rows, num_q_heads, num_kv_heads, head_dim, num_ranges, &s);
     if (st != FP8KV_OK) return st;
     if ((st = check_out_dtype(out_dtype)) != FP8KV_OK) return st;
+    // no request: nothing is read or written, any pointer may be NULL
+    if (batch == 0) return ok();
     if (!out) return fail(FP8KV_E_NULL, "paged_decode_merge: out is NULL");
     if (!workspace)
         return fail(FP8KV_E_WORKSPACE, "paged_decode_merge: workspace is NULL");
@@ -573,7 +577,6 @@ int fp8kv_paged_decode_merge(
     const int esz = out_dtype == FP8KV_DTYPE_FP32 ? 4 : 2;
     if (!aligned(out, esz) || !aligned(workspace, 256))
         return fail(FP8KV_E_ALIGN, "out or workspace misaligned");
-    if (batch == 0) return ok();
     if (checked()) {
         if ((st = checked_begin(stream)) != FP8KV_OK) return st;
         if ((st = check_device_ptrs({{workspace, "workspace"}, {out, "out"}})) != FP8KV_OK)
@@ -615,7 +618,7 @@ int fp8kv_paged_decode_attn_fp8(
     // validate everything before enqueueing anything
     int st = check_out_dtype(out_dtype);
     if (st != FP8KV_OK) return st;
-    if (!out) return fail(FP8KV_E_NULL, "paged_decode: out is NULL");
+    if (!out && batch > 0) return fail(FP8KV_E_NULL, "paged_decode: out is NULL");
     if (out_stride_b < 0 || out_stride_row < 0 || out_stride_head < 0)
         return fail(FP8KV_E_STRIDE, "paged_decode: negative out stride");
     if (!aligned(out, out_dtype == FP8KV_DTYPE_FP32 ? 4 : 2))
@@ -652,7 +655,7 @@ int fp8kv_sparse_decode_attn_fp8(
     // validate everything before enqueueing anything
     int st = check_out_dtype(out_dtype);
     if (st != FP8KV_OK) return st;
-    if (!out) return fail(FP8KV_E_NULL, "sparse_decode: out is NULL");
+    if (!out && batch > 0) return fail(FP8KV_E_NULL, "sparse_decode: out is NULL");
     if (out_stride_b < 0 || out_stride_row < 0 || out_stride_head < 0)
         return fail(FP8KV_E_STRIDE, "sparse_decode: negative out stride");
     if (!aligned(out, out_dtype == FP8KV_DTYPE_FP32 ? 4 : 2))
@@ -687,7 +690,7 @@ int fp8kv_paged_decode_attn_unscaled(
     // validate everything before enqueueing anything
     int st = check_out_dtype(out_dtype);
     if (st != FP8KV_OK) return st;
-    if (!out) return fail(FP8KV_E_NULL, "paged_decode: out is NULL");
+    if (!out && batch > 0) return fail(FP8KV_E_NULL, "paged_decode: out is NULL");
     if (out_stride_b < 0 || out_stride_row < 0 || out_stride_head < 0)
         return fail(FP8KV_E_STRIDE, "paged_decode: negative out stride");
     if (!aligned(out, out_dtype == FP8KV_DTYPE_FP32 ? 4 : 2))
@@ -732,6 +735,8 @@ int fp8kv_prefill_attn_fp8(
         return fail(FP8KV_E_UNSUPPORTED, "GQA group %d: must divide %d", group, kMaxStackedRows);
     if (block_size < 16 || block_size % 16 != 0)
         return fail(FP8KV_E_UNSUPPORTED, "block_size %d: must be a positive multiple of 16", block_size);
+    // no query row: nothing is read or written, any pointer may be NULL
+    if (batch == 0 || max_q == 0) return ok();
     if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables || !context_lens ||
         !q_lens || !out)
         return fail(FP8KV_E_NULL, "prefill: a required pointer is NULL");
@@ -760,7 +765,6 @@ int fp8kv_prefill_attn_fp8(
         return fail(FP8KV_E_SHAPE, "num_slots / block_size exceeds int32 block ids");
     if (cache_stride_slot > (INT32_MAX / 16) || scale_stride_slot > (INT32_MAX / 64))
         return fail(FP8KV_E_SHAPE, "slot stride too large for 32-bit in-block offsets");
-    if (batch == 0 || max_q == 0) return ok();
     if (checked()) {
         if ((st = checked_begin(stream)) != FP8KV_OK) return st;
         st = check_device_ptrs({{q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"},
@@ -826,6 +830,7 @@ int fp8kv_index_keys_quantize(
         return fail(FP8KV_E_UNSUPPORTED, "key_format %d", key_format);
     if (num_keys < 0 || num_keys > (INT64_C(1) << 36))
         return fail(FP8KV_E_SHAPE, "num_keys %lld", (long long)num_keys);
+    if (num_keys == 0) return ok();      // nothing read or written, any pointer may be NULL
     if (!keys || !codes || !scales)
         return fail(FP8KV_E_NULL, "index_keys_quantize: a required pointer is NULL");
     if (key_stride < 0 || code_stride < 0 || scale_stride < 0)
@@ -837,7 +842,6 @@ int fp8kv_index_keys_quantize(
         return fail(FP8KV_E_ALIGN, "code rows must start on %d-byte boundaries", e4m3 ? 8 : 4);
     if (e4m3 && !aligned(scales, 4))
         return fail(FP8KV_E_ALIGN, "fp32 key scales misaligned");
-    if (num_keys == 0) return ok();
     if (checked()) {
         int st = checked_begin(stream);
         if (st != FP8KV_OK) return st;
@@ -870,6 +874,7 @@ int fp8kv_index_keys_build(
         return fail(FP8KV_E_SHAPE, "batch %d, groups [%lld, %lld)", batch, (long long)g0,
                     (long long)g1);
     const bool bf16 = key_format == FP8KV_KEYS_BF16;
+    if (batch == 0 || g1 == g0) return ok();     // nothing read or written, pointers may be NULL
     if (!raw || !codes || (!scales && !bf16))
         return fail(FP8KV_E_NULL, "index_keys_build: a required pointer is NULL");
     if (raw_stride_b < 0 || raw_stride_tok < 0 || code_stride_b < 0 || code_stride_key < 0 ||
@@ -882,7 +887,6 @@ int fp8kv_index_keys_build(
         return fail(FP8KV_E_ALIGN, "code rows must start on %d-byte boundaries", cal);
     if (key_format == FP8KV_KEYS_E4M3 && !aligned(scales, 4))
         return fail(FP8KV_E_ALIGN, "fp32 key scales misaligned");
-    if (batch == 0 || g1 == g0) return ok();
     if (checked()) {
         int st = checked_begin(stream);
         if (st != FP8KV_OK) return st;
@@ -928,6 +932,7 @@ int fp8kv_index_score_mxfp4(
         return fail(FP8KV_E_SHAPE, "batch %d, rows %d, num_keys %d", batch, rows, num_keys);
     if (key_chunk < 0 || key_chunk % 16)
         return fail(FP8KV_E_SHAPE, "key_chunk %d: 0 (auto) or a positive multiple of 16", key_chunk);
+    if (batch == 0 || num_keys == 0) return ok();     // nothing read or written, pointers may be NULL
     if (!q || !w || !codes || !scales || !out)
         return fail(FP8KV_E_NULL, "index_score: a required pointer is NULL");
     if (q_stride_b < 0 || q_stride_row < 0 || q_stride_head < 0 || w_stride_b < 0 ||
@@ -941,7 +946,6 @@ int fp8kv_index_score_mxfp4(
     const bool e4m3 = key_format == FP8KV_KEYS_E4M3;
     if (!aligned(w, 4) || !aligned(out, 4) || (e4m3 && !aligned(scales, 4)))
         return fail(FP8KV_E_ALIGN, "w, out or key scales misaligned");
-    if (batch == 0 || num_keys == 0) return ok();
     if (checked()) {
         int st = checked_begin(stream);
         if (st != FP8KV_OK) return st;

@@ -36,6 +36,10 @@
  *     read by the host; the kernels bound every id they use (see each call)
  *     so a bad id never reads or writes outside the buffers described by the
  *     arguments.
+ *   - A call with nothing to do (no token to store, no request, no query
+ *     row, no key) returns FP8KV_OK after its shape and dtype checks,
+ *     enqueues nothing, and accepts NULL for every pointer (empty tensors
+ *     have no storage).
  *   - fp8kv_last_error() returns a thread-local description of the most
  *     recent failure on the calling thread.
  *   - An optional checked mode (fp8kv_set_checked) adds pointer-kind and

@@ -427,3 +427,20 @@ def test_unscaled_decode_refusals(L):
     assert call(D=96) == E_UNSUPPORTED
     assert call(wsb=16) == E_WORKSPACE
     assert call(B=0) == OK
+
+
+def test_zero_size_calls_accept_null_pointers(L):
+    """Nothing to do: status OK with every pointer NULL, no device touched
+    (explicit num_ranges, so no device query either); a bad shape or dtype
+    is still refused."""
+    assert qs(L, T=0, k=0, v=0, slots=0, kc=0, vc=0, ks=0, vs=0) == OK
+    assert qs(L, T=0, D=96, k=0, v=0, slots=0, kc=0, vc=0, ks=0, vs=0) == E_UNSUPPORTED
+    for fn in ("fp8kv_paged_decode_attn_fp8", "fp8kv_paged_decode_partials"):
+        assert dec(L, fn=fn, B=0, q=0, kc=0, vc=0, ks=0, vs=0, bt=0, cl=0, ws=0,
+                   out=0) == OK
+        assert dec(L, fn=fn, B=0, D=96, q=0, kc=0, vc=0, ks=0, vs=0, bt=0, cl=0, ws=0,
+                   out=0) == E_UNSUPPORTED
+    assert sdec(L, B=0, q=0, kc=0, vc=0, ks=0, vs=0, bt=0, bv=0, cl=0, ws=0,
+                out=0) == OK
+    assert L.fp8kv_paged_decode_merge(0, 1, 32, 8, 128, 384, None, 0, None, 0, 0, 0,
+                                      BF16, None) == OK
