@@ -181,6 +181,19 @@ def cache_build(torch, fk, k, v, slots, k_cache, v_cache, k_plane, v_plane,
     return ev0.elapsed_time(ev1)
 
 
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or the platform's."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(case, dc, lens, max_threads=16, budget_s=30.0):
     """The oracle (as it stands) on the same decode workload: every query row
     of as many of the 64 requests as fit the CPU budget (all of them here),
@@ -216,7 +229,8 @@ def cpu_baseline(case, dc, lens, max_threads=16, budget_s=30.0):
     first = host_request(0)
     t0 = time.perf_counter()
     run(first)
-    per_token = (time.perf_counter() - t0) / max(lens[0], 1)
+    t_first = time.perf_counter() - t0
+    per_token = t_first / max(lens[0], 1)
     n, work = 0, 0.0
     while n < len(lens) and work + per_token * lens[n] <= budget_s:
         work += per_token * lens[n]
@@ -231,6 +245,11 @@ def cpu_baseline(case, dc, lens, max_threads=16, budget_s=30.0):
     alg = tokens * H * 2 * (D + 4)
     return {"value": round(alg / wall / 1e9, 4), "unit": "GB/s",
             "cores": min(cores, n), "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "single_thread": {"value": round(lens[0] * H * 2 * (D + 4) / t_first / 1e9, 4),
+                              "unit": "GB/s", "seconds": round(t_first, 3),
+                              "sample": f"request 0 ({lens[0]} cached tokens x {H} KV "
+                                        f"heads, all {case.num_q_heads} query rows) on one core"},
             "sample": f"all {case.num_q_heads} query rows of {n} of the {len(lens)} "
                       f"decode requests ({tokens} cached tokens x {H} KV heads), "
                       f"one request per task; ~{work:.1f} s of single-core work",
@@ -284,7 +303,7 @@ def main():
     q = case.q.to(dev)
     bt = L.block_tables.to(dev)
     cl = L.context_lens.to(dev)
-    maxc = 32768
+    maxc = bt.shape[1] * bs            # the page tables' coverage (>= every length)
     nr = fk.decode_num_ranges(Hkv, args.ranges)
     ws = torch.empty(fk.decode_workspace_bytes(B, R, Hq, Hkv, D, nr),
                      dtype=torch.uint8, device=dev)
@@ -554,7 +573,7 @@ def sparse_decode(torch, fk, synth, dev, stream, case, q, bt, k_cache, v_cache,
                      dtype=torch.uint8, device=dev)
     out = torch.empty((B, R, Hq, D), dtype=torch.bfloat16, device=dev)
     kw = dict(num_kv_heads=Hkv, block_size=bs, softmax_scale=case.softmax_scale,
-              max_context=32768, num_ranges=nr, workspace=ws)
+              max_context=sbt.shape[1] * bs, num_ranges=nr, workspace=ws)
 
     def partials():
         fk.sparse_decode_partials(q, k_cache, v_cache, k_plane.t(), v_plane.t(),
@@ -613,7 +632,8 @@ def unscaled_decode(torch, fk, synth, dev, stream, case, q, bt, cl, reps=20):
             build_ms += e0.elapsed_time(e1)
             del k, v
         kw = dict(num_kv_heads=Hkv, block_size=L.block_size, softmax_scale=case.softmax_scale,
-                  max_context=32768, code_format=cf, num_ranges=nr, workspace=ws)
+                  max_context=bt.shape[1] * L.block_size, code_format=cf,
+                  num_ranges=nr, workspace=ws)
         run = lambda: fk.paged_decode_partials_unscaled(q, kc, vc, bt, cl, **kw)
         ms = sorted(time_events(run, reps, stream))
         med = ms[len(ms) // 2]

@@ -128,25 +128,79 @@ def _dev(*ts):
 
 
 def _cache_strides(cache: torch.Tensor):
-    """(stride_slot, stride_head) of a [S, H, D] or [NB, bs, H, D] code
-    buffer, inner stride 1."""
+    """(stride_slot, stride_head, S, H, D) of a uint8 [S, H, D] or
+    [NB, bs, H, D] code buffer whose head_dim is contiguous."""
+    if cache.dtype != torch.uint8:
+        raise ValueError("code buffers are uint8")
     if cache.dim() == 4:
         nb, bs, H, D = cache.shape
         if cache.stride(0) != bs * cache.stride(1):
             raise ValueError("4-D cache: blocks must be evenly spaced slots")
-        return cache.stride(1), cache.stride(2), nb * bs, H, D
-    if cache.dim() == 3:
+        css, csh, S = cache.stride(1), cache.stride(2), nb * bs
+    elif cache.dim() == 3:
         S, H, D = cache.shape
-        return cache.stride(0), cache.stride(1), S, H, D
-    raise ValueError("cache must be [S, H, D] or [NB, bs, H, D]")
+        css, csh = cache.stride(0), cache.stride(1)
+    else:
+        raise ValueError("cache must be [S, H, D] or [NB, bs, H, D]")
+    if D > 1 and cache.stride(-1) != 1:
+        raise ValueError("cache: head_dim must be the contiguous dimension")
+    return css, csh, S, H, D
 
 
-def _scale_strides(scale: torch.Tensor):
+def _kv_caches(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    """Geometry of a K/V code-buffer pair: same shape and strides."""
+    geom = _cache_strides(k_cache)
+    if v_cache.shape != k_cache.shape or _cache_strides(v_cache)[:2] != geom[:2]:
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    return geom
+
+
+def _scale_strides(scale: torch.Tensor, S=None, H=None):
+    """(stride_slot, stride_head) of an fp32 scale plane viewed as [S, H]
+    or [NB, bs, H]; with S and H given, the plane must cover exactly the
+    cache's S slots and H heads."""
+    if scale.dtype != torch.float32:
+        raise ValueError("scale planes are float32")
     if scale.dim() == 3:          # [NB, bs, H]
-        return scale.stride(1), scale.stride(2)
-    if scale.dim() == 2:          # [S, H]
-        return scale.stride(0), scale.stride(1)
-    raise ValueError("scale plane must be [S, H] or [NB, bs, H]")
+        nb, bs, h = scale.shape
+        if nb > 1 and scale.stride(0) != bs * scale.stride(1):
+            raise ValueError("3-D scale plane: blocks must be evenly spaced slots")
+        shape, strides = (nb * bs, h), (scale.stride(1), scale.stride(2))
+    elif scale.dim() == 2:        # [S, H]
+        shape, strides = tuple(scale.shape), (scale.stride(0), scale.stride(1))
+    else:
+        raise ValueError("scale plane must be [S, H] or [NB, bs, H]")
+    if S is not None and shape != (S, H):
+        raise ValueError(f"scale plane covers {shape} (slots, heads), the cache ({S}, {H})")
+    return strides
+
+
+def _scale_pair(k_scale, v_scale, S, H):
+    sss, ssh = _scale_strides(k_scale, S, H)
+    if _scale_strides(v_scale, S, H) != (sss, ssh):
+        raise ValueError("k_scale and v_scale must share strides")
+    return sss, ssh
+
+
+def _tables(block_tables, context_lens, B, block_size, max_context, extra=()):
+    """Page tables and per-request lengths of B requests: every length the
+    kernels use is clamped to max_context, so the tables must hold
+    ceil(max_context / block_size) entries per request."""
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or \
+            (block_tables.shape[1] > 1 and block_tables.stride(1) != 1):
+        raise ValueError("block_tables must be int32 [B, max_blocks], rows contiguous")
+    for t in (context_lens,) + tuple(extra):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+            raise ValueError("context_lens / q_lens must be contiguous int32 [B]")
+        if t.shape[0] != B:
+            raise ValueError(f"context_lens / q_lens hold {t.shape[0]} entries for {B} requests")
+    if block_size <= 0 or max_context < 0:
+        raise ValueError("block_size must be positive and max_context >= 0")
+    if B > 0 and block_tables.shape[0] < B:
+        raise ValueError(f"block_tables has {block_tables.shape[0]} rows for {B} requests")
+    if B > 0 and block_tables.shape[1] * block_size < max_context:
+        raise ValueError(f"block_tables rows cover {block_tables.shape[1] * block_size} "
+                         f"tokens, max_context is {max_context}")
 
 
 def abi_version() -> int:
@@ -169,7 +223,6 @@ def kv_quant_scatter(k: torch.Tensor, v: torch.Tensor, slot_ids: torch.Tensor,
     """Quantize K and V ([T, Hkv, D] bf16 views, each at its own strides) to
     E4M3 + fp32 row scales and scatter them to ``slot_ids`` (int64 [T],
     device) in one launch. Slot ids < 0 or >= num_slots are skipped."""
-    _dev(k, v, slot_ids, k_cache, v_cache, k_scale, v_scale)
     if k.shape != v.shape or k.dim() != 3:
         raise ValueError("k and v must both be [T, Hkv, D]")
     if k.dtype != v.dtype or k.dtype not in _TORCH_DTYPE:
@@ -180,19 +233,12 @@ def kv_quant_scatter(k: torch.Tensor, v: torch.Tensor, slot_ids: torch.Tensor,
         raise ValueError("slot_ids must be int64 [T]")
     if not slot_ids.is_contiguous():
         raise ValueError("slot_ids must be contiguous")
-    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
-        raise ValueError("code buffers are uint8")
-    if k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32:
-        raise ValueError("scale planes are float32")
-    css, csh, S, H, D = _cache_strides(k_cache)
-    if _cache_strides(v_cache)[:2] != (css, csh):
-        raise ValueError("k_cache and v_cache must share strides")
-    sss, ssh = _scale_strides(k_scale)
-    if _scale_strides(v_scale) != (sss, ssh):
-        raise ValueError("k_scale and v_scale must share strides")
+    css, csh, S, H, D = _kv_caches(k_cache, v_cache)
+    sss, ssh = _scale_pair(k_scale, v_scale, S, H)
     T, Hk, Dk = k.shape
     if (Hk, Dk) != (H, D):
         raise ValueError("K/V head count or head_dim differs from the cache")
+    _dev(k, v, slot_ids, k_cache, v_cache, k_scale, v_scale)
     _check(lib().fp8kv_kv_quant_scatter(
         k.data_ptr(), k.stride(0), k.stride(1),
         v.data_ptr(), v.stride(0), v.stride(1),
@@ -211,7 +257,6 @@ def kv_quant_scatter_unscaled(k: torch.Tensor, v: torch.Tensor, slot_ids: torch.
                               code_format: int = CODES_E4M3) -> None:
     """Store K and V ([T, Hkv, D] bf16 views) as unscaled E4M3 or E5M2 codes
     (round to nearest even, saturating) at ``slot_ids``; no scale planes."""
-    _dev(k, v, slot_ids, k_cache, v_cache)
     if k.dim() != 3 or v.shape != k.shape or k.dtype not in _TORCH_DTYPE or v.dtype != k.dtype:
         raise ValueError("k and v must be [T, Hkv, D] views of one float dtype")
     if k.stride(2) != 1 or v.stride(2) != 1:
@@ -219,14 +264,11 @@ def kv_quant_scatter_unscaled(k: torch.Tensor, v: torch.Tensor, slot_ids: torch.
     if slot_ids.dtype != torch.int64 or slot_ids.shape != (k.shape[0],) or \
             not slot_ids.is_contiguous():
         raise ValueError("slot_ids must be contiguous int64 [T]")
-    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
-        raise ValueError("code buffers are uint8")
-    css, csh, S, H, D = _cache_strides(k_cache)
-    if _cache_strides(v_cache)[:2] != (css, csh):
-        raise ValueError("k_cache and v_cache must share strides")
+    css, csh, S, H, D = _kv_caches(k_cache, v_cache)
     T, Hk, Dk = k.shape
     if (Hk, Dk) != (H, D):
         raise ValueError("K/V head count or head_dim differs from the cache")
+    _dev(k, v, slot_ids, k_cache, v_cache)
     _check(lib().fp8kv_kv_quant_scatter_unscaled(
         k.data_ptr(), k.stride(0), k.stride(1),
         v.data_ptr(), v.stride(0), v.stride(1),
@@ -260,26 +302,20 @@ def _decode_args(q, k_cache, v_cache, k_scale, v_scale, block_tables,
     """Argument list of the scaled decode calls; with k_scale = v_scale =
     None that of the unscaled ones (no scale planes)."""
     unscaled = k_scale is None and v_scale is None
-    _dev(q, k_cache, v_cache, block_tables, context_lens)
-    if not unscaled:
-        _dev(k_scale, v_scale)
     if q.dim() != 4 or q.stride(3) != 1:
         raise ValueError("q must be [B, R, Hq, D] with contiguous head_dim")
     if q.dtype not in _TORCH_DTYPE:
         raise ValueError("unsupported q dtype")
-    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or \
-            block_tables.stride(1) != 1:
-        raise ValueError("block_tables must be int32 [B, max_blocks], rows contiguous")
-    if context_lens.dtype != torch.int32 or not context_lens.is_contiguous():
-        raise ValueError("context_lens must be contiguous int32 [B]")
     B, R, Hq, D = q.shape
-    css, csh, S, H, Dc = _cache_strides(k_cache)
-    if _cache_strides(v_cache)[:2] != (css, csh) or H != num_kv_heads or Dc != D:
+    css, csh, S, H, Dc = _kv_caches(k_cache, v_cache)
+    if H != num_kv_heads or Dc != D:
         raise ValueError("cache geometry does not match q / num_kv_heads")
     if not unscaled:
-        sss, ssh = _scale_strides(k_scale)
-        if _scale_strides(v_scale) != (sss, ssh):
-            raise ValueError("k_scale and v_scale must share strides")
+        sss, ssh = _scale_pair(k_scale, v_scale, S, H)
+    _tables(block_tables, context_lens, B, block_size, int(max_context))
+    _dev(q, k_cache, v_cache, block_tables, context_lens)
+    if not unscaled:
+        _dev(k_scale, v_scale)
     ws_bytes = decode_workspace_bytes(B, R, Hq, num_kv_heads, D, num_ranges)
     if workspace is None:
         workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8,
@@ -423,22 +459,15 @@ def prefill_attn_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables,
     request's last q_lens[b] tokens (already in the cache); token i attends
     to the cached tokens 0 .. context_lens[b] - q_lens[b] + i. Returns out
     [B, max_q, Hq, D] (rows i >= q_lens[b] are left untouched)."""
-    _dev(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, q_lens)
     if q.dim() != 4 or q.stride(3) != 1 or q.dtype not in _TORCH_DTYPE:
         raise ValueError("q must be [B, max_q, Hq, D] with contiguous head_dim")
-    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or \
-            block_tables.stride(1) != 1:
-        raise ValueError("block_tables must be int32 [B, max_blocks], rows contiguous")
-    for t in (context_lens, q_lens):
-        if t.dtype != torch.int32 or not t.is_contiguous():
-            raise ValueError("context_lens and q_lens must be contiguous int32 [B]")
     B, Q, Hq, D = q.shape
-    css, csh, S, H, Dc = _cache_strides(k_cache)
-    if _cache_strides(v_cache)[:2] != (css, csh) or H != num_kv_heads or Dc != D:
+    css, csh, S, H, Dc = _kv_caches(k_cache, v_cache)
+    if H != num_kv_heads or Dc != D:
         raise ValueError("cache geometry does not match q / num_kv_heads")
-    sss, ssh = _scale_strides(k_scale)
-    if _scale_strides(v_scale) != (sss, ssh):
-        raise ValueError("k_scale and v_scale must share strides")
+    sss, ssh = _scale_pair(k_scale, v_scale, S, H)
+    _tables(block_tables, context_lens, B, block_size, int(max_context), extra=(q_lens,))
+    _dev(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, q_lens)
     if out is None:
         out = torch.zeros(q.shape, dtype=out_dtype, device=q.device)
     _dev(out)

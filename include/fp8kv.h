@@ -151,9 +151,10 @@ int fp8kv_kv_quant_scatter(
 
 /*
  * Paged GQA decode attention over the E4M3 cache (ATOM #2655, description,
- * K/V bullet: the attend reads E4M3 tiles, multiplies the key scale into
- * its score column and folds the value scale into the probability before
- * PV; sglang-jax #1776, "Modifications": K/V tiles are widened to the query
+ * K/V bullet: the attention kernel works on E4M3 tiles, scales each key's
+ * score by that key's scale and weights each value row's probability by
+ * the value's scale ahead of the PV product; sglang-jax #1776,
+ * "Modifications": K/V tiles are widened to the query
  * dtype before the score dot and the probabilities are never rounded to the
  * cache dtype).
  *
@@ -278,10 +279,10 @@ int fp8kv_paged_decode_merge(
  * fp8kv_sparse_decode_attn_fp8 -- the decode attention over SELECTED blocks
  * only ([ATOM] "fix(qwen4-exp): register the QSA FP8 scale planes for KV
  * offload", ROCm/ATOM #2655, description, K/V bullet: the sparse GQA kernel
- * reads E4M3 tiles, key scale on the score column, value scale folded into
- * P; "feat(kvcache): store the KV cache as fp8 e4m3 codes", FreeToken #354,
- * description: the block-selection keys stay 16-bit and only the selected
- * K/V rows are read back as codes).
+ * works on E4M3 tiles with the same key- and value-scale handling;
+ * "feat(kvcache): store the KV cache as fp8 e4m3 codes", FreeToken #354,
+ * description: block selection uses 16-bit keys, and the codes of the
+ * chosen rows are all that is fetched from the cache).
  *
  * Same arguments, rules and workspace as fp8kv_paged_decode_attn_fp8,
  * except:
@@ -407,8 +408,8 @@ int fp8kv_paged_decode_partials_unscaled(
  * ("feat(dsa): implement fp8 KV cache (e4m3) with a bf16 indexer cache",
  * sglang-jax #1776, "Modifications", qblock prefill bullet: the KV tile is
  * upcast to the query dtype once before the score dot and P never goes to
- * the cache dtype; ATOM #2655 description, K/V bullet: key scale on the
- * score column, value scale folded into P).
+ * the cache dtype; ATOM #2655 description, K/V bullet: key scale applied to
+ * each score, value scale to each probability weight).
  *
  * Request b has context_lens[b] cached tokens, the last q_lens[b] of which
  * are its chunk (already written with fp8kv_kv_quant_scatter); its query
@@ -478,9 +479,9 @@ int fp8kv_index_keys_quantize(
 
 /*
  * fp8kv_index_keys_build -- build compressed index keys from raw bf16 index
- * keys ([ATOM] description, compressed-index bullet: the raw index keys stay
- * BF16, are mean-pooled before normalization, and a pooling group can
- * straddle a prefill chunk). For every request b < batch and compressed key
+ * keys ([ATOM] description, compressed-index bullet: the raw index keys are
+ * kept in BF16, averaged in groups before the normalization, and a group
+ * may span two prefill chunks). For every request b < batch and compressed key
  * g in [g0, g1):
  *   m[d] = (r[4g][d] + r[4g+1][d] + r[4g+2][d] + r[4g+3][d]) / 4      (fp32)
  *   k[d] = bf16_rne(m[d] / ||m||_2)            (0 when m = 0)

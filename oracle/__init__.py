@@ -88,6 +88,9 @@ def _load():
     lib.fo_mxfp4_encode_group.argtypes = [P, P, P]
     lib.fo_index_keys_mxfp4.argtypes = [P, I64, I64, I64, P, I64, P, I64]
     lib.fo_index_keys_pool.argtypes = [P, I64, I64, I64, I64, P]
+    lib.fo_bf16_rne.argtypes = [D]
+    lib.fo_bf16_rne.restype = ctypes.c_uint16
+    lib.fo_index_keys_build_bf16.argtypes = [P, I64, I64, I64, I64, P]
     lib.fo_index_score.argtypes = [I, P, I64, I64, I64, P, I64, I64, I64,
                                    P, I64, I64, P, I64, I64,
                                    I64, I64, I64, I64, I64, P]
@@ -350,6 +353,32 @@ def index_keys_pool(raw_bits, g0, g1):
     out = np.empty((g1 - g0, D), np.float64)
     _load().fo_index_keys_pool(_ptr(r), r.strides[0] // 2, D, g0, g1, _ptr(out))
     return out
+
+
+def bf16_rne(x) -> np.ndarray:
+    """bf16 bits (uint16) of each float64 value, rounded once to nearest,
+    ties to even."""
+    x = np.asarray(x, dtype=np.float64)
+    f = _load().fo_bf16_rne
+    return np.array([f(float(v)) for v in x.reshape(-1)], np.uint16).reshape(x.shape)
+
+
+def index_keys_build(raw_bits, g0, g1, key_format):
+    """Compressed keys g0 .. g1-1 of one request's raw bf16 keys [L, D]
+    (bits), built end to end: pooled and normalized in double, rounded once
+    to bf16, then encoded. Returns the bf16 bits [g1 - g0, D] and, for
+    KEYS_MXFP4 / KEYS_E4M3, the (codes, scales) of those keys."""
+    r = np.asarray(raw_bits)
+    assert r.dtype == np.uint16 and r.ndim == 2 and r.strides[1] == 2
+    L, D = r.shape
+    assert 0 <= g0 <= g1 and 4 * g1 <= L and D <= 512
+    kb = np.empty((g1 - g0, D), np.uint16)
+    _load().fo_index_keys_build_bf16(_ptr(r), r.strides[0] // 2, D, g0, g1, _ptr(kb))
+    if key_format == KEYS_MXFP4:
+        return kb, index_keys_mxfp4(kb)
+    if key_format == KEYS_E4M3:
+        return kb, index_keys_e4m3(kb)
+    return kb, None
 
 
 def index_score(q_bits, w, key_format, codes, scales):

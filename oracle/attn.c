@@ -210,8 +210,8 @@ void fo_paged_decode_attn(
 /*
  * Decode attention over selected blocks ([ATOM] description, K/V bullet:
  * the sparse GQA kernel reads E4M3 tiles with the same scale handling;
- * FreeToken #354, description: only the selected K/V rows are read back
- * as codes). The selected blocks of request b are its page table, in
+ * FreeToken #354, description: the selection keys are 16-bit and the
+ * cache is fetched, as codes, for the chosen rows alone). The selected blocks of request b are its page table, in
  * position order; block_valid[b][i] (0 .. bs) counts the tokens of the i-th
  * selected block that are keys, from its start. Virtual position
  * j = i * bs + o is a key iff o < block_valid[b][i]; row r of R sees the

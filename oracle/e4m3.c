@@ -7,8 +7,8 @@
  * code whose mantissa LSB is 0 (round-to-nearest-even, the rounding the
  * FreeToken fix commit names for its reference quantizer). Out-of-range
  * magnitudes saturate to the largest finite value: a row scale of
- * amax / FP8 max never needs it ([ATOM] description, K/V bullet: dynamic
- * scales never saturate), so saturation only decides what a caller that
+ * amax / FP8 max never needs it ([ATOM] description, K/V bullet: with a
+ * scale taken from each row, no value leaves the format's range), so saturation only decides what a caller that
  * passes larger values gets.
  *
  * Parity pins: decode table against torch's float8_e4m3fn / float8_e5m2

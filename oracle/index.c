@@ -5,8 +5,8 @@
  * Source: "fix(qwen4-exp): register the QSA FP8 scale planes for KV
  * offload" (ROCm/ATOM #2655), description: the compressed index keys are
  * stored either as FP8 with one fp32 scale per row, or as MXFP4 -- packed
- * E2M1 pairs with one E8M0 exponent per 32 dims, the exponent rounded up so
- * that a group never clips; the decode-sized scorer stacks rows x index
+ * E2M1 pairs with one E8M0 exponent per 32 dims, the exponent chosen high
+ * enough that no element of the group overflows; the decode-sized scorer stacks rows x index
  * heads into the MFMA M dimension and applies the per-head ReLU before the
  * heads are summed. The scored quantity, per (row r, key n):
  *     score[r, n] = sum_h w[r, h] * max(0, q[r, h, :] . k^[n, :])
@@ -16,7 +16,7 @@
  *   - E2M1 is the OCP FP4 format: 1 sign, 2 exponent bits (bias 1), 1
  *     mantissa bit; no inf/NaN; magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}.
  *   - E8M0 code c is the scale 2^(c - 127) (c = 255, NaN, is never written).
- *   - "Rounded up so a group never clips": e is the smallest integer with
+ *   - The upward-rounded group exponent: e is the smallest integer with
  *     amax <= 6 * 2^e, found by exact comparison; code = e + 127, clamped
  *     to [0, 254]. An all-zero group gets code 127.
  *   - Each element is x / 2^e (exact) rounded to the nearest E2M1 magnitude,
@@ -149,8 +149,8 @@ void fo_index_score(int key_format, const uint16_t* q, int64_t qb, int64_t qr, i
 }
 
 /* Index-key builder ([ATOM] description, compressed-index bullet: the raw
- * index keys stay BF16 and are mean-pooled before normalization; a pooling
- * group can straddle a prefill chunk). Compressed key g of a request is
+ * index keys are kept in BF16, averaged in groups first and normalized
+ * after; a group may span two prefill chunks). Compressed key g of a request is
  *     m[d] = (r[4g][d] + r[4g+1][d] + r[4g+2][d] + r[4g+3][d]) / 4
  *     k[d] = m[d] / ||m||_2            (k = 0 when m = 0)
  * evaluated in double for groups g0 .. g1-1 of raw keys r (bf16 bits, row
@@ -170,5 +170,44 @@ void fo_index_keys_pool(const uint16_t* raw, int64_t rs, int64_t d, int64_t g0,
         }
         const double n = sqrt(ss);
         for (int64_t i = 0; i < d; ++i) k[i] = n > 0.0 ? k[i] / n : 0.0;
+    }
+}
+
+/* bf16 bits of the bf16 value nearest to x (finite, |x| < 2^128), ties to
+ * the value with an even last mantissa bit: one rounding straight from
+ * double. bf16 keeps 8 significant bits for exponents >= -126 and a fixed
+ * quantum of 2^-133 below (subnormals). The rounded value is exactly a
+ * float, whose upper 16 bits are the bf16 encoding. */
+uint16_t fo_bf16_rne(double x) {
+    const double a = fabs(x);
+    double r = 0.0;
+    if (a > 0.0) {
+        int e2;
+        frexp(a, &e2);                       /* a = f * 2^e2, f in [0.5, 1)  */
+        const int e = e2 - 1;                /* a in [2^e, 2^(e+1))          */
+        const double quantum = ldexp(1.0, (e < -126 ? -126 : e) - 7);
+        const double n = a / quantum;        /* exact: a power-of-two scale  */
+        double k = floor(n);
+        const double frac = n - k;           /* exact                        */
+        if (frac > 0.5 || (frac == 0.5 && fmod(k, 2.0) != 0.0)) k += 1.0;
+        r = k * quantum;                     /* exact, representable as float */
+    }
+    float f = (float)r;
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    if (signbit(x)) bits |= 0x80000000u;
+    return (uint16_t)(bits >> 16);
+}
+
+/* Compressed keys g0 .. g1-1 of one request as bf16 bits: the pooled and
+ * normalized key of fo_index_keys_pool (double), rounded once to bf16 --
+ * the "compressed keys are bf16 before they are quantized" reading;
+ * out[(g - g0) * d + i]. */
+void fo_index_keys_build_bf16(const uint16_t* raw, int64_t rs, int64_t d, int64_t g0,
+                              int64_t g1, uint16_t* out) {
+    double k[512];
+    for (int64_t g = g0; g < g1; ++g) {
+        fo_index_keys_pool(raw, rs, d, g, g + 1, k);
+        for (int64_t i = 0; i < d; ++i) out[(g - g0) * d + i] = fo_bf16_rne(k[i]);
     }
 }

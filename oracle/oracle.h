@@ -11,8 +11,8 @@
  *   [ATOM]  "fix(qwen4-exp): register the QSA FP8 scale planes for KV
  *           offload" (ROCm/ATOM #2655), description, K/V bullet: one FP32
  *           scale per (token, KV head) = row amax / FP8 max; the attend
- *           multiplies the key scale into the score column and folds the
- *           value scale into the probability.
+ *           applies each key's scale to that key's score and the value's
+ *           scale to its probability weight.
  *   [FT]    "feat(kvcache): store the KV cache as fp8 e4m3 codes"
  *           (FreeToken #354), description: head_dim codes + ONE fp32
  *           symmetric scale per row, uint8 code buffer with the 16-bit
@@ -144,6 +144,9 @@ void   fo_index_keys_mxfp4(const uint16_t* keys, int64_t n, int64_t d, int64_t k
                            uint8_t* packed, int64_t ps, uint8_t* exps, int64_t es);
 void   fo_index_keys_pool(const uint16_t* raw, int64_t rs, int64_t d, int64_t g0,
                           int64_t g1, double* out);
+uint16_t fo_bf16_rne(double x);                      /* one rounding to bf16  */
+void   fo_index_keys_build_bf16(const uint16_t* raw, int64_t rs, int64_t d, int64_t g0,
+                                int64_t g1, uint16_t* out);
 void   fo_index_score(int key_format, const uint16_t* q, int64_t qb, int64_t qr, int64_t qh,
                       const float* w, int64_t wb, int64_t wr, int64_t wh,
                       const void* codes, int64_t cb, int64_t cs,

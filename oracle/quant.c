@@ -26,7 +26,7 @@
  * id < 0 or >= num_slots writes nothing.
  *
  * Parity pins: codes equal torch's (x / scale).to(float8_e4m3fn) cast; the
- * row maximum always encodes to +-448 ("never saturate"); reconstruction
+ * row maximum always encodes to +-448 (dynamic row scales cannot overflow the format); reconstruction
  * within the format's relative half-ulp; zero rows; the strided-pitch
  * scenario of the FreeToken fix with distinct K and V pitches; sentinel
  * pools that show exactly the addressed rows change.

@@ -44,7 +44,7 @@ def test_sparse_decode_replays():
     ws = torch.empty(fk.decode_workspace_bytes(3, 1, 32, 8, 128, 29), dtype=torch.uint8, device=DEV)
     out = torch.empty(q.shape, device=DEV)
     kw = dict(num_kv_heads=8, block_size=16, softmax_scale=case.softmax_scale,
-              max_context=3072, num_ranges=29, workspace=ws)
+              max_context=16 * width, num_ranges=29, workspace=ws)
     run = lambda o: fk.sparse_decode_attn_fp8(q, dc.k_cache, dc.v_cache, dc.k_scale,
                                               dc.v_scale, bt, bv, cl, out=o, **kw)
     g = capture(lambda: run(out))

@@ -400,3 +400,57 @@ def test_builder_index_workload_full_size_sampled():
         rc, rs = oracle_keys(torch.from_numpy(bf16_keys_of(kb)[b][pick.numpy()].view(np.int16)).view(torch.bfloat16), MX)
         assert np.array_equal(codes[b][pick.to(DEV)].cpu().numpy(), rc)
         assert np.array_equal(scales[b][pick.to(DEV)].cpu().numpy(), rs)
+
+
+@pytest.mark.parametrize("fmt", [MX, E4])
+def test_builder_end_to_end_full_size(fmt):
+    """The index workload's keys (8 requests x 262,144 raw keys -> 65,536
+    compressed keys each) against the oracle end to end: pool and normalize
+    in double, one rounding to bf16, encode. Every key whose bf16 values the
+    kernel rounds like the oracle has bit-identical codes and scales; the
+    keys that differ are counted and logged, and every value that differs
+    is one bf16 step away with the exact pooled value within 2^-16
+    (relative) of the midpoint between the two (the fp32 mean and norm are
+    accurate to a few fp32 ulps)."""
+    from concurrent.futures import ThreadPoolExecutor
+    B, N = 8, 65536
+    raw = synth.normal_bf16((B, 4 * N, 128), synth.gen(63, DEV), device=DEV)
+    kb, _ = build_keys(raw, 0, N, fk.KEYS_BF16)
+    codes, scales = build_keys(raw, 0, N, fmt)
+    raw_h = bf16_bits(raw)
+    del raw
+    kb_h = bf16_keys_of(kb)
+    codes_h = codes.cpu().numpy()
+    scales_h = scales.cpu().numpy()
+
+    def one(b):
+        okb, (oc, osc) = oracle.index_keys_build(raw_h[b], 0, N, fmt)
+        pooled = oracle.index_keys_pool(raw_h[b], 0, N)
+        diff = kb_h[b] != okb
+        dk = diff.any(axis=1)
+        same = ~dk
+        ok_codes = np.array_equal(codes_h[b][same], oc[same])
+        if fmt == MX:
+            ok_scales = np.array_equal(scales_h[b][same], osc[same])
+        else:
+            ok_scales = np.array_equal(scales_h[b][same].view(np.uint32),
+                                       np.asarray(osc, np.float32)[same].view(np.uint32))
+        gv = oracle.bf16_to_f32(kb_h[b][diff]).astype(np.float64)
+        ov = oracle.bf16_to_f32(okb[diff]).astype(np.float64)
+        steps = np.abs(kb_h[b][diff].astype(np.int32) - okb[diff].astype(np.int32))
+        x = pooled[diff]
+        in_band = np.abs(x - 0.5 * (gv + ov)) <= TOL * np.abs(x)
+        return (int(dk.sum()), int(diff.sum()), ok_codes, ok_scales,
+                bool(np.all(steps == 1)), bool(np.all(in_band)))
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        res = list(ex.map(one, range(B)))
+    keys_off = sum(r[0] for r in res)
+    vals_off = sum(r[1] for r in res)
+    log(f"  builder end to end, format {fmt}: {keys_off} of {B * N} keys "
+        f"({vals_off} of {B * N * 128} bf16 values) differ from the oracle's "
+        f"one-rounding result; all others bit-exact")
+    for b, r in enumerate(res):
+        assert r[2] and r[3], f"request {b}: codes or scales differ on an equal key"
+        assert r[4] and r[5], f"request {b}: a differing value is outside the midpoint band"
+    assert vals_off <= B * N * 128 // 10000

@@ -294,3 +294,60 @@ def test_groups_follow_positions_not_chunks():
     raw2[20:24] = bf16_bits_of(np.full((4, 128), 7.0, np.float32))
     diff = np.abs(oracle.index_keys_pool(raw2, 0, 9) - whole).max(axis=1)
     assert np.all(diff[[0, 1, 2, 3, 4, 6, 7, 8]] == 0) and diff[5] > 0
+
+
+# ------------------------------------------- bf16 rounding of the pooled keys
+def bf16_value(bits):
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_bf16_rne_matches_torch_on_float_inputs():
+    """Inputs that are exact floats: torch's float32 -> bfloat16 cast (round
+    to nearest even) is the reference. Every midpoint between consecutive
+    bf16 values of a few binades, its float neighbours, log-uniform values
+    of both signs, and bf16 subnormals."""
+    base = np.arange(0x3E00, 0x4100, dtype=np.uint32)          # 0.125 .. 8
+    lo = (base << 16).view(np.float32)
+    mids = ((base << 16) | 0x8000).view(np.float32)            # exact midpoints
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(0))
+    g = np.random.default_rng(7)
+    logu = (np.exp(g.uniform(-80, 80, 20000)) * g.choice([-1, 1], 20000)).astype(np.float32)
+    sub = (np.arange(1, 300, dtype=np.float64) * 2.0 ** -134).astype(np.float32)
+    x = np.concatenate([lo, mids, up, dn, -mids, logu, sub, -sub, [0.0, -0.0]]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.bf16_rne(x.astype(np.float64))
+    assert np.array_equal(got, want), int((got != want).sum())
+
+
+def test_bf16_rne_rounds_once_from_double():
+    """Doubles within a float ulp of a bf16 midpoint round to the side they
+    lie on (a detour through float would make them ties)."""
+    base = np.arange(0x3F00, 0x4000, dtype=np.uint32)          # 0.5 .. 2
+    mid = bf16_value(base) + 0.5 * (bf16_value(base + 1) - bf16_value(base))
+    eps = mid * 2.0 ** -40
+    assert np.array_equal(oracle.bf16_rne(mid + eps), base + 1)
+    assert np.array_equal(oracle.bf16_rne(mid - eps), base)
+    # exact ties go to the even last bit
+    even = np.where(base % 2 == 0, base, base + 1)
+    assert np.array_equal(oracle.bf16_rne(mid), even)
+
+
+def test_index_keys_build_is_pool_then_torch_rounding_then_encode():
+    """End to end: the built bf16 keys equal torch's float64 mean and
+    normalization rounded to bf16 (wherever a detour through float cannot
+    change the rounding), and the codes equal the encoders' on those keys."""
+    g = torch.Generator().manual_seed(8)
+    raw = bf16_bits_of(torch.randn((4 * 300, 128), generator=g).numpy())
+    want64 = pool_torch(raw, 0, 300)
+    want = torch.from_numpy(want64).float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    # exclude values within 2^-20 (relative) of a bf16 midpoint
+    lo = bf16_value(want)
+    step = np.abs(bf16_value(want + np.uint16(1)) - lo)
+    near = np.abs(np.abs(want64 - lo) - 0.5 * step) <= 2.0 ** -20 * np.abs(want64)
+    for fmt in (oracle.KEYS_MXFP4, oracle.KEYS_E4M3):
+        kb, enc = oracle.index_keys_build(raw, 0, 300, fmt)
+        assert np.array_equal(kb[~near], want[~near])
+        ref = oracle.index_keys_mxfp4(kb) if fmt == oracle.KEYS_MXFP4 else oracle.index_keys_e4m3(kb)
+        for a, b in zip(enc, ref):
+            assert np.array_equal(np.asarray(a), np.asarray(b))

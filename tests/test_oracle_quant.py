@@ -3,8 +3,8 @@
 Fixed outside the oracle:
 * the torch-side reference the FreeToken fix commit checks codes against:
   scale = amax / 448 in fp32, codes = (x / scale).to(float8_e4m3fn);
-* "dynamic scales ... never saturate" (ATOM #2655, description): the row
-  maximum maps exactly onto the format maximum;
+* dynamic row scales never overflow the format (ATOM #2655, description,
+  K/V bullet): the row maximum maps exactly onto the format maximum;
 * half-ulp reconstruction bounds of the format;
 * the byte accounting of the FreeToken description: codes halve the bytes
   of a 16-bit row and the scale sidecar costs 4/head_dim (~3% at 128);

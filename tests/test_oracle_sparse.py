@@ -1,8 +1,9 @@
 """Pins of the oracle's decode attention over selected blocks ([ATOM]
 "fix(qwen4-exp): register the QSA FP8 scale planes for KV offload",
 description, K/V bullet: the sparse GQA kernel reads E4M3 tiles with the key
-scale on the score column and the value scale folded into P; FreeToken
-#354 description: only the selected K/V rows are read back as codes).
+scale applied to each score and the value scale to each probability weight;
+FreeToken #354 description: only the chosen rows of the cache are fetched,
+as codes).
 
 Fixed outside the oracle:
 * torch float64 softmax(scale * q K^T) V over exactly the keys the
