@@ -154,7 +154,7 @@ def test_out_of_range_ids_are_refused(checked):
     expect(E_RANGE, lambda: fk.sparse_decode_attn_fp8(
         case.q.to(DEV), dc.k_cache, dc.v_cache, dc.k_scale, dc.v_scale,
         sel.block_tables.to(DEV), bv.to(DEV), sel.context_lens.to(DEV),
-        **decode_kw(case)))
+        **dict(decode_kw(case), max_context=L.block_size * sel.block_tables.shape[1])))
 
     # prefill: a chunk longer than its request
     pc = synth.decode_case([100, 60], 8, 2, 128, 16, rows=64, seed=96)
