@@ -68,6 +68,8 @@ def lib():
            P, I32, I32, I32, I32, I32, I32, F, I32, I32, P, SZ]
     L.fp8kv_paged_decode_attn_fp8.argtypes = dec + [P, I64, I64, I64, I32, P]
     L.fp8kv_paged_decode_attn_fp8.restype = ctypes.c_int
+    L.fp8kv_paged_decode_attn_fp8_noalloc.argtypes = dec[:-2] + [P, I64, I64, I64, I32, P]
+    L.fp8kv_paged_decode_attn_fp8_noalloc.restype = ctypes.c_int
     L.fp8kv_paged_decode_partials.argtypes = dec + [P]
     L.fp8kv_paged_decode_partials.restype = ctypes.c_int
     L.fp8kv_kv_quant_scatter_unscaled.argtypes = [P, I64, I64, P, I64, I64, I32, I32,
@@ -298,9 +300,10 @@ def decode_num_ranges(num_kv_heads, num_ranges=0) -> int:
 
 def _decode_args(q, k_cache, v_cache, k_scale, v_scale, block_tables,
                  context_lens, num_kv_heads, block_size, softmax_scale,
-                 max_context, num_ranges, workspace):
+                 max_context, num_ranges, workspace, with_workspace=True):
     """Argument list of the scaled decode calls; with k_scale = v_scale =
-    None that of the unscaled ones (no scale planes)."""
+    None that of the unscaled ones (no scale planes); with_workspace=False
+    leaves out the workspace arguments (and allocates none)."""
     unscaled = k_scale is None and v_scale is None
     if q.dim() != 4 or q.stride(3) != 1:
         raise ValueError("q must be [B, R, Hq, D] with contiguous head_dim")
@@ -316,19 +319,21 @@ def _decode_args(q, k_cache, v_cache, k_scale, v_scale, block_tables,
     _dev(q, k_cache, v_cache, block_tables, context_lens)
     if not unscaled:
         _dev(k_scale, v_scale)
-    ws_bytes = decode_workspace_bytes(B, R, Hq, num_kv_heads, D, num_ranges)
-    if workspace is None:
-        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8,
-                                device=q.device)
-    _dev(workspace)
     scales = [] if unscaled else [k_scale.data_ptr(), v_scale.data_ptr(), sss, ssh]
     args = [q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
             _TORCH_DTYPE[q.dtype], k_cache.data_ptr(), v_cache.data_ptr(),
             css, csh] + scales + [S,
             block_tables.data_ptr(), block_tables.stride(0),
             context_lens.data_ptr(), B, R, Hq, num_kv_heads, D, block_size,
-            float(softmax_scale), int(num_ranges), int(max_context),
-            workspace.data_ptr(), workspace.numel() * workspace.element_size()]
+            float(softmax_scale), int(num_ranges), int(max_context)]
+    if not with_workspace:
+        return args, None
+    ws_bytes = decode_workspace_bytes(B, R, Hq, num_kv_heads, D, num_ranges)
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8,
+                                device=q.device)
+    _dev(workspace)
+    args += [workspace.data_ptr(), workspace.numel() * workspace.element_size()]
     return args, workspace
 
 
@@ -349,6 +354,28 @@ def paged_decode_attn_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables,
     if out.shape != q.shape or out.stride(3) != 1:
         raise ValueError("out must be [B, R, Hq, D] with contiguous head_dim")
     _check(lib().fp8kv_paged_decode_attn_fp8(
+        *args, out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
+        _TORCH_DTYPE[out.dtype], _stream(q.device)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def paged_decode_attn_fp8_noalloc(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                  context_lens, out, *, num_kv_heads, block_size,
+                                  softmax_scale, max_context, num_ranges=0):
+    """paged_decode_attn_fp8 without a workspace: the partials go to a device
+    array the library holds (NOALLOC_SCRATCH_BYTES per GPU), so the call
+    allocates nothing; ``out`` [B, R, Hq, D] (bf16 or fp32) is required.
+    Calls on one GPU share that array: order them on one stream."""
+    args, _ = _decode_args(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                           context_lens, num_kv_heads, block_size, softmax_scale,
+                           max_context, num_ranges, None, with_workspace=False)
+    _dev(out)
+    if out.shape != q.shape or out.stride(3) != 1 or out.dtype not in _TORCH_DTYPE:
+        raise ValueError("out must be [B, R, Hq, D] with contiguous head_dim")
+    _check(lib().fp8kv_paged_decode_attn_fp8_noalloc(
         *args, out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
         _TORCH_DTYPE[out.dtype], _stream(q.device)))
     return out

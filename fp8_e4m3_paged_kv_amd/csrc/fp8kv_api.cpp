@@ -638,6 +638,49 @@ int fp8kv_paged_decode_attn_fp8(
         out_stride_head, out_dtype, stream);
 }
 
+int fp8kv_paged_decode_attn_fp8_noalloc(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype, const uint8_t* k_cache,
+    const uint8_t* v_cache, int64_t cache_stride_slot,
+    int64_t cache_stride_head, const float* k_scale, const float* v_scale,
+    int64_t scale_stride_slot, int64_t scale_stride_head, int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, int32_t batch, int32_t rows,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float softmax_scale, int32_t num_ranges,
+    int32_t max_context, void* out, int64_t out_stride_b,
+    int64_t out_stride_row, int64_t out_stride_head, int32_t out_dtype,
+    void* stream) {
+    // the partials must fit the library's scratch: refuse before any HIP call
+    DecodeShape s;
+    int st = decode_shape(batch, rows, num_q_heads, num_kv_heads, head_dim, num_ranges, &s);
+    if (st != FP8KV_OK) return st;
+    if (s.ws_bytes > (int64_t)FP8KV_NOALLOC_SCRATCH_BYTES)
+        return fail(FP8KV_E_WORKSPACE,
+                    "paged_decode_noalloc: the partials need %lld bytes, more than the "
+                    "%lld-byte library scratch; use fp8kv_paged_decode_attn_fp8 with a workspace",
+                    (long long)s.ws_bytes, (long long)FP8KV_NOALLOC_SCRATCH_BYTES);
+    static_assert(fp8kv::kNoAllocScratchBytes == FP8KV_NOALLOC_SCRATCH_BYTES,
+                  "header and library agree on the scratch size");
+    void* scratch = nullptr;
+    if (batch > 0) {
+        const hipError_t e = fp8kv::noalloc_scratch(&scratch);
+        if (e != hipSuccess)
+            return fail(FP8KV_E_LAUNCH, "paged_decode_noalloc: scratch address: %s",
+                        hipGetErrorString(e));
+    }
+    // the scratch holds only the split's partials, each written before the
+    // merge reads it: nothing needs clearing between calls
+    return fp8kv_paged_decode_attn_fp8(
+        q, q_stride_b, q_stride_row, q_stride_head, q_dtype, k_cache, v_cache,
+        cache_stride_slot, cache_stride_head, k_scale, v_scale,
+        scale_stride_slot, scale_stride_head, num_slots, block_tables,
+        block_table_stride, context_lens, batch, rows, num_q_heads,
+        num_kv_heads, head_dim, block_size, softmax_scale, num_ranges,
+        max_context, scratch, batch > 0 ? (size_t)FP8KV_NOALLOC_SCRATCH_BYTES : 0, out,
+        out_stride_b, out_stride_row, out_stride_head, out_dtype, stream);
+}
+
 int fp8kv_sparse_decode_attn_fp8(
     const void* q, int64_t q_stride_b, int64_t q_stride_row,
     int64_t q_stride_head, int32_t q_dtype, const uint8_t* k_cache,

@@ -107,6 +107,12 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stre
 int decode_wave_slots(int device);
 
 hipError_t launch_decode_partitions(const DecodeParams& p, int head_dim, hipStream_t stream);
+
+// Library-held device scratch of the decode entry point that allocates
+// nothing: its size, and its address on the current device (looked up once
+// per device with hipGetSymbolAddress, then cached).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_decode_merge(const MergeParams& p, int head_dim,
                                hipStream_t stream);
 

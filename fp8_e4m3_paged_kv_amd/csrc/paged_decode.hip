@@ -29,9 +29,17 @@
 // The tile math (operand layouts, widening, softmax, PV) is in attn_tile.h.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "attn_tile.h"
 #include "fp8kv_device.h"
 #include "fp8kv_internal.h"
+
+// The decode partials of fp8kv_paged_decode_attn_fp8_noalloc: a device array
+// of fixed size that every GPU the library runs on holds until the process
+// ends. In host code this name is only a stand-in for the device symbol;
+// its device address comes from fp8kv::noalloc_scratch().
+static __device__ __align__(256) unsigned char scratch[fp8kv::kNoAllocScratchBytes];
 
 namespace fp8kv {
 namespace {
@@ -485,6 +493,29 @@ hipError_t launch_split_bs(const DecodeParams& p, hipStream_t stream) {
 }
 }  // namespace
 
+
+// Address of `scratch` on the current device: each GPU holds its own copy
+// at its own address, looked up the first time a call runs on that device
+// (with the device current) and cached.
+hipError_t noalloc_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 int decode_wave_slots(int device) {
     int cus = 0;

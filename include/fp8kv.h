@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FP8KV_ABI_VERSION 8
+#define FP8KV_ABI_VERSION 9
 
 typedef enum fp8kv_status {
     FP8KV_OK = 0,
@@ -217,6 +217,47 @@ int fp8kv_paged_decode_attn_fp8(
     int32_t head_dim, int32_t block_size, float softmax_scale,
     int32_t num_ranges, int32_t max_context,
     void* workspace, size_t workspace_bytes,
+    void* out, int64_t out_stride_b, int64_t out_stride_row,
+    int64_t out_stride_head, int32_t out_dtype,
+    void* stream);
+
+/*
+ * fp8kv_paged_decode_attn_fp8_noalloc -- fp8kv_paged_decode_attn_fp8 for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments,
+ * rules and results (bit for bit, for the same num_ranges) without the
+ * workspace: the partials go to a device array the library holds, of
+ * FP8KV_NOALLOC_SCRATCH_BYTES per GPU, kept by each GPU the library runs on
+ * until the process ends.
+ *   - The call allocates and frees nothing; its first call on a device looks
+ *     up that device's copy of the array (hipGetSymbolAddress).
+ *   - A call whose partials need more (fp8kv_paged_decode_workspace_bytes of
+ *     its sizes > FP8KV_NOALLOC_SCRATCH_BYTES) is refused with
+ *     FP8KV_E_WORKSPACE before anything else happens. 16 MiB covers, e.g.,
+ *     64 requests x 32 query heads / 8 KV heads and 4 requests x 4 verify
+ *     rows x 16 / 4 heads at the default split on a 256-CU device.
+ *   - Every call on one GPU shares its array, and the array keeps the last
+ *     call's partials: calls that overlap on one GPU (two streams, or two
+ *     host threads without ordering) race. Order them on one stream. No
+ *     clearing is needed between calls: the split writes every partial the
+ *     merge reads.
+ * Errors: as fp8kv_paged_decode_attn_fp8; E_WORKSPACE as above.
+ */
+#define FP8KV_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+int fp8kv_paged_decode_attn_fp8_noalloc(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype,
+    const uint8_t* k_cache, const uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head,
+    const float* k_scale, const float* v_scale,
+    int64_t scale_stride_slot, int64_t scale_stride_head,
+    int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens,
+    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, float softmax_scale,
+    int32_t num_ranges, int32_t max_context,
     void* out, int64_t out_stride_b, int64_t out_stride_row,
     int64_t out_stride_head, int32_t out_dtype,
     void* stream);

@@ -444,3 +444,49 @@ def test_zero_size_calls_accept_null_pointers(L):
                 out=0) == OK
     assert L.fp8kv_paged_decode_merge(0, 1, 32, 8, 128, 384, None, 0, None, 0, 0, 0,
                                       BF16, None) == OK
+
+
+def noalloc(L, **kw):
+    """fp8kv_paged_decode_attn_fp8_noalloc with the arguments of dec() minus
+    the workspace."""
+    a = dict(q=A, qsb=4096, qsr=4096, qsh=128, qdt=BF16, kc=A, vc=A,
+             css=1024, csh=128, ks=A, vs=A, sss=1, ssh=1 << 20, S=1 << 20,
+             bt=A, bts=2048, cl=A, B=64, R=1, Hq=32, H=8, D=128, bs=16,
+             scale=0.088, P=384, maxc=32768, out=A, osb=4096, osr=4096, osh=128,
+             odt=BF16)
+    a.update(kw)
+    return L.fp8kv_paged_decode_attn_fp8_noalloc(
+        a["q"], a["qsb"], a["qsr"], a["qsh"], a["qdt"], a["kc"], a["vc"], a["css"],
+        a["csh"], a["ks"], a["vs"], a["sss"], a["ssh"], a["S"], a["bt"], a["bts"],
+        a["cl"], a["B"], a["R"], a["Hq"], a["H"], a["D"], a["bs"],
+        ctypes.c_float(a["scale"]), a["P"], a["maxc"], a["out"], a["osb"], a["osr"],
+        a["osh"], a["odt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), E_UNSUPPORTED),
+    (dict(R=5), E_UNSUPPORTED),
+    (dict(P=-1), E_SHAPE),
+    (dict(P=1 << 14), E_WORKSPACE),      # 64 + 16383 pieces x 8 heads x 4 rows x 512 B > 16 MiB
+    (dict(B=40000, P=64), E_WORKSPACE),
+    (dict(B=0, q=0, kc=0, vc=0, ks=0, vs=0, bt=0, cl=0, out=0), OK),
+])
+def test_noalloc_decode_refusals(L, kw, status):
+    """The entry point that allocates nothing refuses sizes whose partials
+    exceed the library's scratch (and everything the workspace call
+    refuses) before it touches any device; nothing to do is OK."""
+    assert noalloc(L, **kw) == status
+    if status == E_WORKSPACE:
+        assert "scratch" in L.fp8kv_last_error().decode()
+
+
+def test_noalloc_scratch_limit_covers_the_bench_workloads(L):
+    """16 MiB holds the partials of the decode workload (64 requests, Hq 32
+    / Hkv 8, 128 ranges per KV head) and of the long-context verify
+    workload (4 requests, 4 rows, Hq 16 / Hkv 4, 256 ranges per KV head)."""
+    text = open(HEADER).read()
+    limit = int(eval(re.search(r"#define FP8KV_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                               text).expand(r"\1 << \2")))
+    assert limit == 16 << 20
+    assert L.fp8kv_paged_decode_workspace_bytes(64, 1, 32, 8, 128, 128) <= limit
+    assert L.fp8kv_paged_decode_workspace_bytes(4, 4, 16, 4, 128, 256) <= limit
