@@ -714,34 +714,42 @@ def prefill_attention(torch, fk, synth, dev, stream, reps=10):
 def index_scorer(torch, fk, synth, dev, stream, reps=20):
     """The compressed-index workload: 8 requests x 256 query rows x 16 index
     heads x 65,536 keys (dim 128), keys stored as MXFP4 and as E4M3; the
-    scorer's useful work is 2 * B * R * H * N * 128 flops (bf16 MFMA)."""
-    log("index scorer (8 x 256 rows x 16 heads x 65,536 keys)...")
-    case = synth.index_workload(seed=4, device=dev)
-    B, R, H, _ = case.q.shape
-    N = case.keys.shape[1]
-    flops = 2.0 * B * R * H * N * 128
-    out = torch.empty((B, R, N), dtype=torch.float32, device=dev)
+    scorer's useful work is 2 * B * R * H * N * 128 flops (bf16 MFMA). The
+    same with 4 index heads (4 rows x 4 heads per MFMA tile), where the
+    537 MB of fp32 scores weigh as much as the MFMA work: its line adds the
+    score bytes per second."""
     res = {}
-    for name, fmt, kbytes in (("mxfp4", fk.KEYS_MXFP4, 64 + 4),
-                              ("e4m3", fk.KEYS_E4M3, 128 + 4)):
-        codes, scales = fk.index_keys_quantize(case.keys, fmt)
-        enc = time_events(lambda: fk.index_keys_quantize(case.keys, fmt, codes, scales),
-                          reps, stream)
-        for _ in range(3):
-            fk.index_score_mxfp4(case.q, case.w, fmt, codes, scales, out=out)
-        ms = time_events(lambda: fk.index_score_mxfp4(case.q, case.w, fmt, codes,
-                                                      scales, out=out), reps, stream)
-        avg = sum(ms) / len(ms)
-        e_avg = sum(enc) / len(enc)
-        tf = flops / (avg * 1e-3) / 1e12
-        res[f"index_score_{name}_us"] = round(avg * 1e3, 1)
-        res[f"index_score_{name}_TFLOPs"] = round(tf, 1)
-        res[f"index_score_{name}_mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
-        res[f"index_keys_{name}_GBps"] = round(
-            B * N * (256 + kbytes) / (e_avg * 1e-3) / 1e9, 1)
-        del codes, scales
-    del case, out
-    torch.cuda.empty_cache()
+    for H in (16, 4):
+        log(f"index scorer (8 x 256 rows x {H} heads x 65,536 keys)...")
+        case = synth.index_workload(seed=4, device=dev, heads=H)
+        B, R, _, _ = case.q.shape
+        N = case.keys.shape[1]
+        flops = 2.0 * B * R * H * N * 128
+        out = torch.empty((B, R, N), dtype=torch.float32, device=dev)
+        tag = "" if H == 16 else f"h{H}_"
+        for name, fmt, kbytes in (("mxfp4", fk.KEYS_MXFP4, 64 + 4),
+                                  ("e4m3", fk.KEYS_E4M3, 128 + 4)):
+            codes, scales = fk.index_keys_quantize(case.keys, fmt)
+            if H == 16:
+                enc = time_events(lambda: fk.index_keys_quantize(case.keys, fmt, codes, scales),
+                                  reps, stream)
+                e_avg = sum(enc) / len(enc)
+                res[f"index_keys_{name}_GBps"] = round(
+                    B * N * (256 + kbytes) / (e_avg * 1e-3) / 1e9, 1)
+            settle(lambda: fk.index_score_mxfp4(case.q, case.w, fmt, codes, scales, out=out))
+            ms = time_events(lambda: fk.index_score_mxfp4(case.q, case.w, fmt, codes,
+                                                          scales, out=out), reps, stream)
+            avg = sum(ms) / len(ms)
+            tf = flops / (avg * 1e-3) / 1e12
+            res[f"index_score_{tag}{name}_us"] = round(avg * 1e3, 1)
+            res[f"index_score_{tag}{name}_TFLOPs"] = round(tf, 1)
+            res[f"index_score_{tag}{name}_mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+            if H != 16:
+                res[f"index_score_{tag}{name}_score_GBps"] = round(
+                    B * R * N * 4 / (avg * 1e-3) / 1e9, 1)
+            del codes, scales
+        del case, out
+        torch.cuda.empty_cache()
     # key builder: 4 raw bf16 keys -> one compressed key (mean, L2 norm, encode)
     raw = synth.normal_bf16((B, 4 * N, 128), synth.gen(5, dev), device=dev)
     for name, fmt, kbytes in (("mxfp4", fk.KEYS_MXFP4, 64 + 4),

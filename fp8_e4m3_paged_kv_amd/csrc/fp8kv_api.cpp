@@ -997,7 +997,8 @@ int fp8kv_index_score_mxfp4(
         if (st != FP8KV_OK) return st;
     }
 
-    const int32_t row_groups = (rows + fp8kv::kIndexRowsPerBlock - 1) / fp8kv::kIndexRowsPerBlock;
+    const int32_t rows_per_block = fp8kv::index_rows_per_block(num_heads);
+    const int32_t row_groups = (rows + rows_per_block - 1) / rows_per_block;
     int32_t chunk = key_chunk;
     if (chunk == 0) {
         // two waves per SIMD, every workgroup a (request, row group, chunk)
@@ -1020,6 +1021,16 @@ int fp8kv_index_score_mxfp4(
     const int64_t key_bytes = (int64_t)(num_keys - 1) * codes_stride_key + (e4m3 ? 128 : 64);
     const int64_t scale_bytes = (int64_t)(num_keys - 1) * scale_key_bytes + 4;
     const int64_t out_bytes = ((int64_t)(rows - 1) * out_stride_row + num_keys) * 4;
+    // score rows must not overlap: the kernel drops the stores of rows past
+    // `rows` by the range check, which needs each row to start past the
+    // previous row's last key (a single row's stride is never used); rows
+    // up to 31 past the end (a wave's last rows) stay below 2^31 bytes
+    const int64_t row_stride = rows > 1 ? out_stride_row : num_keys;
+    if (row_stride < num_keys)
+        return fail(FP8KV_E_STRIDE, "index scorer: out rows overlap (out_stride_row %lld < "
+                                    "num_keys %d)", (long long)out_stride_row, num_keys);
+    if (((int64_t)(rows + 31) * row_stride + num_keys) * 4 >= (INT64_C(1) << 31))
+        return fail(FP8KV_E_SHAPE, "index scorer: score rows span 2^31 bytes or more");
     if (key_bytes >= (INT64_C(1) << 30) || scale_bytes >= (INT64_C(1) << 30) ||
         out_bytes >= (INT64_C(1) << 30))
         return fail(FP8KV_E_SHAPE, "index scorer: one request's keys, scales or scores "
@@ -1042,7 +1053,7 @@ int fp8kv_index_score_mxfp4(
     p.scales_stride_key = e4m3 ? scales_stride_key * 4 : scales_stride_key;
     p.out = out;
     p.out_stride_b = out_stride_b;
-    p.out_stride_row = out_stride_row;
+    p.out_stride_row = row_stride;
     p.batch = batch;
     p.rows = rows;
     p.heads = num_heads;

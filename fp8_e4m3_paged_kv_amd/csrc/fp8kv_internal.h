@@ -122,8 +122,18 @@ constexpr int kKeysE4M3 = 1;
 constexpr int kKeysBF16 = 2;           // the builder's unquantized output
 constexpr int kIndexDim = 128;
 constexpr int kIndexMaxHeads = 16;     // MFMA M dimension
-constexpr int kIndexRowsPerWave = 8;
-constexpr int kIndexRowsPerBlock = 4 * kIndexRowsPerWave;
+// The scorer stacks rows x heads into the 16 MFMA rows: the heads are
+// padded up to a power of two HP, and 16 / HP rows share one MFMA tile.
+constexpr int index_heads_padded(int heads) {
+    return heads <= 1 ? 1 : heads <= 2 ? 2 : heads <= 4 ? 4 : heads <= 8 ? 8 : 16;
+}
+// Query rows per scorer workgroup (4 waves; a wave carries 8 MFMA tiles, or
+// 32 rows when the tiles stack more than 4 rows each).
+constexpr int index_rows_per_block(int heads) {
+    const int rpt = 16 / index_heads_padded(heads);
+    const int tiles = rpt <= 4 ? 8 : 32 / rpt;
+    return 4 * tiles * rpt;
+}
 
 struct IndexKeysParams {
     const uint16_t* keys;      // bf16 bits [num_keys, 128], row stride key_stride elements
@@ -149,7 +159,7 @@ struct IndexScoreParams {
     int32_t batch, rows, heads, num_keys;
     int32_t key_chunk;         // keys per workgroup, a multiple of 16
     int32_t chunks;            // ceil(num_keys / key_chunk)
-    int32_t row_groups;        // ceil(rows / kIndexRowsPerBlock)
+    int32_t row_groups;        // ceil(rows / index_rows_per_block(heads))
     int32_t key_bytes;         // per request: extent of the key codes in bytes
     int32_t scale_bytes;       // per request: extent of the key scales in bytes
     int32_t out_bytes;         // per request: (rows - 1) * out_stride_row * 4 + num_keys * 4

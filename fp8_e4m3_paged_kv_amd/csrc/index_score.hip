@@ -285,17 +285,63 @@ __device__ __forceinline__ float relu(float x) {
 // below 2^30 bytes, so the sum of two such offsets is rejected too).
 constexpr uint32_t kDropped = 0x40000000u;
 
-// Workgroup = 4 waves x RW query rows of one request and one chunk of its
-// keys; each wave scores its rows against every 16-key tile of the chunk.
-// The row groups of one (request, chunk) are placed on one XCD, so their key
-// reads meet in that XCD's L2. The tile loop has no branch: loads past the
-// chunk read in-bounds keys or zeros, stores of rows and keys outside the
-// output carry an offset the range check drops. Key loads run two tiles
-// ahead (three register buffers), and the MFMAs of each quad of rows are
-// issued next to the previous quad's epilogue, which does not depend on
-// them, so the matrix core and the vector ALU work side by side.
-template <int FMT, int RW>
-__global__ __launch_bounds__(256) void index_score_kernel(IndexScoreParams p) {
+// Rows x heads stacking. With HP index heads per row (H padded up to a
+// power of two, HP <= 16), one 16-row MFMA tile stacks RPT = 16 / HP query
+// rows x HP heads: M-row m is row m / HP, head m % HP ("4 rows x 4 index
+// heads into one M = 16 operand" for HP = 4). A wave carries NT such tiles
+// (NT * RPT rows: 8 rows at HP = 16, 16 at HP = 8, 32 below), in two halves
+// of NT / 2 tiles whose MFMAs and epilogues alternate. Lane (g, i) of a
+// tile's result holds M-rows 4g .. 4g+3 for key i, so the ReLU and the
+// weights of those 4 (row, head) pairs are applied in the lane; then
+//   HP = 16: the 4 lane groups hold quarters of one row: 4 tiles are summed
+//            by two swaps (v_permlane32_swap, v_permlane16_swap), leaving
+//            tile 4c + g's row in lane group g;
+//   HP = 8:  pairs of lane groups hold halves of a row: tiles 2v, 2v+1 are
+//            summed by one v_permlane16_swap;
+//   HP = 4:  lane group g holds row g of the tile whole;
+//   HP = 2, 1: lane group g holds 2 or 4 rows whole.
+// Every half thus ends with OS = NT * RPT / 8 "slots": one value per lane,
+// lane group g holding the scores of one row for the tile's 16 keys, which
+// one 4-byte store per lane writes (64 bytes per lane group).
+template <int HP>
+struct Stack {
+    static constexpr int RPT = 16 / HP;                  // rows per MFMA tile
+    static constexpr int NT = RPT <= 4 ? 8 : 32 / RPT;   // MFMA tiles per wave
+    static constexpr int NH = NT / 2;                    // tiles per half
+    static constexpr int ROWS = NT * RPT;                // rows per wave
+    static constexpr int OS = ROWS / 8;                  // store slots per half
+    // wave-relative row of slot s of half c in lane group g, as a part that
+    // depends on the lane group and a wave-uniform part:
+    //   HP = 16: tile 4c + g;               HP = 8: tile 4c + 2s + (g & 1), row g >> 1;
+    //   HP = 4:  tile 4c + s, row g;        HP = 2: tile 2c + s/2, row 2g + s%2;
+    //   HP = 1:  tile c, row 4g + s
+    static __device__ __forceinline__ int lane_row(int g) {
+        if (HP == 16 || HP == 4) return g;
+        if (HP == 8) return 2 * (g & 1) + (g >> 1);
+        return (16 / HP / 4) * g;
+    }
+    static constexpr int uniform_row(int c, int s) {
+        return HP == 16 ? 4 * c
+             : HP == 8  ? 8 * c + 4 * s
+             : HP == 4  ? 16 * c + 4 * s
+             : HP == 2  ? 16 * c + 8 * (s >> 1) + (s & 1)
+                        : 16 * c + s;
+    }
+};
+
+// Workgroup = 4 waves x Stack<HP>::ROWS query rows of one request and one
+// chunk of its keys; each wave scores its rows against every 16-key tile of
+// the chunk. The row groups of one (request, chunk) are placed on one XCD,
+// so their key reads meet in that XCD's L2. The tile loop has no branch:
+// loads past the chunk read in-bounds keys or zeros, stores of rows and keys
+// outside the output carry an offset the range check drops. Key loads run
+// two tiles ahead (three register buffers), and the MFMAs of each half of
+// the tiles are issued next to the other half's epilogue, which does not
+// depend on them, so the matrix core and the vector ALU work side by side.
+template <int FMT, int HP>
+__global__ __launch_bounds__(256, 2) void index_score_kernel(IndexScoreParams p) {
+    typedef Stack<HP> S;
+    constexpr int NT = S::NT, NH = S::NH, OS = S::OS;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 15, lg = lane >> 4;
@@ -311,35 +357,36 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexScoreParams p) {
     const int ck = bc % p.chunks;
     const int b = bc / p.chunks;
     if (b >= p.batch) return;
-    const int row0 = (rg * kScoreWaves + wave) * RW;
+    const int row0 = (rg * kScoreWaves + wave) * S::ROWS;
     const int n_begin = ck * p.key_chunk;
     const int n_end = min(n_begin + p.key_chunk, p.num_keys);
     if (row0 >= p.rows || n_begin >= n_end) return;
 
-    // q (A operand) and w of the wave's rows: lane (g, i) holds head i,
-    // dims [32g, 32g + 32), and the weights of heads 4g .. 4g+3
-    bf16x8 qa[RW][4];
-    float wv[RW][4];
+    // q (A operand) of tile j: lane (g, i) holds M-row i = (row j*RPT + i/HP,
+    // head i%HP), dims [32g, 32g + 32); w of M-rows 4g .. 4g+3
+    bf16x8 qa[NT][4];
+    float wv[NT][4];
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
-        const int row = row0 + r;
-        const bool rv = row < p.rows;
-        if (rv && li < p.heads) {
+    for (int j = 0; j < NT; ++j) {
+        const int row = row0 + j * S::RPT + li / HP;
+        const int head = li % HP;
+        if (row < p.rows && head < p.heads) {
             const uint16_t* qp = p.q + (int64_t)b * p.q_stride_b + (int64_t)row * p.q_stride_row +
-                                 (int64_t)li * p.q_stride_head + 32 * lg;
+                                 (int64_t)head * p.q_stride_head + 32 * lg;
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                qa[r][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 8 * k));
+                qa[j][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 8 * k));
         } else {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) qa[r][k] = bf16x8{};
+            for (int k = 0; k < 4; ++k) qa[j][k] = bf16x8{};
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int h = 4 * lg + j;
-            wv[r][j] = rv && h < p.heads
-                           ? p.w[(int64_t)b * p.w_stride_b + (int64_t)row * p.w_stride_row +
-                                 (int64_t)h * p.w_stride_head]
+        for (int r = 0; r < 4; ++r) {
+            const int wrow = row0 + j * S::RPT + (4 * lg + r) / HP;
+            const int whead = (4 * lg + r) % HP;
+            wv[j][r] = wrow < p.rows && whead < p.heads
+                           ? p.w[(int64_t)b * p.w_stride_b + (int64_t)wrow * p.w_stride_row +
+                                 (int64_t)whead * p.w_stride_head]
                            : 0.0f;
         }
     }
@@ -356,67 +403,120 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexScoreParams p) {
                     (FMT == kKeysE4M3 ? 32u : 16u) * lg;
     uint32_t soff = (uint32_t)(n_begin + li) * (uint32_t)p.scales_stride_key +
                     (FMT == kKeysE4M3 ? 0u : (uint32_t)lg);
-    uint32_t orow[RW / 4];
-#pragma unroll
-    for (int c = 0; c < RW / 4; ++c) {
-        const int row = row0 + 4 * c + lg;
-        orow[c] = row < p.rows ? (uint32_t)row * (uint32_t)p.out_stride_row * 4u : kDropped;
-    }
+    // byte offset of a slot's row: a per-lane part plus a wave-uniform one.
+    // Rows do not overlap (row stride >= num_keys), so a row at or past
+    // p.rows starts at or past the end of the request's scores and its
+    // stores are dropped by the range check; the host keeps every such
+    // offset below 2^31.
+    const uint32_t s4 = (uint32_t)p.out_stride_row * 4u;
+    // Tiles are stored in pairs (keys t .. t+31): one v_permlane16_swap of
+    // a slot's even-tile and odd-tile values gives lanes 0..31 one row's 32
+    // keys and lanes 32..63 another's, so every store writes whole 128-byte
+    // lines (64-byte halves written apart cost extra HBM traffic). Lane
+    // group g of the swapped pair holds the row of lane group g & 2 (first
+    // store) or (g & 2) | 1 (second store), keys t + 16 (g & 1) + i.
+    const uint32_t lb_x = (uint32_t)(row0 + S::lane_row(lg & 2)) * s4;
+    const uint32_t lb_y = (uint32_t)(row0 + S::lane_row((lg & 2) | 1)) * s4;
+    float hold[2][OS];
 
-    static_assert(RW == 8, "two quads of rows per wave");
-    floatx4 acc0[4], acc1[4];
-    auto mfma_quad = [&](const bf16x8 (&kb)[4], int c, floatx4 (&acc)[4]) {
+    floatx4 acc0[NH], acc1[NH];
+    auto mfma_half = [&](const bf16x8 (&kb)[4], int c, floatx4 (&acc)[NH]) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            acc[r] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < NH; ++t) {
+            acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[4 * c + r][k], kb[k], acc[r], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[NH * c + t][k], kb[k], acc[t], 0, 0, 0);
         }
     };
-    auto epilogue = [&](const floatx4 (&acc)[4], int c, float ks, uint32_t ocol) {
-        float s[4];
+    // the ReLU and weights of the lane's (row, head) pairs, reduced to one
+    // value per slot (one row per lane group), then stored
+    auto epilogue = [&](const floatx4 (&acc)[NH], int c, float ks, bool odd, uint32_t ocol) {
+        float v[OS];
+        if constexpr (HP >= 4) {
+            float s[NH];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float* wr = wv[4 * c + r];
-            float v = relu(acc[r][0]) * wr[0];
-            v = __builtin_fmaf(relu(acc[r][1]), wr[1], v);
-            v = __builtin_fmaf(relu(acc[r][2]), wr[2], v);
-            s[r] = __builtin_fmaf(relu(acc[r][3]), wr[3], v);
+            for (int t = 0; t < NH; ++t) {
+                const float* wr = wv[NH * c + t];
+                float x = relu(acc[t][0]) * wr[0];
+                x = __builtin_fmaf(relu(acc[t][1]), wr[1], x);
+                x = __builtin_fmaf(relu(acc[t][2]), wr[2], x);
+                s[t] = __builtin_fmaf(relu(acc[t][3]), wr[3], x);
+            }
+            if constexpr (HP == 16) {
+                v[0] = swap16_sum(swap32_sum(s[0], s[2]), swap32_sum(s[1], s[3]));
+            } else if constexpr (HP == 8) {
+                v[0] = swap16_sum(s[0], s[1]);
+                v[1] = swap16_sum(s[2], s[3]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < NH; ++t) v[t] = s[t];
+            }
+        } else if constexpr (HP == 2) {
+#pragma unroll
+            for (int t = 0; t < NH; ++t) {
+                const float* wr = wv[NH * c + t];
+                v[2 * t] = __builtin_fmaf(relu(acc[t][1]), wr[1], relu(acc[t][0]) * wr[0]);
+                v[2 * t + 1] = __builtin_fmaf(relu(acc[t][3]), wr[3], relu(acc[t][2]) * wr[2]);
+            }
+        } else {
+            const float* wr = wv[c];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = relu(acc[0][r]) * wr[r];
         }
-        const float sc = swap16_sum(swap32_sum(s[0], s[2]), swap32_sum(s[1], s[3])) * ks;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(sc), ors, (int)(orow[c] + ocol), 0,
-                                              kStoreNT);
+        if (!odd) {
+#pragma unroll
+            for (int sl = 0; sl < OS; ++sl) hold[c][sl] = v[sl] * ks;
+        } else {
+#pragma unroll
+            for (int sl = 0; sl < OS; ++sl) {
+                const auto xy = __builtin_amdgcn_permlane16_swap(
+                    __float_as_uint(hold[c][sl]), __float_as_uint(v[sl] * ks), false, false);
+                const uint32_t u = (uint32_t)S::uniform_row(c, sl) * s4 + ocol;
+                __builtin_amdgcn_raw_buffer_store_b32((int)xy[0], ors, (int)(lb_x + u), 0, kStoreNT);
+                __builtin_amdgcn_raw_buffer_store_b32((int)xy[1], ors, (int)(lb_y + u), 0, kStoreNT);
+            }
+        }
     };
-    auto col = [&](int t) { return t + li < n_end ? (uint32_t)(t + li) * 4u : kDropped; };
+    // column of the lane in the swapped pair starting at key t
+    auto colp = [&](int t) {
+        const int k = t + 16 * (lg & 1) + li;
+        return k < n_end ? (uint32_t)k * 4u : kDropped;
+    };
 
-    // one step: tile t's quad 0 MFMAs overlap the previous tile's quad 1
-    // epilogue, tile t's quad 1 MFMAs overlap its own quad 0 epilogue
+    // one step: tile t's half-0 MFMAs overlap the previous tile's half-1
+    // epilogue, tile t's half-1 MFMAs overlap its own half-0 epilogue; the
+    // epilogue of an even tile (from the chunk's start) holds its values, that
+    // of an odd tile stores the pair
     float ks_prev = 0.f;
+    bool odd_prev = false;
     uint32_t ocol_prev = kDropped;
     auto step = [&](const KeyTile<FMT>& kt, int t) {
         bf16x8 kb[4];
         kt.widen(kb);
         const float ks = FMT == kKeysE4M3 ? kt.kscale : 1.0f;
-        const uint32_t ocol = col(t);
-        mfma_quad(kb, 0, acc0);
-        epilogue(acc1, 1, ks_prev, ocol_prev);
-        mfma_quad(kb, 1, acc1);
-        epilogue(acc0, 0, ks, ocol);
+        const bool odd = ((t - n_begin) >> 4) & 1;
+        const uint32_t ocol = colp(t - 16);
+        mfma_half(kb, 0, acc0);
+        epilogue(acc1, 1, ks_prev, odd_prev, ocol_prev);
+        mfma_half(kb, 1, acc1);
+        epilogue(acc0, 0, ks, odd, ocol);
         ks_prev = ks;
+        odd_prev = odd;
         ocol_prev = ocol;
     };
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc1[r] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NH; ++t) acc1[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // tiles n_begin, n_begin + 16, ... and one more (its stores all dropped)
-    // to drain the pipeline; loads run two tiles ahead in three buffers
+    // tiles n_begin, n_begin + 16, ... and at least two more (their own
+    // stores all dropped) to drain the pipeline and complete the last pair;
+    // loads run two tiles ahead in three buffers
     KeyTile<FMT> ta, tb, tc;
     ta.load(krs, srs, koff, soff);
     koff += kstep;
     soff += sstep;
     tb.load(krs, srs, koff, soff);
-    for (int t = n_begin; t < n_end + 16; t += 48) {
+    for (int t = n_begin; t < n_end + 32; t += 48) {
         koff += kstep;
         soff += sstep;
         tc.load(krs, srs, koff, soff);
@@ -432,15 +532,26 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexScoreParams p) {
     }
 }
 
-template <int FMT>
-hipError_t launch_score(const IndexScoreParams& p, hipStream_t stream) {
+template <int FMT, int HP>
+hipError_t launch_score_hp(const IndexScoreParams& p, hipStream_t stream) {
     const int64_t m = p.row_groups;
     int64_t wgs = (int64_t)p.batch * p.chunks * m;
     if (m > 1) wgs = (wgs + 8 * m - 1) / (8 * m) * (8 * m);
     if (wgs > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((index_score_kernel<FMT, kIndexRowsPerWave>), dim3((unsigned)wgs),
+    hipLaunchKernelGGL((index_score_kernel<FMT, HP>), dim3((unsigned)wgs),
                        dim3(64 * kScoreWaves), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_score(const IndexScoreParams& p, hipStream_t stream) {
+    switch (index_heads_padded(p.heads)) {
+        case 16: return launch_score_hp<FMT, 16>(p, stream);
+        case 8: return launch_score_hp<FMT, 8>(p, stream);
+        case 4: return launch_score_hp<FMT, 4>(p, stream);
+        case 2: return launch_score_hp<FMT, 2>(p, stream);
+        default: return launch_score_hp<FMT, 1>(p, stream);
+    }
 }
 
 }  // namespace

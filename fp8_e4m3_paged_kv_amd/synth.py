@@ -284,9 +284,10 @@ def index_case(batch: int, rows: int, heads: int, num_keys: int, seed: int,
     return IndexCase(q, w, k.to(torch.bfloat16))
 
 
-def index_workload(seed: int = 4, device="cpu") -> IndexCase:
-    """8 requests x 256 query rows, 16 index heads, 65,536 keys each."""
-    return index_case(8, 256, 16, 65536, seed, device=device)
+def index_workload(seed: int = 4, device="cpu", heads: int = 16) -> IndexCase:
+    """8 requests x 256 query rows, 16 index heads (or `heads`), 65,536 keys
+    each."""
+    return index_case(8, 256, heads, 65536, seed, device=device)
 
 
 @dataclass

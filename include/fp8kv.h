@@ -556,7 +556,10 @@ int fp8kv_index_keys_build(
  * for b < batch, r < rows, n < num_keys, with k^ the dequantized key
  * (MXFP4: E2M1 value * 2^e of its group; E4M3: code value * key scale),
  * accumulated in fp32 (the products of bf16 q and the exactly widened key
- * elements are exact; the sums are fp32 MFMA and lane sums).
+ * elements are exact; the sums are fp32 MFMA and lane sums). Rows and
+ * index heads share the 16 MFMA rows (the page's stacked decode scorer):
+ * with H heads padded up to a power of two HP, 16 / HP rows x HP heads fill
+ * one tile (HP = 4: 4 rows x 4 heads), so few heads cost no idle MFMA rows.
  *
  * q           (device) FP8KV_DTYPE_BF16, element (b, r, h, d) at
  *             b*q_stride_b + r*q_stride_row + h*q_stride_head + d; pointer
@@ -573,6 +576,9 @@ int fp8kv_index_keys_build(
  * key_chunk   keys per workgroup: 0 = chosen for the current device, else
  *             a positive multiple of 16.
  * out         (device) fp32, (b, r, n) at b*out_stride_b + r*out_stride_row + n.
+ *             Rows must not overlap: out_stride_row >= num_keys when rows > 1
+ *             (else E_STRIDE), and ((rows + 31) * out_stride_row + num_keys)
+ *             * 4 < 2^31 (else E_SHAPE).
  * Errors: E_NULL, E_SHAPE, E_STRIDE, E_ALIGN, E_UNSUPPORTED, E_LAUNCH.
  */
 int fp8kv_index_score_mxfp4(

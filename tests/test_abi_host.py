@@ -272,6 +272,8 @@ def isc(L, **kw):
     (dict(fmt=E4M3, csk=128, scales=A + 1), E_ALIGN),
     (dict(out=A + 2), E_ALIGN),
     (dict(osr=1 << 22), E_SHAPE),        # one request's scores span >= 2^30 bytes
+    (dict(osr=65535), E_STRIDE),         # score rows overlap
+    (dict(R=2, osr=1 << 27), E_SHAPE),   # a wave's rows past the end would pass 2^31 bytes
     (dict(B=0), OK),
     (dict(N=0), OK),
 ])

@@ -227,8 +227,17 @@ def test_mxfp4_widening_subnormal_exponents():
     (2, 37, 16, 333, 0),        # ragged rows and keys, library chunking
     (3, 5, 16, 200, 48),        # several chunks with a tail
     (1, 1, 4, 17, 16),          # one row, 4 heads, a 1-key tail tile
-    (2, 70, 1, 64, 32),         # one head, rows across 3 workgroups
+    (2, 70, 1, 64, 32),         # one head: 16 rows per MFMA tile
+    (1, 300, 1, 100, 0),        # one head, rows across 3 workgroups of 128
     (1, 256, 16, 1000, 0),      # the verify-sized row count
+    (2, 37, 8, 333, 0),         # 2 rows x 8 heads per MFMA tile, ragged rows
+    (1, 70, 8, 96, 32),         # 8 heads: rows across 2 workgroups of 64
+    (2, 4, 4, 500, 0),          # 4 verify rows x 4 heads: one MFMA tile
+    (1, 130, 4, 333, 0),        # 4 heads: rows across 2 workgroups of 128
+    (2, 45, 2, 200, 48),        # 8 rows x 2 heads per tile
+    (1, 33, 3, 77, 16),         # 3 heads padded to 4
+    (1, 19, 5, 64, 0),          # 5 heads padded to 8
+    (1, 11, 12, 64, 0),         # 12 heads padded to 16
 ])
 def test_scores_match_oracle(fmt, B, R, H, N, chunk):
     case = synth.index_case(B, R, H, N, seed=B * 1000 + R + N)
@@ -240,11 +249,12 @@ def test_scores_match_oracle(fmt, B, R, H, N, chunk):
     check_scores(out, q, w, fmt, codes, scales, f"B{B} R{R} H{H} N{N}")
 
 
+@pytest.mark.parametrize("H", [16, 4, 1])
 @pytest.mark.parametrize("fmt", [MX, E4])
-def test_scores_strided_views_and_signed_weights(fmt):
+def test_scores_strided_views_and_signed_weights(fmt, H):
     """q and w as non-contiguous views, negative weights, keys with padded
     rows, out with a padded row stride: only the addressed bytes matter."""
-    B, R, H, N = 2, 9, 16, 130
+    B, R, N = 2, 9, 130
     case = synth.index_case(B, R, H, N, seed=77)
     qbig = torch.zeros((B, R, H + 3, 136), dtype=torch.bfloat16)
     qbig[:, :, 1:H + 1, :128] = case.q
@@ -279,13 +289,13 @@ def test_negative_dots_contribute_nothing():
         assert torch.all(out == 0)
 
 
-@pytest.mark.parametrize("fmt", [MX, E4])
-def test_index_workload_full_size_sampled(fmt):
-    """8 requests x 256 rows x 16 heads x 65,536 keys, the benchmark's
-    launch (library-chosen chunks); key codes of two requests are checked
-    bit for bit, and the oracle rescores 8 rows x 2048 keys of two
-    requests."""
-    case = synth.index_workload(seed=4, device=DEV)
+@pytest.mark.parametrize("fmt,H", [(MX, 16), (E4, 16), (MX, 4), (E4, 4)])
+def test_index_workload_full_size_sampled(fmt, H):
+    """8 requests x 256 rows x 16 (or 4) heads x 65,536 keys, the
+    benchmark's launches (library-chosen chunks); key codes of two requests
+    are checked bit for bit, and the oracle rescores 10 rows (every lane
+    group and store slot of the stacking) x 2048 keys of two requests."""
+    case = synth.index_workload(seed=4, device=DEV, heads=H)
     codes, scales = encode(case.keys, fmt)
     out = fk.index_score_mxfp4(case.q, case.w, fmt, codes, scales)
     torch.cuda.synchronize()
@@ -293,7 +303,7 @@ def test_index_workload_full_size_sampled(fmt):
     for b in (0, 7):
         rc, rs = oracle_keys(case.keys[b].cpu(), fmt)
         assert np.array_equal(codes[b].cpu().numpy(), rc)
-    rows = torch.tensor([0, 3, 64, 100, 127, 128, 200, 255])
+    rows = torch.tensor([0, 1, 2, 3, 64, 100, 127, 128, 200, 255])
     keys = torch.arange(0, 65536, 32)
     for b in (1, 6):
         sub_q = case.q[b:b + 1, rows]
