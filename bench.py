@@ -700,15 +700,40 @@ def prefill_attention(torch, fk, synth, dev, stream, reps=10):
         fk.prefill_attn_fp8(q, k_cache, v_cache, k_plane.t(), v_plane.t(), bt, cl, ql,
                             num_kv_heads=H, block_size=L.block_size,
                             softmax_scale=case.softmax_scale, max_context=ctx, out=out)
+    settle(run)
     ms = time_events(run, reps, stream)
     avg = sum(ms) / len(ms)
     flops = (P * C + C * (C + 1) // 2) * Hq * 4 * D
     tf = flops / (avg * 1e-3) / 1e12
+    res = {"prefill_attn_us": round(avg * 1e3, 1),
+           "prefill_attn_TFLOPs": round(tf, 1),
+           "prefill_attn_mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+    # the same chunk over selected blocks: 1/8 of the blocks before the
+    # chunk, then the chunk's own (every selected block full)
+    log("prefill attention over selected blocks (1/8 of the context)...")
+    sel = synth.prefill_selection(L, [C], 0.125, seed=72)
+    sbt, sbv, scl = (t.to(dev) for t in (sel.block_tables, sel.block_valid, sel.context_lens))
+    vctx = int(sel.context_lens[0])
+    Pv = vctx - C
+
+    def run_sel():
+        fk.sparse_prefill_attn_fp8(q, k_cache, v_cache, k_plane.t(), v_plane.t(), sbt, sbv,
+                                   scl, ql, num_kv_heads=H, block_size=L.block_size,
+                                   softmax_scale=case.softmax_scale,
+                                   max_context=L.block_size * sbt.shape[1], out=out)
+    settle(run_sel)
+    ms = time_events(run_sel, reps, stream)
+    avg = sum(ms) / len(ms)
+    flops = (Pv * C + C * (C + 1) // 2) * Hq * 4 * D
+    tf = flops / (avg * 1e-3) / 1e12
+    res.update({"sparse_prefill_selected_tokens": vctx,
+                "sparse_prefill_attn_us": round(avg * 1e3, 1),
+                "sparse_prefill_attn_TFLOPs": round(tf, 1),
+                "sparse_prefill_attn_mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
     del k_cache, v_cache, k_plane, v_plane, out
     torch.cuda.empty_cache()
-    return {"prefill_attn_us": round(avg * 1e3, 1),
-            "prefill_attn_TFLOPs": round(tf, 1),
-            "prefill_attn_mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    return res
 
 
 def index_scorer(torch, fk, synth, dev, stream, reps=20):

@@ -90,6 +90,9 @@ def lib():
                                          I32, I32, I32, I32, I32, I32, F, I32,
                                          P, I64, I64, I64, I32, P]
     L.fp8kv_prefill_attn_fp8.restype = ctypes.c_int
+    pre = L.fp8kv_prefill_attn_fp8.argtypes
+    L.fp8kv_sparse_prefill_attn_fp8.argtypes = pre[:16] + [P, I64] + pre[16:]
+    L.fp8kv_sparse_prefill_attn_fp8.restype = ctypes.c_int
     L.fp8kv_paged_decode_merge.argtypes = [I32, I32, I32, I32, I32, I32, P,
                                            SZ, P, I64, I64, I64, I32, P]
     L.fp8kv_paged_decode_merge.restype = ctypes.c_int
@@ -478,14 +481,11 @@ def sparse_decode_partials(q, k_cache, v_cache, k_scale, v_scale, block_tables,
     return workspace
 
 
-def prefill_attn_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables,
-                     context_lens, q_lens, *, num_kv_heads, block_size,
-                     softmax_scale, max_context, out=None,
-                     out_dtype=torch.bfloat16):
-    """Chunked-prefill attention: q [B, max_q, Hq, D] bf16 holds each
-    request's last q_lens[b] tokens (already in the cache); token i attends
-    to the cached tokens 0 .. context_lens[b] - q_lens[b] + i. Returns out
-    [B, max_q, Hq, D] (rows i >= q_lens[b] are left untouched)."""
+def _prefill_args(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                  q_lens, num_kv_heads, block_size, softmax_scale, max_context, out,
+                  out_dtype, block_valid=None):
+    """Argument list of the prefill calls (with block_valid: the selected-
+    block call) and the output tensor."""
     if q.dim() != 4 or q.stride(3) != 1 or q.dtype not in _TORCH_DTYPE:
         raise ValueError("q must be [B, max_q, Hq, D] with contiguous head_dim")
     B, Q, Hq, D = q.shape
@@ -494,20 +494,59 @@ def prefill_attn_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables,
         raise ValueError("cache geometry does not match q / num_kv_heads")
     sss, ssh = _scale_pair(k_scale, v_scale, S, H)
     _tables(block_tables, context_lens, B, block_size, int(max_context), extra=(q_lens,))
+    if block_valid is not None:
+        if block_valid.shape != block_tables.shape or block_valid.dtype != torch.int32 or \
+                (block_valid.shape[1] > 1 and block_valid.stride(1) != 1):
+            raise ValueError("block_valid must be int32 with the shape of block_tables, "
+                             "rows contiguous")
     _dev(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, q_lens)
+    if block_valid is not None:
+        _dev(block_valid)
     if out is None:
         out = torch.zeros(q.shape, dtype=out_dtype, device=q.device)
     _dev(out)
     if out.shape != q.shape or out.stride(3) != 1:
         raise ValueError("out must be [B, max_q, Hq, D] with contiguous head_dim")
-    _check(lib().fp8kv_prefill_attn_fp8(
-        q.data_ptr(), q.stride(0), q.stride(1), q.stride(2), _TORCH_DTYPE[q.dtype],
-        k_cache.data_ptr(), v_cache.data_ptr(), css, csh, k_scale.data_ptr(),
-        v_scale.data_ptr(), sss, ssh, S, block_tables.data_ptr(),
-        block_tables.stride(0), context_lens.data_ptr(), q_lens.data_ptr(), B, Q,
-        Hq, num_kv_heads, D, block_size, float(softmax_scale), int(max_context),
-        out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
-        _TORCH_DTYPE[out.dtype], _stream(q.device)))
+    sel = [] if block_valid is None else [block_valid.data_ptr(), block_valid.stride(0)]
+    args = [q.data_ptr(), q.stride(0), q.stride(1), q.stride(2), _TORCH_DTYPE[q.dtype],
+            k_cache.data_ptr(), v_cache.data_ptr(), css, csh, k_scale.data_ptr(),
+            v_scale.data_ptr(), sss, ssh, S, block_tables.data_ptr(),
+            block_tables.stride(0)] + sel + [context_lens.data_ptr(), q_lens.data_ptr(), B, Q,
+            Hq, num_kv_heads, D, block_size, float(softmax_scale), int(max_context),
+            out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
+            _TORCH_DTYPE[out.dtype], _stream(q.device)]
+    return args, out
+
+
+def prefill_attn_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                     context_lens, q_lens, *, num_kv_heads, block_size,
+                     softmax_scale, max_context, out=None,
+                     out_dtype=torch.bfloat16):
+    """Chunked-prefill attention: q [B, max_q, Hq, D] bf16 holds each
+    request's last q_lens[b] tokens (already in the cache); token i attends
+    to the cached tokens 0 .. context_lens[b] - q_lens[b] + i. Returns out
+    [B, max_q, Hq, D] (rows i >= q_lens[b] are left untouched)."""
+    args, out = _prefill_args(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                              context_lens, q_lens, num_kv_heads, block_size,
+                              softmax_scale, max_context, out, out_dtype)
+    _check(lib().fp8kv_prefill_attn_fp8(*args))
+    return out
+
+
+def sparse_prefill_attn_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                            block_valid, context_lens, q_lens, *, num_kv_heads,
+                            block_size, softmax_scale, max_context, out=None,
+                            out_dtype=torch.bfloat16):
+    """Chunked-prefill attention over selected blocks: block_tables [B,
+    max_sel] lists each request's selected blocks in position order (the
+    chunk's blocks among them), block_valid [B, max_sel] the keys of each
+    from its start, context_lens the virtual positions; chunk token i
+    attends positions 0 .. context_lens[b] - q_lens[b] + i."""
+    args, out = _prefill_args(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                              context_lens, q_lens, num_kv_heads, block_size,
+                              softmax_scale, max_context, out, out_dtype,
+                              block_valid=block_valid)
+    _check(lib().fp8kv_sparse_prefill_attn_fp8(*args))
     return out
 
 

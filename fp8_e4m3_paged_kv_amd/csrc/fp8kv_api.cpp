@@ -751,16 +751,18 @@ int fp8kv_paged_decode_attn_unscaled(
         out_stride_head, out_dtype, stream);
 }
 
-int fp8kv_prefill_attn_fp8(
+static int prefill(
     const void* q, int64_t q_stride_b, int64_t q_stride_tok, int64_t q_stride_head,
     int32_t q_dtype, const uint8_t* k_cache, const uint8_t* v_cache,
     int64_t cache_stride_slot, int64_t cache_stride_head, const float* k_scale,
     const float* v_scale, int64_t scale_stride_slot, int64_t scale_stride_head,
     int64_t num_slots, const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* block_valid, int64_t block_valid_stride,
     const int32_t* context_lens, const int32_t* q_lens, int32_t batch, int32_t max_q,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
     float softmax_scale, int32_t max_context, void* out, int64_t out_stride_b,
-    int64_t out_stride_tok, int64_t out_stride_head, int32_t out_dtype, void* stream) {
+    int64_t out_stride_tok, int64_t out_stride_head, int32_t out_dtype, void* stream,
+    bool selected) {
     if (head_dim != 64 && head_dim != 128)
         return fail(FP8KV_E_UNSUPPORTED, "head_dim %d: only 64 and 128 are supported", head_dim);
     if (q_dtype != FP8KV_DTYPE_BF16)
@@ -781,11 +783,12 @@ int fp8kv_prefill_attn_fp8(
     // no query row: nothing is read or written, any pointer may be NULL
     if (batch == 0 || max_q == 0) return ok();
     if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables || !context_lens ||
-        !q_lens || !out)
+        !q_lens || !out || (selected && !block_valid))
         return fail(FP8KV_E_NULL, "prefill: a required pointer is NULL");
     if (q_stride_b < 0 || q_stride_tok < 0 || q_stride_head < 0 || cache_stride_slot < 0 ||
         cache_stride_head < 0 || scale_stride_slot < 0 || scale_stride_head < 0 ||
-        block_table_stride < 0 || out_stride_b < 0 || out_stride_tok < 0 || out_stride_head < 0)
+        block_table_stride < 0 || block_valid_stride < 0 || out_stride_b < 0 ||
+        out_stride_tok < 0 || out_stride_head < 0)
         return fail(FP8KV_E_STRIDE, "prefill: negative stride");
     if (!aligned(q, 16) || q_stride_b % 8 || q_stride_tok % 8 || q_stride_head % 8)
         return fail(FP8KV_E_ALIGN, "q rows must start on 16-byte boundaries");
@@ -798,7 +801,7 @@ int fp8kv_prefill_attn_fp8(
         (out_stride_head * oel) % oal)
         return fail(FP8KV_E_ALIGN, "out rows must start on %d-byte boundaries", oal);
     if (!aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(block_tables, 4) ||
-        !aligned(context_lens, 4) || !aligned(q_lens, 4))
+        !aligned(block_valid, 4) || !aligned(context_lens, 4) || !aligned(q_lens, 4))
         return fail(FP8KV_E_ALIGN, "scale planes or tables misaligned");
     const int64_t num_blocks = num_slots / block_size;
     if (batch > 0 && max_context > 0 && num_blocks < 1)
@@ -812,12 +815,13 @@ int fp8kv_prefill_attn_fp8(
         if ((st = checked_begin(stream)) != FP8KV_OK) return st;
         st = check_device_ptrs({{q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"},
                                 {k_scale, "k_scale"}, {v_scale, "v_scale"},
-                                {block_tables, "block_tables"}, {context_lens, "context_lens"},
-                                {q_lens, "q_lens"}, {out, "out"}});
+                                {block_tables, "block_tables"}, {block_valid, "block_valid"},
+                                {context_lens, "context_lens"}, {q_lens, "q_lens"}, {out, "out"}});
         if (st != FP8KV_OK) return st;
         std::vector<int32_t> lens, qls;
-        st = check_tables(context_lens, block_tables, block_table_stride, nullptr, 0, batch,
-                          block_size, num_blocks, max_context, stream, &lens);
+        st = check_tables(context_lens, block_tables, block_table_stride, block_valid,
+                          block_valid_stride, batch, block_size, num_blocks, max_context, stream,
+                          &lens);
         if (st != FP8KV_OK) return st;
         if ((st = fetch(qls, q_lens, batch, stream)) != FP8KV_OK) return st;
         for (int32_t b = 0; b < batch; ++b)
@@ -840,6 +844,8 @@ int fp8kv_prefill_attn_fp8(
     p.scale_stride_head = scale_stride_head;
     p.block_tables = block_tables;
     p.block_table_stride = block_table_stride;
+    p.block_valid = selected ? block_valid : nullptr;
+    p.block_valid_stride = block_valid_stride;
     p.context_lens = context_lens;
     p.q_lens = q_lens;
     p.out = out;
@@ -861,6 +867,43 @@ int fp8kv_prefill_attn_fp8(
     p.max_context = max_context;
     p.score_scale_log2 = softmax_scale * 1.4426950408889634f;
     return launched(fp8kv::launch_prefill(p, head_dim, (hipStream_t)stream), "prefill_attn");
+}
+
+int fp8kv_prefill_attn_fp8(
+    const void* q, int64_t q_stride_b, int64_t q_stride_tok, int64_t q_stride_head,
+    int32_t q_dtype, const uint8_t* k_cache, const uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head, const float* k_scale,
+    const float* v_scale, int64_t scale_stride_slot, int64_t scale_stride_head,
+    int64_t num_slots, const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, const int32_t* q_lens, int32_t batch, int32_t max_q,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    float softmax_scale, int32_t max_context, void* out, int64_t out_stride_b,
+    int64_t out_stride_tok, int64_t out_stride_head, int32_t out_dtype, void* stream) {
+    return prefill(q, q_stride_b, q_stride_tok, q_stride_head, q_dtype, k_cache, v_cache,
+                   cache_stride_slot, cache_stride_head, k_scale, v_scale, scale_stride_slot,
+                   scale_stride_head, num_slots, block_tables, block_table_stride, nullptr, 0,
+                   context_lens, q_lens, batch, max_q, num_q_heads, num_kv_heads, head_dim,
+                   block_size, softmax_scale, max_context, out, out_stride_b, out_stride_tok,
+                   out_stride_head, out_dtype, stream, false);
+}
+
+int fp8kv_sparse_prefill_attn_fp8(
+    const void* q, int64_t q_stride_b, int64_t q_stride_tok, int64_t q_stride_head,
+    int32_t q_dtype, const uint8_t* k_cache, const uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head, const float* k_scale,
+    const float* v_scale, int64_t scale_stride_slot, int64_t scale_stride_head,
+    int64_t num_slots, const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* block_valid, int64_t block_valid_stride,
+    const int32_t* context_lens, const int32_t* q_lens, int32_t batch, int32_t max_q,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    float softmax_scale, int32_t max_context, void* out, int64_t out_stride_b,
+    int64_t out_stride_tok, int64_t out_stride_head, int32_t out_dtype, void* stream) {
+    return prefill(q, q_stride_b, q_stride_tok, q_stride_head, q_dtype, k_cache, v_cache,
+                   cache_stride_slot, cache_stride_head, k_scale, v_scale, scale_stride_slot,
+                   scale_stride_head, num_slots, block_tables, block_table_stride, block_valid,
+                   block_valid_stride, context_lens, q_lens, batch, max_q, num_q_heads,
+                   num_kv_heads, head_dim, block_size, softmax_scale, max_context, out,
+                   out_stride_b, out_stride_tok, out_stride_head, out_dtype, stream, true);
 }
 
 int fp8kv_index_keys_quantize(

@@ -85,6 +85,8 @@ struct PrefillParams {
     int64_t scale_stride_slot, scale_stride_head;
     const int32_t* block_tables;
     int64_t block_table_stride;
+    const int32_t* block_valid;    // selected blocks: valid keys per entry, or null (dense)
+    int64_t block_valid_stride;
     const int32_t* context_lens;   // cached tokens of request b, the chunk included
     const int32_t* q_lens;         // query tokens of request b: its last q_lens[b] tokens
     void* out;                     // [B, max_q, Hq, D]

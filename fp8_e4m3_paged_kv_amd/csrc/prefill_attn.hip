@@ -25,6 +25,15 @@
 // the scales as four consecutive tokens per lane (no lane broadcast needed).
 // Workgroups of one (request, KV head) run on one XCD, the deepest query
 // blocks first.
+// Selected blocks (SP): the page table lists the blocks a request selected,
+// in position order, with a count of valid keys per entry (from the block's
+// start), as in the decode over selected blocks; positions are virtual
+// (offset j % bs of selected block j / bs) and the chunk is causal on them.
+// A loader wave bounds its half by the block's count, so a partial block's
+// tail is never read, and publishes the half's key count in LDS; a tile
+// with a partial half takes the masked path, where a position past its
+// block's count is no key and adds exactly nothing (a row may see no key
+// in a tile, or at all: its output is then 0).
 // The prefill kernel keeps a row's running maximum until a tile's scores
 // exceed it by more than kLazyMax (log2 units), so p = exp2(s - m) stays
 // below 2^kLazyMax; its P' range factor is 2^(141 - kLazyMax - e), which
@@ -40,7 +49,7 @@ namespace {
 
 constexpr int kLazyMax = 8;
 
-template <int D, bool BSP2, int NT>
+template <int D, bool BSP2, int NT, bool SP>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     constexpr int KSTEPS = D / 32;
     constexpr int DL = D / 16;
@@ -55,6 +64,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     __shared__ __align__(16) uint8_t lds_k[2][32 * ROW];
     __shared__ __align__(16) uint8_t lds_v[2][32 * ROW];
     __shared__ __align__(16) float lds_s[2][2][32];   // [buf][k_scale * score scale | v_scale][token]
+    __shared__ int lds_nv[2][2];                      // selected blocks: [buf][half] keys of the half
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -125,19 +135,24 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     const float* ksbase = p.k_scale + (int64_t)h * p.scale_stride_head;
     const float* vsbase = p.v_scale + (int64_t)h * p.scale_stride_head;
     const int32_t* bt = p.block_tables + (int64_t)b * p.block_table_stride;
+    const int32_t* bv = SP ? p.block_valid + (int64_t)b * p.block_valid_stride : nullptr;
     intx4 kr = {0, 0, 0, 0}, vr = {0, 0, 0, 0};
     float sr = 0.f;
+    int ld_nv = 16;
     auto load_tile = [&](int ti) {
         // the wave's half: keys stok .. stok + nvalid - 1, all in one block
+        // (with selected blocks: only the block's valid keys from stok)
         const int stok = (ti << 5) + 16 * ld_half;
-        const int nvalid = min(16, kv_end - stok);
+        int nvalid = min(16, kv_end - stok);
         int64_t slot = 0;
         if (nvalid > 0) {
             const int bi = BSP2 ? (stok >> p.block_shift) : stok / p.block_size;
             const int bo = BSP2 ? (stok & (p.block_size - 1)) : stok - bi * p.block_size;
             const int blk = min(max(bt[bi], 0), p.num_blocks - 1);
             slot = (int64_t)blk * p.block_size + bo;
+            if (SP) nvalid = min(nvalid, min(max(bv[bi], 0), p.block_size) - bo);
         }
+        ld_nv = max(nvalid, 0);
         const int nrc = nvalid > 0 ? (nvalid - 1) * (int)p.cache_stride_slot + D : 0;
         const int nrs = nvalid > 0 ? 4 * ((nvalid - 1) * (int)p.scale_stride_slot + 1) : 0;
         const int64_t coff = slot * p.cache_stride_slot;
@@ -154,6 +169,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
         *reinterpret_cast<intx4*>(&lds_k[buf][lds_code]) = kr;
         *reinterpret_cast<intx4*>(&lds_v[buf][lds_code]) = vr;
         if (ld_chunk < 2) lds_s[buf][ld_chunk][ld_tok] = sr;
+        if (SP && lane == 0 && ((wave * TPL) & 15) == 0) lds_nv[buf][ld_half] = ld_nv;
     };
 
     if (loader) {
@@ -213,7 +229,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
             for (int r = 0; r < 4; ++r) sv[s][r] *= kappa;
 
         // ---- online softmax of each row tile; P' = p * v_scale * kappa
-        const bool masked = (ti << 5) + 31 > wave_lim;
+        int nv[2] = {16, 16};
+        if (SP) {
+            nv[0] = lds_nv[buf][0];
+            nv[1] = lds_nv[buf][1];
+        }
+        const bool masked = (ti << 5) + 31 > wave_lim || (SP && (nv[0] < 16 || nv[1] < 16));
         f16x8 pb[NT];
         WaveState<DL>* sts[NT];
 #pragma unroll
@@ -230,7 +251,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) s2[s][r] = 16 * s + r <= d ? s2[s][r] : kNeg;
+                    for (int r = 0; r < 4; ++r)
+                        s2[s][r] = (16 * s + r <= d && (!SP || 4 * lg + r < nv[s])) ? s2[s][r] : kNeg;
             }
             // lazy maximum: the running maximum moves only when a score
             // exceeds it by more than kLazyMax, so most tiles skip the rescale.
@@ -255,7 +277,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
                 for (int r = 0; r < 4; ++r) {
                     // a masked score gives exp2(kNeg - m) = 0: every row sees
                     // key 0 in the first tile, so m is a real score throughout
-                    const float e = __builtin_amdgcn_exp2f(s2[s][r] - st[j].m_run);
+                    // (with selected blocks a row may have seen no key yet, so
+                    // masked positions are zeroed explicitly)
+                    float e = __builtin_amdgcn_exp2f(s2[s][r] - st[j].m_run);
+                    if (SP && masked) e = s2[s][r] == kNeg ? 0.f : e;
                     st[j].l_run += e;
                     pr[r] = e * sv[s][r];
                 }
@@ -313,13 +338,24 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stre
     const int64_t wgs = ((int64_t)p.batch * p.num_kv_heads * p.qblocks + 7) / 8 * 8;
     if (wgs > INT32_MAX) return hipErrorInvalidValue;
     const bool pow2 = p.block_shift >= 0;
+    const bool sp = p.block_valid != nullptr;
     dim3 grid((unsigned)wgs), block(256);
     if (head_dim == 128) {
-        if (pow2) hipLaunchKernelGGL((prefill_kernel<128, true, kPrefillRowTiles>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((prefill_kernel<128, false, kPrefillRowTiles>), grid, block, 0, stream, p);
+        if (sp) {
+            if (pow2) hipLaunchKernelGGL((prefill_kernel<128, true, kPrefillRowTiles, true>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((prefill_kernel<128, false, kPrefillRowTiles, true>), grid, block, 0, stream, p);
+        } else {
+            if (pow2) hipLaunchKernelGGL((prefill_kernel<128, true, kPrefillRowTiles, false>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((prefill_kernel<128, false, kPrefillRowTiles, false>), grid, block, 0, stream, p);
+        }
     } else {
-        if (pow2) hipLaunchKernelGGL((prefill_kernel<64, true, kPrefillRowTiles>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((prefill_kernel<64, false, kPrefillRowTiles>), grid, block, 0, stream, p);
+        if (sp) {
+            if (pow2) hipLaunchKernelGGL((prefill_kernel<64, true, kPrefillRowTiles, true>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((prefill_kernel<64, false, kPrefillRowTiles, true>), grid, block, 0, stream, p);
+        } else {
+            if (pow2) hipLaunchKernelGGL((prefill_kernel<64, true, kPrefillRowTiles, false>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((prefill_kernel<64, false, kPrefillRowTiles, false>), grid, block, 0, stream, p);
+        }
     }
     return hipGetLastError();
 }

@@ -337,6 +337,44 @@ def sparse_selection(layout: PagedLayout, keep_frac: float, seed: int,
     return SparseSelection(bt, bv, torch.tensor(vlens, dtype=torch.int32))
 
 
+def prefill_selection(layout: PagedLayout, q_lens, keep_frac: float, seed: int,
+                      partial_frac: float = 0.0) -> SparseSelection:
+    """A block selection for a prefill chunk: every block that holds a chunk
+    token (the last q_lens[b] tokens of request b) in position order, after
+    a random fraction `keep_frac` of the blocks before them. Valid counts are
+    the block size, the last block's filled count, and for a fraction
+    `partial_frac` of the blocks before the chunk a random count in
+    [0, bs]; the chunk's tokens are then the last q_lens[b] virtual
+    positions."""
+    g = gen(seed)
+    bs = layout.block_size
+    lens = layout.context_lens.tolist()
+    tables, valids, vlens = [], [], []
+    for b, n in enumerate(lens):
+        nb = (n + bs - 1) // bs
+        first = (n - int(q_lens[b])) // bs             # first block holding a chunk token
+        k = int(round(keep_frac * first))
+        pick = torch.randperm(first, generator=g)[:k].sort().values.tolist() if first else []
+        idx = pick + list(range(first, nb))
+        valid = [bs] * len(idx)
+        if idx:
+            valid[-1] = n - (nb - 1) * bs
+        for i in range(len(pick)):
+            if float(torch.rand((), generator=g)) < partial_frac:
+                valid[i] = int(torch.randint(0, bs + 1, (), generator=g))
+        tables.append([int(layout.block_tables[b, i]) for i in idx])
+        valids.append(valid)
+        vlens.append((len(idx) - 1) * bs + valid[-1] if idx else 0)
+    m = max(1, max(len(t) for t in tables))
+    bt = torch.zeros((len(lens), m), dtype=torch.int32)
+    bv = torch.zeros((len(lens), m), dtype=torch.int32)
+    for b in range(len(lens)):
+        if tables[b]:
+            bt[b, :len(tables[b])] = torch.tensor(tables[b], dtype=torch.int32)
+            bv[b, :len(valids[b])] = torch.tensor(valids[b], dtype=torch.int32)
+    return SparseSelection(bt, bv, torch.tensor(vlens, dtype=torch.int32))
+
+
 def prefill_attn_workload(seed: int = 71, device="cpu") -> DecodeCase:
     """One request of 32,768 cached tokens whose last 4096 are the prefill
     chunk being attended (q [1, 4096, 32, 128]); Hkv 8, bs 16, N(0,1)."""

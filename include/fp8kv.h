@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FP8KV_ABI_VERSION 9
+#define FP8KV_ABI_VERSION 10
 
 typedef enum fp8kv_status {
     FP8KV_OK = 0,
@@ -475,6 +475,42 @@ int fp8kv_prefill_attn_fp8(
     const float* k_scale, const float* v_scale,
     int64_t scale_stride_slot, int64_t scale_stride_head, int64_t num_slots,
     const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, const int32_t* q_lens,
+    int32_t batch, int32_t max_q, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, float softmax_scale, int32_t max_context,
+    void* out, int64_t out_stride_b, int64_t out_stride_tok, int64_t out_stride_head,
+    int32_t out_dtype, void* stream);
+
+/*
+ * fp8kv_sparse_prefill_attn_fp8 -- chunked-prefill attention over SELECTED
+ * blocks only ([ATOM] "fix(qwen4-exp): register the QSA FP8 scale planes for
+ * KV offload", ROCm/ATOM #2655, description, MI355X results: the sparse GQA
+ * prefill over the E4M3 cache; "feat(kvcache): store the KV cache as fp8
+ * e4m3 codes", FreeToken #354, description: the codes of the chosen rows
+ * are all that is fetched from the cache).
+ *
+ * fp8kv_prefill_attn_fp8 over the selection of fp8kv_sparse_decode_attn_fp8:
+ * block_tables  (device) int32: row b lists the blocks request b selected,
+ *               in position order; the chunk's own tokens are among them.
+ * block_valid   (device) int32, entry (b, i) at b*block_valid_stride + i:
+ *               how many tokens of the i-th selected block, from its start,
+ *               are keys (clamped to [0, block_size]). Must not be NULL.
+ * context_lens  (device) int32: virtual positions of request b (position j
+ *               is offset j % block_size of selected block j / block_size);
+ *               its last q_lens[b] positions are the chunk, and chunk token i
+ *               attends the keys at positions 0 .. context_lens[b] -
+ *               q_lens[b] + i. A token that sees no key gets out = 0.
+ * With every block selected and full counts this is fp8kv_prefill_attn_fp8.
+ * Errors: as fp8kv_prefill_attn_fp8; E_NULL for block_valid.
+ */
+int fp8kv_sparse_prefill_attn_fp8(
+    const void* q, int64_t q_stride_b, int64_t q_stride_tok, int64_t q_stride_head,
+    int32_t q_dtype, const uint8_t* k_cache, const uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head,
+    const float* k_scale, const float* v_scale,
+    int64_t scale_stride_slot, int64_t scale_stride_head, int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* block_valid, int64_t block_valid_stride,
     const int32_t* context_lens, const int32_t* q_lens,
     int32_t batch, int32_t max_q, int32_t num_q_heads, int32_t num_kv_heads,
     int32_t head_dim, int32_t block_size, float softmax_scale, int32_t max_context,
