@@ -296,7 +296,6 @@ def main():
     last = torch.tensor([sum(lens[:b + 1]) - 1 for b in range(B)], device=dev)
     k_new = case.k[last].contiguous()
     v_new = case.v[last].contiguous()
-    slots_new = slots_all[last].contiguous()
     del case.k, case.v
     torch.cuda.empty_cache()
 
@@ -315,14 +314,17 @@ def main():
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     rec = {"i": None}
 
+    # the step's new K/V rows, one per request, as [B, 1, Hkv, D]: the split
+    # launch quantizes them into the cache before it reads their tiles
+    k_new_rows = k_new.unsqueeze(1)
+    v_new_rows = v_new.unsqueeze(1)
+
     def step():
-        fk.kv_quant_scatter(k_new, v_new, slots_new, k_cache, v_cache,
-                            k_plane.t(), v_plane.t())
         i = rec["i"]
         if i is not None:
             ev_a[i].record(stream)
-        fk.paged_decode_partials(q, k_cache, v_cache, k_plane.t(), v_plane.t(),
-                                 bt, cl, workspace=ws, **kw)
+        fk.paged_decode_append_partials(q, k_new_rows, v_new_rows, k_cache, v_cache,
+                                        k_plane.t(), v_plane.t(), bt, cl, workspace=ws, **kw)
         if i is not None:
             ev_b[i].record(stream)
         fk.paged_decode_merge(ws, out, rows=R, num_q_heads=Hq,
@@ -357,9 +359,12 @@ def main():
     part_avg_ms = sum(part_ms) / len(part_ms)
 
     dec_bytes, dec_kv = decode_bytes(lens, Hkv, D, B, R, Hq, bs)
-    step_bytes = dec_bytes + quant_bytes(B, Hkv, D)
+    # the appended rows: bf16 K/V read, codes and scales written (their slots
+    # come from the page table the decode reads anyway)
+    app_bytes = quant_bytes(B, Hkv, D) - 8 * B
+    step_bytes = dec_bytes + app_bytes
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    part_bytes = dec_bytes - B * R * Hq * D * 2     # the merge writes out
+    part_bytes = dec_bytes - B * R * Hq * D * 2 + app_bytes   # the merge writes out
     achieved = part_bytes / (part_avg_ms * 1e-3) / 1e9
     log(f"decode step: {ms_per_step * 1e3:.1f} us, split kernel "
         f"{part_avg_ms * 1e3:.1f} us = {achieved:.0f} GB/s")
@@ -378,8 +383,9 @@ def main():
         "vs_baseline": None,
         "dtype": "e4m3 codes (u8) + fp32 scales; bf16/fp16 MFMA, fp32 accumulate",
         "data": "synthetic (seeded N(0,1) bf16 K/V/q)",
-        "config": {"workload": "decode step: quant-scatter of 64 new tokens + paged GQA "
-                               "decode, 64 requests, lengths U[1024,32768]",
+        "config": {"workload": "decode step: 64 new tokens quantized into the cache inside "
+                               "the split launch + paged GQA decode, 64 requests, "
+                               "lengths U[1024,32768]",
                    "batch": B, "context_tokens": sum(lens), "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "block_size": bs,
                    "decode_ranges_per_kv_head": nr,
@@ -400,7 +406,16 @@ def main():
 
     extras = set() if args.no_extras else set(args.extras.split(","))
     if "prefill" in extras:
-        result["also"].update(prefill_quant_scatter(torch, fk, synth, dev, stream))
+        qs = prefill_quant_scatter(torch, fk, synth, dev, stream)
+        fl = chunk_store_floors(torch, dev, stream)
+        # the chunk store against a plain 2:1 stream of its bytes launched
+        # the same way (graph replay, rotating buffers)
+        fl["quant_scatter_prefill_floor_tokens_per_s"] = round(
+            4096 / (fl["graph_floor_stream_2to1_25MB_us"] * 1e-6), 0)
+        fl["quant_scatter_prefill_over_floor"] = round(
+            qs["quant_scatter_prefill_us"] / fl["graph_floor_stream_2to1_25MB_us"], 3)
+        result["also"].update(qs)
+        result["also"].update(fl)
     if "longctx" in extras:
         result["also"].update(longctx_decode(torch, fk, synth, dev, stream))
     if "sparse" in extras:
@@ -648,21 +663,92 @@ def unscaled_decode(torch, fk, synth, dev, stream, case, q, bt, cl, reps=20):
     return res
 
 
+def probes_lib():
+    """The benchmark's probe kernels (libfp8kv_probes.so, built beside the
+    cache library): fp8kv_probe(kind, a, b, dst, bytes, stream) with kind 0
+    read, 1 copy, 2 read a and b / write dst (2:1), 3 write, 4 empty."""
+    import ctypes
+    from fp8_e4m3_paged_kv_amd import build as hipbuild
+    if not os.path.exists(hipbuild.PROBES_LIB):
+        raise ImportError(f"{hipbuild.PROBES_LIB} is missing: run the build")
+    L = ctypes.CDLL(hipbuild.PROBES_LIB)
+    P = ctypes.c_void_p
+    L.fp8kv_probe.argtypes = [ctypes.c_int, P, P, P, ctypes.c_size_t, P]
+    L.fp8kv_probe.restype = ctypes.c_int
+    return L
+
+
+def probe(L, stream, kind, a=None, b=None, d=None, nbytes=0):
+    st = L.fp8kv_probe(kind, None if a is None else a.data_ptr(),
+                       None if b is None else b.data_ptr(),
+                       None if d is None else d.data_ptr(), nbytes, stream.cuda_stream)
+    if st != 0:
+        raise RuntimeError(f"probe kind {kind}: status {st}")
+
+
 def hbm_ceilings(torch, dev, stream, gib=2, reps=10):
-    """What plain library kernels reach on this GPU: a device copy of 2 GiB
-    (read + write bytes) and an int64 sum over 2 GiB (read bytes)."""
-    log("HBM ceilings (library copy and read kernels)...")
+    """What plain streaming kernels reach on this GPU (the probe library's
+    16-byte non-temporal streams over 2 GiB buffers: read, copy, 2:1
+    read:write, write), and what the library's own copy and sum kernels
+    reach, for reference."""
+    log("HBM ceilings (probe streams, library copy and read kernels)...")
+    L = probes_lib()
     n = gib << 30
-    src = torch.ones(n // 8, dtype=torch.int64, device=dev)
-    dst = torch.empty_like(src)
+    a = torch.ones(n // 8, dtype=torch.int64, device=dev)
+    b = torch.ones_like(a)
+    d = torch.empty_like(a)
     res = {}
-    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * n),
-                            ("read", lambda: src.sum(), n)):
-        for _ in range(3):
-            fn()
+    for name, fn, moved in (
+            ("read", lambda: probe(L, stream, 0, a=a, d=d, nbytes=n), n),
+            ("copy", lambda: probe(L, stream, 1, a=a, d=d, nbytes=n), 2 * n),
+            ("read2_write1", lambda: probe(L, stream, 2, a=a, b=b, d=d, nbytes=n), 3 * n),
+            ("write", lambda: probe(L, stream, 3, d=d, nbytes=n), n),
+            ("torch_copy", lambda: d.copy_(a), 2 * n),
+            ("torch_sum", lambda: a.sum(), n)):
+        settle(fn, 0.1)
         ms = sorted(time_events(fn, reps, stream))
-        res[f"hbm_{name}_ceiling_GBps"] = round(moved / (ms[len(ms) // 2] * 1e-3) / 1e9, 1)
-    del src, dst
+        res[f"hbm_{name}_GBps"] = round(moved / (ms[len(ms) // 2] * 1e-3) / 1e9, 1)
+    del a, b, d
+    torch.cuda.empty_cache()
+    return res
+
+
+def chunk_store_floors(torch, dev, stream, sets=32, reps=4):
+    """Floors for the 4096-token prefill-chunk store, in its own harness
+    (one HIP graph of `sets` launches, replayed): an empty kernel (the
+    per-launch floor), and a 2:1 read:write stream of the chunk's bytes
+    (two 8.4 MB reads, one 8.4 MB write: 25.2 MB per launch, rotating
+    over `sets` buffer sets as the store rotates its inputs)."""
+    log("prefill-chunk floors (empty kernel, 25 MB 2:1 stream, graph replay)...")
+    L = probes_lib()
+    part = 4096 * 8 * 128 * 2 // 2                        # bytes of K (or V) in bf16 / 2
+    bufs = [tuple(torch.empty(part // 8, dtype=torch.int64, device=dev) for _ in range(3))
+            for _ in range(sets)]
+    res = {}
+    side = torch.cuda.Stream(dev)
+    for name, launch in (("empty", lambda i: probe(L, side, 4)),
+                         ("stream_2to1_25MB", lambda i: probe(L, side, 2, a=bufs[i][0], b=bufs[i][1],
+                                                              d=bufs[i][2], nbytes=part))):
+        torch.cuda.synchronize()
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(sets):
+                launch(i)
+        stream.wait_stream(side)
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        res[f"graph_floor_{name}_us"] = round(t0.elapsed_time(t1) / (reps * sets) * 1e3, 2)
+        del graph
+    del bufs
     torch.cuda.empty_cache()
     return res
 

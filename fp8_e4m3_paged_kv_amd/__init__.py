@@ -68,6 +68,12 @@ def lib():
            P, I32, I32, I32, I32, I32, I32, F, I32, I32, P, SZ]
     L.fp8kv_paged_decode_attn_fp8.argtypes = dec + [P, I64, I64, I64, I32, P]
     L.fp8kv_paged_decode_attn_fp8.restype = ctypes.c_int
+    L.fp8kv_paged_decode_append_attn_fp8.argtypes = (dec[:5] + [P, I64, I64, I64, P, I64, I64, I64, I32]
+                                                      + dec[5:] + [P, I64, I64, I64, I32, P])
+    L.fp8kv_paged_decode_append_attn_fp8.restype = ctypes.c_int
+    L.fp8kv_paged_decode_append_partials.argtypes = (dec[:5] + [P, I64, I64, I64, P, I64, I64, I64, I32]
+                                                      + dec[5:] + [P])
+    L.fp8kv_paged_decode_append_partials.restype = ctypes.c_int
     L.fp8kv_paged_decode_attn_fp8_noalloc.argtypes = dec[:-2] + [P, I64, I64, I64, I32, P]
     L.fp8kv_paged_decode_attn_fp8_noalloc.restype = ctypes.c_int
     L.fp8kv_paged_decode_partials.argtypes = dec + [P]
@@ -360,6 +366,63 @@ def paged_decode_attn_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables,
         *args, out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
         _TORCH_DTYPE[out.dtype], _stream(q.device)))
     return out
+
+
+def _append_args(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables,
+                 context_lens, num_kv_heads, block_size, softmax_scale, max_context,
+                 num_ranges, workspace):
+    """Argument list of the append calls (without out) and the workspace."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, R, Hq, D]")
+    B, R, _, D = q.shape
+    for t in (k_new, v_new):
+        if t.dim() != 4 or t.dtype != torch.bfloat16 or t.stride(3) != 1:
+            raise ValueError("k_new and v_new must be bf16 [B, R, Hkv, D], contiguous D")
+        if tuple(t.shape) != (B, R, num_kv_heads, D):
+            raise ValueError("k_new / v_new must be [B, R, Hkv, D] matching q")
+    args, workspace = _decode_args(q, k_cache, v_cache, k_scale, v_scale,
+                                   block_tables, context_lens, num_kv_heads,
+                                   block_size, softmax_scale, max_context,
+                                   num_ranges, workspace)
+    _dev(k_new, v_new)
+    new = [k_new.data_ptr(), k_new.stride(0), k_new.stride(1), k_new.stride(2),
+           v_new.data_ptr(), v_new.stride(0), v_new.stride(1), v_new.stride(2), DTYPE_BF16]
+    return args[:5] + new + args[5:], workspace
+
+
+def paged_decode_append_attn_fp8(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                                 block_tables, context_lens, *, num_kv_heads, block_size,
+                                 softmax_scale, max_context, num_ranges=0, out=None,
+                                 out_dtype=torch.bfloat16, workspace=None):
+    """One decode step: k_new / v_new [B, R, Hkv, D] bf16 (each at its own
+    strides) are the K/V rows of every request's last R positions (already
+    counted in context_lens); they are quantized into the cache at the slots
+    its page table gives, and the decode attention of paged_decode_attn_fp8
+    runs over the cache including them. Returns out [B, R, Hq, D]."""
+    args, workspace = _append_args(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                                   block_tables, context_lens, num_kv_heads, block_size,
+                                   softmax_scale, max_context, num_ranges, workspace)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _dev(out)
+    if out.shape != q.shape or out.stride(3) != 1:
+        raise ValueError("out must be [B, R, Hq, D] with contiguous head_dim")
+    _check(lib().fp8kv_paged_decode_append_attn_fp8(
+        *args, out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
+        _TORCH_DTYPE[out.dtype], _stream(q.device)))
+    return out
+
+
+def paged_decode_append_partials(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                                 block_tables, context_lens, *, num_kv_heads, block_size,
+                                 softmax_scale, max_context, num_ranges=0, workspace=None):
+    """Split phase of paged_decode_append_attn_fp8 (the new rows' store and
+    the partials); returns the workspace for paged_decode_merge."""
+    args, workspace = _append_args(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                                   block_tables, context_lens, num_kv_heads, block_size,
+                                   softmax_scale, max_context, num_ranges, workspace)
+    _check(lib().fp8kv_paged_decode_append_partials(*args, _stream(q.device)))
+    return workspace
 
 
 NOALLOC_SCRATCH_BYTES = 16 << 20

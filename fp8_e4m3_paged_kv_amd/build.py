@@ -12,6 +12,9 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libfp8kv.so")
+# measurement kernels for the benchmark (HBM streams, launch floor)
+PROBES_LIB = os.path.join(PKG, "libfp8kv_probes.so")
+PROBES_SRC = os.path.join(PKG, "csrc", "probes", "hbm_probes.hip")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -35,18 +38,24 @@ def sources():
                   glob.glob(os.path.join(csrc, "*.cpp")))
 
 
-def build(verbose: bool = False) -> str:
+def _hipcc(srcs, out, verbose):
     hipcc = os.environ.get("HIPCC", "hipcc")
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc] + HIPCC_FLAGS + ["-I", os.path.join(ROOT, "include"),
-                                   "-o", tmp] + sources()
+                                   "-o", tmp] + srcs
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libfp8kv.so")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Build libfp8kv.so and the benchmark's probe library."""
+    _hipcc(sources(), LIB, verbose)
+    _hipcc([PROBES_SRC], PROBES_LIB, verbose)
     return LIB
 
 

@@ -216,6 +216,14 @@ int check_tables(const int32_t* context_lens, const int32_t* block_tables, int64
     return FP8KV_OK;
 }
 
+// New K/V rows of fp8kv_paged_decode_append_attn_fp8 (k == nullptr: none).
+struct AppendRows {
+    const void* k = nullptr;
+    int64_t k_sb = 0, k_sr = 0, k_sh = 0;
+    const void* v = nullptr;
+    int64_t v_sb = 0, v_sr = 0, v_sh = 0;
+};
+
 static int decode_partials(
     const void* q, int64_t q_stride_b, int64_t q_stride_row,
     int64_t q_stride_head, int32_t q_dtype, const uint8_t* k_cache,
@@ -228,7 +236,7 @@ static int decode_partials(
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
     int32_t block_size, float softmax_scale, int32_t num_ranges,
     int32_t max_context, void* workspace, size_t workspace_bytes,
-    int32_t codes, void* stream) {
+    int32_t codes, void* stream, const AppendRows& app = AppendRows()) {
     DecodeShape s;
     int st = decode_shape(batch, rows, num_q_heads, num_kv_heads, head_dim, num_ranges, &s);
     if (st != FP8KV_OK) return st;
@@ -251,6 +259,20 @@ static int decode_partials(
     if ((int64_t)workspace_bytes < s.ws_bytes)
         return fail(FP8KV_E_WORKSPACE, "workspace %zu bytes < required %lld",
                     workspace_bytes, (long long)s.ws_bytes);
+    if (app.k || app.v) {
+        // the new rows: bf16 [B, rows, Hkv, D], rows on head_dim/8-byte
+        // boundaries (the quantizer's one 16- or 8-byte load per lane)
+        const int64_t el = head_dim / 16;
+        if (!app.k || !app.v)
+            return fail(FP8KV_E_NULL, "paged_decode_append: k_new or v_new is NULL");
+        if (app.k_sb < 0 || app.k_sr < 0 || app.k_sh < 0 || app.v_sb < 0 || app.v_sr < 0 ||
+            app.v_sh < 0)
+            return fail(FP8KV_E_STRIDE, "paged_decode_append: negative new-row stride");
+        if (!aligned(app.k, 2 * el) || !aligned(app.v, 2 * el) || app.k_sb % el ||
+            app.k_sr % el || app.k_sh % el || app.v_sb % el || app.v_sr % el || app.v_sh % el)
+            return fail(FP8KV_E_ALIGN, "new K/V rows must start on %lld-byte boundaries",
+                        (long long)(2 * el));
+    }
     if (q_stride_b < 0 || q_stride_row < 0 || q_stride_head < 0 ||
         cache_stride_slot < 0 || cache_stride_head < 0 ||
         scale_stride_slot < 0 || scale_stride_head < 0 ||
@@ -279,7 +301,8 @@ static int decode_partials(
         st = check_device_ptrs({{q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"},
                                 {k_scale, "k_scale"}, {v_scale, "v_scale"},
                                 {block_tables, "block_tables"}, {block_valid, "block_valid"},
-                                {context_lens, "context_lens"}, {workspace, "workspace"}});
+                                {context_lens, "context_lens"}, {workspace, "workspace"},
+                                {app.k, "k_new"}, {app.v, "v_new"}});
         if (st != FP8KV_OK) return st;
         st = check_tables(context_lens, block_tables, block_table_stride, block_valid,
                           block_valid_stride, batch, block_size, num_blocks, max_context, stream,
@@ -287,7 +310,7 @@ static int decode_partials(
         if (st != FP8KV_OK) return st;
     }
 
-    fp8kv::DecodeParams p;
+    fp8kv::DecodeParams p{};
     p.q = static_cast<const uint16_t*>(q);
     p.q_stride_b = q_stride_b;
     p.q_stride_row = q_stride_row;
@@ -323,6 +346,14 @@ static int decode_partials(
     p.ws_o = reinterpret_cast<float*>(ws);
     p.ws_lse = reinterpret_cast<float*>(ws + s.lse_offset_bytes);
     p.ws_prefix = reinterpret_cast<int32_t*>(ws + s.prefix_offset_bytes);
+    p.k_new = static_cast<const uint16_t*>(app.k);
+    p.v_new = static_cast<const uint16_t*>(app.v);
+    p.kn_stride_b = app.k_sb;
+    p.kn_stride_row = app.k_sr;
+    p.kn_stride_head = app.k_sh;
+    p.vn_stride_b = app.v_sb;
+    p.vn_stride_row = app.v_sr;
+    p.vn_stride_head = app.v_sh;
     return launched(fp8kv::launch_decode_partitions(p, head_dim, (hipStream_t)stream),
                     "paged_decode_partials");
 }
@@ -636,6 +667,88 @@ int fp8kv_paged_decode_attn_fp8(
         batch, rows, num_q_heads, num_kv_heads, head_dim, num_ranges,
         workspace, workspace_bytes, out, out_stride_b, out_stride_row,
         out_stride_head, out_dtype, stream);
+}
+
+int fp8kv_paged_decode_append_partials(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row, int64_t q_stride_head,
+    int32_t q_dtype, const void* k_new, int64_t k_new_stride_b, int64_t k_new_stride_row,
+    int64_t k_new_stride_head, const void* v_new, int64_t v_new_stride_b,
+    int64_t v_new_stride_row, int64_t v_new_stride_head, int32_t new_dtype, uint8_t* k_cache,
+    uint8_t* v_cache, int64_t cache_stride_slot, int64_t cache_stride_head, float* k_scale,
+    float* v_scale, int64_t scale_stride_slot, int64_t scale_stride_head, int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride, const int32_t* context_lens,
+    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float softmax_scale, int32_t num_ranges, int32_t max_context,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+int fp8kv_paged_decode_append_attn_fp8(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row, int64_t q_stride_head,
+    int32_t q_dtype, const void* k_new, int64_t k_new_stride_b, int64_t k_new_stride_row,
+    int64_t k_new_stride_head, const void* v_new, int64_t v_new_stride_b,
+    int64_t v_new_stride_row, int64_t v_new_stride_head, int32_t new_dtype, uint8_t* k_cache,
+    uint8_t* v_cache, int64_t cache_stride_slot, int64_t cache_stride_head, float* k_scale,
+    float* v_scale, int64_t scale_stride_slot, int64_t scale_stride_head, int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride, const int32_t* context_lens,
+    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float softmax_scale, int32_t num_ranges, int32_t max_context,
+    void* workspace, size_t workspace_bytes, void* out, int64_t out_stride_b,
+    int64_t out_stride_row, int64_t out_stride_head, int32_t out_dtype, void* stream) {
+    // validate everything before enqueueing anything
+    int st = check_out_dtype(out_dtype);
+    if (st != FP8KV_OK) return st;
+    if (new_dtype != FP8KV_DTYPE_BF16)
+        return fail(FP8KV_E_UNSUPPORTED, "new_dtype %d: only BF16 K/V rows", new_dtype);
+    if (!out && batch > 0) return fail(FP8KV_E_NULL, "paged_decode_append: out is NULL");
+    if (out_stride_b < 0 || out_stride_row < 0 || out_stride_head < 0)
+        return fail(FP8KV_E_STRIDE, "paged_decode_append: negative out stride");
+    if (!aligned(out, out_dtype == FP8KV_DTYPE_FP32 ? 4 : 2))
+        return fail(FP8KV_E_ALIGN, "out misaligned");
+    if (checked() && batch > 0 && (st = check_device_ptr(out, "out")) != FP8KV_OK) return st;
+    st = fp8kv_paged_decode_append_partials(
+        q, q_stride_b, q_stride_row, q_stride_head, q_dtype, k_new, k_new_stride_b,
+        k_new_stride_row, k_new_stride_head, v_new, v_new_stride_b, v_new_stride_row,
+        v_new_stride_head, new_dtype, k_cache, v_cache, cache_stride_slot, cache_stride_head,
+        k_scale, v_scale, scale_stride_slot, scale_stride_head, num_slots, block_tables,
+        block_table_stride, context_lens, batch, rows, num_q_heads, num_kv_heads, head_dim,
+        block_size, softmax_scale, num_ranges, max_context, workspace, workspace_bytes, stream);
+    if (st != FP8KV_OK) return st;
+    return fp8kv_paged_decode_merge(
+        batch, rows, num_q_heads, num_kv_heads, head_dim, num_ranges,
+        workspace, workspace_bytes, out, out_stride_b, out_stride_row,
+        out_stride_head, out_dtype, stream);
+}
+
+int fp8kv_paged_decode_append_partials(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row, int64_t q_stride_head,
+    int32_t q_dtype, const void* k_new, int64_t k_new_stride_b, int64_t k_new_stride_row,
+    int64_t k_new_stride_head, const void* v_new, int64_t v_new_stride_b,
+    int64_t v_new_stride_row, int64_t v_new_stride_head, int32_t new_dtype, uint8_t* k_cache,
+    uint8_t* v_cache, int64_t cache_stride_slot, int64_t cache_stride_head, float* k_scale,
+    float* v_scale, int64_t scale_stride_slot, int64_t scale_stride_head, int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride, const int32_t* context_lens,
+    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float softmax_scale, int32_t num_ranges, int32_t max_context,
+    void* workspace, size_t workspace_bytes, void* stream) {
+    if (new_dtype != FP8KV_DTYPE_BF16)
+        return fail(FP8KV_E_UNSUPPORTED, "new_dtype %d: only BF16 K/V rows", new_dtype);
+    if (batch > 0 && (!k_new || !v_new))
+        return fail(FP8KV_E_NULL, "paged_decode_append: k_new or v_new is NULL");
+    AppendRows app;
+    app.k = batch > 0 ? k_new : nullptr;
+    app.k_sb = k_new_stride_b;
+    app.k_sr = k_new_stride_row;
+    app.k_sh = k_new_stride_head;
+    app.v = batch > 0 ? v_new : nullptr;
+    app.v_sb = v_new_stride_b;
+    app.v_sr = v_new_stride_row;
+    app.v_sh = v_new_stride_head;
+    return decode_partials(q, q_stride_b, q_stride_row, q_stride_head, q_dtype, k_cache, v_cache,
+                           cache_stride_slot, cache_stride_head, k_scale, v_scale,
+                           scale_stride_slot, scale_stride_head, num_slots, block_tables,
+                           block_table_stride, nullptr, 0, context_lens, batch, rows,
+                           num_q_heads, num_kv_heads, head_dim, block_size, softmax_scale,
+                           num_ranges, max_context, workspace, workspace_bytes,
+                           fp8kv::kCodesE4M3Scaled, stream, app);
 }
 
 int fp8kv_paged_decode_attn_fp8_noalloc(

@@ -107,6 +107,28 @@ __device__ __forceinline__ void row_quotients(const float (&x)[N], float scale, 
     }
 }
 
+// The E4M3 row quantizer of one (token, KV head) row held by a 16-lane DPP
+// row (EPL elements per lane, each exactly a bf16 value): amax over the
+// row, scale = fp32(amax / 448) by IEEE division, each code the E4M3 RNE of
+// the correctly rounded quotient x / scale (x itself when the scale is 0),
+// 4 codes per packed word. Every kernel that writes cache rows uses this.
+template <int EPL>
+__device__ __forceinline__ void quantize_row_e4m3(const float (&x)[EPL], float& scale,
+                                                  uint32_t (&packed)[EPL / 4]) {
+#pragma clang fp contract(off)
+    uint32_t amax_bits = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) amax_bits = max(amax_bits, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+    amax_bits = row16_max_u32(amax_bits);
+    const float amax = __uint_as_float(amax_bits);
+    scale = amax / kE4M3Max;                  // IEEE binary32 division
+    float qv[EPL];
+    row_quotients(x, scale, qv);
+#pragma unroll
+    for (int i = 0; i < EPL / 4; ++i)
+        packed[i] = e4m3x4_encode(qv[4 * i], qv[4 * i + 1], qv[4 * i + 2], qv[4 * i + 3]);
+}
+
 // Two E4M3 codes (16-bit half HI of w) -> two bf16, exact.
 template <bool HI>
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {

@@ -61,6 +61,14 @@ struct DecodeParams {
     float* ws_o;               // [(batch + R - 1) * Hkv * M, head_dim]
     float* ws_lse;             // [(batch + R - 1) * Hkv * M]
     int32_t* ws_prefix;        // [batch + 1]: tiles before each request, then U
+    // append (fp8kv_paged_decode_append_attn_fp8): the new K and V rows of
+    // each request's last `rows` positions (bf16 [B, rows, Hkv, D] at these
+    // element strides), quantized into the cache before they are read; null
+    // for the other calls
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    int64_t kn_stride_b, kn_stride_row, kn_stride_head;
+    int64_t vn_stride_b, vn_stride_row, vn_stride_head;
 };
 
 struct MergeParams {

@@ -58,21 +58,18 @@ __device__ __forceinline__ void encode_key(const float (&x)[8], int li, bool sto
         if (store) *reinterpret_cast<uint4*>(code_row + li * 16) = make_uint4(w[0], w[1], w[2], w[3]);
         return;
     }
-    uint32_t amax_bits = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax_bits = max(amax_bits, __float_as_uint(x[i]) & 0x7FFFFFFFu);
     if (FMT == kKeysE4M3) {
-        const float amax = __uint_as_float(row16_max_u32(amax_bits));
-        const float scale = amax / kE4M3Max;         // IEEE binary32 division
-        float qv[8];
-        row_quotients(x, scale, qv);
-        const uint32_t lo = e4m3x4_encode(qv[0], qv[1], qv[2], qv[3]);
-        const uint32_t hi = e4m3x4_encode(qv[4], qv[5], qv[6], qv[7]);
+        float scale;
+        uint32_t packed[2];
+        quantize_row_e4m3<8>(x, scale, packed);      // the KV row quantizer
         if (store) {
-            *reinterpret_cast<uint2*>(code_row + li * 8) = make_uint2(lo, hi);
+            *reinterpret_cast<uint2*>(code_row + li * 8) = make_uint2(packed[0], packed[1]);
             if (li == 0) *static_cast<float*>(scale_row) = scale;
         }
     } else {
+        uint32_t amax_bits = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax_bits = max(amax_bits, __float_as_uint(x[i]) & 0x7FFFFFFFu);
         amax_bits = max(amax_bits, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax_bits, 0xB1, 0xF, 0xF, false));
         amax_bits = max(amax_bits, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax_bits, 0x4E, 0xF, 0xF, false));
         const float amax = __uint_as_float(amax_bits);

@@ -61,10 +61,88 @@ __device__ __forceinline__ int request_tiles(const DecodeParams& p, int b) {
     return (len + 31) >> 5;
 }
 
+// Append: the new K and V rows of request b at positions [n0, n1) (verify
+// row r = position - (len - rows)) for KV head h, quantized by the cache's
+// row quantizer and stored at the slots the page walk reads (block ids
+// clamped to the pool). Two positions per pass: DPP row g holds the K
+// (g even) or V (g odd) row of position pos0 + g / 2. A pass is split into
+// its loads (append_load) and its quantization and stores (append_store),
+// so a wave can issue a tile's loads in between.
+template <int D>
+struct NewRows {
+    uint32_t w[D / 32];         // the lane's D/16 bf16 of its DPP row's K or V row
+    int64_t slot;
+    bool live;
+};
+
+template <int D, bool BSP2>
+__device__ __forceinline__ void append_load(const DecodeParams& p, const int32_t* bt, int b,
+                                            int len, int pos0, int n1, int h, int lane,
+                                            NewRows<D>& nr) {
+    constexpr int EPL = D / 16;                 // elements per lane
+    const int li = lane & 15, sub = lane >> 4;
+    const bool is_v = sub & 1;
+    nr.live = pos0 + (sub >> 1) < n1;
+    const int pos = nr.live ? pos0 + (sub >> 1) : n1 - 1;
+    const uint16_t* row =
+        is_v ? p.v_new + (int64_t)b * p.vn_stride_b + (int64_t)h * p.vn_stride_head +
+                   (int64_t)(pos - (len - p.rows)) * p.vn_stride_row
+             : p.k_new + (int64_t)b * p.kn_stride_b + (int64_t)h * p.kn_stride_head +
+                   (int64_t)(pos - (len - p.rows)) * p.kn_stride_row;
+    if constexpr (EPL == 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(row + li * EPL);
+        nr.w[0] = v.x; nr.w[1] = v.y; nr.w[2] = v.z; nr.w[3] = v.w;
+    } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(row + li * EPL);
+        nr.w[0] = v.x; nr.w[1] = v.y;
+    }
+    const int bi = BSP2 ? (pos >> p.block_shift) : pos / p.block_size;
+    const int bo = pos - bi * p.block_size;
+    const int blk = min(max(bt[bi], 0), p.num_blocks - 1);
+    nr.slot = (int64_t)blk * p.block_size + bo;
+}
+
+template <int D>
+__device__ __forceinline__ void append_store(const DecodeParams& p, int h, int lane,
+                                             const NewRows<D>& nr) {
+    constexpr int EPL = D / 16;
+    const int li = lane & 15;
+    const bool is_v = (lane >> 4) & 1;
+    float x[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL / 2; ++i) {
+        x[2 * i] = bf16_lo(nr.w[i]);
+        x[2 * i + 1] = bf16_hi(nr.w[i]);
+    }
+    float scale;
+    uint32_t packed[EPL / 4];
+    quantize_row_e4m3<EPL>(x, scale, packed);
+    if (nr.live) {
+        uint8_t* dst = const_cast<uint8_t*>(is_v ? p.v_cache : p.k_cache) +
+                       (int64_t)h * p.cache_stride_head + nr.slot * p.cache_stride_slot + li * EPL;
+        if constexpr (EPL == 8)
+            *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
+        else
+            *reinterpret_cast<uint32_t*>(dst) = packed[0];
+        if (li == 0)
+            const_cast<float*>(is_v ? p.v_scale : p.k_scale)[(int64_t)h * p.scale_stride_head +
+                                                            nr.slot * p.scale_stride_slot] = scale;
+    }
+}
+
+// The wave's own appended rows are complete before its next loads are
+// issued: the stores have reached the XCD's L2 (the CU's vector L1 is kept
+// coherent with the CU's own stores), so the tile loads read the new codes.
+__device__ __forceinline__ void appended_rows_visible() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
 // One piece: tiles [ja, jb) of request b for KV head h, reduced to a partial
 // (normalized output and log2 log-sum-exp of each of the M rows) at piece
-// id `pid`.
-template <int D, bool BSP2, bool SP, int CODES>
+// id `pid`. With APPEND, the request's new rows that fall in the piece are
+// first written to the cache (append_load, append_store).
+template <int D, bool BSP2, bool SP, int CODES, bool APPEND>
 __device__ __forceinline__ void decode_piece(const DecodeParams& p, int b, int len, int ja, int jb,
                                              int h, int pid, int lane) {
     constexpr int KSTEPS = D / 32;
@@ -94,6 +172,29 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int b, int l
     w.last_base = (p1 - 1) & ~15;
     w.nr_codes_full = 15 * (int)p.cache_stride_slot + D;
     w.nr_scales_full = 4 * (15 * (int)p.scale_stride_slot + 1);
+
+    // new rows in the piece, positions [n0, n1): stored, and made visible
+    // before the loads of the first tile that holds one (tile fence_at of
+    // the piece). When that is not the first tile, the first pass's loads are
+    // issued now and its stores after the first tile's loads, so the wave
+    // does not wait for them before it starts streaming.
+    int fence_at = -1, n0 = 0, n1 = 0;
+    NewRows<D> nr;
+    if constexpr (APPEND) {
+        n0 = max(max(len - p.rows, 0), p0);
+        n1 = p1;
+        if (n0 < n1) {
+            fence_at = (n0 >> 5) - ja;
+            append_load<D, BSP2>(p, w.bt, b, len, n0, n1, h, lane, nr);
+            if (fence_at == 0) {
+                append_store<D>(p, h, lane, nr);
+                for (int pos0 = n0 + 2; pos0 < n1; pos0 += 2) {
+                    append_load<D, BSP2>(p, w.bt, b, len, pos0, n1, h, lane, nr);
+                    append_store<D>(p, h, lane, nr);
+                }
+            }
+        }
+    }
 
     // block-table window of tiles 0..31, and the next one when the piece is longer
     int kw = 0;
@@ -167,17 +268,27 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int b, int l
     int ti = 0;
     entries(0, blk, valid);
     Tile::template address<BSP2, SP>(p, w, 0, blk, valid, ta_a);
+    if (APPEND && fence_at == 0) appended_rows_visible();
     Tile::issue(ta_a, lo, ra);
+    if (APPEND && fence_at > 0) {
+        append_store<D>(p, h, lane, nr);
+        for (int pos0 = n0 + 2; pos0 < n1; pos0 += 2) {
+            append_load<D, BSP2>(p, w.bt, b, len, pos0, n1, h, lane, nr);
+            append_store<D>(p, h, lane, nr);
+        }
+    }
     while (ti < ntiles) {
         Tile::qk(ra, qv, sc);
         entries(ti + 1, blk, valid);
         Tile::template address<BSP2, SP>(p, w, ti + 1, blk, valid, ta_b);
+        if (APPEND && ti + 1 == fence_at) appended_rows_visible();
         Tile::issue(ta_b, lo, rb);
         Tile::template rest<SP>(p, ta_a, ra, sc, p1, lim, lg, st);
         if (++ti >= ntiles) break;
         Tile::qk(rb, qv, sc);
         entries(ti + 1, blk, valid);
         Tile::template address<BSP2, SP>(p, w, ti + 1, blk, valid, ta_a);
+        if (APPEND && ti + 1 == fence_at) appended_rows_visible();
         Tile::issue(ta_a, lo, ra);
         Tile::template rest<SP>(p, ta_b, rb, sc, p1, lim, lg, st);
         ++ti;
@@ -216,7 +327,7 @@ __device__ __forceinline__ int logical_workgroup(int bid, int wgs_per_range) {
     return (k / m) * 8 * m + xcd * m + (k % m);
 }
 
-template <int D, bool BSP2, bool SP, int CODES>
+template <int D, bool BSP2, bool SP, int CODES, bool APPEND>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     const int lane = threadIdx.x & 63;
     // wave index, provably uniform so the page walk and the buffer
@@ -267,7 +378,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         if (n > 0) {
             const int ja = u - pre;
             const int jb = min(n, u1 - pre);
-            decode_piece<D, BSP2, SP, CODES>(p, b, len, ja, jb, h, b + r, lane);
+            decode_piece<D, BSP2, SP, CODES, APPEND>(p, b, len, ja, jb, h, b + r, lane);
             u = pre + jb;
         }
         pre += n;
@@ -475,21 +586,21 @@ __global__ __launch_bounds__(256) void decode_merge_rows_kernel(MergeParams p) {
     }
 }
 
-template <int D, bool BSP2, bool SP, int CODES>
+template <int D, bool BSP2, bool SP, int CODES, bool APPEND>
 hipError_t launch_split(const DecodeParams& p, hipStream_t stream) {
     const int64_t workers = (int64_t)p.num_ranges * p.num_kv_heads;
     const int64_t quantum = p.wgs_per_range > 1 ? 8 * p.wgs_per_range : 1;
     int64_t wgs = (workers + 3) / 4;
     wgs = (wgs + quantum - 1) / quantum * quantum;
     if (wgs > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_split_kernel<D, BSP2, SP, CODES>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, BSP2, SP, CODES, APPEND>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int D, bool SP, int CODES = kCodesE4M3Scaled>
+template <int D, bool SP, int CODES = kCodesE4M3Scaled, bool APPEND = false>
 hipError_t launch_split_bs(const DecodeParams& p, hipStream_t stream) {
-    return p.block_shift >= 0 ? launch_split<D, true, SP, CODES>(p, stream)
-                              : launch_split<D, false, SP, CODES>(p, stream);
+    return p.block_shift >= 0 ? launch_split<D, true, SP, CODES, APPEND>(p, stream)
+                              : launch_split<D, false, SP, CODES, APPEND>(p, stream);
 }
 }  // namespace
 
@@ -526,6 +637,12 @@ int decode_wave_slots(int device) {
 
 hipError_t launch_decode_partitions(const DecodeParams& p, int head_dim, hipStream_t stream) {
     const bool sp = p.block_valid != nullptr;
+    if (p.k_new != nullptr) {
+        // append: the dense walk over a scaled E4M3 cache only
+        if (sp || p.codes != kCodesE4M3Scaled) return hipErrorInvalidValue;
+        return head_dim == 128 ? launch_split_bs<128, false, kCodesE4M3Scaled, true>(p, stream)
+                               : launch_split_bs<64, false, kCodesE4M3Scaled, true>(p, stream);
+    }
     if (p.codes != kCodesE4M3Scaled) {
         // unscaled caches: the dense walk only
         if (sp) return hipErrorInvalidValue;

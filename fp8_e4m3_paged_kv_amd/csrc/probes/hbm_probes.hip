@@ -1,0 +1,141 @@
+// hbm_probes.hip -- measurement kernels (libfp8kv_probes.so, used by the
+// benchmark only, not part of the cache library): plain HBM streams that
+// bound what the cache kernels can reach on this GPU, and an empty kernel
+// for the launch floor of a replayed HIP graph.
+//
+//   kind 0  read:   sum of `bytes` (16-byte non-temporal loads)
+//   kind 1  copy:   dst = a                      (1:1 read:write)
+//   kind 2  2:1:    dst = a ^ b, a and b `bytes` each, dst `bytes`
+//   kind 3  write:  dst = pattern                (write only)
+//   kind 4  empty:  a kernel that does nothing
+// Every thread moves 4 x 16 bytes per grid step, strided by the grid, so
+// each wave's loads and stores are 1 KiB contiguous; the grid is 8
+// workgroups of 256 threads per CU (or fewer when the buffer is small).
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+__global__ __launch_bounds__(kThreads) void probe_read(const u32x4* a, size_t n, uint32_t* sink) {
+    const size_t stride = (size_t)gridDim.x * kThreads;
+    u32x4 acc = {0, 0, 0, 0};
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride * kUnroll) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const size_t j = i + u * stride;
+            v[u] = j < n ? __builtin_nontemporal_load(a + j) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+    }
+    // never true for the buffers the bench passes; keeps the loads alive
+    if ((acc.x & acc.y & acc.z & acc.w) == 0xFFFFFFFFu) sink[0] = acc.x;
+}
+
+__global__ __launch_bounds__(kThreads) void probe_copy(const u32x4* a, u32x4* d, size_t n) {
+    const size_t stride = (size_t)gridDim.x * kThreads;
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride * kUnroll) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const size_t j = i + u * stride;
+            if (j < n) v[u] = __builtin_nontemporal_load(a + j);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const size_t j = i + u * stride;
+            if (j < n) __builtin_nontemporal_store(v[u], d + j);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void probe_read2_write1(const u32x4* a, const u32x4* b,
+                                                               u32x4* d, size_t n) {
+    const size_t stride = (size_t)gridDim.x * kThreads;
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride * kUnroll) {
+        u32x4 v[kUnroll], w[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const size_t j = i + u * stride;
+            if (j < n) {
+                v[u] = __builtin_nontemporal_load(a + j);
+                w[u] = __builtin_nontemporal_load(b + j);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const size_t j = i + u * stride;
+            if (j < n) __builtin_nontemporal_store(v[u] ^ w[u], d + j);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void probe_write(u32x4* d, size_t n) {
+    const size_t stride = (size_t)gridDim.x * kThreads;
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride * kUnroll) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const size_t j = i + u * stride;
+            if (j < n) __builtin_nontemporal_store(u32x4{(uint32_t)j, 1u, 2u, 3u}, d + j);
+        }
+    }
+}
+
+__global__ void probe_empty() {}
+
+}  // namespace
+
+extern "C" {
+
+// Enqueue one probe kernel on `stream`. bytes: the size of each buffer (a
+// multiple of 16). Returns 0, or -1 for a bad argument, -2 for a launch
+// error.
+int fp8kv_probe(int kind, const void* a, const void* b, void* dst, size_t bytes, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (kind == 4) {
+        hipLaunchKernelGGL(probe_empty, dim3(1), dim3(64), 0, s);
+        return hipGetLastError() == hipSuccess ? 0 : -2;
+    }
+    if (bytes % 16 != 0 || bytes == 0) return -1;
+    const size_t n = bytes / 16;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return -2;
+    const size_t per_block = (size_t)kThreads * kUnroll;
+    size_t blocks = (n + per_block - 1) / per_block;
+    if (blocks > (size_t)cus * 8) blocks = (size_t)cus * 8;
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    const u32x4* va = static_cast<const u32x4*>(a);
+    switch (kind) {
+        case 0:
+            if (!a || !dst) return -1;
+            hipLaunchKernelGGL(probe_read, grid, block, 0, s, va, n, static_cast<uint32_t*>(dst));
+            break;
+        case 1:
+            if (!a || !dst) return -1;
+            hipLaunchKernelGGL(probe_copy, grid, block, 0, s, va, static_cast<u32x4*>(dst), n);
+            break;
+        case 2:
+            if (!a || !b || !dst) return -1;
+            hipLaunchKernelGGL(probe_read2_write1, grid, block, 0, s, va,
+                               static_cast<const u32x4*>(b), static_cast<u32x4*>(dst), n);
+            break;
+        case 3:
+            if (!dst) return -1;
+            hipLaunchKernelGGL(probe_write, grid, block, 0, s, static_cast<u32x4*>(dst), n);
+            break;
+        default:
+            return -1;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+}  // extern "C"

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FP8KV_ABI_VERSION 10
+#define FP8KV_ABI_VERSION 11
 
 typedef enum fp8kv_status {
     FP8KV_OK = 0,
@@ -220,6 +220,78 @@ int fp8kv_paged_decode_attn_fp8(
     void* out, int64_t out_stride_b, int64_t out_stride_row,
     int64_t out_stride_head, int32_t out_dtype,
     void* stream);
+
+/*
+ * fp8kv_paged_decode_append_attn_fp8 -- one decode step: the store of each
+ * request's new tokens and the attention over the cache that includes them,
+ * in the decode's two launches ("feat(kvcache): store the KV cache as fp8
+ * e4m3 codes", FreeToken #354, description: the store is one launch under
+ * graph capture, its slots known on the device; ATOM #2655, description,
+ * K/V bullet: the row quantizer).
+ *
+ * The last `rows` positions of request b (positions L - rows .. L - 1,
+ * L = min(context_lens[b], max_context); those below 0 are skipped) are
+ * its new tokens, already counted in context_lens. Their K and V rows,
+ *   k_new[b*k_new_stride_b + r*k_new_stride_row + h*k_new_stride_head + d]
+ *   (row r = position - (L - rows), d < head_dim; v_new likewise at its own
+ *   strides), are quantized exactly as fp8kv_kv_quant_scatter quantizes
+ *   them and stored at the slot the page walk reads for that position
+ *   (block_tables[b][pos / block_size], clamped to the pool, times
+ *   block_size plus pos % block_size); then the decode attention of
+ *   fp8kv_paged_decode_attn_fp8 runs over the cache. The result equals
+ *   fp8kv_kv_quant_scatter with those slots followed by
+ *   fp8kv_paged_decode_attn_fp8 with the same num_ranges, bit for bit (codes,
+ *   scales and output). The wave that reads a new token's tile writes it,
+ *   and waits for its own stores before reading that tile.
+ * k_new, v_new (device) new_dtype FP8KV_DTYPE_BF16; rows on head_dim/8-byte
+ *             boundaries (pointers and strides multiples of head_dim/16).
+ * k_cache, v_cache, k_scale, v_scale (device) written as well as read.
+ * Everything else as fp8kv_paged_decode_attn_fp8 (same workspace).
+ * Errors: as fp8kv_paged_decode_attn_fp8; E_NULL for k_new / v_new,
+ *         E_UNSUPPORTED for new_dtype.
+ */
+int fp8kv_paged_decode_append_attn_fp8(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype,
+    const void* k_new, int64_t k_new_stride_b, int64_t k_new_stride_row,
+    int64_t k_new_stride_head,
+    const void* v_new, int64_t v_new_stride_b, int64_t v_new_stride_row,
+    int64_t v_new_stride_head, int32_t new_dtype,
+    uint8_t* k_cache, uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head,
+    float* k_scale, float* v_scale,
+    int64_t scale_stride_slot, int64_t scale_stride_head,
+    int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens,
+    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, float softmax_scale,
+    int32_t num_ranges, int32_t max_context,
+    void* workspace, size_t workspace_bytes,
+    void* out, int64_t out_stride_b, int64_t out_stride_row,
+    int64_t out_stride_head, int32_t out_dtype,
+    void* stream);
+
+/* Split phase of fp8kv_paged_decode_append_attn_fp8 (the new rows' store
+ * and the partials); merge with fp8kv_paged_decode_merge. */
+int fp8kv_paged_decode_append_partials(
+    const void* q, int64_t q_stride_b, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t q_dtype,
+    const void* k_new, int64_t k_new_stride_b, int64_t k_new_stride_row,
+    int64_t k_new_stride_head,
+    const void* v_new, int64_t v_new_stride_b, int64_t v_new_stride_row,
+    int64_t v_new_stride_head, int32_t new_dtype,
+    uint8_t* k_cache, uint8_t* v_cache,
+    int64_t cache_stride_slot, int64_t cache_stride_head,
+    float* k_scale, float* v_scale,
+    int64_t scale_stride_slot, int64_t scale_stride_head,
+    int64_t num_slots,
+    const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens,
+    int32_t batch, int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, float softmax_scale,
+    int32_t num_ranges, int32_t max_context,
+    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * fp8kv_paged_decode_attn_fp8_noalloc -- fp8kv_paged_decode_attn_fp8 for
