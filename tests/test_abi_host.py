@@ -492,3 +492,47 @@ def test_noalloc_scratch_limit_covers_the_bench_workloads(L):
     assert limit == 16 << 20
     assert L.fp8kv_paged_decode_workspace_bytes(64, 1, 32, 8, 128, 128) <= limit
     assert L.fp8kv_paged_decode_workspace_bytes(4, 4, 16, 4, 128, 256) <= limit
+
+
+def append(L, fn="fp8kv_paged_decode_append_attn_fp8", **kw):
+    """The append calls with the arguments of dec() plus the new rows."""
+    a = dict(q=A, qsb=4096, qsr=4096, qsh=128, qdt=BF16, kn=A, knb=1024, knr=1024,
+             knh=128, vn=A, vnb=1024, vnr=1024, vnh=128, ndt=BF16, kc=A, vc=A,
+             css=1024, csh=128, ks=A, vs=A, sss=1, ssh=1 << 20, S=1 << 20,
+             bt=A, bts=2048, cl=A, B=64, R=1, Hq=32, H=8, D=128, bs=16,
+             scale=0.088, P=384, maxc=32768, ws=A, wsb=1 << 34, out=A,
+             osb=4096, osr=4096, osh=128, odt=BF16)
+    a.update(kw)
+    args = [a["q"], a["qsb"], a["qsr"], a["qsh"], a["qdt"], a["kn"], a["knb"], a["knr"],
+            a["knh"], a["vn"], a["vnb"], a["vnr"], a["vnh"], a["ndt"], a["kc"], a["vc"],
+            a["css"], a["csh"], a["ks"], a["vs"], a["sss"], a["ssh"], a["S"], a["bt"],
+            a["bts"], a["cl"], a["B"], a["R"], a["Hq"], a["H"], a["D"], a["bs"],
+            ctypes.c_float(a["scale"]), a["P"], a["maxc"], a["ws"], a["wsb"]]
+    if fn == "fp8kv_paged_decode_append_partials":
+        return getattr(L, fn)(*args, None)
+    return getattr(L, fn)(*args, a["out"], a["osb"], a["osr"], a["osh"], a["odt"], None)
+
+
+@pytest.mark.parametrize("fn", ["fp8kv_paged_decode_append_attn_fp8",
+                                "fp8kv_paged_decode_append_partials"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(ndt=FP16), E_UNSUPPORTED),
+    (dict(ndt=FP32), E_UNSUPPORTED),
+    (dict(kn=0), E_NULL),
+    (dict(vn=0), E_NULL),
+    (dict(knr=-1024), E_STRIDE),
+    (dict(vnh=-128), E_STRIDE),
+    (dict(kn=A + 8), E_ALIGN),           # rows on 16-byte boundaries at head_dim 128
+    (dict(vnb=1028), E_ALIGN),
+    (dict(D=64, knh=66), E_ALIGN),       # 8-byte boundaries at head_dim 64 (stride in bf16)
+    (dict(D=96), E_UNSUPPORTED),
+    (dict(R=5), E_UNSUPPORTED),
+    (dict(ws=0), E_WORKSPACE),
+    (dict(B=0, q=0, kn=0, vn=0, kc=0, vc=0, ks=0, vs=0, bt=0, cl=0, ws=0, out=0), OK),
+])
+def test_append_refusals(L, fn, kw, status):
+    """The append calls refuse bad new rows (dtype, NULL, strides,
+    alignment) and everything the decode refuses, before enqueueing."""
+    assert append(L, fn, **kw) == status
+    if status != OK:
+        assert L.fp8kv_last_error().decode()
