@@ -8,9 +8,12 @@
 //   kind 2  2:1:    dst = a ^ b, a and b `bytes` each, dst `bytes`
 //   kind 3  write:  dst = pattern                (write only)
 //   kind 4  empty:  a kernel that does nothing
-// Every thread moves 4 x 16 bytes per grid step, strided by the grid, so
-// each wave's loads and stores are 1 KiB contiguous; the grid is 8
-// workgroups of 256 threads per CU (or fewer when the buffer is small).
+// Every thread moves 8 x 16 bytes per grid step, strided by the grid, so
+// each wave's loads and stores are 1 KiB contiguous; the grid is 2
+// workgroups of 256 threads per CU, two waves per SIMD (or fewer when the
+// buffer is small). Measured over 2 GiB on MI355X, this shape reads at 6.58
+// TB/s where 4 x 16 bytes at 8 workgroups per CU read at 5.78 (and the
+// 2:1 stream 5.09 vs 4.62 TB/s).
 #include <hip/hip_runtime.h>
 
 #include <stddef.h>
@@ -20,7 +23,8 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kBlocksPerCU = 2;
+constexpr int kUnroll = 8;
 
 __global__ __launch_bounds__(kThreads) void probe_read(const u32x4* a, size_t n, uint32_t* sink) {
     const size_t stride = (size_t)gridDim.x * kThreads;
@@ -111,7 +115,7 @@ int fp8kv_probe(int kind, const void* a, const void* b, void* dst, size_t bytes,
         return -2;
     const size_t per_block = (size_t)kThreads * kUnroll;
     size_t blocks = (n + per_block - 1) / per_block;
-    if (blocks > (size_t)cus * 8) blocks = (size_t)cus * 8;
+    if (blocks > (size_t)cus * kBlocksPerCU) blocks = (size_t)cus * kBlocksPerCU;
     const dim3 grid((unsigned)blocks), block(kThreads);
     const u32x4* va = static_cast<const u32x4*>(a);
     switch (kind) {
