@@ -688,9 +688,9 @@ def probe(L, stream, kind, a=None, b=None, d=None, nbytes=0):
 
 def hbm_ceilings(torch, dev, stream, gib=2, reps=10):
     """What plain streaming kernels reach on this GPU (the probe library's
-    16-byte non-temporal streams over 2 GiB buffers: read, copy, 2:1
-    read:write, write), and what the library's own copy and sum kernels
-    reach, for reference."""
+    16-byte streams over 2 GiB buffers, non-temporal loads and ordinary
+    stores: read, copy, 2:1 read:write, write), and what the library's own
+    copy and sum kernels reach, for reference."""
     log("HBM ceilings (probe streams, library copy and read kernels)...")
     L = probes_lib()
     n = gib << 30

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     const int32_t* bt = p.block_tables + (int64_t)b * p.block_table_stride;
     const int32_t* bv = SP ? p.block_valid + (int64_t)b * p.block_valid_stride : nullptr;
     intx4 kr = {0, 0, 0, 0}, vr = {0, 0, 0, 0};
-    float sr = 0.f;
+    float ksr = 0.f, vsr = 0.f;
     int ld_nv = 16;
     auto load_tile = [&](int ti) {
         // the wave's half: keys stok .. stok + nvalid - 1, all in one block
@@ -159,15 +159,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
         const int64_t soff = slot * p.scale_stride_slot;
         kr = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(kbase + coff, nrc), ld_code, 0, 0);
         vr = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(vbase + coff, nrc), ld_code, 0, 0);
-        const float ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                       make_rsrc(ksbase + soff, nrs), ld_scale, 0, 0));
-        const float vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                       make_rsrc(vsbase + soff, nrs), ld_scale, 0, 0));
-        sr = ld_chunk == 0 ? ks * p.score_scale_log2 : vs;
+        // every lane loads both scales; they are combined when the tile is
+        // stored (a multiply here would make the wave wait for all of its
+        // loads in flight, the K/V codes included)
+        ksr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                            make_rsrc(ksbase + soff, nrs), ld_scale, 0, 0));
+        vsr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                            make_rsrc(vsbase + soff, nrs), ld_scale, 0, 0));
     };
     auto store_tile = [&](int buf) {
         *reinterpret_cast<intx4*>(&lds_k[buf][lds_code]) = kr;
         *reinterpret_cast<intx4*>(&lds_v[buf][lds_code]) = vr;
+        const float sr = ld_chunk == 0 ? ksr * p.score_scale_log2 : vsr;
         if (ld_chunk < 2) lds_s[buf][ld_chunk][ld_tok] = sr;
         if (SP && lane == 0 && ((wave * TPL) & 15) == 0) lds_nv[buf][ld_half] = ld_nv;
     };

@@ -8,12 +8,14 @@
 //   kind 2  2:1:    dst = a ^ b, a and b `bytes` each, dst `bytes`
 //   kind 3  write:  dst = pattern                (write only)
 //   kind 4  empty:  a kernel that does nothing
-// Every thread moves 8 x 16 bytes per grid step, strided by the grid, so
-// each wave's loads and stores are 1 KiB contiguous; the grid is 2
-// workgroups of 256 threads per CU, two waves per SIMD (or fewer when the
-// buffer is small). Measured over 2 GiB on MI355X, this shape reads at 6.58
-// TB/s where 4 x 16 bytes at 8 workgroups per CU read at 5.78 (and the
-// 2:1 stream 5.09 vs 4.62 TB/s).
+// Every thread moves 2 x 16 bytes: loads carry the non-temporal hint, stores
+// are ordinary; the grid covers the buffer once (no grid-stride loop), so
+// each wave's loads and stores are 1 KiB contiguous. Of the shapes measured
+// over 2 GiB on MI355X (2 to 16 x 16 bytes per thread; grids of 1, 2 or 4
+// workgroups per CU looping, or one pass; non-temporal or ordinary
+// stores), this one is the fastest for every stream: read 6.96, copy 5.76,
+// 2:1 5.71, write 6.58 TB/s (8 x 16 bytes at 2 workgroups per CU with
+// non-temporal stores: 6.58, 4.69, 5.11, 5.24).
 #include <hip/hip_runtime.h>
 
 #include <stddef.h>
@@ -23,8 +25,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
-constexpr int kBlocksPerCU = 2;
-constexpr int kUnroll = 8;
+constexpr int kUnroll = 2;
 
 __global__ __launch_bounds__(kThreads) void probe_read(const u32x4* a, size_t n, uint32_t* sink) {
     const size_t stride = (size_t)gridDim.x * kThreads;
@@ -55,7 +56,7 @@ __global__ __launch_bounds__(kThreads) void probe_copy(const u32x4* a, u32x4* d,
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const size_t j = i + u * stride;
-            if (j < n) __builtin_nontemporal_store(v[u], d + j);
+            if (j < n) d[j] = v[u];
         }
     }
 }
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void probe_read2_write1(const u32x4* a, c
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const size_t j = i + u * stride;
-            if (j < n) __builtin_nontemporal_store(v[u] ^ w[u], d + j);
+            if (j < n) d[j] = v[u] ^ w[u];
         }
     }
 }
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void probe_write(u32x4* d, size_t n) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const size_t j = i + u * stride;
-            if (j < n) __builtin_nontemporal_store(u32x4{(uint32_t)j, 1u, 2u, 3u}, d + j);
+            if (j < n) d[j] = u32x4{(uint32_t)j, 1u, 2u, 3u};
         }
     }
 }
@@ -109,13 +110,9 @@ int fp8kv_probe(int kind, const void* a, const void* b, void* dst, size_t bytes,
     }
     if (bytes % 16 != 0 || bytes == 0) return -1;
     const size_t n = bytes / 16;
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return -2;
     const size_t per_block = (size_t)kThreads * kUnroll;
-    size_t blocks = (n + per_block - 1) / per_block;
-    if (blocks > (size_t)cus * kBlocksPerCU) blocks = (size_t)cus * kBlocksPerCU;
+    const size_t blocks = (n + per_block - 1) / per_block;
+    if (blocks > 0x7FFFFFFFu) return -1;
     const dim3 grid((unsigned)blocks), block(kThreads);
     const u32x4* va = static_cast<const u32x4*>(a);
     switch (kind) {
