@@ -34,6 +34,9 @@
 // with a partial half takes the masked path, where a position past its
 // block's count is no key and adds exactly nothing (a row may see no key
 // in a tile, or at all: its output is then 0).
+// Occupancy: the dense kernel fits 168 VGPRs, 3 waves per SIMD (each wave's
+// tile chain is latency-bound, so a third wave adds throughput); the
+// selected-block kernel needs more registers and runs 2 waves per SIMD.
 // The prefill kernel keeps a row's running maximum until a tile's scores
 // exceed it by more than kLazyMax (log2 units), so p = exp2(s - m) stays
 // below 2^kLazyMax; its P' range factor is 2^(141 - kLazyMax - e), which
@@ -50,7 +53,7 @@ namespace {
 constexpr int kLazyMax = 8;
 
 template <int D, bool BSP2, int NT, bool SP>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(256, SP ? 2 : 3) void prefill_kernel(PrefillParams p) {
     constexpr int KSTEPS = D / 32;
     constexpr int DL = D / 16;
     constexpr int KB = D / 4;
@@ -194,14 +197,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
         }
         floatx4 sc[NT][2];
         Tile::template qk_tiles<NT>(R, qv, sc);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint8_t* src = &lds_v[buf][(16 * (e >> 2) + 4 * lg + (e & 3)) * ROW + li * DL];
-            if constexpr (DL == 8)
-                R.vraw[e] = *reinterpret_cast<const uint2*>(src);
-            else
-                R.vraw[e] = *reinterpret_cast<const uint32_t*>(src);
-        }
         // scales of the lane's score tokens 16 s + 4 lg + r
         float sk[2][4], sv[2][4];
 #pragma unroll
@@ -292,6 +287,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
             }
             pb[j] = __builtin_bit_cast(f16x8, pw);
             sts[j] = &st[j];
+        }
+        // V operands read only now: not held in registers across the softmax
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint8_t* src = &lds_v[buf][(16 * (e >> 2) + 4 * lg + (e & 3)) * ROW + li * DL];
+            if constexpr (DL == 8)
+                R.vraw[e] = *reinterpret_cast<const uint2*>(src);
+            else
+                R.vraw[e] = *reinterpret_cast<const uint32_t*>(src);
         }
         Tile::template pv_tiles<NT>(R, pb, sts);
         if (loader && ti + 1 < ntiles) store_tile(buf ^ 1);
