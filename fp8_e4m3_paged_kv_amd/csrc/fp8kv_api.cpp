@@ -1217,6 +1217,11 @@ int fp8kv_index_score_mxfp4(
     p.key_chunk = chunk;
     p.chunks = (int32_t)chunks;
     p.row_groups = row_groups;
+    // rows whose pitch is a multiple of 64 KiB write their scores to the
+    // same HBM channels at the same column; at 4 heads or fewer (one score
+    // per 4 or more MFMA rows) those stores set the pace, so the waves of a
+    // workgroup start at different columns
+    p.rotate_keys = fp8kv::index_heads_padded(num_heads) <= 4 && ((int64_t)row_stride * 4) % 65536 == 0;
     p.key_bytes = (int32_t)key_bytes;
     p.scale_bytes = (int32_t)scale_bytes;
     p.out_bytes = (int32_t)out_bytes;

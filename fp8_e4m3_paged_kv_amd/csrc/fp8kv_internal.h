@@ -173,6 +173,7 @@ struct IndexScoreParams {
     int32_t key_bytes;         // per request: extent of the key codes in bytes
     int32_t scale_bytes;       // per request: extent of the key scales in bytes
     int32_t out_bytes;         // per request: (rows - 1) * out_stride_row * 4 + num_keys * 4
+    int32_t rotate_keys;       // 1: each wave of a workgroup starts at its own quarter of the chunk
 };
 
 struct IndexBuildParams {

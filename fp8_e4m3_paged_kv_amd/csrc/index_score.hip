@@ -335,7 +335,7 @@ struct Stack {
 // two tiles ahead (three register buffers), and the MFMAs of each half of
 // the tiles are issued next to the other half's epilogue, which does not
 // depend on them, so the matrix core and the vector ALU work side by side.
-template <int FMT, int HP>
+template <int FMT, int HP, bool ROT>
 __global__ __launch_bounds__(256, 2) void index_score_kernel(IndexScoreParams p) {
     typedef Stack<HP> S;
     constexpr int NT = S::NT, NH = S::NH, OS = S::OS;
@@ -400,6 +400,21 @@ __global__ __launch_bounds__(256, 2) void index_score_kernel(IndexScoreParams p)
                     (FMT == kKeysE4M3 ? 32u : 16u) * lg;
     uint32_t soff = (uint32_t)(n_begin + li) * (uint32_t)p.scales_stride_key +
                     (FMT == kKeysE4M3 ? 0u : (uint32_t)lg);
+    // ROT: each wave starts at its own quarter of the chunk (whole 32-key
+    // pairs) and wraps around, so the rows of a workgroup write four column
+    // regions at a time instead of one; this spreads the stores of rows
+    // whose pitch is a multiple of 64 KiB over more HBM channels (the waves
+    // no longer share key tiles through L1, so the host asks for it only
+    // where the score stores set the pace). Virtual tile v (v = 0, 16, ...)
+    // then holds keys key_of(v) .. + 15; without ROT key_of(v) = n_begin + v.
+    const int span32 = (n_end - n_begin + 31) & ~31;
+    const int rot = ROT ? (int)(((int64_t)wave * span32) / (32 * kScoreWaves)) * 32 : 0;
+    auto key_of = [&](int v) { return ROT ? n_begin + (v + rot) % span32 : n_begin + v; };
+    auto offs = [&](int v) {
+        const uint32_t k = (uint32_t)(key_of(v) + li);
+        koff = k * (uint32_t)p.codes_stride_key + (FMT == kKeysE4M3 ? 32u : 16u) * lg;
+        soff = k * (uint32_t)p.scales_stride_key + (FMT == kKeysE4M3 ? 0u : (uint32_t)lg);
+    };
     // byte offset of a slot's row: a per-lane part plus a wave-uniform one.
     // Rows do not overlap (row stride >= num_keys), so a row at or past
     // p.rows starts at or past the end of the request's scores and its
@@ -477,8 +492,14 @@ __global__ __launch_bounds__(256, 2) void index_score_kernel(IndexScoreParams p)
     };
     // column of the lane in the swapped pair starting at key t
     auto colp = [&](int t) {
-        const int k = t + 16 * (lg & 1) + li;
-        return k < n_end ? (uint32_t)k * 4u : kDropped;
+        if constexpr (ROT) {
+            // t: virtual tile; the wrap never splits a pair
+            const int k = key_of(t) + 16 * (lg & 1) + li;
+            return t >= 0 && t < span32 && k < n_end ? (uint32_t)k * 4u : kDropped;
+        } else {
+            const int k = t + 16 * (lg & 1) + li;
+            return k < n_end ? (uint32_t)k * 4u : kDropped;
+        }
     };
 
     // one step: tile t's half-0 MFMAs overlap the previous tile's half-1
@@ -492,7 +513,7 @@ __global__ __launch_bounds__(256, 2) void index_score_kernel(IndexScoreParams p)
         bf16x8 kb[4];
         kt.widen(kb);
         const float ks = FMT == kKeysE4M3 ? kt.kscale : 1.0f;
-        const bool odd = ((t - n_begin) >> 4) & 1;
+        const bool odd = ((ROT ? t : t - n_begin) >> 4) & 1;
         const uint32_t ocol = colp(t - 16);
         mfma_half(kb, 0, acc0);
         epilogue(acc1, 1, ks_prev, odd_prev, ocol_prev);
@@ -505,10 +526,29 @@ __global__ __launch_bounds__(256, 2) void index_score_kernel(IndexScoreParams p)
 #pragma unroll
     for (int t = 0; t < NH; ++t) acc1[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // tiles n_begin, n_begin + 16, ... and at least two more (their own
+    // tiles n_begin, n_begin + 16, ... (with ROT virtual tiles 0, 16, ...)
+    // and at least two more (their own
     // stores all dropped) to drain the pipeline and complete the last pair;
     // loads run two tiles ahead in three buffers
     KeyTile<FMT> ta, tb, tc;
+    if constexpr (ROT) {
+        offs(0);
+        ta.load(krs, srs, koff, soff);
+        offs(16);
+        tb.load(krs, srs, koff, soff);
+        for (int v = 0; v < span32 + 32; v += 48) {
+            offs(v + 32);
+            tc.load(krs, srs, koff, soff);
+            step(ta, v);
+            offs(v + 48);
+            ta.load(krs, srs, koff, soff);
+            step(tb, v + 16);
+            offs(v + 64);
+            tb.load(krs, srs, koff, soff);
+            step(tc, v + 32);
+        }
+        return;
+    }
     ta.load(krs, srs, koff, soff);
     koff += kstep;
     soff += sstep;
@@ -535,7 +575,14 @@ hipError_t launch_score_hp(const IndexScoreParams& p, hipStream_t stream) {
     int64_t wgs = (int64_t)p.batch * p.chunks * m;
     if (m > 1) wgs = (wgs + 8 * m - 1) / (8 * m) * (8 * m);
     if (wgs > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((index_score_kernel<FMT, HP>), dim3((unsigned)wgs),
+    if constexpr (HP <= 4) {
+        if (p.rotate_keys) {
+            hipLaunchKernelGGL((index_score_kernel<FMT, HP, true>), dim3((unsigned)wgs),
+                               dim3(64 * kScoreWaves), 0, stream, p);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((index_score_kernel<FMT, HP, false>), dim3((unsigned)wgs),
                        dim3(64 * kScoreWaves), 0, stream, p);
     return hipGetLastError();
 }

@@ -274,6 +274,32 @@ def test_scores_strided_views_and_signed_weights(fmt, H):
     check_scores(out, q.contiguous(), w.contiguous(), fmt, codes, scales, "strided")
 
 
+@pytest.mark.parametrize("H,N,chunk", [
+    (4, 333, 0),      # library chunking, ragged last chunk
+    (4, 200, 48),     # chunks of 48 keys: a 32-key pair and a lone 16-key tile
+    (2, 1000, 160),   # 2 heads, five 32-key pairs per chunk
+    (1, 77, 16),      # one head, 16-key chunks (a single tile per chunk)
+    (3, 130, 64),     # 3 heads padded to 4
+])
+@pytest.mark.parametrize("fmt", [MX, E4])
+def test_scores_rotated_chunks_on_a_64k_row_pitch(fmt, H, N, chunk):
+    """A row pitch of 16,384 floats (64 KiB) at 4 heads or fewer makes each
+    wave start at its own quarter of its key chunk and wrap around: every
+    score is still written once, within the bound, and nothing past N in a
+    row is touched."""
+    B, R = 2, 37
+    case = synth.index_case(B, R, H, N, seed=500 + N + H)
+    log(f"index score rotated fmt={fmt} H={H} N={N} chunk={chunk}")
+    codes, scales = encode(case.keys.to(DEV), fmt)
+    q, w = case.q.to(DEV), case.w.to(DEV)
+    obuf = torch.full((B, R, 16384), 7.0, device=DEV)
+    out = obuf[:, :, :N]
+    fk.index_score_mxfp4(q, w, fmt, codes, scales, out=out, key_chunk=chunk)
+    torch.cuda.synchronize()
+    assert torch.all(obuf[:, :, N:] == 7.0)
+    check_scores(out, q, w, fmt, codes, scales, f"rotated H{H} N{N} chunk{chunk}")
+
+
 def test_negative_dots_contribute_nothing():
     """Keys = -q direction for every head: every dot is negative and every
     score is exactly 0 (ReLU per head before the head sum)."""
