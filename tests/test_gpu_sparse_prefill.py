@@ -4,8 +4,10 @@ blocks with R = the chunk's rows, on the same dequantized cache.
 
 Bar: as the dense prefill -- fp32 output within max-abs 2e-3 and rel-L2
 1e-3, bf16 output equal to the RNE of the same kernel's fp32 output. A
-selection of every block with full counts gives the dense prefill's output
-bit for bit."""
+selection of every block with full counts walks the same keys as the dense
+prefill; the dense kernel (head_dim 128) splits each query block's keys
+into three groups merged by log-sum-exp, so the two agree within the same
+bar rather than bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -81,7 +83,7 @@ def test_groups_and_head_dims(Hq, Hkv, D):
     check(case, sel, ql, f"Hq{Hq} Hkv{Hkv} D{D}", layout="slot_major" if D == 64 else "head_major")
 
 
-def test_every_block_full_equals_dense_bit_for_bit():
+def test_every_block_full_matches_dense():
     case = synth.decode_case([3000, 777], 32, 8, 128, 16, rows=64, seed=220)
     L = case.layout
     ql = torch.tensor([64, 50], dtype=torch.int32)
@@ -99,7 +101,13 @@ def test_every_block_full_equals_dense_bit_for_bit():
         block_size=16, softmax_scale=case.softmax_scale,
         max_context=16 * L.block_tables.shape[1], out_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert torch.equal(sparse, dense)
+    host = dc.host()
+    for b, n in enumerate(ql.tolist()):
+        ref = oracle_rows(case, host, sel, b, n)
+        assert_attn_close(sparse[b, :n].cpu().numpy(), ref, f"selected, request {b}")
+        assert_attn_close(dense[b, :n].cpu().numpy(), ref, f"dense, request {b}")
+    assert_attn_close(sparse.cpu().numpy(), dense.cpu().numpy().astype(np.float64),
+                      "selected vs dense")
 
 
 def test_tokens_that_see_no_key_output_zero():
