@@ -795,6 +795,26 @@ def prefill_attention(torch, fk, synth, dev, stream, reps=10):
            "prefill_attn_TFLOPs": round(tf, 1),
            "prefill_attn_mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
 
+    # a 1024-token chunk at the end of the same request: one query block per
+    # CU, where the kernel splits each block's keys over three wave groups
+    # (q and out as 1024-row views: the grid follows the buffers' rows)
+    C1 = 1024
+    ql1 = torch.full((B,), C1, dtype=torch.int32, device=dev)
+    q1, out1 = q[:, :C1], out[:, :C1]
+
+    def run_1k():
+        fk.prefill_attn_fp8(q1, k_cache, v_cache, k_plane.t(), v_plane.t(), bt, cl, ql1,
+                            num_kv_heads=H, block_size=L.block_size,
+                            softmax_scale=case.softmax_scale, max_context=ctx, out=out1)
+    settle(run_1k)
+    ms = time_events(run_1k, reps, stream)
+    avg = sum(ms) / len(ms)
+    P1 = ctx - C1
+    tf = (P1 * C1 + C1 * (C1 + 1) // 2) * Hq * 4 * D / (avg * 1e-3) / 1e12
+    res.update({"prefill_attn_1k_us": round(avg * 1e3, 1),
+                "prefill_attn_1k_TFLOPs": round(tf, 1),
+                "prefill_attn_1k_mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
+
     # the same chunk over selected blocks: 1/8 of the blocks before the
     # chunk, then the chunk's own (every selected block full)
     log("prefill attention over selected blocks (1/8 of the context)...")
