@@ -1220,7 +1220,7 @@ int fp8kv_index_score_mxfp4(
     // rows whose pitch is a multiple of 64 KiB write their scores to the
     // same HBM channels at the same column; at 4 heads or fewer (one score
     // per 4 or more MFMA rows) those stores set the pace, so the waves of a
-    // workgroup start at different columns
+    // workgroup start at different columns (128 keys apart)
     p.rotate_keys = fp8kv::index_heads_padded(num_heads) <= 4 && ((int64_t)row_stride * 4) % 65536 == 0;
     p.key_bytes = (int32_t)key_bytes;
     p.scale_bytes = (int32_t)scale_bytes;

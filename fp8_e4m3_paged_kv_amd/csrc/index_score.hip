@@ -400,15 +400,15 @@ __global__ __launch_bounds__(256, 2) void index_score_kernel(IndexScoreParams p)
                     (FMT == kKeysE4M3 ? 32u : 16u) * lg;
     uint32_t soff = (uint32_t)(n_begin + li) * (uint32_t)p.scales_stride_key +
                     (FMT == kKeysE4M3 ? 0u : (uint32_t)lg);
-    // ROT: each wave starts at its own quarter of the chunk (whole 32-key
-    // pairs) and wraps around, so the rows of a workgroup write four column
-    // regions at a time instead of one; this spreads the stores of rows
-    // whose pitch is a multiple of 64 KiB over more HBM channels (the waves
-    // no longer share key tiles through L1, so the host asks for it only
-    // where the score stores set the pace). Virtual tile v (v = 0, 16, ...)
-    // then holds keys key_of(v) .. + 15; without ROT key_of(v) = n_begin + v.
+    // ROT: wave w starts 128 w keys into the chunk (whole 32-key pairs) and
+    // wraps around, so the rows of a workgroup write four column regions at
+    // a time instead of one; this spreads the stores of rows whose pitch is a
+    // multiple of 64 KiB over more HBM channels, and the waves stay close
+    // enough that each key line still comes from HBM about once. Virtual tile
+    // v (v = 0, 16, ...) then holds keys key_of(v) .. + 15; without ROT
+    // key_of(v) = n_begin + v.
     const int span32 = (n_end - n_begin + 31) & ~31;
-    const int rot = ROT ? (int)(((int64_t)wave * span32) / (32 * kScoreWaves)) * 32 : 0;
+    const int rot = ROT ? (128 * wave) % span32 : 0;
     auto key_of = [&](int v) { return ROT ? n_begin + (v + rot) % span32 : n_begin + v; };
     auto offs = [&](int v) {
         const uint32_t k = (uint32_t)(key_of(v) + li);

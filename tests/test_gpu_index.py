@@ -276,17 +276,19 @@ def test_scores_strided_views_and_signed_weights(fmt, H):
 
 @pytest.mark.parametrize("H,N,chunk", [
     (4, 333, 0),      # library chunking, ragged last chunk
+    (4, 1000, 512),   # waves start 0, 128, 256, 384 keys in; a 488-key last chunk
     (4, 200, 48),     # chunks of 48 keys: a 32-key pair and a lone 16-key tile
-    (2, 1000, 160),   # 2 heads, five 32-key pairs per chunk
+    (2, 1000, 160),   # starts 0, 128, 96, 64 (wrapped); a 40-key last chunk
+    (2, 700, 320),    # starts 0, 128, 256, 64
     (1, 77, 16),      # one head, 16-key chunks (a single tile per chunk)
     (3, 130, 64),     # 3 heads padded to 4
 ])
 @pytest.mark.parametrize("fmt", [MX, E4])
 def test_scores_rotated_chunks_on_a_64k_row_pitch(fmt, H, N, chunk):
-    """A row pitch of 16,384 floats (64 KiB) at 4 heads or fewer makes each
-    wave start at its own quarter of its key chunk and wrap around: every
-    score is still written once, within the bound, and nothing past N in a
-    row is touched."""
+    """A row pitch of 16,384 floats (64 KiB) at 4 heads or fewer makes wave
+    w of a workgroup start 128 w keys into its key chunk and wrap around:
+    every score is still written once, within the bound, and nothing past
+    N in a row is touched."""
     B, R = 2, 37
     case = synth.index_case(B, R, H, N, seed=500 + N + H)
     log(f"index score rotated fmt={fmt} H={H} N={N} chunk={chunk}")
