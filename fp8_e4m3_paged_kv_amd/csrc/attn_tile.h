@@ -283,17 +283,21 @@ struct DecodeTile {
     }
 
     // The same for NT 16-row tiles of queries: each K operand is widened
-    // once and feeds every tile's MFMA chain.
+    // once and feeds every tile's MFMA chain. The k-steps are the outer loop,
+    // so the 2 NT accumulation chains (tiles x halves) take turns and no
+    // MFMA waits for the previous one of its own chain.
     template <int NT>
     static __device__ __forceinline__ void qk_tiles(const Regs& R, const bf16x8 (&qv)[NT][KSTEPS],
                                                     floatx4 (&sc)[NT][2]) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int j = 0; j < NT; ++j) sc[j][s] = floatx4{0.f, 0.f, 0.f, 0.f};
-            const uint32_t* kw = reinterpret_cast<const uint32_t*>(R.kraw[s]);
 #pragma unroll
-            for (int k = 0; k < KSTEPS; ++k) {
+        for (int k = 0; k < KSTEPS; ++k) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const uint32_t* kw = reinterpret_cast<const uint32_t*>(R.kraw[s]);
                 const bf16x8 a = widen_k(kw[2 * k], kw[2 * k + 1]);
 #pragma unroll
                 for (int j = 0; j < NT; ++j)
