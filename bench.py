@@ -65,6 +65,9 @@ def parse():
                     default="prefill,longctx,sparse,prefill_attn,index,unscaled,ceilings",
                     help="comma list of the extras to run (prefill, longctx, sparse, "
                          "prefill_attn, index, unscaled, ceilings)")
+    ap.add_argument("--pool", choices=("head", "slot"), default="head",
+                    help="code pool layout: head = [Hkv, slots, D] (each KV head's "
+                         "rows of a block contiguous), slot = [slots, Hkv, D]")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times "
                          "(the known-size reference for HBM byte counters)")
@@ -116,6 +119,21 @@ def quant_bytes(T, Hkv, D):
 
 
 SETTLE_S = 0.3
+POOL = "head"                  # code pool layout (set from --pool)
+POOL_DESC = {"head": "head-major [Hkv, slots, D]", "slot": "slot-major [slots, Hkv, D]"}
+
+
+def alloc_pool(torch, S, H, D, dev):
+    """K and V code pools as [slots, Hkv, D] views (the library takes any
+    slot and head strides); stored head-major ([Hkv, slots, D]: a KV head's
+    rows of a block are contiguous) or slot-major ([slots, Hkv, D])."""
+    if POOL == "head":
+        k = torch.empty((H, S, D), dtype=torch.uint8, device=dev).permute(1, 0, 2)
+        v = torch.empty((H, S, D), dtype=torch.uint8, device=dev).permute(1, 0, 2)
+    else:
+        k = torch.empty((S, H, D), dtype=torch.uint8, device=dev)
+        v = torch.empty_like(k)
+    return k, v
 
 
 def settle(fn, seconds=SETTLE_S):
@@ -155,6 +173,8 @@ def traffic_entry(per_launch_alg_bytes):
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    if t.get("pool_layout") != POOL:               # counters taken on this pool layout
         return None
     return t.get("bytes_per_launch")
 
@@ -205,16 +225,16 @@ def cpu_baseline(case, dc, lens, max_threads=16, budget_s=30.0):
     L = case.layout
     bs = L.block_size
     H, D = case.num_kv_heads, case.head_dim
-    NB = dc["k_cache"].shape[0] // bs
     cores = max(1, min(max_threads, os.cpu_count() or 1))
 
     def host_request(b):
         nb = (lens[b] + bs - 1) // bs
         blk = L.block_tables[b, :nb].long().to(dc["k_cache"].device)
-        kc = dc["k_cache"].view(NB, bs, H, D)[blk].reshape(-1, H, D).cpu().numpy()
-        vc = dc["v_cache"].view(NB, bs, H, D)[blk].reshape(-1, H, D).cpu().numpy()
-        kp = dc["k_plane"].view(H, NB, bs)[:, blk].reshape(H, -1).cpu().numpy()
-        vp = dc["v_plane"].view(H, NB, bs)[:, blk].reshape(H, -1).cpu().numpy()
+        sl = (blk[:, None] * bs + torch.arange(bs, device=blk.device)).reshape(-1)
+        kc = dc["k_cache"][sl].cpu().numpy()
+        vc = dc["v_cache"][sl].cpu().numpy()
+        kp = dc["k_plane"][:, sl].cpu().numpy()
+        vp = dc["v_plane"][:, sl].cpu().numpy()
         bt = np.arange(nb, dtype=np.int32)[None, :]
         q = case.q[b:b + 1].contiguous().view(torch.int16).numpy().view(np.uint16)
         return q, kc, vc, kp.T, vp.T, bt, np.array([lens[b]], np.int32)
@@ -265,6 +285,8 @@ def main():
         print(json.dumps({"error": "the benchmark measures one GPU only; "
                                    "run with --gpus 1"}))
         sys.exit(2)
+    global POOL
+    POOL = args.pool
     import torch
     import fp8_e4m3_paged_kv_amd as fk
     from fp8_e4m3_paged_kv_amd import synth
@@ -280,8 +302,7 @@ def main():
     lens = L.context_lens.tolist()
     B, R, Hq, Hkv, D, bs = 64, 1, 32, 8, 128, L.block_size
     S = L.num_slots
-    k_cache = torch.empty((S, Hkv, D), dtype=torch.uint8, device=dev)
-    v_cache = torch.empty_like(k_cache)
+    k_cache, v_cache = alloc_pool(torch, S, Hkv, D, dev)
     k_plane = torch.empty((Hkv, S), dtype=torch.float32, device=dev)
     v_plane = torch.empty_like(k_plane)
     slots_all = L.token_slots.to(dev)
@@ -389,7 +410,8 @@ def main():
                    "batch": B, "context_tokens": sum(lens), "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "block_size": bs,
                    "decode_ranges_per_kv_head": nr,
-                   "scale_planes": "head-major [Hkv, slots]"},
+                   "scale_planes": "head-major [Hkv, slots]",
+                   "pool_layout": POOL_DESC[POOL]},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -445,8 +467,7 @@ def prefill_quant_scatter(torch, fk, synth, dev, stream, sets=32, reps=4):
     log("prefill-chunk quantize+scatter...")
     H, D, T, S = 8, 128, 4096, 1 << 20
     chunks = [synth.prefill_chunk(seed=100 + i, device=dev) for i in range(sets)]
-    k_cache = torch.empty((S, H, D), dtype=torch.uint8, device=dev)
-    v_cache = torch.empty_like(k_cache)
+    k_cache, v_cache = alloc_pool(torch, S, H, D, dev)
     k_plane = torch.empty((H, S), dtype=torch.float32, device=dev)
     v_plane = torch.empty_like(k_plane)
     it = {"i": 0}
@@ -521,8 +542,7 @@ def longctx_decode(torch, fk, synth, dev, stream, reps=20):
     L = case.layout
     H, D, bs = 4, 128, L.block_size
     S = L.num_slots
-    k_cache = torch.empty((S, H, D), dtype=torch.uint8, device=dev)
-    v_cache = torch.empty_like(k_cache)
+    k_cache, v_cache = alloc_pool(torch, S, H, D, dev)
     k_plane = torch.empty((H, S), dtype=torch.float32, device=dev)
     v_plane = torch.empty_like(k_plane)
     slots = L.token_slots.to(dev)
@@ -623,8 +643,7 @@ def unscaled_decode(torch, fk, synth, dev, stream, case, q, bt, cl, reps=20):
     lens = L.context_lens.tolist()
     g = synth.gen(2 + 1000, dev)
     T = int(sum(lens))
-    kc = torch.empty((S, Hkv, D), dtype=torch.uint8, device=dev)
-    vc = torch.empty_like(kc)
+    kc, vc = alloc_pool(torch, S, Hkv, D, dev)
     slots = L.token_slots.to(dev)
     nr = fk.decode_num_ranges(Hkv, 0)
     ws = torch.empty(fk.decode_workspace_bytes(B, R, Hq, Hkv, D, nr), dtype=torch.uint8,
@@ -766,8 +785,7 @@ def prefill_attention(torch, fk, synth, dev, stream, reps=10):
     L = case.layout
     H, D = case.num_kv_heads, case.head_dim
     S = L.num_slots
-    k_cache = torch.empty((S, H, D), dtype=torch.uint8, device=dev)
-    v_cache = torch.empty_like(k_cache)
+    k_cache, v_cache = alloc_pool(torch, S, H, D, dev)
     k_plane = torch.empty((H, S), dtype=torch.float32, device=dev)
     v_plane = torch.empty_like(k_plane)
     slots = L.token_slots.to(dev)

@@ -26,6 +26,9 @@ def log(msg):
 class DevCache:
     """uint8 code buffers [S, H, D] and fp32 scale planes on the device.
 
+    pool "slot": codes stored [S, H, D]; "head": stored [H, S, D] and passed
+    as the permuted [S, H, D] view (a KV head's rows of a block contiguous).
+
     scale_layout "head_major": planes stored [H, S] and passed as the
     transposed [S, H] view (one head's scales contiguous per slot);
     "interleaved": one [H, S, 2] array holding each row's K and V scales
@@ -33,13 +36,19 @@ class DevCache:
     "slot_major": planes stored [S, H]."""
 
     def __init__(self, num_slots, H, D, device="cuda",
-                 scale_layout="head_major", sentinel=True):
+                 scale_layout="head_major", sentinel=True, pool="slot"):
         self.S, self.H, self.D = num_slots, H, D
         self.layout = scale_layout
         fill = SENTINEL if sentinel else 0
-        self.k_cache = torch.full((num_slots, H, D), fill, dtype=torch.uint8,
-                                  device=device)
-        self.v_cache = torch.full_like(self.k_cache, fill)
+        if pool == "head":
+            self.k_cache = torch.full((H, num_slots, D), fill, dtype=torch.uint8,
+                                      device=device).permute(1, 0, 2)
+            self.v_cache = torch.full((H, num_slots, D), fill, dtype=torch.uint8,
+                                      device=device).permute(1, 0, 2)
+        else:
+            self.k_cache = torch.full((num_slots, H, D), fill, dtype=torch.uint8,
+                                      device=device)
+            self.v_cache = torch.full_like(self.k_cache, fill)
         sfill = SCALE_SENTINEL if sentinel else 0.0
         if scale_layout == "head_major":
             self.k_plane = torch.full((H, num_slots), sfill, device=device)
@@ -59,9 +68,10 @@ class DevCache:
             self.v_scale = self.v_plane
 
     def host(self):
-        """numpy copies with the same element strides as the device views."""
-        kc = self.k_cache.cpu().numpy()
-        vc = self.v_cache.cpu().numpy()
+        """numpy copies with the same element strides as the device views
+        (codes always as contiguous [S, H, D])."""
+        kc = self.k_cache.contiguous().cpu().numpy()
+        vc = self.v_cache.contiguous().cpu().numpy()
         kp = self.k_plane.cpu().numpy()
         vp = self.v_plane.cpu().numpy()
         if self.layout != "slot_major":
@@ -93,11 +103,11 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
-def cache_case(case, device="cuda", scale_layout="head_major"):
+def cache_case(case, device="cuda", scale_layout="head_major", pool="slot"):
     """Build the device cache of a DecodeCase with the GPU quantizer."""
     L = case.layout
     dc = DevCache(L.num_slots, case.num_kv_heads, case.head_dim, device,
-                  scale_layout, sentinel=False)
+                  scale_layout, sentinel=False, pool=pool)
     k = case.k.to(device)
     v = case.v.to(device)
     dc.scatter(k, v, L.token_slots.to(device))

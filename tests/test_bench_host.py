@@ -50,12 +50,16 @@ def test_decode_bytes_count_table_entries_per_request(bench):
 
 
 def test_traffic_only_for_the_measured_source(bench, tmp_path, monkeypatch):
-    good = {"kernel_source_hash": bench.kernel_source_hash(), "bytes_per_launch": 12345}
+    good = {"kernel_source_hash": bench.kernel_source_hash(), "bytes_per_launch": 12345,
+            "pool_layout": bench.POOL}
     f = tmp_path / "traffic.json"
     f.write_text(json.dumps(good))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
     assert bench.traffic_entry(1) == 12345
     f.write_text(json.dumps(dict(good, kernel_source_hash="0" * 16)))
+    assert bench.traffic_entry(1) is None
+    other = "slot" if bench.POOL == "head" else "head"
+    f.write_text(json.dumps(dict(good, pool_layout=other)))      # another pool layout
     assert bench.traffic_entry(1) is None
     f.write_text("not json")
     assert bench.traffic_entry(1) is None
