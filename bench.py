@@ -814,7 +814,7 @@ def prefill_attention(torch, fk, synth, dev, stream, reps=10):
            "prefill_attn_mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
 
     # a 1024-token chunk at the end of the same request: one query block per
-    # CU, where the kernel splits each block's keys over three wave groups
+    # CU, where the kernel splits each block's keys over two wave groups
     # (q and out as 1024-row views: the grid follows the buffers' rows)
     C1 = 1024
     ql1 = torch.full((B,), C1, dtype=torch.int32, device=dev)

@@ -1,30 +1,39 @@
 // prefill_attn.hip -- chunked-prefill attention over the E4M3 cache
 // (sglang-jax #1776, "Modifications": each KV tile is widened to the query
 // dtype before the score dot, and P never takes the cache dtype; ATOM #2655
-// description: prefill sparse GQA over the E4M3 cache). The tile math it
-// shares with the decode split kernel is in attn_tile.h.
+// description: prefill sparse GQA over the E4M3 cache). The state and
+// helpers it shares with the decode split kernel are in attn_tile.h.
 //
 // Every query token of a chunk attends to the cached tokens up to its own
 // position (the chunk was scattered into the cache first). Workgroup = (request,
 // KV head, block of 4 x NT x 16/G query tokens); each of its 4 waves carries
 // NT row tiles, each stacking 16/G tokens x G query heads into the 16 MFMA
-// rows exactly as the decode split kernel stacks verify rows, and runs the
-// decode kernel's tile math (QK^T MFMA, online softmax, P' = p * v_scale in
-// fp16, PV MFMA) with the same rounding at every step. Each K and V operand
-// is widened from E4M3 once per wave and feeds all NT row tiles; the
-// value-scale range exponent of P' depends only on the tile, so it and
-// v_scale * kappa are shared by the row tiles too.
+// rows exactly as the decode split kernel stacks verify rows: QK^T MFMA
+// (bf16), online softmax with the key scale on the score, P' = p * v_scale
+// in fp16, PV MFMA (fp16). The value-scale range exponent of P' depends only
+// on the tile, so it and v_scale * kappa are shared by the row tiles.
 //
 // The K/V codes and scales of each 32-token tile are read from the cache
 // once per workgroup into LDS (double-buffered): every loader wave moves the
 // rows of 8 (head_dim 128) or 16 (head_dim 64) tokens of one 16-token half,
 // whose page lookup is wave-uniform, through buffer descriptors that end
-// after the chunk's last visible key, so nothing past it is read. The key
-// scales go to LDS already multiplied by softmax_scale * log2(e). All 4
-// waves read their operands from LDS in the decode kernel's register layout,
-// the scales as four consecutive tokens per lane (no lane broadcast needed).
-// Workgroups of one (request, KV head) run on one XCD, the deepest query
-// blocks first.
+// after the chunk's last visible key, so nothing past it is read. The loader
+// widens the codes once for the whole workgroup (exact: keys to bf16, values
+// to fp16) before they go to LDS, so the 4 waves read ready MFMA operands:
+// keys with 16-byte reads, values with the transposing reads of gfx950
+// (ds_read_b64_tr_b16), which hand each lane 4 consecutive tokens of one
+// head-dim column. The key scales go to LDS already multiplied by
+// softmax_scale * log2(e); the waves read the scales as four consecutive
+// tokens per lane. Workgroups of one (request, KV head) run on one XCD, the
+// deepest query blocks first.
+// Instruction mix: a wave hides about two cheap vector instructions behind
+// each MFMA of its own instruction stream, while a vector-heavy wave beside
+// an MFMA-heavy one on the same SIMD slows the MFMAs down. So each wave
+// interleaves its own work: row tile j's PV MFMAs are issued between the
+// exponentials of row tile j + 1, and the last row tile's between the
+// loader's conversions of the next tile; the softmax's rare rescale is one
+// branch for all row tiles, so the rest of a tile is one block of code.
+// Occupancy: 2 waves per SIMD (the registers hold a tile's V operands).
 // Selected blocks (SP): the page table lists the blocks a request selected,
 // in position order, with a count of valid keys per entry (from the block's
 // start), as in the decode over selected blocks; positions are virtual
@@ -34,20 +43,19 @@
 // with a partial half takes the masked path, where a position past its
 // block's count is no key and adds exactly nothing (a row may see no key
 // in a tile, or at all: its output is then 0).
-// Occupancy: the dense kernel fits 168 VGPRs, 3 waves per SIMD (each wave's
-// tile chain is latency-bound, so a third wave adds throughput); the
-// selected-block kernel needs more registers and runs 2 waves per SIMD.
-// Key groups (KG = 3, dense head_dim 128, chosen by the host when there are
-// at most 2 query blocks per CU): the workgroup is 3 groups of 4 waves; group
-// g walks tiles [g T / 3, (g + 1) T / 3) of the block's T key tiles with its
-// own LDS buffers, all 12 waves meeting at each tile's barrier, and the
-// groups' normalized rows are merged into group 0 by their log2 sum-exp
+// Key groups (KG = 2, dense head_dim 128, chosen by the host when there are
+// at most as many query blocks as CUs): the workgroup is 2 groups of 4 waves;
+// group g walks tiles [g T / 2, (g + 1) T / 2) of the block's T key tiles
+// with its own LDS buffers, all 8 waves meeting at each tile's barrier, and
+// the groups' normalized rows are merged into group 0 by their log2 sum-exp
 // through LDS. A row may see no key in a group's tiles (its masked
-// probabilities are zeroed and its sum-exp is kNeg, weight 0).
+// probabilities are zero and its sum-exp is kNeg, weight 0).
 // The prefill kernel keeps a row's running maximum until a tile's scores
 // exceed it by more than kLazyMax (log2 units), so p = exp2(s - m) stays
 // below 2^kLazyMax; its P' range factor is 2^(141 - kLazyMax - e), which
-// keeps P' below 2^15 as in the decode kernel.
+// keeps P' below 2^15 as in the decode kernel. The score enters the
+// exponent as one fused multiply-add, s * k_scale' - m; a key a row does
+// not see gets kNeg, whose exp2 is exactly 0.
 #include <hip/hip_runtime.h>
 
 #include "attn_tile.h"
@@ -59,23 +67,57 @@ namespace {
 
 constexpr int kLazyMax = 8;
 
+// PV A operand of a lane from the fp16 value rows: two transposing 8-byte
+// reads (gfx950 ds_read_b64_tr_b16), the second `second` bytes further.
+// Within each 16-lane group, lane 4 a + b receives element b of the 8-byte
+// rows that lanes a, a + 4, a + 8, a + 12 address, in that order.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f16x8 read_v_operand(const uint8_t* src, int second) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    const lds_u8* p = (const lds_u8*)src;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + second));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(f16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+}
+
+template <bool B>
+struct BoolC {
+    static constexpr bool value = B;
+};
+
+// maximum of 8 scores as a chain of three-input maxima (4 instructions)
+__device__ __forceinline__ float max8_chain(const float (&v)[2][4]) {
+    const float a = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[0][0], v[0][1]), v[0][2]);
+    const float b = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[0][3], v[1][0]), v[1][1]);
+    const float c = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[1][2], v[1][3]), a);
+    return __builtin_elementwise_maximum(b, c);
+}
+
 template <int D, bool BSP2, int NT, bool SP, int KG>
-__global__ __launch_bounds__(256 * KG, SP ? 2 : (KG == 1 ? 3 : 1)) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(256 * KG, 2 / KG) void prefill_kernel(PrefillParams p) {
     constexpr int KSTEPS = D / 32;
     constexpr int DL = D / 16;
-    constexpr int KB = D / 4;
-    constexpr int ROW = D + 16;               // padded LDS row: conflict-free row reads
+    constexpr int LROW = 288;                 // LDS row of one key or value (16-bit values)
     constexpr int CPR = D / 16;               // 16-byte chunks per code row
     constexpr int TPL = 64 / CPR;             // tokens one loader wave moves
     constexpr int LOAD_WAVES = 32 / TPL;
+    static_assert(D <= 128, "a widened row fits the 256 bytes of data of an LDS row");
     static_assert(TPL <= 16 && 16 % TPL == 0, "a loader wave stays inside one half");
-    typedef DecodeTile<D> Tile;
-    typedef typename Tile::Regs Regs;
-    // LDS of key group g: K and V code tiles [2][32 * ROW] each, scales
-    // [2][k_scale * score scale | v_scale][32], selected-block key counts
-    // [2][half]; with KG > 1 the same bytes later hold the groups' partial
-    // results for the merge
-    constexpr int TILE_BYTES = 4 * 32 * ROW + 2 * 2 * 32 * 4 + 16;
+    // LDS of key group g, per buffer: the tile's keys widened to bf16 and its
+    // values widened to fp16, one 288-byte row per token (head-dim columns
+    // 8 c .. 8 c + 7 in 16-byte chunk c, chunks permuted per row: K chunk c of
+    // token T at c ^ ((T >> 2) & 3), V chunk c at c ^ ((T >> 2) & 1)); then
+    // scales [2][k_scale * score scale | v_scale][32] and selected-block key
+    // counts [2][half]. The row pitch and permutations keep every LDS access
+    // of the loop free of bank conflicts on gfx950 (the loader's 16-byte
+    // stores, the K operand reads, the transposing V operand reads), and the
+    // operand addresses of a lane differ only by immediate offsets. With KG > 1
+    // the same bytes later hold the groups' partial results for the merge.
+    constexpr int KT_BYTES = 32 * LROW;
+    constexpr int VT_BYTES = 32 * LROW;
+    constexpr int TILE_BYTES = 2 * (KT_BYTES + VT_BYTES) + 2 * 2 * 32 * 4 + 16;
     constexpr int MERGE_BYTES = KG > 1 ? 4 * 64 * NT * (4 * DL + 2) * 4 : 0;
     constexpr int LDS_BYTES = KG * TILE_BYTES > MERGE_BYTES ? KG * TILE_BYTES : MERGE_BYTES;
     __shared__ __align__(16) uint8_t lds_raw[LDS_BYTES];
@@ -83,17 +125,17 @@ __global__ __launch_bounds__(256 * KG, SP ? 2 : (KG == 1 ? 3 : 1)) void prefill_
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int kg = wv >> 2;           // key group: a third of the block's key tiles (KG = 3)
+    const int kg = wv >> 2;           // key group: a 1 / KG share of the block's key tiles
     const int wave = wv & 3;          // role in the query block: rows, loader slice
     const int li = lane & 15, lg = lane >> 4;
     uint8_t* const lds_g = lds_raw + kg * TILE_BYTES;
-    auto lds_k = [&](int buf) { return lds_g + buf * 32 * ROW; };
-    auto lds_v = [&](int buf) { return lds_g + (2 + buf) * 32 * ROW; };
+    auto lds_k = [&](int buf) { return lds_g + buf * KT_BYTES; };
+    auto lds_v = [&](int buf) { return lds_g + 2 * KT_BYTES + buf * VT_BYTES; };
     auto lds_s = [&](int buf, int which) {
-        return reinterpret_cast<float*>(lds_g + 4 * 32 * ROW) + (2 * buf + which) * 32;
+        return reinterpret_cast<float*>(lds_g + 2 * (KT_BYTES + VT_BYTES)) + (2 * buf + which) * 32;
     };
     auto lds_nv = [&](int buf) {
-        return reinterpret_cast<int*>(lds_g + 4 * 32 * ROW + 2 * 2 * 32 * 4) + 2 * buf;
+        return reinterpret_cast<int*>(lds_g + 2 * (KT_BYTES + VT_BYTES) + 2 * 2 * 32 * 4) + 2 * buf;
     };
 
     // XCD-contiguous numbering, deepest query block first within a group
@@ -128,11 +170,12 @@ __global__ __launch_bounds__(256 * KG, SP ? 2 : (KG == 1 ? 3 : 1)) void prefill_
         tq[j] = q0 + (wave * NT + j) * TPW + li / p.group;
         lim[j] = P + tq[j];
         if (tq[j] < qlen) {
+            // k-step k of lane (i, g): head-dim slots [32 k + 8 g, 32 k + 8 g + 8)
             const uint16_t* qp = p.q + (int64_t)b * p.q_stride_b + (int64_t)tq[j] * p.q_stride_tok +
-                                 (int64_t)hq * p.q_stride_head + lg * (D / 4);
+                                 (int64_t)hq * p.q_stride_head + 8 * lg;
 #pragma unroll
             for (int k = 0; k < KSTEPS; ++k)
-                qv[j][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 8 * k));
+                qv[j][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * k));
         } else {
 #pragma unroll
             for (int k = 0; k < KSTEPS; ++k) qv[j][k] = bf16x8{};
@@ -151,15 +194,27 @@ __global__ __launch_bounds__(256 * KG, SP ? 2 : (KG == 1 ? 3 : 1)) void prefill_
     }
     int ef_run = 15;
 
-    // cooperative tile load: lane t of a loader wave moves 16 bytes of token
-    // t / CPR's K and V rows and reads the token's two scales; its chunk-0
-    // lanes store the key scale, its chunk-1 lanes the value scale
+    // cooperative tile load, widened once for all waves: lane l of loader
+    // wave w moves the 16 K and the 16 V codes of chunk l / TPL of token
+    // w TPL + l % TPL (to bf16 and fp16) and reads the token's two scales; its
+    // chunk-0 lanes store the key scale, its chunk-1 lanes the value scale
     const bool loader = wave < LOAD_WAVES;
-    const int ld_tok = (t & 255) / CPR, ld_chunk = t % CPR;
+    const int ld_tok = wave * TPL + lane % TPL, ld_chunk = lane / TPL;
     const int ld_half = (wave * TPL) >> 4;
     const int ld_code = (ld_tok & 15) * (int)p.cache_stride_slot + 16 * ld_chunk;
     const int ld_scale = (ld_tok & 15) * (int)p.scale_stride_slot * 4;
-    const int lds_code = ld_tok * ROW + 16 * ld_chunk;
+    const int kx = (ld_tok >> 2) & 3, vx = (ld_tok >> 2) & 1;
+    const int lds_k0 = ld_tok * LROW + 16 * ((2 * ld_chunk) ^ kx);
+    const int lds_k1 = ld_tok * LROW + 16 * ((2 * ld_chunk + 1) ^ kx);
+    const int lds_v0 = ld_tok * LROW + 16 * ((2 * ld_chunk) ^ vx);
+    const int lds_v1 = ld_tok * LROW + 16 * ((2 * ld_chunk + 1) ^ vx);
+    // operand reads: K of lane (i, g), k-step k, half s at kq + 64 k + 16 LROW s
+    // (token 16 s + i, chunk 4 k + g); V of n-tile n, key half e at
+    // vq + 32 n + 16 LROW e (token 16 e + 4 g + i / 4, columns 16 n + 4 (i % 4)
+    // .. + 3, which the transposing read hands out as column 16 n + i of the
+    // tokens 16 e + 4 g .. 16 e + 4 g + 3)
+    const int kq = li * LROW + 16 * (lg ^ (li >> 2));
+    const int vq = (4 * lg + (li >> 2)) * LROW + 16 * (((li >> 1) & 1) ^ (lg & 1)) + 8 * (li & 1);
     const uint8_t* kbase = p.k_cache + (int64_t)h * p.cache_stride_head;
     const uint8_t* vbase = p.v_cache + (int64_t)h * p.cache_stride_head;
     const float* ksbase = p.k_scale + (int64_t)h * p.scale_stride_head;
@@ -198,8 +253,19 @@ __global__ __launch_bounds__(256 * KG, SP ? 2 : (KG == 1 ? 3 : 1)) void prefill_
                                             make_rsrc(vsbase + soff, nrs), ld_scale, 0, 0));
     };
     auto store_tile = [&](int buf) {
-        *reinterpret_cast<intx4*>(lds_k(buf) + lds_code) = kr;
-        *reinterpret_cast<intx4*>(lds_v(buf) + lds_code) = vr;
+        // 16 codes -> 16 bf16 (K) / fp16 (V) in order (exact), two chunks each
+        uint32_t kw[8], vw[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            kw[2 * i] = e4m3x2_to_bf16x2<false>((uint32_t)kr[i]);
+            kw[2 * i + 1] = e4m3x2_to_bf16x2<true>((uint32_t)kr[i]);
+            vw[2 * i] = e4m3x2_to_f16x2<false>((uint32_t)vr[i]);
+            vw[2 * i + 1] = e4m3x2_to_f16x2<true>((uint32_t)vr[i]);
+        }
+        *reinterpret_cast<uint4*>(lds_k(buf) + lds_k0) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+        *reinterpret_cast<uint4*>(lds_k(buf) + lds_k1) = make_uint4(kw[4], kw[5], kw[6], kw[7]);
+        *reinterpret_cast<uint4*>(lds_v(buf) + lds_v0) = make_uint4(vw[0], vw[1], vw[2], vw[3]);
+        *reinterpret_cast<uint4*>(lds_v(buf) + lds_v1) = make_uint4(vw[4], vw[5], vw[6], vw[7]);
         const float sr = ld_chunk == 0 ? ksr * p.score_scale_log2 : vsr;
         if (ld_chunk < 2) lds_s(buf, ld_chunk)[ld_tok] = sr;
         if (SP && lane == 0 && ((wave * TPL) & 15) == 0) lds_nv(buf)[ld_half] = ld_nv;
@@ -210,22 +276,27 @@ __global__ __launch_bounds__(256 * KG, SP ? 2 : (KG == 1 ? 3 : 1)) void prefill_
         store_tile(0);
     }
     __syncthreads();
-    for (int it = 0; it < nmax; ++it) {
+    // One tile step; MASKED: the visibility test of every score (causal, and
+    // with selected blocks the blocks' key counts). All waves of the
+    // workgroup take the same steps, one barrier each.
+    auto step = [&](int it, auto mask_c) {
+        constexpr bool MASKED = decltype(mask_c)::value;
         const int ti = tg0 + it;
         const int buf = it & 1;
-        if (loader && it + 1 < ng) load_tile(ti + 1);
+        // one key group: the step after the last loads and stores a tile
+        // with no keys (zero-length buffer ranges), which keeps the loader's
+        // work in the same block as the PV MFMAs
+        const bool next = KG == 1 || it + 1 < ng;
+        if (loader && next) load_tile(ti + 1);
         if (it < ng) {
-            // operands in the decode kernel's register layout
-            Regs R;
+            // K operands: lane (i, g) takes token 16 s + i, head-dim slots
+            // [32 k + 8 g, 32 k + 8 g + 8) of k-step k (the q operand's slots)
+            bf16x8 ka[KSTEPS][2];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
+            for (int k = 0; k < KSTEPS; ++k)
 #pragma unroll
-                for (int c = 0; c < Tile::KV4; ++c)
-                    R.kraw[s][c] = *reinterpret_cast<const uint4*>(
-                        lds_k(buf) + (16 * s + li) * ROW + lg * KB + 16 * c);
-            }
-            floatx4 sc[NT][2];
-            Tile::template qk_tiles<NT>(R, qv, sc);
+                for (int s = 0; s < 2; ++s)
+                    ka[k][s] = *reinterpret_cast<const bf16x8*>(lds_k(buf) + kq + 64 * k + 16 * LROW * s);
             // scales of the lane's score tokens 16 s + 4 lg + r
             float sk[2][4], sv[2][4];
 #pragma unroll
@@ -235,15 +306,28 @@ __global__ __launch_bounds__(256 * KG, SP ? 2 : (KG == 1 ? 3 : 1)) void prefill_
                 sk[s][0] = a.x; sk[s][1] = a.y; sk[s][2] = a.z; sk[s][3] = a.w;
                 sv[s][0] = c.x; sv[s][1] = c.y; sv[s][2] = c.z; sv[s][3] = c.w;
             }
+            // S = K q^T; the k-steps are the outer loop, so the 2 NT
+            // accumulation chains take turns
+            floatx4 sc[NT][2];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) sc[j][0] = sc[j][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < KSTEPS; ++k)
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int j = 0; j < NT; ++j)
+                        sc[j][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[k][s], qv[j][k], sc[j][s], 0, 0, 0);
 
             // ---- P' range of the tile (keys past the chunk have v_scale 0);
-            // the scales are >= 0, so their bit patterns order as integers
+            // the scales are >= 0, so their bit patterns order as integers;
+            // the range bookkeeping is wave-uniform (scalar)
             uint32_t svm = 0;
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) svm = max(svm, __float_as_uint(sv[s][r]));
-            svm = rows_max_u32(svm);
+            svm = __builtin_amdgcn_readfirstlane(rows_max_u32(svm));
             const int ef_t = max((int)(svm >> 23), 15);
             const int ef_new = max(ef_run, ef_t);
             const bool ef_up = ef_new > ef_run;
@@ -261,78 +345,117 @@ __global__ __launch_bounds__(256 * KG, SP ? 2 : (KG == 1 ? 3 : 1)) void prefill_
                 nv[0] = lds_nv(buf)[0];
                 nv[1] = lds_nv(buf)[1];
             }
-            const bool masked = (ti << 5) + 31 > wave_lim || (SP && (nv[0] < 16 || nv[1] < 16));
-            f16x8 pb[NT];
-            WaveState<DL>* sts[NT];
+            // key 16 s + 4 lg + r of the tile is visible to row tile j iff
+            // 16 s + r <= lim[j] - t0 - 4 lg (and, with selected blocks,
+            // 4 lg + r < nv[s])
+            auto visible = [&](int j, int s, int r) {
+                return 16 * s + r <= lim[j] - (ti << 5) - 4 * lg && (!SP || 4 * lg + r < nv[s]);
+            };
+            // x = score (log2 units) - running maximum, one rounding; an
+            // invisible key gets kNeg, whose exp2 is exactly 0
+            float x[NT][2][4];
+            bool need = ef_up;
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
-                float s2[2][4];
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) s2[s][r] = sc[j][s][r] * sk[s][r];
-                if (masked) {
-                    // key 16 s + 4 lg + r of the tile is visible iff
-                    // 16 s + r <= lim - t0 - 4 lg
-                    const int d = lim[j] - (ti << 5) - 4 * lg;
+                    for (int r = 0; r < 4; ++r) {
+                        x[j][s][r] = __builtin_fmaf(sc[j][s][r], sk[s][r], -st[j].m_run);
+                        if constexpr (MASKED) x[j][s][r] = visible(j, s, r) ? x[j][s][r] : kNeg;
+                    }
+                need = need | __any(max8_chain(x[j]) > kLazyMax);
+            }
+            // lazy maximum: a row tile's running maximum moves only when a
+            // score exceeds it by more than kLazyMax, so most tiles skip the
+            // rescale (one branch for all row tiles). m_run is the same in the
+            // four lanes of a row, so "some lane's scores exceed it" is "some
+            // row's scores exceed it". A row that saw no key yet has m_run =
+            // kNeg: its visible keys give x = 1e30 and take the branch.
+            if (need) {
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    if (!(__any(max8_chain(x[j]) > kLazyMax) || ef_up)) continue;
+                    float s2[2][4];
 #pragma unroll
                     for (int s = 0; s < 2; ++s)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            s2[s][r] = (16 * s + r <= d && (!SP || 4 * lg + r < nv[s])) ? s2[s][r] : kNeg;
-                }
-                // lazy maximum: the running maximum moves only when a score
-                // exceeds it by more than kLazyMax, so most tiles skip the rescale.
-                // m_run is the same in the four lanes of a row, so "some lane's
-                // scores exceed it" is "some row's scores exceed it": the row
-                // maximum across lanes is only needed when the branch is taken
-                const float ml = max8(s2);
-                if (__any(ml > st[j].m_run + kLazyMax) || ef_up) {
-                    const float m_new = fmax_fin(st[j].m_run, rows_max_fin(ml));
+                        for (int r = 0; r < 4; ++r) {
+                            s2[s][r] = sc[j][s][r] * sk[s][r];
+                            if constexpr (MASKED) s2[s][r] = visible(j, s, r) ? s2[s][r] : kNeg;
+                        }
+                    const float m_new = fmax_fin(st[j].m_run, rows_max_fin(max8_chain(s2)));
                     const float a = __builtin_amdgcn_exp2f(st[j].m_run - m_new);
                     const float f = a * fe;
 #pragma unroll
                     for (int n = 0; n < DL; ++n) st[j].acc[n] *= f;
                     st[j].l_run *= a;
                     st[j].m_run = m_new;
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            x[j][s][r] = __builtin_fmaf(sc[j][s][r], sk[s][r], -m_new);
+                            if constexpr (MASKED) x[j][s][r] = visible(j, s, r) ? x[j][s][r] : kNeg;
+                        }
                 }
+            }
+            // P' of row tile j in fp16 (the PV B operand); l accumulates p
+            auto make_p = [&](int j) {
                 uint32_t pw[4];
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     float pr[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        // a masked score gives exp2(kNeg - m) = 0: every row sees
-                        // key 0 in the first tile, so m is a real score throughout
-                        // (with selected blocks a row may have seen no key yet, so
-                        // masked positions are zeroed explicitly)
-                        float e = __builtin_amdgcn_exp2f(s2[s][r] - st[j].m_run);
-                        if ((SP || KG > 1) && masked) e = s2[s][r] == kNeg ? 0.f : e;
+                        const float e = __builtin_amdgcn_exp2f(x[j][s][r]);
                         st[j].l_run += e;
                         pr[r] = e * sv[s][r];
                     }
                     pw[2 * s] = pack_f16x2(pr[0], pr[1]);
                     pw[2 * s + 1] = pack_f16x2(pr[2], pr[3]);
                 }
-                pb[j] = __builtin_bit_cast(f16x8, pw);
-                sts[j] = &st[j];
-            }
-            // V operands read only now: not held in registers across the softmax
+                return __builtin_bit_cast(f16x8, pw);
+            };
+            // O^T += V^T P'^T: n-tile n of lane (i, g) is head-dim column
+            // 16 n + i over the lane's 8 keys 4 g + r, 16 + 4 g + r (P's order)
+            // V operands read once and kept; row tile j's PV MFMAs are
+            // issued between the vector work of row tile j + 1's P' (and
+            // the last row tile's between the loader's conversions), so
+            // the matrix cores and the vector ALU work at the same time
+            f16x8 va[DL];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint8_t* src = lds_v(buf) + (16 * (e >> 2) + 4 * lg + (e & 3)) * ROW + li * DL;
-                if constexpr (DL == 8)
-                    R.vraw[e] = *reinterpret_cast<const uint2*>(src);
-                else
-                    R.vraw[e] = *reinterpret_cast<const uint32_t*>(src);
+            for (int n = 0; n < DL; ++n) va[n] = read_v_operand(lds_v(buf) + vq + 32 * n, 16 * LROW);
+            f16x8 pb = make_p(0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const f16x8 pj = pb;
+                if (j + 1 < NT) pb = make_p(j + 1);
+#pragma unroll
+                for (int n = 0; n < DL; ++n)
+                    st[j].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[n], pj, st[j].acc[n], 0, 0, 0);
             }
-            Tile::template pv_tiles<NT>(R, pb, sts);
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int n = 0; n < DL; ++n) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                }
         }
-        if (loader && it + 1 < ng) store_tile(buf ^ 1);
+        if (loader && next) store_tile(buf ^ 1);
         __syncthreads();
+    };
+    int it = 0;
+    if constexpr (!SP) {
+        // tiles every row of the block sees whole: keys up to P + q0
+        const int n_clean = min(max(((P + q0 + 1) >> 5) - tg0, 0), ng);
+        for (; it < n_clean; ++it) step(it, BoolC<false>{});
     }
+    for (; it < nmax; ++it) step(it, BoolC<true>{});
 
-    // normalized output of row li of each tile: dims [DL*4 lg, DL*4 lg + DL*4)
+    // normalized output of row li of each tile: dims 16 n + 4 lg + r
     const float un = pow2i(max(ef_run - 141 + kLazyMax, -126));
     if constexpr (KG > 1) {
 #pragma unroll
@@ -393,30 +516,17 @@ __global__ __launch_bounds__(256 * KG, SP ? 2 : (KG == 1 ? 3 : 1)) void prefill_
         // is their summed weight
         const float inv = KG == 1 ? (l_sum > 0.f ? un / l_sum : 0.f) : 1.0f / st[j].l_run;
         const int64_t off = (int64_t)b * p.out_stride_b + (int64_t)tq[j] * p.out_stride_tok +
-                            (int64_t)hq * p.out_stride_head + (DL * 4) * lg;
+                            (int64_t)hq * p.out_stride_head + 4 * lg;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float vals[DL];
-#pragma unroll
-            for (int n = 0; n < DL; ++n) vals[n] = st[j].acc[n][r] * inv;
+        for (int n = 0; n < DL; ++n) {
+            const floatx4 v = st[j].acc[n] * inv;
             if (p.out_fp32) {
-                float* o = static_cast<float*>(p.out) + off + DL * r;
-#pragma unroll
-                for (int c = 0; c < DL / 4; ++c)
-                    *reinterpret_cast<float4*>(o + 4 * c) =
-                        make_float4(vals[4 * c], vals[4 * c + 1], vals[4 * c + 2], vals[4 * c + 3]);
+                *reinterpret_cast<float4*>(static_cast<float*>(p.out) + off + 16 * n) =
+                    make_float4(v[0], v[1], v[2], v[3]);
             } else {
-                uint16_t* o = static_cast<uint16_t*>(p.out) + off + DL * r;
-                uint32_t w[DL / 2];
-#pragma unroll
-                for (int n = 0; n < DL / 2; ++n) {
-                    const bf16x2 v2 = {(__bf16)vals[2 * n], (__bf16)vals[2 * n + 1]};
-                    w[n] = __builtin_bit_cast(uint32_t, v2);
-                }
-                if constexpr (DL == 8)
-                    *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
-                else
-                    *reinterpret_cast<uint2*>(o) = make_uint2(w[0], w[1]);
+                const bf16x2 lo = {(__bf16)v[0], (__bf16)v[1]}, hi = {(__bf16)v[2], (__bf16)v[3]};
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off + 16 * n) =
+                    make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
             }
         }
     }
@@ -431,23 +541,22 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stre
     const bool sp = p.block_valid != nullptr;
     const dim3 grid((unsigned)wgs);
     constexpr int NT = kPrefillRowTiles;
-    // Dense head_dim 128 runs 3 waves per SIMD. With at most 2 query blocks
-    // per CU that many waves only exist if each block's keys are split:
-    // three key groups per block (12 waves), merged by log-sum-exp. With
-    // more blocks, one group of 4 waves per block (the 12-wave barrier of
-    // every tile costs more than the split gains).
+    // Every instance runs 2 waves per SIMD (2 query blocks of 4 waves per
+    // CU). With at most one query block per CU, dense head_dim 128 splits
+    // each block's keys into two key groups (one 8-wave workgroup per CU),
+    // merged by log-sum-exp, so the CU still runs 8 waves.
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 0;
-    const bool groups = wgs <= 2 * (int64_t)cus;
+    const bool groups = wgs <= (int64_t)cus;
     if (head_dim == 128) {
         if (sp) {
             if (pow2) hipLaunchKernelGGL((prefill_kernel<128, true, NT, true, 1>), grid, dim3(256), 0, stream, p);
             else hipLaunchKernelGGL((prefill_kernel<128, false, NT, true, 1>), grid, dim3(256), 0, stream, p);
         } else if (groups) {
-            if (pow2) hipLaunchKernelGGL((prefill_kernel<128, true, NT, false, 3>), grid, dim3(768), 0, stream, p);
-            else hipLaunchKernelGGL((prefill_kernel<128, false, NT, false, 3>), grid, dim3(768), 0, stream, p);
+            if (pow2) hipLaunchKernelGGL((prefill_kernel<128, true, NT, false, 2>), grid, dim3(512), 0, stream, p);
+            else hipLaunchKernelGGL((prefill_kernel<128, false, NT, false, 2>), grid, dim3(512), 0, stream, p);
         } else {
             if (pow2) hipLaunchKernelGGL((prefill_kernel<128, true, NT, false, 1>), grid, dim3(256), 0, stream, p);
             else hipLaunchKernelGGL((prefill_kernel<128, false, NT, false, 1>), grid, dim3(256), 0, stream, p);

@@ -540,9 +540,9 @@ int fp8kv_paged_decode_partials_unscaled(
  * block_size a multiple of 16. No workspace.
  * Launch shape: one workgroup per block of query rows up to max_q, so a
  * max_q near the longest chunk avoids workgroups with no rows; when there
- * are few blocks per compute unit (head_dim 128) each block's keys are
- * split over three groups of waves and merged (same result within the
- * floating-point bar; the split rounds differently).
+ * are at most as many blocks as compute units (head_dim 128) each block's
+ * keys are split over two groups of waves and merged (same result within
+ * the floating-point bar; the split rounds differently).
  * Errors: E_NULL, E_SHAPE, E_STRIDE, E_ALIGN, E_UNSUPPORTED, E_LAUNCH.
  */
 int fp8kv_prefill_attn_fp8(

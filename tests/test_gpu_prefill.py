@@ -66,9 +66,9 @@ def test_chunk_matches_oracle(lens, C, Hq, Hkv, D, bs):
 
 def test_many_query_blocks_one_key_group():
     """Enough query blocks (20 requests x 8 KV heads x 5 blocks of 32
-    tokens = 800 workgroups, more than 2 per CU on a 256-CU GPU) that each
+    tokens = 800 workgroups, more than one per CU on a 256-CU GPU) that each
     block's keys stay in one group of 4 waves; the small chunks above run
-    three key groups per block, merged by log-sum-exp. Both meet the bar."""
+    two key groups per block, merged by log-sum-exp. Both meet the bar."""
     lens = [300 + 37 * i for i in range(20)]
     case = synth.decode_case(lens, 32, 8, 128, 16, rows=160, seed=160)
     log(f"prefill one key group: {len(lens)} requests, C=160")

@@ -6,7 +6,7 @@ Bar: as the dense prefill -- fp32 output within max-abs 2e-3 and rel-L2
 1e-3, bf16 output equal to the RNE of the same kernel's fp32 output. A
 selection of every block with full counts walks the same keys as the dense
 prefill; the dense kernel (head_dim 128) splits each query block's keys
-into three groups merged by log-sum-exp, so the two agree within the same
+into two groups merged by log-sum-exp, so the two agree within the same
 bar rather than bit for bit."""
 import numpy as np
 import pytest
