@@ -46,9 +46,9 @@
 // Key groups (KG = 2, dense head_dim 128, chosen by the host when there are
 // at most as many query blocks as CUs): the workgroup is 2 groups of 4 waves;
 // group g walks tiles [g T / 2, (g + 1) T / 2) of the block's T key tiles
-// with its own LDS buffers, all 8 waves meeting at each tile's barrier, and
-// the groups' normalized rows are merged into group 0 by their log2 sum-exp
-// through LDS. A row may see no key in a group's tiles (its masked
+// with its own LDS buffers (four: its loader runs two tiles ahead), all 8
+// waves meeting at a barrier every second tile, and the groups' normalized
+// rows are merged into group 0 by their log2 sum-exp through LDS. A row may see no key in a group's tiles (its masked
 // probabilities are zero and its sum-exp is kNeg, weight 0).
 // The prefill kernel keeps a row's running maximum until a tile's scores
 // exceed it by more than kLazyMax (log2 units), so p = exp2(s - m) stays
@@ -115,9 +115,17 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void prefill_kernel(PrefillParams
     // stores, the K operand reads, the transposing V operand reads), and the
     // operand addresses of a lane differ only by immediate offsets. With KG > 1
     // the same bytes later hold the groups' partial results for the merge.
+    // tile buffers: with one key group the loader stores tile t + 1 while
+    // tile t is read (two buffers, a barrier every tile); with key groups it
+    // stores tile t + 2 while tiles t and t + 1 are read (four buffers, a
+    // barrier every second tile: the 8 waves of the workgroup then wait for
+    // each other half as often; one 4-wave group per workgroup is faster with
+    // a barrier every tile)
+    constexpr int AHEAD = KG > 1 ? 2 : 1;
+    constexpr int NBUF = 2 * AHEAD;
     constexpr int KT_BYTES = 32 * LROW;
     constexpr int VT_BYTES = 32 * LROW;
-    constexpr int TILE_BYTES = 2 * (KT_BYTES + VT_BYTES) + 2 * 2 * 32 * 4 + 16;
+    constexpr int TILE_BYTES = NBUF * (KT_BYTES + VT_BYTES + 2 * 32 * 4 + 16);
     constexpr int MERGE_BYTES = KG > 1 ? 4 * 64 * NT * (4 * DL + 2) * 4 : 0;
     constexpr int LDS_BYTES = KG * TILE_BYTES > MERGE_BYTES ? KG * TILE_BYTES : MERGE_BYTES;
     __shared__ __align__(16) uint8_t lds_raw[LDS_BYTES];
@@ -130,12 +138,12 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void prefill_kernel(PrefillParams
     const int li = lane & 15, lg = lane >> 4;
     uint8_t* const lds_g = lds_raw + kg * TILE_BYTES;
     auto lds_k = [&](int buf) { return lds_g + buf * KT_BYTES; };
-    auto lds_v = [&](int buf) { return lds_g + 2 * KT_BYTES + buf * VT_BYTES; };
+    auto lds_v = [&](int buf) { return lds_g + NBUF * KT_BYTES + buf * VT_BYTES; };
     auto lds_s = [&](int buf, int which) {
-        return reinterpret_cast<float*>(lds_g + 2 * (KT_BYTES + VT_BYTES)) + (2 * buf + which) * 32;
+        return reinterpret_cast<float*>(lds_g + NBUF * (KT_BYTES + VT_BYTES)) + (2 * buf + which) * 32;
     };
     auto lds_nv = [&](int buf) {
-        return reinterpret_cast<int*>(lds_g + 2 * (KT_BYTES + VT_BYTES) + 2 * 2 * 32 * 4) + 2 * buf;
+        return reinterpret_cast<int*>(lds_g + NBUF * (KT_BYTES + VT_BYTES + 2 * 32 * 4)) + 2 * buf;
     };
 
     // XCD-contiguous numbering, deepest query block first within a group
@@ -272,8 +280,11 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void prefill_kernel(PrefillParams
     };
 
     if (loader && ng > 0) {
-        load_tile(tg0);
-        store_tile(0);
+#pragma unroll
+        for (int a = 0; a < AHEAD; ++a) {
+            load_tile(tg0 + a);
+            store_tile(a);
+        }
     }
     __syncthreads();
     // One tile step; MASKED: the visibility test of every score (causal, and
@@ -282,12 +293,14 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void prefill_kernel(PrefillParams
     auto step = [&](int it, auto mask_c) {
         constexpr bool MASKED = decltype(mask_c)::value;
         const int ti = tg0 + it;
-        const int buf = it & 1;
+        // tile it in buffer it % NBUF; the loader fills buffer (it + AHEAD) %
+        // NBUF, whose last readers (step it - AHEAD) passed a barrier since
+        const int buf = it & (NBUF - 1);
         // one key group: the step after the last loads and stores a tile
         // with no keys (zero-length buffer ranges), which keeps the loader's
         // work in the same block as the PV MFMAs
-        const bool next = KG == 1 || it + 1 < ng;
-        if (loader && next) load_tile(ti + 1);
+        const bool next = KG == 1 || it + AHEAD < ng;
+        if (loader && next) load_tile(ti + AHEAD);
         if (it < ng) {
             // K operands: lane (i, g) takes token 16 s + i, head-dim slots
             // [32 k + 8 g, 32 k + 8 g + 8) of k-step k (the q operand's slots)
@@ -444,8 +457,11 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void prefill_kernel(PrefillParams
                     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
                 }
         }
-        if (loader && next) store_tile(buf ^ 1);
-        __syncthreads();
+        if (loader && next) store_tile((it + AHEAD) & (NBUF - 1));
+        // AHEAD = 2: tile it + 2 was stored in this step or the previous one;
+        // a barrier after every odd step makes it visible before step it + 2
+        // and keeps step it + 2's store behind step it's readers
+        if (AHEAD == 1 || (it & 1)) __syncthreads();
     };
     int it = 0;
     if constexpr (!SP) {
