@@ -141,3 +141,36 @@ def test_prefill_workload_full_size_sampled():
                                    case.layout.block_size, case.softmax_scale, rows=rows)
     got = out[0].reshape(-1, 128)[rows].cpu().numpy()
     assert_attn_close(got, ref, "prefill sampled")
+
+
+def test_1k_chunk_two_key_groups_full_size_sampled():
+    """The last 1024 tokens of the prefill workload's 32,768-token request
+    as the chunk (the benchmark's 1024-row views of q and out): 256 query
+    blocks, so each block's keys run in two key groups of about 500 tiles,
+    a barrier every second tile, merged by log-sum-exp; the oracle
+    recomputes 64 sampled rows."""
+    case = synth.prefill_attn_workload(seed=71, device=DEV)
+    dc = cache_case(case, DEV)
+    L = case.layout
+    C1 = 1024
+    q1 = case.q[:, :C1]
+    out = torch.full(q1.shape, 7.0, device=DEV)
+    ql = torch.full((1,), C1, dtype=torch.int32)
+    fk.prefill_attn_fp8(q1.to(DEV), dc.k_cache, dc.v_cache, dc.k_scale, dc.v_scale,
+                        L.block_tables.to(DEV), L.context_lens.to(DEV), ql.to(DEV),
+                        num_kv_heads=case.num_kv_heads, block_size=L.block_size,
+                        softmax_scale=case.softmax_scale,
+                        max_context=L.block_size * L.block_tables.shape[1], out=out)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(out))
+    host, bt, cl = compact_host_cache(case, dc, [0])
+    g = torch.Generator().manual_seed(73)
+    Hq = q1.shape[2]
+    toks = torch.cat([torch.tensor([0, 1, 31, 32, C1 - 1]), torch.randint(0, C1, (11,), generator=g)])
+    heads = torch.randint(0, Hq, (4,), generator=g)
+    rows = [(int(t) * Hq + int(hh)) for t in toks for hh in heads]
+    log(f"prefill 1024-token chunk, {len(rows)} sampled rows")
+    ref = oracle.paged_decode_attn(bf16_bits(q1.contiguous()), *host, bt, cl, case.num_kv_heads,
+                                   L.block_size, case.softmax_scale, rows=rows)
+    got = out[0].reshape(-1, 128)[rows].cpu().numpy()
+    assert_attn_close(got, ref, "1024-token chunk sampled")
