@@ -1,7 +1,8 @@
-// attn_tile.h -- the tile math shared by the decode split kernel
-// (paged_decode.hip) and the chunked-prefill kernel (prefill_attn.hip):
-// E4M3 widening, the QK^T and PV MFMA tiles, the online softmax with the
-// key scale on the score and the value scale folded into P.
+// attn_tile.h -- the tile math of the decode split kernel
+// (paged_decode.hip): E4M3 widening, the QK^T and PV MFMA tiles, the
+// online softmax with the key scale on the score and the value scale
+// folded into P; and the softmax state and lane reductions the
+// chunked-prefill kernel (prefill_attn.hip) shares with it.
 //
 // Per 32-token tile (two 16-token halves s = 0, 1), lane l = 16*g + i:
 //   QK^T  v_mfma_f32_16x16x32_bf16, A = K codes (token i, 8 head-dim slots
@@ -61,10 +62,6 @@ __device__ __forceinline__ float rows_sum(float v) {
 // agree (up to the sign of a zero maximum, which exp2 does not see).
 __device__ __forceinline__ float fmax_fin(float a, float b) {
     return __builtin_elementwise_maximum(a, b);
-}
-__device__ __forceinline__ float max8(const float (&v)[2][4]) {
-    return fmax_fin(fmax_fin(fmax_fin(v[0][0], v[0][1]), fmax_fin(v[0][2], v[0][3])),
-                    fmax_fin(fmax_fin(v[1][0], v[1][1]), fmax_fin(v[1][2], v[1][3])));
 }
 __device__ __forceinline__ float rows_max_fin(float v) {
     auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -278,30 +275,6 @@ struct DecodeTile {
             for (int k = 0; k < KSTEPS; ++k) {
                 const bf16x8 a = widen_k(kw[2 * k], kw[2 * k + 1]);
                 sc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[k], sc[s], 0, 0, 0);
-            }
-        }
-    }
-
-    // The same for NT 16-row tiles of queries: each K operand is widened
-    // once and feeds every tile's MFMA chain. The k-steps are the outer loop,
-    // so the 2 NT accumulation chains (tiles x halves) take turns and no
-    // MFMA waits for the previous one of its own chain.
-    template <int NT>
-    static __device__ __forceinline__ void qk_tiles(const Regs& R, const bf16x8 (&qv)[NT][KSTEPS],
-                                                    floatx4 (&sc)[NT][2]) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int j = 0; j < NT; ++j) sc[j][s] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < KSTEPS; ++k) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const uint32_t* kw = reinterpret_cast<const uint32_t*>(R.kraw[s]);
-                const bf16x8 a = widen_k(kw[2 * k], kw[2 * k + 1]);
-#pragma unroll
-                for (int j = 0; j < NT; ++j)
-                    sc[j][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[j][k], sc[j][s], 0, 0, 0);
             }
         }
     }

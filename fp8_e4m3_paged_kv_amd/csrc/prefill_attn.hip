@@ -105,22 +105,23 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void prefill_kernel(PrefillParams
     constexpr int LOAD_WAVES = 32 / TPL;
     static_assert(D <= 128, "a widened row fits the 256 bytes of data of an LDS row");
     static_assert(TPL <= 16 && 16 % TPL == 0, "a loader wave stays inside one half");
-    // LDS of key group g, per buffer: the tile's keys widened to bf16 and its
-    // values widened to fp16, one 288-byte row per token (head-dim columns
-    // 8 c .. 8 c + 7 in 16-byte chunk c, chunks permuted per row: K chunk c of
-    // token T at c ^ ((T >> 2) & 3), V chunk c at c ^ ((T >> 2) & 1)); then
-    // scales [2][k_scale * score scale | v_scale][32] and selected-block key
-    // counts [2][half]. The row pitch and permutations keep every LDS access
-    // of the loop free of bank conflicts on gfx950 (the loader's 16-byte
-    // stores, the K operand reads, the transposing V operand reads), and the
-    // operand addresses of a lane differ only by immediate offsets. With KG > 1
-    // the same bytes later hold the groups' partial results for the merge.
-    // tile buffers: with one key group the loader stores tile t + 1 while
+    // LDS of key group g: NBUF tile buffers of the tile's keys widened to
+    // bf16, then NBUF of its values widened to fp16, one 288-byte row per
+    // token (head-dim columns 8 c .. 8 c + 7 in 16-byte chunk c, chunks
+    // permuted per row: K chunk c of token T at c ^ ((T >> 2) & 3), V chunk c
+    // at c ^ ((T >> 2) & 1)); then scales [NBUF][k_scale * score scale |
+    // v_scale][32] and selected-block key counts [NBUF][half]. The row pitch
+    // and permutations keep every LDS access of the loop free of bank
+    // conflicts on gfx950 (the loader's 16-byte stores, the K operand reads,
+    // the transposing V operand reads), and the operand addresses of a lane
+    // differ only by immediate offsets. With KG > 1 the same bytes later hold
+    // the groups' partial results for the merge.
+    // Tile buffers: with one key group the loader stores tile t + 1 while
     // tile t is read (two buffers, a barrier every tile); with key groups it
     // stores tile t + 2 while tiles t and t + 1 are read (four buffers, a
     // barrier every second tile: the 8 waves of the workgroup then wait for
     // each other half as often; one 4-wave group per workgroup is faster with
-    // a barrier every tile)
+    // a barrier every tile).
     constexpr int AHEAD = KG > 1 ? 2 : 1;
     constexpr int NBUF = 2 * AHEAD;
     constexpr int KT_BYTES = 32 * LROW;
