@@ -278,6 +278,13 @@ __device__ __forceinline__ float relu(float x) {
     return __int_as_float(max(__float_as_int(x), 0));
 }
 
+// A tile's parity within its key chunk as a type: the loops are unrolled so
+// that every step's parity, and so its store count, is known at compile time.
+template <bool B>
+struct Parity {
+    static constexpr bool value = B;
+};
+
 // Byte offset that every store range check rejects (request spans are
 // below 2^30 bytes, so the sum of two such offsets is rejected too).
 constexpr uint32_t kDropped = 0x40000000u;
@@ -429,7 +436,7 @@ __global__ __launch_bounds__(256, 2) void index_score_kernel(IndexScoreParams p)
     // store) or (g & 2) | 1 (second store), keys t + 16 (g & 1) + i.
     const uint32_t lb_x = (uint32_t)(row0 + S::lane_row(lg & 2)) * s4;
     const uint32_t lb_y = (uint32_t)(row0 + S::lane_row((lg & 2) | 1)) * s4;
-    float hold[2][OS];
+    float hold[2][OS] = {};
 
     floatx4 acc0[NH], acc1[NH];
     auto mfma_half = [&](const bf16x8 (&kb)[4], int c, floatx4 (&acc)[NH]) {
@@ -443,7 +450,7 @@ __global__ __launch_bounds__(256, 2) void index_score_kernel(IndexScoreParams p)
     };
     // the ReLU and weights of the lane's (row, head) pairs, reduced to one
     // value per slot (one row per lane group), then stored
-    auto epilogue = [&](const floatx4 (&acc)[NH], int c, float ks, bool odd, uint32_t ocol) {
+    auto epilogue = [&](const floatx4 (&acc)[NH], int c, float ks, auto odd_c, uint32_t ocol) {
         float v[OS];
         if constexpr (HP >= 4) {
             float s[NH];
@@ -476,7 +483,7 @@ __global__ __launch_bounds__(256, 2) void index_score_kernel(IndexScoreParams p)
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = relu(acc[0][r]) * wr[r];
         }
-        if (!odd) {
+        if constexpr (!decltype(odd_c)::value) {
 #pragma unroll
             for (int sl = 0; sl < OS; ++sl) hold[c][sl] = v[sl] * ks;
         } else {
@@ -505,68 +512,58 @@ __global__ __launch_bounds__(256, 2) void index_score_kernel(IndexScoreParams p)
     // one step: tile t's half-0 MFMAs overlap the previous tile's half-1
     // epilogue, tile t's half-1 MFMAs overlap its own half-0 epilogue; the
     // epilogue of an even tile (from the chunk's start) holds its values, that
-    // of an odd tile stores the pair
+    // of an odd tile stores the pair. The first step's previous tile is odd
+    // and stores nothing (its column is the dropped offset).
     float ks_prev = 0.f;
-    bool odd_prev = false;
     uint32_t ocol_prev = kDropped;
-    auto step = [&](const KeyTile<FMT>& kt, int t) {
+    auto step = [&](const KeyTile<FMT>& kt, int t, auto odd_c) {
+        constexpr bool odd = decltype(odd_c)::value;
         bf16x8 kb[4];
         kt.widen(kb);
         const float ks = FMT == kKeysE4M3 ? kt.kscale : 1.0f;
-        const bool odd = ((ROT ? t : t - n_begin) >> 4) & 1;
         const uint32_t ocol = colp(t - 16);
         mfma_half(kb, 0, acc0);
-        epilogue(acc1, 1, ks_prev, odd_prev, ocol_prev);
+        epilogue(acc1, 1, ks_prev, Parity<!odd>{}, ocol_prev);
         mfma_half(kb, 1, acc1);
-        epilogue(acc0, 0, ks, odd, ocol);
+        epilogue(acc0, 0, ks, odd_c, ocol);
         ks_prev = ks;
-        odd_prev = odd;
         ocol_prev = ocol;
+        __builtin_amdgcn_sched_barrier(0);
     };
 #pragma unroll
     for (int t = 0; t < NH; ++t) acc1[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     // tiles n_begin, n_begin + 16, ... (with ROT virtual tiles 0, 16, ...)
-    // and at least two more (their own
-    // stores all dropped) to drain the pipeline and complete the last pair;
-    // loads run two tiles ahead in three buffers
+    // and at least two more (their own stores all dropped) to drain the
+    // pipeline and complete the last pair. Loads run two tiles ahead in three
+    // buffers; the loop body is six tiles (buffer and parity both repeat),
+    // then up to two three-tile bodies finish the chunk.
     KeyTile<FMT> ta, tb, tc;
-    if constexpr (ROT) {
-        offs(0);
-        ta.load(krs, srs, koff, soff);
-        offs(16);
-        tb.load(krs, srs, koff, soff);
-        for (int v = 0; v < span32 + 32; v += 48) {
-            offs(v + 32);
-            tc.load(krs, srs, koff, soff);
-            step(ta, v);
-            offs(v + 48);
-            ta.load(krs, srs, koff, soff);
-            step(tb, v + 16);
-            offs(v + 64);
-            tb.load(krs, srs, koff, soff);
-            step(tc, v + 32);
-        }
-        return;
-    }
-    ta.load(krs, srs, koff, soff);
-    koff += kstep;
-    soff += sstep;
-    tb.load(krs, srs, koff, soff);
-    for (int t = n_begin; t < n_end + 32; t += 48) {
-        koff += kstep;
-        soff += sstep;
+    auto next = [&](int v) { offs(ROT ? v : v - n_begin); };
+    auto body3 = [&](int v, auto p0) {
+        constexpr bool e = decltype(p0)::value;
+        next(v + 32);
         tc.load(krs, srs, koff, soff);
-        step(ta, t);
-        koff += kstep;
-        soff += sstep;
+        step(ta, v, p0);
+        next(v + 48);
         ta.load(krs, srs, koff, soff);
-        step(tb, t + 16);
-        koff += kstep;
-        soff += sstep;
+        step(tb, v + 16, Parity<!e>{});
+        next(v + 64);
         tb.load(krs, srs, koff, soff);
-        step(tc, t + 32);
+        step(tc, v + 32, p0);
+    };
+    const int first = ROT ? 0 : n_begin;
+    const int last = ROT ? span32 + 32 : n_end + 32;   // steps run while v < last
+    offs(0);
+    ta.load(krs, srs, koff, soff);
+    next(first + 16);
+    tb.load(krs, srs, koff, soff);
+    int v = first;
+    for (; v + 48 < last; v += 96) {
+        body3(v, Parity<false>{});
+        body3(v + 48, Parity<true>{});
     }
+    if (v < last) body3(v, Parity<false>{});
 }
 
 template <int FMT, int HP>
