@@ -685,7 +685,10 @@ def unscaled_decode(torch, fk, synth, dev, stream, case, q, bt, cl, reps=20):
 def probes_lib():
     """The benchmark's probe kernels (libfp8kv_probes.so, built beside the
     cache library): fp8kv_probe(kind, a, b, dst, bytes, stream) with kind 0
-    read, 1 copy, 2 read a and b / write dst (2:1), 3 write, 4 empty."""
+    read, 1 copy, 2 read a and b / write dst (2:1), 3 write, 4 empty, 5-7
+    read a's 2 KiB blocks in the order of the int32 ids b (5: one block per
+    wave, one pass; 6, 7: one wave per SIMD, 4 or 8 blocks per load
+    group)."""
     import ctypes
     from fp8_e4m3_paged_kv_amd import build as hipbuild
     if not os.path.exists(hipbuild.PROBES_LIB):
@@ -709,25 +712,37 @@ def hbm_ceilings(torch, dev, stream, gib=2, reps=10):
     """What plain streaming kernels reach on this GPU (the probe library's
     16-byte streams over 2 GiB buffers, non-temporal loads and ordinary
     stores: read, copy, 2:1 read:write, write), and what the library's own
-    copy and sum kernels reach, for reference."""
+    copy and sum kernels reach, for reference. The paged reads fetch the
+    same 2 GiB as 2 KiB blocks (one KV head's codes of a 16-token block) in
+    a random order, as the decode kernels walk the cache: in one pass
+    (`paged_read`), and by one wave per SIMD in groups of 8 or 16 KiB, the
+    next group's loads issued before the current one is consumed
+    (`paged_read_1wave_8k` / `_16k`; 8 KiB is one decode tile of K and V
+    codes, and the decode kernel also loads one tile ahead)."""
     log("HBM ceilings (probe streams, library copy and read kernels)...")
     L = probes_lib()
     n = gib << 30
     a = torch.ones(n // 8, dtype=torch.int64, device=dev)
     b = torch.ones_like(a)
     d = torch.empty_like(a)
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    ids = torch.randperm(n // 2048, generator=g, device=dev).to(torch.int32)
     res = {}
     for name, fn, moved in (
             ("read", lambda: probe(L, stream, 0, a=a, d=d, nbytes=n), n),
             ("copy", lambda: probe(L, stream, 1, a=a, d=d, nbytes=n), 2 * n),
             ("read2_write1", lambda: probe(L, stream, 2, a=a, b=b, d=d, nbytes=n), 3 * n),
             ("write", lambda: probe(L, stream, 3, d=d, nbytes=n), n),
+            ("paged_read", lambda: probe(L, stream, 5, a=a, b=ids, d=d, nbytes=n), n),
+            ("paged_read_1wave_8k", lambda: probe(L, stream, 6, a=a, b=ids, d=d, nbytes=n), n),
+            ("paged_read_1wave_16k", lambda: probe(L, stream, 7, a=a, b=ids, d=d, nbytes=n), n),
             ("torch_copy", lambda: d.copy_(a), 2 * n),
             ("torch_sum", lambda: a.sum(), n)):
         settle(fn, 0.1)
         ms = sorted(time_events(fn, reps, stream))
         res[f"hbm_{name}_GBps"] = round(moved / (ms[len(ms) // 2] * 1e-3) / 1e9, 1)
-    del a, b, d
+    del a, b, d, ids
     torch.cuda.empty_cache()
     return res
 

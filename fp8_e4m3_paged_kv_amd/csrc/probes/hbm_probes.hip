@@ -8,6 +8,13 @@
 //   kind 2  2:1:    dst = a ^ b, a and b `bytes` each, dst `bytes`
 //   kind 3  write:  dst = pattern                (write only)
 //   kind 4  empty:  a kernel that does nothing
+//   kind 5  paged read: sum of the 2 KiB blocks of `a` in the order of the
+//           int32 block ids `b` (bytes / 2048 of them; a 16-token block of
+//           one KV head's 128-byte code rows), one block per wave, one pass
+//   kind 6, 7  the same blocks read by one wave per SIMD, each wave walking
+//           its share of the ids in groups of U = 4 or 8 blocks (8 or 16
+//           KiB: U = 4 is one 32-token tile of K and V codes), the next
+//           group's loads issued before the current group is consumed
 // Every thread moves 2 x 16 bytes: loads carry the non-temporal hint, stores
 // are ordinary; the grid covers the buffer once (no grid-stride loop), so
 // each wave's loads and stores are 1 KiB contiguous. Of the shapes measured
@@ -95,6 +102,71 @@ __global__ __launch_bounds__(kThreads) void probe_write(u32x4* d, size_t n) {
 
 __global__ void probe_empty() {}
 
+// one 2 KiB block per wave; ids are clamped to the buffer's blocks
+__global__ __launch_bounds__(kThreads) void probe_paged_read(const u32x4* a, const int32_t* ids,
+                                                             uint32_t nblk, uint32_t* sink) {
+    const uint32_t w = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    u32x4 acc = {0, 0, 0, 0};
+    if (w < nblk) {
+        const uint32_t id = min((uint32_t)ids[w], nblk - 1);
+        const u32x4* q = a + (size_t)id * 128 + lane;
+        acc = __builtin_nontemporal_load(q) ^ __builtin_nontemporal_load(q + 64);
+    }
+    if ((acc.x & acc.y & acc.z & acc.w) == 0xFFFFFFFFu) sink[0] = acc.x;
+}
+
+template <int U>
+struct BlockGroup {
+    u32x4 v[U][2];
+    __device__ __forceinline__ void load(const u32x4* a, const int32_t* ids, uint32_t i, uint32_t b1,
+                                         uint32_t nblk, int lane) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t id = min((uint32_t)ids[min(i + u, b1 - 1)], nblk - 1);
+            const u32x4* q = a + (size_t)id * 128 + lane;
+            v[u][0] = __builtin_nontemporal_load(q);
+            v[u][1] = __builtin_nontemporal_load(q + 64);
+        }
+    }
+    __device__ __forceinline__ void consume(u32x4& acc) const {
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1];
+    }
+};
+
+// one wave per SIMD; the wave's share of the ids in groups of U blocks,
+// the next group's loads issued before the current group is consumed (the
+// decode kernel's one-tile-ahead pipeline without its arithmetic)
+template <int U>
+__global__ __launch_bounds__(kThreads) void probe_paged_read_persistent(const u32x4* a,
+                                                                        const int32_t* ids,
+                                                                        uint32_t nblk,
+                                                                        uint32_t* sink) {
+    const uint32_t waves = gridDim.x * (kThreads / 64);
+    const uint32_t w = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const uint32_t per = (nblk + waves - 1) / waves;
+    const uint32_t b0 = min(w * per, nblk), b1 = min(b0 + per, nblk);
+    u32x4 acc = {0, 0, 0, 0};
+    if (b0 < b1) {
+        BlockGroup<U> g0, g1;
+        g0.load(a, ids, b0, b1, nblk, lane);
+        uint32_t i = b0;
+        for (;;) {
+            if (i + U >= b1) { g0.consume(acc); break; }
+            g1.load(a, ids, i + U, b1, nblk, lane);
+            g0.consume(acc);
+            i += U;
+            if (i + U >= b1) { g1.consume(acc); break; }
+            g0.load(a, ids, i + U, b1, nblk, lane);
+            g1.consume(acc);
+            i += U;
+        }
+    }
+    if ((acc.x & acc.y & acc.z & acc.w) == 0xFFFFFFFFu) sink[0] = acc.x;
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,6 +181,31 @@ int fp8kv_probe(int kind, const void* a, const void* b, void* dst, size_t bytes,
         return hipGetLastError() == hipSuccess ? 0 : -2;
     }
     if (bytes % 16 != 0 || bytes == 0) return -1;
+    if (kind >= 5 && kind <= 7) {
+        // b: bytes / 2048 int32 block ids
+        if (!a || !b || !dst || bytes % 2048 != 0 || bytes / 2048 > 0x7FFFFFFFu) return -1;
+        const uint32_t nblk = (uint32_t)(bytes / 2048);
+        const int32_t* ids = static_cast<const int32_t*>(b);
+        uint32_t* sink = static_cast<uint32_t*>(dst);
+        const u32x4* va = static_cast<const u32x4*>(a);
+        if (kind == 5) {
+            const uint32_t wgs = (nblk + kThreads / 64 - 1) / (kThreads / 64);
+            hipLaunchKernelGGL(probe_paged_read, dim3(wgs), dim3(kThreads), 0, s, va, ids, nblk, sink);
+        } else {
+            int dev = 0, cus = 0;
+            if (hipGetDevice(&dev) != hipSuccess ||
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+                cus <= 0)
+                return -2;
+            if (kind == 6)
+                hipLaunchKernelGGL(probe_paged_read_persistent<4>, dim3(cus), dim3(kThreads), 0, s, va, ids,
+                                   nblk, sink);
+            else
+                hipLaunchKernelGGL(probe_paged_read_persistent<8>, dim3(cus), dim3(kThreads), 0, s, va, ids,
+                                   nblk, sink);
+        }
+        return hipGetLastError() == hipSuccess ? 0 : -2;
+    }
     const size_t n = bytes / 16;
     const size_t per_block = (size_t)kThreads * kUnroll;
     const size_t blocks = (n + per_block - 1) / per_block;
