@@ -39,10 +39,11 @@
 // start), as in the decode over selected blocks; positions are virtual
 // (offset j % bs of selected block j / bs) and the chunk is causal on them.
 // A loader wave bounds its half by the block's count, so a partial block's
-// tail is never read, and publishes the half's key count in LDS; a tile
-// with a partial half takes the masked path, where a position past its
-// block's count is no key and adds exactly nothing (a row may see no key
-// in a tile, or at all: its output is then 0).
+// tail is never read, and publishes the half's key count in LDS. The
+// unmasked steps end at the first tile with a partial half; it and every
+// later tile take the masked path, where a position past its block's count
+// is no key and adds exactly nothing (a row may see no key in a tile, or
+// at all: its output is then 0).
 // Key groups (KG = 2, dense head_dim 128, chosen by the host when there are
 // at most as many query blocks as CUs): the workgroup is 2 groups of 4 waves;
 // group g walks tiles [g T / 2, (g + 1) T / 2) of the block's T key tiles
@@ -464,11 +465,18 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void prefill_kernel(PrefillParams
         // and keeps step it + 2's store behind step it's readers
         if (AHEAD == 1 || (it & 1)) __syncthreads();
     };
+    // tiles every row of the block sees whole: keys up to P + q0
+    const int n_clean = min(max(((P + q0 + 1) >> 5) - tg0, 0), ng);
     int it = 0;
-    if constexpr (!SP) {
-        // tiles every row of the block sees whole: keys up to P + q0
-        const int n_clean = min(max(((P + q0 + 1) >> 5) - tg0, 0), ng);
-        for (; it < n_clean; ++it) step(it, BoolC<false>{});
+    for (; it < n_clean; ++it) {
+        if constexpr (SP) {
+            // with selected blocks the unmasked steps end at the first tile
+            // with a half of fewer than 16 keys (the counts the loader left
+            // in LDS before the last barrier); the masked steps take the rest
+            const int* nvb = lds_nv(it & (NBUF - 1));
+            if (__builtin_amdgcn_readfirstlane(nvb[0] & nvb[1]) != 16) break;
+        }
+        step(it, BoolC<false>{});
     }
     for (; it < nmax; ++it) step(it, BoolC<true>{});
 
