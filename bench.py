@@ -436,6 +436,10 @@ def main():
             4096 / (fl["graph_floor_stream_2to1_25MB_us"] * 1e-6), 0)
         fl["quant_scatter_prefill_over_floor"] = round(
             qs["quant_scatter_prefill_us"] / fl["graph_floor_stream_2to1_25MB_us"], 3)
+        # and against the probe that moves the store's own bytes to the same
+        # slots without its arithmetic
+        fl["quant_scatter_prefill_over_traffic_floor"] = round(
+            qs["quant_scatter_prefill_us"] / qs["quant_scatter_prefill_traffic_floor_us"], 3)
         result["also"].update(qs)
         result["also"].update(fl)
     if "longctx" in extras:
@@ -463,7 +467,10 @@ def main():
 def prefill_quant_scatter(torch, fk, synth, dev, stream, sets=32, reps=4):
     """Quantize+scatter of the 4096-token prefill chunk, rotating 32 input
     sets (1.6 GB > the 256 MB MALL) and slot sets; timed per launch from
-    graph replays (and eagerly, for reference)."""
+    graph replays (and eagerly, for reference). Beside it, the probe
+    library's copy of the store's memory traffic without its arithmetic
+    (the same strided reads, 128-byte code rows and 4-byte scales to the
+    same slots), replayed the same way: the floor of this access pattern."""
     log("prefill-chunk quantize+scatter...")
     H, D, T, S = 8, 128, 4096, 1 << 20
     chunks = [synth.prefill_chunk(seed=100 + i, device=dev) for i in range(sets)]
@@ -481,59 +488,73 @@ def prefill_quant_scatter(torch, fk, synth, dev, stream, sets=32, reps=4):
         one()
     ms = time_events(one, sets * reps, stream)
     avg = sum(ms) / len(ms)
-    # the same launches replayed from one HIP graph (one launch per input
-    # set, slot ids device-resident): the per-launch time without the
-    # host's launch overhead
-    torch.cuda.synchronize()
     side = torch.cuda.Stream(dev)
-    side.wait_stream(stream)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=side):
-        for _ in range(sets):
-            one()
-    stream.wait_stream(side)
-    for _ in range(2):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(reps):
-        graph.replay()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    g_avg = t0.elapsed_time(t1) / (reps * sets)
-    del graph
-    # the same chunks stored into consecutive slots (a prefill filling
+
+    def graph_us(launch):
+        # launch(i) for every input set, captured in one HIP graph and
+        # replayed: the per-launch time without the host's launch overhead
+        torch.cuda.synchronize()
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(sets):
+                launch(i)
+        stream.wait_stream(side)
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        del graph
+        return t0.elapsed_time(t1) / (reps * sets) * 1e3
+
+    def store(slots):
+        return lambda i: fk.kv_quant_scatter(chunks[i].k_view(), chunks[i].v_view(), slots(i),
+                                             k_cache, v_cache, k_plane.t(), v_plane.t())
+    L = probes_lib()
+
+    def traffic(slots, mode=0):
+        # mode: bit 0 no code stores, bit 1 no scale stores, bit 2 dense
+        # source rows (the first 16.8 MB of the set's qkv buffer)
+        def launch(i):
+            kv, vv = chunks[i].k_view(), chunks[i].v_view()
+            src = chunks[i].qkv if mode & 4 else kv
+            sl = slots(i)
+            st = L.fp8kv_probe_scatter(
+                src.data_ptr(), vv.data_ptr(), kv.stride(0), kv.stride(1), sl.data_ptr(), T, H,
+                k_cache.data_ptr(), v_cache.data_ptr(), k_cache.stride(1), k_cache.stride(0),
+                k_plane.data_ptr(), v_plane.data_ptr(), S, 1, S, mode, side.cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"scatter probe: status {st}")
+        return launch
+    # the chunks also stored into consecutive slots (a prefill filling
     # freshly allocated blocks): input set i takes slots [i*T, (i+1)*T)
     contig = [torch.arange(i * T, (i + 1) * T, device=dev) for i in range(sets)]
-    graph = torch.cuda.CUDAGraph()
-    side.wait_stream(stream)
-    with torch.cuda.graph(graph, stream=side):
-        for i, c in enumerate(chunks):
-            fk.kv_quant_scatter(c.k_view(), c.v_view(), contig[i], k_cache,
-                                v_cache, k_plane.t(), v_plane.t())
-    stream.wait_stream(side)
-    for _ in range(2):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for _ in range(reps):
-        graph.replay()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    c_avg = t0.elapsed_time(t1) / (reps * sets)
-    del graph
-    tok_s = T / (g_avg * 1e-3)
-    gbs = quant_bytes(T, H, D) / (g_avg * 1e-3) / 1e9
+    g_us = graph_us(store(lambda i: chunks[i].slot_ids))
+    c_us = graph_us(store(lambda i: contig[i]))
+    f_us = graph_us(traffic(lambda i: chunks[i].slot_ids))
+    fc_us = graph_us(traffic(lambda i: contig[i]))
+    parts = {name: graph_us(traffic(lambda i: chunks[i].slot_ids, mode))
+             for name, mode in (("no_scales", 2), ("no_codes", 1), ("reads_only", 3),
+                                ("dense_source", 4))}
+    tok_s = T / (g_us * 1e-6)
+    gbs = quant_bytes(T, H, D) / (g_us * 1e-6) / 1e9
     del chunks
     torch.cuda.empty_cache()
     return {"quant_scatter_prefill_tokens_per_s": round(tok_s, 0),
-            "quant_scatter_prefill_us": round(g_avg * 1e3, 2),
+            "quant_scatter_prefill_us": round(g_us, 2),
             "quant_scatter_prefill_GBps": round(gbs, 1),
             "quant_scatter_prefill_eager_us": round(avg * 1e3, 2),
-            "quant_scatter_prefill_contiguous_slots_us": round(c_avg * 1e3, 2),
-            "quant_scatter_prefill_contiguous_slots_tokens_per_s": round(T / (c_avg * 1e-3), 0)}
+            "quant_scatter_prefill_contiguous_slots_us": round(c_us, 2),
+            "quant_scatter_prefill_contiguous_slots_tokens_per_s": round(T / (c_us * 1e-6), 0),
+            "quant_scatter_prefill_traffic_floor_us": round(f_us, 2),
+            "quant_scatter_prefill_traffic_floor_contiguous_us": round(fc_us, 2),
+            **{f"quant_scatter_prefill_traffic_{k}_us": round(v, 2) for k, v in parts.items()}}
 
 
 def longctx_decode(torch, fk, synth, dev, stream, reps=20):
@@ -697,6 +718,10 @@ def probes_lib():
     P = ctypes.c_void_p
     L.fp8kv_probe.argtypes = [ctypes.c_int, P, P, P, ctypes.c_size_t, P]
     L.fp8kv_probe.restype = ctypes.c_int
+    I64, I32 = ctypes.c_int64, ctypes.c_int
+    L.fp8kv_probe_scatter.argtypes = [P, P, I64, I64, P, I32, I32, P, P, I64, I64, P, P,
+                                      I64, I64, I64, I32, P]
+    L.fp8kv_probe_scatter.restype = ctypes.c_int
     return L
 
 

@@ -15,6 +15,16 @@
 //           its share of the ids in groups of U = 4 or 8 blocks (8 or 16
 //           KiB: U = 4 is one 32-token tile of K and V codes), the next
 //           group's loads issued before the current group is consumed
+// fp8kv_probe_scatter: the prefill-chunk store's memory traffic without its
+// arithmetic (head_dim 128): each (token, KV head) row of K and of V is read
+// from its strided source (256 bytes), and 128 bytes (the two 16-byte halves
+// of each 32-byte piece xor-ed) go to the row's slot in a head-major code
+// pool with the non-temporal hint, plus one ordinary 4-byte store to the
+// row's scale plane; 8 lanes per row, 2 row pieces per thread. `mode`
+// leaves parts out to attribute the time: bit 0 no code stores, bit 1 no
+// scale stores, bit 2 rows read from a dense source (row r at r x 256
+// bytes of k, which must then hold 2 x tokens x heads rows) instead of the
+// strided slices.
 // Every thread moves 2 x 16 bytes: loads carry the non-temporal hint, stores
 // are ordinary; the grid covers the buffer once (no grid-stride loop), so
 // each wave's loads and stores are 1 KiB contiguous. Of the shapes measured
@@ -167,6 +177,47 @@ __global__ __launch_bounds__(kThreads) void probe_paged_read_persistent(const u3
     if ((acc.x & acc.y & acc.z & acc.w) == 0xFFFFFFFFu) sink[0] = acc.x;
 }
 
+struct ScatterArgs {
+    const uint16_t* k;
+    const uint16_t* v;
+    int64_t tok_stride, head_stride;     // source strides, elements
+    const int64_t* slots;
+    uint8_t* kpool;
+    uint8_t* vpool;
+    int64_t pool_head_stride, pool_slot_stride;   // bytes
+    float* kplane;
+    float* vplane;
+    int64_t plane_head_stride, plane_slot_stride; // elements
+    int64_t num_slots;
+    uint32_t units;                      // 2 x tokens x heads x 8
+    uint32_t heads, kv_rows;             // kv_rows = tokens x heads
+    uint32_t mode;
+};
+
+__global__ __launch_bounds__(kThreads) void probe_scatter_rows(ScatterArgs a) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t j = blockIdx.x * kThreads * kUnroll + u * kThreads + threadIdx.x;
+        if (j >= a.units) continue;
+        const uint32_t row = j >> 3, piece = j & 7;
+        const bool is_v = row >= a.kv_rows;
+        const uint32_t r = is_v ? row - a.kv_rows : row;
+        const uint32_t t = r / a.heads, h = r - t * a.heads;
+        const int64_t slot = min(max(a.slots[t], (int64_t)0), a.num_slots - 1);
+        const uint16_t* src = (a.mode & 4) ? a.k + (int64_t)row * 128 + 16 * piece
+                                            : (is_v ? a.v : a.k) + (int64_t)t * a.tok_stride +
+                                                  (int64_t)h * a.head_stride + 16 * piece;
+        const u32x4 x0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+        const u32x4 x1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + 1);
+        uint8_t* dst = (is_v ? a.vpool : a.kpool) + (int64_t)h * a.pool_head_stride +
+                       slot * a.pool_slot_stride + 16 * piece;
+        if (!(a.mode & 1)) __builtin_nontemporal_store(x0 ^ x1, reinterpret_cast<u32x4*>(dst));
+        if (piece == 0 && !(a.mode & 2))
+            (is_v ? a.vplane : a.kplane)[(int64_t)h * a.plane_head_stride + slot * a.plane_slot_stride] =
+                __uint_as_float(x0.x & 0x3FFFFFFFu);
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -233,6 +284,30 @@ int fp8kv_probe(int kind, const void* a, const void* b, void* dst, size_t bytes,
         default:
             return -1;
     }
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// The prefill-chunk store's traffic (see probe_scatter_rows) for `tokens`
+// tokens of `heads` KV heads, head_dim 128, parts left out by `mode`. Returns 0, -1 for a bad argument,
+// -2 for a launch error.
+int fp8kv_probe_scatter(const void* k, const void* v, int64_t tok_stride, int64_t head_stride,
+                        const int64_t* slots, int tokens, int heads, void* kpool, void* vpool,
+                        int64_t pool_head_stride, int64_t pool_slot_stride, void* kplane,
+                        void* vplane, int64_t plane_head_stride, int64_t plane_slot_stride,
+                        int64_t num_slots, int mode, void* stream) {
+    if (!k || !v || !slots || !kpool || !vpool || !kplane || !vplane || tokens <= 0 || heads <= 0 ||
+        num_slots <= 0 || (int64_t)tokens * heads * 16 > 0x7FFFFFFF)
+        return -1;
+    ScatterArgs a{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), tok_stride,
+                  head_stride, slots, static_cast<uint8_t*>(kpool), static_cast<uint8_t*>(vpool),
+                  pool_head_stride, pool_slot_stride, static_cast<float*>(kplane),
+                  static_cast<float*>(vplane), plane_head_stride, plane_slot_stride, num_slots,
+                  (uint32_t)tokens * (uint32_t)heads * 16u, (uint32_t)heads,
+                  (uint32_t)tokens * (uint32_t)heads, (uint32_t)mode};
+    const uint32_t per_block = kThreads * kUnroll;
+    const uint32_t blocks = (a.units + per_block - 1) / per_block;
+    hipLaunchKernelGGL(probe_scatter_rows, dim3(blocks), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), a);
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 
