@@ -4,11 +4,12 @@
 One step = one serving decode step over the decode workload (64 requests,
 context lengths uniform in [1024, 32768], 32 query / 8 KV heads, head_dim
 128, 16-token blocks, bf16 ~ N(0,1) K/V/q):
-  1. kv_quant_scatter of the step's 64 new K/V rows (one per request, at the
-     slot of its last token), and
-  2. paged GQA decode attention of the 64 query rows over the whole E4M3
-     cache (split phase: every KV head's tile sequence cut into equal
-     ranges, one wave each; then the log-sum-exp merge).
+  1. the split launch: the step's 64 new K/V rows (one per request, at the
+     slot of its last token) quantized and stored by the split kernel
+     itself, and paged GQA decode attention of the 64 query rows over the
+     whole E4M3 cache (every KV head's tile sequence cut into equal ranges,
+     one wave each), then
+  2. the log-sum-exp merge of the ranges.
 `value` is the step's algorithmic HBM bytes / step time (GB/s), the K timed
 steps running back to back with no instrumentation between their kernels.
 The dominant kernel (the decode split kernel) is then timed per launch with
@@ -18,16 +19,20 @@ for the roofline object.
 Also measured in the same run (reported under "also"): quantize+scatter
 tokens/s on the 4096-token prefill chunk (fused qkv, K/V strided slices,
 random slots in a 1,048,576-slot pool, 32 rotating input sets so reads come
-from HBM, replayed from a HIP graph; and the same chunks stored into
-consecutive slots, as a prefill filling fresh blocks), the cache-build bandwidth, the
-long-context verify decode (4 requests of 256K..1M tokens, 4 verify rows,
-16/4 heads, 64-token blocks), the decode over selected blocks (1/8 of the
-decode workload's blocks), chunked-prefill attention (a 4096-token chunk
-after 28,672 cached tokens), the compressed-index scorer (8 x 256 rows x 16
-heads x 65,536 keys, MXFP4 and E4M3 keys) with its key encoders and key
-builder, the decode workload over unscaled E4M3 / E5M2 caches, and the HBM
-ceilings of plain library copy and read kernels on the
-same GPU.
+from HBM, replayed from a HIP graph; the same chunks stored into
+consecutive slots, as a prefill filling fresh blocks; and the floors of
+that launch: an empty kernel, a contiguous stream of its bytes, and a probe
+moving its own bytes to the same slots without arithmetic), the
+cache-build bandwidth, the long-context verify decode (4 requests of
+256K..1M tokens, 4 verify rows, 16/4 heads, 64-token blocks), the decode
+over selected blocks (1/8 of the decode workload's blocks), chunked-prefill
+attention (a 4096-token chunk after 28,672 cached tokens, its last 1024
+tokens as a chunk, and the 4096-token chunk over 1/8 of the blocks), the
+compressed-index scorer (8 x 256 rows x 16 and 4 heads x 65,536 keys,
+MXFP4 and E4M3 keys) with its key encoders and key builder, the decode
+workload over unscaled E4M3 / E5M2 caches, and the HBM ceilings of plain
+probe streams (sequential, and the cache's random 2 KiB blocks) and of the
+library's copy and sum kernels on the same GPU.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """

@@ -14,7 +14,8 @@
 // on the tile, so it and v_scale * kappa are shared by the row tiles.
 //
 // The K/V codes and scales of each 32-token tile are read from the cache
-// once per workgroup into LDS (double-buffered): every loader wave moves the
+// once per workgroup into LDS (two buffers; with key groups four per group,
+// the loader two tiles ahead): every loader wave moves the
 // rows of 8 (head_dim 128) or 16 (head_dim 64) tokens of one 16-token half,
 // whose page lookup is wave-uniform, through buffer descriptors that end
 // after the chunk's last visible key, so nothing past it is read. The loader
