@@ -18,7 +18,10 @@
 // reduces each request piece of its range to a partial (normalized output,
 // log-sum-exp) in the workspace; piece (request b, range r) has id b + r,
 // unique because ids grow along the sequence, and a request's pieces have
-// consecutive ids. A second kernel merges each request's pieces by
+// consecutive ids. Where a range goes on into the next request, the
+// loads of that piece's first tile (and its q and first block-table window)
+// are issued during the current piece's last tile, so the stream does not
+// stop at the boundary. A second kernel merges each request's pieces by
 // log-sum-exp. The four waves of a workgroup are four KV heads of one
 // range, and the workgroups of a range sit on one XCD, so a tile's K/V
 // rows for all heads are read through one L2 at about the same time.
@@ -142,9 +145,73 @@ __device__ __forceinline__ void appended_rows_visible() {
 // (normalized output and log2 log-sum-exp of each of the M rows) at piece
 // id `pid`. With APPEND, the request's new rows that fall in the piece are
 // first written to the cache (append_load, append_store).
+// The next piece of a wave's range (request b + 1 from its first tile),
+// when the range goes on into it.
+struct NextPiece {
+    bool valid;
+    int b, len, jb;
+};
+
+// A wave's tile registers, kept across the pieces of its range: the two
+// tile register sets and descriptors of the A/B pipeline and the q operand.
+// When `ready`, a piece's last tile has already issued the next piece's
+// first tile (into set B if `first_in_b`, else A) and loaded its q, and
+// `btw` / `bvw` hold the next piece's first block-table window.
+template <int D, int CODES>
+struct WaveTiles {
+    typename DecodeTile<D, CODES>::Regs ra, rb;
+    TileAddr ta_a, ta_b;
+    bf16x8 qv[D / 32];
+    bool ready, first_in_b;
+    int btw, bvw;
+};
+
+// Page-walk constants of piece [ja, jb) of request b (length len) for KV head h.
+template <int D, int CODES>
+__device__ __forceinline__ typename DecodeTile<D, CODES>::WalkConsts piece_walk(
+    const DecodeParams& p, int b, int len, int ja, int jb, int h) {
+    typename DecodeTile<D, CODES>::WalkConsts w;
+    const int p1 = min(jb << 5, len);
+    w.kbase = p.k_cache + (int64_t)h * p.cache_stride_head;
+    w.vbase = p.v_cache + (int64_t)h * p.cache_stride_head;
+    w.ksbase = p.k_scale + (int64_t)h * p.scale_stride_head;
+    w.vsbase = p.v_scale + (int64_t)h * p.scale_stride_head;
+    w.bt = p.block_tables + (int64_t)b * p.block_table_stride;
+    w.bv = p.block_valid ? p.block_valid + (int64_t)b * p.block_valid_stride : nullptr;
+    w.p0 = ja << 5;
+    w.p1 = p1;
+    w.ntiles = jb - ja;
+    // tokens below full_end are visible to every row
+    w.full_end = min(p1, len - p.rows + 1);
+    w.last_base = (p1 - 1) & ~15;
+    w.nr_codes_full = 15 * (int)p.cache_stride_slot + D;
+    w.nr_scales_full = 4 * (15 * (int)p.scale_stride_slot + 1);
+    return w;
+}
+
+// q operand of row li of the stacked (verify row, query head) block of
+// request b, KV head h (zeros for the padding rows)
+template <int D>
+__device__ __forceinline__ void load_q(const DecodeParams& p, int b, int h, int li, int lg,
+                                       bf16x8 (&qv)[D / 32]) {
+    if (li < p.m_rows) {
+        const int r = li / p.group;
+        const int hq = h * p.group + (li - r * p.group);
+        const uint16_t* qp = p.q + (int64_t)b * p.q_stride_b + (int64_t)r * p.q_stride_row +
+                             (int64_t)hq * p.q_stride_head + lg * (D / 4);
+#pragma unroll
+        for (int k = 0; k < D / 32; ++k)
+            qv[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 8 * k));
+    } else {
+#pragma unroll
+        for (int k = 0; k < D / 32; ++k) qv[k] = bf16x8{};
+    }
+}
+
 template <int D, bool BSP2, bool SP, int CODES, bool APPEND>
 __device__ __forceinline__ void decode_piece(const DecodeParams& p, int b, int len, int ja, int jb,
-                                             int h, int pid, int lane) {
+                                             int h, int pid, int lane, const NextPiece& nx,
+                                             WaveTiles<D, CODES>& wt) {
     constexpr int KSTEPS = D / 32;
     constexpr int DL = D / 16;
     constexpr int KB = D / 4;
@@ -153,31 +220,16 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int b, int l
     const int li = lane & 15;
     const int lg = lane >> 4;
 
-    const int p0 = ja << 5;
-    const int p1 = min(jb << 5, len);
-    const int ntiles = jb - ja;
-
-    typename Tile::WalkConsts w;
-    w.kbase = p.k_cache + (int64_t)h * p.cache_stride_head;
-    w.vbase = p.v_cache + (int64_t)h * p.cache_stride_head;
-    w.ksbase = p.k_scale + (int64_t)h * p.scale_stride_head;
-    w.vsbase = p.v_scale + (int64_t)h * p.scale_stride_head;
-    w.bt = p.block_tables + (int64_t)b * p.block_table_stride;
-    w.bv = SP ? p.block_valid + (int64_t)b * p.block_valid_stride : nullptr;
-    w.p0 = p0;
-    w.p1 = p1;
-    w.ntiles = ntiles;
-    // tokens below full_end are visible to every row
-    w.full_end = min(p1, len - p.rows + 1);
-    w.last_base = (p1 - 1) & ~15;
-    w.nr_codes_full = 15 * (int)p.cache_stride_slot + D;
-    w.nr_scales_full = 4 * (15 * (int)p.scale_stride_slot + 1);
+    const typename Tile::WalkConsts w = piece_walk<D, CODES>(p, b, len, ja, jb, h);
+    const int p0 = w.p0, p1 = w.p1, ntiles = w.ntiles;
+    const bool ready = wt.ready;
 
     // new rows in the piece, positions [n0, n1): stored, and made visible
     // before the loads of the first tile that holds one (tile fence_at of
     // the piece). When that is not the first tile, the first pass's loads are
     // issued now and its stores after the first tile's loads, so the wave
-    // does not wait for them before it starts streaming.
+    // does not wait for them before it starts streaming. (A piece whose
+    // first tile holds a new row is never handed a prefetched first tile.)
     int fence_at = -1, n0 = 0, n1 = 0;
     NewRows<D> nr;
     if constexpr (APPEND) {
@@ -198,27 +250,23 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int b, int l
 
     // block-table window of tiles 0..31, and the next one when the piece is longer
     int kw = 0;
-    int btw = Tile::template table_window<BSP2>(p, w, w.bt, 0, lane);
+    int btw = ready ? wt.btw : Tile::template table_window<BSP2>(p, w, w.bt, 0, lane);
     int btn = ntiles > 32 ? Tile::template table_window<BSP2>(p, w, w.bt, 32, lane) : 0;
-    int bvw = SP ? Tile::template table_window<BSP2>(p, w, w.bv, 0, lane) : 0;
+    int bvw = SP ? (ready ? wt.bvw : Tile::template table_window<BSP2>(p, w, w.bv, 0, lane)) : 0;
     int bvn = SP && ntiles > 32 ? Tile::template table_window<BSP2>(p, w, w.bv, 32, lane) : 0;
 
     // q operand: row li of the stacked (verify row, query head) block
-    bf16x8 qv[KSTEPS];
-    int lim;                                   // last token row li sees
-    if (li < p.m_rows) {
-        const int r = li / p.group;
-        const int hq = h * p.group + (li - r * p.group);
-        const uint16_t* qp = p.q + (int64_t)b * p.q_stride_b + (int64_t)r * p.q_stride_row +
-                             (int64_t)hq * p.q_stride_head + lg * (D / 4);
-#pragma unroll
-        for (int k = 0; k < KSTEPS; ++k)
-            qv[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 8 * k));
-        lim = len - p.rows + r;
-    } else {
-#pragma unroll
-        for (int k = 0; k < KSTEPS; ++k) qv[k] = bf16x8{};
-        lim = len - 1;
+    bf16x8 (&qv)[KSTEPS] = wt.qv;
+    if (!ready) load_q<D>(p, b, h, li, lg, qv);
+    const int lim = li < p.m_rows ? len - p.rows + li / p.group : len - 1;   // last token row li sees
+
+    // the next piece's walk and first table window, in flight during this piece
+    typename Tile::WalkConsts wn;
+    int nbtw = 0, nbvw = 0;
+    if (nx.valid) {
+        wn = piece_walk<D, CODES>(p, nx.b, nx.len, 0, nx.jb, h);
+        nbtw = Tile::template table_window<BSP2>(p, wn, wn.bt, 0, lane);
+        if (SP) nbvw = Tile::template table_window<BSP2>(p, wn, wn.bv, 0, lane);
     }
 
     WaveState<DL> st;
@@ -257,19 +305,41 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int b, int l
         valid[0] = SP ? __builtin_amdgcn_readlane(bvw, j) : 0;
         valid[1] = SP ? __builtin_amdgcn_readlane(bvw, j + 1) : 0;
     };
+    // loads of tile k of the piece; after its last tile, those of the next
+    // piece's first tile and its q (the last QK^T has used this piece's), or
+    // with no next piece an empty tile
+    auto issue_tile = [&](int k, TileAddr& ta, Regs& r) {
+        int blk[2], valid[2];
+        if (k < ntiles || !nx.valid) {
+            entries(k, blk, valid);
+            Tile::template address<BSP2, SP>(p, w, k, blk, valid, ta);
+            if (APPEND && k == fence_at) appended_rows_visible();
+        } else {
+            blk[0] = __builtin_amdgcn_readlane(nbtw, 0);
+            blk[1] = __builtin_amdgcn_readlane(nbtw, 1);
+            valid[0] = SP ? __builtin_amdgcn_readlane(nbvw, 0) : 0;
+            valid[1] = SP ? __builtin_amdgcn_readlane(nbvw, 1) : 0;
+            Tile::template address<BSP2, SP>(p, wn, 0, blk, valid, ta);
+            load_q<D>(p, nx.b, h, li, lg, qv);
+        }
+        Tile::issue(ta, lo, r);
+    };
 
     // Two tiles in flight: after a tile's QK^T has consumed its K registers,
     // the loads of the next tile are issued, then the tile's softmax and PV
     // run while they are in flight (A/B ping-pong).
-    TileAddr ta_a, ta_b;
-    Regs ra, rb;
+    TileAddr& ta_a = wt.ta_a;
+    TileAddr& ta_b = wt.ta_b;
+    Regs& ra = wt.ra;
+    Regs& rb = wt.rb;
     floatx4 sc[2];
-    int blk[2], valid[2];
     int ti = 0;
-    entries(0, blk, valid);
-    Tile::template address<BSP2, SP>(p, w, 0, blk, valid, ta_a);
-    if (APPEND && fence_at == 0) appended_rows_visible();
-    Tile::issue(ta_a, lo, ra);
+    if (!ready) {
+        issue_tile(0, ta_a, ra);
+    } else if (wt.first_in_b) {
+        ra = rb;
+        ta_a = ta_b;
+    }
     if (APPEND && fence_at > 0) {
         append_store<D>(p, h, lane, nr);
         for (int pos0 = n0 + 2; pos0 < n1; pos0 += 2) {
@@ -277,19 +347,17 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int b, int l
             append_store<D>(p, h, lane, nr);
         }
     }
+    bool last_in_b = false;        // the tile after the last one went to set B
     while (ti < ntiles) {
         Tile::qk(ra, qv, sc);
-        entries(ti + 1, blk, valid);
-        Tile::template address<BSP2, SP>(p, w, ti + 1, blk, valid, ta_b);
-        if (APPEND && ti + 1 == fence_at) appended_rows_visible();
-        Tile::issue(ta_b, lo, rb);
+        issue_tile(ti + 1, ta_b, rb);
         Tile::template rest<SP>(p, ta_a, ra, sc, p1, lim, lg, st);
-        if (++ti >= ntiles) break;
+        if (++ti >= ntiles) {
+            last_in_b = true;
+            break;
+        }
         Tile::qk(rb, qv, sc);
-        entries(ti + 1, blk, valid);
-        Tile::template address<BSP2, SP>(p, w, ti + 1, blk, valid, ta_a);
-        if (APPEND && ti + 1 == fence_at) appended_rows_visible();
-        Tile::issue(ta_a, lo, ra);
+        issue_tile(ti + 1, ta_a, ra);
         Tile::template rest<SP>(p, ta_b, rb, sc, p1, lim, lg, st);
         ++ti;
     }
@@ -314,6 +382,12 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int b, int l
         }
         if (lg == 0) p.ws_lse[u] = any ? st.m_run + __log2f(st.l_run) : -INFINITY;
     }
+
+    // the next piece finds its first tile and q issued, and its table window
+    wt.ready = nx.valid;
+    wt.first_in_b = last_in_b;
+    wt.btw = nbtw;
+    wt.bvw = nbvw;
 }
 
 // Workgroup = 4 waves = 4 workers; worker = (range r, KV head h). When the
@@ -370,16 +444,35 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         carry = __builtin_amdgcn_readlane(incl, 63);
     }
 
-    // walk the pieces of the range
+    // walk the pieces of the range; when the range goes on into the next
+    // request, its first tile is loaded during this piece's last one
     int u = u0;
+    WaveTiles<D, CODES> wt;
+    wt.ready = false;
+    wt.first_in_b = false;
     while (u < u1) {
         const int len = min(max(p.context_lens[b], 0), p.max_context);
         const int n = (len + 31) >> 5;
         if (n > 0) {
             const int ja = u - pre;
             const int jb = min(n, u1 - pre);
-            decode_piece<D, BSP2, SP, CODES, APPEND>(p, b, len, ja, jb, h, b + r, lane);
+            NextPiece nx{false, 0, 0, 0};
+            // (not over selected blocks, whose pieces are short and whose
+            // kernel measured slower with the prefetch)
+            if (!SP && pre + jb < u1 && b + 1 < p.batch) {
+                const int nlen = min(max(p.context_lens[b + 1], 0), p.max_context);
+                const int nn = (nlen + 31) >> 5;
+                const int njb = min(nn, u1 - (pre + n));
+                // a first tile that holds one of the step's new rows is
+                // loaded only after they are stored
+                const bool fenced = APPEND && max(nlen - p.rows, 0) < min(njb << 5, nlen) &&
+                                    max(nlen - p.rows, 0) < 32;
+                nx = NextPiece{nn > 0 && !fenced, b + 1, nlen, njb};
+            }
+            decode_piece<D, BSP2, SP, CODES, APPEND>(p, b, len, ja, jb, h, b + r, lane, nx, wt);
             u = pre + jb;
+        } else {
+            wt.ready = false;
         }
         pre += n;
         ++b;
