@@ -69,7 +69,8 @@ def parse():
     ap.add_argument("--extras",
                     default="prefill,longctx,sparse,prefill_attn,index,unscaled,ceilings",
                     help="comma list of the extras to run (prefill, longctx, sparse, "
-                         "prefill_attn, index, unscaled, ceilings)")
+                         "prefill_attn, index, unscaled, ceilings; not by default: ops, "
+                         "the instruction-cost probes)")
     ap.add_argument("--pool", choices=("head", "slot"), default="head",
                     help="code pool layout: head = [Hkv, slots, D] (each KV head's "
                          "rows of a block contiguous), slot = [slots, Hkv, D]")
@@ -460,6 +461,8 @@ def main():
         result["also"].update(unscaled_decode(torch, fk, synth, dev, stream, case, q, bt, cl))
     if "ceilings" in extras:
         result["also"].update(hbm_ceilings(torch, dev, stream))
+    if "ops" in extras:
+        result["also"].update(op_costs(torch, dev, stream))
 
     if not args.no_cpu_baseline:
         log("timing the oracle on host cores...")
@@ -727,6 +730,8 @@ def probes_lib():
     L.fp8kv_probe_scatter.argtypes = [P, P, I64, I64, P, I32, I32, P, P, I64, I64, P, P,
                                       I64, I64, I64, I32, P]
     L.fp8kv_probe_scatter.restype = ctypes.c_int
+    L.fp8kv_probe_ops.argtypes = [I32, P, P, I32, I32, P]
+    L.fp8kv_probe_ops.restype = ctypes.c_int
     return L
 
 
@@ -774,6 +779,49 @@ def hbm_ceilings(torch, dev, stream, gib=2, reps=10):
         res[f"hbm_{name}_GBps"] = round(moved / (ms[len(ms) // 2] * 1e-3) / 1e9, 1)
     del a, b, d, ids
     torch.cuda.empty_cache()
+    return res
+
+
+OP_PROBES = ("exp2_f32", "exp2_f16", "fma", "mfma", "mfma_2fma", "mfma_4fma", "mfma_1exp2",
+             "mfma_3fma", "mfma_wave_beside_fma_wave", "fma_wave_alone")
+
+
+def op_costs(torch, dev, stream, iters=4000):
+    """Instruction costs on this GPU (the probe library's fp8kv_probe_ops):
+    every wave runs `iters` iterations of 8 independent chains of one
+    operation (exp2 f32, exp2 f16, FMA), or of 8 independent 16x16x32 bf16
+    MFMA chains with 2, 4, 3 FMAs or one exp2 per MFMA in the same wave, at
+    one and two waves per SIMD; and, at two waves per SIMD, an MFMA-only
+    wave beside a wave running 2 FMAs per MFMA slot on each SIMD, and that
+    FMA wave alone. Reported: each kernel's time and, per SIMD, the time
+    per operation (exp2 / FMA chains, the FMA wave alone) or per MFMA (the
+    others)."""
+    log("instruction-cost probes...")
+    L = probes_lib()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    res = {}
+    for wps in (1, 2):
+        blocks = cus * wps
+        out = torch.zeros(blocks * 4, device=dev)
+        cyc = torch.zeros(blocks * 4, dtype=torch.int64, device=dev)
+        for v, name in enumerate(OP_PROBES):
+            split = name in ("mfma_wave_beside_fma_wave", "fma_wave_alone")
+            if split and wps != 2:
+                continue
+
+            def launch():
+                st = L.fp8kv_probe_ops(v, out.data_ptr(), cyc.data_ptr(), iters, blocks,
+                                       stream.cuda_stream)
+                if st != 0:
+                    raise RuntimeError(f"op probe {v}: status {st}")
+            for _ in range(3):
+                launch()
+            ms = sorted(time_events(launch, 5, stream))[2]
+            # operations per SIMD: wps waves x iters x 8 (the split variants:
+            # one MFMA wave x 8 MFMAs, or one FMA wave x 16 FMAs, per iteration)
+            ops = iters * (16 if name == "fma_wave_alone" else 8) * (1 if split else wps)
+            res[f"op_{name}_w{wps}_us"] = round(ms * 1e3, 1)
+            res[f"op_{name}_w{wps}_ns_per_op"] = round(ms * 1e6 / ops, 3)
     return res
 
 

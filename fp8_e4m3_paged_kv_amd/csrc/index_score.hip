@@ -24,8 +24,8 @@
 // summed score; MXFP4 exponents vary along the dims and are folded into the
 // widened keys (E2M1 * 2^e is exact in bf16). The ReLU and head weights cost
 // two VALU ops per (row, head, key), which bounds the kernel together with
-// the MFMAs: on gfx950 the vector ALU and the matrix core overlap only in
-// part.
+// the MFMAs: on gfx950 a wave's own vector instructions beside its MFMAs
+// overlap them only in part.
 #include <hip/hip_runtime.h>
 
 #include "fp8kv_device.h"

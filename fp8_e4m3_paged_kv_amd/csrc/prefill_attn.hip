@@ -28,9 +28,10 @@
 // tokens per lane. Workgroups of one (request, KV head) run on one XCD, the
 // deepest query blocks first.
 // Instruction mix: a wave hides about two cheap vector instructions behind
-// each MFMA of its own instruction stream, while a vector-heavy wave beside
-// an MFMA-heavy one on the same SIMD slows the MFMAs down. So each wave
-// interleaves its own work: row tile j's PV MFMAs are issued between the
+// each MFMA of its own instruction stream; giving the MFMA and the vector
+// phases to different waves of a SIMD instead leaves each vector phase
+// waiting on its own dependency chains. So each wave interleaves its own
+// work: row tile j's PV MFMAs are issued between the
 // exponentials of row tile j + 1, and the last row tile's between the
 // loader's conversions of the next tile; the softmax's rare rescale is one
 // branch for all row tiles, so the rest of a tile is one block of code.

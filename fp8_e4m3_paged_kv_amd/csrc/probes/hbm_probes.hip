@@ -15,6 +15,12 @@
 //           its share of the ids in groups of U = 4 or 8 blocks (8 or 16
 //           KiB: U = 4 is one 32-token tile of K and V codes), the next
 //           group's loads issued before the current group is consumed
+// fp8kv_probe_ops: instruction-cost probes (no memory traffic but one value
+// and one cycle count per wave): every wave runs `iters` iterations of 8
+// independent chains of one operation, or of 8 independent 16x16x32 bf16
+// MFMA chains with K vector FMAs (or one exp2) beside each MFMA in the same
+// instruction stream, or (variant 8) MFMA-only and FMA-only waves
+// alternating on each SIMD; see fp8kv_probe_ops below for the variants.
 // fp8kv_probe_scatter: the prefill-chunk store's memory traffic without its
 // arithmetic (head_dim 128): each (token, KV head) row of K and of V is read
 // from its strided source (256 bytes), and 128 bytes (the two 16-byte halves
@@ -177,6 +183,66 @@ __global__ __launch_bounds__(kThreads) void probe_paged_read_persistent(const u3
     if ((acc.x & acc.y & acc.z & acc.w) == 0xFFFFFFFFu) sink[0] = acc.x;
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+// OP: 0 exp2 f32 (+ multiply), 1 exp2 f16 (+ multiply), 2 FMA;
+// MF: MFMA chains, with K FMAs (OP 2) or K exp2 (OP 0) per MFMA in the same
+// wave; SPLIT (8-wave workgroups, one per CU): waves 4..7 run only the FMAs
+// (K per MFMA slot), waves 0..3 only the MFMAs, so each SIMD holds one wave
+// of each kind (the role is wave-uniform: each wave issues one kind)
+template <int OP, bool MF, int K, bool SPLIT>
+__global__ __launch_bounds__(512) void probe_ops(float* out, unsigned long long* cyc, int iters) {
+    const int t = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    bf16x8_t a, b;
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(0.001f * (t + i));
+        b[i] = (__bf16)(0.002f * (t - i));
+    }
+    floatx4_t acc[8];
+    for (int c = 0; c < 8; ++c) acc[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    float x[8];
+    _Float16 hx[8];
+    for (int k = 0; k < 8; ++k) {
+        x[k] = 0.001f * (t + k);
+        hx[k] = (_Float16)(0.001f * (t + k));
+    }
+    const float y = 0.9999f, z = 0.0001f;
+    auto valu_op = [&](int k) {
+        if (OP == 0) x[k] = __builtin_amdgcn_exp2f(x[k]) * 0.5f;
+        else if (OP == 1) hx[k] = __builtin_exp2f16(hx[k]) * (_Float16)0.5f;
+        else x[k] = __builtin_fmaf(x[k], y, z);
+    };
+    const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+    if (SPLIT && wave >= 4) {
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int c = 0; c < 8 * K; ++c) valu_op(c & 7);
+    } else {
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                if (MF) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+                if (!SPLIT) {
+                    constexpr int per = MF ? K : 1;
+#pragma unroll
+                    for (int j = 0; j < per; ++j) valu_op((c * per + j) & 7);
+                }
+            }
+        }
+    }
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+    float s = 0.f;
+    for (int c = 0; c < 8; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+    for (int k = 0; k < 8; ++k) s += x[k] + (float)hx[k];
+    const int w = blockIdx.x * (blockDim.x >> 6) + (t >> 6);
+    if ((t & 63) == 0) {
+        out[w] = s;
+        cyc[w] = t1 - t0;
+    }
+}
+
 struct ScatterArgs {
     const uint16_t* k;
     const uint16_t* v;
@@ -283,6 +349,43 @@ int fp8kv_probe(int kind, const void* a, const void* b, void* dst, size_t bytes,
             break;
         default:
             return -1;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// Instruction-cost probe `variant` over `blocks` workgroups of 4 waves
+// (blocks = CUs x waves per SIMD; variants 8 and 9 take blocks / 2
+// workgroups of 8 waves, blocks even); out and cyc hold blocks x 4 entries.
+//   0  8 exp2 f32 chains        1  8 exp2 f16 chains      2  8 FMA chains
+//   3  8 MFMA chains            4  + 2 FMA per MFMA       5  + 4 FMA per MFMA
+//   6  + 1 exp2 per MFMA        7  + 3 FMA per MFMA
+//   8  MFMA-only waves and FMA-only waves (2 FMAs per MFMA slot) alternating,
+//   9  FMA-only waves of variant 8 alone (16 FMA chains' worth per iteration)
+// Returns 0, -1 for a bad argument, -2 for a launch error.
+int fp8kv_probe_ops(int variant, float* out, unsigned long long* cyc, int iters, int blocks, void* stream) {
+    if (!out || !cyc || iters <= 0 || blocks <= 0) return -1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 g((unsigned)blocks), b(256);
+    switch (variant) {
+        case 0: hipLaunchKernelGGL((probe_ops<0, false, 1, false>), g, b, 0, s, out, cyc, iters); break;
+        case 1: hipLaunchKernelGGL((probe_ops<1, false, 1, false>), g, b, 0, s, out, cyc, iters); break;
+        case 2: hipLaunchKernelGGL((probe_ops<2, false, 1, false>), g, b, 0, s, out, cyc, iters); break;
+        case 3: hipLaunchKernelGGL((probe_ops<2, true, 0, false>), g, b, 0, s, out, cyc, iters); break;
+        case 4: hipLaunchKernelGGL((probe_ops<2, true, 2, false>), g, b, 0, s, out, cyc, iters); break;
+        case 5: hipLaunchKernelGGL((probe_ops<2, true, 4, false>), g, b, 0, s, out, cyc, iters); break;
+        case 6: hipLaunchKernelGGL((probe_ops<0, true, 1, false>), g, b, 0, s, out, cyc, iters); break;
+        case 7: hipLaunchKernelGGL((probe_ops<2, true, 3, false>), g, b, 0, s, out, cyc, iters); break;
+        case 8:
+        case 9:
+            if (blocks % 2) return -1;
+            if (variant == 8)
+                hipLaunchKernelGGL((probe_ops<2, true, 2, true>), dim3((unsigned)blocks / 2), dim3(512), 0, s,
+                                   out, cyc, iters);
+            else
+                hipLaunchKernelGGL((probe_ops<2, false, 2, true>), dim3((unsigned)blocks / 2), dim3(512), 0, s,
+                                   out, cyc, iters);
+            break;
+        default: return -1;
     }
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
