@@ -71,6 +71,9 @@ def parse():
                     help="comma list of the extras to run (prefill, longctx, sparse, "
                          "prefill_attn, index, unscaled, ceilings; not by default: ops, "
                          "the instruction-cost probes)")
+    ap.add_argument("--scales", choices=("head", "interleaved"), default="head",
+                    help="scale planes: head = two [Hkv, slots] planes; interleaved = one "
+                         "[Hkv, slots, 2] array holding each row's K and V scales side by side")
     ap.add_argument("--pool", choices=("head", "slot"), default="head",
                     help="code pool layout: head = [Hkv, slots, D] (each KV head's "
                          "rows of a block contiguous), slot = [slots, Hkv, D]")
@@ -127,6 +130,21 @@ def quant_bytes(T, Hkv, D):
 SETTLE_S = 0.3
 POOL = "head"                  # code pool layout (set from --pool)
 POOL_DESC = {"head": "head-major [Hkv, slots, D]", "slot": "slot-major [slots, Hkv, D]"}
+SCALES = "head"                # scale plane layout (set from --scales)
+SCALES_DESC = {"head": "head-major [Hkv, slots]",
+               "interleaved": "K/V-interleaved [Hkv, slots, 2]"}
+
+
+def alloc_planes(torch, S, H, dev):
+    """K and V scale planes as [Hkv, slots] views (passed transposed, as
+    [slots, Hkv]): two planes, or one [Hkv, slots, 2] array with each row's
+    K and V scales side by side (a 16-token block's 32 scales of one head
+    are then one 128-byte line)."""
+    if SCALES == "interleaved":
+        kv = torch.empty((H, S, 2), dtype=torch.float32, device=dev)
+        return kv[:, :, 0], kv[:, :, 1]
+    k = torch.empty((H, S), dtype=torch.float32, device=dev)
+    return k, torch.empty_like(k)
 
 
 def alloc_pool(torch, S, H, D, dev):
@@ -181,6 +199,8 @@ def traffic_entry(per_launch_alg_bytes):
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
     if t.get("pool_layout") != POOL:               # counters taken on this pool layout
+        return None
+    if t.get("scale_layout", "head") != SCALES:    # ... and these scale planes
         return None
     return t.get("bytes_per_launch")
 
@@ -291,8 +311,9 @@ def main():
         print(json.dumps({"error": "the benchmark measures one GPU only; "
                                    "run with --gpus 1"}))
         sys.exit(2)
-    global POOL
+    global POOL, SCALES
     POOL = args.pool
+    SCALES = args.scales
     import torch
     import fp8_e4m3_paged_kv_amd as fk
     from fp8_e4m3_paged_kv_amd import synth
@@ -309,8 +330,7 @@ def main():
     B, R, Hq, Hkv, D, bs = 64, 1, 32, 8, 128, L.block_size
     S = L.num_slots
     k_cache, v_cache = alloc_pool(torch, S, Hkv, D, dev)
-    k_plane = torch.empty((Hkv, S), dtype=torch.float32, device=dev)
-    v_plane = torch.empty_like(k_plane)
+    k_plane, v_plane = alloc_planes(torch, S, Hkv, dev)
     slots_all = L.token_slots.to(dev)
     T = slots_all.numel()
     # cache build: quantize+scatter of every cached token
@@ -416,7 +436,7 @@ def main():
                    "batch": B, "context_tokens": sum(lens), "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "block_size": bs,
                    "decode_ranges_per_kv_head": nr,
-                   "scale_planes": "head-major [Hkv, slots]",
+                   "scale_planes": SCALES_DESC[SCALES],
                    "pool_layout": POOL_DESC[POOL]},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
@@ -483,8 +503,7 @@ def prefill_quant_scatter(torch, fk, synth, dev, stream, sets=32, reps=4):
     H, D, T, S = 8, 128, 4096, 1 << 20
     chunks = [synth.prefill_chunk(seed=100 + i, device=dev) for i in range(sets)]
     k_cache, v_cache = alloc_pool(torch, S, H, D, dev)
-    k_plane = torch.empty((H, S), dtype=torch.float32, device=dev)
-    v_plane = torch.empty_like(k_plane)
+    k_plane, v_plane = alloc_planes(torch, S, H, dev)
     it = {"i": 0}
 
     def one():
@@ -536,7 +555,8 @@ def prefill_quant_scatter(torch, fk, synth, dev, stream, sets=32, reps=4):
             st = L.fp8kv_probe_scatter(
                 src.data_ptr(), vv.data_ptr(), kv.stride(0), kv.stride(1), sl.data_ptr(), T, H,
                 k_cache.data_ptr(), v_cache.data_ptr(), k_cache.stride(1), k_cache.stride(0),
-                k_plane.data_ptr(), v_plane.data_ptr(), S, 1, S, mode, side.cuda_stream)
+                k_plane.data_ptr(), v_plane.data_ptr(), k_plane.stride(0), k_plane.stride(1), S,
+                mode, side.cuda_stream)
             if st != 0:
                 raise RuntimeError(f"scatter probe: status {st}")
         return launch
@@ -572,8 +592,7 @@ def longctx_decode(torch, fk, synth, dev, stream, reps=20):
     H, D, bs = 4, 128, L.block_size
     S = L.num_slots
     k_cache, v_cache = alloc_pool(torch, S, H, D, dev)
-    k_plane = torch.empty((H, S), dtype=torch.float32, device=dev)
-    v_plane = torch.empty_like(k_plane)
+    k_plane, v_plane = alloc_planes(torch, S, H, dev)
     slots = L.token_slots.to(dev)
     T = slots.numel()
     build_ms = cache_build(torch, fk, case.k, case.v, slots, k_cache, v_cache,
@@ -879,8 +898,7 @@ def prefill_attention(torch, fk, synth, dev, stream, reps=10):
     H, D = case.num_kv_heads, case.head_dim
     S = L.num_slots
     k_cache, v_cache = alloc_pool(torch, S, H, D, dev)
-    k_plane = torch.empty((H, S), dtype=torch.float32, device=dev)
-    v_plane = torch.empty_like(k_plane)
+    k_plane, v_plane = alloc_planes(torch, S, H, dev)
     slots = L.token_slots.to(dev)
     cache_build(torch, fk, case.k, case.v, slots, k_cache, v_cache, k_plane, v_plane, stream)
     del case.k, case.v
