@@ -63,3 +63,21 @@ def test_traffic_only_for_the_measured_source(bench, tmp_path, monkeypatch):
     assert bench.traffic_entry(1) is None
     f.write_text("not json")
     assert bench.traffic_entry(1) is None
+
+
+def test_traffic_only_for_the_measured_scale_layout(bench, tmp_path, monkeypatch):
+    """Counters taken on head-major scale planes (the record names none or
+    "head") do not apply to a run on K/V-interleaved planes, and back."""
+    good = {"kernel_source_hash": bench.kernel_source_hash(), "bytes_per_launch": 777,
+            "pool_layout": bench.POOL}
+    f = tmp_path / "traffic.json"
+    f.write_text(json.dumps(good))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    monkeypatch.setattr(bench, "SCALES", "head")
+    assert bench.traffic_entry(1) == 777
+    monkeypatch.setattr(bench, "SCALES", "interleaved")
+    assert bench.traffic_entry(1) is None
+    f.write_text(json.dumps(dict(good, scale_layout="interleaved")))
+    assert bench.traffic_entry(1) == 777
+    monkeypatch.setattr(bench, "SCALES", "head")
+    assert bench.traffic_entry(1) is None
