@@ -193,7 +193,6 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void prefill_kernel(PrefillParams
             for (int k = 0; k < KSTEPS; ++k) qv[j][k] = bf16x8{};
         }
     }
-    const int wave_lim = P + q0 + wave * NT * TPW;        // smallest limit of the wave's rows
 
     // softmax state of each row tile; the P' range exponent is shared
     WaveState<DL> st[NT];
