@@ -10,8 +10,11 @@
 // NT row tiles, each stacking 16/G tokens x G query heads into the 16 MFMA
 // rows exactly as the decode split kernel stacks verify rows: QK^T MFMA
 // (bf16), online softmax with the key scale on the score, P' = p * v_scale
-// in fp16, PV MFMA (fp16). The value-scale range exponent of P' depends only
-// on the tile, so it and v_scale * kappa are shared by the row tiles.
+// in fp16, PV MFMA (fp16). The range exponent of P' is fixed per workgroup
+// before the key loop: one pass over the value scales of every key the
+// workgroup will read takes their largest exponent (the value the decode
+// kernel's running exponent reaches at its last tile), so the loader stores
+// v_scale * kappa in LDS and the tiles do no range bookkeeping.
 //
 // The K/V codes and scales of each 32-token tile are read from the cache
 // once per workgroup into LDS (two buffers; with key groups four per group,
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void prefill_kernel(PrefillParams
     // token (head-dim columns 8 c .. 8 c + 7 in 16-byte chunk c, chunks
     // permuted per row: K chunk c of token T at c ^ ((T >> 2) & 3), V chunk c
     // at c ^ ((T >> 2) & 1)); then scales [NBUF][k_scale * score scale |
-    // v_scale][32] and selected-block key counts [NBUF][half]. The row pitch
+    // v_scale * kappa][32] and selected-block key counts [NBUF][half]. The row pitch
     // and permutations keep every LDS access of the loop free of bank
     // conflicts on gfx950 (the loader's 16-byte stores, the K operand reads,
     // the transposing V operand reads), and the operand addresses of a lane
@@ -126,6 +129,9 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void prefill_kernel(PrefillParams
     // each other half as often; one 4-wave group per workgroup is faster with
     // a barrier every tile).
     constexpr int AHEAD = KG > 1 ? 2 : 1;
+    // one key group: the P' range exponent is fixed before the key loop;
+    // key groups keep a running one per group (measured faster there)
+    constexpr bool FIXED_EF = KG == 1;
     constexpr int NBUF = 2 * AHEAD;
     constexpr int KT_BYTES = 32 * LROW;
     constexpr int VT_BYTES = 32 * LROW;
@@ -203,7 +209,71 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void prefill_kernel(PrefillParams
         st[j].m_run = kNeg;
         st[j].l_run = 0.f;
     }
+
+    const float* ksbase = p.k_scale + (int64_t)h * p.scale_stride_head;
+    const float* vsbase = p.v_scale + (int64_t)h * p.scale_stride_head;
+    const int32_t* bt = p.block_tables + (int64_t)b * p.block_table_stride;
+    const int32_t* bv = SP ? p.block_valid + (int64_t)b * p.block_valid_stride : nullptr;
+    // P' range exponent: the largest exponent field of the value scales of
+    // the keys the loader will read (tokens below kv_end; with selected
+    // blocks the blocks' valid keys), at least 15; the scales are >= 0, so
+    // their bit patterns order as integers. Each thread takes 8 blocks at a
+    // time (their table entries first, then all their scales, so that the
+    // loads are in flight together); every load stays inside its block and
+    // a scale past the block's last key read counts as 0. Each wave's
+    // maximum goes to LDS, and every wave takes the maximum of all of them.
     int ef_run = 15;
+    if constexpr (FIXED_EF) {
+        __shared__ uint32_t wave_max[4];
+        constexpr int NTH = 256 * KG;
+        uint32_t mx = 0;
+        const int nblk = (kv_end + p.block_size - 1) / p.block_size;
+        const bool dense16 = p.block_size == 16 && p.scale_stride_slot == 1 &&
+                             (reinterpret_cast<uintptr_t>(vsbase) & 15) == 0;
+        for (int b0 = 0; b0 < nblk; b0 += 8 * NTH) {
+            int blk[8], nv[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int bi = b0 + k * NTH + t;
+                blk[k] = 0;
+                nv[k] = 0;
+                if (bi < nblk) {
+                    blk[k] = min(max(bt[bi], 0), p.num_blocks - 1);
+                    nv[k] = min(p.block_size, kv_end - bi * p.block_size);
+                    if (SP) nv[k] = min(nv[k], min(max(bv[bi], 0), p.block_size));
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float* sp = vsbase + (int64_t)blk[k] * p.block_size * p.scale_stride_slot;
+                if (dense16) {
+                    // the block's 16 scales are 64 contiguous bytes
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint4 u = *reinterpret_cast<const uint4*>(sp + 4 * c);
+                        mx = max(mx, 4 * c + 0 < nv[k] ? u.x : 0u);
+                        mx = max(mx, 4 * c + 1 < nv[k] ? u.y : 0u);
+                        mx = max(mx, 4 * c + 2 < nv[k] ? u.z : 0u);
+                        mx = max(mx, 4 * c + 3 < nv[k] ? u.w : 0u);
+                    }
+                } else {
+                    for (int j = 0; j < nv[k]; ++j)
+                        mx = max(mx, __float_as_uint(sp[(int64_t)j * p.scale_stride_slot]));
+                }
+            }
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+        mx = rows_max_u32(mx);
+        if (lane == 0) wave_max[wv] = mx;
+        __syncthreads();
+        uint32_t all = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) all = max(all, wave_max[w]);
+        ef_run = max((int)(__builtin_amdgcn_readfirstlane(all) >> 23), 15);
+    }
+    // P' = p * (v_scale * kappa) < 2^kLazyMax * 2^(ef_run - 126) * kappa = 2^15
+    const float kappa_wg = pow2i(141 - kLazyMax - ef_run);
 
     // cooperative tile load, widened once for all waves: lane l of loader
     // wave w moves the 16 K and the 16 V codes of chunk l / TPL of token
@@ -228,10 +298,6 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void prefill_kernel(PrefillParams
     const int vq = (4 * lg + (li >> 2)) * LROW + 16 * (((li >> 1) & 1) ^ (lg & 1)) + 8 * (li & 1);
     const uint8_t* kbase = p.k_cache + (int64_t)h * p.cache_stride_head;
     const uint8_t* vbase = p.v_cache + (int64_t)h * p.cache_stride_head;
-    const float* ksbase = p.k_scale + (int64_t)h * p.scale_stride_head;
-    const float* vsbase = p.v_scale + (int64_t)h * p.scale_stride_head;
-    const int32_t* bt = p.block_tables + (int64_t)b * p.block_table_stride;
-    const int32_t* bv = SP ? p.block_valid + (int64_t)b * p.block_valid_stride : nullptr;
     intx4 kr = {0, 0, 0, 0}, vr = {0, 0, 0, 0};
     float ksr = 0.f, vsr = 0.f;
     int ld_nv = 16;
@@ -277,7 +343,7 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void prefill_kernel(PrefillParams
         *reinterpret_cast<uint4*>(lds_k(buf) + lds_k1) = make_uint4(kw[4], kw[5], kw[6], kw[7]);
         *reinterpret_cast<uint4*>(lds_v(buf) + lds_v0) = make_uint4(vw[0], vw[1], vw[2], vw[3]);
         *reinterpret_cast<uint4*>(lds_v(buf) + lds_v1) = make_uint4(vw[4], vw[5], vw[6], vw[7]);
-        const float sr = ld_chunk == 0 ? ksr * p.score_scale_log2 : vsr;
+        const float sr = ld_chunk == 0 ? ksr * p.score_scale_log2 : (FIXED_EF ? vsr * kappa_wg : vsr);
         if (ld_chunk < 2) lds_s(buf, ld_chunk)[ld_tok] = sr;
         if (SP && lane == 0 && ((wave * TPL) & 15) == 0) lds_nv(buf)[ld_half] = ld_nv;
     };
@@ -335,27 +401,31 @@ __global__ __launch_bounds__(256 * KG, 2 / KG) void prefill_kernel(PrefillParams
                     for (int j = 0; j < NT; ++j)
                         sc[j][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[k][s], qv[j][k], sc[j][s], 0, 0, 0);
 
-            // ---- P' range of the tile (keys past the chunk have v_scale 0);
-            // the scales are >= 0, so their bit patterns order as integers;
-            // the range bookkeeping is wave-uniform (scalar)
-            uint32_t svm = 0;
+            // ---- key groups: P' range of the tile (keys past the chunk have
+            // v_scale 0); the scales are >= 0, so their bit patterns order as
+            // integers; the range bookkeeping is wave-uniform (scalar)
+            bool ef_up = false;
+            float fe = 1.0f;
+            if constexpr (!FIXED_EF) {
+                uint32_t svm = 0;
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+                for (int s = 0; s < 2; ++s)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) svm = max(svm, __float_as_uint(sv[s][r]));
-            svm = __builtin_amdgcn_readfirstlane(rows_max_u32(svm));
-            const int ef_t = max((int)(svm >> 23), 15);
-            const int ef_new = max(ef_run, ef_t);
-            const bool ef_up = ef_new > ef_run;
-            const float fe = pow2i(max(ef_run - ef_new, -126));
-            ef_run = ef_new;
-            const float kappa = pow2i(141 - kLazyMax - ef_run);
+                    for (int r = 0; r < 4; ++r) svm = max(svm, __float_as_uint(sv[s][r]));
+                svm = __builtin_amdgcn_readfirstlane(rows_max_u32(svm));
+                const int ef_t = max((int)(svm >> 23), 15);
+                const int ef_new = max(ef_run, ef_t);
+                ef_up = ef_new > ef_run;
+                fe = pow2i(max(ef_run - ef_new, -126));
+                ef_run = ef_new;
+                const float kappa = pow2i(141 - kLazyMax - ef_run);
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+                for (int s = 0; s < 2; ++s)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sv[s][r] *= kappa;
+                    for (int r = 0; r < 4; ++r) sv[s][r] *= kappa;
+            }
 
-            // ---- online softmax of each row tile; P' = p * v_scale * kappa
+            // ---- online softmax of each row tile; P' = p * (v_scale * kappa)
             int nv[2] = {16, 16};
             if (SP) {
                 nv[0] = lds_nv(buf)[0];

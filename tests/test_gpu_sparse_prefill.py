@@ -83,6 +83,35 @@ def test_groups_and_head_dims(Hq, Hkv, D):
     check(case, sel, ql, f"Hq{Hq} Hkv{Hkv} D{D}", layout="slot_major" if D == 64 else "head_major")
 
 
+def test_unread_scales_do_not_move_the_range():
+    """Every value and key scale the kernel must not read -- past a selected
+    block's valid count, and in blocks no request selected -- set to 2^100.
+    The kernel fixes its P' range exponent from the scales of the keys it
+    reads; had it taken one of these, P' would underflow and the output
+    would collapse towards zero."""
+    case = synth.decode_case([900, 2000, 130], 32, 8, 128, 16, rows=70, seed=230)
+    ql = torch.tensor([70, 33, 70], dtype=torch.int32)
+    sel = synth.prefill_selection(case.layout, ql, 0.3, seed=231, partial_frac=0.6)
+    bs = case.layout.block_size
+    dc = cache_case(case, DEV)
+    readable = torch.zeros(case.layout.num_slots, dtype=torch.bool)
+    for b, vlen in enumerate(sel.context_lens.tolist()):
+        for i in range((vlen + bs - 1) // bs):
+            n = min(bs, vlen - i * bs, max(int(sel.block_valid[b, i]), 0))
+            blk = int(sel.block_tables[b, i])
+            readable[blk * bs: blk * bs + max(n, 0)] = True
+    far = readable.logical_not().to(DEV)
+    log(f"unread scales: {int(far.sum())} of {far.numel()} slots set to 2^100")
+    dc.v_scale[far] = 2.0 ** 100
+    dc.k_scale[far] = 2.0 ** 100
+    out = run(case, dc, sel, ql)
+    torch.cuda.synchronize()
+    host = dc.host()
+    for b, n in enumerate(ql.tolist()):
+        ref = oracle_rows(case, host, sel, b, n)
+        assert_attn_close(out[b, :n].cpu().numpy(), ref, f"unread scales, request {b}")
+
+
 def test_every_block_full_matches_dense():
     case = synth.decode_case([3000, 777], 32, 8, 128, 16, rows=64, seed=220)
     L = case.layout
