@@ -10,11 +10,13 @@
 // NT row tiles, each stacking 16/G tokens x G query heads into the 16 MFMA
 // rows exactly as the decode split kernel stacks verify rows: QK^T MFMA
 // (bf16), online softmax with the key scale on the score, P' = p * v_scale
-// in fp16, PV MFMA (fp16). The range exponent of P' is fixed per workgroup
-// before the key loop: one pass over the value scales of every key the
-// workgroup will read takes their largest exponent (the value the decode
-// kernel's running exponent reaches at its last tile), so the loader stores
-// v_scale * kappa in LDS and the tiles do no range bookkeeping.
+// in fp16, PV MFMA (fp16). With one key group the range exponent of P' is
+// fixed per workgroup before the key loop: one pass over the value scales
+// of every key the workgroup will read takes their largest exponent (the
+// value the decode kernel's running exponent reaches at its last tile), so
+// the loader stores v_scale * kappa in LDS and the tiles do no range
+// bookkeeping. Key groups keep a running exponent per group, updated per
+// tile and shared by the row tiles.
 //
 // The K/V codes and scales of each 32-token tile are read from the cache
 // once per workgroup into LDS (two buffers; with key groups four per group,
