@@ -79,6 +79,31 @@ def test_many_query_blocks_one_key_group():
     assert_attn_close(out.cpu().numpy(), ref, "one key group")
 
 
+def test_unread_scales_do_not_move_the_range():
+    """One key group (800 workgroups): every scale the kernel must not read
+    -- past each request's context in its last block, and in blocks no
+    request uses -- set to 2^100. The kernel fixes its P' range exponent
+    from the scales of the keys it reads; had it taken one of these, P'
+    would underflow and the output would collapse towards zero."""
+    lens = [300 + 37 * i for i in range(20)]
+    case = synth.decode_case(lens, 32, 8, 128, 16, rows=160, seed=161)
+    L = case.layout
+    dc = cache_case(case, DEV)
+    readable = torch.zeros(L.num_slots, dtype=torch.bool)
+    for b, n in enumerate(L.context_lens.tolist()):
+        for i in range((n + 15) // 16):
+            blk = int(L.block_tables[b, i])
+            readable[blk * 16: blk * 16 + min(16, n - i * 16)] = True
+    far = readable.logical_not().to(DEV)
+    log(f"prefill unread scales: {int(far.sum())} of {far.numel()} slots set to 2^100")
+    dc.v_scale[far] = 2.0 ** 100
+    dc.k_scale[far] = 2.0 ** 100
+    out = run_prefill(case, dc)
+    torch.cuda.synchronize()
+    ref = oracle_prefill(case, dc.host())
+    assert_attn_close(out.cpu().numpy(), ref, "unread scales")
+
+
 def test_value_ranges_and_growing_scores():
     """Mixed V magnitudes (rows x1e-3, x100, zero, ~1e-33) with 1% K outlier
     channels, and K rows whose size grows along the sequence, so a row's
